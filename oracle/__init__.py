@@ -1,0 +1,23 @@
+"""CPU oracle (float64, exact gate logits) -- TEST INFRASTRUCTURE ONLY.
+
+Imported only by tests/, the package smoke check and the benchmark's CPU-baseline
+leg.  It shares no code with the HIP library.
+"""
+from .moe_oracle import (  # noqa: F401
+    e4m3_value,
+    e8m0_value,
+    E4M3_TABLE,
+    mx_dequant,
+    exact_logits,
+    topk_ids,
+    softmax_pick_renormalise,
+    route,
+    route_replay,
+    validate_replay_ids,
+    dispatch,
+    silu,
+    expert_ffn,
+    layer,
+    layer_dense,
+    normwise_rel_err,
+)

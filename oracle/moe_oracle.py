@@ -1,0 +1,290 @@
+"""CPU oracle of one Mixture-of-Experts layer's forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import this module; the library never does, and
+it shares no code with the HIP path (the seeded input generator aside, which
+holds none of this arithmetic).
+
+What it computes, and where that is defined:
+  * A gating layer picks, for each token, 8 of 384 experts from the token's hidden
+    state (Training Data podcast page "How Cursor Trained Composer on Fireworks",
+    section on floating point and MoE; same fact on the page "Cursor 訓練 Composer 2
+    的五大工程挑戰", section "浮點數的陷阱").  The pages do not state the gating
+    function; the reading used here is softmax over all experts, keep the top k,
+    renormalise the kept probabilities to sum to one, ties to the lower index.
+  * Router replay: the inference engine returns the chosen expert IDs per token per
+    MoE layer and the training forward overrides the router's assignment with them,
+    while the router still computes gate scores (Composer 2 Technical Report, §6.2,
+    paragraph on inference and weight sync).
+  * The experts run as one grouped GEMM per expert group (Composer 2 Technical
+    Report, §6.1 "Kernels", Figure 10); each expert is a SwiGLU FFN
+    (silu(x W1) * (x W3)) W2; the tokens' expert outputs are combined as the
+    routing-weighted sum (§6.1 "Parallelism": dispatch and combine), plus the
+    always-on shared expert when present.
+
+Precision: every input value is converted to float64 exactly.  Gate logits are the
+correctly rounded value of the exact sum (each product of two stored values is
+exact in float64: at most 24 + 24 significant bits and no underflow for fp32, bf16
+or MXFP8 inputs; ``math.fsum`` then rounds the exact sum once).  Selection uses
+those exact logits.  Everything after selection is ordinary float64 (numpy).
+
+Every function here is pinned by a CPU test against something other than itself
+(closed forms, brute force, exact rational arithmetic, an independent
+formulation); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def f64(a) -> np.ndarray:
+    """Exact conversion of stored values (fp32, bf16-as-fp32, ints) to float64."""
+    return np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 decoding (OCP Microscaling Formats v1.0: E4M3 elements, E8M0 scales)
+# ---------------------------------------------------------------------------
+def e4m3_value(code: int) -> float:
+    """Value of one FP8 E4M3 code: sign, 4-bit exponent (bias 7), 3-bit mantissa.
+
+    Exponent field 0 holds subnormals m/8 * 2^-6; S.1111.111 is NaN; there are no
+    infinities, so S.1111.110 = 448 is the largest magnitude.
+    """
+    s = (code >> 7) & 1
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    if e == 0:
+        v = (m / 8.0) * 2.0 ** -6
+    else:
+        v = (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return -v if s else v
+
+
+def e8m0_value(code: int) -> float:
+    """Value of one E8M0 scale code: 2^(code - 127); code 255 is NaN."""
+    if code == 255:
+        return math.nan
+    return 2.0 ** (int(code) - 127)
+
+
+E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def mx_dequant(codes, scales, block: int = 32) -> np.ndarray:
+    """Exact float64 values of an MXFP8 tensor stored along its last dimension."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    K = codes.shape[-1]
+    assert scales.shape[-1] * block == K
+    vals = E4M3_TABLE[codes]
+    sc = np.vectorize(e8m0_value, otypes=[np.float64])(scales)
+    return vals * np.repeat(sc, block, axis=-1)
+
+
+# ---------------------------------------------------------------------------
+# Routing
+# ---------------------------------------------------------------------------
+def exact_logits(x, w_gate, bias=None) -> np.ndarray:
+    """logit[t, e] = sum_i x[t, i] * w_gate[i, e] (+ bias[e]), correctly rounded.
+
+    x [T, d], w_gate [d, E], bias [E] or None.  Each product is exact in float64
+    (see the module docstring), and ``math.fsum`` returns the exact sum rounded
+    once, so the result does not depend on any summation order.
+    """
+    x = f64(x)
+    w = f64(w_gate)
+    T, d = x.shape
+    d2, E = w.shape
+    assert d == d2
+    assert np.all(np.isfinite(x)) and np.all(np.isfinite(w))
+    b = None if bias is None else f64(bias)
+    out = np.empty((T, E), dtype=np.float64)
+    for t in range(T):
+        prods = x[t][:, None] * w          # [d, E], every entry exact
+        for e in range(E):
+            terms = prods[:, e].tolist()
+            if b is not None:
+                terms.append(float(b[e]))
+            out[t, e] = math.fsum(terms)
+    return out
+
+
+def topk_ids(logits, k: int) -> np.ndarray:
+    """The k largest logits of each row, ordered by (logit descending, index ascending)."""
+    logits = f64(logits)
+    T, E = logits.shape
+    assert 1 <= k <= E
+    ids = np.empty((T, k), dtype=np.int64)
+    for t in range(T):
+        row = logits[t]
+        order = sorted(range(E), key=lambda e: (-row[e], e))
+        ids[t] = order[:k]
+    return ids
+
+
+def softmax_pick_renormalise(logits, ids) -> np.ndarray:
+    """Softmax over all experts, keep the probabilities at ``ids``, renormalise them.
+
+    Rows of the result sum to one; column r is the weight of expert ids[t, r].
+    """
+    logits = f64(logits)
+    m = logits.max(axis=1, keepdims=True)
+    p = np.exp(logits - m)
+    p = p / p.sum(axis=1, keepdims=True)
+    picked = np.take_along_axis(p, np.asarray(ids, dtype=np.int64), axis=1)
+    return picked / picked.sum(axis=1, keepdims=True)
+
+
+def route(x, w_gate, bias, k: int):
+    """Learned routing: returns (ids [T,k], weights [T,k] float64, logits [T,E])."""
+    logits = exact_logits(x, w_gate, bias)
+    ids = topk_ids(logits, k)
+    return ids, softmax_pick_renormalise(logits, ids), logits
+
+
+def validate_replay_ids(ids_in, E: int) -> None:
+    """Replayed IDs must lie in [0, E) and be distinct within each row."""
+    ids = np.asarray(ids_in)
+    if ids.ndim != 2:
+        raise ValueError("replayed ids must be [T, k]")
+    if ids.size and (ids.min() < 0 or ids.max() >= E):
+        raise ValueError("replayed expert id out of range")
+    for t in range(ids.shape[0]):
+        if len(set(ids[t].tolist())) != ids.shape[1]:
+            raise ValueError(f"replayed ids of token {t} are not distinct")
+
+
+def route_replay(x, w_gate, bias, ids_in, weights_in=None):
+    """Replayed routing: the caller's IDs override the router's choice.
+
+    The gate logits are still computed.  Weights are the caller's (used verbatim)
+    when given, else the router's softmax probabilities at the replayed IDs,
+    renormalised, in the caller's column order.  Returns (ids, weights, logits).
+    """
+    logits = exact_logits(x, w_gate, bias)
+    E = logits.shape[1]
+    validate_replay_ids(ids_in, E)
+    ids = np.asarray(ids_in, dtype=np.int64)
+    if weights_in is not None:
+        w = f64(weights_in).copy()
+    else:
+        w = softmax_pick_renormalise(logits, ids)
+    return ids, w, logits
+
+
+# ---------------------------------------------------------------------------
+# Dispatch (token permutation into contiguous per-expert segments)
+# ---------------------------------------------------------------------------
+def dispatch(ids, E: int):
+    """Sort the T*k (token, slot) pairs by (expert ascending, token ascending).
+
+    Returns offsets [E+1] (segment e is rows offsets[e]..offsets[e+1]-1),
+    perm [T*k] with perm[j] = t*k + r for sorted row j, and row_of [T*k] with
+    row_of[t*k + r] = j (the inverse of perm).
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    T, k = ids.shape
+    pairs = sorted((int(ids[t, r]), t, r) for t in range(T) for r in range(k))
+    counts = [0] * E
+    for e, _, _ in pairs:
+        counts[e] += 1
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    perm = np.array([t * k + r for (_, t, r) in pairs], dtype=np.int64)
+    row_of = np.empty(T * k, dtype=np.int64)
+    row_of[perm] = np.arange(T * k)
+    return offsets, perm, row_of
+
+
+# ---------------------------------------------------------------------------
+# Expert FFN and combine
+# ---------------------------------------------------------------------------
+def silu(z):
+    """silu(z) = z / (1 + exp(-z)) = z * sigmoid(z)."""
+    z = f64(z)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def expert_ffn(x_rows, w1, w3, w2) -> np.ndarray:
+    """SwiGLU expert: (silu(x W1) * (x W3)) W2 in float64.
+
+    Weights are stored output-major: w1, w3 [I, d] and w2 [d, I], so the
+    mathematical W1 is ``w1.T``.
+    """
+    xr = f64(x_rows)
+    a = xr @ f64(w1).T
+    g = xr @ f64(w3).T
+    return (silu(a) * g) @ f64(w2).T
+
+
+def layer(x, w_gate, bias, experts, shared, k: int, ids_in=None, weights_in=None):
+    """One MoE layer forward through dispatch, per-expert FFN and combine.
+
+    ``experts[e]`` -> (w1, w3, w2) for routed expert e (any indexable; it may fetch
+    lazily); ``shared`` is (w1, w3, w2) or None.  With ``ids_in`` the routing is
+    replayed.  Returns a dict with y [T, d] and the routing/dispatch intermediates.
+    """
+    xf = f64(x)
+    T, d = xf.shape
+    if ids_in is None:
+        ids, w, logits = route(xf, w_gate, bias, k)
+    else:
+        ids, w, logits = route_replay(xf, w_gate, bias, ids_in, weights_in)
+    E = logits.shape[1]
+    offsets, perm, row_of = dispatch(ids, E)
+    rows = np.zeros((T * k, d), dtype=np.float64)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        toks = perm[lo:hi] // k
+        w1, w3, w2 = experts[e]
+        rows[lo:hi] = expert_ffn(xf[toks], w1, w3, w2)
+    y = np.zeros((T, d), dtype=np.float64)
+    for t in range(T):
+        for r in range(k):
+            y[t] += w[t, r] * rows[row_of[t * k + r]]
+    if shared is not None:
+        y += expert_ffn(xf, *shared)
+    return {"y": y, "ids": ids, "weights": w, "logits": logits,
+            "offsets": offsets, "perm": perm, "row_of": row_of, "rows": rows}
+
+
+def layer_dense(x, w_gate, bias, experts, shared, k: int):
+    """The same layer without dispatch: y = sum_e g_e(x) FFN_e(x) + shared(x).
+
+    g_e is the routing weight if e was selected for the token, else 0.  Every
+    expert runs on every token, so this form never permutes anything.
+    """
+    xf = f64(x)
+    T, d = xf.shape
+    ids, w, logits = route(xf, w_gate, bias, k)
+    E = logits.shape[1]
+    G = np.zeros((T, E), dtype=np.float64)
+    for t in range(T):
+        for r in range(k):
+            G[t, ids[t, r]] = w[t, r]
+    y = np.zeros((T, d), dtype=np.float64)
+    for e in range(E):
+        if not np.any(G[:, e]):
+            continue
+        y += G[:, e:e + 1] * expert_ffn(xf, *experts[e])
+    if shared is not None:
+        y += expert_ffn(xf, *shared)
+    return y
+
+
+def normwise_rel_err(y, y_ref) -> float:
+    """max |y - y_ref| / max |y_ref| over all elements compared."""
+    y = f64(y)
+    y_ref = f64(y_ref)
+    den = np.max(np.abs(y_ref))
+    if den == 0:
+        return float(np.max(np.abs(y)))
+    return float(np.max(np.abs(y - y_ref)) / den)

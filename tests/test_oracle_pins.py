@@ -1,0 +1,366 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each test ties one oracle function to exact rational arithmetic, a closed form,
+brute force, an independent formulation, or a hand-derived fixture, chosen so a
+dropped term, a wrong sign or index, or a transposed operand fails at least one.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _f32(a):
+    return np.asarray(a, dtype=np.float32)
+
+
+def _bf16_values(rng, shape, scale=1.0):
+    """Random values exactly representable in bf16 (top 16 bits of an fp32)."""
+    v = _f32(rng.standard_normal(shape) * scale)
+    u = v.view(np.uint32) & np.uint32(0xFFFF0000)
+    return u.view(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# logits
+# ---------------------------------------------------------------------------
+def _rational_logits(x, w, b):
+    T, d = x.shape
+    E = w.shape[1]
+    out = np.empty((T, E))
+    for t in range(T):
+        for e in range(E):
+            s = sum(Fraction(float(x[t, i])) * Fraction(float(w[i, e])) for i in range(d))
+            if b is not None:
+                s += Fraction(float(b[e]))
+            out[t, e] = float(s)       # Fraction -> float rounds correctly
+    return out
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_exact_logits_equal_rational_arithmetic(seed):
+    rng = np.random.default_rng(seed)
+    T, d, E = 4, 9, 7
+    x = _bf16_values(rng, (T, d))
+    w = _f32(rng.standard_normal((d, E)) / 3)
+    b = _f32(rng.standard_normal(E))
+    # add cancellation-heavy columns: big +/- pairs around small terms
+    w[:, 0] = _f32([2.0 ** 60, 1.0, -(2.0 ** 60), 3.0, -3.0, 2.0 ** -30, 1e20, -1e20, 0.5])
+    x[:, :] = np.where(np.arange(d)[None, :] < 9, x, x)
+    x[0] = 1.0
+    got = oracle.exact_logits(x, w, b)
+    want = _rational_logits(x, w, b)
+    assert np.array_equal(got, want)
+
+
+def test_exact_logits_beat_naive_summation():
+    # (2^60 + 1) - 2^60 is 0 left to right in float64 but exactly 1.
+    x = _f32([[1.0, 1.0, 1.0]])
+    w = _f32([[2.0 ** 60], [1.0], [-(2.0 ** 60)]])
+    assert oracle.exact_logits(x, w)[0, 0] == 1.0
+    assert (np.float64(2.0 ** 60) + 1.0) - 2.0 ** 60 == 0.0
+
+
+def test_unit_vector_gives_gate_row():
+    rng = np.random.default_rng(3)
+    d, E = 16, 12
+    w = _f32(rng.standard_normal((d, E)))
+    b = _f32(rng.standard_normal(E))
+    for i in (0, 5, d - 1):
+        x = np.zeros((1, d), np.float32)
+        x[0, i] = 1.0
+        assert np.array_equal(oracle.exact_logits(x, w, b)[0], w[i].astype(np.float64) + b)
+        assert np.array_equal(oracle.exact_logits(x, w)[0], w[i].astype(np.float64))
+
+
+def test_zero_input_routes_to_lowest_indices_with_equal_weights():
+    d, E, k = 8, 384, 8
+    rng = np.random.default_rng(4)
+    w = _f32(rng.standard_normal((d, E)))
+    ids, wts, logits = oracle.route(np.zeros((3, d), np.float32), w, None, k)
+    assert np.all(logits == 0)
+    assert np.array_equal(ids, np.tile(np.arange(k), (3, 1)))
+    assert np.all(wts == 1.0 / k)
+
+
+# ---------------------------------------------------------------------------
+# top-k
+# ---------------------------------------------------------------------------
+def _brute_topk(row, k):
+    """Rank of e = number of experts that beat it (larger, or equal with lower index)."""
+    E = len(row)
+    ids = [None] * k
+    for e in range(E):
+        beaten = sum(1 for j in range(E) if row[j] > row[e] or (row[j] == row[e] and j < e))
+        if beaten < k:
+            ids[beaten] = e
+    return ids
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_matches_brute_force_with_ties(seed):
+    rng = np.random.default_rng(10 + seed)
+    E = int(rng.integers(3, 11))
+    k = int(rng.integers(1, E + 1))
+    # few distinct values -> many exact ties
+    logits = rng.integers(-3, 4, size=(20, E)).astype(np.float64) / 4
+    ids = oracle.topk_ids(logits, k)
+    for t in range(20):
+        assert list(ids[t]) == _brute_topk(list(logits[t]), k)
+
+
+def test_topk_set_maximises_sum_when_distinct():
+    rng = np.random.default_rng(7)
+    E, k = 10, 3
+    for _ in range(10):
+        row = rng.standard_normal(E)
+        best = max(itertools.combinations(range(E), k), key=lambda s: sum(row[list(s)]))
+        got = oracle.topk_ids(row[None, :], k)[0]
+        assert sorted(got) == sorted(best)
+        assert all(row[got[i]] > row[got[i + 1]] for i in range(k - 1))
+
+
+def test_duplicate_gate_columns_tie_to_lower_index():
+    rng = np.random.default_rng(8)
+    d, E = 32, 12
+    w = _f32(rng.standard_normal((d, E)))
+    w[:, 9] = w[:, 2]              # experts 2 and 9 always tie exactly
+    x = _bf16_values(rng, (50, d))
+    ids, _, logits = oracle.route(x, w, None, 6)
+    for t in range(50):
+        row = list(ids[t])
+        if 2 in row and 9 in row:
+            assert row.index(2) < row.index(9)
+        if 9 in row:
+            assert 2 in row
+        assert logits[t, 2] == logits[t, 9]
+
+
+# ---------------------------------------------------------------------------
+# gate weights
+# ---------------------------------------------------------------------------
+def test_weights_closed_forms():
+    rng = np.random.default_rng(9)
+    logits = rng.standard_normal((30, 20)) * 3
+    # k = 1 -> weight exactly 1
+    ids1 = oracle.topk_ids(logits, 1)
+    assert np.all(oracle.softmax_pick_renormalise(logits, ids1) == 1.0)
+    # k = 2 -> (sigmoid(l0 - l1), sigmoid(l1 - l0))
+    ids2 = oracle.topk_ids(logits, 2)
+    w2 = oracle.softmax_pick_renormalise(logits, ids2)
+    for t in range(30):
+        l0, l1 = logits[t, ids2[t, 0]], logits[t, ids2[t, 1]]
+        assert abs(w2[t, 0] - 1 / (1 + math.exp(l1 - l0))) < 1e-15
+        assert abs(w2[t, 1] - 1 / (1 + math.exp(l0 - l1))) < 1e-15
+    # equal logits -> 1/k
+    eq = np.zeros((2, 16))
+    assert np.allclose(oracle.softmax_pick_renormalise(eq, oracle.topk_ids(eq, 8)), 1 / 8, rtol=0, atol=1e-16)
+
+
+def test_full_softmax_equals_restricted_form_and_sums_to_one():
+    rng = np.random.default_rng(11)
+    logits = rng.standard_normal((40, 384)) * 2
+    k = 8
+    ids = oracle.topk_ids(logits, k)
+    w = oracle.softmax_pick_renormalise(logits, ids)
+    for t in range(40):
+        sel = logits[t, ids[t]]
+        ex = [math.exp(v - sel[0]) for v in sel]
+        s = math.fsum(ex)
+        assert np.allclose(w[t], [v / s for v in ex], rtol=0, atol=1e-15)
+        assert abs(math.fsum(w[t]) - 1.0) < 1e-15
+        assert all(w[t, r] >= w[t, r + 1] for r in range(k - 1))
+
+
+# ---------------------------------------------------------------------------
+# dispatch
+# ---------------------------------------------------------------------------
+def test_dispatch_golden():
+    g = json.load(open(os.path.join(GOLDEN, "dispatch_hand_sorted.json")))
+    off, perm, row_of = oracle.dispatch(np.array(g["ids"]), g["E"])
+    assert off.tolist() == g["offsets"]
+    assert perm.tolist() == g["perm"]
+    assert row_of.tolist() == g["row_of"]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_dispatch_brute_force_and_invariants(seed):
+    rng = np.random.default_rng(20 + seed)
+    T, E, k = int(rng.integers(1, 40)), int(rng.integers(1, 30)), 0
+    k = int(rng.integers(1, min(E, 6) + 1))
+    p = 1.0 / np.arange(1, E + 1) ** 1.5
+    p /= p.sum()
+    ids = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)])
+    off, perm, row_of = oracle.dispatch(ids, E)
+    # brute force: walk experts, then tokens, then slots
+    bf = [t * k + r for e in range(E) for t in range(T) for r in range(k) if ids[t, r] == e]
+    assert perm.tolist() == bf
+    assert off[0] == 0 and off[E] == T * k
+    assert np.all(np.diff(off) >= 0)
+    for e in range(E):
+        seg = perm[off[e]:off[e + 1]]
+        assert np.all(ids.ravel()[seg] == e)
+        assert np.all(np.diff(seg // k) > 0)          # tokens strictly ascending
+    assert np.array_equal(np.bincount(perm // k, minlength=T), np.full(T, k))
+    assert np.array_equal(perm[row_of], np.arange(T * k))
+    assert np.array_equal(row_of[perm], np.arange(T * k))
+
+
+# ---------------------------------------------------------------------------
+# expert FFN
+# ---------------------------------------------------------------------------
+def test_ffn_scalar_closed_form():
+    # d = I = 1: x=2, W1=0.5, W3=3, W2=-1.5 -> a=1, g=6, out = -1.5 * 6 * silu(1)
+    out = oracle.expert_ffn([[2.0]], [[0.5]], [[3.0]], [[-1.5]])
+    assert abs(out[0, 0] - (-9.0 / (1 + math.exp(-1)))) < 1e-15
+    assert oracle.silu(0.0) == 0.0
+    assert abs(oracle.silu(40.0) - 40.0) < 1e-12
+    assert abs(oracle.silu(-40.0)) < 1e-15
+
+
+def test_ffn_zero_cases():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((5, 6))
+    w1, w3, w2 = rng.standard_normal((4, 6)), rng.standard_normal((4, 6)), rng.standard_normal((6, 4))
+    assert np.all(oracle.expert_ffn(x, np.zeros_like(w1), w3, w2) == 0)
+    assert np.all(oracle.expert_ffn(np.zeros_like(x), w1, w3, w2) == 0)
+
+
+def test_ffn_matches_elementwise_loops_and_layout():
+    rng = np.random.default_rng(13)
+    n, d, I = 3, 4, 5
+    x = rng.standard_normal((n, d))
+    w1, w3, w2 = rng.standard_normal((I, d)), rng.standard_normal((I, d)), rng.standard_normal((d, I))
+    got = oracle.expert_ffn(x, w1, w3, w2)
+    for t in range(n):
+        h = []
+        for j in range(I):
+            a = math.fsum(x[t, i] * w1[j, i] for i in range(d))
+            g = math.fsum(x[t, i] * w3[j, i] for i in range(d))
+            h.append(a / (1 + math.exp(-a)) * g)
+        for c in range(d):
+            want = math.fsum(h[j] * w2[c, j] for j in range(I))
+            assert abs(got[t, c] - want) < 1e-12
+    # swapping W1 and W3 changes the result (silu applies to the W1 branch only)
+    assert not np.allclose(oracle.expert_ffn(x, w3, w1, w2), got)
+
+
+# ---------------------------------------------------------------------------
+# whole layer
+# ---------------------------------------------------------------------------
+def test_layer_golden_closed_form():
+    g = json.load(open(os.path.join(GOLDEN, "tiny_layer_closed_form.json")))
+    ev = lambda s: eval(s, {"exp": math.exp, "__builtins__": {}})  # noqa: E731 (fixture expressions)
+    experts = [(np.array(g["w1"][e]), np.array(g["w3"][e]), np.array(g["w2"][e])) for e in range(4)]
+    res = oracle.layer(np.array(g["x"]), np.array(g["w_gate"]), None, experts, None, g["k"])
+    assert res["ids"].tolist() == g["expected_ids"]
+    want_w = np.array([[ev(s) for s in row] for row in g["expected_weights_expr"]])
+    want_y = np.array([[ev(s) for s in row] for row in g["expected_y_expr"]])
+    assert np.allclose(res["weights"], want_w, rtol=0, atol=1e-15)
+    assert np.allclose(res["y"], want_y, rtol=0, atol=1e-15)
+
+
+def _small_layer(seed, T=10, d=8, I=4, E=16, k=4, shared=True, bias=False):
+    rng = np.random.default_rng(seed)
+    x = _bf16_values(rng, (T, d))
+    wg = _f32(rng.standard_normal((d, E)) / math.sqrt(d))
+    b = _f32(rng.standard_normal(E)) if bias else None
+    experts = [(rng.standard_normal((I, d)) / math.sqrt(d), rng.standard_normal((I, d)) / math.sqrt(d),
+                rng.standard_normal((d, I)) / math.sqrt(I)) for _ in range(E)]
+    sh = (rng.standard_normal((I, d)), rng.standard_normal((I, d)), rng.standard_normal((d, I))) if shared else None
+    return x, wg, b, experts, sh, k
+
+
+@pytest.mark.parametrize("seed,shared,bias", [(0, True, False), (1, False, True), (2, True, True)])
+def test_layer_dispatched_equals_dense(seed, shared, bias):
+    x, wg, b, experts, sh, k = _small_layer(seed, shared=shared, bias=bias)
+    y = oracle.layer(x, wg, b, experts, sh, k)["y"]
+    yd = oracle.layer_dense(x, wg, b, experts, sh, k)
+    assert np.max(np.abs(y - yd)) <= 1e-12 * max(1.0, np.max(np.abs(yd)))
+
+
+def test_layer_token_permutation_permutes_output():
+    x, wg, b, experts, sh, k = _small_layer(3, T=12)
+    y = oracle.layer(x, wg, b, experts, sh, k)["y"]
+    p = np.random.default_rng(5).permutation(12)
+    yp = oracle.layer(x[p], wg, b, experts, sh, k)["y"]
+    assert np.max(np.abs(yp - y[p])) <= 1e-12
+
+
+def test_replay_own_ids_equals_learned():
+    x, wg, b, experts, sh, k = _small_layer(4, bias=True)
+    learned = oracle.layer(x, wg, b, experts, sh, k)
+    rep = oracle.layer(x, wg, b, experts, sh, k, ids_in=learned["ids"])
+    assert np.array_equal(rep["y"], learned["y"])
+    assert np.array_equal(rep["weights"], learned["weights"])
+    rep2 = oracle.layer(x, wg, b, experts, sh, k, ids_in=learned["ids"], weights_in=learned["weights"])
+    assert np.array_equal(rep2["y"], learned["y"])
+
+
+def test_replay_weights_used_verbatim_and_column_order_kept():
+    x, wg, b, experts, sh, k = _small_layer(5)
+    ids = np.array([[3, 1, 7, 0]] * x.shape[0])
+    wts = np.tile([0.1, 0.2, 0.3, 0.5], (x.shape[0], 1))   # sums to 1.1: not renormalised
+    res = oracle.layer(x, wg, b, experts, sh, k, ids_in=ids, weights_in=wts)
+    assert np.array_equal(res["weights"], wts)
+    # reversing the column order of (ids, weights) leaves y unchanged in exact terms
+    res2 = oracle.layer(x, wg, b, experts, sh, k, ids_in=ids[:, ::-1], weights_in=wts[:, ::-1])
+    assert np.max(np.abs(res2["y"] - res["y"])) < 1e-12
+    # replay weights from the router at the given ids (no weights passed)
+    res3 = oracle.layer(x, wg, b, experts, sh, k, ids_in=ids)
+    lg = oracle.exact_logits(x, wg, b)
+    for t in range(x.shape[0]):
+        ex = np.exp(lg[t, ids[t]] - lg[t, ids[t]].max())
+        assert np.allclose(res3["weights"][t], ex / ex.sum(), rtol=0, atol=1e-15)
+
+
+def test_replay_rejects_bad_ids():
+    x, wg, b, experts, sh, k = _small_layer(6)
+    T = x.shape[0]
+    with pytest.raises(ValueError):
+        oracle.route_replay(x, wg, b, np.full((T, k), 16))
+    with pytest.raises(ValueError):
+        oracle.route_replay(x, wg, b, np.full((T, k), -1))
+    bad = np.tile(np.arange(k), (T, 1))
+    bad[3, 1] = bad[3, 0]
+    with pytest.raises(ValueError):
+        oracle.route_replay(x, wg, b, bad)
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 decoding
+# ---------------------------------------------------------------------------
+def test_e4m3_table_hand_values():
+    # OCP MX v1.0 FP8 E4M3: bias 7, subnormal step 2^-9, max 448, S.1111.111 NaN
+    assert oracle.e4m3_value(0x00) == 0.0
+    assert oracle.e4m3_value(0x01) == 2.0 ** -9
+    assert oracle.e4m3_value(0x07) == 7 * 2.0 ** -9
+    assert oracle.e4m3_value(0x08) == 2.0 ** -6
+    assert oracle.e4m3_value(0x38) == 1.0
+    assert oracle.e4m3_value(0x3C) == 1.5
+    assert oracle.e4m3_value(0x7E) == 448.0
+    assert math.isnan(oracle.e4m3_value(0x7F))
+    assert oracle.e4m3_value(0xFE) == -448.0
+    assert oracle.e4m3_value(0xB8) == -1.0
+    pos = oracle.E4M3_TABLE[1:0x7F]
+    assert np.all(np.diff(pos) > 0)               # codes 1..126 strictly increasing
+    assert len(set(pos.tolist())) == 126
+    assert oracle.e8m0_value(127) == 1.0
+    assert oracle.e8m0_value(0) == 2.0 ** -127
+    assert oracle.e8m0_value(254) == 2.0 ** 127
+    assert math.isnan(oracle.e8m0_value(255))
+
+
+def test_mx_dequant_blocks():
+    codes = np.array([[0x38] * 32 + [0x3C] * 32], dtype=np.uint8)
+    scales = np.array([[127, 129]], dtype=np.uint8)
+    v = oracle.mx_dequant(codes, scales)
+    assert np.all(v[0, :32] == 1.0) and np.all(v[0, 32:] == 6.0)

@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of one MoE-layer forward on one MI355X.
+
+A step is one pass of the whole hot path over one batch: gate GEMM + top-k +
+softmax-renormalise (or router replay), counting-sort dispatch, grouped SwiGLU FFN
+(W1/W3 GEMM with the SwiGLU epilogue, then the W2 GEMM) and the fixed-order
+combine, all through the libmoe C ABI on the current stream.  Inputs are drawn
+once, on the GPU, before timing and stay resident in HBM.
+
+Prints one JSON line with tokens/s, per-stage HIP-event durations, the roofline of
+the dominant kernel and the CPU oracle timed on a bounded token sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + MFMA util, 384-expert top-8 d=7168 T=4096 bf16"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="bf16_t4096",
+                    help="bf16_t4096 (default), replay_zipf_t4096, bf16_t128_stream, tiny_fp32_t32")
+    ap.add_argument("--cpu-sample", type=int, default=6,
+                    help="tokens of the same batch the CPU oracle is timed on (0: skip)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the single-GPU hot path only; --gpus must be 1 "
+              "(the layer is not sharded across GPUs in this library).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import parity_gate_gemm_amd as pg
+    import synth
+
+    pg.lib()  # fail loudly if the HIP library is missing
+    wl = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_draw = time.perf_counter()
+    inp = synth.make_layer_inputs(wl, device="cuda")
+    torch.cuda.synchronize()
+    t_draw = time.perf_counter() - t_draw
+
+    T, d, E, k, I = wl.T, wl.d, wl.E, wl.k, wl.inter
+    dt = {"f32": pg.MOE_F32, "bf16": pg.MOE_BF16, "mxfp8": pg.MOE_MXFP8}[wl.dtype]
+    replay = wl.routing == "replay"
+    has_shared = inp["shared"] is not None
+    ws = pg.Workspace(T, d, E, k, I, dt)
+    x, wg, bias = inp["x"], inp["w_gate"], inp["bias"]
+    routed = {n: inp[n] for n in ("w1", "w3", "w2", "w1_scale", "w3_scale", "w2_scale")}
+    shared = inp["shared"]
+    rows = T * k + (T if has_shared else 0)
+    odt = torch.float32 if dt == pg.MOE_F32 else torch.bfloat16
+    ids = inp["ids_in"] if replay else torch.empty(T, k, dtype=torch.int32, device=dev)
+    weights = torch.empty(T, k, dtype=torch.float32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    row_of = torch.empty(T * k, dtype=torch.int32, device=dev)
+    out = torch.empty(rows, d, dtype=odt, device=dev)
+    y = torch.empty(T, d, dtype=odt, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        if replay:
+            pg.moe_route_replay(x, wg, bias, ids, ws, weights_in=inp["weights_in"],
+                                x_scale=inp["x_scale"], weights_out=weights)
+        else:
+            pg.moe_route(x, wg, bias, k, ws, x_scale=inp["x_scale"], ids=ids, weights=weights)
+        if ev is not None:
+            ev[1].record()
+        pg.moe_dispatch(ids, E, ws, offsets=offsets, perm=perm, row_of=row_of)
+        if ev is not None:
+            ev[2].record()
+        pg.moe_expert_ffn_gate_up(x, routed, shared, offsets, perm, k, ws, x_scale=inp["x_scale"])
+        if ev is not None:
+            ev[3].record()
+        pg.moe_expert_ffn_down(dt, T, d, routed, shared, k, ws, out=out)
+        if ev is not None:
+            ev[4].record()
+        pg.moe_combine(out, row_of, weights, T, has_shared, dt, y=y)
+        if ev is not None:
+            ev[5].record()
+
+    for _ in range(args.warmup):
+        step()
+    st = pg.moe_check(ws)
+    if st != 0:
+        raise pg.MoeError(st, "warmup")
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = pg.moe_check(ws)
+    if st != 0:
+        raise pg.MoeError(st, "timed steps")
+
+    names = ["route", "dispatch", "ffn_gate_up", "ffn_down", "combine"]
+    stage_ms = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1])
+                                  for i in range(args.steps)])) for j, n in enumerate(names)}
+    ms_per_step = wall * 1e3 / args.steps
+
+    # ---- algorithmic work of one step (see the kernel notes in the design doc) ----
+    seg = np.diff(offsets.cpu().numpy())
+    touched = int((seg > 0).sum())
+    eb = {"f32": 4, "bf16": 2, "mxfp8": 1}[wl.dtype]
+    hb = 4 if dt == pg.MOE_F32 else 2
+    ob = 4 if dt == pg.MOE_F32 else 2
+    n_mats = touched + (1 if has_shared else 0)
+    mat = I * d * eb
+    bytes_gate_up = n_mats * 2 * mat + T * d * eb + rows * I * hb + T * k * 4
+    bytes_down = n_mats * mat + rows * I * hb + rows * d * ob
+    bytes_route = T * d * eb + d * E * 4 + T * k * 8 + (E * 4 if bias is not None else 0)
+    bytes_dispatch = T * k * 4 * 3 + (E + 1) * 4
+    bytes_combine = rows * d * ob + T * d * ob + T * k * 8
+    flops_gate_up = 2.0 * rows * d * 2 * I
+    flops_down = 2.0 * rows * I * d
+    gbs = lambda b, ms: b / (ms * 1e-3) / 1e9  # noqa: E731
+    stages = {
+        "route": {"ms": stage_ms["route"], "alg_bytes": bytes_route, "GB_s": gbs(bytes_route, stage_ms["route"])},
+        "dispatch": {"ms": stage_ms["dispatch"], "alg_bytes": bytes_dispatch,
+                     "GB_s": gbs(bytes_dispatch, stage_ms["dispatch"])},
+        "ffn_gate_up": {"ms": stage_ms["ffn_gate_up"], "alg_bytes": bytes_gate_up,
+                        "GB_s": gbs(bytes_gate_up, stage_ms["ffn_gate_up"]),
+                        "TFLOP_s": flops_gate_up / (stage_ms["ffn_gate_up"] * 1e-3) / 1e12},
+        "ffn_down": {"ms": stage_ms["ffn_down"], "alg_bytes": bytes_down,
+                     "GB_s": gbs(bytes_down, stage_ms["ffn_down"]),
+                     "TFLOP_s": flops_down / (stage_ms["ffn_down"] * 1e-3) / 1e12},
+        "combine": {"ms": stage_ms["combine"], "alg_bytes": bytes_combine,
+                    "GB_s": gbs(bytes_combine, stage_ms["combine"])},
+    }
+    dom = max(("ffn_gate_up", "ffn_down"), key=lambda n: stage_ms[n])
+    dom_kernel = {"ffn_gate_up": "grouped_gemm_bf16_kernel<0> (W1/W3 + SwiGLU)",
+                  "ffn_down": "grouped_gemm_bf16_kernel<1> (W2)"}[dom]
+    achieved = stages[dom]["GB_s"]
+    gemm_tflops = (flops_gate_up + flops_down) / ((stage_ms["ffn_gate_up"] + stage_ms["ffn_down"]) * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": T, "d": d, "E": E, "k": k, "inter": I,
+                   "shared_experts": 1 if has_shared else 0, "routing": wl.routing,
+                   "seed": wl.seed, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": dom_kernel,
+                     "alg_bytes_per_launch": stages[dom]["alg_bytes"],
+                     "launch_ms": stage_ms[dom]},
+        "mfma": {"gemm_TFLOP_s": gemm_tflops, "peak_TFLOP_s": BF16_MFMA_PEAK_TFLOPS,
+                 "frac": gemm_tflops / BF16_MFMA_PEAK_TFLOPS,
+                 "flops_per_step": flops_gate_up + flops_down},
+        "stages": stages,
+        "experts_touched": touched,
+        "input_draw_s": t_draw,
+    }
+
+    if args.cpu_sample > 0:
+        result["cpu_baseline"] = cpu_baseline(inp, wl, ids, args.cpu_sample)
+    print(json.dumps(result))
+
+
+class _ExpertCache:
+    """experts[e] -> host fp32 arrays; filled before the oracle is timed."""
+
+    def __init__(self, inp):
+        self.inp = inp
+        self.cache = {}
+
+    def fetch(self, e):
+        if e not in self.cache:
+            self.cache[e] = tuple(self.inp[n][e].float().cpu().numpy() for n in ("w1", "w3", "w2"))
+        return self.cache[e]
+
+    def __getitem__(self, e):
+        return self.fetch(e)
+
+
+def cpu_baseline(inp, wl, ids, n_tok):
+    """The CPU oracle (as it is) on the first n_tok tokens of the same batch."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+
+    rows = np.arange(min(n_tok, wl.T))
+    x = inp["x"][rows].float().cpu().numpy()
+    wg = inp["w_gate"].cpu().numpy()
+    bias = None if inp["bias"] is None else inp["bias"].cpu().numpy()
+    experts = _ExpertCache(inp)
+    for e in np.unique(ids[rows].cpu().numpy()):
+        experts.fetch(int(e))                       # host copies: not part of the timed work
+    sh = inp["shared"]
+    shared = None if sh is None else tuple(sh[n].float().cpu().numpy() for n in ("w1", "w3", "w2"))
+    kw = {}
+    if wl.routing == "replay":
+        kw = {"ids_in": inp["ids_in"][rows].cpu().numpy(), "weights_in": inp["weights_in"][rows].cpu().numpy()}
+    t0 = time.perf_counter()
+    oracle.layer(x, wg, bias, experts, shared, wl.k, **kw)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {len(rows)} tokens of the {wl.name} batch (exact fsum gate logits over "
+                      f"{wl.E} experts, fp64 SwiGLU for each chosen expert), {dt:.1f} s",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,203 @@
+/*
+ * libmoe -- the forward pass of one Mixture-of-Experts (MoE) layer on AMD MI355X (gfx950).
+ *
+ * Each token's hidden state is gated to its top-k experts (or routed by replayed
+ * expert IDs), the (token, slot) pairs are counting-sorted into contiguous
+ * per-expert segments, every segment runs through its expert's SwiGLU FFN as one
+ * grouped GEMM, and the k expert outputs of each token are combined by a
+ * fixed-order weighted sum.  Every reduction in the library has one fixed order and
+ * no floating-point atomics, so results are bitwise reproducible and do not depend
+ * on which other tokens share the batch or on the order of the tokens.
+ *
+ * Sources of the operations (page title, then section):
+ *   - gate picks 8 of 384 experts per token and layer; a tiny hidden-state
+ *     difference can flip the choice: Training Data podcast page "How Cursor Trained
+ *     Composer on Fireworks" (Chinese rewrite), section on floating point and MoE;
+ *     same facts on the page "Cursor 訓練 Composer 2 的五大工程挑戰", section
+ *     "浮點數的陷阱".  Both pages also describe fixed-order (batch-invariant)
+ *     kernels as the cure for train/inference mismatch.
+ *   - router replay (IDs from inference override the router; gate scores are still
+ *     computed): Composer 2 Technical Report, section 6.2, paragraph on inference
+ *     and weight sync.
+ *   - grouped-GEMM MoE flow: Composer 2 Technical Report, section 6.1 "Kernels",
+ *     Figure 10; token dispatch/combine with MXFP8 tokens before dispatch and a BF16
+ *     combine: section 6.1 "Parallelism".
+ *   - MXFP8 = E4M3 elements with one E8M0 scale per 32-element block: section 6.1
+ *     "Kernels" (backward-pass format), OCP Microscaling Formats v1.0.
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE pointers to row-major arrays owned by the
+ *     caller; the library never allocates, frees or synchronises, except in
+ *     moe_check.  Every call enqueues its kernels asynchronously on `stream`
+ *     (a hipStream_t; NULL = the default stream) and returns.
+ *   - Host-side argument validation happens before any launch; on any status other
+ *     than MOE_OK nothing was enqueued by that call (MOE_ERR_HIP: a launch failed).
+ *   - Device-detected errors (bad replayed IDs, non-finite logits) are OR-ed into a
+ *     flag in the workspace header and reported by moe_check.  Results of a call
+ *     are defined only if moe_check reports MOE_OK afterwards.
+ *   - Calls that share one workspace must be ordered on one stream: calls that
+ *     overlap on the same workspace race.
+ *   - dtype (moe_dtype) names the storage of activations and expert weights:
+ *       MOE_F32   : fp32 x, fp32 weights, fp32 intermediate, fp32 outputs.
+ *       MOE_BF16  : bf16 x, bf16 weights, fp32 accumulation, bf16 intermediate
+ *                   h = silu(x W1) * (x W3) and bf16 expert outputs and y.
+ *       MOE_MXFP8 : OCP MXFP8 x and weights (uint8 E4M3 codes plus one uint8 E8M0
+ *                   scale per 32 consecutive elements of the contiguous dimension),
+ *                   fp32 accumulation, bf16 expert outputs and y.
+ *   - Expert weight layout (per expert, output-major, reduction dimension
+ *     contiguous): w1, w3 [I][d] and w2 [d][I]; i.e. the mathematical W1 [d x I]
+ *     is stored transposed.  A bank of n experts is n such matrices back to back.
+ *   - The gate weight is fp32 [d][E] (expert index contiguous), the optional
+ *     per-expert logit bias fp32 [E].
+ */
+#ifndef LIBMOE_MOE_H
+#define LIBMOE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned pointer, bad dtype */
+  MOE_ERR_UNSUPPORTED = 2, /* valid request this build does not implement (shape/dtype) */
+  MOE_ERR_WORKSPACE = 3,   /* ws_bytes is smaller than moe_workspace_size() requires */
+  MOE_ERR_BAD_IDS = 4,     /* (moe_check) an expert id was out of range or repeated in a row */
+  MOE_ERR_NONFINITE = 5,   /* (moe_check) a gate logit was NaN or infinite */
+  MOE_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2 } moe_dtype;
+
+/* One bank of SwiGLU experts (n experts stored back to back; see layout above).
+ * The *_scale pointers are the E8M0 scales for MOE_MXFP8 ([n][I][d/32] for w1/w3,
+ * [n][d][I/32] for w2) and must be NULL for the other dtypes. */
+typedef struct {
+  const void* w1;
+  const void* w3;
+  const void* w2;
+  const uint8_t* w1_scale;
+  const uint8_t* w3_scale;
+  const uint8_t* w2_scale;
+} moe_expert_bank;
+
+/* Size in bytes of the workspace that every call below accepts for a layer with
+ * T tokens, hidden size d, E routed experts, top-k, expert intermediate size
+ * `inter` and storage dtype.  One workspace serves every call of the layer.
+ * Returns MOE_ERR_INVALID_ARG for out-of-range sizes (T < 0, d < 1, E outside
+ * [1, 1024], k outside [1, min(E, 32)], inter < 1) or a null `bytes`. */
+moe_status moe_workspace_size(int T, int d, int E, int k, int inter, int dtype, size_t* bytes);
+
+/* Clears the workspace header (the device error flag).  Call once after
+ * allocating a workspace, before its first use. */
+moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Learned routing: gate GEMM, softmax over the E experts, top-k, renormalise.
+ *   x       [T][d] activations in `dtype` (x_scale [T][d/32] E8M0 for MOE_MXFP8,
+ *           else NULL; the gate reads the exact dequantised values).
+ *   w_gate  fp32 [d][E]; bias fp32 [E] or NULL (added to the logits used for both
+ *           the selection and the weights).
+ *   ids     out int32 [T][k]: the k experts with the largest logits, ordered by
+ *           (logit descending, expert index ascending).  The selection equals the
+ *           one made on the exactly rounded logits: an fp64 GEMM with a rigorous
+ *           per-token error bound decides every token it can, and tokens whose
+ *           top-(k+1) ordering the bound cannot certify are recomputed with exact
+ *           (error-free) summation on the device.
+ *   weights out fp32 [T][k]: softmax probabilities of the chosen experts
+ *           renormalised to sum to one (computed in fp64 from the fp64 logits,
+ *           rounded once), in the same column order as ids.
+ * Sets MOE_ERR_NONFINITE in the device flag if any logit of a token is not finite.
+ * T == 0 is a valid no-op. */
+moe_status moe_route(const void* x, const uint8_t* x_scale, int dtype, int T, int d,
+                     const float* w_gate, const float* bias, int E, int k,
+                     int32_t* ids, float* weights,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Router replay: the caller's expert IDs override the router's choice.  The gate
+ * logits are still computed (as in moe_route).
+ *   ids_in      int32 [T][k]: replayed expert IDs; each must lie in [0, E) and be
+ *               distinct within its row, else the device flag gets MOE_ERR_BAD_IDS.
+ *               Column order is the combine's rank order.
+ *   weights_in  fp32 [T][k] used verbatim, or NULL: then the weights are the gate's
+ *               softmax probabilities at ids_in renormalised to sum to one, with
+ *               exactly the arithmetic moe_route uses, so replaying moe_route's own
+ *               ids reproduces its weights bit for bit.
+ *   weights_out fp32 [T][k]. */
+moe_status moe_route_replay(const void* x, const uint8_t* x_scale, int dtype, int T, int d,
+                            const float* w_gate, const float* bias, int E, int k,
+                            const int32_t* ids_in, const float* weights_in, float* weights_out,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Counting sort of the T*k (token, slot) pairs by (expert ascending, token
+ * ascending), the grouped GEMM's input order.  Positions come from deterministic
+ * histograms and prefix sums, never from atomic position counters.
+ *   ids     int32 [T][k] (from moe_route or replayed).  An id outside [0, E) sets
+ *           MOE_ERR_BAD_IDS and is treated as expert 0 so every output stays a
+ *           valid permutation.
+ *   offsets out int32 [E+1]: segment e is sorted rows offsets[e] .. offsets[e+1]-1.
+ *   perm    out int32 [T*k]: perm[j] = t*k + r of sorted row j.
+ *   row_of  out int32 [T*k]: row_of[t*k + r] = j (inverse of perm). */
+moe_status moe_dispatch(const int32_t* ids, int T, int E, int k,
+                        int32_t* offsets, int32_t* perm, int32_t* row_of,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Grouped SwiGLU expert FFN over the dispatched segments (one grouped GEMM for
+ * W1 and W3 with the SwiGLU epilogue, one for W2).
+ *   x        [T][d] activations in `dtype` (x_scale as in moe_route); rows are
+ *            gathered through perm inside the GEMM (no separate permuted copy).
+ *   routed   bank of E experts; shared: bank of 1 always-on expert, or NULL.
+ *   offsets, perm from moe_dispatch.
+ *   out      [T*k + (shared ? T : 0)][d]: row j < T*k is expert(j)'s output for the
+ *            pair perm[j]; row T*k + t is the shared expert's output for token t.
+ *            fp32 for MOE_F32, bf16 otherwise.
+ * Per output element the reduction order is fixed (same instruction sequence for
+ * every row of every segment), so a token's output row does not depend on which
+ * other tokens share its expert.
+ * MOE_ERR_UNSUPPORTED: MOE_BF16 needs d % 128 == 0 and inter % 64 == 0;
+ * MOE_MXFP8 is not implemented yet. */
+moe_status moe_expert_ffn(const void* x, const uint8_t* x_scale, int dtype, int T, int d,
+                          int E, int k, int inter,
+                          const moe_expert_bank* routed, const moe_expert_bank* shared,
+                          const int32_t* offsets, const int32_t* perm, void* out,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* The two halves of moe_expert_ffn, for callers that schedule or time them apart
+ * (same kernels, same results).  moe_expert_ffn_gate_up builds the segment table and
+ * runs the W1/W3 grouped GEMM with the SwiGLU epilogue, leaving h in the workspace;
+ * moe_expert_ffn_down runs the W2 grouped GEMM on that h and table and writes `out`.
+ * The down call must follow a gate_up call with the same shape arguments and banks
+ * on the same workspace and stream, with no other call on that workspace between. */
+moe_status moe_expert_ffn_gate_up(const void* x, const uint8_t* x_scale, int dtype, int T, int d,
+                                  int E, int k, int inter,
+                                  const moe_expert_bank* routed, const moe_expert_bank* shared,
+                                  const int32_t* offsets, const int32_t* perm,
+                                  void* ws, size_t ws_bytes, void* stream);
+moe_status moe_expert_ffn_down(int dtype, int T, int d, int E, int k, int inter,
+                               const moe_expert_bank* routed, const moe_expert_bank* shared,
+                               void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Fixed-order combine: y[t] = round( (...((w[t,0]*O0 + w[t,1]*O1) + ...) + w[t,k-1]*O_{k-1})
+ * + S[t] ) with O_r = out[row_of[t*k + r]] and S[t] = out[T*k + t] when has_shared;
+ * fp32 fused multiply-adds in rank order r = 0..k-1, shared output last, one final
+ * rounding to the output dtype.  No atomics.
+ *   out      expert outputs from moe_expert_ffn (fp32 for MOE_F32, else bf16).
+ *   weights  fp32 [T][k]; y out [T][d] (fp32 for MOE_F32, else bf16).
+ * Requires d % 8 == 0. */
+moe_status moe_combine(const void* out, int dtype, const int32_t* row_of, const float* weights,
+                       int T, int d, int k, int has_shared, void* y, void* stream);
+
+/* Synchronises `stream`, reads and clears the workspace's device error flag and
+ * returns MOE_ERR_BAD_IDS, MOE_ERR_NONFINITE or MOE_OK. */
+moe_status moe_check(void* ws, size_t ws_bytes, void* stream);
+
+/* Static string naming a status code. */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMOE_MOE_H */

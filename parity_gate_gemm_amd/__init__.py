@@ -1,0 +1,268 @@
+"""Python binding of libmoe (the C ABI in include/moe.h) over torch tensors.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+``libmoe.so``.  Tensors must already live on the GPU; the binding passes their
+device pointers and the current HIP stream.  There is no fallback: if the library
+is not built, importing the call table raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "MOE_F32", "MOE_BF16", "MOE_MXFP8", "MoeError", "lib", "Workspace",
+    "moe_workspace_size", "moe_workspace_init", "moe_route", "moe_route_replay",
+    "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_gate_up", "moe_expert_ffn_down", "moe_combine", "moe_check", "moe_status_string",
+    "layer_forward",
+]
+
+MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {moe_status_string(status)}")
+
+
+class _Bank(ctypes.Structure):
+    _fields_ = [("w1", ctypes.c_void_p), ("w3", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("w1_scale", ctypes.c_void_p), ("w3_scale", ctypes.c_void_p),
+                ("w2_scale", ctypes.c_void_p)]
+
+
+def lib():
+    """The loaded libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libmoe.so not found at {LIB_PATH}; build it with "
+                              "`python -m parity_gate_gemm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, SZ, PSZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)
+        sig = {
+            "moe_workspace_size": [I, I, I, I, I, I, PSZ],
+            "moe_workspace_init": [P, SZ, P],
+            "moe_route": [P, P, I, I, I, P, P, I, I, P, P, P, SZ, P],
+            "moe_route_replay": [P, P, I, I, I, P, P, I, I, P, P, P, P, SZ, P],
+            "moe_dispatch": [P, I, I, I, P, P, P, P, SZ, P],
+            "moe_expert_ffn": [P, P, I, I, I, I, I, I, ctypes.POINTER(_Bank), ctypes.POINTER(_Bank),
+                               P, P, P, P, SZ, P],
+            "moe_expert_ffn_gate_up": [P, P, I, I, I, I, I, I, ctypes.POINTER(_Bank),
+                                       ctypes.POINTER(_Bank), P, P, P, SZ, P],
+            "moe_expert_ffn_down": [I, I, I, I, I, I, ctypes.POINTER(_Bank), ctypes.POINTER(_Bank),
+                                    P, P, SZ, P],
+            "moe_combine": [P, I, P, P, I, I, I, I, P, P],
+            "moe_check": [P, SZ, P],
+            "moe_status_string": [I],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_char_p if name == "moe_status_string" else ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def moe_status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def _ok(status: int, where: str):
+    if status != 0:
+        raise MoeError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_of(x: torch.Tensor) -> int:
+    if x.dtype == torch.float32:
+        return MOE_F32
+    if x.dtype == torch.bfloat16:
+        return MOE_BF16
+    if x.dtype == torch.uint8:
+        return MOE_MXFP8
+    raise TypeError(f"unsupported activation dtype {x.dtype}")
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("libmoe takes device tensors only")
+            if not t.is_contiguous():
+                raise ValueError("libmoe takes contiguous (row-major) tensors only")
+
+
+def moe_workspace_size(T: int, d: int, E: int, k: int, inter: int, dtype: int) -> int:
+    n = ctypes.c_size_t(0)
+    _ok(lib().moe_workspace_size(T, d, E, k, inter, dtype, ctypes.byref(n)), "moe_workspace_size")
+    return n.value
+
+
+def moe_workspace_init(ws: torch.Tensor):
+    _ok(lib().moe_workspace_init(_ptr(ws), ws.numel(), _stream(ws.device)), "moe_workspace_init")
+
+
+class Workspace:
+    """A device workspace sized for one layer shape, with its header initialised."""
+
+    def __init__(self, T, d, E, k, inter, dtype, device="cuda"):
+        self.nbytes = moe_workspace_size(T, d, E, k, inter, dtype)
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        moe_workspace_init(self.buf)
+
+    @property
+    def ptr(self):
+        return _ptr(self.buf)
+
+
+def moe_route(x, w_gate, bias, k, ws: Workspace, x_scale=None, ids=None, weights=None):
+    _check_dev(x, w_gate, bias, x_scale)
+    T, d = x.shape
+    E = w_gate.shape[1]
+    ids = torch.empty(T, k, dtype=torch.int32, device=x.device) if ids is None else ids
+    weights = torch.empty(T, k, dtype=torch.float32, device=x.device) if weights is None else weights
+    _ok(lib().moe_route(_ptr(x), _ptr(x_scale), _dtype_of(x), T, d, _ptr(w_gate), _ptr(bias), E, k,
+                        _ptr(ids), _ptr(weights), ws.ptr, ws.nbytes, _stream(x.device)), "moe_route")
+    return ids, weights
+
+
+def moe_route_replay(x, w_gate, bias, ids_in, ws: Workspace, weights_in=None, x_scale=None,
+                     weights_out=None):
+    _check_dev(x, w_gate, bias, x_scale, ids_in, weights_in)
+    T, d = x.shape
+    E = w_gate.shape[1]
+    k = ids_in.shape[1]
+    wo = torch.empty(T, k, dtype=torch.float32, device=x.device) if weights_out is None else weights_out
+    _ok(lib().moe_route_replay(_ptr(x), _ptr(x_scale), _dtype_of(x), T, d, _ptr(w_gate), _ptr(bias),
+                               E, k, _ptr(ids_in), _ptr(weights_in), _ptr(wo), ws.ptr, ws.nbytes,
+                               _stream(x.device)), "moe_route_replay")
+    return wo
+
+
+def moe_dispatch(ids, E, ws: Workspace, offsets=None, perm=None, row_of=None):
+    _check_dev(ids)
+    T, k = ids.shape
+    dev = ids.device
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev) if perm is None else perm
+    row_of = torch.empty(T * k, dtype=torch.int32, device=dev) if row_of is None else row_of
+    _ok(lib().moe_dispatch(_ptr(ids), T, E, k, _ptr(offsets), _ptr(perm), _ptr(row_of), ws.ptr,
+                           ws.nbytes, _stream(dev)), "moe_dispatch")
+    return offsets, perm, row_of
+
+
+def _bank(b):
+    if b is None:
+        return None
+    _check_dev(b["w1"], b["w3"], b["w2"], b.get("w1_scale"), b.get("w3_scale"), b.get("w2_scale"))
+    return _Bank(b["w1"].data_ptr(), b["w3"].data_ptr(), b["w2"].data_ptr(),
+                 *(b[n].data_ptr() if b.get(n) is not None else None
+                   for n in ("w1_scale", "w3_scale", "w2_scale")))
+
+
+def moe_expert_ffn(x, routed: dict, shared, offsets, perm, k, ws: Workspace, x_scale=None, out=None):
+    """routed/shared: dicts with w1, w3, w2 (and *_scale for MXFP8); shared may be None."""
+    _check_dev(x, x_scale, offsets, perm)
+    T, d = x.shape
+    E = routed["w1"].shape[0]
+    inter = routed["w1"].shape[1]
+    dt = _dtype_of(x)
+    rows = T * k + (T if shared is not None else 0)
+    if out is None:
+        out = torch.empty(rows, d, dtype=torch.float32 if dt == MOE_F32 else torch.bfloat16,
+                          device=x.device)
+    rb, sb = _bank(routed), _bank(shared)
+    _ok(lib().moe_expert_ffn(_ptr(x), _ptr(x_scale), dt, T, d, E, k, inter, ctypes.byref(rb),
+                             ctypes.byref(sb) if sb is not None else None, _ptr(offsets), _ptr(perm),
+                             _ptr(out), ws.ptr, ws.nbytes, _stream(x.device)), "moe_expert_ffn")
+    return out
+
+
+def moe_expert_ffn_gate_up(x, routed: dict, shared, offsets, perm, k, ws: Workspace, x_scale=None):
+    """GEMM1 half of moe_expert_ffn (h stays in the workspace)."""
+    _check_dev(x, x_scale, offsets, perm)
+    T, d = x.shape
+    E, inter = routed["w1"].shape[0], routed["w1"].shape[1]
+    rb, sb = _bank(routed), _bank(shared)
+    _ok(lib().moe_expert_ffn_gate_up(_ptr(x), _ptr(x_scale), _dtype_of(x), T, d, E, k, inter,
+                                     ctypes.byref(rb), ctypes.byref(sb) if sb is not None else None,
+                                     _ptr(offsets), _ptr(perm), ws.ptr, ws.nbytes, _stream(x.device)),
+        "moe_expert_ffn_gate_up")
+
+
+def moe_expert_ffn_down(dtype, T, d, routed: dict, shared, k, ws: Workspace, out=None):
+    """GEMM2 half of moe_expert_ffn, after moe_expert_ffn_gate_up on the same workspace."""
+    E, inter = routed["w1"].shape[0], routed["w1"].shape[1]
+    rows = T * k + (T if shared is not None else 0)
+    dev = routed["w1"].device
+    if out is None:
+        out = torch.empty(rows, d, dtype=torch.float32 if dtype == MOE_F32 else torch.bfloat16, device=dev)
+    _check_dev(out)
+    rb, sb = _bank(routed), _bank(shared)
+    _ok(lib().moe_expert_ffn_down(dtype, T, d, E, k, inter, ctypes.byref(rb),
+                                  ctypes.byref(sb) if sb is not None else None, _ptr(out), ws.ptr,
+                                  ws.nbytes, _stream(dev)), "moe_expert_ffn_down")
+    return out
+
+
+def moe_combine(out, row_of, weights, T, has_shared, dtype, y=None):
+    _check_dev(out, row_of, weights)
+    d = out.shape[1]
+    k = weights.shape[1] if weights.dim() == 2 else 1
+    if y is None:
+        y = torch.empty(T, d, dtype=torch.float32 if dtype == MOE_F32 else torch.bfloat16,
+                        device=out.device)
+    _ok(lib().moe_combine(_ptr(out), dtype, _ptr(row_of), _ptr(weights), T, d, k,
+                          1 if has_shared else 0, _ptr(y), _stream(out.device)), "moe_combine")
+    return y
+
+
+def moe_check(ws: Workspace) -> int:
+    """Synchronises, reads and clears the device error flag; returns the status code."""
+    return lib().moe_check(ws.ptr, ws.nbytes, _stream(ws.buf.device))
+
+
+def layer_forward(inp: dict, k: int, ws: Workspace | None = None, replay: bool = False,
+                  check: bool = True):
+    """One MoE layer forward through the five C calls.
+
+    ``inp`` holds device tensors: x, x_scale, w_gate, bias, w1, w3, w2 (+ *_scale),
+    shared (dict or None) and, for replay, ids_in / weights_in.
+    """
+    x = inp["x"]
+    T, d = x.shape
+    E = inp["w_gate"].shape[1]
+    inter = inp["w1"].shape[1]
+    dt = _dtype_of(x)
+    if ws is None:
+        ws = Workspace(T, d, E, k, inter, dt, device=x.device)
+    if replay:
+        ids = inp["ids_in"]
+        weights = moe_route_replay(x, inp["w_gate"], inp.get("bias"), ids, ws,
+                                   weights_in=inp.get("weights_in"), x_scale=inp.get("x_scale"))
+    else:
+        ids, weights = moe_route(x, inp["w_gate"], inp.get("bias"), k, ws, x_scale=inp.get("x_scale"))
+    offsets, perm, row_of = moe_dispatch(ids, E, ws)
+    routed = {n: inp.get(n) for n in ("w1", "w3", "w2", "w1_scale", "w3_scale", "w2_scale")}
+    out = moe_expert_ffn(x, routed, inp.get("shared"), offsets, perm, k, ws, x_scale=inp.get("x_scale"))
+    y = moe_combine(out, row_of, weights, T, inp.get("shared") is not None, dt)
+    if check:
+        st = moe_check(ws)
+        if st != 0:
+            raise MoeError(st, "layer_forward")
+    return {"y": y, "ids": ids, "weights": weights, "offsets": offsets, "perm": perm,
+            "row_of": row_of, "out": out}

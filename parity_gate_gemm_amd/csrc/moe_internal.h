@@ -1,0 +1,136 @@
+// Internal helpers shared by the libmoe translation units: workspace layout,
+// device error flags, element decoding, host-side argument checks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Limits and tile constants
+// ---------------------------------------------------------------------------
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int kDispatchTokens = 64;   // tokens per dispatch block
+constexpr int kGemmBM = 128;          // rows per grouped-GEMM tile
+
+// Device error flag bits (OR-ed into the workspace header).
+constexpr int kFlagBadId = 1;
+constexpr int kFlagDupId = 2;
+constexpr int kFlagNonFinite = 4;
+constexpr int kFlagCorrupt = 8;       // internal consistency (bad offsets/perm fed to the FFN)
+
+constexpr size_t kHeaderBytes = 256;
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---------------------------------------------------------------------------
+// Workspace layout.  Byte 0..255: header (int flag at offset 0).  The rest is
+// scratch that each call uses for its own duration only.
+// ---------------------------------------------------------------------------
+struct RouteWs {
+  size_t logits, tok_flag, xnorm, wnorm, bytes;
+};
+inline RouteWs route_ws(int T, int E) {
+  RouteWs w;
+  size_t o = kHeaderBytes;
+  w.logits = o;   o = align_up(o + (size_t)T * E * sizeof(double), 256);
+  w.tok_flag = o; o = align_up(o + (size_t)T * sizeof(int), 256);
+  w.xnorm = o;    o = align_up(o + (size_t)T * sizeof(double), 256);
+  w.wnorm = o;    o = align_up(o + (size_t)E * sizeof(double), 256);
+  w.bytes = o;
+  return w;
+}
+
+struct DispatchWs {
+  size_t hist, total, bytes;
+  int nblocks;
+};
+inline DispatchWs dispatch_ws(int T, int E) {
+  DispatchWs w;
+  w.nblocks = (T + kDispatchTokens - 1) / kDispatchTokens;
+  size_t o = kHeaderBytes;
+  w.hist = o;  o = align_up(o + (size_t)w.nblocks * E * sizeof(int), 256);
+  w.total = o; o = align_up(o + (size_t)E * sizeof(int), 256);
+  w.bytes = o;
+  return w;
+}
+
+inline size_t elem_bytes_h(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
+
+struct FfnWs {
+  size_t h, seg, bytes;
+  long long rows;
+};
+// seg table: mstart[S+1] (int), rowstart[S] (int), rowcount[S] (int), S = E + 1
+inline FfnWs ffn_ws(int T, int E, int k, int inter, int dtype) {
+  FfnWs w;
+  w.rows = (long long)T * k + T;
+  size_t o = kHeaderBytes;
+  w.h = o;   o = align_up(o + (size_t)w.rows * inter * elem_bytes_h(dtype), 256);
+  w.seg = o; o = align_up(o + (size_t)(3 * (E + 2)) * sizeof(int), 256);
+  w.bytes = o;
+  return w;
+}
+
+inline size_t workspace_bytes(int T, int d, int E, int k, int inter, int dtype) {
+  (void)d;
+  size_t a = route_ws(T, E).bytes, b = dispatch_ws(T, E).bytes, c = ffn_ws(T, E, k, inter, dtype).bytes;
+  size_t m = a > b ? a : b;
+  return m > c ? m : c;
+}
+
+inline bool valid_dtype(int dt) { return dt == MOE_F32 || dt == MOE_BF16 || dt == MOE_MXFP8; }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+inline moe_status launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void raise_flag(int* ws_flag, int bits) { atomicOr(ws_flag, bits); }
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// OCP FP8 E4M3 code -> exact value (as double; every E4M3 value is exact in fp32 too).
+__device__ __forceinline__ double e4m3_to_f64(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 0xF, m = c & 7;
+  double v;
+  if (e == 0xF && m == 7) v = __builtin_nan("");
+  else if (e == 0) v = ldexp((double)m, -9);
+  else v = ldexp((double)(8 + m), e - 10);
+  return s ? -v : v;
+}
+
+// E8M0 scale code -> 2^(code-127) (255 is NaN).
+__device__ __forceinline__ double e8m0_to_f64(uint8_t c) {
+  return c == 255 ? __builtin_nan("") : ldexp(1.0, (int)c - 127);
+}
+
+// Exact value of element i of activation row `row` (length d) in `dtype`.
+__device__ __forceinline__ double load_act_f64(const void* x, const uint8_t* xs, int dtype,
+                                               size_t row, int d, int i) {
+  size_t idx = row * (size_t)d + i;
+  if (dtype == MOE_F32) return (double)((const float*)x)[idx];
+  if (dtype == MOE_BF16) return (double)bf16_to_f32(((const uint16_t*)x)[idx]);
+  return e4m3_to_f64(((const uint8_t*)x)[idx]) * e8m0_to_f64(xs[row * (size_t)(d / 32) + i / 32]);
+}
+
+}  // namespace moe

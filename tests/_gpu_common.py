@@ -1,0 +1,102 @@
+"""Shared helpers for the GPU parity tests (not collected by pytest)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import parity_gate_gemm_amd as pg
+
+TOL = {"f32": 2e-2, "bf16": 2e-2, "mxfp8": 6e-2}   # normwise max-abs-rel bar
+WEIGHT_TOL = 2e-6                                   # fp32 weights vs fp64 oracle
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def host(t):
+    """Stored values of a device/host tensor as float64 numpy (exact)."""
+    if t is None:
+        return None
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.cpu().numpy().astype(np.float64) if t.dtype != torch.int32 else t.cpu().numpy()
+
+
+class LazyExperts:
+    """experts[e] -> (w1, w3, w2) float64 numpy, fetched from device tensors on demand."""
+
+    def __init__(self, inp):
+        self.inp = inp
+
+    def __getitem__(self, e):
+        return tuple(host(self.inp[n][e]) for n in ("w1", "w3", "w2"))
+
+
+def shared_of(inp):
+    sh = inp.get("shared")
+    if sh is None:
+        return None
+    return (host(sh["w1"]), host(sh["w3"]), host(sh["w2"]))
+
+
+def to_device(inp, device="cuda"):
+    out = {}
+    for kk, v in inp.items():
+        if isinstance(v, torch.Tensor):
+            out[kk] = v.to(device)
+        elif isinstance(v, dict):
+            out[kk] = {a: (b.to(device) if isinstance(b, torch.Tensor) else b) for a, b in v.items()}
+        else:
+            out[kk] = v
+    return out
+
+
+def oracle_for_rows(inp, rows, k, replay=False):
+    """Oracle layer on a subset of token rows (routing and FFN are row-local)."""
+    x = host(inp["x"])[rows]
+    kw = {}
+    if replay:
+        kw["ids_in"] = inp["ids_in"].cpu().numpy()[rows]
+        if inp.get("weights_in") is not None:
+            kw["weights_in"] = host(inp["weights_in"])[rows]
+    return oracle.layer(x, host(inp["w_gate"]), host(inp.get("bias")), LazyExperts(inp),
+                        shared_of(inp), k, **kw)
+
+
+def compare_rows(res_gpu, ref, rows, dtype, replay=False):
+    """ids bit-exact, weights within WEIGHT_TOL, y normwise within the dtype's bar."""
+    ids = res_gpu["ids"].cpu().numpy()[rows]
+    assert np.array_equal(ids, ref["ids"]), (ids, ref["ids"])
+    w = res_gpu["weights"].cpu().numpy()[rows].astype(np.float64)
+    assert np.max(np.abs(w - ref["weights"])) <= WEIGHT_TOL, np.max(np.abs(w - ref["weights"]))
+    y = host(res_gpu["y"])[rows]
+    err = oracle.normwise_rel_err(y, ref["y"])
+    assert err <= TOL[dtype], err
+    return err
+
+
+def check_dispatch_properties(ids_gpu, offsets, perm, row_of, E):
+    """Properties that pin the counting sort at any size (computed on the host)."""
+    ids = ids_gpu.cpu().numpy().astype(np.int64)
+    off = offsets.cpu().numpy().astype(np.int64)
+    pm = perm.cpu().numpy().astype(np.int64)
+    ro = row_of.cpu().numpy().astype(np.int64)
+    T, k = ids.shape
+    assert off[0] == 0 and off[E] == T * k
+    assert np.array_equal(np.diff(off), np.bincount(ids.ravel(), minlength=E))
+    assert np.array_equal(np.sort(pm), np.arange(T * k))
+    assert np.array_equal(pm[ro], np.arange(T * k))
+    seg_e = np.repeat(np.arange(E), np.diff(off))
+    assert np.array_equal(ids.ravel()[pm], seg_e)
+    key = seg_e * (T * k) + pm             # (expert, token, slot) ascending
+    assert np.all(np.diff(key) > 0)
+
+
+def run_layer(inp, k, replay=False, ws=None):
+    return pg.layer_forward(inp, k, ws=ws, replay=replay)

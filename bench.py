@@ -33,9 +33,23 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="bf16_t4096",
                     help="bf16_t4096 (default), replay_zipf_t4096, bf16_t128_stream, tiny_fp32_t32")
-    ap.add_argument("--cpu-sample", type=int, default=6,
+    ap.add_argument("--cpu-sample", type=int, default=32,
                     help="tokens of the same batch the CPU oracle is timed on (0: skip)")
+    ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
+                    help="only run a plain device-to-device copy of GIB GiB (three times), the "
+                         "reference for scaling the FETCH_SIZE/WRITE_SIZE counters, and exit")
     return ap.parse_args()
+
+
+def calibrate_copy(gib: float):
+    import torch
+    n = int(gib * (1 << 30))
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copied {n} bytes x3 (one copy kernel per iteration)")
 
 
 def main():
@@ -45,6 +59,10 @@ def main():
         print("bench.py measures the single-GPU hot path only; --gpus must be 1 "
               "(the layer is not sharded across GPUs in this library).", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy > 0:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import numpy as np
     import torch
@@ -187,13 +205,30 @@ def main():
         "input_draw_s": t_draw,
     }
 
+    result["roofline"]["traffic"] = measured_traffic(wl.name) if dom == "ffn_gate_up" else None
     if args.cpu_sample > 0:
         result["cpu_baseline"] = cpu_baseline(inp, wl, ids, args.cpu_sample)
     print(json.dumps(result))
 
 
+def measured_traffic(workload):
+    """HBM bytes per GEMM1 launch from the committed rocprofv3 FETCH_SIZE + WRITE_SIZE
+    summary (each scaled by the plain-copy calibration), or None when no summary exists
+    for this workload or the kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"gemm1_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, "parity_gate_gemm_amd", "csrc", "ffn.hip"), "rb").read()
+    if hashlib.sha256(src).hexdigest() != rec["ffn_source_sha256"]:
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
+
+
 class _ExpertCache:
-    """experts[e] -> host fp32 arrays; filled before the oracle is timed."""
+    """experts[e] -> host arrays of the stored values.  The device-to-host copies are
+    made before the oracle is timed; the widening to fp32 is part of the timed work."""
 
     def __init__(self, inp):
         self.inp = inp
@@ -201,11 +236,11 @@ class _ExpertCache:
 
     def fetch(self, e):
         if e not in self.cache:
-            self.cache[e] = tuple(self.inp[n][e].float().cpu().numpy() for n in ("w1", "w3", "w2"))
+            self.cache[e] = tuple(self.inp[n][e].cpu() for n in ("w1", "w3", "w2"))
         return self.cache[e]
 
     def __getitem__(self, e):
-        return self.fetch(e)
+        return tuple(t.float().numpy() for t in self.fetch(e))
 
 
 def cpu_baseline(inp, wl, ids, n_tok):

@@ -24,6 +24,16 @@ constexpr int BK = 64;        // reduction step
 constexpr int LDSS = BK + 8;  // LDS row stride in bf16 elements (144 B: conflict-free 16-B reads)
 constexpr int kXcds = 8;      // MI355X: 8 XCDs, workgroups dealt round-robin
 
+// Tuning knobs of the bf16 grouped GEMM (same results for every setting).
+#ifndef MOE_GEMM_DEPTH
+#define MOE_GEMM_DEPTH 1
+#endif
+#ifndef MOE_GEMM_NT_B
+#define MOE_GEMM_NT_B 0
+#endif
+constexpr int kGemmDepth = MOE_GEMM_DEPTH;   // K-steps of loads in flight per thread
+constexpr bool kGemmNtB = MOE_GEMM_NT_B != 0; // nontemporal weight loads
+
 // Segment table: segment s < E is routed expert s (rows offsets[s]..offsets[s+1]-1),
 // segment E is the shared expert (rows T*k .. T*k+T-1).  mstart = exclusive prefix of
 // the per-segment tile-row counts.  Offsets are clamped into [0, T*k] and flagged if
@@ -89,7 +99,7 @@ __device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + expf(-a)
 // MODE 1: GEMM2 (W2, 128 output features per tile).
 // 256 threads = 4 wavefronts in a 2 x 2 arrangement; each wavefront owns a
 // 64-row x 64-B-row quarter of the 128 x 128 tile as 2 x 2 MFMA 32x32x16 blocks.
-template <int MODE>
+template <int MODE, int DEPTH, bool NT_B>
 __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[BM * LDSS];
   __shared__ __attribute__((aligned(16))) uint16_t sB[BNR * LDSS];
@@ -168,28 +178,28 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
-  u32x4_t ra[4], rb[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ra[i] = *(const u32x4_t*)(aptr[i]);
-    rb[i] = *(const u32x4_t*)(bptr[i]);
-  }
-
-  for (int k0 = 0; k0 < g.K; k0 += BK) {
+  // K loop: DEPTH register sets keep DEPTH K-steps of global loads in flight; each
+  // step goes registers -> LDS -> MFMA.  Weight (B) loads may bypass L2 retention
+  // (nontemporal): every weight byte is used by one tile only.
+  u32x4_t ra[DEPTH][4], rb[DEPTH][4];
+  auto gload = [&](u32x4_t(&A)[4], u32x4_t(&B)[4], int kofs) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      *(u32x4_t*)&sA[(lr + 32 * i) * LDSS + lc] = ra[i];
-      *(u32x4_t*)&sB[(lr + 32 * i) * LDSS + lc] = rb[i];
+      A[i] = *(const u32x4_t*)(aptr[i] + kofs);
+      if (NT_B)
+        B[i] = __builtin_nontemporal_load((const u32x4_t*)(bptr[i] + kofs));
+      else
+        B[i] = *(const u32x4_t*)(bptr[i] + kofs);
+    }
+  };
+  auto step = [&](u32x4_t(&A)[4], u32x4_t(&B)[4], int knext) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *(u32x4_t*)&sA[(lr + 32 * i) * LDSS + lc] = A[i];
+      *(u32x4_t*)&sB[(lr + 32 * i) * LDSS + lc] = B[i];
     }
     __syncthreads();
-    const int kn = k0 + BK;
-    if (kn < g.K) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ra[i] = *(const u32x4_t*)(aptr[i] + kn);
-        rb[i] = *(const u32x4_t*)(bptr[i] + kn);
-      }
-    }
+    if (knext < g.K) gload(A, B, knext);
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
       const int kc = kk + (lane >> 5) * 8;
@@ -211,6 +221,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bf[nb], acc[mb][nb], 0, 0, 0);
     }
     __syncthreads();
+  };
+#pragma unroll
+  for (int s2 = 0; s2 < DEPTH; ++s2)
+    if (s2 * BK < g.K) gload(ra[s2], rb[s2], s2 * BK);
+  for (int k0 = 0; k0 < g.K; k0 += DEPTH * BK) {
+#pragma unroll
+    for (int s2 = 0; s2 < DEPTH; ++s2)
+      if (k0 + s2 * BK < g.K) step(ra[s2], rb[s2], k0 + (s2 + DEPTH) * BK);
   }
 
   // ---- epilogue.  Accumulator element v of a lane is C[i][j] with
@@ -380,7 +398,7 @@ static moe_status run_gate_up(const void* x, int dtype, int T, int d, int E, int
     g.flag = p.flag;
     const long long grid = (p.mt_bound * g.NT + kXcds - 1) / kXcds * kXcds;
     if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
-    grouped_gemm_bf16_kernel<0><<<(unsigned)grid, 256, 0, s>>>(g);
+    grouped_gemm_bf16_kernel<0, kGemmDepth, kGemmNtB><<<(unsigned)grid, 256, 0, s>>>(g);
   } else {
     F32Args g{};
     g.a = (const float*)x;
@@ -433,7 +451,7 @@ static moe_status run_down(int dtype, int T, int d, int E, int k, int inter,
     g.flag = p.flag;
     const long long grid = (p.mt_bound * g.NT + kXcds - 1) / kXcds * kXcds;
     if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
-    grouped_gemm_bf16_kernel<1><<<(unsigned)grid, 256, 0, s>>>(g);
+    grouped_gemm_bf16_kernel<1, kGemmDepth, kGemmNtB><<<(unsigned)grid, 256, 0, s>>>(g);
   } else {
     F32Args g{};
     g.a = (const float*)p.h;

@@ -21,79 +21,173 @@
 namespace moe {
 
 constexpr int GT_M = 64;   // tokens per gate tile
-constexpr int GT_E = 64;   // experts per gate tile
-constexpr int GT_K = 16;   // reduction chunk staged in LDS
+constexpr int GT_E = 32;   // experts per gate tile
+constexpr int GT_K = 64;   // reduction step staged in LDS
 
-// logits[t][e] = sum_i x[t][i] * wg[i][e]  (+ bias[e]), fp64, i ascending, one fma per
-// term; the bias is added last.  Rounding error of every output is at most
-// gamma_{d+1} * (sum_i |x_i w_ie| + |b_e|) <= gamma_{d+1} * (||x_t|| ||w_e|| + |b_e|).
-// The WGs of the first expert tile also write ||x_t||, those of the first token tile
-// ||w_e|| (fp64 sums of squares over the same tiles).
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_v __attribute__((ext_vector_type(4)));
+typedef float f32x4_v __attribute__((ext_vector_type(4)));
+
+// Raw registers of one thread's 16 consecutive activations of one token, per dtype.
+template <int DT>
+struct XChunk;
+template <>
+struct XChunk<MOE_BF16> {
+  u32x4_v r[2];
+  __device__ void load(const void* x, const uint8_t*, size_t row, int d, int k) {
+    const u32x4_v* p = (const u32x4_v*)((const uint16_t*)x + row * d + k);
+    r[0] = p[0];
+    r[1] = p[1];
+  }
+  __device__ void zero() { r[0] = r[1] = (u32x4_v){0, 0, 0, 0}; }
+  __device__ double get(int i) const {
+    const uint32_t w = r[i >> 3][(i >> 1) & 3];
+    return (double)bf16_to_f32((uint16_t)((i & 1) ? (w >> 16) : (w & 0xffff)));
+  }
+};
+template <>
+struct XChunk<MOE_F32> {
+  f32x4_v r[4];
+  __device__ void load(const void* x, const uint8_t*, size_t row, int d, int k) {
+    const f32x4_v* p = (const f32x4_v*)((const float*)x + row * d + k);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = p[i];
+  }
+  __device__ void zero() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = (f32x4_v){0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ double get(int i) const { return (double)r[i >> 2][i & 3]; }
+};
+template <>
+struct XChunk<MOE_MXFP8> {
+  u32x4_v r;
+  double scale;
+  __device__ void load(const void* x, const uint8_t* xs, size_t row, int d, int k) {
+    r = *(const u32x4_v*)((const uint8_t*)x + row * d + k);
+    scale = e8m0_to_f64(xs[row * (size_t)(d / 32) + k / 32]);   // 16 codes lie in one 32-block
+  }
+  __device__ void zero() {
+    r = (u32x4_v){0, 0, 0, 0};
+    scale = 0.0;
+  }
+  __device__ double get(int i) const {
+    return e4m3_to_f64((uint8_t)(r[i >> 2] >> (8 * (i & 3)))) * scale;
+  }
+};
+
+// logits[t][e] = sum_i x[t][i] * wg[i][e]  (+ bias[e]) in fp64 on the matrix cores
+// (v_mfma_f64_16x16x4f64), K ascending in steps of 4; the bias is added last.  Every
+// product is exact in fp64 and every addition rounds once, so the rounding error of
+// each output is at most gamma_{d+1} * (sum_i |x_i w_ie| + |b_e|)
+//                    <= gamma_{d+1} * (||x_t|| ||w_e|| + |b_e|).
+// The workgroups of the first expert tile also write ||x_t||, those of the first
+// token tile ||w_e|| (fp64 sums of squares in a fixed order).
+// 256 threads = 4 wavefronts; wavefront w owns tokens 16w..16w+15 of the tile and all
+// 32 experts as two 16x16 MFMA blocks.  Loads of the next K-step are in flight while
+// the current one is multiplied.  Requires d % 16 == 0.
+template <int DT>
 __global__ __launch_bounds__(256) void gate_gemm_f64_kernel(
-    const void* __restrict__ x, const uint8_t* __restrict__ xs, int dtype, int T, int d,
+    const void* __restrict__ x, const uint8_t* __restrict__ xs, int T, int d,
     const float* __restrict__ wg, const float* __restrict__ bias, int E,
     double* __restrict__ logits, double* __restrict__ xnorm, double* __restrict__ wnorm) {
-  __shared__ double sx[GT_K][GT_M + 1];
+  __shared__ double sx[GT_M][GT_K + 1];
   __shared__ double sw[GT_K][GT_E + 1];
-  const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+  __shared__ double wpart[4][GT_E];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.y * GT_M, e0 = blockIdx.x * GT_E;
-  const bool x_owner = (blockIdx.x == 0) && tid < GT_M;
-  const bool w_owner = (blockIdx.y == 0) && tid >= 64 && tid < 64 + GT_E;
-  double acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-  double sq = 0.0;
+  const int xm = tid >> 2, xk = (tid & 3) * 16;   // x loader: token xm, k xk..xk+15
+  const int wk = tid >> 2, we = (tid & 3) * 8;    // w loader: k row wk, experts we..we+7
+  const bool x_row_ok = t0 + xm < T;
+  const bool need_xn = blockIdx.x == 0, need_wn = blockIdx.y == 0;
 
+  f64x4_t acc[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[nb][i] = 0.0;
+  double xsq = 0.0, wsq[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) wsq[j] = 0.0;
+
+  XChunk<DT> xc;
+  float wv[8];
+  auto gload = [&](int k0) {
+    if (x_row_ok && k0 + xk < d) xc.load(x, xs, (size_t)(t0 + xm), d, k0 + xk);
+    else xc.zero();
+    const int kw = k0 + wk;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = e0 + we + j;
+      wv[j] = (kw < d && e < E) ? wg[(size_t)kw * E + e] : 0.0f;
+    }
+  };
+  gload(0);
   for (int k0 = 0; k0 < d; k0 += GT_K) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int l = tid + 256 * i, m = l / GT_K, kk = l % GT_K;
-      const int t = t0 + m, kx = k0 + kk;
-      sx[kk][m] = (t < T && kx < d) ? load_act_f64(x, xs, dtype, (size_t)t, d, kx) : 0.0;
+    for (int i = 0; i < 16; ++i) {
+      const double v = xc.get(i);
+      sx[xm][xk + i] = v;
+      if (need_xn) xsq = fma(v, v, xsq);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int l = tid + 256 * i, kk = l / GT_E, ee = l % GT_E;
-      const int e = e0 + ee, kw = k0 + kk;
-      sw[kk][ee] = (e < E && kw < d) ? (double)wg[(size_t)kw * E + e] : 0.0;
+    for (int j = 0; j < 8; ++j) {
+      const double v = (double)wv[j];
+      sw[wk][we + j] = v;
+      if (need_wn) wsq[j] = fma(v, v, wsq[j]);
     }
     __syncthreads();
-    if (x_owner) {
+    if (k0 + GT_K < d) gload(k0 + GT_K);
+    // A operand: lane holds x[16*wave + lane%16][k + lane/16]; B: w[k + lane/16][16*nb + lane%16].
 #pragma unroll
-      for (int kk = 0; kk < GT_K; ++kk) sq = fma(sx[kk][tid], sx[kk][tid], sq);
-    }
-    if (w_owner) {
+    for (int kk = 0; kk < GT_K; kk += 4) {
+      const double a = sx[16 * wave + (lane & 15)][kk + (lane >> 4)];
 #pragma unroll
-      for (int kk = 0; kk < GT_K; ++kk) sq = fma(sw[kk][tid - 64], sw[kk][tid - 64], sq);
-    }
-#pragma unroll
-    for (int kk = 0; kk < GT_K; ++kk) {
-      double a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = sx[kk][ty + 16 * i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = sw[kk][tx + 16 * j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+      for (int nb = 0; nb < 2; ++nb) {
+        const double b = sw[kk + (lane >> 4)][16 * nb + (lane & 15)];
+        acc[nb] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[nb], 0, 0, 0);
+      }
     }
     __syncthreads();
   }
-  if (x_owner && t0 + tid < T) xnorm[t0 + tid] = sqrt(sq);
-  if (w_owner && e0 + tid - 64 < E) wnorm[e0 + tid - 64] = sqrt(sq);
+  // Norms: the four x-loader threads of a token hold its partial sums (k strided by
+  // chunk), the 64 w-loader threads of an expert chunk hold per-k-row partials.
+  if (need_xn) {
+    const double s1 = xsq + __shfl_xor(xsq, 1);
+    const double s2 = s1 + __shfl_xor(s1, 2);
+    if ((tid & 3) == 0 && x_row_ok) xnorm[t0 + xm] = sqrt(s2);
+  }
+  if (need_wn) {
+    // Reduce over the 16 k rows of each wavefront (lanes with equal lane%4), then
+    // over the 4 wavefronts, in a fixed order.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + ty + 16 * i;
-    if (t >= T) continue;
+    for (int j = 0; j < 8; ++j) {
+      double v = wsq[j];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tx + 16 * j;
-      if (e >= E) continue;
-      double v = acc[i][j];
-      if (bias) v = v + (double)bias[e];
+      for (int off = 4; off < 64; off <<= 1) v += __shfl_xor(v, off);
+      wsq[j] = v;
+    }
+    if (lane < 4) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) wpart[wave][we + j] = wsq[j];
+    }
+    __syncthreads();
+    if (tid < GT_E && e0 + tid < E)
+      wnorm[e0 + tid] = sqrt(((wpart[0][tid] + wpart[1][tid]) + wpart[2][tid]) + wpart[3][tid]);
+  }
+  // D layout of a 16x16 fp64 block: element i of a lane is row lane/16 + 4*i, column
+  // lane%16 (interleaved, unlike the fp32 16x16 layouts).
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int e = e0 + 16 * nb + (lane & 15);
+    if (e >= E) continue;
+    const double b = bias ? (double)bias[e] : 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 16 * wave + (lane >> 4) + 4 * i;
+      if (t >= T) continue;
+      double v = acc[nb][i];
+      if (bias) v = v + b;
       logits[(size_t)t * E + e] = v;
     }
   }
@@ -354,6 +448,8 @@ static moe_status check_route_args(const void* x, const uint8_t* x_scale, int dt
   if (!x || !w_gate || !ws) return MOE_ERR_INVALID_ARG;
   if (dtype == MOE_MXFP8 && (!x_scale || d % 32 != 0)) return MOE_ERR_INVALID_ARG;
   if (dtype != MOE_MXFP8 && x_scale) return MOE_ERR_INVALID_ARG;
+  if (d % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!aligned(x, 16)) return MOE_ERR_INVALID_ARG;
   if ((long long)T * E > 0x7fffffffLL || (long long)T * k > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
   if (ws_bytes < route_ws(T, E).bytes) return MOE_ERR_WORKSPACE;
   return MOE_OK;
@@ -371,9 +467,15 @@ static moe_status launch_gate(const void* x, const uint8_t* xs, int dtype, int T
                               hipStream_t s) {
   const RouteWs L = route_ws(T, E);
   dim3 grid((E + GT_E - 1) / GT_E, (T + GT_M - 1) / GT_M);
-  gate_gemm_f64_kernel<<<grid, 256, 0, s>>>(x, xs, dtype, T, d, w_gate, bias, E,
-                                            (double*)(w + L.logits), (double*)(w + L.xnorm),
-                                            (double*)(w + L.wnorm));
+  double* lg = (double*)(w + L.logits);
+  double* xn = (double*)(w + L.xnorm);
+  double* wn = (double*)(w + L.wnorm);
+  if (dtype == MOE_BF16)
+    gate_gemm_f64_kernel<MOE_BF16><<<grid, 256, 0, s>>>(x, xs, T, d, w_gate, bias, E, lg, xn, wn);
+  else if (dtype == MOE_F32)
+    gate_gemm_f64_kernel<MOE_F32><<<grid, 256, 0, s>>>(x, xs, T, d, w_gate, bias, E, lg, xn, wn);
+  else
+    gate_gemm_f64_kernel<MOE_MXFP8><<<grid, 256, 0, s>>>(x, xs, T, d, w_gate, bias, E, lg, xn, wn);
   return launch_status();
 }
 

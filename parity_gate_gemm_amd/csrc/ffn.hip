@@ -32,6 +32,10 @@ constexpr int kXcds = 8;      // MI355X: 8 XCDs, workgroups dealt round-robin
 #define MOE_GEMM_NT_B 0
 #endif
 constexpr int kGemmDepth = MOE_GEMM_DEPTH;   // K-steps of loads in flight per thread
+#ifndef MOE_GEMM_GROUP_M
+#define MOE_GEMM_GROUP_M 8
+#endif
+constexpr int kGroupM = MOE_GEMM_GROUP_M;       // row tiles per raster group
 constexpr bool kGemmNtB = MOE_GEMM_NT_B != 0; // nontemporal weight loads
 
 // Segment table: segment s < E is routed expert s (rows offsets[s]..offsets[s+1]-1),
@@ -119,7 +123,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   const int s = lo;
   const int mtiles = g.mstart[s + 1] - g.mstart[s];
   const int local = tile - g.mstart[s] * g.NT;
-  const int nt = local / mtiles, mt = local % mtiles;   // consecutive tiles share a weight slab
+  // Row tiles in groups of kGroupM: within a group, consecutive tiles share a weight
+  // slab (column tile) and the group's activation rows are reused by every column tile.
+  const int grp = local / (kGroupM * g.NT), rem = local % (kGroupM * g.NT);
+  const int gm = min(kGroupM, mtiles - grp * kGroupM);
+  const int nt = rem / gm, mt = grp * kGroupM + rem % gm;
   const int row0 = g.rowstart[s] + mt * BM;
   const int mrows = min(BM, g.rowcount[s] - mt * BM);
   const int n0 = nt * (MODE == 0 ? 64 : 128);
@@ -258,6 +266,280 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
+// MXFP8 path (OCP MX: E4M3 elements, one E8M0 scale per 32 elements along K) on the
+// block-scaled matrix cores: v_mfma_scale_f32_32x32x64_f8f6f4.  Lane l of an operand
+// holds row (or column) l % 32; with h = l / 32, its bytes 0..15 are k = 16h..16h+15 of
+// the instruction's 64-wide k range and bytes 16..31 are k = 32+16h..32+16h+15, so
+// k-block 0 (k < 32) is split over both lane halves, and lane half h supplies the E8M0
+// scale of k-block h.
+// GEMM1 requantises h = silu(x W1) * (x W3) to MXFP8 row by row (one 32-column block per
+// half wavefront) for GEMM2; GEMM2 writes bf16.
+// ---------------------------------------------------------------------------
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+constexpr int MBK = 128;               // reduction step in elements (= bytes)
+constexpr int MLDS = MBK + 16;         // LDS row stride in bytes
+
+struct MxArgs {
+  const uint8_t* a;          // GEMM1: x codes [T][d]; GEMM2: h codes [rows][I]
+  const uint8_t* as;         // matching E8M0 scales [.][K/32]
+  const int32_t* perm;
+  int T, k, E;
+  long long Tk;
+  const uint8_t* b0;         // GEMM1: W1 codes; GEMM2: W2 codes
+  const uint8_t* b1;         // GEMM1: W3 codes
+  const uint8_t* b0s;
+  const uint8_t* b1s;
+  const uint8_t* sb0;        // shared expert
+  const uint8_t* sb1;
+  const uint8_t* sb0s;
+  const uint8_t* sb1s;
+  int K, N, NT;
+  const int* mstart;
+  const int* rowstart;
+  const int* rowcount;
+  int S;
+  void* out;                 // GEMM1: h codes [rows][I]; GEMM2: bf16 [rows][d]
+  uint8_t* out_scale;        // GEMM1: h scales [rows][I/32]
+  int* flag;
+};
+
+// fp32 (already divided by its block scale) -> E4M3 code, round to nearest even,
+// saturating to +-448 (NaN -> 0x7F).
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fabsf(v);
+  if (a != a) return 0x7Fu;
+  if (!(a < 448.0f)) return sign | 0x7Eu;
+  const uint32_t ua = __float_as_uint(a);
+  if (ua < 0x00800000u) return sign;                 // below 2^-126: rounds to zero
+  const int e = (int)(ua >> 23) - 127;
+  const uint32_t full = (ua & 0x7FFFFFu) | 0x800000u;
+  const int shift = e >= -6 ? 20 : 20 + (-6 - e);
+  if (shift > 24) return sign;                       // below 2^-10: rounds to zero
+  uint32_t keep = full >> shift;
+  const uint32_t rem = full & ((1u << shift) - 1u), half = 1u << (shift - 1);
+  keep += (rem > half || (rem == half && (keep & 1u))) ? 1u : 0u;
+  if (e >= -6) {
+    int ef = e + 7;
+    if (keep == 16u) {
+      ++ef;
+      keep = 8u;
+    }
+    return sign | ((uint32_t)ef << 3) | (keep - 8u);
+  }
+  return sign | keep;                                // subnormal grid (keep == 8: 2^-6)
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void grouped_gemm_mx_kernel(MxArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t sA[BM * MLDS];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[BNR * MLDS];
+  __shared__ uint32_t sAs[BM];
+  __shared__ uint32_t sBs[BNR];
+
+  const int total = g.mstart[g.S] * g.NT;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int xcd = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
+  if (q >= per) return;
+  const int tile = xcd * per + q;
+  if (tile >= total) return;
+  int lo = 0, hi = g.S;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (g.mstart[mid] * g.NT <= tile) lo = mid; else hi = mid;
+  }
+  const int s = lo;
+  const int mtiles = g.mstart[s + 1] - g.mstart[s];
+  const int local = tile - g.mstart[s] * g.NT;
+  const int grp = local / (kGroupM * g.NT), rem = local % (kGroupM * g.NT);
+  const int gm = min(kGroupM, mtiles - grp * kGroupM);
+  const int nt = rem / gm, mt = grp * kGroupM + rem % gm;
+  const int row0 = g.rowstart[s] + mt * BM;
+  const int mrows = min(BM, g.rowcount[s] - mt * BM);
+  const int n0 = nt * (MODE == 0 ? 64 : 128);
+  const bool is_shared = (s == g.E);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = tid >> 3, lc = (tid & 7) * 16;     // loader: rows lr + 32 i, 16-byte chunk lc
+  const int KB = g.K / 32;                           // scale bytes per row
+
+  const uint8_t* aptr[4];
+  const uint8_t* bptr[4];
+  int bad = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = lr + 32 * i;
+    const long long jr = (long long)row0 + (r < mrows ? r : 0);
+    long long src;
+    if (MODE == 0) {
+      src = is_shared ? jr - g.Tk : (long long)(g.perm[jr] / g.k);
+      if (src < 0 || src >= g.T) {
+        bad = 1;
+        src = 0;
+      }
+    } else {
+      src = jr;
+    }
+    aptr[i] = g.a + src * (long long)g.K + lc;
+    long long brow;
+    const uint8_t* bank;
+    if (MODE == 0) {
+      const int blk = r >> 5, within = r & 31;
+      bank = (blk & 1) ? (is_shared ? g.sb1 : g.b1) : (is_shared ? g.sb0 : g.b0);
+      brow = (long long)n0 + (blk >> 1) * 32 + within;
+    } else {
+      bank = is_shared ? g.sb0 : g.b0;
+      brow = (long long)n0 + r;
+    }
+    const long long e = is_shared ? 0 : s;
+    bptr[i] = bank + (e * g.N + brow) * (long long)g.K + lc;
+  }
+  // Scale rows: threads 0..127 stage A's scales (row tid), 128..255 B's (row tid-128).
+  const uint8_t* sptr;
+  {
+    const int r = tid & 127;
+    if (tid < 128) {
+      const long long jr = (long long)row0 + (r < mrows ? r : 0);
+      long long src;
+      if (MODE == 0) {
+        src = is_shared ? jr - g.Tk : (long long)(g.perm[jr] / g.k);
+        if (src < 0 || src >= g.T) src = 0;
+      } else {
+        src = jr;
+      }
+      sptr = g.as + src * (long long)KB;
+    } else {
+      long long brow;
+      const uint8_t* bank;
+      if (MODE == 0) {
+        const int blk = r >> 5, within = r & 31;
+        bank = (blk & 1) ? (is_shared ? g.sb1s : g.b1s) : (is_shared ? g.sb0s : g.b0s);
+        brow = (long long)n0 + (blk >> 1) * 32 + within;
+      } else {
+        bank = is_shared ? g.sb0s : g.b0s;
+        brow = (long long)n0 + r;
+      }
+      const long long e = is_shared ? 0 : s;
+      sptr = bank + (e * g.N + brow) * (long long)KB;
+    }
+  }
+  if (bad) raise_flag(g.flag, kFlagCorrupt);
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+
+  u32x4_t ra[4], rb[4];
+  uint32_t rs;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ra[i] = *(const u32x4_t*)(aptr[i]);
+    rb[i] = *(const u32x4_t*)(bptr[i]);
+  }
+  rs = *(const uint32_t*)(sptr);
+
+  for (int k0 = 0; k0 < g.K; k0 += MBK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *(u32x4_t*)&sA[(lr + 32 * i) * MLDS + lc] = ra[i];
+      *(u32x4_t*)&sB[(lr + 32 * i) * MLDS + lc] = rb[i];
+    }
+    if (tid < 128) sAs[tid] = rs; else sBs[tid - 128] = rs;
+    __syncthreads();
+    const int kn = k0 + MBK;
+    if (kn < g.K) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ra[i] = *(const u32x4_t*)(aptr[i] + kn);
+        rb[i] = *(const u32x4_t*)(bptr[i] + kn);
+      }
+      rs = *(const uint32_t*)(sptr + kn / 32);
+    }
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int kc = sub * 64 + (lane >> 5) * 16;       // bytes 0..15; bytes 16..31 at kc + 32
+      const int sh = 8 * (sub * 2 + (lane >> 5));       // scale byte of k-block (2 sub + half)
+      i32x8_t af[2], bf[2];
+      int sa[2], sb[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int row = wm * 64 + mb * 32 + (lane & 31);
+        const u32x4_t u0 = *(const u32x4_t*)&sA[row * MLDS + kc];
+        const u32x4_t u1 = *(const u32x4_t*)&sA[row * MLDS + kc + 32];
+        af[mb] = (i32x8_t){(int)u0[0], (int)u0[1], (int)u0[2], (int)u0[3],
+                           (int)u1[0], (int)u1[1], (int)u1[2], (int)u1[3]};
+        sa[mb] = (int)((sAs[row] >> sh) & 0xFFu);
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int row = wn * 64 + nb * 32 + (lane & 31);
+        const u32x4_t u0 = *(const u32x4_t*)&sB[row * MLDS + kc];
+        const u32x4_t u1 = *(const u32x4_t*)&sB[row * MLDS + kc + 32];
+        bf[nb] = (i32x8_t){(int)u0[0], (int)u0[1], (int)u0[2], (int)u0[3],
+                           (int)u1[0], (int)u1[1], (int)u1[2], (int)u1[3]};
+        sb[nb] = (int)((sBs[row] >> sh) & 0xFFu);
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              af[mb], bf[nb], acc[mb][nb], 0, 0, 0, sa[mb], 0, sb[nb]);
+    }
+    __syncthreads();
+  }
+
+  const int j = lane & 31;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int i = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      const int r = wm * 64 + mb * 32 + i;
+      const long long orow = (long long)row0 + r;
+      if (MODE == 0) {
+        // One MX block = this row's 32 columns, spread over the 32 lanes of a half.
+        const float h = silu_f32(acc[mb][0][v]) * acc[mb][1][v];
+        float amax = fabsf(h);
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        int se;
+        uint32_t scode;
+        if (amax == 0.0f) {
+          se = -127;
+          scode = 0;
+        } else if (!(amax <= 3.0e38f)) {
+          se = 0;
+          scode = 255;
+        } else {
+          se = min(max(ilogbf(amax) - 8, -127), 127);
+          scode = (uint32_t)(se + 127);
+        }
+        if (r < mrows) {
+          const int col = n0 + wn * 32 + j;
+          ((uint8_t*)g.out)[orow * g.N + col] = (uint8_t)e4m3_rne_sat(ldexpf(h, -se));
+          if (j == 0) g.out_scale[orow * (g.N / 32) + col / 32] = (uint8_t)scode;
+        }
+      } else {
+        if (r < mrows) {
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            const int col = n0 + wn * 64 + nb * 32 + j;
+            ((uint16_t*)g.out)[orow * g.N + col] = f32_to_bf16(acc[mb][nb][v]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 path (MOE_F32): one thread per output element, fp32 fma in ascending order.
 // ---------------------------------------------------------------------------
 struct F32Args {
@@ -325,6 +607,11 @@ static bool bank_ok(const moe_expert_bank* b, int dtype) {
   return true;
 }
 
+static bool mx_bank_aligned(const moe_expert_bank* b) {
+  return aligned(b->w1, 16) && aligned(b->w3, 16) && aligned(b->w2, 16) && aligned(b->w1_scale, 4) &&
+         aligned(b->w3_scale, 4) && aligned(b->w2_scale, 4);
+}
+
 // Checks shared by the three FFN entry points (everything but the per-half pointers).
 static moe_status check_ffn_shape(int dtype, int T, int d, int E, int k, int inter,
                                   const moe_expert_bank* routed, const moe_expert_bank* shared,
@@ -334,8 +621,8 @@ static moe_status check_ffn_shape(int dtype, int T, int d, int E, int k, int int
     return MOE_ERR_INVALID_ARG;
   if (!bank_ok(routed, dtype) || (shared && !bank_ok(shared, dtype))) return MOE_ERR_INVALID_ARG;
   if (!ws) return MOE_ERR_INVALID_ARG;
-  if (dtype == MOE_MXFP8) return MOE_ERR_UNSUPPORTED;
   if (dtype == MOE_BF16 && (d % 128 != 0 || inter % 64 != 0)) return MOE_ERR_UNSUPPORTED;
+  if (dtype == MOE_MXFP8 && (d % 128 != 0 || inter % 128 != 0)) return MOE_ERR_UNSUPPORTED;
   if ((long long)T * k > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
   if (ws_bytes < ffn_ws(T, E, k, inter, dtype).bytes) return MOE_ERR_WORKSPACE;
   return MOE_OK;
@@ -347,6 +634,7 @@ struct FfnPlan {
   int* rowstart;
   int* rowcount;
   void* h;
+  uint8_t* hs;
   int S, has_shared;
   long long Tk, rows, mt_bound;
 };
@@ -360,6 +648,7 @@ static FfnPlan plan_of(void* ws, int T, int E, int k, int inter, int dtype, bool
   p.rowstart = p.mstart + (E + 2);
   p.rowcount = p.rowstart + (E + 2);
   p.h = w + L.h;
+  p.hs = (uint8_t*)(w + L.hs);
   p.has_shared = has_shared ? 1 : 0;
   p.S = E + p.has_shared;
   p.Tk = (long long)T * k;
@@ -369,13 +658,43 @@ static FfnPlan plan_of(void* ws, int T, int E, int k, int inter, int dtype, bool
 }
 
 // GEMM1 half: segment table, then h = silu(x W1) * (x W3) for every dispatched row.
-static moe_status run_gate_up(const void* x, int dtype, int T, int d, int E, int k, int inter,
-                              const moe_expert_bank* routed, const moe_expert_bank* shared,
-                              const int32_t* offsets, const int32_t* perm, const FfnPlan& p,
-                              hipStream_t s) {
+static moe_status run_gate_up(const void* x, const uint8_t* xs, int dtype, int T, int d, int E,
+                              int k, int inter, const moe_expert_bank* routed,
+                              const moe_expert_bank* shared, const int32_t* offsets,
+                              const int32_t* perm, const FfnPlan& p, hipStream_t s) {
   seg_table_kernel<<<1, 1024, 0, s>>>(offsets, E, p.Tk, T, p.has_shared, p.mstart, p.rowstart,
                                       p.rowcount, p.flag);
-  if (dtype == MOE_BF16) {
+  if (dtype == MOE_MXFP8) {
+    MxArgs g{};
+    g.a = (const uint8_t*)x;
+    g.as = xs;
+    g.perm = perm;
+    g.T = T;
+    g.k = k;
+    g.E = E;
+    g.Tk = p.Tk;
+    g.b0 = (const uint8_t*)routed->w1;
+    g.b1 = (const uint8_t*)routed->w3;
+    g.b0s = routed->w1_scale;
+    g.b1s = routed->w3_scale;
+    g.sb0 = shared ? (const uint8_t*)shared->w1 : nullptr;
+    g.sb1 = shared ? (const uint8_t*)shared->w3 : nullptr;
+    g.sb0s = shared ? shared->w1_scale : nullptr;
+    g.sb1s = shared ? shared->w3_scale : nullptr;
+    g.K = d;
+    g.N = inter;
+    g.NT = inter / 64;
+    g.mstart = p.mstart;
+    g.rowstart = p.rowstart;
+    g.rowcount = p.rowcount;
+    g.S = p.S;
+    g.out = p.h;
+    g.out_scale = p.hs;
+    g.flag = p.flag;
+    const long long grid = (p.mt_bound * g.NT + kXcds - 1) / kXcds * kXcds;
+    if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+    grouped_gemm_mx_kernel<0><<<(unsigned)grid, 256, 0, s>>>(g);
+  } else if (dtype == MOE_BF16) {
     GemmArgs g{};
     g.a = (const uint16_t*)x;
     g.perm = perm;
@@ -430,7 +749,32 @@ static moe_status run_gate_up(const void* x, int dtype, int T, int d, int E, int
 static moe_status run_down(int dtype, int T, int d, int E, int k, int inter,
                            const moe_expert_bank* routed, const moe_expert_bank* shared, void* out,
                            const FfnPlan& p, hipStream_t s) {
-  if (dtype == MOE_BF16) {
+  if (dtype == MOE_MXFP8) {
+    MxArgs g{};
+    g.a = (const uint8_t*)p.h;
+    g.as = p.hs;
+    g.perm = nullptr;
+    g.T = T;
+    g.k = k;
+    g.E = E;
+    g.Tk = p.Tk;
+    g.b0 = (const uint8_t*)routed->w2;
+    g.b0s = routed->w2_scale;
+    g.sb0 = shared ? (const uint8_t*)shared->w2 : nullptr;
+    g.sb0s = shared ? shared->w2_scale : nullptr;
+    g.K = inter;
+    g.N = d;
+    g.NT = d / 128;
+    g.mstart = p.mstart;
+    g.rowstart = p.rowstart;
+    g.rowcount = p.rowcount;
+    g.S = p.S;
+    g.out = out;
+    g.flag = p.flag;
+    const long long grid = (p.mt_bound * g.NT + kXcds - 1) / kXcds * kXcds;
+    if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+    grouped_gemm_mx_kernel<1><<<(unsigned)grid, 256, 0, s>>>(g);
+  } else if (dtype == MOE_BF16) {
     GemmArgs g{};
     g.a = (const uint16_t*)p.h;
     g.perm = nullptr;
@@ -491,9 +835,12 @@ extern "C" moe_status moe_expert_ffn_gate_up(const void* x, const uint8_t* x_sca
   if (!offsets) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !perm) return MOE_ERR_INVALID_ARG;
-  if (dtype == MOE_BF16 && !aligned(x, 16)) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_F32 && !aligned(x, 16)) return MOE_ERR_INVALID_ARG;
+  if (dtype == MOE_MXFP8 && (!aligned(x_scale, 4) || !mx_bank_aligned(routed) ||
+                             (shared && !mx_bank_aligned(shared))))
+    return MOE_ERR_INVALID_ARG;
   const FfnPlan p = plan_of(ws, T, E, k, inter, dtype, shared != nullptr);
-  return run_gate_up(x, dtype, T, d, E, k, inter, routed, shared, offsets, perm, p,
+  return run_gate_up(x, x_scale, dtype, T, d, E, k, inter, routed, shared, offsets, perm, p,
                      (hipStream_t)stream);
 }
 
@@ -505,7 +852,9 @@ extern "C" moe_status moe_expert_ffn_down(int dtype, int T, int d, int E, int k,
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!out) return MOE_ERR_INVALID_ARG;
-  if (dtype == MOE_BF16 && !aligned(out, 16)) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_F32 && !aligned(out, 16)) return MOE_ERR_INVALID_ARG;
+  if (dtype == MOE_MXFP8 && (!mx_bank_aligned(routed) || (shared && !mx_bank_aligned(shared))))
+    return MOE_ERR_INVALID_ARG;
   const FfnPlan p = plan_of(ws, T, E, k, inter, dtype, shared != nullptr);
   return run_down(dtype, T, d, E, k, inter, routed, shared, out, p, (hipStream_t)stream);
 }
@@ -521,10 +870,14 @@ extern "C" moe_status moe_expert_ffn(const void* x, const uint8_t* x_scale, int 
   if (!offsets) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !perm || !out) return MOE_ERR_INVALID_ARG;
-  if (dtype == MOE_BF16 && (!aligned(x, 16) || !aligned(out, 16))) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_F32 && (!aligned(x, 16) || !aligned(out, 16))) return MOE_ERR_INVALID_ARG;
+  if (dtype == MOE_MXFP8 && (!aligned(x_scale, 4) || !mx_bank_aligned(routed) ||
+                             (shared && !mx_bank_aligned(shared))))
+    return MOE_ERR_INVALID_ARG;
   const FfnPlan p = plan_of(ws, T, E, k, inter, dtype, shared != nullptr);
   hipStream_t s = (hipStream_t)stream;
-  if ((st = run_gate_up(x, dtype, T, d, E, k, inter, routed, shared, offsets, perm, p, s)) != MOE_OK)
+  if ((st = run_gate_up(x, x_scale, dtype, T, d, E, k, inter, routed, shared, offsets, perm, p, s)) !=
+      MOE_OK)
     return st;
   return run_down(dtype, T, d, E, k, inter, routed, shared, out, p, s);
 }

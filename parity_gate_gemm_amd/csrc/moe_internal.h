@@ -60,18 +60,21 @@ inline DispatchWs dispatch_ws(int T, int E) {
   return w;
 }
 
-inline size_t elem_bytes_h(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
+inline size_t elem_bytes_h(int dtype) { return dtype == MOE_F32 ? 4 : (dtype == MOE_BF16 ? 2 : 1); }
 
 struct FfnWs {
-  size_t h, seg, bytes;
+  size_t h, hs, seg, bytes;
   long long rows;
 };
-// seg table: mstart[S+1] (int), rowstart[S] (int), rowcount[S] (int), S = E + 1
+// h: intermediate activations [T*k + T][inter] (fp32 / bf16 / E4M3 codes);
+// hs: E8M0 scales of h [T*k + T][inter/32] (MXFP8 only);
+// seg table: mstart[S+1] (int), rowstart[S] (int), rowcount[S] (int), S = E + 1.
 inline FfnWs ffn_ws(int T, int E, int k, int inter, int dtype) {
   FfnWs w;
   w.rows = (long long)T * k + T;
   size_t o = kHeaderBytes;
   w.h = o;   o = align_up(o + (size_t)w.rows * inter * elem_bytes_h(dtype), 256);
+  w.hs = o;  o = align_up(o + (dtype == MOE_MXFP8 ? (size_t)w.rows * (inter / 32) : 0), 256);
   w.seg = o; o = align_up(o + (size_t)(3 * (E + 2)) * sizeof(int), 256);
   w.bytes = o;
   return w;

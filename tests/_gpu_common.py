@@ -28,6 +28,14 @@ def host(t):
     return t.cpu().numpy().astype(np.float64) if t.dtype != torch.int32 else t.cpu().numpy()
 
 
+def values(t, scale=None):
+    """Exact float64 values of a stored tensor; MXFP8 codes are dequantised by the
+    oracle's own decoder."""
+    if scale is None:
+        return host(t)
+    return oracle.mx_dequant(t.cpu().numpy(), scale.cpu().numpy())
+
+
 class LazyExperts:
     """experts[e] -> (w1, w3, w2) float64 numpy, fetched from device tensors on demand."""
 
@@ -35,14 +43,15 @@ class LazyExperts:
         self.inp = inp
 
     def __getitem__(self, e):
-        return tuple(host(self.inp[n][e]) for n in ("w1", "w3", "w2"))
+        sc = lambda n: None if self.inp.get(n + "_scale") is None else self.inp[n + "_scale"][e]  # noqa: E731
+        return tuple(values(self.inp[n][e], sc(n)) for n in ("w1", "w3", "w2"))
 
 
 def shared_of(inp):
     sh = inp.get("shared")
     if sh is None:
         return None
-    return (host(sh["w1"]), host(sh["w3"]), host(sh["w2"]))
+    return tuple(values(sh[n], sh.get(n + "_scale")) for n in ("w1", "w3", "w2"))
 
 
 def to_device(inp, device="cuda"):
@@ -59,7 +68,8 @@ def to_device(inp, device="cuda"):
 
 def oracle_for_rows(inp, rows, k, replay=False):
     """Oracle layer on a subset of token rows (routing and FFN are row-local)."""
-    x = host(inp["x"])[rows]
+    xs = inp.get("x_scale")
+    x = values(inp["x"][rows], None if xs is None else xs[rows])
     kw = {}
     if replay:
         kw["ids_in"] = inp["ids_in"].cpu().numpy()[rows]

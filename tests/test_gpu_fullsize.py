@@ -144,3 +144,36 @@ def test_bf16_t128_stream(c4):
     say(f"  rows {rows.tolist()} normwise err {err:.3e}")
     for _ in range(9):
         assert torch.equal(run_layer(inp, wl.k)["y"], res["y"])
+
+
+@pytest.fixture(scope="module")
+def c5():
+    wl = synth.WORKLOADS["mxfp8_t32768"]
+    say("drawing mxfp8_t32768 inputs on the GPU")
+    inp = synth.make_layer_inputs(wl, device="cuda")
+    torch.cuda.synchronize()
+    yield wl, inp
+    del inp
+    torch.cuda.empty_cache()
+
+
+def test_mxfp8_t32768(c5):
+    wl, inp = c5
+    say("case mxfp8_t32768")
+    ws = pg.Workspace(wl.T, wl.d, wl.E, wl.k, wl.inter, pg.MOE_MXFP8)
+    res = run_layer(inp, wl.k, ws=ws)
+    check_dispatch_properties(res["ids"], res["offsets"], res["perm"], res["row_of"], wl.E)
+    seg = np.diff(res["offsets"].cpu().numpy())
+    say(f"  segment rows: max {seg.max()} median {int(np.median(seg))} min {seg.min()} "
+        f"touched {(seg > 0).sum()}")
+    rows = _sample_rows(res, wl.T, 4, 5)
+    ref = oracle_for_rows(inp, rows, wl.k)
+    err = compare_rows(res, ref, rows, "mxfp8")
+    say(f"  rows {rows.tolist()} normwise err {err:.3e}")
+    for _ in range(9):
+        assert torch.equal(run_layer(inp, wl.k, ws=ws)["y"], res["y"])
+    p = torch.randperm(wl.T, generator=torch.Generator().manual_seed(4)).cuda()
+    pin = dict(inp, x=inp["x"][p].contiguous(), x_scale=inp["x_scale"][p].contiguous())
+    rp = run_layer(pin, wl.k, ws=ws)
+    assert torch.equal(rp["ids"], res["ids"][p])
+    assert torch.equal(rp["y"], res["y"][p])

@@ -46,6 +46,9 @@ SMALL = [
     (200, 128, 64, 384, 8, True, False, "bf16"),
     (64, 128, 64, 8, 8, False, True, "bf16"),      # k == E
     (129, 128, 64, 3, 1, False, False, "bf16"),    # k == 1, one expert gets >128 rows
+    (200, 128, 128, 16, 4, True, True, "mxfp8"),
+    (300, 256, 256, 4, 2, True, False, "mxfp8"),   # 150 rows/expert: 2 row tiles, ragged
+    (1, 128, 128, 384, 8, False, True, "mxfp8"),
     (50, 64, 32, 16, 3, True, True, "f32"),
     (5, 96, 40, 1024, 32, True, False, "f32"),     # largest E and k
 ]
@@ -180,9 +183,10 @@ def test_nonfinite_input_is_flagged():
     assert ei.value.status == 5                # MOE_ERR_NONFINITE
 
 
-def test_determinism_permutation_and_batch_invariance_small():
+@pytest.mark.parametrize("dtype", ["bf16", "mxfp8"])
+def test_determinism_permutation_and_batch_invariance_small(dtype):
     wl = synth.Workload("inv", T=333, d=256, inter=128, E=64, k=8, shared=True, bias=True,
-                        dtype="bf16", seed=21)
+                        dtype=dtype, seed=21)
     inp = _inputs(wl)
     say("case invariance small")
     base = run_layer(inp, wl.k)
@@ -190,9 +194,13 @@ def test_determinism_permutation_and_batch_invariance_small():
         assert torch.equal(run_layer(inp, wl.k)["y"], base["y"])
     p = torch.randperm(wl.T, generator=torch.Generator().manual_seed(0)).cuda()
     perm_in = dict(inp, x=inp["x"][p].contiguous())
+    if inp["x_scale"] is not None:
+        perm_in["x_scale"] = inp["x_scale"][p].contiguous()
     yp = run_layer(perm_in, wl.k)["y"]
     assert torch.equal(yp, base["y"][p])
     # a token alone gives the same bits as in the batch
     for t in (0, 17, 332):
         one = dict(inp, x=inp["x"][t:t + 1].contiguous())
+        if inp["x_scale"] is not None:
+            one["x_scale"] = inp["x_scale"][t:t + 1].contiguous()
         assert torch.equal(run_layer(one, wl.k)["y"][0], base["y"][t])

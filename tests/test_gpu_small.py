@@ -100,6 +100,27 @@ def test_exact_and_near_ties_and_zero_tokens():
             assert 2 in row and row.index(2) < row.index(9)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "mxfp8"])
+def test_near_ties_below_fp32_resolution(dtype):
+    """Two large gate columns differing by a relative 2^-18: their logits differ by ~1e-5
+    for every token, far below what a bf16 or fp32 gate resolves and far above the fp64
+    gate's bound; ids must equal the exact-logit selection for every dtype."""
+    T, d, I, E, k = 256, 256, 128, 32, 4
+    wl = synth.Workload("refine", T=T, d=d, inter=I, E=E, k=k, dtype=dtype, seed=13)
+    inp = synth.make_layer_inputs(wl)
+    wg = inp["w_gate"]
+    wg[:, 5] *= 4.0
+    wg[:, 6] = (wg[:, 5].double() * (1.0 + 2.0 ** -18)).float()
+    inp = to_device(inp)
+    say(f"case near ties {dtype}")
+    res = run_layer(inp, k)
+    ref = oracle_for_rows(inp, np.arange(T), k)
+    compare_rows(res, ref, np.arange(T), dtype)
+    ids = res["ids"].cpu().numpy()
+    both = [t for t in range(T) if 5 in ids[t] and 6 in ids[t]]
+    assert len(both) > T // 4          # the pair is usually selected together
+
+
 def test_replay_own_ids_equals_learned_bitwise():
     wl = synth.Workload("rep", T=150, d=128, inter=64, E=32, k=4, shared=True, bias=True,
                         dtype="bf16", seed=11)

@@ -156,8 +156,13 @@ moe_status moe_dispatch(const int32_t* ids, int T, int E, int k,
  * Per output element the reduction order is fixed (same instruction sequence for
  * every row of every segment), so a token's output row does not depend on which
  * other tokens share its expert.
+ * For MOE_MXFP8 the intermediate h is requantised to MXFP8 per row (one E8M0
+ * scale per 32 columns, E4M3 elements rounded to nearest even and saturated at
+ * +-448) before the W2 GEMM, so it is consumed by the same block-scaled MFMA.
  * MOE_ERR_UNSUPPORTED: MOE_BF16 needs d % 128 == 0 and inter % 64 == 0;
- * MOE_MXFP8 is not implemented yet. */
+ * MOE_MXFP8 needs d % 128 == 0 and inter % 128 == 0.
+ * MOE_ERR_INVALID_ARG: x or a weight pointer not 16-byte aligned (bf16, MXFP8),
+ * or an MXFP8 scale pointer not 4-byte aligned. */
 moe_status moe_expert_ffn(const void* x, const uint8_t* x_scale, int dtype, int T, int d,
                           int E, int k, int inter,
                           const moe_expert_bank* routed, const moe_expert_bank* shared,

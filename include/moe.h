@@ -98,8 +98,9 @@ moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
 /* Learned routing: gate GEMM, softmax over the E experts, top-k, renormalise.
  *   x       [T][d] activations in `dtype` (x_scale [T][d/32] E8M0 for MOE_MXFP8,
  *           else NULL; the gate reads the exact dequantised values).
- *   w_gate  fp32 [d][E]; bias fp32 [E] or NULL (added to the logits used for both
- *           the selection and the weights).
+ *   w_gate  fp32 [d][E], 16-byte aligned when E % 4 == 0 (else 4-byte aligned);
+ *           bias fp32 [E] or NULL (added to the logits used for both the selection
+ *           and the weights).
  *   ids     out int32 [T][k]: the k experts with the largest logits, ordered by
  *           (logit descending, expert index ascending).  The selection equals the
  *           one made on the exactly rounded logits: an fp64 GEMM with a rigorous
@@ -109,7 +110,10 @@ moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
  *   weights out fp32 [T][k]: softmax probabilities of the chosen experts
  *           renormalised to sum to one (computed in fp64 from the fp64 logits,
  *           rounded once), in the same column order as ids.
+ * Every logit is summed in one fixed order that depends on d only (not on T or on
+ * the other tokens), so a token's ids and weights are the same in every batch.
  * Sets MOE_ERR_NONFINITE in the device flag if any logit of a token is not finite.
+ * MOE_ERR_INVALID_ARG: misaligned x or w_gate.  MOE_ERR_UNSUPPORTED: d % 16 != 0.
  * T == 0 is a valid no-op. */
 moe_status moe_route(const void* x, const uint8_t* x_scale, int dtype, int T, int d,
                      const float* w_gate, const float* bias, int E, int k,

@@ -32,16 +32,38 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Workspace layout.  Byte 0..255: header (int flag at offset 0).  The rest is
 // scratch that each call uses for its own duration only.
 // ---------------------------------------------------------------------------
+// K-splits of the fp64 gate sums: the reduction over d restarts every d / S
+// elements and the S partial sums are added in ascending order.  S depends on d
+// only, never on T, so every logit has the same summation order in every batch.
+inline int gate_splits(int d) {
+  if (d % 64 != 0) return 1;
+  const int steps = d / 64;
+  for (int s = 8; s > 1; s >>= 1)
+    if (steps % s == 0 && steps / s >= 4) return s;
+  return 1;
+}
+// Output tiles of the gate (64 tokens x 32 experts) below which the K-splits run in
+// separate workgroups (partial sums in the workspace) instead of one after another.
+constexpr int kGateSplitTiles = 256;
+inline int gate_tiles(int T, int E) { return ((T + 63) / 64) * ((E + 31) / 32); }
+inline bool gate_split_launch(int T, int d, int E) {
+  return gate_splits(d) > 1 && gate_tiles(T, E) < kGateSplitTiles;
+}
+
 struct RouteWs {
-  size_t logits, tok_flag, xnorm, wnorm, bytes;
+  size_t logits, tok_flag, xnorm, wnorm, part, xsq, wsq, bytes;
 };
-inline RouteWs route_ws(int T, int E) {
+inline RouteWs route_ws(int T, int d, int E) {
   RouteWs w;
+  const size_t S = gate_split_launch(T, d, E) ? (size_t)gate_splits(d) : 0;
   size_t o = kHeaderBytes;
   w.logits = o;   o = align_up(o + (size_t)T * E * sizeof(double), 256);
   w.tok_flag = o; o = align_up(o + (size_t)T * sizeof(int), 256);
   w.xnorm = o;    o = align_up(o + (size_t)T * sizeof(double), 256);
   w.wnorm = o;    o = align_up(o + (size_t)E * sizeof(double), 256);
+  w.part = o;     o = align_up(o + S * T * E * sizeof(double), 256);
+  w.xsq = o;      o = align_up(o + S * T * sizeof(double), 256);
+  w.wsq = o;      o = align_up(o + S * E * sizeof(double), 256);
   w.bytes = o;
   return w;
 }
@@ -82,7 +104,7 @@ inline FfnWs ffn_ws(int T, int E, int k, int inter, int dtype) {
 
 inline size_t workspace_bytes(int T, int d, int E, int k, int inter, int dtype) {
   (void)d;
-  size_t a = route_ws(T, E).bytes, b = dispatch_ws(T, E).bytes, c = ffn_ws(T, E, k, inter, dtype).bytes;
+  size_t a = route_ws(T, d, E).bytes, b = dispatch_ws(T, E).bytes, c = ffn_ws(T, E, k, inter, dtype).bytes;
   size_t m = a > b ? a : b;
   return m > c ? m : c;
 }

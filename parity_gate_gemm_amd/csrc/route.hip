@@ -193,6 +193,353 @@ __global__ __launch_bounds__(256) void gate_gemm_f64_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same fp64 gate GEMM staged through a three-stage LDS ring that direct
+// global->LDS loads fill (global_load_lds_dwordx4: lane l of a wavefront writes its 16
+// bytes at base + 16 l), used whenever E % 4 == 0.  Activations stay in their stored
+// format in LDS and are widened to fp64 as the MFMA operands are read; two K-steps of
+// loads are in flight while a third is multiplied.
+// Reduction order: for every logit, the K range is cut into S = gate_splits(d) equal
+// parts; each part is a chain of v_mfma_f64_16x16x4f64 from zero over its 16-wide
+// chunks in ascending order, where MFMA m (0..3) of a chunk at c sums the products at
+// c + m, c + 4 + m, c + 8 + m, c + 12 + m; the parts are added in ascending order and
+// the bias last.  A workgroup either runs all S parts itself or, for small batches,
+// one part whose partial sum gate_finish_kernel adds in the same order: the bits do
+// not depend on which.  Every sum still has at most d + 1 rounded additions, so the
+// error bound of gate_gemm_f64_kernel holds.
+// Stage layout: 64 activation rows of 64 elements, then 64 rows (k) of the 32 experts'
+// fp32 weights (128 B).  A 16-byte chunk c of activation row r sits in slot
+// c ^ (r & min(7, slots - 1)); weight chunk c of row k in slot c ^ (4 * ((k >> 2) & 1)),
+// so the lanes of one LDS read phase meet distinct banks (the activation read keeps a
+// 2-way conflict: 16 rows share 8 slots).
+// ---------------------------------------------------------------------------
+constexpr int GD_STAGES = 3;
+
+template <int DT>
+struct GateStage;   // bytes of one activation row's 64-element step
+template <>
+struct GateStage<MOE_BF16> { static constexpr int RB = 128; };
+template <>
+struct GateStage<MOE_F32> { static constexpr int RB = 256; };
+template <>
+struct GateStage<MOE_MXFP8> { static constexpr int RB = 64; };
+
+// One lane's LDS reads for a 16-wide chunk of the ring gate kernel: its four
+// activations (8, 16 or 4 bytes at xa) and the weights of its k rows for two 16-expert
+// blocks (4 rows, 128 bytes apart, at wa0 and at wa1).  Issued from inline assembly
+// with their own lgkmcnt(0) wait, so that the compiler does not tie them to the
+// outstanding global->LDS loads of the other ring stages (it would wait for all of
+// them); the K loop's vmcnt wait and barrier order them against those loads.
+typedef uint32_t u32x2_v __attribute__((ext_vector_type(2)));
+#define MOE_GATE_WREADS                                                                      \
+  "ds_read_b32 %1, %9\n\tds_read_b32 %2, %9 offset:128\n\tds_read_b32 %3, %9 offset:256\n\t" \
+  "ds_read_b32 %4, %9 offset:384\n\tds_read_b32 %5, %10\n\tds_read_b32 %6, %10 offset:128\n\t" \
+  "ds_read_b32 %7, %10 offset:256\n\tds_read_b32 %8, %10 offset:384\n\ts_waitcnt lgkmcnt(0)"
+#define MOE_GATE_OUTS(X)                                                                       \
+  : "=&v"(X), "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(w[4]), "=&v"(w[5]), \
+    "=&v"(w[6]), "=&v"(w[7])                                                                   \
+  : "v"(wa0), "v"(wa1), "v"(xa)
+template <int DT>
+__device__ __forceinline__ void gate_lds_reads(uint32_t xa, uint32_t wa0, uint32_t wa1, uint32_t sa,
+                                               u32x4_v& x, uint32_t (&w)[8]) {
+  if constexpr (DT == MOE_F32) {
+    asm volatile("ds_read_b128 %0, %11\n\t" MOE_GATE_WREADS MOE_GATE_OUTS(x));
+  } else if constexpr (DT == MOE_BF16) {
+    u32x2_v v;
+    asm volatile("ds_read_b64 %0, %11\n\t" MOE_GATE_WREADS MOE_GATE_OUTS(v));
+    x[0] = v[0];
+    x[1] = v[1];
+  } else {   // MXFP8: four E4M3 codes, and the E8M0 scale byte of their block at sa
+    uint32_t v, sc;
+    asm volatile(
+        "ds_read_b32 %0, %12\n\tds_read_u8 %9, %13\n\t"
+        "ds_read_b32 %1, %10\n\tds_read_b32 %2, %10 offset:128\n\tds_read_b32 %3, %10 offset:256\n\t"
+        "ds_read_b32 %4, %10 offset:384\n\tds_read_b32 %5, %11\n\tds_read_b32 %6, %11 offset:128\n\t"
+        "ds_read_b32 %7, %11 offset:256\n\tds_read_b32 %8, %11 offset:384\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(v), "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(w[4]), "=&v"(w[5]),
+          "=&v"(w[6]), "=&v"(w[7]), "=&v"(sc)
+        : "v"(wa0), "v"(wa1), "v"(xa), "v"(sa));
+    x[0] = v;
+    x[1] = sc;
+  }
+}
+#undef MOE_GATE_OUTS
+#undef MOE_GATE_WREADS
+
+struct GateArgs {
+  const uint8_t* x;        // activations (bytes)
+  const uint8_t* xs;       // MXFP8 scales [T][d/32]
+  int T, d, E;
+  const float* wg;         // [d][E], 16-byte aligned, E % 4 == 0
+  const float* bias;       // [E] or null
+  int ks;                  // elements per K part (d / S)
+  int spw;                 // K parts per workgroup (S, or 1 when split over gridDim.z)
+  double* logits;          // [T][E] final (gridDim.z == 1)
+  double* part;            // [z][T][E] partial sums (gridDim.z > 1)
+  double* xnorm;           // ||x_t|| (gridDim.z == 1) or partial squares [z][T]
+  double* wnorm;           // ||w_e|| (gridDim.z == 1) or partial squares [z][E]
+};
+
+template <int N>
+__device__ __forceinline__ void gate_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void gate_gemm_f64_ring_kernel(GateArgs g) {
+  constexpr int RB = GateStage<DT>::RB;
+  constexpr int EB = RB / 64;                  // bytes per activation element
+  constexpr int SPR = RB / 16;                 // 16-byte slots per activation row
+  constexpr int XSW = SPR < 8 ? SPR - 1 : 7;   // activation slot swizzle mask
+  constexpr int RPI = 1024 / RB;               // activation rows per 1 KB load
+  constexpr int NXA = GT_M / RPI / 4;          // activation loads per wavefront per step
+  constexpr int NWA = 2;                       // weight loads per wavefront per step
+  constexpr int XB = GT_M * RB;
+  constexpr int STAGE = XB + GT_K * 128;
+  constexpr int PER_STEP = NXA + NWA;
+  static_assert(NXA * 4 * RPI == GT_M && GT_K * 128 == NWA * 4 * 1024, "loader shape");
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e0 = blockIdx.x * GT_E, t0 = blockIdx.y * GT_M, z = blockIdx.z;
+  const int nss = (g.ks + GT_K - 1) / GT_K;    // steps per K part
+  const int nsteps = g.spw * nss;
+  const int part0 = z * g.spw;
+  const size_t xrow = (size_t)g.d * EB;
+
+  // ---- loader addresses (byte offsets without the step's K offset) ----
+  size_t xo[NXA];
+  int xk[NXA];   // element offset of the chunk within a step
+#pragma unroll
+  for (int i = 0; i < NXA; ++i) {
+    const int r = (wave * NXA + i) * RPI + lane / SPR;
+    const int ch = (lane % SPR) ^ (r & XSW);
+    const int t = t0 + r < g.T ? t0 + r : 0;
+    xo[i] = (size_t)t * xrow + (size_t)ch * 16;
+    xk[i] = ch * 16 / EB;
+  }
+  size_t wo[NWA];
+  int wr[NWA];
+  bool wok[NWA];
+#pragma unroll
+  for (int i = 0; i < NWA; ++i) {
+    const int kr = (wave * NWA + i) * 8 + lane / 8;
+    const int slot = (lane % 8) ^ (((kr >> 2) & 1) << 2);
+    const int e = e0 + 4 * slot;
+    wok[i] = e < g.E;
+    wo[i] = (size_t)kr * g.E + e;
+    wr[i] = kr;
+  }
+  // the activation row this lane reads
+  const int rr = 16 * wave + (lane & 15), j = lane >> 4;
+  // MXFP8: the E8M0 scales of the tile's 64 rows over this workgroup's K range, staged
+  // once in LDS (row r at sscale + r * nkb) before the ring starts
+  extern __shared__ uint8_t sscale[];
+  const int nkb = DT == MOE_MXFP8 ? g.spw * g.ks / 32 : 0;
+  if (DT == MOE_MXFP8) {
+    const int nb32 = g.d / 32, kb0 = part0 * g.ks / 32;
+    for (int q = tid; q < GT_M * nkb; q += 256) {
+      const int r = q / nkb, c = q % nkb;
+      const int t = t0 + r < g.T ? t0 + r : 0;
+      sscale[q] = g.xs[(size_t)t * nb32 + kb0 + c];
+    }
+    __syncthreads();
+  }
+
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  auto kbase = [&](int i) { return (part0 + i / nss) * g.ks + (i % nss) * GT_K; };
+  auto issue = [&](uint8_t* st, int i) {
+    const int k0 = kbase(i), loc = (i % nss) * GT_K;
+#if defined(__HIP_DEVICE_COMPILE__)   // a gfx950 builtin: device pass only
+#pragma unroll
+    for (int q = 0; q < NXA; ++q) {
+      const uint8_t* src = loc + xk[q] < g.ks ? g.x + xo[q] + (size_t)k0 * EB : g.x;
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr)(st + (wave * NXA + q) * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < NWA; ++q) {
+      const float* src = (wok[q] && loc + wr[q] < g.ks) ? g.wg + wo[q] + (size_t)k0 * g.E : g.wg;
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr)(st + XB + (wave * NWA + q) * 1024), 16, 0, 0);
+    }
+#endif
+  };
+
+  f64x4_t acc[2], tot[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[nb][q] = tot[nb][q] = 0.0;
+  double xsq = 0.0, wsq[2] = {0.0, 0.0};
+  const bool do_xn = blockIdx.x == 0, do_wn = blockIdx.y == 0 && wave == 0;
+
+  // fragment offsets within a stage
+  const int wsl = (j & 1) << 2;                // weight slot swizzle of this lane's k rows
+  int wof[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int el = 16 * nb + (lane & 15);
+    wof[nb] = XB + (((el >> 2) ^ wsl) << 4) + (el & 3) * 4;
+  }
+  auto xoff = [&](int c16) -> int {
+    if (DT == MOE_BF16) return rr * RB + (((2 * c16 + (j >> 1)) ^ (rr & XSW)) << 4) + (j & 1) * 8;
+    if (DT == MOE_F32) return rr * RB + (((4 * c16 + j) ^ (rr & XSW)) << 4);
+    return rr * RB + ((c16 ^ (rr & XSW)) << 4) + 4 * j;
+  };
+
+  const uint32_t sbase = (uint32_t)(uintptr_t)(lds_u8*)sscale + rr * nkb;
+  auto compute = [&](const uint8_t* st, int i) {
+    const int loc = (i % nss) * GT_K;
+#pragma unroll
+    for (int c16 = 0; c16 < 4; ++c16) {
+      if (loc + 16 * c16 >= g.ks) break;       // ragged last step of a part
+      double a[4], b[2][4];
+      const uint32_t sb = (uint32_t)(uintptr_t)(lds_u8*)st;
+      const uint32_t wa = sb + (16 * c16 + 4 * j) * 128;
+      u32x4_v xv;
+      uint32_t w[8];
+      gate_lds_reads<DT>(sb + xoff(c16), wa + wof[0], wa + wof[1],
+                         sbase + ((i / nss) * g.ks + loc + 16 * c16) / 32, xv, w);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        b[0][m] = (double)__uint_as_float(w[m]);
+        b[1][m] = (double)__uint_as_float(w[4 + m]);
+      }
+      if (DT == MOE_BF16) {
+        a[0] = (double)__uint_as_float(xv[0] << 16);
+        a[1] = (double)__uint_as_float(xv[0] & 0xffff0000u);
+        a[2] = (double)__uint_as_float(xv[1] << 16);
+        a[3] = (double)__uint_as_float(xv[1] & 0xffff0000u);
+      } else if (DT == MOE_F32) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) a[m] = (double)__uint_as_float(xv[m]);
+      } else {
+        const double sf = e8m0_to_f64((uint8_t)xv[1]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) a[m] = e4m3_to_f64((uint8_t)(xv[0] >> (8 * m))) * sf;
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[nb] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[m], b[nb][m], acc[nb], 0, 0, 0);
+      }
+      if (do_xn) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) xsq = fma(a[m], a[m], xsq);
+      }
+      if (do_wn) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) wsq[nb] = fma(b[nb][m], b[nb][m], wsq[nb]);
+      }
+    }
+    if (i % nss == nss - 1) {                  // end of a K part: add it to the total
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        tot[nb] = (i == nss - 1) ? acc[nb] : tot[nb] + acc[nb];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[nb][q] = 0.0;
+      }
+    }
+  };
+
+  // ---- K loop over the ring; step i lives in st[i % 3] ----
+  issue(st0, 0);
+  if (nsteps > 1) issue(st1, 1);
+  auto kstep = [&](int i, const uint8_t* cur, uint8_t* nxt) {
+    if (i + 1 < nsteps)
+      gate_wait_vmcnt<PER_STEP>();
+    else
+      gate_wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (i + 2 < nsteps) issue(nxt, i + 2);
+    compute(cur, i);
+  };
+  for (int i = 0; i < nsteps; i += GD_STAGES) {
+    kstep(i, st0, st2);
+    if (i + 1 < nsteps) kstep(i + 1, st1, st0);
+    if (i + 2 < nsteps) kstep(i + 2, st2, st1);
+  }
+
+  // ---- outputs.  D layout of a 16x16 fp64 block: element q of a lane is row
+  //      lane/16 + 4q, column lane%16. ----
+  const bool final_out = gridDim.z == 1;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int e = e0 + 16 * nb + (lane & 15);
+    if (e >= g.E) continue;
+    const double bb = (final_out && g.bias) ? (double)g.bias[e] : 0.0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int t = t0 + 16 * wave + (lane >> 4) + 4 * q;
+      if (t >= g.T) continue;
+      if (final_out) {
+        double v = tot[nb][q];
+        if (g.bias) v = v + bb;
+        g.logits[(size_t)t * g.E + e] = v;
+      } else {
+        g.part[((size_t)z * g.T + t) * g.E + e] = tot[nb][q];
+      }
+    }
+  }
+  if (do_xn) {
+    double v = xsq + __shfl_xor(xsq, 16);
+    v = v + __shfl_xor(v, 32);
+    const int t = t0 + rr;
+    if (j == 0 && t < g.T) {
+      if (final_out) g.xnorm[t] = sqrt(v);
+      else g.xnorm[(size_t)z * g.T + t] = v;
+    }
+  }
+  if (do_wn) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      double v = wsq[nb] + __shfl_xor(wsq[nb], 16);
+      v = v + __shfl_xor(v, 32);
+      const int e = e0 + 16 * nb + (lane & 15);
+      if (j == 0 && e < g.E) {
+        if (final_out) g.wnorm[e] = sqrt(v);
+        else g.wnorm[(size_t)z * g.E + e] = v;
+      }
+    }
+  }
+}
+
+// Adds the S partial sums of a K-split gate launch in ascending order, then the bias
+// (the order gate_gemm_f64_ring_kernel uses when one workgroup runs every part), and
+// finishes the norms.
+__global__ __launch_bounds__(256) void gate_finish_kernel(const double* __restrict__ part,
+                                                          const double* __restrict__ xsq,
+                                                          const double* __restrict__ wsq,
+                                                          const float* __restrict__ bias, int T,
+                                                          int E, int S, double* __restrict__ logits,
+                                                          double* __restrict__ xnorm,
+                                                          double* __restrict__ wnorm) {
+  const size_t n = (size_t)T * E;
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    double v = part[i];
+    for (int z = 1; z < S; ++z) v = v + part[(size_t)z * n + i];
+    if (bias) v = v + (double)bias[i % E];
+    logits[i] = v;
+  }
+  if (i < (size_t)T) {
+    double v = xsq[i];
+    for (int z = 1; z < S; ++z) v = v + xsq[(size_t)z * T + i];
+    xnorm[i] = sqrt(v);
+  }
+  if (i < (size_t)E) {
+    double v = wsq[i];
+    for (int z = 1; z < S; ++z) v = v + wsq[(size_t)z * E + i];
+    wnorm[i] = sqrt(v);
+  }
+}
+
 // "a ranks before b": larger logit first, then lower expert index.
 __device__ __forceinline__ bool ranks_before(double av, int ae, double bv, int be) {
   return av > bv || (av == bv && ae < be);
@@ -451,7 +798,9 @@ static moe_status check_route_args(const void* x, const uint8_t* x_scale, int dt
   if (d % 16 != 0) return MOE_ERR_UNSUPPORTED;
   if (!aligned(x, 16)) return MOE_ERR_INVALID_ARG;
   if ((long long)T * E > 0x7fffffffLL || (long long)T * k > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
-  if (ws_bytes < route_ws(T, E).bytes) return MOE_ERR_WORKSPACE;
+  if (E % 4 == 0 && !aligned(w_gate, 16)) return MOE_ERR_INVALID_ARG;
+  if (!aligned(w_gate, 4)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < route_ws(T, d, E).bytes) return MOE_ERR_WORKSPACE;
   return MOE_OK;
 }
 
@@ -465,17 +814,48 @@ static double two_gamma(int d) {
 static moe_status launch_gate(const void* x, const uint8_t* xs, int dtype, int T, int d,
                               const float* w_gate, const float* bias, int E, char* w,
                               hipStream_t s) {
-  const RouteWs L = route_ws(T, E);
-  dim3 grid((E + GT_E - 1) / GT_E, (T + GT_M - 1) / GT_M);
+  const RouteWs L = route_ws(T, d, E);
   double* lg = (double*)(w + L.logits);
   double* xn = (double*)(w + L.xnorm);
   double* wn = (double*)(w + L.wnorm);
+  if (E % 4 != 0) {   // weight rows not 16-byte granular: register-staged kernel
+    dim3 grid((E + GT_E - 1) / GT_E, (T + GT_M - 1) / GT_M);
+    if (dtype == MOE_BF16)
+      gate_gemm_f64_kernel<MOE_BF16><<<grid, 256, 0, s>>>(x, xs, T, d, w_gate, bias, E, lg, xn, wn);
+    else if (dtype == MOE_F32)
+      gate_gemm_f64_kernel<MOE_F32><<<grid, 256, 0, s>>>(x, xs, T, d, w_gate, bias, E, lg, xn, wn);
+    else
+      gate_gemm_f64_kernel<MOE_MXFP8><<<grid, 256, 0, s>>>(x, xs, T, d, w_gate, bias, E, lg, xn, wn);
+    return launch_status();
+  }
+  const int S = gate_splits(d);
+  const bool split = gate_split_launch(T, d, E);
+  GateArgs g{};
+  g.x = (const uint8_t*)x;
+  g.xs = xs;
+  g.T = T;
+  g.d = d;
+  g.E = E;
+  g.wg = w_gate;
+  g.bias = bias;
+  g.ks = d / S;
+  g.spw = split ? 1 : S;
+  g.logits = lg;
+  g.part = (double*)(w + L.part);
+  g.xnorm = split ? (double*)(w + L.xsq) : xn;
+  g.wnorm = split ? (double*)(w + L.wsq) : wn;
+  dim3 grid((E + GT_E - 1) / GT_E, (T + GT_M - 1) / GT_M, split ? S : 1);
   if (dtype == MOE_BF16)
-    gate_gemm_f64_kernel<MOE_BF16><<<grid, 256, 0, s>>>(x, xs, T, d, w_gate, bias, E, lg, xn, wn);
+    gate_gemm_f64_ring_kernel<MOE_BF16><<<grid, 256, 0, s>>>(g);
   else if (dtype == MOE_F32)
-    gate_gemm_f64_kernel<MOE_F32><<<grid, 256, 0, s>>>(x, xs, T, d, w_gate, bias, E, lg, xn, wn);
+    gate_gemm_f64_ring_kernel<MOE_F32><<<grid, 256, 0, s>>>(g);
   else
-    gate_gemm_f64_kernel<MOE_MXFP8><<<grid, 256, 0, s>>>(x, xs, T, d, w_gate, bias, E, lg, xn, wn);
+    gate_gemm_f64_ring_kernel<MOE_MXFP8><<<grid, 256, (size_t)GT_M * (g.spw * g.ks / 32), s>>>(g);
+  if (split) {
+    const size_t n = (size_t)T * E;
+    gate_finish_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
+        g.part, g.xnorm, g.wnorm, bias, T, E, S, lg, xn, wn);
+  }
   return launch_status();
 }
 
@@ -492,7 +872,7 @@ extern "C" moe_status moe_route(const void* x, const uint8_t* x_scale, int dtype
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
   int* flag = (int*)w;
-  const RouteWs L = route_ws(T, E);
+  const RouteWs L = route_ws(T, d, E);
   if ((st = launch_gate(x, x_scale, dtype, T, d, w_gate, bias, E, w, s)) != MOE_OK) return st;
   select_topk_kernel<<<(T + SEL_WAVES - 1) / SEL_WAVES, 256, 0, s>>>(
       (const double*)(w + L.logits), (const double*)(w + L.xnorm), (const double*)(w + L.wnorm),
@@ -513,7 +893,7 @@ extern "C" moe_status moe_route_replay(const void* x, const uint8_t* x_scale, in
   if (!ids_in || !weights_out) return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
-  const RouteWs L = route_ws(T, E);
+  const RouteWs L = route_ws(T, d, E);
   if ((st = launch_gate(x, x_scale, dtype, T, d, w_gate, bias, E, w, s)) != MOE_OK) return st;
   replay_kernel<<<(T + SEL_WAVES - 1) / SEL_WAVES, 256, 0, s>>>(
       (const double*)(w + L.logits), T, E, k, ids_in, weights_in, weights_out, (int*)w);

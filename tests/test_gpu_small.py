@@ -225,3 +225,25 @@ def test_determinism_permutation_and_batch_invariance_small(dtype):
         if inp["x_scale"] is not None:
             one["x_scale"] = inp["x_scale"][t:t + 1].contiguous()
         assert torch.equal(run_layer(one, wl.k)["y"][0], base["y"][t])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "mxfp8"])
+def test_gate_k_split_matches_unsplit(dtype):
+    """d = 1024 cuts every gate sum into 4 parts.  A batch of 8192 tokens x 64 experts
+    runs the parts one after another in each workgroup; a single token runs them in 4
+    workgroups and adds the partial sums afterwards.  Both must give the same bits."""
+    wl = synth.Workload("split", T=8192, d=1024, inter=128, E=64, k=4, shared=False, bias=True,
+                        dtype=dtype, seed=31)
+    inp = synth.make_layer_inputs(wl, device="cuda")
+    say(f"case gate K-split {dtype}")
+    base = run_layer(inp, wl.k)
+    for t in (0, 4097, 8191):
+        one = dict(inp, x=inp["x"][t:t + 1].contiguous())
+        if inp["x_scale"] is not None:
+            one["x_scale"] = inp["x_scale"][t:t + 1].contiguous()
+        r = run_layer(one, wl.k)
+        assert torch.equal(r["ids"][0], base["ids"][t])
+        assert torch.equal(r["weights"][0], base["weights"][t])
+        assert torch.equal(r["y"][0], base["y"][t])
+    rows = np.array([0, 4097, 8191])
+    compare_rows(base, oracle_for_rows(inp, rows, wl.k), rows, dtype)

@@ -45,6 +45,19 @@ constexpr bool kGemmNtB = MOE_GEMM_NT_B != 0; // nontemporal weight loads
 #ifndef MOE_GEMM2_WN
 #define MOE_GEMM2_WN 4
 #endif
+// MXFP8 tile shape: wavefronts along M and N, 32-row B blocks per wavefront.
+#ifndef MOE_MX_WM
+#define MOE_MX_WM 2
+#endif
+#ifndef MOE_MX_WN
+#define MOE_MX_WN 2
+#endif
+#ifndef MOE_MX_FN
+#define MOE_MX_FN 2
+#endif
+#ifndef MOE_MX_WAVES
+#define MOE_MX_WAVES 1   // minimum wavefronts per SIMD the register allocation must allow
+#endif
 #ifndef MOE_GEMM_DMA
 #define MOE_GEMM_DMA 0
 #endif
@@ -54,10 +67,10 @@ constexpr bool kGemmNtB = MOE_GEMM_NT_B != 0; // nontemporal weight loads
 
 // Segment table: segment s < E is routed expert s (rows offsets[s]..offsets[s+1]-1),
 // segment E is the shared expert (rows T*k .. T*k+T-1).  mstart = exclusive prefix of
-// the per-segment tile-row counts.  Offsets are clamped into [0, T*k] and flagged if
+// the per-segment counts of tm-row tiles.  Offsets are clamped into [0, T*k] and flagged if
 // they are not a valid segmentation.
 __global__ __launch_bounds__(1024) void seg_table_kernel(const int32_t* __restrict__ offsets, int E,
-                                                         long long Tk, int T, int has_shared,
+                                                         long long Tk, int T, int has_shared, int tm,
                                                          int* __restrict__ mstart,
                                                          int* __restrict__ rowstart,
                                                          int* __restrict__ rowcount, int* flag) {
@@ -78,7 +91,7 @@ __global__ __launch_bounds__(1024) void seg_table_kernel(const int32_t* __restri
     }
     rowstart[s] = (int)a;
     rowcount[s] = (int)(b - a);
-    cnt[s] = (int)((b - a + BM - 1) / BM);
+    cnt[s] = (int)((b - a + tm - 1) / tm);
   }
   if (bad) raise_flag(flag, kFlagCorrupt);
   __syncthreads();
@@ -575,12 +588,49 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
   return sign | keep;                                // subnormal grid (keep == 8: 2^-6)
 }
 
-template <int MODE>
-__global__ __launch_bounds__(256) void grouped_gemm_mx_kernel(MxArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t sA[BM * MLDS];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[BNR * MLDS];
-  __shared__ uint32_t sAs[BM];
-  __shared__ uint32_t sBs[BNR];
+// Requantise one row's 32-feature MX block (this value and the 31 other lanes of the
+// half wavefront) and store code and scale: OCP MX scale 2^(floor(log2 amax) - 8).
+__device__ __forceinline__ void mx_store_h(float h, bool live, uint8_t* code, uint8_t* scale,
+                                           bool first) {
+  float amax = fabsf(h);
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  int se;
+  uint32_t scode;
+  if (amax == 0.0f) {
+    se = -127;
+    scode = 0;
+  } else if (!(amax <= 3.0e38f)) {
+    se = 0;
+    scode = 255;
+  } else {
+    se = min(max(ilogbf(amax) - 8, -127), 127);
+    scode = (uint32_t)(se + 127);
+  }
+  if (live) {
+    *code = (uint8_t)e4m3_rne_sat(ldexpf(h, -se));
+    if (first) *scale = (uint8_t)scode;
+  }
+}
+
+// Tile: (64 WM) rows x (32 FN WN) staged B rows, WM x WN wavefronts; each wavefront
+// owns 64 rows x 32 FN B rows as 2 x FN MFMA blocks.  K advances 128 bytes a step:
+// registers -> LDS (144-byte rows) -> two 64-wide MFMA steps, with the next step's
+// loads in flight.  GEMM1 (MODE 0): B rows alternate 32-row blocks of W1 and W3, so a
+// wavefront's blocks 2p and 2p + 1 are the W1 and W3 halves of 32 features.
+template <int MODE, int WM, int WN, int FN>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(MOE_MX_WAVES)))
+void grouped_gemm_mx_kernel(MxArgs g) {
+  constexpr int NTHR = 64 * WM * WN;
+  constexpr int TM = 64 * WM;                 // tile rows
+  constexpr int TB = 32 * FN * WN;            // staged B rows
+  constexpr int RSTEP = NTHR / 8;             // loader row stride (8 threads per 128-byte row)
+  constexpr int LA = TM / RSTEP, LB = TB / RSTEP;
+  static_assert(LA * RSTEP == TM && LB * RSTEP == TB && FN % 2 == 0, "tile shape");
+  __shared__ __attribute__((aligned(16))) uint8_t sA[TM * MLDS];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[TB * MLDS];
+  __shared__ uint32_t sAs[TM];
+  __shared__ uint32_t sBs[TB];
 
   const int total = g.mstart[g.S] * g.NT;
   const int per = (total + kXcds - 1) / kXcds;
@@ -599,22 +649,19 @@ __global__ __launch_bounds__(256) void grouped_gemm_mx_kernel(MxArgs g) {
   const int grp = local / (kGroupM * g.NT), rem = local % (kGroupM * g.NT);
   const int gm = min(kGroupM, mtiles - grp * kGroupM);
   const int nt = rem / gm, mt = grp * kGroupM + rem % gm;
-  const int row0 = g.rowstart[s] + mt * BM;
-  const int mrows = min(BM, g.rowcount[s] - mt * BM);
-  const int n0 = nt * (MODE == 0 ? 64 : 128);
+  const int row0 = g.rowstart[s] + mt * TM;
+  const int mrows = min(TM, g.rowcount[s] - mt * TM);
+  const int n0 = nt * (MODE == 0 ? TB / 2 : TB);
   const bool is_shared = (s == g.E);
+  const long long e = is_shared ? 0 : s;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int lr = tid >> 3, lc = (tid & 7) * 16;     // loader: rows lr + 32 i, 16-byte chunk lc
+  const int wm = wave / WN, wn = wave % WN;
+  const int lr = tid >> 3, lc = (tid & 7) * 16;     // loader: rows lr + RSTEP i, 16-byte chunk lc
   const int KB = g.K / 32;                           // scale bytes per row
 
-  const uint8_t* aptr[4];
-  const uint8_t* bptr[4];
-  int bad = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = lr + 32 * i;
+  // source row of A tile row r (rows past the segment re-read the tile's first row)
+  auto a_src = [&](int r, int& bad) -> long long {
     const long long jr = (long long)row0 + (r < mrows ? r : 0);
     long long src;
     if (MODE == 0) {
@@ -626,91 +673,97 @@ __global__ __launch_bounds__(256) void grouped_gemm_mx_kernel(MxArgs g) {
     } else {
       src = jr;
     }
-    aptr[i] = g.a + src * (long long)g.K + lc;
-    long long brow;
-    const uint8_t* bank;
+    return src;
+  };
+  // row (within expert e's matrix) of staged B row r, with its code and scale banks
+  auto b_row = [&](int r, const uint8_t*& bank, const uint8_t*& sbank) -> long long {
     if (MODE == 0) {
       const int blk = r >> 5, within = r & 31;
-      bank = (blk & 1) ? (is_shared ? g.sb1 : g.b1) : (is_shared ? g.sb0 : g.b0);
-      brow = (long long)n0 + (blk >> 1) * 32 + within;
-    } else {
-      bank = is_shared ? g.sb0 : g.b0;
-      brow = (long long)n0 + r;
+      const bool w3 = blk & 1;
+      bank = w3 ? (is_shared ? g.sb1 : g.b1) : (is_shared ? g.sb0 : g.b0);
+      sbank = w3 ? (is_shared ? g.sb1s : g.b1s) : (is_shared ? g.sb0s : g.b0s);
+      return (long long)n0 + (blk >> 1) * 32 + within;
     }
-    const long long e = is_shared ? 0 : s;
-    bptr[i] = bank + (e * g.N + brow) * (long long)g.K + lc;
+    bank = is_shared ? g.sb0 : g.b0;
+    sbank = is_shared ? g.sb0s : g.b0s;
+    return (long long)n0 + r;
+  };
+
+  int bad = 0;
+  const uint8_t* aptr[LA];
+  const uint8_t* bptr[LB];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) aptr[i] = g.a + a_src(lr + RSTEP * i, bad) * (long long)g.K + lc;
+#pragma unroll
+  for (int i = 0; i < LB; ++i) {
+    const uint8_t *bank, *sbank;
+    const long long br = b_row(lr + RSTEP * i, bank, sbank);
+    bptr[i] = bank + (e * g.N + br) * (long long)g.K + lc;
   }
-  // Scale rows: threads 0..127 stage A's scales (row tid), 128..255 B's (row tid-128).
-  const uint8_t* sptr;
-  {
-    const int r = tid & 127;
-    if (tid < 128) {
-      const long long jr = (long long)row0 + (r < mrows ? r : 0);
-      long long src;
-      if (MODE == 0) {
-        src = is_shared ? jr - g.Tk : (long long)(g.perm[jr] / g.k);
-        if (src < 0 || src >= g.T) src = 0;
-      } else {
-        src = jr;
-      }
-      sptr = g.as + src * (long long)KB;
+  // Scale rows: thread t < TM stages A row t's four scale bytes of the step, threads
+  // TM .. TM + TB - 1 those of B row t - TM (strided when there are fewer threads).
+  constexpr int NS = (TM + TB + NTHR - 1) / NTHR;
+  const uint8_t* sptr[NS];
+  bool sact[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int sr = tid + NTHR * i;
+    sact[i] = sr < TM + TB;
+    if (sr < TM) {
+      sptr[i] = g.as + a_src(sr, bad) * (long long)KB;
     } else {
-      long long brow;
-      const uint8_t* bank;
-      if (MODE == 0) {
-        const int blk = r >> 5, within = r & 31;
-        bank = (blk & 1) ? (is_shared ? g.sb1s : g.b1s) : (is_shared ? g.sb0s : g.b0s);
-        brow = (long long)n0 + (blk >> 1) * 32 + within;
-      } else {
-        bank = is_shared ? g.sb0s : g.b0s;
-        brow = (long long)n0 + r;
-      }
-      const long long e = is_shared ? 0 : s;
-      sptr = bank + (e * g.N + brow) * (long long)KB;
+      const uint8_t *bank, *sbank;
+      const long long br = b_row(sact[i] ? sr - TM : 0, bank, sbank);
+      sptr[i] = sbank + (e * g.N + br) * (long long)KB;
     }
   }
   if (bad) raise_flag(g.flag, kFlagCorrupt);
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[2][FN];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < FN; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
-  u32x4_t ra[4], rb[4];
-  uint32_t rs;
+  u32x4_t ra[LA], rb[LB];
+  uint32_t rs[NS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ra[i] = *(const u32x4_t*)(aptr[i]);
-    rb[i] = *(const u32x4_t*)(bptr[i]);
-  }
-  rs = *(const uint32_t*)(sptr);
+  for (int i = 0; i < LA; ++i) ra[i] = *(const u32x4_t*)(aptr[i]);
+#pragma unroll
+  for (int i = 0; i < LB; ++i) rb[i] = *(const u32x4_t*)(bptr[i]);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) rs[i] = sact[i] ? *(const uint32_t*)(sptr[i]) : 0u;
 
   for (int k0 = 0; k0 < g.K; k0 += MBK) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *(u32x4_t*)&sA[(lr + 32 * i) * MLDS + lc] = ra[i];
-      *(u32x4_t*)&sB[(lr + 32 * i) * MLDS + lc] = rb[i];
+    for (int i = 0; i < LA; ++i) *(u32x4_t*)&sA[(lr + RSTEP * i) * MLDS + lc] = ra[i];
+#pragma unroll
+    for (int i = 0; i < LB; ++i) *(u32x4_t*)&sB[(lr + RSTEP * i) * MLDS + lc] = rb[i];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int sr = tid + NTHR * i;
+      if (sr < TM) sAs[sr] = rs[i];
+      else if (sact[i]) sBs[sr - TM] = rs[i];
     }
-    if (tid < 128) sAs[tid] = rs; else sBs[tid - 128] = rs;
     __syncthreads();
     const int kn = k0 + MBK;
     if (kn < g.K) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ra[i] = *(const u32x4_t*)(aptr[i] + kn);
-        rb[i] = *(const u32x4_t*)(bptr[i] + kn);
-      }
-      rs = *(const uint32_t*)(sptr + kn / 32);
+      for (int i = 0; i < LA; ++i) ra[i] = *(const u32x4_t*)(aptr[i] + kn);
+#pragma unroll
+      for (int i = 0; i < LB; ++i) rb[i] = *(const u32x4_t*)(bptr[i] + kn);
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+        if (sact[i]) rs[i] = *(const uint32_t*)(sptr[i] + kn / 32);
     }
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int kc = sub * 64 + (lane >> 5) * 16;       // bytes 0..15; bytes 16..31 at kc + 32
       const int sh = 8 * (sub * 2 + (lane >> 5));       // scale byte of k-block (2 sub + half)
-      i32x8_t af[2], bf[2];
-      int sa[2], sb[2];
+      i32x8_t af[2], bf[FN];
+      int sa[2], sb[FN];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const int row = wm * 64 + mb * 32 + (lane & 31);
@@ -721,8 +774,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_mx_kernel(MxArgs g) {
         sa[mb] = (int)((sAs[row] >> sh) & 0xFFu);
       }
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int row = wn * 64 + nb * 32 + (lane & 31);
+      for (int nb = 0; nb < FN; ++nb) {
+        const int row = (wn * FN + nb) * 32 + (lane & 31);
         const u32x4_t u0 = *(const u32x4_t*)&sB[row * MLDS + kc];
         const u32x4_t u1 = *(const u32x4_t*)&sB[row * MLDS + kc + 32];
         bf[nb] = (i32x8_t){(int)u0[0], (int)u0[1], (int)u0[2], (int)u0[3],
@@ -732,13 +785,15 @@ __global__ __launch_bounds__(256) void grouped_gemm_mx_kernel(MxArgs g) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < FN; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               af[mb], bf[nb], acc[mb][nb], 0, 0, 0, sa[mb], 0, sb[nb]);
     }
     __syncthreads();
   }
 
+  // ---- epilogue.  Accumulator element v of a lane is C[i][j], j = lane % 32,
+  //      i = 8 (v / 4) + 4 (lane / 32) + v % 4. ----
   const int j = lane & 31;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
@@ -748,33 +803,19 @@ __global__ __launch_bounds__(256) void grouped_gemm_mx_kernel(MxArgs g) {
       const int r = wm * 64 + mb * 32 + i;
       const long long orow = (long long)row0 + r;
       if (MODE == 0) {
-        // One MX block = this row's 32 columns, spread over the 32 lanes of a half.
-        const float h = silu_f32(acc[mb][0][v]) * acc[mb][1][v];
-        float amax = fabsf(h);
+        // One MX block = this row's 32 features, spread over the 32 lanes of a half.
 #pragma unroll
-        for (int off = 1; off < 32; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-        int se;
-        uint32_t scode;
-        if (amax == 0.0f) {
-          se = -127;
-          scode = 0;
-        } else if (!(amax <= 3.0e38f)) {
-          se = 0;
-          scode = 255;
-        } else {
-          se = min(max(ilogbf(amax) - 8, -127), 127);
-          scode = (uint32_t)(se + 127);
-        }
-        if (r < mrows) {
-          const int col = n0 + wn * 32 + j;
-          ((uint8_t*)g.out)[orow * g.N + col] = (uint8_t)e4m3_rne_sat(ldexpf(h, -se));
-          if (j == 0) g.out_scale[orow * (g.N / 32) + col / 32] = (uint8_t)scode;
+        for (int p = 0; p < FN / 2; ++p) {
+          const float hv = silu_f32(acc[mb][2 * p][v]) * acc[mb][2 * p + 1][v];
+          const int col = n0 + (wn * FN / 2 + p) * 32 + j;
+          mx_store_h(hv, r < mrows, (uint8_t*)g.out + orow * g.N + col,
+                     g.out_scale + orow * (g.N / 32) + col / 32, j == 0);
         }
       } else {
         if (r < mrows) {
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            const int col = n0 + wn * 64 + nb * 32 + j;
+          for (int nb = 0; nb < FN; ++nb) {
+            const int col = n0 + (wn * FN + nb) * 32 + j;
             ((uint16_t*)g.out)[orow * g.N + col] = f32_to_bf16(acc[mb][nb][v]);
           }
         }
@@ -881,6 +922,7 @@ struct FfnPlan {
   uint8_t* hs;
   int S, has_shared;
   long long Tk, rows, mt_bound;
+  int tm;   // rows per GEMM tile (the segment table counts tiles of this height)
 };
 
 static FfnPlan plan_of(void* ws, int T, int E, int k, int inter, int dtype, bool has_shared) {
@@ -897,7 +939,8 @@ static FfnPlan plan_of(void* ws, int T, int E, int k, int inter, int dtype, bool
   p.S = E + p.has_shared;
   p.Tk = (long long)T * k;
   p.rows = p.Tk + (has_shared ? T : 0);
-  p.mt_bound = (p.Tk + (long long)E * (BM - 1)) / BM + (has_shared ? (T + BM - 1) / BM : 0);
+  p.tm = dtype == MOE_MXFP8 ? 64 * MOE_MX_WM : BM;
+  p.mt_bound = (p.Tk + (long long)E * (p.tm - 1)) / p.tm + (has_shared ? (T + p.tm - 1) / p.tm : 0);
   return p;
 }
 
@@ -938,7 +981,7 @@ static moe_status run_gate_up(const void* x, const uint8_t* xs, int dtype, int T
                               int k, int inter, const moe_expert_bank* routed,
                               const moe_expert_bank* shared, const int32_t* offsets,
                               const int32_t* perm, const FfnPlan& p, hipStream_t s) {
-  seg_table_kernel<<<1, 1024, 0, s>>>(offsets, E, p.Tk, T, p.has_shared, p.mstart, p.rowstart,
+  seg_table_kernel<<<1, 1024, 0, s>>>(offsets, E, p.Tk, T, p.has_shared, p.tm, p.mstart, p.rowstart,
                                       p.rowcount, p.flag);
   if (dtype == MOE_MXFP8) {
     MxArgs g{};
@@ -959,7 +1002,7 @@ static moe_status run_gate_up(const void* x, const uint8_t* xs, int dtype, int T
     g.sb1s = shared ? shared->w3_scale : nullptr;
     g.K = d;
     g.N = inter;
-    g.NT = inter / 64;
+    g.NT = inter / (16 * MOE_MX_FN * MOE_MX_WN);
     g.mstart = p.mstart;
     g.rowstart = p.rowstart;
     g.rowcount = p.rowcount;
@@ -969,7 +1012,8 @@ static moe_status run_gate_up(const void* x, const uint8_t* xs, int dtype, int T
     g.flag = p.flag;
     const long long grid = (p.mt_bound * g.NT + kXcds - 1) / kXcds * kXcds;
     if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
-    grouped_gemm_mx_kernel<0><<<(unsigned)grid, 256, 0, s>>>(g);
+    grouped_gemm_mx_kernel<0, MOE_MX_WM, MOE_MX_WN, MOE_MX_FN>
+        <<<(unsigned)grid, 64 * MOE_MX_WM * MOE_MX_WN, 0, s>>>(g);
   } else if (dtype == MOE_BF16) {
     GemmArgs g{};
     g.a = (const uint16_t*)x;
@@ -1042,16 +1086,23 @@ static moe_status run_down(int dtype, int T, int d, int E, int k, int inter,
     g.sb0s = shared ? shared->w2_scale : nullptr;
     g.K = inter;
     g.N = d;
-    g.NT = d / 128;
     g.mstart = p.mstart;
     g.rowstart = p.rowstart;
     g.rowcount = p.rowcount;
     g.S = p.S;
     g.out = out;
     g.flag = p.flag;
+    // the configured tile where its width divides d, else 64-column tiles of the same
+    // height (same bits: every output is the same MFMA chain)
+    const bool wide = d % (32 * MOE_MX_FN * MOE_MX_WN) == 0;
+    g.NT = wide ? d / (32 * MOE_MX_FN * MOE_MX_WN) : d / 64;
     const long long grid = (p.mt_bound * g.NT + kXcds - 1) / kXcds * kXcds;
     if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
-    grouped_gemm_mx_kernel<1><<<(unsigned)grid, 256, 0, s>>>(g);
+    if (wide)
+      grouped_gemm_mx_kernel<1, MOE_MX_WM, MOE_MX_WN, MOE_MX_FN>
+          <<<(unsigned)grid, 64 * MOE_MX_WM * MOE_MX_WN, 0, s>>>(g);
+    else
+      grouped_gemm_mx_kernel<1, MOE_MX_WM, 1, 2><<<(unsigned)grid, 64 * MOE_MX_WM, 0, s>>>(g);
   } else if (dtype == MOE_BF16) {
     GemmArgs g{};
     g.a = (const uint16_t*)p.h;

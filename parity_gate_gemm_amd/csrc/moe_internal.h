@@ -50,8 +50,28 @@ inline bool gate_split_launch(int T, int d, int E) {
   return gate_splits(d) > 1 && gate_tiles(T, E) < kGateSplitTiles;
 }
 
+// Candidate experts per token kept by the bf16 screen of the gate (more go to the
+// exact fallback).
+constexpr int kCandMax = 32;
+
+// K parts of the bf16 screen: enough workgroups (128 tokens x 128 experts x part) to
+// fill the chip; the screen has no fixed-order requirement.
+inline int screen_parts(int T, int d, int E) {
+  const int tiles = ((E + 127) / 128) * ((T + 127) / 128);
+  const int steps = d / 32;
+  if (tiles < 1 || steps < 1) return 1;
+  int nz = (512 + tiles - 1) / tiles;
+  if (nz > 16) nz = 16;
+  if (nz > steps / 4) nz = steps / 4;
+  if (nz < 1) nz = 1;
+  const int spart = (steps + nz - 1) / nz;
+  return (steps + spart - 1) / spart;
+}
+
 struct RouteWs {
-  size_t logits, tok_flag, xnorm, wnorm, part, xsq, wsq, bytes;
+  size_t logits, tok_flag, xnorm, wnorm, part, xsq, wsq;   // fp64 gate GEMM path
+  size_t wt, planes, cand, cval, ccount, screen, sxsq, pcnt, pairs;   // screened path
+  size_t bytes;
 };
 inline RouteWs route_ws(int T, int d, int E) {
   RouteWs w;
@@ -64,8 +84,26 @@ inline RouteWs route_ws(int T, int d, int E) {
   w.part = o;     o = align_up(o + S * T * E * sizeof(double), 256);
   w.xsq = o;      o = align_up(o + S * T * sizeof(double), 256);
   w.wsq = o;      o = align_up(o + S * E * sizeof(double), 256);
+  w.wt = o;       o = align_up(o + (size_t)E * d * sizeof(float), 256);
+  w.planes = o;   o = align_up(o + (size_t)3 * E * d * sizeof(uint16_t), 256);
+  w.cand = o;     o = align_up(o + (size_t)T * kCandMax * sizeof(int32_t), 256);
+  w.cval = o;     o = align_up(o + (size_t)T * kCandMax * sizeof(double), 256);
+  w.ccount = o;   o = align_up(o + (size_t)T * sizeof(int), 256);
+  const size_t nz = d % 32 == 0 ? (size_t)screen_parts(T, d, E) : 1;
+  w.screen = o;   o = align_up(o + nz * T * E * sizeof(double), 256);
+  w.sxsq = o;     o = align_up(o + nz * T * sizeof(double), 256);
+  w.pcnt = o;     o = align_up(o + (size_t)(2 * E + 1) * sizeof(int), 256);
+  w.pairs = o;    o = align_up(o + (size_t)T * kCandMax * sizeof(int32_t), 256);
   w.bytes = o;
   return w;
+}
+
+// bf16 and MXFP8 activations with d % 32 == 0 take their weights (and, under
+// replay, everything) from per-pair fp64 logits; the ids come from the bf16 screen
+// for large batches and from the fp64 gate GEMM for small ones (gate_split_launch).
+// fp32 activations use the fp64 gate GEMM for ids and weights.
+inline bool gate_screened(int dtype, int d) {
+  return (dtype == MOE_BF16 || dtype == MOE_MXFP8) && d % 32 == 0;
 }
 
 struct DispatchWs {
@@ -135,18 +173,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 // OCP FP8 E4M3 code -> exact value (as double; every E4M3 value is exact in fp32 too).
+// Normal codes (exponent field e > 0) are (1 + m/8) 2^(e-7): the fp64 bit pattern is
+// built directly (biased exponent e + 1016, the 3 mantissa bits at the top of the
+// fraction).  Subnormal codes are m 2^-9.  Exponent 15 with mantissa 7 is NaN.
 __device__ __forceinline__ double e4m3_to_f64(uint8_t c) {
-  int s = c >> 7, e = (c >> 3) & 0xF, m = c & 7;
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
   double v;
-  if (e == 0xF && m == 7) v = __builtin_nan("");
-  else if (e == 0) v = ldexp((double)m, -9);
-  else v = ldexp((double)(8 + m), e - 10);
-  return s ? -v : v;
+  if (e == 15u && m == 7u) v = __builtin_nan("");
+  else if (e == 0u) v = (double)m * 0x1p-9;
+  else v = __hiloint2double((int)(((e + 1016u) << 20) | (m << 17)), 0);
+  return (c & 0x80u) ? -v : v;
 }
 
-// E8M0 scale code -> 2^(code-127) (255 is NaN).
+// E8M0 scale code -> 2^(code-127) (255 is NaN); every such power is a normal double.
 __device__ __forceinline__ double e8m0_to_f64(uint8_t c) {
-  return c == 255 ? __builtin_nan("") : ldexp(1.0, (int)c - 127);
+  return c == 255 ? __builtin_nan("") : __hiloint2double((int)((uint32_t)(c + 896) << 20), 0);
 }
 
 // Exact value of element i of activation row `row` (length d) in `dtype`.
@@ -157,5 +198,21 @@ __device__ __forceinline__ double load_act_f64(const void* x, const uint8_t* xs,
   if (dtype == MOE_BF16) return (double)bf16_to_f32(((const uint16_t*)x)[idx]);
   return e4m3_to_f64(((const uint8_t*)x)[idx]) * e8m0_to_f64(xs[row * (size_t)(d / 32) + i / 32]);
 }
+
+// Screened gate (screen.hip).  screen_route_select leaves ids for every token and
+// tok_flag 1 for the tokens the exact fallback must decide; screen_route_weights then
+// writes the weights of the final ids.
+moe_status screen_route_select(const void* x, const uint8_t* xs, int dtype, int T, int d,
+                               const float* w_gate, const float* bias, int E, int k, int32_t* ids,
+                               char* ws, hipStream_t s);
+moe_status screen_route_weights(const void* x, const uint8_t* xs, int dtype, int T, int d,
+                                const float* bias, int E, int k, const int32_t* ids,
+                                const float* weights_in, float* weights, char* ws, hipStream_t s);
+moe_status chosen_ids_refine(const void* x, const uint8_t* xs, int dtype, int T, int d,
+                             const float* w_gate, const float* bias, int E, int k, const int32_t* ids,
+                             char* ws, hipStream_t s);
+moe_status screen_replay(const void* x, const uint8_t* xs, int dtype, int T, int d,
+                         const float* w_gate, const float* bias, int E, int k, const int32_t* ids_in,
+                         const float* weights_in, float* weights_out, char* ws, hipStream_t s);
 
 }  // namespace moe

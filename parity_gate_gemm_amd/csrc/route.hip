@@ -701,7 +701,7 @@ __global__ __launch_bounds__(256) void exact_fallback_kernel(
     const float* __restrict__ wg, const float* __restrict__ bias, int E, int k,
     const int* __restrict__ tok_flag, int32_t* __restrict__ ids, int* flag) {
   const int t = blockIdx.x;
-  if (t >= T || tok_flag[t] == 0) return;
+  if (t >= T || tok_flag[t] != 1) return;
   __shared__ double ex[kMaxExperts];
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     Expansion acc;
@@ -873,12 +873,24 @@ extern "C" moe_status moe_route(const void* x, const uint8_t* x_scale, int dtype
   char* w = (char*)ws;
   int* flag = (int*)w;
   const RouteWs L = route_ws(T, d, E);
+  if (gate_screened(dtype, d) && !gate_split_launch(T, d, E)) {
+    if ((st = screen_route_select(x, x_scale, dtype, T, d, w_gate, bias, E, k, ids, w, s)) != MOE_OK)
+      return st;
+    exact_fallback_kernel<<<T, 256, 0, s>>>(x, x_scale, dtype, T, d, w_gate, bias, E, k,
+                                            (const int*)(w + L.tok_flag), ids, flag);
+    return screen_route_weights(x, x_scale, dtype, T, d, bias, E, k, ids, nullptr, weights, w, s);
+  }
   if ((st = launch_gate(x, x_scale, dtype, T, d, w_gate, bias, E, w, s)) != MOE_OK) return st;
   select_topk_kernel<<<(T + SEL_WAVES - 1) / SEL_WAVES, 256, 0, s>>>(
       (const double*)(w + L.logits), (const double*)(w + L.xnorm), (const double*)(w + L.wnorm),
       bias, T, E, k, two_gamma(d), ids, (int*)(w + L.tok_flag), flag);
   exact_fallback_kernel<<<T, 256, 0, s>>>(x, x_scale, dtype, T, d, w_gate, bias, E, k,
                                           (const int*)(w + L.tok_flag), ids, flag);
+  if (gate_screened(dtype, d)) {   // weights from the per-pair fp64 logits, as for large batches
+    if ((st = chosen_ids_refine(x, x_scale, dtype, T, d, w_gate, bias, E, k, ids, w, s)) != MOE_OK)
+      return st;
+    return screen_route_weights(x, x_scale, dtype, T, d, bias, E, k, ids, nullptr, weights, w, s);
+  }
   route_weights_kernel<<<(T + 255) / 256, 256, 0, s>>>((const double*)(w + L.logits), T, E, k, ids,
                                                        weights);
   return launch_status();
@@ -893,6 +905,9 @@ extern "C" moe_status moe_route_replay(const void* x, const uint8_t* x_scale, in
   if (!ids_in || !weights_out) return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
+  if (gate_screened(dtype, d))
+    return screen_replay(x, x_scale, dtype, T, d, w_gate, bias, E, k, ids_in, weights_in, weights_out,
+                         w, s);
   const RouteWs L = route_ws(T, d, E);
   if ((st = launch_gate(x, x_scale, dtype, T, d, w_gate, bias, E, w, s)) != MOE_OK) return st;
   replay_kernel<<<(T + SEL_WAVES - 1) / SEL_WAVES, 256, 0, s>>>(

@@ -1,0 +1,877 @@
+// Two-tier gate for bf16 and MXFP8 activations: a bf16 matrix-core screen with a
+// rigorous error bound picks, per token, the experts that can still be among the top
+// k; only those get fp64 logits, which decide the selection (with the fp64 bound, and
+// the exact fallback for what that bound cannot separate) and give the weights.
+//
+// The gate picks the top-k experts per token (Training Data podcast page "How Cursor
+// Trained Composer on Fireworks", section on floating point and MoE: 8 of 384 experts
+// per layer, and a fifth-decimal difference in the hidden state can flip the choice),
+// so the selection has to equal the one made on the exact logits.
+//
+// Screen: Wg is split exactly into three bf16 planes, w = hi + mid + lo.  For each
+// chunk of the reduction (64 elements for bf16 x, one 32-element MX block for MXFP8
+// x) v_mfma_f32_32x32x16_bf16 sums x * plane in fp32 from zero, and the chunk sums are
+// added in fp64 (times the chunk's E8M0 scale for MXFP8).  Every product of two bf16
+// values is exact in fp32; a chunk sum of m = 3 * chunk products has at most m
+// rounded additions, so with u = 2^-23 (which also covers truncating adders)
+//   |screen - exact| <= gamma_m(u) * (1 + 2^-6) * ||x_t|| ||w_e||
+//                       + gamma_{d+1}(2^-53) * (||x_t|| ||w_e|| + |b_e|) + flush term,
+// doubled for safety (the flush term covers fp32 results below 2^-126 flushed to zero).
+// Every expert whose screen interval reaches the k-th largest lower bound is a
+// candidate; any other expert's exact logit lies below k candidates' exact logits.
+#include <math.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// Gate weights, transposed: wt [E][d] fp32 (for the fp64 logits) and, when `planes`
+// is given, the exact three-way bf16 split planes [3][E][d] (hi, mid, lo).
+// hi = RNE(w); w - hi is exact in fp32 with at most 16 significant bits, mid = RNE of
+// it, and the rest has at most 8 bits, so lo holds it exactly (w below 2^-110 aside,
+// whose parts can fall under bf16's subnormal grid: the flush term covers them).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gate_prep_kernel(const float* __restrict__ wg, int d, int E,
+                                                        float* __restrict__ wt,
+                                                        uint16_t* __restrict__ planes) {
+  __shared__ float tile[64][65];
+  const int k0 = blockIdx.x * 64, e0 = blockIdx.y * 64, tid = threadIdx.x;
+  for (int q = tid; q < 64 * 64; q += 256) {
+    const int kr = q / 64, ec = q % 64;
+    const int k = k0 + kr, e = e0 + ec;
+    tile[kr][ec] = (k < d && e < E) ? wg[(size_t)k * E + e] : 0.0f;
+  }
+  __syncthreads();
+  const size_t plane = (size_t)E * d;
+  for (int q = tid; q < 64 * 64; q += 256) {
+    const int er = q / 64, kc = q % 64;
+    const int k = k0 + kc, e = e0 + er;
+    if (k < d && e < E) {
+      const float w = tile[kc][er];
+      const size_t o = (size_t)e * d + k;
+      wt[o] = w;
+      if (planes) {
+        const uint16_t hi = f32_to_bf16(w);
+        const float r1 = w - bf16_to_f32(hi);
+        const uint16_t mid = f32_to_bf16(r1);
+        const float r2 = r1 - bf16_to_f32(mid);
+        planes[o] = hi;
+        planes[plane + o] = mid;
+        planes[2 * plane + o] = f32_to_bf16(r2);
+      }
+    }
+  }
+}
+
+// ||w_e||_2 in fp64, one workgroup per expert (thread-strided sums, then a fixed
+// tree over the 256 threads).
+__global__ __launch_bounds__(256) void gate_wnorm_kernel(const float* __restrict__ wt, int d, int E,
+                                                         double* __restrict__ wnorm) {
+  __shared__ double part[256];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  const float* row = wt + (size_t)e * d;
+  double acc = 0.0;
+  for (int i = tid; i < d; i += 256) {
+    const double v = (double)row[i];
+    acc = fma(v, v, acc);
+  }
+  part[tid] = acc;
+  __syncthreads();
+  for (int h = 128; h >= 1; h >>= 1) {
+    if (tid < h) part[tid] += part[tid + h];
+    __syncthreads();
+  }
+  if (tid == 0) wnorm[e] = sqrt(part[0]);
+}
+
+// E4M3 code -> bf16 bits of the same value (every E4M3 value is a bf16 value).
+__device__ __forceinline__ uint16_t e4m3_to_bf16_bits(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  uint32_t b;
+  if (e == 15u && m == 7u) b = 0x7FC0u;                                    // NaN
+  else if (e == 0u) b = __float_as_uint((float)m * 0x1p-9f) >> 16;         // subnormal grid
+  else b = ((e + 120u) << 7) | (m << 4);
+  return (uint16_t)(b | ((c & 0x80u) << 8));
+}
+
+// ---------------------------------------------------------------------------
+// Screen GEMM.  Workgroup tile: 128 experts x 128 tokens; 8 wavefronts, wavefront
+// (we, wt) owns experts 64 we .. +63 (two 32-row A blocks, one per plane triple) and
+// tokens 32 wt .. +31 (one 32-column B block).  The experts are the MFMA's rows, so a
+// lane's 16 accumulator values all belong to one token (column lane % 32) and the
+// token's MX scale is one value per lane.  K advances 32 per step through LDS (80-byte
+// rows) with the next step's loads in registers.
+// The K steps are cut into gridDim.z parts of `spart` steps (more workgroups for small
+// batches; the screen needs no fixed summation order, only its bound, which holds for
+// any grouping of the chunk sums).  Output: partial sums s[z][t][e] (fp64, without the
+// bias); the first expert tile also writes the partial squared norms xsq[z][t].
+// ---------------------------------------------------------------------------
+constexpr int SC_E = 128, SC_T = 128, SC_K = 32, SC_LDS = SC_K + 8, SC_THR = 512;
+
+template <int DT>
+__global__ __launch_bounds__(SC_THR) void gate_screen_kernel(const void* __restrict__ x,
+                                                          const uint8_t* __restrict__ xs, int T,
+                                                          int d, int E, int spart,
+                                                          const uint16_t* __restrict__ planes,
+                                                          double* __restrict__ s,
+                                                          double* __restrict__ xsqp) {
+  constexpr int CH = DT == MOE_BF16 ? 2 : 1;   // K steps per fp32 chunk
+  __shared__ __attribute__((aligned(16))) uint16_t sW[3][SC_E][SC_LDS];
+  __shared__ __attribute__((aligned(16))) uint16_t sX[SC_T][SC_LDS];
+  __shared__ double sS[SC_T];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int we = wave >> 2, wt = wave & 3;
+  const int e0 = blockIdx.x * SC_E, t0 = blockIdx.y * SC_T;
+  const size_t plane = (size_t)E * d;
+
+  // loader: plane chunks q = tid + 512 i: plane q / 512, row (q % 512) / 4, k (q % 4) * 8
+  constexpr int NW = 3 * SC_E * SC_K / 8 / SC_THR;
+  const uint16_t* wp[NW];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int q = tid + SC_THR * i, p = q / 512, r = (q % 512) / 4, c = (q % 4) * 8;
+    const int e = e0 + r < E ? e0 + r : 0;
+    wp[i] = planes + p * plane + (size_t)e * d + c;
+  }
+  const int xr = DT == MOE_BF16 ? tid / 4 : tid / 2;
+  const int xc = DT == MOE_BF16 ? (tid % 4) * 8 : (tid % 2) * 16;
+  const int xt = t0 + xr < T ? t0 + xr : 0;
+  const bool xload = DT == MOE_BF16 || tid < 2 * SC_T;
+  const int nb32 = d / 32;
+
+  u32x4_t rw[NW], rx = {0, 0, 0, 0};
+  uint32_t rsc = 0;
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) rw[i] = *(const u32x4_t*)(wp[i] + k0);
+    if (DT == MOE_BF16) {
+      rx = *(const u32x4_t*)((const uint16_t*)x + (size_t)xt * d + k0 + xc);
+    } else {
+      if (xload) rx = *(const u32x4_t*)((const uint8_t*)x + (size_t)xt * d + k0 + xc);
+      if (tid < SC_T) rsc = xs[(size_t)(t0 + tid < T ? t0 + tid : 0) * nb32 + k0 / 32];
+    }
+  };
+
+  f32x16_t acc32[2];
+  double acc64[2][16];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      acc32[mb][v] = 0.0f;
+      acc64[mb][v] = 0.0;
+    }
+  const bool do_xn = blockIdx.x == 0 && we == 0;
+  double xsq = 0.0, csq = 0.0;    // csq: this chunk's sum of squared (unscaled) activations
+
+  const int st0 = blockIdx.z * spart;
+  const int nsteps = min(d / SC_K - st0, spart);
+  gload(st0 * SC_K);
+  for (int st = 0; st < nsteps; ++st) {
+    // registers -> LDS
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const int q = tid + SC_THR * i, p = q / 512, r = (q % 512) / 4, c = (q % 4) * 8;
+      *(u32x4_t*)&sW[p][r][c] = rw[i];
+    }
+    if (DT == MOE_BF16) {
+      *(u32x4_t*)&sX[xr][xc] = rx;
+    } else {
+      if (xload) {
+        uint16_t b[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) b[q] = e4m3_to_bf16_bits((rx[q >> 2] >> (8 * (q & 3))) & 0xFFu);
+        u32x4_t lo, hi;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          lo[q] = (uint32_t)b[2 * q] | ((uint32_t)b[2 * q + 1] << 16);
+          hi[q] = (uint32_t)b[8 + 2 * q] | ((uint32_t)b[8 + 2 * q + 1] << 16);
+        }
+        *(u32x4_t*)&sX[xr][xc] = lo;
+        *(u32x4_t*)&sX[xr][xc + 8] = hi;
+      }
+      if (tid < SC_T) sS[tid] = e8m0_to_f64((uint8_t)rsc);
+    }
+    __syncthreads();
+    if (st + 1 < nsteps) gload((st0 + st + 1) * SC_K);
+
+#pragma unroll
+    for (int kk = 0; kk < SC_K; kk += 16) {
+      const int kc = kk + 8 * (lane >> 5);
+      const bf16x8_t bx = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)&sX[wt * 32 + (lane & 31)][kc]);
+      if (do_xn) {
+        const u32x4_t u = __builtin_bit_cast(u32x4_t, bx);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const double v = (double)__uint_as_float((q & 1) ? (u[q >> 1] & 0xffff0000u) : (u[q >> 1] << 16));
+          csq = fma(v, v, csq);
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const bf16x8_t aw =
+              __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)&sW[p][we * 64 + mb * 32 + (lane & 31)][kc]);
+          acc32[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, bx, acc32[mb], 0, 0, 0);
+        }
+    }
+    if ((st + 1) % CH == 0 || st + 1 == nsteps) {   // end of a chunk: fold into fp64
+      const double sc = DT == MOE_BF16 ? 1.0 : sS[wt * 32 + (lane & 31)];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          acc64[mb][v] = fma((double)acc32[mb][v], sc, acc64[mb][v]);
+          acc32[mb][v] = 0.0f;
+        }
+      if (do_xn) {
+        xsq = fma(csq, sc * sc, xsq);
+        csq = 0.0;
+      }
+    }
+    __syncthreads();
+  }
+
+  // outputs: accumulator element v is expert row 8 (v / 4) + 4 (lane / 32) + v % 4 of
+  // the block, token column lane % 32
+  const int t = t0 + wt * 32 + (lane & 31);
+  double* sz = s + (size_t)blockIdx.z * T * E;
+  if (t < T) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int e = e0 + we * 64 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (e < E) sz[(size_t)t * E + e] = acc64[mb][v];
+      }
+  }
+  if (do_xn) {
+    const double v = xsq + __shfl_xor(xsq, 32);
+    if (lane < 32 && t < T) xsqp[(size_t)blockIdx.z * T + t] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp64 logit x_t . w_e, computed by one whole wavefront: lane l accumulates elements
+// 8 l + 512 j .. +7 (j ascending) with fma, then a fixed butterfly adds the lanes.
+// Every product is exact in fp64, so each term is rounded once.  The same function
+// serves the learned path, router replay and the weights, so their values agree bit
+// for bit.  Requires d % 8 == 0.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void wave_dot_xload(const void* __restrict__ x, const uint8_t* __restrict__ xs,
+                                               int dtype, int t, int d, int i0, double (&xv)[8]) {
+  if (dtype == MOE_BF16) {
+    const u32x4_t u = *(const u32x4_t*)((const uint16_t*)x + (size_t)t * d + i0);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      xv[q] = (double)__uint_as_float((q & 1) ? (u[q >> 1] & 0xffff0000u) : (u[q >> 1] << 16));
+  } else {
+    const u32x2_t u = *(const u32x2_t*)((const uint8_t*)x + (size_t)t * d + i0);
+    const double sc = e8m0_to_f64(xs[(size_t)t * (d / 32) + i0 / 32]);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) xv[q] = e4m3_to_f64((uint8_t)(u[q >> 2] >> (8 * (q & 3)))) * sc;
+  }
+}
+
+__device__ __forceinline__ void wave_dot_load(const void* __restrict__ x, const uint8_t* __restrict__ xs,
+                                              int dtype, int t, int d, const float* __restrict__ w,
+                                              int i0, double (&xv)[8], float (&wv)[8]) {
+  wave_dot_xload(x, xs, dtype, t, d, i0, xv);
+  const float4 w0 = *(const float4*)(w + i0), w1 = *(const float4*)(w + i0 + 4);
+  wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w;
+  wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
+}
+
+__device__ double wave_dot(const void* __restrict__ x, const uint8_t* __restrict__ xs, int dtype,
+                           int t, int d, const float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  double acc = 0.0;
+  int i0 = 8 * lane;
+  for (; i0 + 512 < d; i0 += 1024) {     // two iterations' loads issued before their fmas
+    double xa[8], xb[8];
+    float wa[8], wb[8];
+    wave_dot_load(x, xs, dtype, t, d, w, i0, xa, wa);
+    wave_dot_load(x, xs, dtype, t, d, w, i0 + 512, xb, wb);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc = fma(xa[q], (double)wa[q], acc);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc = fma(xb[q], (double)wb[q], acc);
+  }
+  if (i0 < d) {
+    double xa[8];
+    float wa[8];
+    wave_dot_load(x, xs, dtype, t, d, w, i0, xa, wa);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc = fma(xa[q], (double)wa[q], acc);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  return acc;
+}
+
+// Adds the K parts of the screen (into part 0) and of the squared norms.
+__global__ __launch_bounds__(256) void screen_reduce_kernel(double* __restrict__ s,
+                                                            double* __restrict__ xsqp, int T, int E,
+                                                            int nz) {
+  const size_t n = (size_t)T * E;
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    double v = s[i];
+    for (int z = 1; z < nz; ++z) v += s[(size_t)z * n + i];
+    s[i] = v;
+  }
+  if (i < (size_t)T) {
+    double v = xsqp[i];
+    for (int z = 1; z < nz; ++z) v += xsqp[(size_t)z * T + i];
+    xsqp[i] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Candidates, one wavefront per token: lower/upper screen bounds (bias added in
+// fp64), L = k-th largest lower bound, candidates = experts whose upper bound reaches
+// L, listed in ascending expert order.  tok_flag: 0 candidates listed, 1 more than
+// kCandMax candidates (exact fallback), 2 non-finite screen value (flagged; ids 0..k-1).
+// ---------------------------------------------------------------------------
+template <int CD_NV>   // experts per lane (E <= 64 CD_NV)
+__global__ __launch_bounds__(256) void screen_cand_kernel(
+    const double* __restrict__ s, int nz, const double* __restrict__ xsqp, double* __restrict__ xnorm,
+    const double* __restrict__ wnorm, const float* __restrict__ bias, const uint8_t* __restrict__ xs,
+    int dtype, int T, int d, int E, int k, double cs, double tg, double ca,
+    int32_t* __restrict__ cand, int* __restrict__ ccount, int* __restrict__ tok_flag,
+    int32_t* __restrict__ ids, int* flag) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  // flush term scale: the token's largest MX block scale (1 for bf16)
+  double sfac = 1.0;
+  if (dtype == MOE_MXFP8) {
+    int m = 0;
+    for (int b = lane; b < d / 32; b += 64) m = max(m, (int)xs[(size_t)t * (d / 32) + b]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = max(m, __shfl_xor(m, off));
+    sfac = ldexp(1.0, m - 127);
+  }
+  double xq = xsqp[t];
+  for (int z = 1; z < nz; ++z) xq += xsqp[(size_t)z * T + t];
+  const double xn = sqrt(xq);
+  if (lane == 0) xnorm[t] = xn;
+  double lo[CD_NV], up[CD_NV];
+  bool finite = isfinite(xn);
+#pragma unroll
+  for (int i = 0; i < CD_NV; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) {
+      const double b = bias ? (double)bias[e] : 0.0;
+      double sv = s[(size_t)t * E + e];
+      for (int z = 1; z < nz; ++z) sv += s[((size_t)z * T + t) * E + e];
+      const double v = sv + b;
+      const double bnd = cs * xn * wnorm[e] + tg * fabs(b) + ca * sfac;
+      finite = finite && isfinite(v) && isfinite(bnd);
+      lo[i] = v - bnd;
+      up[i] = v + bnd;
+    } else {
+      lo[i] = -INFINITY;
+      up[i] = -INFINITY;
+    }
+  }
+  if (!__all(finite)) {
+    if (lane == 0) {
+      raise_flag(flag, kFlagNonFinite);
+      tok_flag[t] = 2;
+      ccount[t] = 0;
+    }
+    for (int r = lane; r < k; r += 64) ids[(size_t)t * k + r] = r;
+    return;
+  }
+  // L: the k-th largest lower bound (k rounds of a wave-wide maximum, one removal each)
+  uint32_t taken = 0;
+  double L = -INFINITY;
+  for (int r = 0; r < k; ++r) {
+    double bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < CD_NV; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E && !((taken >> i) & 1u) && (lo[i] > bv || (lo[i] == bv && e < bi))) {
+        bv = lo[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (lane == (bi & 63)) taken |= 1u << (bi >> 6);
+    L = bv;
+  }
+  int m = 0;
+  uint64_t masks[CD_NV];
+#pragma unroll
+  for (int i = 0; i < CD_NV; ++i) {
+    masks[i] = __ballot(lane + 64 * i < E && up[i] >= L);
+    m += __popcll(masks[i]);
+  }
+  if (m > kCandMax) {
+    if (lane == 0) {
+      tok_flag[t] = 1;
+      ccount[t] = 0;
+    }
+    return;
+  }
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < CD_NV; ++i) {
+    if ((masks[i] >> lane) & 1u) {
+      const int pos = base + __popcll(masks[i] & ((1ull << lane) - 1ull));
+      cand[(size_t)t * kCandMax + pos] = lane + 64 * i;
+    }
+    base += __popcll(masks[i]);
+  }
+  if (lane == 0) {
+    ccount[t] = m;
+    tok_flag[t] = 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp64 logits of the candidates: workgroup (expert e, 64 tokens) gathers the tokens
+// whose candidate list holds e and gives each (token, slot) pair to one wavefront.
+// cval[t][j] = wave_dot(x_t, w_e) + b_e.
+// ---------------------------------------------------------------------------
+// Candidate pairs grouped by expert: per-expert counts, their exclusive scan, then
+// each (token, slot) pair placed in its expert's range (the order inside a range is
+// whatever the atomics give; every pair's value is computed on its own, so the results
+// do not depend on it).
+__global__ __launch_bounds__(1024) void pair_clear_kernel(int* __restrict__ cnt, int E) {
+  for (int e = threadIdx.x; e < 2 * E + 1; e += blockDim.x) cnt[e] = 0;
+}
+
+// Counts in LDS per workgroup of 256 tokens, one global atomic per touched expert.
+__global__ __launch_bounds__(256) void pair_count_kernel(const int32_t* __restrict__ cand,
+                                                         const int* __restrict__ ccount, int T, int E,
+                                                         int* __restrict__ cnt) {
+  __shared__ int h[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) h[e] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < T) {
+    const int m = ccount[t];
+    for (int j = 0; j < m; ++j) atomicAdd(&h[cand[(size_t)t * kCandMax + j]], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    if (h[e]) atomicAdd(&cnt[e], h[e]);
+}
+
+// cnt[0..E): counts -> start[0..E] (exclusive scan, written to cnt + E), cursors zeroed.
+__global__ __launch_bounds__(1024) void pair_scan_kernel(int* __restrict__ cnt, int E) {
+  __shared__ int c[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) c[e] = cnt[e];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int e = 0; e < E; ++e) {
+      cnt[E + e] = run;
+      run += c[e];
+    }
+    cnt[2 * E] = run;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;   // now the placement cursors
+}
+
+// Each workgroup reserves one range per touched expert, then fills it from LDS cursors.
+__global__ __launch_bounds__(256) void pair_place_kernel(const int32_t* __restrict__ cand,
+                                                         const int* __restrict__ ccount, int T, int E,
+                                                         int* __restrict__ cnt,
+                                                         int32_t* __restrict__ pairs) {
+  __shared__ int h[kMaxExperts];
+  __shared__ int base[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) h[e] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const int m = t < T ? ccount[t] : 0;
+  for (int j = 0; j < m; ++j) atomicAdd(&h[cand[(size_t)t * kCandMax + j]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    base[e] = h[e] ? cnt[E + e] + atomicAdd(&cnt[e], h[e]) : 0;
+    h[e] = 0;
+  }
+  __syncthreads();
+  for (int j = 0; j < m; ++j) {
+    const int e = cand[(size_t)t * kCandMax + j];
+    pairs[base[e] + atomicAdd(&h[e], 1)] = t * kCandMax + j;
+  }
+}
+
+// Chunks of RF_P consecutive pairs (expert order; 8 to 64 by batch size) per
+// workgroup, one wavefront per pair; the gate column of the chunk's first expert is staged in LDS (when it fits) and
+// read from there by every pair of that expert.
+constexpr int RF_W = 8, RF_LDS_MAX = 16384;
+
+// wave_dot with w in LDS: the same fma sequence (lane-strided blocks of 8, ascending,
+// then the same butterfly) as wave_dot, hence the same bits; activation loads run up
+// to 4 blocks ahead.
+__device__ double wave_dot_lds(const void* __restrict__ x, const uint8_t* __restrict__ xs, int dtype,
+                               int t, int d, const float* w) {
+  const int lane = threadIdx.x & 63;
+  double acc = 0.0;
+  int i0 = 8 * lane;
+  for (; i0 + 3 * 512 < d; i0 += 4 * 512) {
+    double xa[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) wave_dot_xload(x, xs, dtype, t, d, i0 + 512 * u, xa[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float4 w0 = *(const float4*)(w + i0 + 512 * u), w1 = *(const float4*)(w + i0 + 512 * u + 4);
+      const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc = fma(xa[u][q], (double)wv[q], acc);
+    }
+  }
+  for (; i0 < d; i0 += 512) {
+    double xa[8];
+    wave_dot_xload(x, xs, dtype, t, d, i0, xa);
+    const float4 w0 = *(const float4*)(w + i0), w1 = *(const float4*)(w + i0 + 4);
+    const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc = fma(xa[q], (double)wv[q], acc);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  return acc;
+}
+
+__global__ __launch_bounds__(64 * RF_W) void screen_refine_kernel(
+    const void* __restrict__ x, const uint8_t* __restrict__ xs, int dtype, int T, int d,
+    const float* __restrict__ wt, const float* __restrict__ bias, const int32_t* __restrict__ cand,
+    const int32_t* __restrict__ pairs, const int* __restrict__ cnt, int E, int RF_P,
+    double* __restrict__ cval) {
+  extern __shared__ __attribute__((aligned(16))) float wl[];   // d floats when d <= RF_LDS_MAX
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int np = cnt[2 * E];
+  const bool stage = d <= RF_LDS_MAX;
+  for (int c0 = blockIdx.x * RF_P; c0 < np; c0 += gridDim.x * RF_P) {
+    const int es = cand[pairs[c0]];
+    if (stage) {
+      __syncthreads();   // the previous chunk's readers are done
+      const float* src = wt + (size_t)es * d;
+      for (int i = 4 * threadIdx.x; i < d; i += 4 * 64 * RF_W) *(float4*)(wl + i) = *(const float4*)(src + i);
+      __syncthreads();
+    }
+    const int cend = min(c0 + RF_P, np);
+    for (int p = c0 + wave; p < cend; p += RF_W) {
+      const int tj = pairs[p];
+      const int t = tj / kCandMax;
+      const int e = cand[tj];
+      const double v = (stage && e == es) ? wave_dot_lds(x, xs, dtype, t, d, wl)
+                                          : wave_dot(x, xs, dtype, t, d, wt + (size_t)e * d);
+      if (lane == 0) cval[tj] = bias ? v + (double)bias[e] : v;
+    }
+  }
+}
+
+__device__ __forceinline__ bool sc_ranks_before(double av, int ae, double bv, int be) {
+  return av > bv || (av == bv && ae < be);
+}
+
+// ---------------------------------------------------------------------------
+// Selection among the candidates, one wavefront per token: k rounds of a wave-wide
+// arg-max on (fp64 logit desc, expert asc); certified when every adjacent pair of the
+// top k, and rank k-1 against the best remaining candidate, stay ordered after
+// widening each logit by its fp64 bound tg (||x|| ||w_e|| + |b_e|), with the relative
+// margin 2^-45 that keeps the exact values more than an ulp apart.  Experts outside
+// the candidate list are below k candidates by the screen bound.  Uncertified tokens
+// get tok_flag 1 (exact fallback).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void screen_select_kernel(
+    const int32_t* __restrict__ cand, const int* __restrict__ ccount, const double* __restrict__ cval,
+    const double* __restrict__ xnorm, const double* __restrict__ wnorm,
+    const float* __restrict__ bias, int T, int k, double tg, int* __restrict__ tok_flag,
+    int32_t* __restrict__ ids, int* flag) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T || tok_flag[t] != 0) return;
+  const int m = ccount[t];
+  const bool live = lane < m;
+  const int e = live ? cand[(size_t)t * kCandMax + lane] : 0x7fffffff;
+  const double v = live ? cval[(size_t)t * kCandMax + lane] : -INFINITY;
+  const double bnd = live ? tg * (xnorm[t] * wnorm[e] + (bias ? fabs((double)bias[e]) : 0.0)) : 0.0;
+  if (!__all(!live || isfinite(v))) {
+    if (lane == 0) {
+      raise_flag(flag, kFlagNonFinite);
+      tok_flag[t] = 2;
+    }
+    for (int r = lane; r < k; r += 64) ids[(size_t)t * k + r] = r;
+    return;
+  }
+  bool taken = false, ok = true;
+  double pv = 0.0, pb = 0.0;
+  for (int r = 0; r < k; ++r) {
+    double bv = (live && !taken) ? v : -INFINITY;
+    int be = (live && !taken) ? e : 0x7fffffff;
+    double bb = bnd;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      const double ob = __shfl_xor(bb, off);
+      if (sc_ranks_before(ov, oe, bv, be)) {
+        bv = ov;
+        be = oe;
+        bb = ob;
+      }
+    }
+    if (e == be) taken = true;
+    if (lane == 0) ids[(size_t)t * k + r] = be;
+    if (r > 0) ok = ok && ((pv - pb) - (bv + bb) > 0x1p-45 * (fabs(pv) + fabs(bv)));
+    pv = bv;
+    pb = bb;
+  }
+  double u = (live && !taken) ? v + bnd : -INFINITY;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) u = fmax(u, __shfl_xor(u, off));
+  if (u > -INFINITY) ok = ok && ((pv - pb) - u > 0x1p-45 * (fabs(pv) + fabs(u)));
+  if (lane == 0 && !ok) tok_flag[t] = 1;
+}
+
+// ---------------------------------------------------------------------------
+// Weights, one wavefront per token: the fp64 logits of the k chosen experts (from the
+// candidate list, or wave_dot when the token had too many candidates), then the
+// restricted softmax exp(l_r - m) / sum_s exp(l_s - m) in fp64, sum in column order,
+// one rounding to fp32.  With `weights_in` the caller's weights are copied instead
+// (router replay); the logits are still computed and checked for finiteness.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void screen_weights_kernel(
+    const void* __restrict__ x, const uint8_t* __restrict__ xs, int dtype, int T, int d, int E,
+    int k, const float* __restrict__ wt, const float* __restrict__ bias,
+    const int32_t* __restrict__ cand, const int* __restrict__ ccount, const double* __restrict__ cval,
+    const int32_t* __restrict__ ids, const float* __restrict__ weights_in,
+    float* __restrict__ weights, int* flag) {
+  __shared__ double lv[4][kMaxTopK];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const int m = ccount[t];
+  for (int r = 0; r < k; ++r) {
+    const int e = min(max(ids[(size_t)t * k + r], 0), E - 1);
+    const bool hit = lane < m && cand[(size_t)t * kCandMax + lane] == e;
+    const uint64_t hm = __ballot(hit);
+    double v;
+    if (hm) {
+      v = cval[(size_t)t * kCandMax + (__ffsll((long long)hm) - 1)];
+    } else {
+      v = wave_dot(x, xs, dtype, t, d, wt + (size_t)e * d);
+      if (bias) v = v + (double)bias[e];
+    }
+    if (lane == 0) lv[wave][r] = v;
+  }
+  if (lane != 0) return;
+  bool finite = true;
+  double mx = -INFINITY;
+  for (int r = 0; r < k; ++r) {
+    finite = finite && isfinite(lv[wave][r]);
+    mx = fmax(mx, lv[wave][r]);
+  }
+  if (!finite) raise_flag(flag, kFlagNonFinite);
+  float* wo = weights + (size_t)t * k;
+  if (weights_in) {
+    for (int r = 0; r < k; ++r) wo[r] = weights_in[(size_t)t * k + r];
+    return;
+  }
+  double sum = 0.0;
+  for (int r = 0; r < k; ++r) sum += exp(lv[wave][r] - mx);
+  for (int r = 0; r < k; ++r) wo[r] = (float)(exp(lv[wave][r] - mx) / sum);
+}
+
+// fp64 logits of listed pairs without grouping them by expert (small batches): one
+// wavefront per (token, slot < k).
+__global__ __launch_bounds__(256) void direct_refine_kernel(
+    const void* __restrict__ x, const uint8_t* __restrict__ xs, int dtype, int T, int d, int k,
+    const float* __restrict__ wt, const float* __restrict__ bias, const int32_t* __restrict__ cand,
+    double* __restrict__ cval) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long long p = (long long)blockIdx.x * 4 + wave;
+  if (p >= (long long)T * k) return;
+  const int t = (int)(p / k), j = (int)(p % k);
+  const int e = cand[(size_t)t * kCandMax + j];
+  const double v = wave_dot(x, xs, dtype, t, d, wt + (size_t)e * d);
+  if (lane == 0) cval[(size_t)t * kCandMax + j] = bias ? v + (double)bias[e] : v;
+}
+
+// Router replay: the caller's ids are the candidate lists (validated: in range and
+// distinct within the row, else flagged; clamped for the reads).
+__global__ __launch_bounds__(256) void replay_cand_kernel(const int32_t* __restrict__ ids_in, int T,
+                                                          int E, int k, int32_t* __restrict__ cand,
+                                                          int* __restrict__ ccount, int* flag) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  const int32_t* idr = ids_in + (size_t)t * k;
+  int bits = 0;
+  for (int r = 0; r < k; ++r) {
+    const int e = idr[r];
+    if (e < 0 || e >= E) bits |= kFlagBadId;
+    for (int q = 0; q < r; ++q)
+      if (idr[q] == e) bits |= kFlagDupId;
+    cand[(size_t)t * kCandMax + r] = min(max(e, 0), E - 1);
+  }
+  if (bits && flag) raise_flag(flag, bits);
+  ccount[t] = k;
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+static double gamma_n(double n, double u) { return n * u / (1.0 - n * u); }
+
+struct ScreenWs {
+  double* logits;   // screen partial sums [parts][T][E]
+  double* xsq;      // partial squared activation norms [parts][T]
+  int* tok_flag;
+  double* xnorm;
+  double* wnorm;
+  float* wt;
+  uint16_t* planes;
+  int32_t* cand;
+  double* cval;
+  int* ccount;
+  int* pcnt;        // per-expert pair counts / cursors [E], starts [E + 1]
+  int32_t* pairs;   // candidate pairs t * kCandMax + j in expert order
+};
+
+static ScreenWs screen_ws_of(char* w, int T, int d, int E) {
+  const RouteWs L = route_ws(T, d, E);
+  ScreenWs s;
+  s.logits = (double*)(w + L.screen);
+  s.xsq = (double*)(w + L.sxsq);
+  s.tok_flag = (int*)(w + L.tok_flag);
+  s.xnorm = (double*)(w + L.xnorm);
+  s.wnorm = (double*)(w + L.wnorm);
+  s.wt = (float*)(w + L.wt);
+  s.planes = (uint16_t*)(w + L.planes);
+  s.cand = (int32_t*)(w + L.cand);
+  s.cval = (double*)(w + L.cval);
+  s.ccount = (int*)(w + L.ccount);
+  s.pcnt = (int*)(w + L.pcnt);
+  s.pairs = (int32_t*)(w + L.pairs);
+  return s;
+}
+
+// fp64 logits of every listed candidate pair (at most T * kCandMax pairs).
+static moe_status refine_pairs(const void* x, const uint8_t* xs, int dtype, int T, int d, int E, int k,
+                               const float* bias, const ScreenWs& S, hipStream_t s) {
+  (void)k;
+  pair_clear_kernel<<<1, 1024, 0, s>>>(S.pcnt, E);
+  pair_count_kernel<<<(T + 255) / 256, 256, 0, s>>>(S.cand, S.ccount, T, E, S.pcnt);
+  pair_scan_kernel<<<1, 1024, 0, s>>>(S.pcnt, E);
+  pair_place_kernel<<<(T + 255) / 256, 256, 0, s>>>(S.cand, S.ccount, T, E, S.pcnt, S.pairs);
+  // about 8 pairs per token: aim at >= 1024 chunks
+  int rf_p = 8;
+  while (rf_p < 64 && (long long)rf_p * 2 * 1024 <= (long long)T * 8) rf_p *= 2;
+  const long long nblk = ((long long)T * kCandMax + rf_p - 1) / rf_p;
+  const size_t lds = d <= RF_LDS_MAX ? (size_t)d * sizeof(float) : 0;
+  screen_refine_kernel<<<(unsigned)(nblk < 2048 ? nblk : 2048), 64 * RF_W, lds, s>>>(
+      x, xs, dtype, T, d, S.wt, bias, S.cand, S.pairs, S.pcnt, E, rf_p, S.cval);
+  return launch_status();
+}
+
+// fp64 logits of the k listed ids per token (router replay, or the ids the fp64 gate
+// chose): grouped by expert for large batches, one wavefront per pair for small ones.
+static moe_status refine_ids(const void* x, const uint8_t* xs, int dtype, int T, int d, int E, int k,
+                             const float* bias, const ScreenWs& S, hipStream_t s) {
+  if (gate_split_launch(T, d, E)) {
+    direct_refine_kernel<<<(unsigned)(((long long)T * k + 3) / 4), 256, 0, s>>>(x, xs, dtype, T, d, k, S.wt,
+                                                                                bias, S.cand, S.cval);
+    return launch_status();
+  }
+  return refine_pairs(x, xs, dtype, T, d, E, k, bias, S, s);
+}
+
+moe_status screen_route_select(const void* x, const uint8_t* xs, int dtype, int T, int d,
+                               const float* w_gate, const float* bias, int E, int k, int32_t* ids,
+                               char* w, hipStream_t s) {
+  const ScreenWs S = screen_ws_of(w, T, d, E);
+  int* flag = (int*)w;
+  moe_status st;
+  gate_prep_kernel<<<dim3((d + 63) / 64, (E + 63) / 64), 256, 0, s>>>(w_gate, d, E, S.wt, S.planes);
+  gate_wnorm_kernel<<<E, 256, 0, s>>>(S.wt, d, E, S.wnorm);
+  const int tiles = ((E + SC_E - 1) / SC_E) * ((T + SC_T - 1) / SC_T);
+  const int nsteps = d / SC_K;
+  const int nz = screen_parts(T, d, E);
+  const int spart = (nsteps + nz - 1) / nz;
+  const dim3 grid((E + SC_E - 1) / SC_E, (T + SC_T - 1) / SC_T, (nsteps + spart - 1) / spart);
+  (void)tiles;
+  if (dtype == MOE_BF16)
+    gate_screen_kernel<MOE_BF16><<<grid, SC_THR, 0, s>>>(x, xs, T, d, E, spart, S.planes, S.logits, S.xsq);
+  else
+    gate_screen_kernel<MOE_MXFP8><<<grid, SC_THR, 0, s>>>(x, xs, T, d, E, spart, S.planes, S.logits, S.xsq);
+  const int chunk = dtype == MOE_BF16 ? 64 : 32;
+  const double tg = 2.0 * gamma_n(d + 1, 0x1p-53);
+  const double cs = 2.0 * (gamma_n(3.0 * chunk, 0x1p-23) * (1.0 + 0x1p-6) + gamma_n(d + 1, 0x1p-53));
+  const double ca = 2.0 * (4.0 * d + 64.0) * 0x1p-126;
+  const int nzl = (int)grid.z;
+  if (nzl > 1) {
+    const size_t n = (size_t)T * E;
+    screen_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(S.logits, S.xsq, T, E, nzl);
+  }
+#define MOE_CAND(NV)                                                                             \
+  screen_cand_kernel<NV><<<(T + 3) / 4, 256, 0, s>>>(S.logits, 1, S.xsq, S.xnorm, S.wnorm, bias,   \
+                                                     xs, dtype, T, d, E, k, cs, tg, ca, S.cand,     \
+                                                     S.ccount, S.tok_flag, ids, flag)
+  if (E <= 128) MOE_CAND(2);
+  else if (E <= 256) MOE_CAND(4);
+  else if (E <= 512) MOE_CAND(8);
+  else MOE_CAND(16);
+#undef MOE_CAND
+  if ((st = refine_pairs(x, xs, dtype, T, d, E, k, bias, S, s)) != MOE_OK) return st;
+  screen_select_kernel<<<(T + 3) / 4, 256, 0, s>>>(S.cand, S.ccount, S.cval, S.xnorm, S.wnorm, bias, T,
+                                                   k, tg, S.tok_flag, ids, flag);
+  return launch_status();
+}
+
+// The fp64 gate chose the ids (small batches): their fp64 logits for the weights.
+moe_status chosen_ids_refine(const void* x, const uint8_t* xs, int dtype, int T, int d,
+                             const float* w_gate, const float* bias, int E, int k, const int32_t* ids,
+                             char* w, hipStream_t s) {
+  const ScreenWs S = screen_ws_of(w, T, d, E);
+  gate_prep_kernel<<<dim3((d + 63) / 64, (E + 63) / 64), 256, 0, s>>>(w_gate, d, E, S.wt, nullptr);
+  replay_cand_kernel<<<(T + 255) / 256, 256, 0, s>>>(ids, T, E, k, S.cand, S.ccount, nullptr);
+  return refine_ids(x, xs, dtype, T, d, E, k, bias, S, s);
+}
+
+moe_status screen_route_weights(const void* x, const uint8_t* xs, int dtype, int T, int d,
+                                const float* bias, int E, int k, const int32_t* ids,
+                                const float* weights_in, float* weights, char* w, hipStream_t s) {
+  const ScreenWs S = screen_ws_of(w, T, d, E);
+  screen_weights_kernel<<<(T + 3) / 4, 256, 0, s>>>(x, xs, dtype, T, d, E, k, S.wt, bias, S.cand,
+                                                    S.ccount, S.cval, ids, weights_in, weights,
+                                                    (int*)w);
+  return launch_status();
+}
+
+moe_status screen_replay(const void* x, const uint8_t* xs, int dtype, int T, int d,
+                         const float* w_gate, const float* bias, int E, int k, const int32_t* ids_in,
+                         const float* weights_in, float* weights_out, char* w, hipStream_t s) {
+  const ScreenWs S = screen_ws_of(w, T, d, E);
+  gate_prep_kernel<<<dim3((d + 63) / 64, (E + 63) / 64), 256, 0, s>>>(w_gate, d, E, S.wt, nullptr);
+  replay_cand_kernel<<<(T + 255) / 256, 256, 0, s>>>(ids_in, T, E, k, S.cand, S.ccount, (int*)w);
+  moe_status st = refine_ids(x, xs, dtype, T, d, E, k, bias, S, s);
+  if (st != MOE_OK) return st;
+  return screen_route_weights(x, xs, dtype, T, d, bias, E, k, ids_in, weights_in, weights_out, w, s);
+}
+
+}  // namespace moe

@@ -45,6 +45,8 @@ def test_workspace_size(L):
     assert a > 4096 * 384 * 8 and a > (4096 * 9) * 2048 * 2
     assert b > 0
     assert pg.moe_workspace_size(0, 128, 16, 2, 64, pg.MOE_BF16) > 0
+    assert pg.moe_workspace_size(0, 64, 16, 2, 64, pg.MOE_BF16) > 0      # empty batch, short rows
+    assert pg.moe_workspace_size(0, 7168, 384, 8, 2048, pg.MOE_MXFP8) > 0
     n = ctypes.c_size_t()
     for bad in [(-1, 128, 16, 2, 64, 1), (8, 0, 16, 2, 64, 1), (8, 128, 2000, 2, 64, 1),
                 (8, 128, 16, 17, 64, 1), (8, 128, 16, 33, 64, 1), (8, 128, 64, 33, 64, 1),

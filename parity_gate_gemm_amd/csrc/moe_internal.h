@@ -58,7 +58,7 @@ constexpr int kCandMax = 32;
 // fill the chip; the screen has no fixed-order requirement.
 inline int screen_parts(int T, int d, int E) {
   const int tiles = ((E + 127) / 128) * ((T + 127) / 128);
-  const int steps = d / 32;
+  const int steps = d / 64;
   if (tiles < 1 || steps < 1) return 1;
   int nz = (512 + tiles - 1) / tiles;
   if (nz > 16) nz = 16;
@@ -89,7 +89,7 @@ inline RouteWs route_ws(int T, int d, int E) {
   w.cand = o;     o = align_up(o + (size_t)T * kCandMax * sizeof(int32_t), 256);
   w.cval = o;     o = align_up(o + (size_t)T * kCandMax * sizeof(double), 256);
   w.ccount = o;   o = align_up(o + (size_t)T * sizeof(int), 256);
-  const size_t nz = d % 32 == 0 ? (size_t)screen_parts(T, d, E) : 1;
+  const size_t nz = d % 64 == 0 ? (size_t)screen_parts(T, d, E) : 1;
   w.screen = o;   o = align_up(o + nz * T * E * sizeof(double), 256);
   w.sxsq = o;     o = align_up(o + nz * T * sizeof(double), 256);
   w.pcnt = o;     o = align_up(o + (size_t)(2 * E + 1) * sizeof(int), 256);
@@ -98,12 +98,12 @@ inline RouteWs route_ws(int T, int d, int E) {
   return w;
 }
 
-// bf16 and MXFP8 activations with d % 32 == 0 take their weights (and, under
+// bf16 and MXFP8 activations with d % 64 == 0 take their weights (and, under
 // replay, everything) from per-pair fp64 logits; the ids come from the bf16 screen
 // for large batches and from the fp64 gate GEMM for small ones (gate_split_launch).
 // fp32 activations use the fp64 gate GEMM for ids and weights.
 inline bool gate_screened(int dtype, int d) {
-  return (dtype == MOE_BF16 || dtype == MOE_MXFP8) && d % 32 == 0;
+  return (dtype == MOE_BF16 || dtype == MOE_MXFP8) && d % 64 == 0;
 }
 
 struct DispatchWs {

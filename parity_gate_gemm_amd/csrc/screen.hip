@@ -105,58 +105,68 @@ __device__ __forceinline__ uint16_t e4m3_to_bf16_bits(uint32_t c) {
 // (we, wt) owns experts 64 we .. +63 (two 32-row A blocks, one per plane triple) and
 // tokens 32 wt .. +31 (one 32-column B block).  The experts are the MFMA's rows, so a
 // lane's 16 accumulator values all belong to one token (column lane % 32) and the
-// token's MX scale is one value per lane.  K advances 32 per step through LDS (80-byte
+// token's MX scale is one value per lane.  K advances 64 per step through LDS (144-byte
 // rows) with the next step's loads in registers.
 // The K steps are cut into gridDim.z parts of `spart` steps (more workgroups for small
 // batches; the screen needs no fixed summation order, only its bound, which holds for
 // any grouping of the chunk sums).  Output: partial sums s[z][t][e] (fp64, without the
 // bias); the first expert tile also writes the partial squared norms xsq[z][t].
 // ---------------------------------------------------------------------------
-constexpr int SC_E = 128, SC_T = 128, SC_K = 32, SC_LDS = SC_K + 8, SC_THR = 512;
+constexpr int SC_E = 128, SC_T = 128, SC_K = 64, SC_LDS = SC_K + 8, SC_THR = 512;
 
 template <int DT>
 __global__ __launch_bounds__(SC_THR) void gate_screen_kernel(const void* __restrict__ x,
-                                                          const uint8_t* __restrict__ xs, int T,
-                                                          int d, int E, int spart,
-                                                          const uint16_t* __restrict__ planes,
-                                                          double* __restrict__ s,
-                                                          double* __restrict__ xsqp) {
-  constexpr int CH = DT == MOE_BF16 ? 2 : 1;   // K steps per fp32 chunk
+                                                             const uint8_t* __restrict__ xs, int T,
+                                                             int d, int E, int spart,
+                                                             const uint16_t* __restrict__ planes,
+                                                             double* __restrict__ s,
+                                                             double* __restrict__ xsqp) {
+  constexpr int CPR = SC_K / 8;                           // 16-byte bf16 chunks per row
+  constexpr int NW = 3 * SC_E * CPR / SC_THR;             // plane chunks per thread
+  constexpr int NX = DT == MOE_BF16 ? SC_T * CPR / SC_THR : 1;
   __shared__ __attribute__((aligned(16))) uint16_t sW[3][SC_E][SC_LDS];
   __shared__ __attribute__((aligned(16))) uint16_t sX[SC_T][SC_LDS];
-  __shared__ double sS[SC_T];
+  __shared__ double sS[SC_T][2];                          // MXFP8: the two block scales of a step
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int we = wave >> 2, wt = wave & 3;
   const int e0 = blockIdx.x * SC_E, t0 = blockIdx.y * SC_T;
   const size_t plane = (size_t)E * d;
+  const int nb32 = d / 32;
 
-  // loader: plane chunks q = tid + 512 i: plane q / 512, row (q % 512) / 4, k (q % 4) * 8
-  constexpr int NW = 3 * SC_E * SC_K / 8 / SC_THR;
+  // loaders: plane chunk q = tid + SC_THR i is plane q / (SC_E CPR), row (q % (SC_E CPR)) / CPR,
+  // k offset 8 (q % CPR); activation chunk likewise (bf16: 8 values; MXFP8: 16 codes).
   const uint16_t* wp[NW];
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
-    const int q = tid + SC_THR * i, p = q / 512, r = (q % 512) / 4, c = (q % 4) * 8;
+    const int q = tid + SC_THR * i, p = q / (SC_E * CPR), r = (q % (SC_E * CPR)) / CPR, c = (q % CPR) * 8;
     const int e = e0 + r < E ? e0 + r : 0;
     wp[i] = planes + p * plane + (size_t)e * d + c;
   }
-  const int xr = DT == MOE_BF16 ? tid / 4 : tid / 2;
-  const int xc = DT == MOE_BF16 ? (tid % 4) * 8 : (tid % 2) * 16;
-  const int xt = t0 + xr < T ? t0 + xr : 0;
-  const bool xload = DT == MOE_BF16 || tid < 2 * SC_T;
-  const int nb32 = d / 32;
+  int xr[NX], xc[NX];
+  size_t xo[NX];
+#pragma unroll
+  for (int i = 0; i < NX; ++i) {
+    const int q = tid + SC_THR * i;
+    xr[i] = DT == MOE_BF16 ? q / CPR : q / 4;
+    xc[i] = DT == MOE_BF16 ? (q % CPR) * 8 : (q % 4) * 16;
+    const int t = t0 + xr[i] < T ? t0 + xr[i] : 0;
+    xo[i] = (size_t)t * d + xc[i];
+  }
+  const int sr = tid >> 1, sb = tid & 1;                  // MXFP8 scale loader (tid < 2 SC_T)
+  const size_t so = (size_t)(t0 + sr < T ? t0 + sr : 0) * nb32 + sb;
 
-  u32x4_t rw[NW], rx = {0, 0, 0, 0};
+  u32x4_t rw[NW], rx[NX];
   uint32_t rsc = 0;
   auto gload = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < NW; ++i) rw[i] = *(const u32x4_t*)(wp[i] + k0);
-    if (DT == MOE_BF16) {
-      rx = *(const u32x4_t*)((const uint16_t*)x + (size_t)xt * d + k0 + xc);
-    } else {
-      if (xload) rx = *(const u32x4_t*)((const uint8_t*)x + (size_t)xt * d + k0 + xc);
-      if (tid < SC_T) rsc = xs[(size_t)(t0 + tid < T ? t0 + tid : 0) * nb32 + k0 / 32];
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      if (DT == MOE_BF16) rx[i] = *(const u32x4_t*)((const uint16_t*)x + xo[i] + k0);
+      else rx[i] = *(const u32x4_t*)((const uint8_t*)x + xo[i] + k0);
     }
+    if (DT == MOE_MXFP8 && tid < 2 * SC_T) rsc = xs[so + k0 / 32];
   };
 
   f32x16_t acc32[2];
@@ -170,6 +180,22 @@ __global__ __launch_bounds__(SC_THR) void gate_screen_kernel(const void* __restr
     }
   const bool do_xn = blockIdx.x == 0 && we == 0;
   double xsq = 0.0, csq = 0.0;    // csq: this chunk's sum of squared (unscaled) activations
+  const int trow = wt * 32 + (lane & 31);
+
+  // fold the fp32 chunk sums (times the chunk's scale) into the fp64 accumulators
+  auto fold = [&](double sc) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        acc64[mb][v] = fma((double)acc32[mb][v], sc, acc64[mb][v]);
+        acc32[mb][v] = 0.0f;
+      }
+    if (do_xn) {
+      xsq = fma(csq, sc * sc, xsq);
+      csq = 0.0;
+    }
+  };
 
   const int st0 = blockIdx.z * spart;
   const int nsteps = min(d / SC_K - st0, spart);
@@ -178,34 +204,35 @@ __global__ __launch_bounds__(SC_THR) void gate_screen_kernel(const void* __restr
     // registers -> LDS
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-      const int q = tid + SC_THR * i, p = q / 512, r = (q % 512) / 4, c = (q % 4) * 8;
+      const int q = tid + SC_THR * i, p = q / (SC_E * CPR), r = (q % (SC_E * CPR)) / CPR, c = (q % CPR) * 8;
       *(u32x4_t*)&sW[p][r][c] = rw[i];
     }
-    if (DT == MOE_BF16) {
-      *(u32x4_t*)&sX[xr][xc] = rx;
-    } else {
-      if (xload) {
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      if (DT == MOE_BF16) {
+        *(u32x4_t*)&sX[xr[i]][xc[i]] = rx[i];
+      } else {
         uint16_t b[16];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) b[q] = e4m3_to_bf16_bits((rx[q >> 2] >> (8 * (q & 3))) & 0xFFu);
+        for (int q = 0; q < 16; ++q) b[q] = e4m3_to_bf16_bits((rx[i][q >> 2] >> (8 * (q & 3))) & 0xFFu);
         u32x4_t lo, hi;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           lo[q] = (uint32_t)b[2 * q] | ((uint32_t)b[2 * q + 1] << 16);
           hi[q] = (uint32_t)b[8 + 2 * q] | ((uint32_t)b[8 + 2 * q + 1] << 16);
         }
-        *(u32x4_t*)&sX[xr][xc] = lo;
-        *(u32x4_t*)&sX[xr][xc + 8] = hi;
+        *(u32x4_t*)&sX[xr[i]][xc[i]] = lo;
+        *(u32x4_t*)&sX[xr[i]][xc[i] + 8] = hi;
       }
-      if (tid < SC_T) sS[tid] = e8m0_to_f64((uint8_t)rsc);
     }
+    if (DT == MOE_MXFP8 && tid < 2 * SC_T) sS[sr][sb] = e8m0_to_f64((uint8_t)rsc);
     __syncthreads();
     if (st + 1 < nsteps) gload((st0 + st + 1) * SC_K);
 
 #pragma unroll
     for (int kk = 0; kk < SC_K; kk += 16) {
       const int kc = kk + 8 * (lane >> 5);
-      const bf16x8_t bx = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)&sX[wt * 32 + (lane & 31)][kc]);
+      const bf16x8_t bx = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)&sX[trow][kc]);
       if (do_xn) {
         const u32x4_t u = __builtin_bit_cast(u32x4_t, bx);
 #pragma unroll
@@ -222,27 +249,16 @@ __global__ __launch_bounds__(SC_THR) void gate_screen_kernel(const void* __restr
               __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)&sW[p][we * 64 + mb * 32 + (lane & 31)][kc]);
           acc32[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, bx, acc32[mb], 0, 0, 0);
         }
+      // chunk ends: every 32 k for MXFP8 (one scale block), every 64 k for bf16
+      if (DT == MOE_MXFP8 && (kk == 16 || kk == 48)) fold(sS[trow][kk >> 5]);
     }
-    if ((st + 1) % CH == 0 || st + 1 == nsteps) {   // end of a chunk: fold into fp64
-      const double sc = DT == MOE_BF16 ? 1.0 : sS[wt * 32 + (lane & 31)];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          acc64[mb][v] = fma((double)acc32[mb][v], sc, acc64[mb][v]);
-          acc32[mb][v] = 0.0f;
-        }
-      if (do_xn) {
-        xsq = fma(csq, sc * sc, xsq);
-        csq = 0.0;
-      }
-    }
+    if (DT == MOE_BF16) fold(1.0);
     __syncthreads();
   }
 
   // outputs: accumulator element v is expert row 8 (v / 4) + 4 (lane / 32) + v % 4 of
   // the block, token column lane % 32
-  const int t = t0 + wt * 32 + (lane & 31);
+  const int t = t0 + trow;
   double* sz = s + (size_t)blockIdx.z * T * E;
   if (t < T) {
 #pragma unroll

@@ -58,6 +58,9 @@ constexpr bool kGemmNtB = MOE_GEMM_NT_B != 0; // nontemporal weight loads
 #ifndef MOE_MX_WAVES
 #define MOE_MX_WAVES 1   // minimum wavefronts per SIMD the register allocation must allow
 #endif
+#ifndef MOE_MX_RING
+#define MOE_MX_RING 1   // MXFP8 GEMMs on the LDS ring where the shape tiles
+#endif
 #ifndef MOE_GEMM_DMA
 #define MOE_GEMM_DMA 0
 #endif
@@ -613,6 +616,38 @@ __device__ __forceinline__ void mx_store_h(float h, bool live, uint8_t* code, ui
   }
 }
 
+// Requantise one MX block held in one lane (32 consecutive features of a row) and
+// store its 32 codes (two 16-byte stores) and its scale.  Same scale rule and encoding
+// as mx_store_h.
+__device__ __forceinline__ void mx_store_block(const float (&h)[32], uint8_t* code, uint8_t* scale) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) amax = fmaxf(amax, fabsf(h[k]));
+  int se;
+  uint32_t scode;
+  if (amax == 0.0f) {
+    se = -127;
+    scode = 0;
+  } else if (!(amax <= 3.0e38f)) {
+    se = 0;
+    scode = 255;
+  } else {
+    se = min(max(ilogbf(amax) - 8, -127), 127);
+    scode = (uint32_t)(se + 127);
+  }
+  u32x4_t w[2];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    uint32_t d = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) d |= e4m3_rne_sat(ldexpf(h[4 * k + b], -se)) << (8 * b);
+    w[k >> 2][k & 3] = d;
+  }
+  *(u32x4_t*)code = w[0];
+  *(u32x4_t*)(code + 16) = w[1];
+  *scale = (uint8_t)scode;
+}
+
 // Tile: (64 WM) rows x (32 FN WN) staged B rows, WM x WN wavefronts; each wavefront
 // owns 64 rows x 32 FN B rows as 2 x FN MFMA blocks.  K advances 128 bytes a step:
 // registers -> LDS (144-byte rows) -> two 64-wide MFMA steps, with the next step's
@@ -825,6 +860,403 @@ void grouped_gemm_mx_kernel(MxArgs g) {
 }
 
 // ---------------------------------------------------------------------------
+// MXFP8 grouped GEMM on a four-stage LDS ring (the path for shapes it tiles: N of
+// GEMM2 a multiple of 256).  Tiles are 256 rows x 256 staged B rows; K advances 64
+// bytes (one MFMA k range) a step.  Eight wavefronts, 2 along M x 4 along N, each own
+// 128 rows x 64 B rows as 4 x 2 MFMA blocks, two wavefronts per SIMD.
+// Loads go straight from global memory into LDS (global_load_lds_dwordx4: lane l of a
+// wavefront writes its 16 bytes at base + 16 l), three steps ahead of the step being
+// multiplied.  A stage holds the A tile (256 rows x 64 B) and the B tile (256 x 64 B).
+// E8M0 scales travel in groups of 16 bytes per row (512 K, eight steps), into one of two
+// scale buffers, issued eight steps before their first use: a per-step scale load
+// would cost one memory request per row for 2 bytes.
+// The 16-byte chunk c of a row r is stored in slot c ^ ((r >> 2) & 3), so the sixteen
+// rows that one ds_read_b128 phase touches fall in distinct banks.
+// Row blocks past the tile's valid rows are not multiplied (a wavefront skips its
+// 32-row blocks that hold no valid row), so a short tile costs MFMA time in
+// proportion to its 32-row blocks.  Every output is the same MFMA chain as in
+// grouped_gemm_mx_kernel (K ascending in 64-wide scaled MFMAs from zero), hence the
+// same bits.
+// The loads are issued from inline assembly: the compiler then treats the fragment
+// reads as ordinary LDS loads (it does not wait for the ring's outstanding loads before
+// each of them), and the K loop orders them itself with an explicit vmcnt wait and
+// s_barrier per step.  No other global load is in flight inside the K loop.
+// ---------------------------------------------------------------------------
+constexpr int XR_M = 256;                        // tile rows
+constexpr int XR_N = 256;                        // staged B rows
+constexpr int XR_K = 64;                         // K bytes per ring step (one MFMA k range)
+constexpr int XR_ST = 4;                         // ring stages
+constexpr int XR_P = 4;                          // steps of loads in flight
+constexpr int XR_A = 0, XR_B = XR_M * XR_K;      // tile offsets within a stage
+constexpr int XR_STAGE = (XR_M + XR_N) * XR_K;   // 32 KB
+constexpr int XR_GK = 8;                         // steps per scale group (16 E8M0 bytes per row)
+constexpr int XR_GB = XR_GK * XR_K;              // K per scale group
+constexpr int XR_SC = XR_ST * XR_STAGE;          // two scale-group buffers after the stages
+constexpr int XR_SCB = (XR_M + XR_N) * 16;       // bytes per scale-group buffer (A rows, then B)
+constexpr int XR_LDS = XR_SC + 2 * XR_SCB;       // 144 KB
+constexpr int XR_DL = (XR_M + XR_N) * XR_K / 1024 / 4;   // data loads per wavefront per step (8)
+constexpr int XR_EPI_ROW = 272;                  // epilogue staging: bytes per local row
+constexpr int XR_EPI = 128 * XR_EPI_ROW;         // epilogue staging per wavefront (34 KB)
+static_assert(XR_LDS <= 160 * 1024 && 4 * XR_EPI <= XR_LDS, "LDS budget");
+
+// slot of the 16-byte chunk c of row r: c ^ ((r >> 2) & 3); the sixteen rows that one
+// ds_read_b128 phase touches (one chunk each) then fall in distinct banks
+__device__ __forceinline__ int xr_swz(int r) { return (r >> 2) & 3; }
+
+__device__ __forceinline__ void xr_load16(uint32_t lds, const void* src) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory");
+}
+// the same from a wavefront-uniform base plus a 32-bit per-lane byte offset
+__device__ __forceinline__ void xr_load16(uint32_t lds, uint32_t off, const void* base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base)
+               : "memory");
+}
+// Wait until at most N ring loads of this wavefront are outstanding and every LDS
+// access of this wavefront has completed, then meet the other wavefronts.
+template <int N>
+__device__ __forceinline__ void xr_sync() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void xr_sync_n(int n) {
+  switch (n) {
+    case 2: xr_sync<2>(); break;
+    case 8: xr_sync<8>(); break;
+    case 10: xr_sync<10>(); break;
+    case 16: xr_sync<16>(); break;
+    case 18: xr_sync<18>(); break;
+    case 24: xr_sync<24>(); break;
+    default: xr_sync<0>(); break;   // 0, or any other count: wait for everything (still correct)
+  }
+}
+
+// Fragments of one K step for a wavefront: NA of its row blocks, 4 B blocks, scales.
+template <int NA>
+struct XrFrag {
+  i32x8_t a[NA > 0 ? NA : 1], b[4];
+  int sa[NA > 0 ? NA : 1], sb[4];
+};
+
+// Read step j's fragments from stage st / scale buffer scb.  aof/bof: this lane's
+// first chunk (the second is XOR 32); asf/bsf: its scale byte of k-block 0; sc: the
+// step's first k-block within the scale group.
+template <int NA>
+__device__ __forceinline__ void xr_read(XrFrag<NA>& f, const uint8_t* st, const uint8_t* scb, uint32_t aof,
+                                        uint32_t bof, uint32_t asf, uint32_t bsf, int sc) {
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const uint32_t o = bof + nb * 32 * XR_K;
+    const u32x4_t lo = *(const u32x4_t*)(st + o);
+    const u32x4_t hi = *(const u32x4_t*)(st + (o ^ 32));
+    f.b[nb] = (i32x8_t){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    f.sb[nb] = scb[bsf + nb * 32 * 16 + sc];
+  }
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const uint32_t o = aof + i * 64 * XR_K;   // row blocks wm, wm + 2, ...: 64 rows apart
+    const u32x4_t lo = *(const u32x4_t*)(st + o);
+    const u32x4_t hi = *(const u32x4_t*)(st + (o ^ 32));
+    f.a[i] = (i32x8_t){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    f.sa[i] = scb[asf + i * 64 * 16 + sc];
+  }
+}
+
+// An empty asm that reads every accumulator: the MFMAs of a step are then issued before
+// the ring loads that follow it in program order (the compiler would otherwise sink
+// them past those loads, next to their next use).
+__device__ __forceinline__ void xr_pin(const f32x16_t (&acc)[4][4]) {
+  asm volatile("" ::"a"(acc[0][0]), "a"(acc[0][1]), "a"(acc[0][2]), "a"(acc[0][3]), "a"(acc[1][0]),
+               "a"(acc[1][1]), "a"(acc[1][2]), "a"(acc[1][3]), "a"(acc[2][0]), "a"(acc[2][1]),
+               "a"(acc[2][2]), "a"(acc[2][3]), "a"(acc[3][0]), "a"(acc[3][1]), "a"(acc[3][2]),
+               "a"(acc[3][3]));
+}
+
+template <int NA>
+__device__ __forceinline__ void xr_mfma(const XrFrag<NA>& f, f32x16_t (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < NA; ++i)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      acc[i][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[nb], acc[i][nb], 0, 0, 0,
+                                                                   f.sa[i], 0, f.sb[nb]);
+}
+
+// The K loop for a wavefront that multiplies NA of its 4 row blocks (NA = 0: it only
+// loads and synchronises).  The data of step j is loaded at step j - 4 into stage j % 4;
+// its fragments are read into registers at step j - 1 (so stage j % 4 is free again at
+// step j), and multiplied at step j.  Scale group g (steps 8 g .. 8 g + 7) is loaded at
+// step 8 (g - 1), after that step's data, into buffer g % 2.
+// Load sources: A rows at abase + aoff[i] (wavefront-uniform base, per-lane offset), B
+// rows at bbase[i] + boff[i], A scale groups at asbase + asoff, B scale groups at bsp.
+struct XrSrc {
+  const uint8_t* abase;
+  const uint8_t* bbase[4];
+  const uint8_t* asbase;
+  const uint8_t* bsp;
+  uint32_t aoff[4], boff[4], asoff;
+};
+
+template <int NA>
+__device__ __forceinline__ void xr_kloop(const uint8_t* ring, uint32_t ring_lds, int nsteps, const XrSrc& src,
+                                         int wave, uint32_t aof, uint32_t bof, uint32_t asf, uint32_t bsf,
+                                         f32x16_t (&acc)[4][4]) {
+  const uint32_t la = XR_A + wave * 4096, lb = XR_B + wave * 4096;
+  const int ngroups = nsteps / XR_GK;
+  auto issue = [&](int j) {
+    const uint32_t st = ring_lds + (uint32_t)(j % XR_ST) * XR_STAGE;
+    const int k0 = j * XR_K;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xr_load16(st + la + 1024 * i, src.aoff[i], src.abase + k0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xr_load16(st + lb + 1024 * i, src.boff[i], src.bbase[i] + k0);
+  };
+  auto issue_scales = [&](int grp) {
+    const uint32_t sb = ring_lds + XR_SC + (uint32_t)(grp & 1) * XR_SCB;
+    xr_load16(sb + wave * 1024, src.asoff, src.asbase + 16 * grp);
+    xr_load16(sb + XR_M * 16 + wave * 1024, src.bsp + 16 * grp);
+  };
+  auto scales_at = [&](int i) { return i >= 0 && i % XR_GK == 0 && i / XR_GK + 1 < ngroups ? 2 : 0; };
+  auto read = [&](XrFrag<NA>& f, int j) {
+    if constexpr (NA > 0)
+      xr_read<NA>(f, ring + (j % XR_ST) * XR_STAGE, ring + XR_SC + ((j / XR_GK) & 1) * XR_SCB, aof, bof,
+                  asf, bsf, 2 * (j % XR_GK));
+  };
+  // wait for step j's data: the loads issued after it (at step j - 4) are the scale
+  // group of that step, the data of steps j+1 .. j+2 (issued by the end of step j - 1)
+  // and the scale groups of steps j-3 .. j-1 (loads complete in issue order)
+  auto sync_for = [&](int j) {
+    int after = 0;
+    if (j == 0) {   // after the prologue: the data of steps 1 .. 3
+      xr_sync_n(XR_DL * (min(nsteps, XR_P) - 1));
+      return;
+    }
+    for (int i = j + 1; i <= j + 2; ++i) after += (i < nsteps) ? XR_DL : 0;
+    for (int i = j - 4; i <= j - 2; ++i) after += scales_at(i);
+    xr_sync_n(after);
+  };
+
+  XrFrag<NA> f0, f1;
+  issue_scales(0);
+  for (int j = 0; j < XR_P && j < nsteps; ++j) issue(j);
+  // step j (< nsteps - 1): make step j+1 visible, refill the ring, read step j+1's
+  // fragments, multiply step j's
+  auto step = [&](int j, XrFrag<NA>& cur, XrFrag<NA>& nxt) {
+    sync_for(j + 1);
+    read(nxt, j + 1);
+    if constexpr (NA > 0) {
+      xr_mfma<NA>(cur, acc);
+      // interleave the fragment reads of step j+1 with the MFMAs of step j
+      constexpr int kRd = 6 * NA + 12;   // ds_read_b128 and ds_read_u8 of one step
+      constexpr int kMf = 4 * NA;
+      constexpr int kPer = (kRd + kMf - 1) / kMf;
+#pragma unroll
+      for (int m = 0; m < kMf; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, kPer, 0);  // then a few LDS reads
+      }
+      xr_pin(acc);
+    }
+    if (j + XR_P < nsteps) issue(j + XR_P);
+    if (scales_at(j)) issue_scales(j / XR_GK + 1);
+  };
+  sync_for(0);
+  read(f0, 0);
+  // nsteps is even (K is a multiple of 512)
+  int j = 0;
+  for (; j + 2 < nsteps; j += 2) {
+    step(j, f0, f1);
+    step(j + 1, f1, f0);
+  }
+  step(j, f0, f1);
+  if constexpr (NA > 0) xr_mfma<NA>(f1, acc);
+}
+
+// MXFP8 grouped GEMM, 256 x 256 tiles, four wavefronts (2 x 2), each 4 row blocks x
+// 4 B blocks of 32 x 32.  Wavefront (wm, wn) owns the row blocks wm, wm + 2, wm + 4,
+// wm + 6, so a short tile splits its valid 32-row blocks evenly over the SIMDs.
+template <int MODE>
+__global__ __launch_bounds__(256) void grouped_gemm_mx_ring_kernel(MxArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[XR_LDS];
+
+  // ---- tile decode (as grouped_gemm_mx_kernel, tiles of XR_M rows) ----
+  const int total = g.mstart[g.S] * g.NT;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int xcd = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
+  if (q >= per) return;
+  const int tile = xcd * per + q;
+  if (tile >= total) return;
+  int lo = 0, hi = g.S;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (g.mstart[mid] * g.NT <= tile) lo = mid; else hi = mid;
+  }
+  const int s = lo;
+  const int mtiles = g.mstart[s + 1] - g.mstart[s];
+  const int local = tile - g.mstart[s] * g.NT;
+  const int grp = local / (kGroupM * g.NT), rem = local % (kGroupM * g.NT);
+  const int gm = min(kGroupM, mtiles - grp * kGroupM);
+  const int nt = rem / gm, mt = grp * kGroupM + rem % gm;
+  const int row0 = g.rowstart[s] + mt * XR_M;
+  const int mrows = min(XR_M, g.rowcount[s] - mt * XR_M);
+  const int n0 = nt * (MODE == 0 ? XR_N / 2 : XR_N);
+  const bool is_shared = (s == g.E);
+  const long long e = is_shared ? 0 : s;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int KB = g.K / 32;   // scale bytes per row
+
+  int bad = 0;
+  // source row of A tile row r (rows past the segment re-read the tile's first row)
+  auto a_src = [&](int r) -> long long {
+    const long long jr = (long long)row0 + (r < mrows ? r : 0);
+    if (MODE != 0) return jr;
+    long long src = is_shared ? jr - g.Tk : (long long)(g.perm[jr] / g.k);
+    if (src < 0 || src >= g.T) {
+      bad = 1;
+      src = 0;
+    }
+    return src;
+  };
+  // row (within expert e's matrix) of staged B row r; GEMM1 alternates 32-row blocks of
+  // W1 and W3 for the same 32 features
+  auto b_row = [&](int r, const uint8_t*& bank, const uint8_t*& sbank) -> long long {
+    if (MODE == 0) {
+      const int blk = r >> 5;
+      const bool w3 = blk & 1;
+      bank = w3 ? (is_shared ? g.sb1 : g.b1) : (is_shared ? g.sb0 : g.b0);
+      sbank = w3 ? (is_shared ? g.sb1s : g.b1s) : (is_shared ? g.sb0s : g.b0s);
+      return (long long)n0 + (blk >> 1) * 32 + (r & 31);
+    }
+    bank = is_shared ? g.sb0 : g.b0;
+    sbank = is_shared ? g.sb0s : g.b0s;
+    return (long long)n0 + r;
+  };
+
+  // ---- loader: wavefront w fills A rows and B rows 64 w .. 64 w + 63 (four loads of 16
+  //      rows each; lane l -> row + l / 4, slot l % 4 <- chunk slot ^ swz(row)) and the
+  //      16-byte scale groups of A rows and B rows 64 w + l.  Every byte offset from a
+  //      load's base fits 32 bits (one activation matrix, or one expert's matrix). ----
+  XrSrc src;
+  src.abase = g.a;
+  src.asbase = g.as;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 64 * wave + 16 * i + (lane >> 2);   // 32-row block 2 wave + i / 2: uniform
+    const int chunk = (lane & 3) ^ xr_swz(r);
+    src.aoff[i] = (uint32_t)(a_src(r) * g.K + 16 * chunk);
+    const uint8_t *bank, *sbank;
+    const long long br = b_row(r, bank, sbank);
+    src.bbase[i] = bank + e * g.N * (long long)g.K;
+    src.boff[i] = (uint32_t)(br * g.K + 16 * chunk);
+  }
+  src.asoff = (uint32_t)(a_src(64 * wave + lane) * KB);
+  {
+    const uint8_t *bank, *sbank;   // GEMM1: W1 scales for lanes 0..31, W3 for 32..63
+    const long long br = b_row(64 * wave + lane, bank, sbank);
+    src.bsp = sbank + (e * g.N + br) * (long long)KB;
+  }
+  if (bad) raise_flag(g.flag, kFlagCorrupt);
+
+  // ---- fragment offsets within a stage: lane reads row (block base + lane % 32),
+  //      chunks lane / 32 (bytes 0..15) and 2 + lane / 32 (bytes 16..31: offset ^ 32) ----
+  const int j32 = lane & 31, hh = lane >> 5;
+  const int ra = 32 * wm + j32, rb = 128 * wn + j32;
+  const uint32_t aof = XR_A + ra * XR_K + 16 * (hh ^ xr_swz(ra));
+  const uint32_t bof = XR_B + rb * XR_K + 16 * (hh ^ xr_swz(rb));
+  const uint32_t asf = ra * 16 + hh, bsf = XR_M * 16 + rb * 16 + hh;   // within a scale buffer
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_u8*)ring;
+  const int nsteps = g.K / XR_K;
+  // this wavefront's row blocks wm + 2 i that hold a valid row (uniform per wavefront)
+  const int nvb = (mrows + 31) >> 5;
+  const int na = min(4, max(0, (nvb - wm + 1) >> 1));
+  switch (na) {
+    case 4: xr_kloop<4>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, acc); break;
+    case 3: xr_kloop<3>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, acc); break;
+    case 2: xr_kloop<2>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, acc); break;
+    case 1: xr_kloop<1>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, acc); break;
+    default: xr_kloop<0>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, acc); break;
+  }
+
+  // ---- epilogue through LDS: each wavefront stages its 128 x (64 or 128) outputs
+  //      row-major in its own 34 KB of the (now idle) ring, then writes whole MX blocks
+  //      (GEMM1) or 16-byte row chunks (GEMM2).  Accumulator element v of a lane is
+  //      C[i][j], j = lane % 32, i = 8 (v / 4) + 4 (lane / 32) + v % 4; the wavefront's
+  //      local row 32 ib + i is tile row 32 (wm + 2 ib) + i. ----
+  __syncthreads();   // every wavefront is done reading the ring
+  uint8_t* stg = ring + wave * XR_EPI;
+#pragma unroll
+  for (int ib = 0; ib < 4; ++ib) {
+    if (ib >= na) break;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int rl = 32 * ib + 8 * (v >> 2) + 4 * hh + (v & 3);
+      if (MODE == 0) {
+        // B blocks (0, 1) and (2, 3) are the W1 and W3 halves of 32 features each
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          *(float*)(stg + rl * XR_EPI_ROW + (32 * p + j32) * 4) =
+              silu_f32(acc[ib][2 * p][v]) * acc[ib][2 * p + 1][v];
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          *(uint16_t*)(stg + rl * XR_EPI_ROW + (32 * nb + j32) * 2) = f32_to_bf16(acc[ib][nb][v]);
+      }
+    }
+  }
+  // (a wavefront reads back only what it wrote: its LDS accesses complete in order)
+  if (MODE == 0) {
+    // lane l: local row 32 q + l / 2, MX block l % 2 (32 features) of the wavefront's 64
+    const int pb = lane & 1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (q >= na) break;
+      const int rl = 32 * q + (lane >> 1);
+      const int r = 32 * (wm + 2 * q) + (lane >> 1);
+      if (r < mrows) {
+        float hv[32];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float4 t = *(const float4*)(stg + rl * XR_EPI_ROW + pb * 128 + 16 * c);
+          hv[4 * c] = t.x;
+          hv[4 * c + 1] = t.y;
+          hv[4 * c + 2] = t.z;
+          hv[4 * c + 3] = t.w;
+        }
+        const long long orow = (long long)row0 + r;
+        const int col = n0 + (2 * wn + pb) * 32;
+        mx_store_block(hv, (uint8_t*)g.out + orow * g.N + col, g.out_scale + orow * (g.N / 32) + col / 32);
+      }
+    }
+  } else {
+    // lane l: local row 4 q + l / 16, 16-byte chunk l % 16 of the row's 128 outputs
+    const int c = lane & 15;
+#pragma unroll 4
+    for (int q = 0; q < 32; ++q) {
+      const int rl = 4 * q + (lane >> 4);
+      const int r = 32 * (wm + 2 * (rl >> 5)) + (rl & 31);
+      if ((rl >> 5) < na && r < mrows) {
+        const u32x4_t t = *(const u32x4_t*)(stg + rl * XR_EPI_ROW + 16 * c);
+        *(u32x4_t*)((uint16_t*)g.out + ((long long)row0 + r) * g.N + n0 + wn * 128 + 8 * c) = t;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 path (MOE_F32): one thread per output element, fp32 fma in ascending order.
 // ---------------------------------------------------------------------------
 struct F32Args {
@@ -923,9 +1355,10 @@ struct FfnPlan {
   int S, has_shared;
   long long Tk, rows, mt_bound;
   int tm;   // rows per GEMM tile (the segment table counts tiles of this height)
+  bool mx_ring;   // MXFP8 on grouped_gemm_mx_ring_kernel (both GEMMs)
 };
 
-static FfnPlan plan_of(void* ws, int T, int E, int k, int inter, int dtype, bool has_shared) {
+static FfnPlan plan_of(void* ws, int T, int d, int E, int k, int inter, int dtype, bool has_shared) {
   const FfnWs L = ffn_ws(T, E, k, inter, dtype);
   char* w = (char*)ws;
   FfnPlan p;
@@ -939,7 +1372,10 @@ static FfnPlan plan_of(void* ws, int T, int E, int k, int inter, int dtype, bool
   p.S = E + p.has_shared;
   p.Tk = (long long)T * k;
   p.rows = p.Tk + (has_shared ? T : 0);
-  p.tm = dtype == MOE_MXFP8 ? 64 * MOE_MX_WM : BM;
+  // the ring tiles GEMM2's output by XR_N columns and loads scales 16 bytes (512 K) at a time
+  p.mx_ring = MOE_MX_RING && dtype == MOE_MXFP8 && d % XR_N == 0 && d % XR_GB == 0 &&
+              inter % XR_GB == 0;
+  p.tm = p.mx_ring ? XR_M : dtype == MOE_MXFP8 ? 64 * MOE_MX_WM : BM;
   p.mt_bound = (p.Tk + (long long)E * (p.tm - 1)) / p.tm + (has_shared ? (T + p.tm - 1) / p.tm : 0);
   return p;
 }
@@ -1002,7 +1438,7 @@ static moe_status run_gate_up(const void* x, const uint8_t* xs, int dtype, int T
     g.sb1s = shared ? shared->w3_scale : nullptr;
     g.K = d;
     g.N = inter;
-    g.NT = inter / (16 * MOE_MX_FN * MOE_MX_WN);
+    g.NT = p.mx_ring ? inter / (XR_N / 2) : inter / (16 * MOE_MX_FN * MOE_MX_WN);
     g.mstart = p.mstart;
     g.rowstart = p.rowstart;
     g.rowcount = p.rowcount;
@@ -1012,8 +1448,11 @@ static moe_status run_gate_up(const void* x, const uint8_t* xs, int dtype, int T
     g.flag = p.flag;
     const long long grid = (p.mt_bound * g.NT + kXcds - 1) / kXcds * kXcds;
     if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
-    grouped_gemm_mx_kernel<0, MOE_MX_WM, MOE_MX_WN, MOE_MX_FN>
-        <<<(unsigned)grid, 64 * MOE_MX_WM * MOE_MX_WN, 0, s>>>(g);
+    if (p.mx_ring)
+      grouped_gemm_mx_ring_kernel<0><<<(unsigned)grid, 256, 0, s>>>(g);
+    else
+      grouped_gemm_mx_kernel<0, MOE_MX_WM, MOE_MX_WN, MOE_MX_FN>
+          <<<(unsigned)grid, 64 * MOE_MX_WM * MOE_MX_WN, 0, s>>>(g);
   } else if (dtype == MOE_BF16) {
     GemmArgs g{};
     g.a = (const uint16_t*)x;
@@ -1095,10 +1534,12 @@ static moe_status run_down(int dtype, int T, int d, int E, int k, int inter,
     // the configured tile where its width divides d, else 64-column tiles of the same
     // height (same bits: every output is the same MFMA chain)
     const bool wide = d % (32 * MOE_MX_FN * MOE_MX_WN) == 0;
-    g.NT = wide ? d / (32 * MOE_MX_FN * MOE_MX_WN) : d / 64;
+    g.NT = p.mx_ring ? d / XR_N : wide ? d / (32 * MOE_MX_FN * MOE_MX_WN) : d / 64;
     const long long grid = (p.mt_bound * g.NT + kXcds - 1) / kXcds * kXcds;
     if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
-    if (wide)
+    if (p.mx_ring)
+      grouped_gemm_mx_ring_kernel<1><<<(unsigned)grid, 256, 0, s>>>(g);
+    else if (wide)
       grouped_gemm_mx_kernel<1, MOE_MX_WM, MOE_MX_WN, MOE_MX_FN>
           <<<(unsigned)grid, 64 * MOE_MX_WM * MOE_MX_WN, 0, s>>>(g);
     else
@@ -1170,7 +1611,7 @@ extern "C" moe_status moe_expert_ffn_gate_up(const void* x, const uint8_t* x_sca
   if (dtype == MOE_MXFP8 && (!aligned(x_scale, 4) || !mx_bank_aligned(routed) ||
                              (shared && !mx_bank_aligned(shared))))
     return MOE_ERR_INVALID_ARG;
-  const FfnPlan p = plan_of(ws, T, E, k, inter, dtype, shared != nullptr);
+  const FfnPlan p = plan_of(ws, T, d, E, k, inter, dtype, shared != nullptr);
   return run_gate_up(x, x_scale, dtype, T, d, E, k, inter, routed, shared, offsets, perm, p,
                      (hipStream_t)stream);
 }
@@ -1186,7 +1627,7 @@ extern "C" moe_status moe_expert_ffn_down(int dtype, int T, int d, int E, int k,
   if (dtype != MOE_F32 && !aligned(out, 16)) return MOE_ERR_INVALID_ARG;
   if (dtype == MOE_MXFP8 && (!mx_bank_aligned(routed) || (shared && !mx_bank_aligned(shared))))
     return MOE_ERR_INVALID_ARG;
-  const FfnPlan p = plan_of(ws, T, E, k, inter, dtype, shared != nullptr);
+  const FfnPlan p = plan_of(ws, T, d, E, k, inter, dtype, shared != nullptr);
   return run_down(dtype, T, d, E, k, inter, routed, shared, out, p, (hipStream_t)stream);
 }
 
@@ -1205,7 +1646,7 @@ extern "C" moe_status moe_expert_ffn(const void* x, const uint8_t* x_scale, int 
   if (dtype == MOE_MXFP8 && (!aligned(x_scale, 4) || !mx_bank_aligned(routed) ||
                              (shared && !mx_bank_aligned(shared))))
     return MOE_ERR_INVALID_ARG;
-  const FfnPlan p = plan_of(ws, T, E, k, inter, dtype, shared != nullptr);
+  const FfnPlan p = plan_of(ws, T, d, E, k, inter, dtype, shared != nullptr);
   hipStream_t s = (hipStream_t)stream;
   if ((st = run_gate_up(x, x_scale, dtype, T, d, E, k, inter, routed, shared, offsets, perm, p, s)) !=
       MOE_OK)

@@ -49,6 +49,9 @@ SMALL = [
     (200, 128, 128, 16, 4, True, True, "mxfp8"),
     (300, 256, 256, 4, 2, True, False, "mxfp8"),   # 150 rows/expert: 2 row tiles, ragged
     (1, 128, 128, 384, 8, False, True, "mxfp8"),
+    # d and I multiples of 512: the MXFP8 GEMMs run on the 256-row LDS-ring tiles
+    (700, 1024, 512, 16, 4, True, True, "mxfp8"),   # 175 rows/expert (1 ragged tile); shared 3 tiles
+    (1500, 512, 512, 4, 2, False, False, "mxfp8"),  # 750 rows/expert: 3 row tiles, ragged
     (50, 64, 32, 16, 3, True, True, "f32"),
     (5, 96, 40, 1024, 32, True, False, "f32"),     # largest E and k
 ]
@@ -204,9 +207,9 @@ def test_nonfinite_input_is_flagged():
     assert ei.value.status == 5                # MOE_ERR_NONFINITE
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "mxfp8"])
-def test_determinism_permutation_and_batch_invariance_small(dtype):
-    wl = synth.Workload("inv", T=333, d=256, inter=128, E=64, k=8, shared=True, bias=True,
+@pytest.mark.parametrize("dtype,d,I", [("bf16", 256, 128), ("mxfp8", 256, 128), ("mxfp8", 1024, 512)])
+def test_determinism_permutation_and_batch_invariance_small(dtype, d, I):
+    wl = synth.Workload("inv", T=333, d=d, inter=I, E=64, k=8, shared=True, bias=True,
                         dtype=dtype, seed=21)
     inp = _inputs(wl)
     say("case invariance small")

@@ -884,32 +884,31 @@ void grouped_gemm_mx_kernel(MxArgs g) {
 // ---------------------------------------------------------------------------
 constexpr int XR_M = 256;                        // tile rows
 constexpr int XR_N = 256;                        // staged B rows
-constexpr int XR_K = 64;                         // K bytes per ring step (one MFMA k range)
-constexpr int XR_ST = 4;                         // ring stages
-constexpr int XR_P = 4;                          // steps of loads in flight
+constexpr int XR_K = 128;                        // K bytes per ring step (two MFMA k ranges)
+constexpr int XR_ST = 2;                         // ring stages
 constexpr int XR_A = 0, XR_B = XR_M * XR_K;      // tile offsets within a stage
-constexpr int XR_STAGE = (XR_M + XR_N) * XR_K;   // 32 KB
-constexpr int XR_GK = 8;                         // steps per scale group (16 E8M0 bytes per row)
-constexpr int XR_GB = XR_GK * XR_K;              // K per scale group
+constexpr int XR_STAGE = (XR_M + XR_N) * XR_K;   // 64 KB
+constexpr int XR_GS = 4;                         // steps per scale group (16 E8M0 bytes per row)
+constexpr int XR_GB = XR_GS * XR_K;              // K per scale group
 constexpr int XR_SC = XR_ST * XR_STAGE;          // two scale-group buffers after the stages
 constexpr int XR_SCB = (XR_M + XR_N) * 16;       // bytes per scale-group buffer (A rows, then B)
 constexpr int XR_LDS = XR_SC + 2 * XR_SCB;       // 144 KB
-constexpr int XR_DL = (XR_M + XR_N) * XR_K / 1024 / 4;   // data loads per wavefront per step (8)
-constexpr int XR_EPI_ROW = 272;                  // epilogue staging: bytes per local row
-constexpr int XR_EPI = 128 * XR_EPI_ROW;         // epilogue staging per wavefront (34 KB)
-static_assert(XR_LDS <= 160 * 1024 && 4 * XR_EPI <= XR_LDS, "LDS budget");
+constexpr int XR_EPI_ROW = 144;                  // epilogue staging: bytes per local row
+constexpr int XR_EPI = 128 * XR_EPI_ROW;         // epilogue staging per wavefront (18 KB)
+static_assert(XR_LDS <= 160 * 1024 && 8 * XR_EPI <= XR_LDS, "LDS budget");
 
-// slot of the 16-byte chunk c of row r: c ^ ((r >> 2) & 3); the sixteen rows that one
+// slot of the 16-byte chunk c of row r: c ^ ((r >> 1) & 7); the sixteen rows that one
 // ds_read_b128 phase touches (one chunk each) then fall in distinct banks
-__device__ __forceinline__ int xr_swz(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int xr_swz(int r) { return (r >> 1) & 7; }
 
-__device__ __forceinline__ void xr_load16(uint32_t lds, const void* src) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory");
-}
-// the same from a wavefront-uniform base plus a 32-bit per-lane byte offset
+// global_load_lds_dwordx4 (lane l writes its 16 bytes at lds + 16 l) from a
+// wavefront-uniform base plus a 32-bit per-lane offset, or from a per-lane address
 __device__ __forceinline__ void xr_load16(uint32_t lds, uint32_t off, const void* base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base)
                : "memory");
+}
+__device__ __forceinline__ void xr_load16(uint32_t lds, const void* src) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory");
 }
 // Wait until at most N ring loads of this wavefront are outstanding and every LDS
 // access of this wavefront has completed, then meet the other wavefronts.
@@ -918,166 +917,144 @@ __device__ __forceinline__ void xr_sync() {
   static_assert(N >= 0 && N <= 63, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
-__device__ __forceinline__ void xr_sync_n(int n) {
-  switch (n) {
-    case 2: xr_sync<2>(); break;
-    case 8: xr_sync<8>(); break;
-    case 10: xr_sync<10>(); break;
-    case 16: xr_sync<16>(); break;
-    case 18: xr_sync<18>(); break;
-    case 24: xr_sync<24>(); break;
-    default: xr_sync<0>(); break;   // 0, or any other count: wait for everything (still correct)
-  }
-}
 
-// Fragments of one K step for a wavefront: NA of its row blocks, 4 B blocks, scales.
-template <int NA>
+// One 64-wide k range of fragments: NB of the wavefront's 4 row blocks, 2 B blocks.
+template <int NB>
 struct XrFrag {
-  i32x8_t a[NA > 0 ? NA : 1], b[4];
-  int sa[NA > 0 ? NA : 1], sb[4];
+  i32x8_t a[NB > 0 ? NB : 1], b[2];
+};
+// The E8M0 scales of one step for a lane: word w of a block holds, from its low byte, the
+// scales of k-blocks 4 (j % 4) + lane / 32 + 0, 1, 2, ... of the row, so the first k range
+// takes byte 0 (MFMA op_sel 0) and the second byte 2 (op_sel 2).
+template <int NB>
+struct XrScale {
+  int a[NB > 0 ? NB : 1], b[2];
 };
 
-// Read step j's fragments from stage st / scale buffer scb.  aof/bof: this lane's
-// first chunk (the second is XOR 32); asf/bsf: its scale byte of k-block 0; sc: the
-// step's first k-block within the scale group.
-template <int NA>
-__device__ __forceinline__ void xr_read(XrFrag<NA>& f, const uint8_t* st, const uint8_t* scb, uint32_t aof,
-                                        uint32_t bof, uint32_t asf, uint32_t bsf, int sc) {
+// Read k range `half` (0 or 1) of the stage at st.  aof/bof: this lane's chunk of k
+// range 0 (k range 1 is XOR 64, the second 16 bytes XOR 32).
+template <int NB>
+__device__ __forceinline__ void xr_read(XrFrag<NB>& f, const uint8_t* st, uint32_t aof, uint32_t bof,
+                                        int half) {
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const uint32_t o = bof + nb * 32 * XR_K;
+  for (int nb = 0; nb < 2; ++nb) {
+    const uint32_t o = (bof ^ (64 * half)) + nb * 32 * XR_K;
     const u32x4_t lo = *(const u32x4_t*)(st + o);
     const u32x4_t hi = *(const u32x4_t*)(st + (o ^ 32));
     f.b[nb] = (i32x8_t){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    f.sb[nb] = scb[bsf + nb * 32 * 16 + sc];
   }
 #pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const uint32_t o = aof + i * 64 * XR_K;   // row blocks wm, wm + 2, ...: 64 rows apart
+  for (int mb = 0; mb < NB; ++mb) {
+    const uint32_t o = (aof ^ (64 * half)) + mb * 32 * XR_K;
     const u32x4_t lo = *(const u32x4_t*)(st + o);
     const u32x4_t hi = *(const u32x4_t*)(st + (o ^ 32));
-    f.a[i] = (i32x8_t){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    f.sa[i] = scb[asf + i * 64 * 16 + sc];
+    f.a[mb] = (i32x8_t){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   }
 }
-
-// An empty asm that reads every accumulator: the MFMAs of a step are then issued before
-// the ring loads that follow it in program order (the compiler would otherwise sink
-// them past those loads, next to their next use).
-__device__ __forceinline__ void xr_pin(const f32x16_t (&acc)[4][4]) {
-  asm volatile("" ::"a"(acc[0][0]), "a"(acc[0][1]), "a"(acc[0][2]), "a"(acc[0][3]), "a"(acc[1][0]),
-               "a"(acc[1][1]), "a"(acc[1][2]), "a"(acc[1][3]), "a"(acc[2][0]), "a"(acc[2][1]),
-               "a"(acc[2][2]), "a"(acc[2][3]), "a"(acc[3][0]), "a"(acc[3][1]), "a"(acc[3][2]),
-               "a"(acc[3][3]));
+// asf/bsf: this lane's row's 16-byte scale group in the scale buffer scb; sc: the step's
+// first k-block within the group (a multiple of 4); sh = 8 (lane / 32).
+template <int NB>
+__device__ __forceinline__ void xr_read_scales(XrScale<NB>& sc4, const uint8_t* scb, uint32_t asf,
+                                               uint32_t bsf, int sc, int sh) {
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) sc4.b[nb] = (int)(*(const uint32_t*)(scb + bsf + nb * 32 * 16 + sc) >> sh);
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb)
+    sc4.a[mb] = (int)(*(const uint32_t*)(scb + asf + mb * 32 * 16 + sc) >> sh);
 }
 
-template <int NA>
-__device__ __forceinline__ void xr_mfma(const XrFrag<NA>& f, f32x16_t (&acc)[4][4]) {
-#pragma unroll
-  for (int i = 0; i < NA; ++i)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-      acc[i][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[nb], acc[i][nb], 0, 0, 0,
-                                                                   f.sa[i], 0, f.sb[nb]);
+// An empty asm that reads every accumulator: the MFMAs before it are issued before the
+// ring loads and barriers that follow it in program order (the compiler would otherwise
+// sink them next to their next use).
+__device__ __forceinline__ void xr_pin(const f32x16_t (&acc)[4][2]) {
+  asm volatile("" ::"a"(acc[0][0]), "a"(acc[0][1]), "a"(acc[1][0]), "a"(acc[1][1]), "a"(acc[2][0]),
+               "a"(acc[2][1]), "a"(acc[3][0]), "a"(acc[3][1]));
 }
 
-// The K loop for a wavefront that multiplies NA of its 4 row blocks (NA = 0: it only
-// loads and synchronises).  The data of step j is loaded at step j - 4 into stage j % 4;
-// its fragments are read into registers at step j - 1 (so stage j % 4 is free again at
-// step j), and multiplied at step j.  Scale group g (steps 8 g .. 8 g + 7) is loaded at
-// step 8 (g - 1), after that step's data, into buffer g % 2.
+template <int NB, int SEL>
+__device__ __forceinline__ void xr_mfma(const XrFrag<NB>& f, const XrScale<NB>& sc4, f32x16_t (&acc)[4][2]) {
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[mb], f.b[nb], acc[mb][nb], 0, 0, SEL,
+                                                                   sc4.a[mb], SEL, sc4.b[nb]);
+}
+
 // Load sources: A rows at abase + aoff[i] (wavefront-uniform base, per-lane offset), B
-// rows at bbase[i] + boff[i], A scale groups at asbase + asoff, B scale groups at bsp.
+// rows at bbase + boff[i], scale groups at sbase + soff (A rows, waves 0..3) or at the
+// per-lane bsp (B rows, waves 4..7).
 struct XrSrc {
   const uint8_t* abase;
-  const uint8_t* bbase[4];
-  const uint8_t* asbase;
+  const uint8_t* bbase;
+  const uint8_t* sbase;
   const uint8_t* bsp;
-  uint32_t aoff[4], boff[4], asoff;
+  uint32_t aoff[4], boff[4], soff;
 };
 
-template <int NA>
+// The K loop of a wavefront that multiplies NB of its 4 row blocks (NB = 0: it only
+// loads and synchronises).  Step j (K bytes 128 j .. 128 j + 127) lives in stage j % 2.
+// At step j: wait for its data, meet (every wavefront is then done with step j - 1, whose
+// stage takes step j + 1's loads), multiply.  Scale group g (steps 4 g .. 4 g + 3) goes
+// out at step 4 (g - 1), after that step's data, into buffer g % 2.
+template <int NB>
 __device__ __forceinline__ void xr_kloop(const uint8_t* ring, uint32_t ring_lds, int nsteps, const XrSrc& src,
                                          int wave, uint32_t aof, uint32_t bof, uint32_t asf, uint32_t bsf,
-                                         f32x16_t (&acc)[4][4]) {
+                                         int sh, f32x16_t (&acc)[4][2]) {
   const uint32_t la = XR_A + wave * 4096, lb = XR_B + wave * 4096;
-  const int ngroups = nsteps / XR_GK;
+  const uint32_t ls = wave < 4 ? wave * 1024 : XR_M * 16 + (wave - 4) * 1024;
+  const int ngroups = nsteps / XR_GS;
   auto issue = [&](int j) {
-    const uint32_t st = ring_lds + (uint32_t)(j % XR_ST) * XR_STAGE;
+    const uint32_t st = ring_lds + (uint32_t)(j & 1) * XR_STAGE;
     const int k0 = j * XR_K;
 #pragma unroll
     for (int i = 0; i < 4; ++i) xr_load16(st + la + 1024 * i, src.aoff[i], src.abase + k0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xr_load16(st + lb + 1024 * i, src.boff[i], src.bbase[i] + k0);
+    for (int i = 0; i < 4; ++i) xr_load16(st + lb + 1024 * i, src.boff[i], src.bbase + k0);
   };
   auto issue_scales = [&](int grp) {
-    const uint32_t sb = ring_lds + XR_SC + (uint32_t)(grp & 1) * XR_SCB;
-    xr_load16(sb + wave * 1024, src.asoff, src.asbase + 16 * grp);
-    xr_load16(sb + XR_M * 16 + wave * 1024, src.bsp + 16 * grp);
+    const uint32_t dst = ring_lds + XR_SC + (uint32_t)(grp & 1) * XR_SCB + ls;
+    if (wave < 4)
+      xr_load16(dst, src.soff, src.sbase + 16 * grp);
+    else
+      xr_load16(dst, src.bsp + 16 * grp);
   };
-  auto scales_at = [&](int i) { return i >= 0 && i % XR_GK == 0 && i / XR_GK + 1 < ngroups ? 2 : 0; };
-  auto read = [&](XrFrag<NA>& f, int j) {
-    if constexpr (NA > 0)
-      xr_read<NA>(f, ring + (j % XR_ST) * XR_STAGE, ring + XR_SC + ((j / XR_GK) & 1) * XR_SCB, aof, bof,
-                  asf, bsf, 2 * (j % XR_GK));
-  };
-  // wait for step j's data: the loads issued after it (at step j - 4) are the scale
-  // group of that step, the data of steps j+1 .. j+2 (issued by the end of step j - 1)
-  // and the scale groups of steps j-3 .. j-1 (loads complete in issue order)
-  auto sync_for = [&](int j) {
-    int after = 0;
-    if (j == 0) {   // after the prologue: the data of steps 1 .. 3
-      xr_sync_n(XR_DL * (min(nsteps, XR_P) - 1));
-      return;
-    }
-    for (int i = j + 1; i <= j + 2; ++i) after += (i < nsteps) ? XR_DL : 0;
-    for (int i = j - 4; i <= j - 2; ++i) after += scales_at(i);
-    xr_sync_n(after);
-  };
+  auto scales_at = [&](int j) { return j >= 0 && j % XR_GS == 0 && j / XR_GS + 1 < ngroups; };
 
-  XrFrag<NA> f0, f1;
   issue_scales(0);
-  for (int j = 0; j < XR_P && j < nsteps; ++j) issue(j);
-  // step j (< nsteps - 1): make step j+1 visible, refill the ring, read step j+1's
-  // fragments, multiply step j's
-  auto step = [&](int j, XrFrag<NA>& cur, XrFrag<NA>& nxt) {
-    sync_for(j + 1);
-    read(nxt, j + 1);
-    if constexpr (NA > 0) {
-      xr_mfma<NA>(cur, acc);
-      // interleave the fragment reads of step j+1 with the MFMAs of step j
-      constexpr int kRd = 6 * NA + 12;   // ds_read_b128 and ds_read_u8 of one step
-      constexpr int kMf = 4 * NA;
-      constexpr int kPer = (kRd + kMf - 1) / kMf;
-#pragma unroll
-      for (int m = 0; m < kMf; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, kPer, 0);  // then a few LDS reads
-      }
+  issue(0);
+  for (int j = 0; j < nsteps; ++j) {
+    // step j's data went out at step j - 1 (or before the loop), followed only by that
+    // step's scale group (loads complete in issue order)
+    if (scales_at(j - 1))
+      xr_sync<1>();
+    else
+      xr_sync<0>();
+    if (j + 1 < nsteps) issue(j + 1);
+    if (scales_at(j)) issue_scales(j / XR_GS + 1);
+    if constexpr (NB > 0) {
+      const uint8_t* st = ring + (j & 1) * XR_STAGE;
+      const uint8_t* scb = ring + XR_SC + ((j / XR_GS) & 1) * XR_SCB;
+      XrScale<NB> sc4;
+      xr_read_scales<NB>(sc4, scb, asf, bsf, (j % XR_GS) * (XR_K / 32), sh);
+      XrFrag<NB> f;
+      xr_read<NB>(f, st, aof, bof, 0);
+      xr_mfma<NB, 0>(f, sc4, acc);
+      xr_read<NB>(f, st, aof, bof, 1);
+      xr_mfma<NB, 2>(f, sc4, acc);
       xr_pin(acc);
     }
-    if (j + XR_P < nsteps) issue(j + XR_P);
-    if (scales_at(j)) issue_scales(j / XR_GK + 1);
-  };
-  sync_for(0);
-  read(f0, 0);
-  // nsteps is even (K is a multiple of 512)
-  int j = 0;
-  for (; j + 2 < nsteps; j += 2) {
-    step(j, f0, f1);
-    step(j + 1, f1, f0);
   }
-  step(j, f0, f1);
-  if constexpr (NA > 0) xr_mfma<NA>(f1, acc);
 }
 
-// MXFP8 grouped GEMM, 256 x 256 tiles, four wavefronts (2 x 2), each 4 row blocks x
-// 4 B blocks of 32 x 32.  Wavefront (wm, wn) owns the row blocks wm, wm + 2, wm + 4,
-// wm + 6, so a short tile splits its valid 32-row blocks evenly over the SIMDs.
+// MXFP8 grouped GEMM, 256 x 256 tiles, eight wavefronts (2 along M x 4 along N, two per
+// SIMD), each 4 row blocks x 2 B blocks of 32 x 32.  A wavefront whose 32-row blocks
+// hold no valid row skips their MFMAs, so a short tile costs MFMA time in proportion to
+// its valid 32-row blocks on the busier half.
 template <int MODE>
-__global__ __launch_bounds__(256) void grouped_gemm_mx_ring_kernel(MxArgs g) {
+__global__ __launch_bounds__(512) void grouped_gemm_mx_ring_kernel(MxArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[XR_LDS];
 
   // ---- tile decode (as grouped_gemm_mx_kernel, tiles of XR_M rows) ----
@@ -1106,7 +1083,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_mx_ring_kernel(MxArgs g) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int KB = g.K / 32;   // scale bytes per row
 
   int bad = 0;
@@ -1136,125 +1113,126 @@ __global__ __launch_bounds__(256) void grouped_gemm_mx_ring_kernel(MxArgs g) {
     return (long long)n0 + r;
   };
 
-  // ---- loader: wavefront w fills A rows and B rows 64 w .. 64 w + 63 (four loads of 16
-  //      rows each; lane l -> row + l / 4, slot l % 4 <- chunk slot ^ swz(row)) and the
-  //      16-byte scale groups of A rows and B rows 64 w + l.  Every byte offset from a
-  //      load's base fits 32 bits (one activation matrix, or one expert's matrix). ----
+  // ---- loader: wavefront w fills A rows and B rows 32 w .. 32 w + 31 (four loads of 8
+  //      rows each; lane l -> row + l / 8, slot l % 8 <- chunk slot ^ swz(row); the B rows
+  //      are one 32-row block, so one bank) and the 16-byte scale groups of A rows
+  //      64 w + l (w < 4) or B rows 64 (w - 4) + l.  Every byte offset from a load's base
+  //      fits 32 bits (one activation matrix, or one expert's matrix). ----
   XrSrc src;
   src.abase = g.a;
-  src.asbase = g.as;
+  src.sbase = g.as;
+  {
+    const uint8_t *bank, *sbank;
+    b_row(32 * wave, bank, sbank);
+    src.bbase = bank + e * g.N * (long long)g.K;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = 64 * wave + 16 * i + (lane >> 2);   // 32-row block 2 wave + i / 2: uniform
-    const int chunk = (lane & 3) ^ xr_swz(r);
+    const int r = 32 * wave + 8 * i + (lane >> 3);
+    const int chunk = (lane & 7) ^ xr_swz(r);
     src.aoff[i] = (uint32_t)(a_src(r) * g.K + 16 * chunk);
     const uint8_t *bank, *sbank;
     const long long br = b_row(r, bank, sbank);
-    src.bbase[i] = bank + e * g.N * (long long)g.K;
     src.boff[i] = (uint32_t)(br * g.K + 16 * chunk);
   }
-  src.asoff = (uint32_t)(a_src(64 * wave + lane) * KB);
+  src.soff = (uint32_t)(a_src(64 * (wave & 3) + lane) * KB);
   {
     const uint8_t *bank, *sbank;   // GEMM1: W1 scales for lanes 0..31, W3 for 32..63
-    const long long br = b_row(64 * wave + lane, bank, sbank);
+    const long long br = b_row(64 * (wave & 3) + lane, bank, sbank);
     src.bsp = sbank + (e * g.N + br) * (long long)KB;
   }
   if (bad) raise_flag(g.flag, kFlagCorrupt);
 
   // ---- fragment offsets within a stage: lane reads row (block base + lane % 32),
-  //      chunks lane / 32 (bytes 0..15) and 2 + lane / 32 (bytes 16..31: offset ^ 32) ----
+  //      chunks lane / 32 and 2 + lane / 32 of the k range ----
   const int j32 = lane & 31, hh = lane >> 5;
-  const int ra = 32 * wm + j32, rb = 128 * wn + j32;
+  const int ra = 128 * wm + j32, rb = 64 * wn + j32;
   const uint32_t aof = XR_A + ra * XR_K + 16 * (hh ^ xr_swz(ra));
   const uint32_t bof = XR_B + rb * XR_K + 16 * (hh ^ xr_swz(rb));
-  const uint32_t asf = ra * 16 + hh, bsf = XR_M * 16 + rb * 16 + hh;   // within a scale buffer
+  const uint32_t asf = ra * 16, bsf = XR_M * 16 + rb * 16;   // within a scale buffer
+  const int sh = 8 * hh;
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][2];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_u8*)ring;
   const int nsteps = g.K / XR_K;
-  // this wavefront's row blocks wm + 2 i that hold a valid row (uniform per wavefront)
-  const int nvb = (mrows + 31) >> 5;
-  const int na = min(4, max(0, (nvb - wm + 1) >> 1));
-  switch (na) {
-    case 4: xr_kloop<4>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, acc); break;
-    case 3: xr_kloop<3>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, acc); break;
-    case 2: xr_kloop<2>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, acc); break;
-    case 1: xr_kloop<1>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, acc); break;
-    default: xr_kloop<0>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, acc); break;
+  // 32-row blocks of this wavefront that hold a valid row (uniform per wavefront)
+  const int nb_act = min(4, max(0, (mrows - wm * 128 + 31) >> 5));
+  switch (nb_act) {
+    case 4: xr_kloop<4>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, sh, acc); break;
+    case 3: xr_kloop<3>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, sh, acc); break;
+    case 2: xr_kloop<2>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, sh, acc); break;
+    case 1: xr_kloop<1>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, sh, acc); break;
+    default: xr_kloop<0>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, sh, acc); break;
   }
 
-  // ---- epilogue through LDS: each wavefront stages its 128 x (64 or 128) outputs
-  //      row-major in its own 34 KB of the (now idle) ring, then writes whole MX blocks
+  // ---- epilogue through LDS: each wavefront stages its 128 x (32 or 64) outputs
+  //      row-major in its own 18 KB of the (now idle) ring, then writes whole MX blocks
   //      (GEMM1) or 16-byte row chunks (GEMM2).  Accumulator element v of a lane is
   //      C[i][j], j = lane % 32, i = 8 (v / 4) + 4 (lane / 32) + v % 4; the wavefront's
-  //      local row 32 ib + i is tile row 32 (wm + 2 ib) + i. ----
+  //      local row 32 mb + i is tile row 128 wm + 32 mb + i. ----
   __syncthreads();   // every wavefront is done reading the ring
   uint8_t* stg = ring + wave * XR_EPI;
 #pragma unroll
-  for (int ib = 0; ib < 4; ++ib) {
-    if (ib >= na) break;
+  for (int mb = 0; mb < 4; ++mb) {
+    if (mb >= nb_act) break;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int rl = 32 * ib + 8 * (v >> 2) + 4 * hh + (v & 3);
+      const int rl = 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
       if (MODE == 0) {
-        // B blocks (0, 1) and (2, 3) are the W1 and W3 halves of 32 features each
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-          *(float*)(stg + rl * XR_EPI_ROW + (32 * p + j32) * 4) =
-              silu_f32(acc[ib][2 * p][v]) * acc[ib][2 * p + 1][v];
+        // B blocks 0 and 1 are the W1 and W3 halves of the same 32 features
+        *(float*)(stg + rl * XR_EPI_ROW + j32 * 4) = silu_f32(acc[mb][0][v]) * acc[mb][1][v];
       } else {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          *(uint16_t*)(stg + rl * XR_EPI_ROW + (32 * nb + j32) * 2) = f32_to_bf16(acc[ib][nb][v]);
+        for (int nb = 0; nb < 2; ++nb)
+          *(uint16_t*)(stg + rl * XR_EPI_ROW + (32 * nb + j32) * 2) = f32_to_bf16(acc[mb][nb][v]);
       }
     }
   }
   // (a wavefront reads back only what it wrote: its LDS accesses complete in order)
   if (MODE == 0) {
-    // lane l: local row 32 q + l / 2, MX block l % 2 (32 features) of the wavefront's 64
-    const int pb = lane & 1;
+    // lane l: local rows l and 64 + l, one MX block (the wavefront's 32 features) each
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (q >= na) break;
-      const int rl = 32 * q + (lane >> 1);
-      const int r = 32 * (wm + 2 * q) + (lane >> 1);
-      if (r < mrows) {
+    for (int q2 = 0; q2 < 2; ++q2) {
+      const int rl = 64 * q2 + lane;
+      const int r = 128 * wm + rl;
+      if ((rl >> 5) < nb_act && r < mrows) {
         float hv[32];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          const float4 t = *(const float4*)(stg + rl * XR_EPI_ROW + pb * 128 + 16 * c);
+          const float4 t = *(const float4*)(stg + rl * XR_EPI_ROW + 16 * c);
           hv[4 * c] = t.x;
           hv[4 * c + 1] = t.y;
           hv[4 * c + 2] = t.z;
           hv[4 * c + 3] = t.w;
         }
         const long long orow = (long long)row0 + r;
-        const int col = n0 + (2 * wn + pb) * 32;
+        const int col = n0 + 32 * wn;
         mx_store_block(hv, (uint8_t*)g.out + orow * g.N + col, g.out_scale + orow * (g.N / 32) + col / 32);
       }
     }
   } else {
-    // lane l: local row 4 q + l / 16, 16-byte chunk l % 16 of the row's 128 outputs
-    const int c = lane & 15;
+    // lane l: local row 8 q + l / 8, 16-byte chunk l % 8 of the row's 64 outputs
+    const int c = lane & 7;
 #pragma unroll 4
-    for (int q = 0; q < 32; ++q) {
-      const int rl = 4 * q + (lane >> 4);
-      const int r = 32 * (wm + 2 * (rl >> 5)) + (rl & 31);
-      if ((rl >> 5) < na && r < mrows) {
+    for (int q2 = 0; q2 < 16; ++q2) {
+      const int rl = 8 * q2 + (lane >> 3);
+      const int r = 128 * wm + rl;
+      if ((rl >> 5) < nb_act && r < mrows) {
         const u32x4_t t = *(const u32x4_t*)(stg + rl * XR_EPI_ROW + 16 * c);
-        *(u32x4_t*)((uint16_t*)g.out + ((long long)row0 + r) * g.N + n0 + wn * 128 + 8 * c) = t;
+        *(u32x4_t*)((uint16_t*)g.out + ((long long)row0 + r) * g.N + n0 + wn * 64 + 8 * c) = t;
       }
     }
   }
 }
+
 
 // ---------------------------------------------------------------------------
 // fp32 path (MOE_F32): one thread per output element, fp32 fma in ascending order.
@@ -1449,7 +1427,7 @@ static moe_status run_gate_up(const void* x, const uint8_t* xs, int dtype, int T
     const long long grid = (p.mt_bound * g.NT + kXcds - 1) / kXcds * kXcds;
     if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
     if (p.mx_ring)
-      grouped_gemm_mx_ring_kernel<0><<<(unsigned)grid, 256, 0, s>>>(g);
+      grouped_gemm_mx_ring_kernel<0><<<(unsigned)grid, 512, 0, s>>>(g);
     else
       grouped_gemm_mx_kernel<0, MOE_MX_WM, MOE_MX_WN, MOE_MX_FN>
           <<<(unsigned)grid, 64 * MOE_MX_WM * MOE_MX_WN, 0, s>>>(g);
@@ -1538,7 +1516,7 @@ static moe_status run_down(int dtype, int T, int d, int E, int k, int inter,
     const long long grid = (p.mt_bound * g.NT + kXcds - 1) / kXcds * kXcds;
     if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
     if (p.mx_ring)
-      grouped_gemm_mx_ring_kernel<1><<<(unsigned)grid, 256, 0, s>>>(g);
+      grouped_gemm_mx_ring_kernel<1><<<(unsigned)grid, 512, 0, s>>>(g);
     else if (wide)
       grouped_gemm_mx_kernel<1, MOE_MX_WM, MOE_MX_WN, MOE_MX_FN>
           <<<(unsigned)grid, 64 * MOE_MX_WM * MOE_MX_WN, 0, s>>>(g);

@@ -616,13 +616,17 @@ __device__ __forceinline__ void mx_store_h(float h, bool live, uint8_t* code, ui
   }
 }
 
-// Requantise one MX block held in one lane (32 consecutive features of a row) and
-// store its 32 codes (two 16-byte stores) and its scale.  Same scale rule and encoding
-// as mx_store_h.
-__device__ __forceinline__ void mx_store_block(const float (&h)[32], uint8_t* code, uint8_t* scale) {
+// Requantise one MX block (32 consecutive fp32 features of a row, at `src` in LDS, read
+// by one lane) and store its 32 codes (two 16-byte stores) and its scale.  Same scale
+// rule and encoding as mx_store_h.  Two passes over LDS (the block's amax, then the
+// codes) keep few values live.
+__device__ __forceinline__ void mx_store_block(const uint8_t* src, uint8_t* code, uint8_t* scale) {
   float amax = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 32; ++k) amax = fmaxf(amax, fabsf(h[k]));
+  for (int c = 0; c < 8; ++c) {
+    const float4 t = *(const float4*)(src + 16 * c);
+    amax = fmaxf(fmaxf(amax, fmaxf(fabsf(t.x), fabsf(t.y))), fmaxf(fabsf(t.z), fabsf(t.w)));
+  }
   int se;
   uint32_t scode;
   if (amax == 0.0f) {
@@ -635,13 +639,24 @@ __device__ __forceinline__ void mx_store_block(const float (&h)[32], uint8_t* co
     se = min(max(ilogbf(amax) - 8, -127), 127);
     scode = (uint32_t)(se + 127);
   }
+  // v_cvt_pk_fp8_f32 rounds to nearest even onto the OCP E4M3 grid; with its input
+  // clamped to +-448 it equals e4m3_rne_sat (checked on every rounding boundary of
+  // every binade from 2^-20 to 2^10, the subnormal grid, +-0 and the infinities), and
+  // NaN is kept as 0x7F explicitly
   u32x4_t w[2];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    uint32_t d = 0;
+  for (int c = 0; c < 8; ++c) {
+    const float4 t = *(const float4*)(src + 16 * c);
+    const float v[4] = {ldexpf(t.x, -se), ldexpf(t.y, -se), ldexpf(t.z, -se), ldexpf(t.w, -se)};
+    int d = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(v[0], -448.0f), 448.0f),
+                                            fminf(fmaxf(v[1], -448.0f), 448.0f), 0, false);
+    d = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(v[2], -448.0f), 448.0f),
+                                        fminf(fmaxf(v[3], -448.0f), 448.0f), d, true);
+    uint32_t du = (uint32_t)d;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) d |= e4m3_rne_sat(ldexpf(h[4 * k + b], -se)) << (8 * b);
-    w[k >> 2][k & 3] = d;
+    for (int b = 0; b < 4; ++b)
+      if (v[b] != v[b]) du = (du & ~(0xFFu << (8 * b))) | (0x7Fu << (8 * b));
+    w[c >> 2][c & 3] = du;
   }
   *(u32x4_t*)code = w[0];
   *(u32x4_t*)(code + 16) = w[1];
@@ -1204,18 +1219,10 @@ __global__ __launch_bounds__(512) void grouped_gemm_mx_ring_kernel(MxArgs g) {
       const int rl = 64 * q2 + lane;
       const int r = 128 * wm + rl;
       if ((rl >> 5) < nb_act && r < mrows) {
-        float hv[32];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const float4 t = *(const float4*)(stg + rl * XR_EPI_ROW + 16 * c);
-          hv[4 * c] = t.x;
-          hv[4 * c + 1] = t.y;
-          hv[4 * c + 2] = t.z;
-          hv[4 * c + 3] = t.w;
-        }
         const long long orow = (long long)row0 + r;
         const int col = n0 + 32 * wn;
-        mx_store_block(hv, (uint8_t*)g.out + orow * g.N + col, g.out_scale + orow * (g.N / 32) + col / 32);
+        mx_store_block(stg + rl * XR_EPI_ROW, (uint8_t*)g.out + orow * g.N + col,
+                       g.out_scale + orow * (g.N / 32) + col / 32);
       }
     }
   } else {

@@ -90,16 +90,6 @@ __global__ __launch_bounds__(256) void gate_wnorm_kernel(const float* __restrict
   if (tid == 0) wnorm[e] = sqrt(part[0]);
 }
 
-// E4M3 code -> bf16 bits of the same value (every E4M3 value is a bf16 value).
-__device__ __forceinline__ uint16_t e4m3_to_bf16_bits(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  uint32_t b;
-  if (e == 15u && m == 7u) b = 0x7FC0u;                                    // NaN
-  else if (e == 0u) b = __float_as_uint((float)m * 0x1p-9f) >> 16;         // subnormal grid
-  else b = ((e + 120u) << 7) | (m << 4);
-  return (uint16_t)(b | ((c & 0x80u) << 8));
-}
-
 // ---------------------------------------------------------------------------
 // Screen GEMM.  Workgroup tile: 128 experts x 128 tokens; 8 wavefronts, wavefront
 // (we, wt) owns experts 64 we .. +63 (two 32-row A blocks, one per plane triple) and
@@ -212,14 +202,22 @@ __global__ __launch_bounds__(SC_THR) void gate_screen_kernel(const void* __restr
       if (DT == MOE_BF16) {
         *(u32x4_t*)&sX[xr[i]][xc[i]] = rx[i];
       } else {
-        uint16_t b[16];
-#pragma unroll
-        for (int q = 0; q < 16; ++q) b[q] = e4m3_to_bf16_bits((rx[i][q >> 2] >> (8 * (q & 3))) & 0xFFu);
+        // v_cvt_pk_f32_fp8 decodes two codes exactly into fp32; every E4M3 value is a
+        // bf16 value, so its upper 16 bits are the bf16 encoding (NaN stays NaN)
         u32x4_t lo, hi;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          lo[q] = (uint32_t)b[2 * q] | ((uint32_t)b[2 * q + 1] << 16);
-          hi[q] = (uint32_t)b[8 + 2 * q] | ((uint32_t)b[8 + 2 * q + 1] << 16);
+          const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)rx[i][q], false);   // bytes 0, 1
+          const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)rx[i][q], true);    // bytes 2, 3
+          const uint32_t w0 = (__float_as_uint(a[0]) >> 16) | (__float_as_uint(a[1]) & 0xffff0000u);
+          const uint32_t w1 = (__float_as_uint(b[0]) >> 16) | (__float_as_uint(b[1]) & 0xffff0000u);
+          if (q < 2) {
+            lo[2 * q] = w0;
+            lo[2 * q + 1] = w1;
+          } else {
+            hi[2 * q - 4] = w0;
+            hi[2 * q - 3] = w1;
+          }
         }
         *(u32x4_t*)&sX[xr[i]][xc[i]] = lo;
         *(u32x4_t*)&sX[xr[i]][xc[i] + 8] = hi;

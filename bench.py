@@ -173,8 +173,10 @@ def main():
                     "GB_s": gbs(bytes_combine, stage_ms["combine"])},
     }
     dom = max(("ffn_gate_up", "ffn_down"), key=lambda n: stage_ms[n])
+    # the MXFP8 GEMMs run on the LDS-ring kernel where d and I are multiples of 512
+    mx_ring = d % 512 == 0 and I % 512 == 0
     kname = {"f32": "grouped_ffn_f32_kernel", "bf16": "grouped_gemm_bf16_kernel",
-             "mxfp8": "grouped_gemm_mx_kernel"}[wl.dtype]
+             "mxfp8": "grouped_gemm_mx_ring_kernel" if mx_ring else "grouped_gemm_mx_kernel"}[wl.dtype]
     dom_kernel = {"ffn_gate_up": f"{kname}<0> (W1/W3 + SwiGLU)", "ffn_down": f"{kname}<1> (W2)"}[dom]
     gemm_tflops = (flops_gate_up + flops_down) / ((stage_ms["ffn_gate_up"] + stage_ms["ffn_down"]) * 1e-3) / 1e12
     mfma_peak = MXFP8_MFMA_PEAK_TFLOPS if wl.dtype == "mxfp8" else BF16_MFMA_PEAK_TFLOPS

@@ -9,7 +9,7 @@
 namespace moe {
 
 template <bool kF32>
-__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ out,
+__global__ __launch_bounds__(1024) void combine_kernel(const void* __restrict__ out,
                                                       const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ weights, int T, int d,
                                                       int k, int has_shared, long long rows,
@@ -97,9 +97,13 @@ extern "C" moe_status moe_combine(const void* out, int dtype, const int32_t* row
   if ((long long)T * k > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   const long long rows = (long long)T * k + (has_shared ? T : 0);
+  // as few passes of 8-element chunks over the row as 512 threads allow, with every
+  // thread busy in each pass (d = 7168: 896 chunks, 448 threads, 2 passes)
+  const int chunks = d / 8, passes = (chunks + 511) / 512;
+  const int thr = ((chunks + passes - 1) / passes + 63) / 64 * 64;
   if (dtype == MOE_F32)
-    combine_kernel<true><<<T, 256, 0, s>>>(out, row_of, weights, T, d, k, has_shared ? 1 : 0, rows, y);
+    combine_kernel<true><<<T, thr, 0, s>>>(out, row_of, weights, T, d, k, has_shared ? 1 : 0, rows, y);
   else
-    combine_kernel<false><<<T, 256, 0, s>>>(out, row_of, weights, T, d, k, has_shared ? 1 : 0, rows, y);
+    combine_kernel<false><<<T, thr, 0, s>>>(out, row_of, weights, T, d, k, has_shared ? 1 : 0, rows, y);
   return launch_status();
 }

@@ -68,6 +68,32 @@ constexpr bool kGemmNtB = MOE_GEMM_NT_B != 0; // nontemporal weight loads
 #define MOE_GEMM_NARROW_WAVES 1
 #endif
 
+// Tile of this workgroup.  Workgroup b runs on XCD b % 8.  With CHUNK == 0, XCD x takes
+// the x-th eighth of the tile list; otherwise the list is cut into chunks of CHUNK tiles
+// dealt round-robin to the XCDs.  Either way an XCD runs its tiles in list order, so
+// neighbouring tiles (which share weight columns or activation rows) share its L2.
+// The bf16 GEMMs keep contiguous eighths (each XCD streams one contiguous run of the
+// weight banks); the MXFP8 GEMMs deal chunks of 16 (measured: bf16 GEMM2 +12% with
+// chunks, MXFP8 GEMMs -3 to -4%).
+template <int CHUNK>
+__device__ __forceinline__ bool xcd_tile(int total, int& tile) {
+  const int xcd = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
+  if (CHUNK == 0) {
+    const int per = (total + kXcds - 1) / kXcds;
+    if (q >= per) return false;
+    tile = xcd * per + q;
+  } else {
+    tile = ((q / CHUNK) * kXcds + xcd) * CHUNK + q % CHUNK;
+  }
+  return tile < total;
+}
+// Workgroups to launch for at most `bound` tiles.
+static long long tile_grid(long long bound, int chunk) {
+  const long long g = chunk == 0 ? kXcds : (long long)kXcds * chunk;
+  return (bound + g - 1) / g * g;
+}
+constexpr int kMxXcdChunk = 16;
+
 // Segment table: segment s < E is routed expert s (rows offsets[s]..offsets[s+1]-1),
 // segment E is the shared expert (rows T*k .. T*k+T-1).  mstart = exclusive prefix of
 // the per-segment counts of tm-row tiles.  Offsets are clamped into [0, T*k] and flagged if
@@ -149,11 +175,8 @@ void grouped_gemm_bf16_kernel(GemmArgs g) {
 
   // ---- tile decode: XCD-contiguous ranges of the segment-major tile list ----
   const int total = g.mstart[g.S] * g.NT;
-  const int per = (total + kXcds - 1) / kXcds;
-  const int xcd = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
-  if (q >= per) return;
-  const int tile = xcd * per + q;
-  if (tile >= total) return;
+  int tile;
+  if (!xcd_tile<0>(total, tile)) return;
   int lo = 0, hi = g.S;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -344,11 +367,8 @@ __global__ __launch_bounds__(128 * WN) void grouped_gemm_bf16_dma_kernel(GemmArg
 
   // ---- tile decode (identical to grouped_gemm_bf16_kernel) ----
   const int total = g.mstart[g.S] * g.NT;
-  const int per = (total + kXcds - 1) / kXcds;
-  const int xcd = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
-  if (q >= per) return;
-  const int tile = xcd * per + q;
-  if (tile >= total) return;
+  int tile;
+  if (!xcd_tile<0>(total, tile)) return;
   int lo = 0, hi = g.S;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -683,11 +703,8 @@ void grouped_gemm_mx_kernel(MxArgs g) {
   __shared__ uint32_t sBs[TB];
 
   const int total = g.mstart[g.S] * g.NT;
-  const int per = (total + kXcds - 1) / kXcds;
-  const int xcd = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
-  if (q >= per) return;
-  const int tile = xcd * per + q;
-  if (tile >= total) return;
+  int tile;
+  if (!xcd_tile<0>(total, tile)) return;
   int lo = 0, hi = g.S;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -1074,11 +1091,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_mx_ring_kernel(MxArgs g) {
 
   // ---- tile decode (as grouped_gemm_mx_kernel, tiles of XR_M rows) ----
   const int total = g.mstart[g.S] * g.NT;
-  const int per = (total + kXcds - 1) / kXcds;
-  const int xcd = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
-  if (q >= per) return;
-  const int tile = xcd * per + q;
-  if (tile >= total) return;
+  int tile;
+  if (!xcd_tile<kMxXcdChunk>(total, tile)) return;
   int lo = 0, hi = g.S;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -1431,7 +1445,7 @@ static moe_status run_gate_up(const void* x, const uint8_t* xs, int dtype, int T
     g.out = p.h;
     g.out_scale = p.hs;
     g.flag = p.flag;
-    const long long grid = (p.mt_bound * g.NT + kXcds - 1) / kXcds * kXcds;
+    const long long grid = tile_grid(p.mt_bound * g.NT, p.mx_ring ? kMxXcdChunk : 0);
     if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
     if (p.mx_ring)
       grouped_gemm_mx_ring_kernel<0><<<(unsigned)grid, 512, 0, s>>>(g);
@@ -1461,7 +1475,7 @@ static moe_status run_gate_up(const void* x, const uint8_t* xs, int dtype, int T
     g.flag = p.flag;
     const int wn = bf16_wn(inter, 32, MOE_GEMM1_WN);
     g.NT = inter / (32 * wn);
-    const long long grid = (p.mt_bound * g.NT + kXcds - 1) / kXcds * kXcds;
+    const long long grid = tile_grid(p.mt_bound * g.NT, 0);
     if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
     launch_bf16<0>(wn, (unsigned)grid, s, g);
   } else {
@@ -1520,7 +1534,7 @@ static moe_status run_down(int dtype, int T, int d, int E, int k, int inter,
     // height (same bits: every output is the same MFMA chain)
     const bool wide = d % (32 * MOE_MX_FN * MOE_MX_WN) == 0;
     g.NT = p.mx_ring ? d / XR_N : wide ? d / (32 * MOE_MX_FN * MOE_MX_WN) : d / 64;
-    const long long grid = (p.mt_bound * g.NT + kXcds - 1) / kXcds * kXcds;
+    const long long grid = tile_grid(p.mt_bound * g.NT, p.mx_ring ? kMxXcdChunk : 0);
     if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
     if (p.mx_ring)
       grouped_gemm_mx_ring_kernel<1><<<(unsigned)grid, 512, 0, s>>>(g);
@@ -1550,7 +1564,7 @@ static moe_status run_down(int dtype, int T, int d, int E, int k, int inter,
     g.flag = p.flag;
     const int wn = bf16_wn(d, 64, MOE_GEMM2_WN);
     g.NT = d / (64 * wn);
-    const long long grid = (p.mt_bound * g.NT + kXcds - 1) / kXcds * kXcds;
+    const long long grid = tile_grid(p.mt_bound * g.NT, 0);
     if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
     launch_bf16<1>(wn, (unsigned)grid, s, g);
   } else {

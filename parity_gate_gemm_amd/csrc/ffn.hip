@@ -92,7 +92,10 @@ static long long tile_grid(long long bound, int chunk) {
   const long long g = chunk == 0 ? kXcds : (long long)kXcds * chunk;
   return (bound + g - 1) / g * g;
 }
-constexpr int kMxXcdChunk = 16;
+#ifndef MOE_MX_XCD_CHUNK
+#define MOE_MX_XCD_CHUNK 16
+#endif
+constexpr int kMxXcdChunk = MOE_MX_XCD_CHUNK;
 
 // Segment table: segment s < E is routed expert s (rows offsets[s]..offsets[s+1]-1),
 // segment E is the shared expert (rows T*k .. T*k+T-1).  mstart = exclusive prefix of

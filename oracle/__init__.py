@@ -13,6 +13,7 @@ from .moe_oracle import (  # noqa: F401
     softmax_pick_renormalise,
     route,
     route_replay,
+    route_replay_filtered,
     validate_replay_ids,
     dispatch,
     silu,

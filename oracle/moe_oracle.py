@@ -177,6 +177,48 @@ def route_replay(x, w_gate, bias, ids_in, weights_in=None):
     return ids, w, logits
 
 
+def route_replay_filtered(x, w_gate, bias, ids_in, log_tau: float):
+    """Router replay with the plausibility filter.
+
+    Composer 2 Technical Report, §6.2, paragraph on inference and weight sync: a
+    replayed expert whose gate score falls below a plausibility threshold derived from
+    the router's own top-k choice is dropped and replaced with the router's
+    candidates.  The page fixes neither the score nor the threshold; the reading here:
+      * score = the router's softmax probability p_e; threshold = tau * p_(k), where
+        p_(k) is the probability of the router's own k-th choice (k = row width of
+        ids_in) and tau >= 0 is the caller's parameter;
+      * p_e >= tau p_(k) is tested in logit form, l_e - l_(k) >= ln tau, on the
+        correctly rounded logits, the difference rounded once in float64; the caller
+        passes ln tau (-inf keeps every replayed id: plain replay; +inf drops all:
+        learned routing);
+      * dropped columns are refilled, in column order, by the router's top-k ids in
+        rank order that are not among the kept replayed ids;
+      * weights: the router's softmax probabilities at the final ids, renormalised,
+        in column order (as for replay without caller weights).
+    Returns (ids, weights, keep [T, k] bool, logits).
+    """
+    logits = exact_logits(x, w_gate, bias)
+    T, E = logits.shape
+    validate_replay_ids(ids_in, E)
+    q = np.asarray(ids_in, dtype=np.int64)
+    k = q.shape[1]
+    lt = float(log_tau)
+    if math.isnan(lt):
+        raise ValueError("log_tau is NaN")
+    router = topk_ids(logits, k)
+    ids = np.empty((T, k), dtype=np.int64)
+    keep = np.zeros((T, k), dtype=bool)
+    for t in range(T):
+        lk = float(logits[t, router[t, k - 1]])
+        for j in range(k):
+            keep[t, j] = (float(logits[t, q[t, j]]) - lk) >= lt
+        kept = {int(e) for e, kp in zip(q[t], keep[t]) if kp}
+        fill = [int(e) for e in router[t] if int(e) not in kept]
+        for j in range(k):
+            ids[t, j] = q[t, j] if keep[t, j] else fill.pop(0)
+    return ids, softmax_pick_renormalise(logits, ids), keep, logits
+
+
 # ---------------------------------------------------------------------------
 # Dispatch (token permutation into contiguous per-expert segments)
 # ---------------------------------------------------------------------------

@@ -336,6 +336,113 @@ def test_replay_rejects_bad_ids():
 
 
 # ---------------------------------------------------------------------------
+# Replay plausibility filter
+# ---------------------------------------------------------------------------
+def _filter_inputs(seed, T=24, d=32, E=16, k=4, bias=True):
+    rng = np.random.default_rng(seed)
+    x = _bf16_values(rng, (T, d))
+    wg = _f32(rng.standard_normal((d, E)) * 0.2)
+    b = _f32(rng.standard_normal(E) * 0.1) if bias else None
+    ids_in = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    return x, wg, b, ids_in
+
+
+def test_replay_filter_golden():
+    g = json.load(open(os.path.join(GOLDEN, "replay_filter_hand.json")))
+    x = np.asarray(g["x"], dtype=np.float32)
+    wg = np.asarray(g["w_gate_rows"], dtype=np.float32)
+    for c in g["cases"]:
+        ids, w, keep, _ = oracle.route_replay_filtered(x, wg, None, np.asarray(g["ids_in"]), c["log_tau"])
+        assert ids.tolist() == c["ids"]
+        assert keep.tolist() == c["keep"]
+        assert np.allclose(w, np.asarray(c["weights"]), rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_replay_filter_limits_are_replay_and_learned(seed):
+    x, wg, b, ids_in = _filter_inputs(seed)
+    k = ids_in.shape[1]
+    ids, w, keep, _ = oracle.route_replay_filtered(x, wg, b, ids_in, -math.inf)
+    rid, rw, _ = oracle.route_replay(x, wg, b, ids_in)
+    assert keep.all() and np.array_equal(ids, rid) and np.array_equal(w, rw)
+    ids, w, keep, _ = oracle.route_replay_filtered(x, wg, b, ids_in, math.inf)
+    lid, lw, _ = oracle.route(x, wg, b, k)
+    assert not keep.any() and np.array_equal(ids, lid) and np.array_equal(w, lw)
+
+
+@pytest.mark.parametrize("seed", [2, 3])
+def test_replay_filter_matches_probability_form(seed):
+    """Independent formulation: probabilities from a plain softmax, p_e >= tau p_(k),
+    router order from sorting the probabilities, refill by set difference.  Taus are
+    taken away from every probability ratio, so the two forms must agree."""
+    x, wg, b, ids_in = _filter_inputs(seed, T=40)
+    T, k = ids_in.shape
+    lg = np.asarray(x, np.float64) @ np.asarray(wg, np.float64) + np.asarray(b, np.float64)
+    p = np.exp(lg - lg.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    order = np.argsort(-p, axis=1, kind="stable")
+    ratios = np.sort(np.concatenate([p[t, ids_in[t]] / p[t, order[t, k - 1]] for t in range(T)]))
+    gaps = np.argsort(np.diff(ratios))[::-1][:6]   # taus in the six widest gaps between ratios
+    taus = [0.5 * (ratios[i] + ratios[i + 1]) for i in gaps]
+    for tau in taus:
+        ids, _, keep, _ = oracle.route_replay_filtered(x, wg, b, ids_in, math.log(tau))
+        for t in range(T):
+            pk = p[t, order[t, k - 1]]
+            kp = [p[t, e] >= tau * pk for e in ids_in[t]]
+            assert keep[t].tolist() == kp
+            kept = [e for e, z in zip(ids_in[t], kp) if z]
+            fill = iter([e for e in order[t, :k] if e not in kept])
+            assert ids[t].tolist() == [e if z else next(fill) for e, z in zip(ids_in[t], kp)]
+
+
+@pytest.mark.parametrize("seed", [4, 5])
+def test_replay_filter_tau_one_gives_router_set(seed):
+    """tau = 1: a replayed expert stays iff it is at least as likely as the router's
+    k-th choice, so (no ties) the final set is the router's set."""
+    x, wg, b, ids_in = _filter_inputs(seed)
+    k = ids_in.shape[1]
+    lid, _, _ = oracle.route(x, wg, b, k)
+    ids_in = ids_in.copy()
+    ids_in[::3] = lid[::3, ::-1]   # some rows replay the router's own set, reversed
+    ids, _, keep, _ = oracle.route_replay_filtered(x, wg, b, ids_in, 0.0)
+    for t in range(ids.shape[0]):
+        assert set(ids[t].tolist()) == set(lid[t].tolist())
+        assert keep[t].tolist() == [int(e) in set(lid[t].tolist()) for e in ids_in[t]]
+    assert np.array_equal(ids[::3], ids_in[::3])
+
+
+def test_replay_filter_monotone_in_tau_and_valid():
+    x, wg, b, ids_in = _filter_inputs(6, T=32, E=12, k=5)
+    T, k = ids_in.shape
+    lid, _, _ = oracle.route(x, wg, b, k)
+    prev = None
+    for lt in [-math.inf, -8.0, -3.0, -1.5, -0.7, -0.2, 0.0, 0.5, math.inf]:
+        ids, w, keep, _ = oracle.route_replay_filtered(x, wg, b, ids_in, lt)
+        if prev is not None:
+            assert not (keep & ~prev).any()   # raising tau never keeps more
+        prev = keep
+        assert np.allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+        for t in range(T):
+            assert len(set(ids[t].tolist())) == k
+            assert np.array_equal(ids[t][keep[t]], ids_in[t][keep[t]])
+            assert set(ids[t][~keep[t]].tolist()) <= set(lid[t].tolist())
+
+
+def test_replay_filter_rejects_bad_ids_and_nan_threshold():
+    x, wg, b, ids_in = _filter_inputs(7, T=4)
+    bad = ids_in.copy()
+    bad[1, 0] = wg.shape[1]
+    with pytest.raises(ValueError):
+        oracle.route_replay_filtered(x, wg, b, bad, 0.0)
+    bad = ids_in.copy()
+    bad[2, 1] = bad[2, 0]
+    with pytest.raises(ValueError):
+        oracle.route_replay_filtered(x, wg, b, bad, 0.0)
+    with pytest.raises(ValueError):
+        oracle.route_replay_filtered(x, wg, b, ids_in, math.nan)
+
+
+# ---------------------------------------------------------------------------
 # MXFP8 decoding
 # ---------------------------------------------------------------------------
 def test_e4m3_table_hand_values():

@@ -135,6 +135,37 @@ moe_status moe_route_replay(const void* x, const uint8_t* x_scale, int dtype, in
                             const int32_t* ids_in, const float* weights_in, float* weights_out,
                             void* ws, size_t ws_bytes, void* stream);
 
+/* Router replay with the plausibility filter (Composer 2 Technical Report, section
+ * 6.2, paragraph on inference and weight sync: replayed experts whose gate score
+ * falls below a threshold derived from the router's own top-k are dropped and
+ * replaced with the router's candidates).  The page fixes neither the score nor the
+ * threshold; here the score is the gate's softmax probability p_e and the threshold
+ * tau * p_(k), p_(k) being the probability of the router's own k-th choice.  The
+ * test runs in logit form on the exactly rounded logits:
+ *     replayed column j keeps its expert e  iff  fl(l_e - l_(k)) >= log_tau
+ * (l = the correctly rounded fp64 logits, the difference rounded once), decided on
+ * the device by an fp64 bound and, where that bound cannot separate the two sides,
+ * by exact summation, so the kept set equals the one made on exact logits.
+ *   ids_in      int32 [T][k]: replayed expert IDs, in [0, E) and distinct within a
+ *               row, else the device flag gets MOE_ERR_BAD_IDS (that row's output is
+ *               then the router's own choice).  Must not overlap ids_out.
+ *   log_tau     ln tau, not NaN.  -INFINITY keeps every replayed id (plain replay);
+ *               +INFINITY drops them all (learned routing); 0 keeps exactly the
+ *               replayed experts at least as likely as the router's k-th choice.
+ *   ids_out     out int32 [T][k]: kept columns hold the replayed id; dropped
+ *               columns, in column order, get the router's top-k ids in rank order
+ *               (as moe_route orders them) that no kept column holds.
+ *   weights_out out fp32 [T][k]: the gate's softmax probabilities at ids_out
+ *               renormalised, with exactly moe_route_replay's arithmetic (so
+ *               log_tau = -INFINITY reproduces moe_route_replay bit for bit, and
+ *               +INFINITY reproduces moe_route).
+ * Runs moe_route first (same workspace).  MOE_ERR_INVALID_ARG: NaN log_tau,
+ * overlapping ids_in / ids_out, or as moe_route. */
+moe_status moe_route_replay_filtered(const void* x, const uint8_t* x_scale, int dtype, int T, int d,
+                                     const float* w_gate, const float* bias, int E, int k,
+                                     const int32_t* ids_in, double log_tau, int32_t* ids_out,
+                                     float* weights_out, void* ws, size_t ws_bytes, void* stream);
+
 /* Counting sort of the T*k (token, slot) pairs by (expert ascending, token
  * ascending), the grouped GEMM's input order.  Positions come from deterministic
  * histograms and prefix sums, never from atomic position counters.

@@ -15,6 +15,7 @@ import torch
 __all__ = [
     "MOE_F32", "MOE_BF16", "MOE_MXFP8", "MoeError", "lib", "Workspace",
     "moe_workspace_size", "moe_workspace_init", "moe_route", "moe_route_replay",
+    "moe_route_replay_filtered",
     "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_gate_up", "moe_expert_ffn_down", "moe_combine", "moe_check", "moe_status_string",
     "layer_forward",
 ]
@@ -51,6 +52,8 @@ def lib():
             "moe_workspace_init": [P, SZ, P],
             "moe_route": [P, P, I, I, I, P, P, I, I, P, P, P, SZ, P],
             "moe_route_replay": [P, P, I, I, I, P, P, I, I, P, P, P, P, SZ, P],
+            "moe_route_replay_filtered": [P, P, I, I, I, P, P, I, I, P, ctypes.c_double, P, P, P, SZ,
+                                          P],
             "moe_dispatch": [P, I, I, I, P, P, P, P, SZ, P],
             "moe_expert_ffn": [P, P, I, I, I, I, I, I, ctypes.POINTER(_Bank), ctypes.POINTER(_Bank),
                                P, P, P, P, SZ, P],
@@ -151,6 +154,21 @@ def moe_route_replay(x, w_gate, bias, ids_in, ws: Workspace, weights_in=None, x_
                                E, k, _ptr(ids_in), _ptr(weights_in), _ptr(wo), ws.ptr, ws.nbytes,
                                _stream(x.device)), "moe_route_replay")
     return wo
+
+
+def moe_route_replay_filtered(x, w_gate, bias, ids_in, log_tau, ws: Workspace, x_scale=None,
+                              ids_out=None, weights_out=None):
+    _check_dev(x, w_gate, bias, x_scale, ids_in)
+    T, d = x.shape
+    E = w_gate.shape[1]
+    k = ids_in.shape[1]
+    io = torch.empty(T, k, dtype=torch.int32, device=x.device) if ids_out is None else ids_out
+    wo = torch.empty(T, k, dtype=torch.float32, device=x.device) if weights_out is None else weights_out
+    _ok(lib().moe_route_replay_filtered(_ptr(x), _ptr(x_scale), _dtype_of(x), T, d, _ptr(w_gate),
+                                        _ptr(bias), E, k, _ptr(ids_in), float(log_tau), _ptr(io),
+                                        _ptr(wo), ws.ptr, ws.nbytes, _stream(x.device)),
+        "moe_route_replay_filtered")
+    return io, wo
 
 
 def moe_dispatch(ids, E, ws: Workspace, offsets=None, perm=None, row_of=None):

@@ -215,4 +215,31 @@ moe_status screen_replay(const void* x, const uint8_t* xs, int dtype, int T, int
                          const float* w_gate, const float* bias, int E, int k, const int32_t* ids_in,
                          const float* weights_in, float* weights_out, char* ws, hipStream_t s);
 
+// Replay plausibility filter, run after moe_route has left the router's ids in `ids`
+// and its fp64 logits (or candidate logits) in the workspace.
+struct FilterArgs {
+  const void* x;
+  const uint8_t* xs;
+  int dtype, T, d, E, k;
+  const float* bias;
+  const int32_t* ids_in;
+  double log_tau;
+  double tg;            // relative fp64 logit bound: |l~ - l| <= tg (||x|| ||w_e|| + |b_e|)
+  int32_t* ids;         // in: router top-k in rank order; out: the filtered ids
+  float* weights;
+  // filled by filter_launch from the workspace
+  const double* logits; // fp64 gate logits [T][E] (unscreened gate), else null
+  const float* wt;      // transposed gate [E][d] (screened gate)
+  const int32_t* cand;
+  const int* ccount;
+  const double* cval;
+  const double* xnorm;
+  const double* wnorm;
+  int* tok_flag;
+  int* flag;
+};
+// pass 0: certified decisions, ids and weights; tokens it cannot certify get
+// tok_flag 1.  pass 1: weights of those tokens once their ids are final.
+moe_status filter_launch(FilterArgs a, bool screened, char* ws, int pass, hipStream_t s);
+
 }  // namespace moe

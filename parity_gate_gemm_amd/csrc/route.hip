@@ -723,6 +723,55 @@ __global__ __launch_bounds__(256) void exact_fallback_kernel(
   }
 }
 
+// Replay plausibility filter, the tokens the fp64 bound could not decide (tok_flag 1;
+// their replayed ids are valid and ids still holds the router's top-k): threads
+// 0..k-1 round the replayed ids' logits exactly, thread k the router's k-th choice's;
+// thread 0 then keeps column j iff fl(l_j - l_(k)) >= log_tau and refills the dropped
+// columns with the router's ids in rank order that no kept column holds.
+__global__ __launch_bounds__(64) void filter_exact_kernel(
+    const void* __restrict__ x, const uint8_t* __restrict__ xs, int dtype, int T, int d,
+    const float* __restrict__ wg, const float* __restrict__ bias, int E, int k,
+    const int32_t* __restrict__ ids_in, double log_tau, const int* __restrict__ tok_flag,
+    int32_t* __restrict__ ids, int* flag) {
+  const int t = blockIdx.x;
+  if (t >= T || tok_flag[t] != 1) return;
+  __shared__ double ex[kMaxTopK + 1];
+  __shared__ int rid[kMaxTopK];
+  const int j = threadIdx.x;
+  int32_t* io = ids + (size_t)t * k;
+  if (j <= k) {
+    const int e = j < k ? ids_in[(size_t)t * k + j] : io[k - 1];
+    Expansion acc;
+    for (int i = 0; i < d; ++i) {
+      const double xv = load_act_f64(x, xs, dtype, (size_t)t, d, i);
+      acc.add(xv * (double)wg[(size_t)i * E + e]);
+    }
+    if (bias) acc.add((double)bias[e]);
+    if (acc.overflow) raise_flag(flag, kFlagCorrupt);
+    ex[j] = acc.round_nearest();
+  }
+  if (j < k) rid[j] = io[j];
+  __syncthreads();
+  if (j != 0) return;
+  uint64_t keepm = 0;
+  for (int c = 0; c < k; ++c)
+    if (ex[c] - ex[k] >= log_tau) keepm |= 1ull << c;
+  int next = 0;   // next router rank to try
+  for (int c = 0; c < k; ++c) {
+    if ((keepm >> c) & 1ull) {
+      io[c] = ids_in[(size_t)t * k + c];
+      continue;
+    }
+    for (; next < k; ++next) {   // enough remain: k - kept router ids are not held
+      bool held = false;
+      for (int u = 0; u < k; ++u)
+        if (((keepm >> u) & 1ull) && ids_in[(size_t)t * k + u] == rid[next]) held = true;
+      if (!held) break;
+    }
+    io[c] = rid[next < k ? next++ : 0];
+  }
+}
+
 // Weights of one token: softmax over all experts restricted to the chosen ones and
 // renormalised, i.e. exp(l_r - m) / sum_s exp(l_s - m) with m the largest chosen
 // logit, in fp64 from the fp64 GEMM logits, sum in column order, one rounding to fp32.
@@ -913,4 +962,43 @@ extern "C" moe_status moe_route_replay(const void* x, const uint8_t* x_scale, in
   replay_kernel<<<(T + SEL_WAVES - 1) / SEL_WAVES, 256, 0, s>>>(
       (const double*)(w + L.logits), T, E, k, ids_in, weights_in, weights_out, (int*)w);
   return launch_status();
+}
+
+extern "C" moe_status moe_route_replay_filtered(const void* x, const uint8_t* x_scale, int dtype, int T,
+                                                int d, const float* w_gate, const float* bias, int E,
+                                                int k, const int32_t* ids_in, double log_tau,
+                                                int32_t* ids_out, float* weights_out, void* ws,
+                                                size_t ws_bytes, void* stream) {
+  moe_status st = check_route_args(x, x_scale, dtype, T, d, w_gate, E, k, ws, ws_bytes);
+  if (st != MOE_OK || T == 0) return st;
+  if (!ids_in || !ids_out || !weights_out || isnan(log_tau)) return MOE_ERR_INVALID_ARG;
+  const size_t n = (size_t)T * k;
+  if (ids_in < ids_out + n && ids_out < ids_in + n) return MOE_ERR_INVALID_ARG;
+  // the router's own top-k (rank order) into ids_out, its logits into the workspace
+  if ((st = moe_route(x, x_scale, dtype, T, d, w_gate, bias, E, k, ids_out, weights_out, ws, ws_bytes,
+                      stream)) != MOE_OK)
+    return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  FilterArgs a{};
+  a.x = x;
+  a.xs = x_scale;
+  a.dtype = dtype;
+  a.T = T;
+  a.d = d;
+  a.E = E;
+  a.k = k;
+  a.bias = bias;
+  a.ids_in = ids_in;
+  a.log_tau = log_tau;
+  a.tg = two_gamma(d);
+  a.ids = ids_out;
+  a.weights = weights_out;
+  const bool screened = gate_screened(dtype, d);
+  if ((st = filter_launch(a, screened, w, 0, s)) != MOE_OK) return st;
+  const RouteWs L = route_ws(T, d, E);
+  filter_exact_kernel<<<T, 64, 0, s>>>(x, x_scale, dtype, T, d, w_gate, bias, E, k, ids_in, log_tau,
+                                       (const int*)(w + L.tok_flag), ids_out, (int*)w);
+  if ((st = launch_status()) != MOE_OK) return st;
+  return filter_launch(a, screened, w, 1, s);
 }

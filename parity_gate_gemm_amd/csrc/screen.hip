@@ -758,6 +758,141 @@ __global__ __launch_bounds__(256) void replay_cand_kernel(const int32_t* __restr
 }
 
 // ---------------------------------------------------------------------------
+// Router replay with the plausibility filter (Composer 2 Technical Report, §6.2,
+// paragraph on inference and weight sync): replayed expert e in column j stays when
+// fl(l_e - l_(k)) >= ln tau on the correctly rounded logits, l_(k) being the logit of
+// the router's own k-th choice; dropped columns are refilled, in column order, with
+// the router's top-k ids in rank order that no kept column holds.  One wavefront per
+// token, lane j < k owns column j.
+// ---------------------------------------------------------------------------
+
+// fp64 logit of (t, e) for a wave-uniform e: the value the learned path and plain
+// replay use (the full fp64 gate GEMM, else the token's candidate value, else
+// wave_dot + bias), so the weights below match theirs bit for bit.
+__device__ __forceinline__ double filter_logit(const FilterArgs& a, int t, int e) {
+  if (a.logits) return a.logits[(size_t)t * a.E + e];
+  const int lane = threadIdx.x & 63;
+  const bool hit = lane < a.ccount[t] && a.cand[(size_t)t * kCandMax + lane] == e;
+  const uint64_t hm = __ballot(hit);
+  if (hm) return a.cval[(size_t)t * kCandMax + (__ffsll((long long)hm) - 1)];
+  const double v = wave_dot(a.x, a.xs, a.dtype, t, a.d, a.wt + (size_t)e * a.d);
+  return a.bias ? v + (double)a.bias[e] : v;
+}
+
+// Lane j < k holds the final id f; writes the logits' softmax restricted to the row's
+// ids, renormalised: max, exp(v - max) summed in column order, one division each
+// (the arithmetic of the learned and replay weights).
+__device__ __forceinline__ void filter_weights_row(const FilterArgs& a, int t, int f) {
+  const int lane = threadIdx.x & 63;
+  const bool live = lane < a.k;
+  double v = 0.0;
+  for (int j = 0; j < a.k; ++j) {
+    const double lj = filter_logit(a, t, __shfl(f, j));
+    if (lane == j) v = lj;
+  }
+  double mx = live ? v : -INFINITY;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmax(mx, __shfl_xor(mx, off));
+  const double ex = exp(v - mx);
+  double sum = 0.0;
+  for (int j = 0; j < a.k; ++j) sum += __shfl(ex, j);
+  if (!__all(!live || isfinite(v)) && lane == 0) raise_flag(a.flag, kFlagNonFinite);
+  if (live) a.weights[(size_t)t * a.k + lane] = (float)(ex / sum);
+}
+
+__global__ __launch_bounds__(256) void filter_decide_kernel(FilterArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= a.T) return;
+  const int k = a.k;
+  const bool live = lane < k;
+  const uint64_t kmask = (1ull << k) - 1ull;   // k <= 32
+  int32_t* io = a.ids + (size_t)t * k;
+  const int q = live ? a.ids_in[(size_t)t * k + lane] : -1;
+  const int r = live ? io[lane] : -1;
+  int bits = (live && (q < 0 || q >= a.E)) ? kFlagBadId : 0;
+  for (int j = 0; j < k; ++j) {
+    const int qj = __shfl(q, j);   // every lane takes part in the shuffle
+    if (live && lane > j && qj == q) bits |= kFlagDupId;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) bits |= __shfl_xor(bits, off);
+  if (bits) {   // rejected row: the router's own choice
+    if (lane == 0) {
+      raise_flag(a.flag, bits);
+      a.tok_flag[t] = 0;
+    }
+    filter_weights_row(a, t, r);
+    return;
+  }
+  const double lt = a.log_tau;
+  uint64_t keepm;
+  if (lt == -INFINITY) {
+    keepm = kmask;
+  } else if (lt == INFINITY) {
+    keepm = 0;
+  } else {
+    double lq = 0.0;
+    for (int j = 0; j < k; ++j) {
+      const double v = filter_logit(a, t, __shfl(q, j));
+      if (lane == j) lq = v;
+    }
+    const int ek = __shfl(r, k - 1);
+    const double lk = filter_logit(a, t, ek);
+    const double xn = a.xnorm[t];
+    const double bk = a.tg * (xn * a.wnorm[ek] + (a.bias ? fabs((double)a.bias[ek]) : 0.0));
+    bool keep = false, sure = true;
+    if (live) {
+      // |l~ - l| <= b for both logits (b includes the final rounding of l); the
+      // relative 2^-50 covers the roundings of the difference and of the margin
+      // itself, so keep / drop below hold for the exact fl(l_e - l_(k)).
+      const double bq = a.tg * (xn * a.wnorm[q] + (a.bias ? fabs((double)a.bias[q]) : 0.0));
+      const double dl = lq - lk;
+      const double mg = bq + bk + 0x1p-50 * (fabs(lq) + fabs(lk) + fabs(lt)) + 0x1p-1000;
+      if (isfinite(dl) && isfinite(mg)) {
+        keep = dl - mg >= lt;
+        sure = keep || dl + mg < lt;
+      } else {
+        raise_flag(a.flag, kFlagNonFinite);
+      }
+    }
+    if (!__all(sure)) {
+      if (lane == 0) a.tok_flag[t] = 1;
+      return;
+    }
+    keepm = __ballot(keep) & kmask;
+  }
+  // refill: router ids in rank order that no kept column holds
+  bool held = false;
+  for (int j = 0; j < k; ++j) {
+    const int qj = __shfl(q, j);
+    if (((keepm >> j) & 1ull) && qj == r) held = true;
+  }
+  uint64_t avail = __ballot(live && !held) & kmask;
+  const bool kept = (keepm >> lane) & 1ull;
+  int src = 0;
+  if (live && !kept) {
+    const int n = __popcll(~keepm & kmask & ((1ull << lane) - 1ull));   // dropped columns before j
+    for (int z = 0; z < n; ++z) avail &= avail - 1ull;
+    src = __ffsll((long long)avail) - 1;
+  }
+  const int rv = __shfl(r, src);
+  const int f = kept ? q : rv;
+  if (live) io[lane] = f;
+  if (lane == 0) a.tok_flag[t] = 0;
+  filter_weights_row(a, t, f);
+}
+
+// Weights of the tokens the exact pass decided (their ids are final).
+__global__ __launch_bounds__(256) void filter_weights_kernel(FilterArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= a.T || a.tok_flag[t] != 1) return;
+  const int f = lane < a.k ? a.ids[(size_t)t * a.k + lane] : 0;
+  filter_weights_row(a, t, f);
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 static double gamma_n(double n, double u) { return n * u / (1.0 - n * u); }
@@ -896,6 +1031,34 @@ moe_status screen_replay(const void* x, const uint8_t* xs, int dtype, int T, int
   moe_status st = refine_ids(x, xs, dtype, T, d, E, k, bias, S, s);
   if (st != MOE_OK) return st;
   return screen_route_weights(x, xs, dtype, T, d, bias, E, k, ids_in, weights_in, weights_out, w, s);
+}
+
+moe_status filter_launch(FilterArgs a, bool screened, char* w, int pass, hipStream_t s) {
+  const RouteWs L = route_ws(a.T, a.d, a.E);
+  a.xnorm = (const double*)(w + L.xnorm);
+  a.wnorm = (const double*)(w + L.wnorm);
+  a.tok_flag = (int*)(w + L.tok_flag);
+  a.flag = (int*)w;
+  if (screened) {
+    const ScreenWs S = screen_ws_of(w, a.T, a.d, a.E);
+    a.logits = nullptr;
+    a.wt = S.wt;
+    a.cand = S.cand;
+    a.ccount = S.ccount;
+    a.cval = S.cval;
+  } else {
+    a.logits = (const double*)(w + L.logits);
+    a.wt = nullptr;
+    a.cand = nullptr;
+    a.ccount = nullptr;
+    a.cval = nullptr;
+  }
+  const unsigned blocks = (unsigned)((a.T + 3) / 4);
+  if (pass == 0)
+    filter_decide_kernel<<<blocks, 256, 0, s>>>(a);
+  else
+    filter_weights_kernel<<<blocks, 256, 0, s>>>(a);
+  return launch_status();
 }
 
 }  // namespace moe

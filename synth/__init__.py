@@ -10,6 +10,7 @@ from .inputs import (  # noqa: F401
     WORKLOADS,
     Workload,
     make_layer_inputs,
+    make_gate_inputs,
     zipf_replay_ids,
     dirichlet_weights,
     mxfp8_quantize,

@@ -176,6 +176,33 @@ def _store(v: torch.Tensor, dtype: str):
     raise ValueError(dtype)
 
 
+def _draw_gate(wl: Workload, device: str, draw_device: str | None):
+    """The first draws of the recipe (x, gate weight, gate bias) and the generator's
+    draw function, positioned for the expert weights."""
+    dd = draw_device or device
+    g = torch.Generator(device=dd)
+    g.manual_seed(wl.seed)
+
+    def randn(*shape, std=1.0):
+        t = torch.randn(*shape, generator=g, device=dd, dtype=torch.float32)
+        if std != 1.0:
+            t.mul_(std)
+        return t
+
+    out = {}
+    x, xs = _store(randn(wl.T, wl.d), wl.dtype)
+    out["x"], out["x_scale"] = x.to(device), (xs.to(device) if xs is not None else None)
+    out["w_gate"] = randn(wl.d, wl.E, std=1.0 / math.sqrt(wl.d)).to(device)
+    out["bias"] = randn(wl.E, std=math.sqrt(0.5)).to(device) if wl.bias else None
+    return out, randn
+
+
+def make_gate_inputs(wl: Workload, device: str = "cpu", draw_device: str | None = None):
+    """Only the routing inputs of ``make_layer_inputs`` (x, x_scale, w_gate, bias),
+    the same values for the same seed and draw device, without drawing the experts."""
+    return _draw_gate(wl, device, draw_device)[0]
+
+
 def make_layer_inputs(wl: Workload, device: str = "cpu", draw_device: str | None = None):
     """Draw one layer's inputs for workload ``wl`` (see module docstring for the recipe).
 
@@ -186,22 +213,8 @@ def make_layer_inputs(wl: Workload, device: str = "cpu", draw_device: str | None
     ``*_scale`` are None unless the workload is MXFP8; ``ids_in``/``weights_in`` are
     None unless the workload replays routing.
     """
-    dd = draw_device or device
-    g = torch.Generator(device=dd)
-    g.manual_seed(wl.seed)
+    out, randn = _draw_gate(wl, device, draw_device)
     T, d, I, E = wl.T, wl.d, wl.inter, wl.E
-
-    def randn(*shape, std=1.0):
-        t = torch.randn(*shape, generator=g, device=dd, dtype=torch.float32)
-        if std != 1.0:
-            t.mul_(std)
-        return t
-
-    out = {}
-    x, xs = _store(randn(T, d), wl.dtype)
-    out["x"], out["x_scale"] = x.to(device), (xs.to(device) if xs is not None else None)
-    out["w_gate"] = randn(d, E, std=1.0 / math.sqrt(d)).to(device)
-    out["bias"] = randn(E, std=math.sqrt(0.5)).to(device) if wl.bias else None
 
     elt = {"f32": torch.float32, "bf16": torch.bfloat16, "mxfp8": torch.uint8}[wl.dtype]
 

@@ -69,6 +69,14 @@ def test_route_host_validation(L):
     assert L.moe_route(P, None, 1, 4, 128, P, None, 16, 2, P, P, P, 64, None) == 3           # workspace
     assert L.moe_route(P, None, 1, 4, 128, P, None, 16, 2, None, P, P, 1 << 30, None) == 1   # null ids
     assert L.moe_route_replay(P, None, 1, 4, 128, P, None, 16, 2, None, None, P, P, 1 << 30, None) == 1
+    F, Q = L.moe_route_replay_filtered, ctypes.c_void_p(0x20000)
+    assert F(None, None, 1, 0, 128, None, None, 16, 2, None, 0.0, None, None, None, 0, None) == 0
+    assert F(P, None, 1, 4, 128, P, None, 16, 2, P, float("nan"), Q, P, P, 1 << 30, None) == 1  # NaN tau
+    assert F(P, None, 1, 4, 128, P, None, 16, 2, P, 0.0, ctypes.c_void_p(0x10008), P, P, 1 << 30,
+             None) == 1                                                                        # overlap
+    assert F(P, None, 1, 4, 128, P, None, 16, 2, P, 0.0, None, P, P, 1 << 30, None) == 1       # null ids_out
+    assert F(P, None, 1, 4, 128, P, None, 16, 2, None, 0.0, Q, P, P, 1 << 30, None) == 1       # null ids_in
+    assert F(P, None, 1, 4, 128, P, None, 16, 2, P, 0.0, Q, P, P, 64, None) == 3               # workspace
 
 
 def test_dispatch_ffn_combine_host_validation(L):

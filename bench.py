@@ -34,6 +34,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="bf16_t4096",
                     help="bf16_t4096 (default), replay_zipf_t4096, bf16_t128_stream, tiny_fp32_t32")
+    ap.add_argument("--replay-filter", type=float, default=None, metavar="LOG_TAU",
+                    help="replay workloads: route with the plausibility filter at ln tau = LOG_TAU "
+                         "(the replayed ids are filtered and the weights come from the gate)")
     ap.add_argument("--cpu-sample", type=int, default=32,
                     help="tokens of the same batch the CPU oracle is timed on (0: skip)")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
@@ -83,6 +86,10 @@ def main():
     T, d, E, k, I = wl.T, wl.d, wl.E, wl.k, wl.inter
     dt = {"f32": pg.MOE_F32, "bf16": pg.MOE_BF16, "mxfp8": pg.MOE_MXFP8}[wl.dtype]
     replay = wl.routing == "replay"
+    filt = args.replay_filter
+    if filt is not None and not replay:
+        print("--replay-filter needs a replay workload (replay_zipf_t4096)", file=sys.stderr)
+        sys.exit(2)
     has_shared = inp["shared"] is not None
     ws = pg.Workspace(T, d, E, k, I, dt)
     x, wg, bias = inp["x"], inp["w_gate"], inp["bias"]
@@ -90,7 +97,7 @@ def main():
     shared = inp["shared"]
     rows = T * k + (T if has_shared else 0)
     odt = torch.float32 if dt == pg.MOE_F32 else torch.bfloat16
-    ids = inp["ids_in"] if replay else torch.empty(T, k, dtype=torch.int32, device=dev)
+    ids = inp["ids_in"] if replay and filt is None else torch.empty(T, k, dtype=torch.int32, device=dev)
     weights = torch.empty(T, k, dtype=torch.float32, device=dev)
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     perm = torch.empty(T * k, dtype=torch.int32, device=dev)
@@ -101,7 +108,10 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        if replay:
+        if filt is not None:
+            pg.moe_route_replay_filtered(x, wg, bias, inp["ids_in"], filt, ws, x_scale=inp["x_scale"],
+                                         ids_out=ids, weights_out=weights)
+        elif replay:
             pg.moe_route_replay(x, wg, bias, ids, ws, weights_in=inp["weights_in"],
                                 x_scale=inp["x_scale"], weights_out=weights)
         else:
@@ -154,6 +164,8 @@ def main():
     bytes_gate_up = n_mats * 2 * mat + T * d * eb + rows * I * hb + T * k * 4
     bytes_down = n_mats * mat + rows * I * hb + rows * d * ob
     bytes_route = T * d * eb + d * E * 4 + T * k * 8 + (E * 4 if bias is not None else 0)
+    if filt is not None:
+        bytes_route += T * k * 4        # the replayed ids read besides the filtered ids written
     bytes_dispatch = T * k * 4 * 3 + (E + 1) * 4
     bytes_combine = rows * d * ob + T * d * ob + T * k * 8
     flops_gate_up = 2.0 * rows * d * 2 * I
@@ -207,7 +219,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "d": d, "E": E, "k": k, "inter": I,
                    "shared_experts": 1 if has_shared else 0, "routing": wl.routing,
-                   "seed": wl.seed, "parallelism": "none (1 GPU)"},
+                   "seed": wl.seed, "parallelism": "none (1 GPU)",
+                   **({"replay_filter_log_tau": filt} if filt is not None else {})},
         "roofline": dict(roof, traffic=None, kernel=dom_kernel,
                          alg_bytes_per_launch=stages[dom]["alg_bytes"], launch_ms=stage_ms[dom]),
         "mfma": {"gemm_TFLOP_s": gemm_tflops, "peak_TFLOP_s": mfma_peak,
@@ -222,7 +235,7 @@ def main():
     if wl.dtype != "bf16":
         result["vs_metric_config"] = "this workload is not the metric's configuration (bf16 T=4096)"
     if args.cpu_sample > 0:
-        result["cpu_baseline"] = cpu_baseline(inp, wl, ids, args.cpu_sample)
+        result["cpu_baseline"] = cpu_baseline(inp, wl, ids, args.cpu_sample, filt)
     print(json.dumps(result))
 
 
@@ -251,39 +264,57 @@ class _ExpertCache:
 
     def fetch(self, e):
         if e not in self.cache:
-            self.cache[e] = tuple(self.inp[n][e].cpu() for n in ("w1", "w3", "w2"))
+            self.cache[e] = tuple((self.inp[n][e].cpu(),
+                                   None if self.inp.get(n + "_scale") is None else self.inp[n + "_scale"][e].cpu())
+                                  for n in ("w1", "w3", "w2"))
         return self.cache[e]
 
     def __getitem__(self, e):
-        return tuple(t.float().numpy() for t in self.fetch(e))
+        return tuple(_stored_values(t, sc) for t, sc in self.fetch(e))
 
 
-def cpu_baseline(inp, wl, ids, n_tok):
-    """The CPU oracle (as it is) on the first n_tok tokens of the same batch."""
+def _stored_values(t, scale=None):
+    """Host values of a stored tensor (MXFP8 codes decoded by the oracle's decoder)."""
+    import oracle
+    if scale is None:
+        return t.float().numpy()
+    return oracle.mx_dequant(t.numpy(), scale.numpy())
+
+
+def cpu_baseline(inp, wl, ids, n_tok, log_tau=None):
+    """The CPU oracle (as it is) on the first n_tok tokens of the same batch; with
+    log_tau, the filtered replay routing followed by the layer on the filtered ids."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     import oracle
 
     rows = np.arange(min(n_tok, wl.T))
-    x = inp["x"][rows].float().cpu().numpy()
+    xs = inp["x_scale"]
+    x = _stored_values(inp["x"][rows].cpu(), None if xs is None else xs[rows].cpu())
     wg = inp["w_gate"].cpu().numpy()
     bias = None if inp["bias"] is None else inp["bias"].cpu().numpy()
     experts = _ExpertCache(inp)
     for e in np.unique(ids[rows].cpu().numpy()):
         experts.fetch(int(e))                       # host copies: not part of the timed work
     sh = inp["shared"]
-    shared = None if sh is None else tuple(sh[n].float().cpu().numpy() for n in ("w1", "w3", "w2"))
+    shared = None if sh is None else tuple(
+        _stored_values(sh[n].cpu(), None if sh.get(n + "_scale") is None else sh[n + "_scale"].cpu())
+        for n in ("w1", "w3", "w2"))
     kw = {}
     if wl.routing == "replay":
         kw = {"ids_in": inp["ids_in"][rows].cpu().numpy(), "weights_in": inp["weights_in"][rows].cpu().numpy()}
     t0 = time.perf_counter()
+    if log_tau is not None:
+        fid, fw, _, _ = oracle.route_replay_filtered(x, wg, bias, kw["ids_in"], log_tau)
+        kw = {"ids_in": fid, "weights_in": fw}
     oracle.layer(x, wg, bias, experts, shared, wl.k, **kw)
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {"value": len(rows) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {len(rows)} tokens of the {wl.name} batch (exact fsum gate logits over "
-                      f"{wl.E} experts, fp64 SwiGLU for each chosen expert), {dt:.1f} s",
+                      f"{wl.E} experts{', plausibility filter' if log_tau is not None else ''}, fp64 "
+                      f"SwiGLU for each chosen expert), {dt:.1f} s",
             "host_cpus": len(os.sched_getaffinity(0))}
 
 

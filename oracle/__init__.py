@@ -20,5 +20,9 @@ from .moe_oracle import (  # noqa: F401
     expert_ffn,
     layer,
     layer_dense,
+    layer_backward,
+    expert_backward,
+    softmax_pick_grad,
+    silu_grad,
     normwise_rel_err,
 )

@@ -1,4 +1,4 @@
-"""CPU oracle of one Mixture-of-Experts layer's forward pass.
+"""CPU oracle of one Mixture-of-Experts layer's forward and backward pass.
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and the
 benchmark's CPU-baseline leg may import this module; the library never does, and
@@ -21,6 +21,11 @@ What it computes, and where that is defined:
     (silu(x W1) * (x W3)) W2; the tokens' expert outputs are combined as the
     routing-weighted sum (§6.1 "Parallelism": dispatch and combine), plus the
     always-on shared expert when present.
+  * The backward pass (the MoE layer is trained with grouped GEMMs forward and
+    backward: Composer 2 Technical Report, §6.1 "Kernels", Figure 10; under replay
+    the router still computes gate scores so that gradients flow through them:
+    §6.2, paragraph on inference and weight sync): the chain rule of the forward
+    above, in float64, for a scalar loss with dL/dy given.
 
 Precision: every input value is converted to float64 exactly.  Gate logits are the
 correctly rounded value of the exact sum (each product of two stored values is
@@ -330,3 +335,102 @@ def normwise_rel_err(y, y_ref) -> float:
     if den == 0:
         return float(np.max(np.abs(y)))
     return float(np.max(np.abs(y - y_ref)) / den)
+
+
+# ---------------------------------------------------------------------------
+# Backward pass of the layer (gradients of a scalar loss L with dL/dy = dy)
+# ---------------------------------------------------------------------------
+def silu_grad(z):
+    """d silu / dz = sigmoid(z) (1 + z (1 - sigmoid(z)))."""
+    z = f64(z)
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-z))
+    return s * (1.0 + z * (1.0 - s))
+
+
+def expert_backward(x_rows, d_out_rows, w1, w3, w2):
+    """Chain rule through one SwiGLU expert o = (silu(a) * g) W2, a = x W1, g = x W3.
+
+    x_rows [n, d], d_out_rows = dL/do [n, d]; weights stored output-major (w1, w3
+    [I, d], w2 [d, I]).  Returns (dx [n, d], dw1 [I, d], dw3 [I, d], dw2 [d, I]).
+    """
+    xr = f64(x_rows)
+    do = f64(d_out_rows)
+    w1, w3, w2 = f64(w1), f64(w3), f64(w2)
+    a = xr @ w1.T
+    g = xr @ w3.T
+    h = silu(a) * g
+    dh = do @ w2                      # dL/dh [n, I]
+    dg = dh * silu(a)
+    da = dh * g * silu_grad(a)
+    dx = da @ w1 + dg @ w3
+    return dx, da.T @ xr, dg.T @ xr, do.T @ h
+
+
+def softmax_pick_grad(weights, d_weights):
+    """dL/dl at the chosen experts for w = exp(l_S) / sum exp(l_S) (the softmax over
+    all experts, picked at S and renormalised, depends only on the logits in S):
+    dl_r = w_r (dw_r - sum_s w_s dw_s)."""
+    w = f64(weights)
+    dw = f64(d_weights)
+    return w * (dw - (w * dw).sum(axis=1, keepdims=True))
+
+
+def layer_backward(x, w_gate, bias, experts, shared, k: int, dy, ids_in=None, weights_in=None):
+    """Gradients of L = <dy, y> through one MoE layer forward (``layer``).
+
+    The expert choice is piecewise constant in x, so no gradient flows through the
+    selection; the gate's logits get one through the routing weights whenever those
+    come from the gate (learned routing, or replay without caller weights; the
+    router still computes gate scores so that gradients can flow through it:
+    Composer 2 Technical Report, §6.2, paragraph on inference and weight sync).
+    Returns a dict: dx [T, d], d_weights [T, k], d_w_gate [d, E], d_bias [E] (or
+    None), dw1 / dw3 [E, I, d], dw2 [E, d, I], d_shared (dw1, dw3, dw2) or None, and
+    the forward dict under "fwd".
+    """
+    xf = f64(x)
+    dyf = f64(dy)
+    fwd = layer(xf, w_gate, bias, experts, shared, k, ids_in=ids_in, weights_in=weights_in)
+    T, d = xf.shape
+    E = fwd["logits"].shape[1]
+    ids, w, rows = fwd["ids"], fwd["weights"], fwd["rows"]
+    offsets, perm, row_of = fwd["offsets"], fwd["perm"], fwd["row_of"]
+    # combine: y_t = sum_r w_tr o_tr (+ shared_t)
+    d_weights = np.empty((T, k))
+    d_rows = np.empty_like(rows)
+    for t in range(T):
+        for r in range(k):
+            j = row_of[t * k + r]
+            d_weights[t, r] = float(dyf[t] @ rows[j])
+            d_rows[j] = w[t, r] * dyf[t]
+    dx = np.zeros((T, d))
+    I = f64(experts[0][0]).shape[0]
+    dw1 = np.zeros((E, I, d))
+    dw3 = np.zeros((E, I, d))
+    dw2 = np.zeros((E, d, I))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        toks = perm[lo:hi] // k
+        gx, dw1[e], dw3[e], dw2[e] = expert_backward(xf[toks], d_rows[lo:hi], *experts[e])
+        np.add.at(dx, toks, gx)
+    d_shared = None
+    if shared is not None:
+        gx, s1, s3, s2 = expert_backward(xf, dyf, *shared)
+        dx += gx
+        d_shared = (s1, s3, s2)
+    d_w_gate = np.zeros((d, E))
+    d_bias = None if bias is None else np.zeros(E)
+    if weights_in is None:   # weights are the gate's softmax at the chosen ids
+        dl = softmax_pick_grad(w, d_weights)
+        wg = f64(w_gate)
+        for t in range(T):
+            for r in range(k):
+                e = int(ids[t, r])
+                dx[t] += dl[t, r] * wg[:, e]
+                d_w_gate[:, e] += dl[t, r] * xf[t]
+                if d_bias is not None:
+                    d_bias[e] += dl[t, r]
+    return {"dx": dx, "d_weights": d_weights, "d_w_gate": d_w_gate, "d_bias": d_bias,
+            "dw1": dw1, "dw3": dw3, "dw2": dw2, "d_shared": d_shared, "fwd": fwd}

@@ -471,3 +471,105 @@ def test_mx_dequant_blocks():
     scales = np.array([[127, 129]], dtype=np.uint8)
     v = oracle.mx_dequant(codes, scales)
     assert np.all(v[0, :32] == 1.0) and np.all(v[0, 32:] == 6.0)
+
+
+# ---------------------------------------------------------------------------
+# Backward pass
+# ---------------------------------------------------------------------------
+def _bwd_layer(seed, T=6, d=16, I=8, E=6, k=2, shared=True, bias=True):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d))
+    wg = rng.standard_normal((d, E)) * 0.5
+    b = rng.standard_normal(E) * 0.3 if bias else None
+    experts = [(rng.standard_normal((I, d)) * 0.4, rng.standard_normal((I, d)) * 0.4,
+                rng.standard_normal((d, I)) * 0.4) for _ in range(E)]
+    sh = tuple(rng.standard_normal(s) * 0.4 for s in ((I, d), (I, d), (d, I))) if shared else None
+    dy = rng.standard_normal((T, d))
+    return x, wg, b, experts, sh, k, dy, rng
+
+
+def _loss(x, wg, b, experts, sh, k, dy, **kw):
+    f = oracle.layer(x, wg, b, experts, sh, k, **kw)
+    return float((f["y"] * dy).sum()), f["ids"]
+
+
+@pytest.mark.parametrize("mode", ["learned", "replay_gate_weights", "replay_caller_weights"])
+def test_layer_backward_matches_central_differences(mode):
+    """Every gradient against the derivative of the oracle's own forward along a random
+    direction of each parameter group (central differences, eps = 1e-6; the expert
+    choice is checked unchanged at both ends)."""
+    x, wg, b, experts, sh, k, dy, rng = _bwd_layer(11)
+    T, E = x.shape[0], wg.shape[1]
+    kw = {}
+    if mode != "learned":
+        kw["ids_in"] = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    if mode == "replay_caller_weights":
+        kw["weights_in"] = rng.dirichlet(np.ones(k), size=T)
+    g = oracle.layer_backward(x, wg, b, experts, sh, k, dy, **kw)
+    eps = 1e-6
+
+    def check(name, grad, perturb):
+        v = rng.standard_normal(grad.shape)
+        lp, ip = _loss(*perturb(eps * v), k, dy, **kw)
+        lm, im = _loss(*perturb(-eps * v), k, dy, **kw)
+        assert np.array_equal(ip, im)
+        fd = (lp - lm) / (2 * eps)
+        an = float((grad * v).sum())
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+    check("dx", g["dx"], lambda p: (x + p, wg, b, experts, sh))
+    check("d_w_gate", g["d_w_gate"], lambda p: (x, wg + p, b, experts, sh))
+    check("d_bias", g["d_bias"], lambda p: (x, wg, b + p, experts, sh))
+    for e in range(E):
+        for i, name in enumerate(("dw1", "dw3", "dw2")):
+            def pert(p, e=e, i=i):
+                ex = list(experts)
+                m = list(ex[e])
+                m[i] = m[i] + p
+                ex[e] = tuple(m)
+                return (x, wg, b, ex, sh)
+            check(f"{name}[{e}]", g[name][e], pert)
+    for i in range(3):
+        def pert_s(p, i=i):
+            m = list(sh)
+            m[i] = m[i] + p
+            return (x, wg, b, experts, tuple(m))
+        check(f"shared[{i}]", g["d_shared"][i], pert_s)
+    if mode == "replay_caller_weights":
+        assert not g["d_w_gate"].any() and not g["d_bias"].any()
+
+
+def test_backward_k1_has_no_gate_gradient_and_dense_form():
+    """k = 1: the renormalised weight is 1 whatever the logits, so the gate gets no
+    gradient; then dx is the dense sum of the chosen expert's and the shared expert's
+    input gradients."""
+    x, wg, b, experts, sh, _, dy, _ = _bwd_layer(12, k=1)
+    g = oracle.layer_backward(x, wg, b, experts, sh, 1, dy)
+    assert not g["d_w_gate"].any() and not g["d_bias"].any()
+    ids = g["fwd"]["ids"][:, 0]
+    for t in range(x.shape[0]):
+        gx, *_ = oracle.expert_backward(x[t:t + 1], dy[t:t + 1], *experts[ids[t]])
+        sx, *_ = oracle.expert_backward(x[t:t + 1], dy[t:t + 1], *sh)
+        assert np.allclose(g["dx"][t], gx[0] + sx[0], rtol=1e-12, atol=1e-12)
+
+
+def test_softmax_pick_grad_closed_form_k2():
+    """k = 2: w0 = sigmoid(l0 - l1), so dl0 = w0 w1 (dw0 - dw1) = -dl1."""
+    rng = np.random.default_rng(13)
+    l = rng.standard_normal((20, 2))
+    w = np.exp(l) / np.exp(l).sum(axis=1, keepdims=True)
+    dw = rng.standard_normal((20, 2))
+    dl = oracle.softmax_pick_grad(w, dw)
+    ref = w[:, 0] * w[:, 1] * (dw[:, 0] - dw[:, 1])
+    assert np.allclose(dl[:, 0], ref, rtol=0, atol=1e-15)
+    assert np.allclose(dl[:, 1], -ref, rtol=0, atol=1e-15)
+
+
+def test_silu_grad_values():
+    assert oracle.silu_grad(0.0) == 0.5
+    z = np.linspace(-8, 8, 33)
+    h = 1e-6
+    fd = (oracle.silu(z + h) - oracle.silu(z - h)) / (2 * h)
+    assert np.allclose(oracle.silu_grad(z), fd, rtol=0, atol=1e-9)
+    # large |z|: silu' -> 1 (z >> 0) and -> 0 (z << 0)
+    assert abs(oracle.silu_grad(40.0) - 1.0) < 1e-15 and abs(oracle.silu_grad(-40.0)) < 1e-15

@@ -1,5 +1,6 @@
 /*
- * libmoe -- the forward pass of one Mixture-of-Experts (MoE) layer on AMD MI355X (gfx950).
+ * libmoe -- the forward and backward pass of one Mixture-of-Experts (MoE) layer on AMD
+ * MI355X (gfx950).
  *
  * Each token's hidden state is gated to its top-k experts (or routed by replayed
  * expert IDs), the (token, slot) pairs are counting-sorted into contiguous
@@ -228,6 +229,79 @@ moe_status moe_expert_ffn_down(int dtype, int T, int d, int E, int k, int inter,
  * Requires d % 8 == 0. */
 moe_status moe_combine(const void* out, int dtype, const int32_t* row_of, const float* weights,
                        int T, int d, int k, int has_shared, void* y, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * Backward pass.  The MoE layer is trained as one grouped-GEMM flow forward and
+ * backward (Composer 2 Technical Report, section 6.1 "Kernels", Figure 10), and under
+ * router replay the router still computes gate scores so that gradients can flow
+ * through them (section 6.2, paragraph on inference and weight sync).  Given dL/dy,
+ * the four calls below give dL/dx, the expert weights' gradients and the gate's:
+ *   moe_combine_backward -> moe_expert_ffn_backward -> moe_route_backward.
+ * The expert selection is piecewise constant, so no gradient flows through the ids.
+ * Every reduction has one fixed order (no atomics): results are bitwise reproducible.
+ * ------------------------------------------------------------------------------ */
+
+/* Gradients of one expert bank, fp32, in the bank's layout: dw1, dw3 [n][I][d],
+ * dw2 [n][d][I]; 16-byte aligned. */
+typedef struct {
+  float* dw1;
+  float* dw3;
+  float* dw2;
+} moe_grad_bank;
+
+/* Workspace bytes for the forward calls and the backward calls of one layer shape
+ * (at least moe_workspace_size).  Same argument checks as moe_workspace_size. */
+moe_status moe_backward_workspace_size(int T, int d, int E, int k, int inter, int dtype, size_t* bytes);
+
+/* Backward of moe_combine for y_t = sum_r w_tr out[row_of[t,r]] (+ out[T k + t]).
+ *   dy        [T][d] dL/dy in the layer's output type (bf16; fp32 for MOE_F32).
+ *   out       the expert outputs moe_expert_ffn produced, [T*k (+T)][d].
+ *   d_out     out [T*k (+T)][d], same type: d_out[row_of[t,r]] = w_tr * dy_t (fp32
+ *             product, rounded once); with has_shared, d_out[T*k + t] = dy_t.
+ *   d_weights out fp32 [T][k]: dL/dw_tr = <dy_t, out[row_of[t,r]]>, an fp32 sum in one
+ *             fixed order that depends on d only.
+ * MOE_ERR_UNSUPPORTED: d % 8 != 0.  Pointers to 16-byte aligned rows. */
+moe_status moe_combine_backward(const void* dy, int dtype, const void* out, const int32_t* row_of,
+                                const float* weights, int T, int d, int k, int has_shared,
+                                void* d_out, float* d_weights, void* stream);
+
+/* Backward of moe_expert_ffn (bf16 layers; MOE_ERR_UNSUPPORTED for other dtypes and
+ * unless d % 128 == 0 and inter % 128 == 0).  Arguments x .. perm as moe_expert_ffn.
+ *   d_out     bf16 [T*k (+T)][d] from moe_combine_backward.
+ *   dx_rows   out fp32 [T*k (+T)][d]: each dispatched row's dL/dx, da W1 + dg W3 with
+ *             a = x W1, g = x W3 recomputed as the forward computes them, dh = d_out W2,
+ *             da = dh g silu'(a), dg = dh silu(a) (fp32, rounded to bf16 for the GEMMs).
+ *   routed_grads, shared_grads  out (moe_grad_bank): dW1 = da^T x, dW3 = dg^T x,
+ *             dW2 = d_out^T h per expert over its rows (h = the forward's bf16 h), every
+ *             expert written (zero when it got no rows).  shared_grads is NULL iff
+ *             shared is NULL.
+ *   ws        sized by moe_backward_workspace_size. */
+moe_status moe_expert_ffn_backward(const void* x, const uint8_t* x_scale, int dtype, int T, int d,
+                                   int E, int k, int inter, const moe_expert_bank* routed,
+                                   const moe_expert_bank* shared, const int32_t* offsets,
+                                   const int32_t* perm, const void* d_out, float* dx_rows,
+                                   const moe_grad_bank* routed_grads,
+                                   const moe_grad_bank* shared_grads, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+/* Backward of the routing and of the token gather.
+ *   dx        out fp32 [T][d]: sum_r dx_rows[row_of[t,r]] (r ascending), plus
+ *             dx_rows[T*k + t] when has_shared, plus the gate term below.
+ *   d_w_gate  out fp32 [d][E], or NULL when the routing weights did not come from the
+ *             gate (replay with caller weights): then the gate gets no gradient and dx
+ *             no gate term.  With the gate's weights w = softmax over the chosen ids,
+ *             renormalised: dl_tr = w_tr (d_weights_tr - sum_s w_ts d_weights_ts),
+ *             d_w_gate[:, e] = sum over expert e's rows of dl x_t (token ascending),
+ *             dx_t += sum_r dl_tr w_gate[:, ids_tr].
+ *   d_bias    out fp32 [E] (sum of dl per expert) or NULL; requires d_w_gate.
+ *   ids, weights, d_weights [T][k]; offsets, perm, row_of from moe_dispatch;
+ *   x as moe_route.  ws: moe_backward_workspace_size.  MOE_ERR_UNSUPPORTED: d % 4. */
+moe_status moe_route_backward(const void* x, const uint8_t* x_scale, int dtype, int T, int d,
+                              const float* w_gate, int E, int k, const int32_t* ids,
+                              const float* weights, const float* d_weights, const int32_t* offsets,
+                              const int32_t* perm, const int32_t* row_of, const float* dx_rows,
+                              int has_shared, float* dx, float* d_w_gate, float* d_bias, void* ws,
+                              size_t ws_bytes, void* stream);
 
 /* Synchronises `stream`, reads and clears the workspace's device error flag and
  * returns MOE_ERR_BAD_IDS, MOE_ERR_NONFINITE or MOE_OK. */

@@ -17,7 +17,8 @@ __all__ = [
     "moe_workspace_size", "moe_workspace_init", "moe_route", "moe_route_replay",
     "moe_route_replay_filtered",
     "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_gate_up", "moe_expert_ffn_down", "moe_combine", "moe_check", "moe_status_string",
-    "layer_forward",
+    "layer_forward", "moe_backward_workspace_size", "moe_combine_backward", "moe_expert_ffn_backward",
+    "moe_route_backward", "layer_backward",
 ]
 
 MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
@@ -38,6 +39,10 @@ class _Bank(ctypes.Structure):
                 ("w2_scale", ctypes.c_void_p)]
 
 
+class _GradBank(ctypes.Structure):
+    _fields_ = [("dw1", ctypes.c_void_p), ("dw3", ctypes.c_void_p), ("dw2", ctypes.c_void_p)]
+
+
 def lib():
     """The loaded libmoe.so (raises if it has not been built)."""
     global _lib
@@ -52,6 +57,12 @@ def lib():
             "moe_workspace_init": [P, SZ, P],
             "moe_route": [P, P, I, I, I, P, P, I, I, P, P, P, SZ, P],
             "moe_route_replay": [P, P, I, I, I, P, P, I, I, P, P, P, P, SZ, P],
+            "moe_backward_workspace_size": [I, I, I, I, I, I, PSZ],
+            "moe_combine_backward": [P, I, P, P, P, I, I, I, I, P, P, P],
+            "moe_expert_ffn_backward": [P, P, I, I, I, I, I, I, ctypes.POINTER(_Bank),
+                                        ctypes.POINTER(_Bank), P, P, P, P, ctypes.POINTER(_GradBank),
+                                        ctypes.POINTER(_GradBank), P, SZ, P],
+            "moe_route_backward": [P, P, I, I, I, P, I, I, P, P, P, P, P, P, P, I, P, P, P, P, SZ, P],
             "moe_route_replay_filtered": [P, P, I, I, I, P, P, I, I, P, ctypes.c_double, P, P, P, SZ,
                                           P],
             "moe_dispatch": [P, I, I, I, P, P, P, P, SZ, P],
@@ -284,3 +295,109 @@ def layer_forward(inp: dict, k: int, ws: Workspace | None = None, replay: bool =
             raise MoeError(st, "layer_forward")
     return {"y": y, "ids": ids, "weights": weights, "offsets": offsets, "perm": perm,
             "row_of": row_of, "out": out}
+
+
+# ---------------------------------------------------------------------------
+# Backward pass
+# ---------------------------------------------------------------------------
+def moe_backward_workspace_size(T, d, E, k, inter, dtype) -> int:
+    n = ctypes.c_size_t()
+    _ok(lib().moe_backward_workspace_size(T, d, E, k, inter, dtype, ctypes.byref(n)),
+        "moe_backward_workspace_size")
+    return n.value
+
+
+class BackwardWorkspace(Workspace):
+    """A workspace sized for the forward and the backward calls of one layer shape."""
+
+    def __init__(self, T, d, E, k, inter, dtype, device="cuda"):
+        self.nbytes = moe_backward_workspace_size(T, d, E, k, inter, dtype)
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        moe_workspace_init(self.buf)
+
+
+def moe_combine_backward(dy, out, row_of, weights, T, has_shared, dtype, d_out=None, d_weights=None):
+    _check_dev(dy, out, row_of, weights)
+    d = out.shape[1]
+    k = weights.shape[1]
+    d_out = torch.empty_like(out) if d_out is None else d_out
+    d_weights = torch.empty(T, k, dtype=torch.float32, device=out.device) if d_weights is None else d_weights
+    _ok(lib().moe_combine_backward(_ptr(dy), dtype, _ptr(out), _ptr(row_of), _ptr(weights), T, d, k,
+                                   1 if has_shared else 0, _ptr(d_out), _ptr(d_weights),
+                                   _stream(out.device)), "moe_combine_backward")
+    return d_out, d_weights
+
+
+def _grads(b):
+    return None if b is None else _GradBank(b["w1"].data_ptr(), b["w3"].data_ptr(), b["w2"].data_ptr())
+
+
+def _grad_like(bank):
+    return {n: torch.empty(bank[n].shape, dtype=torch.float32, device=bank[n].device)
+            for n in ("w1", "w3", "w2")}
+
+
+def moe_expert_ffn_backward(x, routed: dict, shared, offsets, perm, k, d_out, ws: Workspace,
+                            x_scale=None, dx_rows=None, grads=None, shared_grads=None):
+    """Returns (dx_rows [rows][d] fp32, grads {w1, w3, w2} fp32, shared grads or None)."""
+    _check_dev(x, x_scale, offsets, perm, d_out)
+    T, d = x.shape
+    E, inter = routed["w1"].shape[0], routed["w1"].shape[1]
+    rows = T * k + (T if shared is not None else 0)
+    dx_rows = torch.empty(rows, d, dtype=torch.float32, device=x.device) if dx_rows is None else dx_rows
+    grads = _grad_like(routed) if grads is None else grads
+    if shared is not None and shared_grads is None:
+        shared_grads = _grad_like(shared)
+    rb, sb = _bank(routed), _bank(shared)
+    rg, sg = _grads(grads), _grads(shared_grads)
+    _ok(lib().moe_expert_ffn_backward(_ptr(x), _ptr(x_scale), _dtype_of(x), T, d, E, k, inter,
+                                      ctypes.byref(rb), ctypes.byref(sb) if sb is not None else None,
+                                      _ptr(offsets), _ptr(perm), _ptr(d_out), _ptr(dx_rows),
+                                      ctypes.byref(rg), ctypes.byref(sg) if sg is not None else None,
+                                      ws.ptr, ws.nbytes, _stream(x.device)), "moe_expert_ffn_backward")
+    return dx_rows, grads, shared_grads
+
+
+def moe_route_backward(x, w_gate, ids, weights, d_weights, offsets, perm, row_of, dx_rows, has_shared,
+                       ws: Workspace, gate_grad=True, bias_grad=True, x_scale=None, dx=None):
+    """Returns (dx [T][d] fp32, d_w_gate [d][E] or None, d_bias [E] or None)."""
+    _check_dev(x, x_scale, w_gate, ids, weights, d_weights, offsets, perm, row_of, dx_rows)
+    T, d = x.shape
+    E = w_gate.shape[1]
+    k = ids.shape[1]
+    dev = x.device
+    dx = torch.empty(T, d, dtype=torch.float32, device=dev) if dx is None else dx
+    dwg = torch.empty(d, E, dtype=torch.float32, device=dev) if gate_grad else None
+    db = torch.empty(E, dtype=torch.float32, device=dev) if gate_grad and bias_grad else None
+    _ok(lib().moe_route_backward(_ptr(x), _ptr(x_scale), _dtype_of(x), T, d, _ptr(w_gate), E, k,
+                                 _ptr(ids), _ptr(weights), _ptr(d_weights), _ptr(offsets), _ptr(perm),
+                                 _ptr(row_of), _ptr(dx_rows), 1 if has_shared else 0, _ptr(dx),
+                                 _ptr(dwg), _ptr(db), ws.ptr, ws.nbytes, _stream(dev)),
+        "moe_route_backward")
+    return dx, dwg, db
+
+
+def layer_backward(inp: dict, k: int, fwd: dict, dy, ws: Workspace, replay: bool = False,
+                   check: bool = True):
+    """Gradients of one layer through the three backward C calls, given the forward's
+    routing/dispatch results and expert outputs (``layer_forward``'s dict) and dL/dy.
+    The gate gets a gradient unless the routing weights were the caller's."""
+    x = inp["x"]
+    T = x.shape[0]
+    dt = _dtype_of(x)
+    has_shared = inp.get("shared") is not None
+    d_out, d_weights = moe_combine_backward(dy, fwd["out"], fwd["row_of"], fwd["weights"], T, has_shared, dt)
+    routed = {n: inp.get(n) for n in ("w1", "w3", "w2", "w1_scale", "w3_scale", "w2_scale")}
+    dx_rows, grads, sgrads = moe_expert_ffn_backward(x, routed, inp.get("shared"), fwd["offsets"],
+                                                     fwd["perm"], k, d_out, ws, x_scale=inp.get("x_scale"))
+    gate_grad = not (replay and inp.get("weights_in") is not None)
+    dx, dwg, db = moe_route_backward(x, inp["w_gate"], fwd["ids"], fwd["weights"], d_weights,
+                                     fwd["offsets"], fwd["perm"], fwd["row_of"], dx_rows, has_shared, ws,
+                                     gate_grad=gate_grad, bias_grad=inp.get("bias") is not None,
+                                     x_scale=inp.get("x_scale"))
+    if check:
+        st = moe_check(ws)
+        if st != 0:
+            raise MoeError(st, "layer_backward")
+    return {"dx": dx, "d_weights": d_weights, "d_w_gate": dwg, "d_bias": db, "grads": grads,
+            "shared_grads": sgrads, "dx_rows": dx_rows, "d_out": d_out}

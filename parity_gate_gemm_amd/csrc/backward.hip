@@ -1,0 +1,664 @@
+// Backward pass of the MoE layer: the chain rule of the forward (route -> dispatch ->
+// grouped SwiGLU FFN -> combine) for a loss whose gradient dL/dy is given, as grouped
+// GEMMs over the same expert segments as the forward (Composer 2 Technical Report,
+// section 6.1 "Kernels", Figure 10: the MoE layer is trained as one grouped-GEMM flow;
+// under router replay the router still computes gate scores so that gradients flow
+// through them: section 6.2, paragraph on inference and weight sync).
+//
+//   combine:  d_out[row(t,r)] = w_tr dy_t,  d_w_tr = <dy_t, out[row(t,r)]>,
+//             shared rows d_out[T k + t] = dy_t;
+//   experts:  a = x W1, g = x W3 (recomputed), dh = d_out W2, da = dh g silu'(a),
+//             dg = dh silu(a), dx_row = da W1^T + dg W3^T (as stored: da w1 + dg w3),
+//             dW2 = d_out^T h, dW1 = da^T x, dW3 = dg^T x (per expert segment);
+//   route:    dx_t = sum_r dx_row(t,r) + dx_row(shared t) + sum_r dl_tr Wg[:, e_tr],
+//             dl = w (dw - <w, dw>) when the weights are the gate's renormalised
+//             softmax, dWg[:, e] = sum over e's rows of dl x_t, db[e] = sum of dl.
+//
+// Every reduction has one fixed order: a GEMM output sweeps K in ascending 64-wide
+// steps with one MFMA sequence (no split-K, no atomics), token sums run in rank order,
+// so the gradients are bitwise reproducible and a token's dx does not depend on the
+// rest of the batch.
+#include <math.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// combine backward: one workgroup per token; d_w by a per-thread fp32 FMA chain over
+// the thread's 8-element chunks, a fixed butterfly per wavefront and the wavefronts'
+// partial sums added in order.
+// ---------------------------------------------------------------------------
+template <bool kF32>
+__device__ __forceinline__ void load8(const void* p, long long row, int d, int c, float (&v)[8]) {
+  if (kF32) {
+    const float4* q = (const float4*)((const float*)p + row * d + c);
+    const float4 a = q[0], b = q[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4 u = *(const uint4*)((const uint16_t*)p + row * d + c);
+    const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_to_f32((uint16_t)(wd[i] & 0xffff));
+      v[2 * i + 1] = bf16_to_f32((uint16_t)(wd[i] >> 16));
+    }
+  }
+}
+
+template <bool kF32>
+__device__ __forceinline__ void store8(void* p, long long row, int d, int c, const float (&v)[8]) {
+  if (kF32) {
+    float4* q = (float4*)((float*)p + row * d + c);
+    q[0] = make_float4(v[0], v[1], v[2], v[3]);
+    q[1] = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    uint4 u;
+    u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    u.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
+    u.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+    *(uint4*)((uint16_t*)p + row * d + c) = u;
+  }
+}
+
+template <bool kF32>
+__global__ __launch_bounds__(1024) void combine_bwd_kernel(const void* __restrict__ dy,
+                                                          const void* __restrict__ out,
+                                                          const int32_t* __restrict__ row_of,
+                                                          const float* __restrict__ weights, int T,
+                                                          int d, int k, int has_shared,
+                                                          void* __restrict__ d_out,
+                                                          float* __restrict__ d_weights) {
+  __shared__ float part[16];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const long long Tk = (long long)T * k;
+  for (int r = 0; r < k; ++r) {
+    long long j = row_of[(size_t)t * k + r];
+    j = (j < 0 || j >= Tk) ? 0 : j;   // guard against corrupt input (as the forward combine)
+    const float w = weights[(size_t)t * k + r];
+    float acc = 0.0f;
+    for (int c = tid * 8; c < d; c += blockDim.x * 8) {
+      float g[8], o[8], dg[8];
+      load8<kF32>(dy, t, d, c, g);
+      load8<kF32>(out, j, d, c, o);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        acc = fmaf(g[i], o[i], acc);
+        dg[i] = w * g[i];
+      }
+      store8<kF32>(d_out, j, d, c, dg);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) part[wave] = acc;
+    __syncthreads();
+    if (tid == 0) {
+      float s = 0.0f;
+      for (int q = 0; q < nw; ++q) s += part[q];
+      d_weights[(size_t)t * k + r] = s;
+    }
+    __syncthreads();
+  }
+  if (has_shared) {
+    for (int c = tid * 8; c < d; c += blockDim.x * 8) {
+      float g[8];
+      load8<kF32>(dy, t, d, c, g);
+      store8<kF32>(d_out, Tk + t, d, c, g);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward grouped GEMMs (bf16 operands, fp32 accumulation), one kind per launch:
+//   DH   : C[n][i] = sum_j d_out[n][j] W2[e][j][i]      rows x I,  K = d   (+ SwiGLU backward)
+//   DX   : C[n][j] = sum_i dadg[n][i] W13[e][i][j]     rows x d,  K = 2I  (W13 = W1 then W3)
+//   DW2  : C[j][i] = sum_n d_out[n][j] h[n][i]         d x I,     K = the segment's rows
+//   DW13 : C[i][j] = sum_n dadg[n][i] x[tok(n)][j]     2I x d,    K = the segment's rows
+// Tile 128 x 128, 4 wavefronts of 64 x 64 (2 x 2 MFMA 32x32x16 blocks), K steps of 64
+// through LDS rows of 64 K-values (144-byte stride).  An operand stored with K as its
+// row index ("K-major": the weight operands of DH and DX, both operands of the weight
+// gradients) is read as 4 K-rows x 8 columns per thread and transposed in registers
+// before the 8-byte LDS writes; K-rows past a segment's end read as zero.
+// ---------------------------------------------------------------------------
+constexpr int GB_T = 128, GB_K = 64, GB_S = GB_K + 8, GB_THR = 256;
+enum { BK_DH = 0, BK_DX = 1, BK_DW2 = 2, BK_DW13 = 3 };
+
+struct BwdGemm {
+  const uint16_t* x;        // activations [T][d]
+  const int32_t* perm;
+  int T, k, E, d, I;
+  long long Tk;
+  const uint16_t* w1;       // routed banks [E][I][d], [E][I][d], [E][d][I]
+  const uint16_t* w3;
+  const uint16_t* w2;
+  const uint16_t* sw1;      // shared expert (null without one)
+  const uint16_t* sw3;
+  const uint16_t* sw2;
+  const uint16_t* d_out;    // [rows][d]
+  const float* pre;         // [rows][2I]: a, then g
+  uint16_t* dadg;           // [rows][2I]: da, then dg
+  uint16_t* h;              // [rows][I]
+  float* dx_rows;           // [rows][d]
+  float* dw1;               // routed gradients, layout of the banks
+  float* dw3;
+  float* dw2;
+  float* sdw1;              // shared expert's gradients
+  float* sdw3;
+  float* sdw2;
+  const int* mstart;
+  const int* rowstart;
+  const int* rowcount;
+  int S;
+  int MT, NT;               // tiles along M (weight-gradient kinds) and along N
+  int* flag;
+};
+
+__device__ __forceinline__ float silu_of(float a) { return a / (1.0f + expf(-a)); }
+
+template <int KIND>
+__global__ __launch_bounds__(GB_THR) void bwd_gemm_kernel(BwdGemm g) {
+  constexpr bool WGRAD = KIND >= BK_DW2;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[GB_T * GB_S];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[GB_T * GB_S];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---- tile decode ----
+  int s, row0, mrows = GB_T, K, m0 = 0, n0;
+  if (!WGRAD) {
+    const int total = g.mstart[g.S] * g.NT;
+    int tile;
+    if (!xcd_tile<0>(total, tile)) return;
+    int lo = 0, hi = g.S;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (g.mstart[mid] * g.NT <= tile) lo = mid; else hi = mid;
+    }
+    s = lo;
+    const int mtiles = g.mstart[s + 1] - g.mstart[s];
+    const int local = tile - g.mstart[s] * g.NT;
+    constexpr int GM = 8;   // row tiles per raster group (they share each weight slab)
+    const int grp = local / (GM * g.NT), rem = local % (GM * g.NT);
+    const int gm = min(GM, mtiles - grp * GM);
+    const int nt = rem / gm, mt = grp * GM + rem % gm;
+    row0 = g.rowstart[s] + mt * GB_T;
+    mrows = min(GB_T, g.rowcount[s] - mt * GB_T);
+    n0 = nt * GB_T;
+    K = KIND == BK_DH ? g.d : 2 * g.I;
+  } else {
+    const int per = g.MT * g.NT;
+    int tile;
+    if (!xcd_tile<0>(g.S * per, tile)) return;
+    s = tile / per;
+    const int rem = tile % per;
+    m0 = (rem / g.NT) * GB_T;
+    n0 = (rem % g.NT) * GB_T;
+    row0 = g.rowstart[s];
+    K = g.rowcount[s];
+  }
+  const bool is_shared = s == g.E;
+  const long long e = is_shared ? 0 : s;
+
+  // ---- loaders ----
+  // row operand (A of DH / DX): rows lr + 32 i, 16-byte chunk lc of the K-step
+  const int lr = tid >> 3, lc = (tid & 7) * 8;
+  // K-major operands: K-rows 4 kq .. 4 kq + 3 of the step, columns 8 rb .. 8 rb + 7
+  const int kq = tid & 15, rb = tid >> 4;
+  const uint16_t* arow[4];
+  if (!WGRAD) {
+    const uint16_t* base = KIND == BK_DH ? g.d_out : g.dadg;
+    const long long ld = KIND == BK_DH ? g.d : 2LL * g.I;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = lr + 32 * i;
+      arow[i] = base + ((long long)row0 + (r < mrows ? r : 0)) * ld + lc;
+    }
+  }
+  const uint16_t* w1b = is_shared ? g.sw1 : g.w1 + e * g.I * (long long)g.d;
+  const uint16_t* w3b = is_shared ? g.sw3 : g.w3 + e * g.I * (long long)g.d;
+  const uint16_t* w2b = is_shared ? g.sw2 : g.w2 + e * g.d * (long long)g.I;
+  int bad = 0;
+  // source of K-row kg (global K index) of operand `which` (0: A, 1: B), or null for zero
+  auto ksrc = [&](int which, int kg) -> const uint16_t* {
+    if (KIND == BK_DH) return w2b + (long long)kg * g.I + n0 + 8 * rb;
+    if (KIND == BK_DX)
+      return (kg < g.I ? w1b + (long long)kg * g.d : w3b + (long long)(kg - g.I) * g.d) + n0 + 8 * rb;
+    if (kg >= K) return nullptr;
+    const long long j = (long long)row0 + kg;
+    if (KIND == BK_DW2)
+      return which == 0 ? g.d_out + j * g.d + m0 + 8 * rb : g.h + j * g.I + n0 + 8 * rb;
+    if (which == 0) return g.dadg + j * 2LL * g.I + m0 + 8 * rb;
+    long long tok = is_shared ? j - g.Tk : (long long)(g.perm[j] / g.k);
+    if (tok < 0 || tok >= g.T) {
+      bad = 1;
+      tok = 0;
+    }
+    return g.x + tok * g.d + n0 + 8 * rb;
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+
+  u32x4_t ra[4], ka[4], kb[4];
+  const u32x4_t zero4 = {0u, 0u, 0u, 0u};
+  auto gload = [&](int k0) {
+    if (!WGRAD) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ra[i] = *(const u32x4_t*)(arow[i] + k0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t* p = ksrc(0, k0 + 4 * kq + i);
+        ka[i] = p ? *(const u32x4_t*)p : zero4;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t* p = ksrc(1, k0 + 4 * kq + i);
+      kb[i] = p ? *(const u32x4_t*)p : zero4;
+    }
+  };
+  // 4 K-rows x 8 columns -> LDS rows 8 rb + c, K offset 4 kq (two dwords per row)
+  auto tstore = [&](uint16_t* sX, const u32x4_t(&R)[4]) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t s0 = R[0][c >> 1], s1 = R[1][c >> 1], s2 = R[2][c >> 1], s3 = R[3][c >> 1];
+      u32x2_t v;
+      if ((c & 1) == 0) {
+        v[0] = (s0 & 0xffffu) | (s1 << 16);
+        v[1] = (s2 & 0xffffu) | (s3 << 16);
+      } else {
+        v[0] = (s0 >> 16) | (s1 & 0xffff0000u);
+        v[1] = (s2 >> 16) | (s3 & 0xffff0000u);
+      }
+      *(u32x2_t*)&sX[(8 * rb + c) * GB_S + 4 * kq] = v;
+    }
+  };
+
+  const int nsteps = (K + GB_K - 1) / GB_K;
+  if (nsteps > 0) gload(0);
+  for (int st = 0; st < nsteps; ++st) {
+    if (!WGRAD) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *(u32x4_t*)&sA[(lr + 32 * i) * GB_S + lc] = ra[i];
+    } else {
+      tstore(sA, ka);
+    }
+    tstore(sB, kb);
+    __syncthreads();
+    if (st + 1 < nsteps) gload((st + 1) * GB_K);
+#pragma unroll
+    for (int kk = 0; kk < GB_K; kk += 16) {
+      const int kc = kk + (lane >> 5) * 8;
+      bf16x8_t af[2], bf[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        af[mb] = __builtin_bit_cast(bf16x8_t,
+                                    *(const u32x4_t*)&sA[(wm * 64 + mb * 32 + (lane & 31)) * GB_S + kc]);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        bf[nb] = __builtin_bit_cast(bf16x8_t,
+                                    *(const u32x4_t*)&sB[(wn * 64 + nb * 32 + (lane & 31)) * GB_S + kc]);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bf[nb], acc[mb][nb], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  if (bad) raise_flag(g.flag, kFlagCorrupt);
+
+  // ---- epilogue: accumulator element v of a lane is C[i][j], j = lane % 32,
+  //      i = 8 (v / 4) + 4 (lane / 32) + v % 4 ----
+  const int j = lane & 31;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = wm * 64 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (!WGRAD && r >= mrows) continue;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int col = n0 + wn * 64 + nb * 32 + j;
+        const float c = acc[mb][nb][v];
+        if (KIND == BK_DH) {
+          const long long orow = (long long)row0 + r;
+          const float a = g.pre[orow * 2 * g.I + col], gg = g.pre[orow * 2 * g.I + g.I + col];
+          const float sg = 1.0f / (1.0f + expf(-a));
+          const float sl = silu_of(a);
+          g.dadg[orow * 2 * g.I + col] = f32_to_bf16(c * gg * (sg * (1.0f + a * (1.0f - sg))));
+          g.dadg[orow * 2 * g.I + g.I + col] = f32_to_bf16(c * sl);
+          g.h[orow * g.I + col] = f32_to_bf16(sl * gg);
+        } else if (KIND == BK_DX) {
+          g.dx_rows[((long long)row0 + r) * g.d + col] = c;
+        } else if (KIND == BK_DW2) {
+          float* dst = is_shared ? g.sdw2 : g.dw2 + e * g.d * (long long)g.I;
+          dst[(long long)(m0 + r) * g.I + col] = c;
+        } else {
+          const int m = m0 + r;
+          float* dst = m < g.I ? (is_shared ? g.sdw1 : g.dw1 + e * g.I * (long long)g.d)
+                               : (is_shared ? g.sdw3 : g.dw3 + e * g.I * (long long)g.d);
+          dst[(long long)(m < g.I ? m : m - g.I) * g.d + col] = c;
+        }
+      }
+    }
+  }
+}
+
+// Zero fill by a kernel (callers may capture these calls in a graph).
+__global__ __launch_bounds__(256) void zero_fill_kernel(float* __restrict__ p, long long n) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
+    p[i] = 0.0f;
+}
+static void zero_fill(float* p, long long n, hipStream_t s) {
+  if (n <= 0) return;
+  const long long blocks = (n + 255) / 256;
+  zero_fill_kernel<<<(unsigned)(blocks < 65536 ? blocks : 65536), 256, 0, s>>>(p, n);
+}
+
+// ---------------------------------------------------------------------------
+// Route backward
+// ---------------------------------------------------------------------------
+// dl_tr = w_tr (dw_tr - sum_s w_ts dw_ts), the sum in column order.
+__global__ __launch_bounds__(256) void route_bwd_dl_kernel(const float* __restrict__ w,
+                                                           const float* __restrict__ dw, int T, int k,
+                                                           float* __restrict__ dl) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  float s = 0.0f;
+  for (int r = 0; r < k; ++r) s = fmaf(w[(size_t)t * k + r], dw[(size_t)t * k + r], s);
+  for (int r = 0; r < k; ++r) dl[(size_t)t * k + r] = w[(size_t)t * k + r] * (dw[(size_t)t * k + r] - s);
+}
+
+// wt[e][i] = wg[i][e] through 64 x 64 LDS tiles.
+__global__ __launch_bounds__(256) void gate_transpose_kernel(const float* __restrict__ wg, int d, int E,
+                                                             float* __restrict__ wt) {
+  __shared__ float tile[64][65];
+  const int i0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  for (int q = threadIdx.x; q < 64 * 64; q += 256) {
+    const int ir = q / 64, ec = q % 64;
+    tile[ir][ec] = (i0 + ir < d && e0 + ec < E) ? wg[(size_t)(i0 + ir) * E + e0 + ec] : 0.0f;
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < 64 * 64; q += 256) {
+    const int er = q / 64, ic = q % 64;
+    if (i0 + ic < d && e0 + er < E) wt[(size_t)(e0 + er) * d + i0 + ic] = tile[ic][er];
+  }
+}
+
+// dx_t = sum_r dx_rows[row(t,r)] (r ascending) + dx_rows[T k + t] + sum_r dl_tr wt[e_tr]
+// (r ascending), fp32; one workgroup per token, 4 columns per thread.
+__global__ __launch_bounds__(1024) void route_bwd_dx_kernel(
+    const float* __restrict__ dx_rows, const int32_t* __restrict__ row_of, int T, int d, int k,
+    int has_shared, const int32_t* __restrict__ ids, const float* __restrict__ dl,
+    const float* __restrict__ wt, int E, float* __restrict__ dx) {
+  __shared__ long long srow[kMaxTopK];
+  __shared__ int sid[kMaxTopK];
+  __shared__ float sdl[kMaxTopK];
+  const int t = blockIdx.x;
+  const long long Tk = (long long)T * k;
+  if (threadIdx.x < k) {
+    long long r = row_of[(size_t)t * k + threadIdx.x];
+    srow[threadIdx.x] = (r < 0 || r >= Tk) ? 0 : r;
+    if (dl) {
+      const int e = ids[(size_t)t * k + threadIdx.x];
+      sid[threadIdx.x] = (e < 0 || e >= E) ? 0 : e;
+      sdl[threadIdx.x] = dl[(size_t)t * k + threadIdx.x];
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x * 4; c < d; c += blockDim.x * 4) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int r = 0; r < k; ++r) {
+      const float4 v = *(const float4*)(dx_rows + srow[r] * d + c);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    if (has_shared) {
+      const float4 v = *(const float4*)(dx_rows + (Tk + t) * d + c);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    if (dl) {
+      for (int r = 0; r < k; ++r) {
+        const float4 v = *(const float4*)(wt + (size_t)sid[r] * d + c);
+        const float q = sdl[r];
+        acc.x = fmaf(q, v.x, acc.x); acc.y = fmaf(q, v.y, acc.y);
+        acc.z = fmaf(q, v.z, acc.z); acc.w = fmaf(q, v.w, acc.w);
+      }
+    }
+    *(float4*)(dx + (size_t)t * d + c) = acc;
+  }
+}
+
+// dWg[:, e] = sum over expert e's dispatched rows (token ascending) of dl x_t, db[e] the
+// sum of those dl; workgroup (column chunk of 256, expert e).
+__global__ __launch_bounds__(256) void route_bwd_wgate_kernel(
+    const void* __restrict__ x, const uint8_t* __restrict__ xs, int dtype, int T, int d, int k, int E,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
+    const float* __restrict__ dl, float* __restrict__ dwg, float* __restrict__ db, int* flag) {
+  const int e = blockIdx.y, c = blockIdx.x * 256 + threadIdx.x;
+  const long long Tk = (long long)T * k;
+  long long lo = offsets[e], hi = offsets[e + 1];
+  lo = lo < 0 ? 0 : (lo > Tk ? Tk : lo);
+  hi = hi < lo ? lo : (hi > Tk ? Tk : hi);
+  float acc = 0.0f, bacc = 0.0f;
+  int bad = 0;
+  for (long long n = lo; n < hi; ++n) {
+    long long p = perm[n];
+    if (p < 0 || p >= Tk) {
+      bad = 1;
+      p = 0;
+    }
+    const float q = dl[p];
+    if (c < d) acc = fmaf(q, (float)load_act_f64(x, xs, dtype, (size_t)(p / k), d, c), acc);
+    bacc += q;
+  }
+  if (bad && threadIdx.x == 0) raise_flag(flag, kFlagCorrupt);
+  if (c < d) dwg[(size_t)c * E + e] = acc;
+  if (db && blockIdx.x == 0 && threadIdx.x == 0) db[e] = bacc;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" moe_status moe_backward_workspace_size(int T, int d, int E, int k, int inter, int dtype,
+                                                  size_t* bytes) {
+  if (!bytes || T < 0 || d < 1 || E < 1 || E > kMaxExperts || k < 1 || k > E || k > kMaxTopK ||
+      inter < 1 || !valid_dtype(dtype))
+    return MOE_ERR_INVALID_ARG;
+  const size_t a = workspace_bytes(T, d, E, k, inter, dtype), b = bwd_ws(T, d, E, k, inter).bytes;
+  *bytes = a > b ? a : b;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_combine_backward(const void* dy, int dtype, const void* out,
+                                           const int32_t* row_of, const float* weights, int T, int d,
+                                           int k, int has_shared, void* d_out, float* d_weights,
+                                           void* stream) {
+  if (!valid_dtype(dtype) || T < 0 || d < 1 || k < 1 || k > kMaxTopK) return MOE_ERR_INVALID_ARG;
+  if (d % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!dy || !out || !row_of || !weights || !d_out || !d_weights) return MOE_ERR_INVALID_ARG;
+  if (!aligned(dy, 16) || !aligned(out, 16) || !aligned(d_out, 16)) return MOE_ERR_INVALID_ARG;
+  if ((long long)T * k > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  const int chunks = d / 8, passes = (chunks + 1023) / 1024;
+  const int thr = ((chunks + passes - 1) / passes + 63) / 64 * 64;
+  if (dtype == MOE_F32)
+    combine_bwd_kernel<true><<<T, thr, 0, s>>>(dy, out, row_of, weights, T, d, k, has_shared ? 1 : 0,
+                                               d_out, d_weights);
+  else
+    combine_bwd_kernel<false><<<T, thr, 0, s>>>(dy, out, row_of, weights, T, d, k, has_shared ? 1 : 0,
+                                                d_out, d_weights);
+  return launch_status();
+}
+
+static bool grads_ok(const moe_grad_bank* g) {
+  return g && g->dw1 && g->dw3 && g->dw2 && aligned(g->dw1, 16) && aligned(g->dw3, 16) &&
+         aligned(g->dw2, 16);
+}
+
+extern "C" moe_status moe_expert_ffn_backward(const void* x, const uint8_t* x_scale, int dtype, int T,
+                                              int d, int E, int k, int inter,
+                                              const moe_expert_bank* routed,
+                                              const moe_expert_bank* shared, const int32_t* offsets,
+                                              const int32_t* perm, const void* d_out, float* dx_rows,
+                                              const moe_grad_bank* routed_grads,
+                                              const moe_grad_bank* shared_grads, void* ws,
+                                              size_t ws_bytes, void* stream) {
+  if (!valid_dtype(dtype) || T < 0 || d < 1 || E < 1 || E > kMaxExperts || k < 1 || k > E ||
+      k > kMaxTopK || inter < 1)
+    return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (x_scale) return MOE_ERR_INVALID_ARG;
+  if (d % 128 != 0 || inter % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!ws || !routed || !routed->w1 || !routed->w3 || !routed->w2 || routed->w1_scale ||
+      routed->w3_scale || routed->w2_scale || !grads_ok(routed_grads))
+    return MOE_ERR_INVALID_ARG;
+  if ((shared != nullptr) != (shared_grads != nullptr)) return MOE_ERR_INVALID_ARG;
+  if (shared && (!shared->w1 || !shared->w3 || !shared->w2 || !grads_ok(shared_grads)))
+    return MOE_ERR_INVALID_ARG;
+  if ((long long)T * k > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+  const BwdWs L = bwd_ws(T, d, E, k, inter);
+  if (ws_bytes < L.bytes) return MOE_ERR_WORKSPACE;
+  if (T > 0 && (!x || !offsets || !perm || !d_out || !dx_rows)) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!aligned(x, 16) || !aligned(d_out, 16) || !aligned(dx_rows, 16)))
+    return MOE_ERR_INVALID_ARG;
+  const moe_expert_bank* banks[2] = {routed, shared};
+  for (const moe_expert_bank* b : banks)
+    if (b && (!aligned(b->w1, 16) || !aligned(b->w3, 16) || !aligned(b->w2, 16)))
+      return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  const int has_shared = shared ? 1 : 0;
+  BwdGemm g{};
+  g.x = (const uint16_t*)x;
+  g.perm = perm;
+  g.T = T;
+  g.k = k;
+  g.E = E;
+  g.d = d;
+  g.I = inter;
+  g.Tk = (long long)T * k;
+  g.w1 = (const uint16_t*)routed->w1;
+  g.w3 = (const uint16_t*)routed->w3;
+  g.w2 = (const uint16_t*)routed->w2;
+  g.sw1 = shared ? (const uint16_t*)shared->w1 : nullptr;
+  g.sw3 = shared ? (const uint16_t*)shared->w3 : nullptr;
+  g.sw2 = shared ? (const uint16_t*)shared->w2 : nullptr;
+  g.d_out = (const uint16_t*)d_out;
+  g.pre = (const float*)(w + L.pre);
+  g.dadg = (uint16_t*)(w + L.dadg);
+  g.h = (uint16_t*)(w + L.h);
+  g.dx_rows = dx_rows;
+  g.dw1 = routed_grads->dw1;
+  g.dw3 = routed_grads->dw3;
+  g.dw2 = routed_grads->dw2;
+  g.sdw1 = shared ? shared_grads->dw1 : nullptr;
+  g.sdw3 = shared ? shared_grads->dw3 : nullptr;
+  g.sdw2 = shared ? shared_grads->dw2 : nullptr;
+  int* seg = (int*)(w + L.seg);
+  g.mstart = seg;
+  g.rowstart = seg + (E + 2);
+  g.rowcount = seg + 2 * (E + 2);
+  g.S = E + has_shared;
+  g.flag = (int*)w;
+  moe_status st;
+  if (T > 0) {
+    // recomputed pre-activations (and the segment table the kernels below read)
+    if ((st = ffn_recompute_pre(x, T, d, E, k, inter, routed, shared, offsets, perm, seg, (float*)g.pre,
+                                g.flag, s)) != MOE_OK)
+      return st;
+    const long long mt_bound = (g.Tk + (long long)E * (GB_T - 1)) / GB_T + (has_shared ? (T + GB_T - 1) / GB_T : 0);
+    g.NT = inter / GB_T;
+    long long grid = tile_grid(mt_bound * g.NT, 0);
+    if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+    bwd_gemm_kernel<BK_DH><<<(unsigned)grid, GB_THR, 0, s>>>(g);
+    g.NT = d / GB_T;
+    grid = tile_grid(mt_bound * g.NT, 0);
+    if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+    bwd_gemm_kernel<BK_DX><<<(unsigned)grid, GB_THR, 0, s>>>(g);
+  } else {   // empty batch: every weight gradient is zero
+    const long long n13 = (long long)E * inter * d;
+    zero_fill(routed_grads->dw1, n13, s);
+    zero_fill(routed_grads->dw3, n13, s);
+    zero_fill(routed_grads->dw2, n13, s);
+    if (shared) {
+      zero_fill(shared_grads->dw1, (long long)inter * d, s);
+      zero_fill(shared_grads->dw3, (long long)inter * d, s);
+      zero_fill(shared_grads->dw2, (long long)inter * d, s);
+    }
+    return launch_status();
+  }
+  g.MT = d / GB_T;
+  g.NT = inter / GB_T;
+  long long grid = tile_grid((long long)g.S * g.MT * g.NT, 0);
+  if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+  bwd_gemm_kernel<BK_DW2><<<(unsigned)grid, GB_THR, 0, s>>>(g);
+  g.MT = 2 * inter / GB_T;
+  g.NT = d / GB_T;
+  grid = tile_grid((long long)g.S * g.MT * g.NT, 0);
+  if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+  bwd_gemm_kernel<BK_DW13><<<(unsigned)grid, GB_THR, 0, s>>>(g);
+  return launch_status();
+}
+
+extern "C" moe_status moe_route_backward(const void* x, const uint8_t* x_scale, int dtype, int T, int d,
+                                         const float* w_gate, int E, int k, const int32_t* ids,
+                                         const float* weights, const float* d_weights,
+                                         const int32_t* offsets, const int32_t* perm,
+                                         const int32_t* row_of, const float* dx_rows, int has_shared,
+                                         float* dx, float* d_w_gate, float* d_bias, void* ws,
+                                         size_t ws_bytes, void* stream) {
+  if (!valid_dtype(dtype) || T < 0 || d < 1 || E < 1 || E > kMaxExperts || k < 1 || k > E ||
+      k > kMaxTopK)
+    return MOE_ERR_INVALID_ARG;
+  if (dtype == MOE_MXFP8 && (!x_scale || d % 32 != 0)) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_MXFP8 && x_scale) return MOE_ERR_INVALID_ARG;
+  if (d % 4 != 0) return MOE_ERR_UNSUPPORTED;
+  if (d_bias && !d_w_gate) return MOE_ERR_INVALID_ARG;
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  const BwdWs L = bwd_ws(T, d, E, k, 0);   // dl and wt come before every inter-sized buffer
+  if (ws_bytes < L.wt + (size_t)E * d * sizeof(float)) return MOE_ERR_WORKSPACE;
+  if ((long long)T * k > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  if (T == 0) {
+    if (d_w_gate) zero_fill(d_w_gate, (long long)d * E, s);
+    if (d_bias) zero_fill(d_bias, E, s);
+    return launch_status();
+  }
+  if (!x || !row_of || !dx_rows || !dx || !aligned(dx_rows, 16) || !aligned(dx, 16))
+    return MOE_ERR_INVALID_ARG;
+  if (d_w_gate && (!w_gate || !ids || !weights || !d_weights || !offsets || !perm))
+    return MOE_ERR_INVALID_ARG;
+  float* dl = nullptr;
+  float* wt = nullptr;
+  if (d_w_gate) {
+    dl = (float*)(w + L.dl);
+    wt = (float*)(w + L.wt);
+    route_bwd_dl_kernel<<<(T + 255) / 256, 256, 0, s>>>(weights, d_weights, T, k, dl);
+    gate_transpose_kernel<<<dim3((d + 63) / 64, (E + 63) / 64), 256, 0, s>>>(w_gate, d, E, wt);
+  }
+  const int q4 = d / 4, passes = (q4 + 1023) / 1024;
+  const int thr = ((q4 + passes - 1) / passes + 63) / 64 * 64;
+  route_bwd_dx_kernel<<<T, thr, 0, s>>>(dx_rows, row_of, T, d, k, has_shared ? 1 : 0, ids, dl, wt, E, dx);
+  if (d_w_gate)
+    route_bwd_wgate_kernel<<<dim3((d + 255) / 256, E), 256, 0, s>>>(x, x_scale, dtype, T, d, k, E, offsets,
+                                                                    perm, dl, d_w_gate, d_bias, (int*)w);
+  return launch_status();
+}

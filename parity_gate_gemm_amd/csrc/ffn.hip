@@ -22,7 +22,6 @@ constexpr int BM = kGemmBM;   // 128 rows per tile
 constexpr int BNR = 128;      // B rows (output features) staged per tile
 constexpr int BK = 64;        // reduction step
 constexpr int LDSS = BK + 8;  // LDS row stride in bf16 elements (144 B: conflict-free 16-B reads)
-constexpr int kXcds = 8;      // MI355X: 8 XCDs, workgroups dealt round-robin
 
 // Tuning knobs of the bf16 grouped GEMM (same results for every setting).
 #ifndef MOE_GEMM_DEPTH
@@ -68,30 +67,6 @@ constexpr bool kGemmNtB = MOE_GEMM_NT_B != 0; // nontemporal weight loads
 #define MOE_GEMM_NARROW_WAVES 1
 #endif
 
-// Tile of this workgroup.  Workgroup b runs on XCD b % 8.  With CHUNK == 0, XCD x takes
-// the x-th eighth of the tile list; otherwise the list is cut into chunks of CHUNK tiles
-// dealt round-robin to the XCDs.  Either way an XCD runs its tiles in list order, so
-// neighbouring tiles (which share weight columns or activation rows) share its L2.
-// The bf16 GEMMs keep contiguous eighths (each XCD streams one contiguous run of the
-// weight banks); the MXFP8 GEMMs deal chunks of 16 (measured: bf16 GEMM2 +12% with
-// chunks, MXFP8 GEMMs -3 to -4%).
-template <int CHUNK>
-__device__ __forceinline__ bool xcd_tile(int total, int& tile) {
-  const int xcd = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
-  if (CHUNK == 0) {
-    const int per = (total + kXcds - 1) / kXcds;
-    if (q >= per) return false;
-    tile = xcd * per + q;
-  } else {
-    tile = ((q / CHUNK) * kXcds + xcd) * CHUNK + q % CHUNK;
-  }
-  return tile < total;
-}
-// Workgroups to launch for at most `bound` tiles.
-static long long tile_grid(long long bound, int chunk) {
-  const long long g = chunk == 0 ? kXcds : (long long)kXcds * chunk;
-  return (bound + g - 1) / g * g;
-}
 #ifndef MOE_MX_XCD_CHUNK
 #define MOE_MX_XCD_CHUNK 16
 #endif
@@ -153,6 +128,7 @@ struct GemmArgs {
   const int* rowcount;
   int S;
   uint16_t* out;          // GEMM1: h [rows][I]; GEMM2: out [rows][d]
+  float* out_pre;         // MODE 2: pre-activations [rows][2I] (x W1, then x W3), fp32
   int* flag;
 };
 
@@ -160,6 +136,8 @@ __device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + expf(-a)
 
 // MODE 0: GEMM1 (W1 and W3, SwiGLU epilogue, 32 * WN output features per tile).
 // MODE 1: GEMM2 (W2, 64 * WN output features per tile).
+// MODE 2: GEMM1 without the epilogue: the fp32 pre-activations x W1 and x W3 (the
+//         backward pass recomputes them; same MFMA sequence as MODE 0).
 // 128 * WN threads = 2 x WN wavefronts; each wavefront owns a 64-row x 64-B-row part
 // of the 128 x (64 * WN) tile as 2 x 2 MFMA 32x32x16 blocks.  In GEMM1 the staged B
 // rows alternate 32-row blocks of W1 and W3 for the same features, so a wavefront's
@@ -169,6 +147,7 @@ template <int MODE, int DEPTH, bool NT_B, int WN>
 __global__ __launch_bounds__(128 * WN)
 __attribute__((amdgpu_waves_per_eu(WN >= 4 ? 4 : MOE_GEMM_NARROW_WAVES)))
 void grouped_gemm_bf16_kernel(GemmArgs g) {
+  constexpr bool G1 = MODE != 1;                // GEMM1 operands (gathered x; W1 / W3)
   constexpr int NTHR = 128 * WN;
   constexpr int BNW = 64 * WN;                  // staged B rows per tile
   constexpr int RSTEP = NTHR / 8;               // loader row stride
@@ -195,7 +174,7 @@ void grouped_gemm_bf16_kernel(GemmArgs g) {
   const int nt = rem / gm, mt = grp * kGroupM + rem % gm;
   const int row0 = g.rowstart[s] + mt * BM;
   const int mrows = min(BM, g.rowcount[s] - mt * BM);
-  const int n0 = nt * (MODE == 0 ? BNW / 2 : BNW);
+  const int n0 = nt * (G1 ? BNW / 2 : BNW);
   const bool is_shared = (s == g.E);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -212,7 +191,7 @@ void grouped_gemm_bf16_kernel(GemmArgs g) {
     const int r = lr + RSTEP * i;
     const long long j = (long long)row0 + (r < mrows ? r : 0);
     long long src;
-    if (MODE == 0) {
+    if (G1) {
       if (is_shared) {
         src = j - g.Tk;
       } else {
@@ -232,7 +211,7 @@ void grouped_gemm_bf16_kernel(GemmArgs g) {
     const int r = lr + RSTEP * i;
     long long brow;
     const uint16_t* bank;
-    if (MODE == 0) {
+    if (G1) {
       const int blk = r >> 5, within = r & 31;
       bank = (blk & 1) ? (is_shared ? g.sb1 : g.b1) : (is_shared ? g.sb0 : g.b0);
       brow = (long long)n0 + (blk >> 1) * 32 + within;
@@ -321,6 +300,10 @@ void grouped_gemm_bf16_kernel(GemmArgs g) {
         const float a = acc[mb][0][v], gg = acc[mb][1][v];
         const int col = n0 + wn * 32 + j;
         g.out[orow * g.N + col] = f32_to_bf16(silu_f32(a) * gg);   // 32 features per wave
+      } else if (MODE == 2) {
+        const int col = n0 + wn * 32 + j;
+        g.out_pre[orow * 2 * g.N + col] = acc[mb][0][v];
+        g.out_pre[orow * 2 * g.N + g.N + col] = acc[mb][1][v];
       } else {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
@@ -1590,6 +1573,47 @@ static moe_status run_down(int dtype, int T, int d, int E, int k, int inter,
     const long long n = p.rows * d;
     grouped_ffn_f32_kernel<1><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(g);
   }
+  return launch_status();
+}
+
+moe_status ffn_recompute_pre(const void* x, int T, int d, int E, int k, int inter,
+                             const moe_expert_bank* routed, const moe_expert_bank* shared,
+                             const int32_t* offsets, const int32_t* perm, int* seg, float* pre,
+                             int* flag, hipStream_t s) {
+  const int has_shared = shared ? 1 : 0;
+  const long long Tk = (long long)T * k;
+  int* mstart = seg;
+  int* rowstart = seg + (E + 2);
+  int* rowcount = rowstart + (E + 2);
+  seg_table_kernel<<<1, 1024, 0, s>>>(offsets, E, Tk, T, has_shared, BM, mstart, rowstart, rowcount,
+                                      flag);
+  GemmArgs g{};
+  g.a = (const uint16_t*)x;
+  g.perm = perm;
+  g.T = T;
+  g.k = k;
+  g.E = E;
+  g.Tk = Tk;
+  g.b0 = (const uint16_t*)routed->w1;
+  g.b1 = (const uint16_t*)routed->w3;
+  g.sb0 = shared ? (const uint16_t*)shared->w1 : nullptr;
+  g.sb1 = shared ? (const uint16_t*)shared->w3 : nullptr;
+  g.K = d;
+  g.N = inter;
+  g.mstart = mstart;
+  g.rowstart = rowstart;
+  g.rowcount = rowcount;
+  g.S = E + has_shared;
+  g.out = nullptr;
+  g.out_pre = pre;
+  g.flag = flag;
+  const int wn = bf16_wn(inter, 32, MOE_GEMM1_WN);
+  g.NT = inter / (32 * wn);
+  const long long mt_bound = (Tk + (long long)E * (BM - 1)) / BM + (has_shared ? (T + BM - 1) / BM : 0);
+  const long long grid = tile_grid(mt_bound * g.NT, 0);
+  if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+  if (grid == 0) return launch_status();
+  launch_bf16<2>(wn, (unsigned)grid, s, g);
   return launch_status();
 }
 

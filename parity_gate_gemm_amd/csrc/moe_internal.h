@@ -147,6 +147,28 @@ inline size_t workspace_bytes(int T, int d, int E, int k, int inter, int dtype) 
   return m > c ? m : c;
 }
 
+// Backward pass (bf16 layers): segment table, recomputed pre-activations a | g
+// [rows][2 inter] fp32, their gradients da | dg [rows][2 inter] bf16, h [rows][inter]
+// bf16, the routing-weight gradients through the gate dl [T][k] fp32, the transposed
+// gate [E][d] fp32.
+struct BwdWs {
+  size_t seg, pre, dadg, h, dl, wt, bytes;
+  long long rows;
+};
+inline BwdWs bwd_ws(int T, int d, int E, int k, int inter) {
+  BwdWs w;
+  w.rows = (long long)T * k + T;
+  size_t o = kHeaderBytes;
+  w.seg = o;  o = align_up(o + (size_t)(3 * (E + 2)) * sizeof(int), 256);
+  w.dl = o;   o = align_up(o + (size_t)T * k * sizeof(float), 256);
+  w.wt = o;   o = align_up(o + (size_t)E * d * sizeof(float), 256);
+  w.pre = o;  o = align_up(o + (size_t)w.rows * 2 * inter * sizeof(float), 256);
+  w.dadg = o; o = align_up(o + (size_t)w.rows * 2 * inter * sizeof(uint16_t), 256);
+  w.h = o;    o = align_up(o + (size_t)w.rows * inter * sizeof(uint16_t), 256);
+  w.bytes = o;
+  return w;
+}
+
 inline bool valid_dtype(int dt) { return dt == MOE_F32 || dt == MOE_BF16 || dt == MOE_MXFP8; }
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -198,6 +220,44 @@ __device__ __forceinline__ double load_act_f64(const void* x, const uint8_t* xs,
   if (dtype == MOE_BF16) return (double)bf16_to_f32(((const uint16_t*)x)[idx]);
   return e4m3_to_f64(((const uint8_t*)x)[idx]) * e8m0_to_f64(xs[row * (size_t)(d / 32) + i / 32]);
 }
+
+// ---------------------------------------------------------------------------
+// Grouped-GEMM tile order across the XCDs
+// ---------------------------------------------------------------------------
+constexpr int kXcds = 8;      // MI355X: 8 XCDs, workgroups dealt round-robin
+
+// Tile of this workgroup.  Workgroup b runs on XCD b % 8.  With CHUNK == 0, XCD x takes
+// the x-th eighth of the tile list; otherwise the list is cut into chunks of CHUNK tiles
+// dealt round-robin to the XCDs.  Either way an XCD runs its tiles in list order, so
+// neighbouring tiles (which share weight columns or activation rows) share its L2.
+// The bf16 GEMMs keep contiguous eighths (each XCD streams one contiguous run of the
+// weight banks); the MXFP8 GEMMs deal chunks of 16 (measured: bf16 GEMM2 +12% with
+// chunks, MXFP8 GEMMs -3 to -4%).
+template <int CHUNK>
+__device__ __forceinline__ bool xcd_tile(int total, int& tile) {
+  const int xcd = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
+  if (CHUNK == 0) {
+    const int per = (total + kXcds - 1) / kXcds;
+    if (q >= per) return false;
+    tile = xcd * per + q;
+  } else {
+    tile = ((q / CHUNK) * kXcds + xcd) * CHUNK + q % CHUNK;
+  }
+  return tile < total;
+}
+// Workgroups to launch for at most `bound` tiles.
+inline long long tile_grid(long long bound, int chunk) {
+  const long long g = chunk == 0 ? kXcds : (long long)kXcds * chunk;
+  return (bound + g - 1) / g * g;
+}
+// Backward-pass support from the forward FFN (ffn.hip): the segment table for 128-row
+// tiles into seg (mstart [E + 2], rowstart [E + 2], rowcount [E + 2]) and the GEMM1
+// pre-activations of every dispatched row, pre [rows][2 inter] fp32 (x W1, then x W3),
+// with the forward's MFMA sequence (bf16 only).
+moe_status ffn_recompute_pre(const void* x, int T, int d, int E, int k, int inter,
+                             const moe_expert_bank* routed, const moe_expert_bank* shared,
+                             const int32_t* offsets, const int32_t* perm, int* seg, float* pre,
+                             int* flag, hipStream_t s);
 
 // Screened gate (screen.hip).  screen_route_select leaves ids for every token and
 // tok_flag 1 for the tokens the exact fallback must decide; screen_route_weights then

@@ -99,5 +99,28 @@ def test_dispatch_ffn_combine_host_validation(L):
     assert L.moe_combine(P, 1, P, P, 4, 128, 0, 0, P, None) == 1
     assert L.moe_combine(None, 1, P, P, 4, 128, 2, 0, P, None) == 1
     assert L.moe_combine(P, 1, P, P, 0, 128, 2, 0, P, None) == 0
+    # backward calls
+    G = pg._GradBank(0x10000, 0x10000, 0x10000)
+    GB = ctypes.byref(G)
+    assert L.moe_combine_backward(P, 1, P, P, P, 4, 100, 2, 0, P, P, None) == 2           # d % 8
+    assert L.moe_combine_backward(None, 1, P, P, P, 4, 128, 2, 0, P, P, None) == 1
+    assert L.moe_combine_backward(P, 1, P, P, P, 0, 128, 2, 0, P, P, None) == 0           # T = 0
+    assert L.moe_expert_ffn_backward(P, None, 0, 4, 128, 16, 2, 128, B, None, P, P, P, P, GB, None,
+                                     P, 1 << 30, None) == 2                                # fp32
+    assert L.moe_expert_ffn_backward(P, None, 1, 4, 128, 16, 2, 64, B, None, P, P, P, P, GB, None,
+                                     P, 1 << 30, None) == 2                                # I % 128
+    assert L.moe_expert_ffn_backward(P, None, 1, 4, 128, 16, 2, 128, B, B, P, P, P, P, GB, None,
+                                     P, 1 << 30, None) == 1                                # shared w/o grads
+    assert L.moe_expert_ffn_backward(P, None, 1, 4, 128, 16, 2, 128, B, None, P, P, P, P, GB, None,
+                                     P, 64, None) == 3                                     # workspace
+    assert L.moe_route_backward(P, None, 1, 4, 128, P, 16, 2, P, P, P, P, P, P, P, 0, P, None, P,
+                                P, 1 << 30, None) == 1                                     # bias w/o gate
+    assert L.moe_route_backward(P, None, 1, 4, 126, P, 16, 2, P, P, P, P, P, P, P, 0, P, P, None,
+                                P, 1 << 30, None) == 2                                     # d % 4
+    assert L.moe_route_backward(P, None, 1, 4, 128, P, 16, 2, P, P, P, P, P, P, P, 0, P, P, None,
+                                P, 64, None) == 3                                          # workspace
+    n = ctypes.c_size_t()
+    assert L.moe_backward_workspace_size(4096, 7168, 384, 8, 2048, 1, ctypes.byref(n)) == 0
+    assert n.value >= pg.moe_workspace_size(4096, 7168, 384, 8, 2048, 1)
     assert L.moe_check(None, 0, None) == 1
     assert L.moe_workspace_init(None, 0, None) == 1

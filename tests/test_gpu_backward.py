@@ -1,0 +1,126 @@
+"""GPU parity of the layer's backward pass (bf16 layers) against the oracle's chain
+rule in fp64.
+
+Every gradient (dx, the routing-weight gradients, the gate's, every expert's dW1 / dW3
+/ dW2 and the shared expert's) is compared as a whole tensor, normwise (max |err| /
+max |ref|), to 2e-2: the bf16 roundings of h, of the expert outputs and of the
+gradients fed to the bf16 GEMMs are inside that bar, as for the forward.  Shapes
+span several 128-row tiles, ragged segments, experts with no rows (their gradients
+must be exactly zero), k = 1 and the three routing modes (learned, replay with the
+gate's weights, replay with caller weights: no gate gradient).  The backward is
+bitwise reproducible run to run, and a token's dx does not depend on the batch.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity_gate_gemm_amd as pg
+import synth
+from _gpu_common import LazyExperts, host, say, shared_of, to_device, values
+
+pytestmark = pytest.mark.gpu
+
+BAR = 2e-2
+
+
+def _nerr(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(got - ref)) / (den if den > 0 else 1.0))
+
+
+def _dy(T, d, seed):
+    g = torch.Generator().manual_seed(seed)
+    return synth.bf16_round(torch.randn(T, d, generator=g)).to(torch.bfloat16).cuda()
+
+
+def _run(inp, k, dy, replay=False, ws=None):
+    x = inp["x"]
+    T, d = x.shape
+    E, inter = inp["w_gate"].shape[1], inp["w1"].shape[1]
+    ws = ws or pg.BackwardWorkspace(T, d, E, k, inter, pg.MOE_BF16)
+    fwd = pg.layer_forward(inp, k, ws=ws, replay=replay)
+    bwd = pg.layer_backward(inp, k, fwd, dy, ws, replay=replay)
+    return fwd, bwd
+
+
+def _oracle(inp, k, dy, replay=False):
+    kw = {}
+    if replay:
+        kw["ids_in"] = inp["ids_in"].cpu().numpy()
+        if inp.get("weights_in") is not None:
+            kw["weights_in"] = host(inp["weights_in"])
+    return oracle.layer_backward(values(inp["x"]), host(inp["w_gate"]), host(inp.get("bias")),
+                                 LazyExperts(inp), shared_of(inp), k, host(dy), **kw)
+
+
+def _compare(bwd, ref, E, has_shared, gate):
+    errs = {"dx": _nerr(host(bwd["dx"]), ref["dx"]),
+            "d_weights": _nerr(host(bwd["d_weights"]), ref["d_weights"])}
+    for n in ("w1", "w3", "w2"):
+        got = host(bwd["grads"][n])
+        errs["d" + n] = _nerr(got, ref["d" + n])
+        for e in range(E):          # experts without rows: exactly zero
+            if not ref["d" + n][e].any():
+                assert not got[e].any(), (n, e)
+    if has_shared:
+        for i, n in enumerate(("w1", "w3", "w2")):
+            errs["shared_d" + n] = _nerr(host(bwd["shared_grads"][n]), ref["d_shared"][i])
+    if gate:
+        errs["d_w_gate"] = _nerr(host(bwd["d_w_gate"]), ref["d_w_gate"])
+        if ref["d_bias"] is not None:
+            errs["d_bias"] = _nerr(host(bwd["d_bias"]), ref["d_bias"])
+    else:
+        assert bwd["d_w_gate"] is None
+    say("  " + ", ".join(f"{a} {b:.2e}" for a, b in errs.items()))
+    bad = {a: b for a, b in errs.items() if not b <= BAR}
+    assert not bad, bad
+
+
+# (name, T, d, I, E, k, shared, bias, routing, seed)
+CASES = [
+    ("small_learned", 40, 128, 128, 8, 2, True, True, "learned", 1),
+    ("ragged_multi_tile", 300, 256, 256, 6, 3, True, False, "learned", 2),
+    ("empty_experts", 20, 128, 128, 64, 2, False, True, "learned", 3),
+    ("k1_no_shared", 150, 256, 128, 12, 1, False, True, "learned", 4),
+    ("replay_gate_weights", 100, 128, 256, 8, 3, True, True, "replay_gate", 5),
+    ("replay_caller_weights", 100, 128, 128, 8, 3, True, True, "replay", 6),
+]
+
+
+@pytest.mark.parametrize("name,T,d,I,E,k,shared,bias,routing,seed", CASES, ids=[c[0] for c in CASES])
+def test_backward_small_parity(name, T, d, I, E, k, shared, bias, routing, seed):
+    wl = synth.Workload(name, T=T, d=d, inter=I, E=E, k=k, shared=shared, bias=bias, dtype="bf16",
+                        routing="replay" if routing.startswith("replay") else "learned", seed=seed)
+    inp = to_device(synth.make_layer_inputs(wl, device="cpu"))
+    if routing == "replay_gate":
+        inp["weights_in"] = None
+    dy = _dy(T, d, seed)
+    say(f"case backward {name}")
+    fwd, bwd = _run(inp, k, dy, replay=routing != "learned")
+    ref = _oracle(inp, k, dy, replay=routing != "learned")
+    assert np.array_equal(fwd["ids"].cpu().numpy(), ref["fwd"]["ids"])
+    _compare(bwd, ref, E, shared, gate=routing != "replay")
+
+
+def test_backward_bitwise_repeatable_and_token_local_dx():
+    wl = synth.Workload("rep", T=260, d=256, inter=128, E=8, k=2, shared=True, bias=True, dtype="bf16",
+                        seed=7)
+    inp = to_device(synth.make_layer_inputs(wl, device="cpu"))
+    dy = _dy(wl.T, wl.d, 7)
+    ws = pg.BackwardWorkspace(wl.T, wl.d, wl.E, wl.k, wl.inter, pg.MOE_BF16)
+    say("case backward determinism")
+    _, a = _run(inp, wl.k, dy, ws=ws)
+    _, b = _run(inp, wl.k, dy, ws=ws)
+    for n in ("dx", "d_weights", "d_w_gate", "d_bias"):
+        assert torch.equal(a[n], b[n]), n
+    for n in ("w1", "w3", "w2"):
+        assert torch.equal(a["grads"][n], b["grads"][n]) and torch.equal(a["shared_grads"][n],
+                                                                      b["shared_grads"][n])
+    # one token alone: its dx equals its row in the batch, bit for bit
+    for t in (0, 137, wl.T - 1):
+        one = dict(inp, x=inp["x"][t:t + 1].contiguous())
+        _, c = _run(one, wl.k, dy[t:t + 1].contiguous())
+        assert torch.equal(c["dx"][0], a["dx"][t]), t

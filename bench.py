@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--replay-filter", type=float, default=None, metavar="LOG_TAU",
                     help="replay workloads: route with the plausibility filter at ln tau = LOG_TAU "
                          "(the replayed ids are filtered and the weights come from the gate)")
+    ap.add_argument("--backward", action="store_true",
+                    help="bf16 workloads: a step is the forward and the backward pass of the layer "
+                         "(dL/dy drawn once, fp32 weight and gate gradients)")
     ap.add_argument("--cpu-sample", type=int, default=32,
                     help="tokens of the same batch the CPU oracle is timed on (0: skip)")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
@@ -91,7 +94,11 @@ def main():
         print("--replay-filter needs a replay workload (replay_zipf_t4096)", file=sys.stderr)
         sys.exit(2)
     has_shared = inp["shared"] is not None
-    ws = pg.Workspace(T, d, E, k, I, dt)
+    bwd = args.backward
+    if bwd and wl.dtype != "bf16":
+        print("--backward runs the bf16 workloads only", file=sys.stderr)
+        sys.exit(2)
+    ws = pg.BackwardWorkspace(T, d, E, k, I, dt) if bwd else pg.Workspace(T, d, E, k, I, dt)
     x, wg, bias = inp["x"], inp["w_gate"], inp["bias"]
     routed = {n: inp[n] for n in ("w1", "w3", "w2", "w1_scale", "w3_scale", "w2_scale")}
     shared = inp["shared"]
@@ -104,6 +111,18 @@ def main():
     row_of = torch.empty(T * k, dtype=torch.int32, device=dev)
     out = torch.empty(rows, d, dtype=odt, device=dev)
     y = torch.empty(T, d, dtype=odt, device=dev)
+    if bwd:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(wl.seed + 100)
+        dy = torch.randn(T, d, generator=gen, device=dev).to(odt)
+        d_out = torch.empty(rows, d, dtype=odt, device=dev)
+        d_weights = torch.empty(T, k, dtype=torch.float32, device=dev)
+        dx_rows = torch.empty(rows, d, dtype=torch.float32, device=dev)
+        grads = {n: torch.empty(routed[n].shape, dtype=torch.float32, device=dev) for n in ("w1", "w3", "w2")}
+        sgrads = ({n: torch.empty(shared[n].shape, dtype=torch.float32, device=dev) for n in ("w1", "w3", "w2")}
+                  if has_shared else None)
+        dx = torch.empty(T, d, dtype=torch.float32, device=dev)
+        gate_grad = not (replay and filt is None and inp["weights_in"] is not None)
 
     def step(ev=None):
         if ev is not None:
@@ -130,6 +149,22 @@ def main():
         pg.moe_combine(out, row_of, weights, T, has_shared, dt, y=y)
         if ev is not None:
             ev[5].record()
+        if not bwd:
+            return
+        pg.moe_combine_backward(dy, out, row_of, weights, T, has_shared, dt, d_out=d_out, d_weights=d_weights)
+        if ev is not None:
+            ev[6].record()
+        pg.moe_expert_ffn_backward_data(x, routed, shared, offsets, perm, k, d_out, ws, dx_rows=dx_rows)
+        if ev is not None:
+            ev[7].record()
+        pg.moe_expert_ffn_backward_weights(x, routed, shared, perm, k, d_out, ws, grads=grads,
+                                           shared_grads=sgrads)
+        if ev is not None:
+            ev[8].record()
+        pg.moe_route_backward(x, wg, ids, weights, d_weights, offsets, perm, row_of, dx_rows, has_shared, ws,
+                              gate_grad=gate_grad, bias_grad=bias is not None, dx=dx)
+        if ev is not None:
+            ev[9].record()
 
     for _ in range(args.warmup):
         step()
@@ -137,7 +172,7 @@ def main():
     if st != 0:
         raise pg.MoeError(st, "warmup")
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(10 if bwd else 6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -149,6 +184,8 @@ def main():
         raise pg.MoeError(st, "timed steps")
 
     names = ["route", "dispatch", "ffn_gate_up", "ffn_down", "combine"]
+    if bwd:
+        names += ["combine_backward", "ffn_backward_data", "ffn_backward_weights", "route_backward"]
     stage_ms = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1])
                                   for i in range(args.steps)])) for j, n in enumerate(names)}
     ms_per_step = wall * 1e3 / args.steps
@@ -184,6 +221,20 @@ def main():
         "combine": {"ms": stage_ms["combine"], "alg_bytes": bytes_combine,
                     "GB_s": gbs(bytes_combine, stage_ms["combine"])},
     }
+    if bwd:
+        n_all = E + (1 if has_shared else 0)      # the weights half writes every expert's gradients
+        bytes_cbwd = T * d * ob + T * k * d * ob * 2 + (T * d * ob if has_shared else 0) + T * k * 12
+        bytes_data = (n_mats * 3 * mat * 2 + T * d * eb + rows * 2 * I * 4 * 2 + rows * d * ob
+                      + rows * 2 * I * 2 * 2 + rows * I * 2 + rows * d * 4)
+        bytes_wts = n_all * 3 * I * d * 4 + rows * d * ob + rows * I * 2 + rows * 2 * I * 2 + rows * d * eb
+        bytes_rbwd = rows * d * 4 + T * d * 4 + 2 * E * d * 4 + d * E * 4 + T * k * d * eb + T * k * 16
+        flops_data = 2.0 * rows * d * I * 5
+        flops_wts = 2.0 * rows * d * I * 3
+        for n, b, f in (("combine_backward", bytes_cbwd, None), ("ffn_backward_data", bytes_data, flops_data),
+                        ("ffn_backward_weights", bytes_wts, flops_wts), ("route_backward", bytes_rbwd, None)):
+            stages[n] = {"ms": stage_ms[n], "alg_bytes": b, "GB_s": gbs(b, stage_ms[n])}
+            if f is not None:
+                stages[n]["TFLOP_s"] = f / (stage_ms[n] * 1e-3) / 1e12
     dom = max(("ffn_gate_up", "ffn_down"), key=lambda n: stage_ms[n])
     # the MXFP8 GEMMs run on the LDS-ring kernel where d and I are multiples of 512
     mx_ring = d % 512 == 0 and I % 512 == 0
@@ -204,8 +255,19 @@ def main():
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
 
+    if bwd:
+        # the step's largest stage is one of the two backward halves; both stream HBM
+        bdom = max(("ffn_backward_data", "ffn_backward_weights"), key=lambda n: stage_ms[n])
+        dom_kernel = {"ffn_backward_data": "bwd_gemm_kernel<0>/<1> + recompute (dx half: "
+                                           "a, g; dh with SwiGLU backward; dx rows)",
+                      "ffn_backward_weights": "bwd_gemm_kernel<2>, <3> (dW2; dW1 and dW3, fp32 "
+                                              "gradients of every expert)"}[bdom]
+        achieved = stages[bdom]["GB_s"]
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+        dom = bdom
     result = {
-        "metric": METRIC,
+        "metric": METRIC if not bwd else "MoE-layer forward+backward tokens/s, 384-expert top-8 d=7168 bf16",
         "value": T / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -232,10 +294,15 @@ def main():
     }
 
     result["roofline"]["traffic"] = measured_traffic(wl.name) if dom == "ffn_gate_up" else None
+    if bwd:
+        result["config"]["pass"] = "forward+backward"
     if wl.dtype != "bf16":
         result["vs_metric_config"] = "this workload is not the metric's configuration (bf16 T=4096)"
+    if bwd:   # the oracle's backward keeps every touched expert's fp64 gradients: few tokens
+        args.cpu_sample = min(args.cpu_sample, 4)
     if args.cpu_sample > 0:
-        result["cpu_baseline"] = cpu_baseline(inp, wl, ids, args.cpu_sample, filt)
+        result["cpu_baseline"] = cpu_baseline(inp, wl, ids, args.cpu_sample, filt,
+                                              dy if bwd else None)
     print(json.dumps(result))
 
 
@@ -281,7 +348,7 @@ def _stored_values(t, scale=None):
     return oracle.mx_dequant(t.numpy(), scale.numpy())
 
 
-def cpu_baseline(inp, wl, ids, n_tok, log_tau=None):
+def cpu_baseline(inp, wl, ids, n_tok, log_tau=None, dy=None):
     """The CPU oracle (as it is) on the first n_tok tokens of the same batch; with
     log_tau, the filtered replay routing followed by the layer on the filtered ids."""
     import numpy as np
@@ -308,13 +375,18 @@ def cpu_baseline(inp, wl, ids, n_tok, log_tau=None):
     if log_tau is not None:
         fid, fw, _, _ = oracle.route_replay_filtered(x, wg, bias, kw["ids_in"], log_tau)
         kw = {"ids_in": fid, "weights_in": fw}
-    oracle.layer(x, wg, bias, experts, shared, wl.k, **kw)
+    if dy is None:
+        oracle.layer(x, wg, bias, experts, shared, wl.k, **kw)
+    else:
+        oracle.layer_backward(x, wg, bias, experts, shared, wl.k, dy[rows].float().cpu().numpy(),
+                              dense=False, **kw)
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {"value": len(rows) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {len(rows)} tokens of the {wl.name} batch (exact fsum gate logits over "
                       f"{wl.E} experts{', plausibility filter' if log_tau is not None else ''}, fp64 "
-                      f"SwiGLU for each chosen expert), {dt:.1f} s",
+                      f"SwiGLU for each chosen expert{', then its fp64 backward' if dy is not None else ''}), "
+                      f"{dt:.1f} s",
             "host_cpus": len(os.sched_getaffinity(0))}
 
 

@@ -284,6 +284,23 @@ moe_status moe_expert_ffn_backward(const void* x, const uint8_t* x_scale, int dt
                                    const moe_grad_bank* shared_grads, void* ws, size_t ws_bytes,
                                    void* stream);
 
+/* The two halves of moe_expert_ffn_backward, for callers that overlap or time them
+ * apart (same arguments, same results).  The data half computes dx_rows and leaves
+ * da | dg, h and the segment table in the workspace; the weights half then writes
+ * the weight gradients from them (call it next on the same workspace and stream). */
+moe_status moe_expert_ffn_backward_data(const void* x, const uint8_t* x_scale, int dtype, int T,
+                                        int d, int E, int k, int inter,
+                                        const moe_expert_bank* routed, const moe_expert_bank* shared,
+                                        const int32_t* offsets, const int32_t* perm,
+                                        const void* d_out, float* dx_rows, void* ws, size_t ws_bytes,
+                                        void* stream);
+moe_status moe_expert_ffn_backward_weights(const void* x, int dtype, int T, int d, int E, int k,
+                                           int inter, const moe_expert_bank* routed,
+                                           const moe_expert_bank* shared, const int32_t* perm,
+                                           const void* d_out, const moe_grad_bank* routed_grads,
+                                           const moe_grad_bank* shared_grads, void* ws,
+                                           size_t ws_bytes, void* stream);
+
 /* Backward of the routing and of the token gather.
  *   dx        out fp32 [T][d]: sum_r dx_rows[row_of[t,r]] (r ascending), plus
  *             dx_rows[T*k + t] when has_shared, plus the gate term below.

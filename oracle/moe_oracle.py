@@ -376,7 +376,8 @@ def softmax_pick_grad(weights, d_weights):
     return w * (dw - (w * dw).sum(axis=1, keepdims=True))
 
 
-def layer_backward(x, w_gate, bias, experts, shared, k: int, dy, ids_in=None, weights_in=None):
+def layer_backward(x, w_gate, bias, experts, shared, k: int, dy, ids_in=None, weights_in=None,
+                   dense: bool = True):
     """Gradients of L = <dy, y> through one MoE layer forward (``layer``).
 
     The expert choice is piecewise constant in x, so no gradient flows through the
@@ -386,7 +387,8 @@ def layer_backward(x, w_gate, bias, experts, shared, k: int, dy, ids_in=None, we
     Composer 2 Technical Report, §6.2, paragraph on inference and weight sync).
     Returns a dict: dx [T, d], d_weights [T, k], d_w_gate [d, E], d_bias [E] (or
     None), dw1 / dw3 [E, I, d], dw2 [E, d, I], d_shared (dw1, dw3, dw2) or None, and
-    the forward dict under "fwd".
+    the forward dict under "fwd".  With dense=False the expert gradients are dicts
+    holding only the experts that got rows (the others are zero).
     """
     xf = f64(x)
     dyf = f64(dy)
@@ -404,10 +406,13 @@ def layer_backward(x, w_gate, bias, experts, shared, k: int, dy, ids_in=None, we
             d_weights[t, r] = float(dyf[t] @ rows[j])
             d_rows[j] = w[t, r] * dyf[t]
     dx = np.zeros((T, d))
-    I = f64(experts[0][0]).shape[0]
-    dw1 = np.zeros((E, I, d))
-    dw3 = np.zeros((E, I, d))
-    dw2 = np.zeros((E, d, I))
+    if dense:
+        I = f64(experts[0][0]).shape[0]
+        dw1 = np.zeros((E, I, d))
+        dw3 = np.zeros((E, I, d))
+        dw2 = np.zeros((E, d, I))
+    else:
+        dw1, dw3, dw2 = {}, {}, {}
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi == lo:

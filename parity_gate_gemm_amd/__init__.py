@@ -18,7 +18,8 @@ __all__ = [
     "moe_route_replay_filtered",
     "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_gate_up", "moe_expert_ffn_down", "moe_combine", "moe_check", "moe_status_string",
     "layer_forward", "moe_backward_workspace_size", "moe_combine_backward", "moe_expert_ffn_backward",
-    "moe_route_backward", "layer_backward",
+    "moe_route_backward", "layer_backward", "moe_expert_ffn_backward_data",
+    "moe_expert_ffn_backward_weights",
 ]
 
 MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
@@ -62,6 +63,11 @@ def lib():
             "moe_expert_ffn_backward": [P, P, I, I, I, I, I, I, ctypes.POINTER(_Bank),
                                         ctypes.POINTER(_Bank), P, P, P, P, ctypes.POINTER(_GradBank),
                                         ctypes.POINTER(_GradBank), P, SZ, P],
+            "moe_expert_ffn_backward_data": [P, P, I, I, I, I, I, I, ctypes.POINTER(_Bank),
+                                             ctypes.POINTER(_Bank), P, P, P, P, P, SZ, P],
+            "moe_expert_ffn_backward_weights": [P, I, I, I, I, I, I, ctypes.POINTER(_Bank),
+                                                ctypes.POINTER(_Bank), P, P, ctypes.POINTER(_GradBank),
+                                                ctypes.POINTER(_GradBank), P, SZ, P],
             "moe_route_backward": [P, P, I, I, I, P, I, I, P, P, P, P, P, P, P, I, P, P, P, P, SZ, P],
             "moe_route_replay_filtered": [P, P, I, I, I, P, P, I, I, P, ctypes.c_double, P, P, P, SZ,
                                           P],
@@ -356,6 +362,39 @@ def moe_expert_ffn_backward(x, routed: dict, shared, offsets, perm, k, d_out, ws
                                       ctypes.byref(rg), ctypes.byref(sg) if sg is not None else None,
                                       ws.ptr, ws.nbytes, _stream(x.device)), "moe_expert_ffn_backward")
     return dx_rows, grads, shared_grads
+
+
+def moe_expert_ffn_backward_data(x, routed: dict, shared, offsets, perm, k, d_out, ws: Workspace,
+                                 x_scale=None, dx_rows=None):
+    _check_dev(x, x_scale, offsets, perm, d_out)
+    T, d = x.shape
+    E, inter = routed["w1"].shape[0], routed["w1"].shape[1]
+    rows = T * k + (T if shared is not None else 0)
+    dx_rows = torch.empty(rows, d, dtype=torch.float32, device=x.device) if dx_rows is None else dx_rows
+    rb, sb = _bank(routed), _bank(shared)
+    _ok(lib().moe_expert_ffn_backward_data(_ptr(x), _ptr(x_scale), _dtype_of(x), T, d, E, k, inter,
+                                           ctypes.byref(rb), ctypes.byref(sb) if sb is not None else None,
+                                           _ptr(offsets), _ptr(perm), _ptr(d_out), _ptr(dx_rows), ws.ptr,
+                                           ws.nbytes, _stream(x.device)), "moe_expert_ffn_backward_data")
+    return dx_rows
+
+
+def moe_expert_ffn_backward_weights(x, routed: dict, shared, perm, k, d_out, ws: Workspace, grads=None,
+                                    shared_grads=None):
+    _check_dev(x, perm, d_out)
+    T, d = x.shape
+    E, inter = routed["w1"].shape[0], routed["w1"].shape[1]
+    grads = _grad_like(routed) if grads is None else grads
+    if shared is not None and shared_grads is None:
+        shared_grads = _grad_like(shared)
+    rb, sb = _bank(routed), _bank(shared)
+    rg, sg = _grads(grads), _grads(shared_grads)
+    _ok(lib().moe_expert_ffn_backward_weights(_ptr(x), _dtype_of(x), T, d, E, k, inter, ctypes.byref(rb),
+                                              ctypes.byref(sb) if sb is not None else None, _ptr(perm),
+                                              _ptr(d_out), ctypes.byref(rg),
+                                              ctypes.byref(sg) if sg is not None else None, ws.ptr,
+                                              ws.nbytes, _stream(x.device)), "moe_expert_ffn_backward_weights")
+    return grads, shared_grads
 
 
 def moe_route_backward(x, w_gate, ids, weights, d_weights, offsets, perm, row_of, dx_rows, has_shared,

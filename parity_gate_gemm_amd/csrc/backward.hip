@@ -512,14 +512,13 @@ static bool grads_ok(const moe_grad_bank* g) {
          aligned(g->dw2, 16);
 }
 
-extern "C" moe_status moe_expert_ffn_backward(const void* x, const uint8_t* x_scale, int dtype, int T,
-                                              int d, int E, int k, int inter,
-                                              const moe_expert_bank* routed,
-                                              const moe_expert_bank* shared, const int32_t* offsets,
-                                              const int32_t* perm, const void* d_out, float* dx_rows,
-                                              const moe_grad_bank* routed_grads,
-                                              const moe_grad_bank* shared_grads, void* ws,
-                                              size_t ws_bytes, void* stream) {
+// Argument checks and kernel arguments shared by the three expert-backward entry points.
+static moe_status bwd_setup(const void* x, const uint8_t* x_scale, int dtype, int T, int d, int E, int k,
+                            int inter, const moe_expert_bank* routed, const moe_expert_bank* shared,
+                            const int32_t* offsets, const int32_t* perm, const void* d_out,
+                            float* dx_rows, const moe_grad_bank* routed_grads,
+                            const moe_grad_bank* shared_grads, void* ws, size_t ws_bytes, bool data,
+                            bool weights, BwdGemm& g) {
   if (!valid_dtype(dtype) || T < 0 || d < 1 || E < 1 || E > kMaxExperts || k < 1 || k > E ||
       k > kMaxTopK || inter < 1)
     return MOE_ERR_INVALID_ARG;
@@ -527,25 +526,27 @@ extern "C" moe_status moe_expert_ffn_backward(const void* x, const uint8_t* x_sc
   if (x_scale) return MOE_ERR_INVALID_ARG;
   if (d % 128 != 0 || inter % 128 != 0) return MOE_ERR_UNSUPPORTED;
   if (!ws || !routed || !routed->w1 || !routed->w3 || !routed->w2 || routed->w1_scale ||
-      routed->w3_scale || routed->w2_scale || !grads_ok(routed_grads))
+      routed->w3_scale || routed->w2_scale)
     return MOE_ERR_INVALID_ARG;
-  if ((shared != nullptr) != (shared_grads != nullptr)) return MOE_ERR_INVALID_ARG;
-  if (shared && (!shared->w1 || !shared->w3 || !shared->w2 || !grads_ok(shared_grads)))
-    return MOE_ERR_INVALID_ARG;
+  if (shared && (!shared->w1 || !shared->w3 || !shared->w2)) return MOE_ERR_INVALID_ARG;
+  if (weights) {
+    if (!grads_ok(routed_grads)) return MOE_ERR_INVALID_ARG;
+    if ((shared != nullptr) != (shared_grads != nullptr)) return MOE_ERR_INVALID_ARG;
+    if (shared && !grads_ok(shared_grads)) return MOE_ERR_INVALID_ARG;
+  }
   if ((long long)T * k > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
   const BwdWs L = bwd_ws(T, d, E, k, inter);
   if (ws_bytes < L.bytes) return MOE_ERR_WORKSPACE;
-  if (T > 0 && (!x || !offsets || !perm || !d_out || !dx_rows)) return MOE_ERR_INVALID_ARG;
-  if (T > 0 && (!aligned(x, 16) || !aligned(d_out, 16) || !aligned(dx_rows, 16)))
+  if (T > 0 && (!x || !perm || !aligned(x, 16) || (data && !offsets))) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && data && (!d_out || !dx_rows || !aligned(d_out, 16) || !aligned(dx_rows, 16)))
     return MOE_ERR_INVALID_ARG;
   const moe_expert_bank* banks[2] = {routed, shared};
   for (const moe_expert_bank* b : banks)
     if (b && (!aligned(b->w1, 16) || !aligned(b->w3, 16) || !aligned(b->w2, 16)))
       return MOE_ERR_INVALID_ARG;
-  hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
   const int has_shared = shared ? 1 : 0;
-  BwdGemm g{};
+  g = BwdGemm{};
   g.x = (const uint16_t*)x;
   g.perm = perm;
   g.T = T;
@@ -565,56 +566,115 @@ extern "C" moe_status moe_expert_ffn_backward(const void* x, const uint8_t* x_sc
   g.dadg = (uint16_t*)(w + L.dadg);
   g.h = (uint16_t*)(w + L.h);
   g.dx_rows = dx_rows;
-  g.dw1 = routed_grads->dw1;
-  g.dw3 = routed_grads->dw3;
-  g.dw2 = routed_grads->dw2;
-  g.sdw1 = shared ? shared_grads->dw1 : nullptr;
-  g.sdw3 = shared ? shared_grads->dw3 : nullptr;
-  g.sdw2 = shared ? shared_grads->dw2 : nullptr;
+  if (weights) {
+    g.dw1 = routed_grads->dw1;
+    g.dw3 = routed_grads->dw3;
+    g.dw2 = routed_grads->dw2;
+    g.sdw1 = shared ? shared_grads->dw1 : nullptr;
+    g.sdw3 = shared ? shared_grads->dw3 : nullptr;
+    g.sdw2 = shared ? shared_grads->dw2 : nullptr;
+  }
   int* seg = (int*)(w + L.seg);
   g.mstart = seg;
   g.rowstart = seg + (E + 2);
   g.rowcount = seg + 2 * (E + 2);
   g.S = E + has_shared;
   g.flag = (int*)w;
+  return MOE_OK;
+}
+
+// Data half: recomputed pre-activations, dh with the SwiGLU backward, dx_rows.
+static moe_status bwd_data(BwdGemm& g, const moe_expert_bank* routed, const moe_expert_bank* shared,
+                           const int32_t* offsets, hipStream_t s) {
+  if (g.T == 0) return MOE_OK;
   moe_status st;
-  if (T > 0) {
-    // recomputed pre-activations (and the segment table the kernels below read)
-    if ((st = ffn_recompute_pre(x, T, d, E, k, inter, routed, shared, offsets, perm, seg, (float*)g.pre,
-                                g.flag, s)) != MOE_OK)
-      return st;
-    const long long mt_bound = (g.Tk + (long long)E * (GB_T - 1)) / GB_T + (has_shared ? (T + GB_T - 1) / GB_T : 0);
-    g.NT = inter / GB_T;
-    long long grid = tile_grid(mt_bound * g.NT, 0);
-    if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
-    bwd_gemm_kernel<BK_DH><<<(unsigned)grid, GB_THR, 0, s>>>(g);
-    g.NT = d / GB_T;
-    grid = tile_grid(mt_bound * g.NT, 0);
-    if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
-    bwd_gemm_kernel<BK_DX><<<(unsigned)grid, GB_THR, 0, s>>>(g);
-  } else {   // empty batch: every weight gradient is zero
-    const long long n13 = (long long)E * inter * d;
-    zero_fill(routed_grads->dw1, n13, s);
-    zero_fill(routed_grads->dw3, n13, s);
-    zero_fill(routed_grads->dw2, n13, s);
-    if (shared) {
-      zero_fill(shared_grads->dw1, (long long)inter * d, s);
-      zero_fill(shared_grads->dw3, (long long)inter * d, s);
-      zero_fill(shared_grads->dw2, (long long)inter * d, s);
+  if ((st = ffn_recompute_pre(g.x, g.T, g.d, g.E, g.k, g.I, routed, shared, offsets, g.perm,
+                              (int*)g.mstart, (float*)g.pre, g.flag, s)) != MOE_OK)
+    return st;
+  const long long mt_bound =
+      (g.Tk + (long long)g.E * (GB_T - 1)) / GB_T + (g.S > g.E ? (g.T + GB_T - 1) / GB_T : 0);
+  g.NT = g.I / GB_T;
+  long long grid = tile_grid(mt_bound * g.NT, 0);
+  if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+  bwd_gemm_kernel<BK_DH><<<(unsigned)grid, GB_THR, 0, s>>>(g);
+  g.NT = g.d / GB_T;
+  grid = tile_grid(mt_bound * g.NT, 0);
+  if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+  bwd_gemm_kernel<BK_DX><<<(unsigned)grid, GB_THR, 0, s>>>(g);
+  return launch_status();
+}
+
+// Weights half: dW2, then dW1 and dW3, for every expert (and the shared one).
+static moe_status bwd_weights(BwdGemm& g, hipStream_t s) {
+  if (g.T == 0) {   // empty batch: every weight gradient is zero
+    const long long n13 = (long long)g.E * g.I * g.d;
+    zero_fill(g.dw1, n13, s);
+    zero_fill(g.dw3, n13, s);
+    zero_fill(g.dw2, n13, s);
+    if (g.S > g.E) {
+      zero_fill(g.sdw1, (long long)g.I * g.d, s);
+      zero_fill(g.sdw3, (long long)g.I * g.d, s);
+      zero_fill(g.sdw2, (long long)g.I * g.d, s);
     }
     return launch_status();
   }
-  g.MT = d / GB_T;
-  g.NT = inter / GB_T;
+  g.MT = g.d / GB_T;
+  g.NT = g.I / GB_T;
   long long grid = tile_grid((long long)g.S * g.MT * g.NT, 0);
   if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
   bwd_gemm_kernel<BK_DW2><<<(unsigned)grid, GB_THR, 0, s>>>(g);
-  g.MT = 2 * inter / GB_T;
-  g.NT = d / GB_T;
+  g.MT = 2 * g.I / GB_T;
+  g.NT = g.d / GB_T;
   grid = tile_grid((long long)g.S * g.MT * g.NT, 0);
   if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
   bwd_gemm_kernel<BK_DW13><<<(unsigned)grid, GB_THR, 0, s>>>(g);
   return launch_status();
+}
+
+extern "C" moe_status moe_expert_ffn_backward(const void* x, const uint8_t* x_scale, int dtype, int T,
+                                              int d, int E, int k, int inter,
+                                              const moe_expert_bank* routed,
+                                              const moe_expert_bank* shared, const int32_t* offsets,
+                                              const int32_t* perm, const void* d_out, float* dx_rows,
+                                              const moe_grad_bank* routed_grads,
+                                              const moe_grad_bank* shared_grads, void* ws,
+                                              size_t ws_bytes, void* stream) {
+  BwdGemm g;
+  moe_status st = bwd_setup(x, x_scale, dtype, T, d, E, k, inter, routed, shared, offsets, perm, d_out,
+                            dx_rows, routed_grads, shared_grads, ws, ws_bytes, true, true, g);
+  if (st != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = bwd_data(g, routed, shared, offsets, s)) != MOE_OK) return st;
+  return bwd_weights(g, s);
+}
+
+extern "C" moe_status moe_expert_ffn_backward_data(const void* x, const uint8_t* x_scale, int dtype,
+                                                   int T, int d, int E, int k, int inter,
+                                                   const moe_expert_bank* routed,
+                                                   const moe_expert_bank* shared,
+                                                   const int32_t* offsets, const int32_t* perm,
+                                                   const void* d_out, float* dx_rows, void* ws,
+                                                   size_t ws_bytes, void* stream) {
+  BwdGemm g;
+  moe_status st = bwd_setup(x, x_scale, dtype, T, d, E, k, inter, routed, shared, offsets, perm, d_out,
+                            dx_rows, nullptr, nullptr, ws, ws_bytes, true, false, g);
+  if (st != MOE_OK) return st;
+  return bwd_data(g, routed, shared, offsets, (hipStream_t)stream);
+}
+
+extern "C" moe_status moe_expert_ffn_backward_weights(const void* x, int dtype, int T, int d, int E,
+                                                      int k, int inter, const moe_expert_bank* routed,
+                                                      const moe_expert_bank* shared,
+                                                      const int32_t* perm, const void* d_out,
+                                                      const moe_grad_bank* routed_grads,
+                                                      const moe_grad_bank* shared_grads, void* ws,
+                                                      size_t ws_bytes, void* stream) {
+  BwdGemm g;
+  moe_status st = bwd_setup(x, nullptr, dtype, T, d, E, k, inter, routed, shared, nullptr, perm, d_out,
+                            nullptr, routed_grads, shared_grads, ws, ws_bytes, false, true, g);
+  if (st != MOE_OK) return st;
+  if (T > 0 && (!d_out || !aligned(d_out, 16))) return MOE_ERR_INVALID_ARG;
+  return bwd_weights(g, (hipStream_t)stream);
 }
 
 extern "C" moe_status moe_route_backward(const void* x, const uint8_t* x_scale, int dtype, int T, int d,

@@ -124,3 +124,42 @@ def test_backward_bitwise_repeatable_and_token_local_dx():
         one = dict(inp, x=inp["x"][t:t + 1].contiguous())
         _, c = _run(one, wl.k, dy[t:t + 1].contiguous())
         assert torch.equal(c["dx"][0], a["dx"][t]), t
+
+
+# ---------------------------------------------------------------------------
+# Full size (the bf16 T = 4096 layer): the shared expert's weight gradients (its rows
+# are every token, so its oracle needs no routing), and sampled tokens' dx and
+# routing-weight gradients (row-local: the oracle runs on the token alone).
+# ---------------------------------------------------------------------------
+def test_backward_fullsize_t4096():
+    wl = synth.WORKLOADS["bf16_t4096"]
+    say("drawing bf16_t4096 inputs on the GPU")
+    inp = synth.make_layer_inputs(wl, device="cuda")
+    dy = _dy(wl.T, wl.d, 11)
+    ws = pg.BackwardWorkspace(wl.T, wl.d, wl.E, wl.k, wl.inter, pg.MOE_BF16)
+    say("case backward bf16_t4096")
+    fwd, bwd = _run(inp, wl.k, dy, ws=ws)
+    x = values(inp["x"])
+    sh = shared_of(inp)
+    say("  oracle: shared expert backward over all 4096 tokens")
+    gx, s1, s3, s2 = oracle.expert_backward(x, host(dy), *sh)
+    errs = [_nerr(host(bwd["shared_grads"][n]), ref) for n, ref in (("w1", s1), ("w3", s3), ("w2", s2))]
+    say(f"  shared dW1 {errs[0]:.2e} dW3 {errs[1]:.2e} dW2 {errs[2]:.2e}")
+    assert max(errs) <= BAR
+    del gx, s1, s3, s2
+    ids = fwd["ids"].cpu().numpy()
+    for t in (5, wl.T - 1):
+        say(f"  oracle: token {t} alone")
+        ref = oracle.layer_backward(x[t:t + 1], host(inp["w_gate"]), host(inp.get("bias")),
+                                    LazyExperts(inp), sh, wl.k, host(dy[t:t + 1]), dense=False)
+        assert np.array_equal(ids[t], ref["fwd"]["ids"][0])
+        e1 = _nerr(host(bwd["dx"][t:t + 1]), ref["dx"])
+        e2 = _nerr(host(bwd["d_weights"][t:t + 1]), ref["d_weights"])
+        say(f"  token {t}: dx {e1:.2e} d_weights {e2:.2e}")
+        assert e1 <= BAR and e2 <= BAR
+    # bitwise repeatable at full size
+    bwd2 = pg.layer_backward(inp, wl.k, fwd, dy, ws)
+    assert torch.equal(bwd2["dx"], bwd["dx"]) and torch.equal(bwd2["d_w_gate"], bwd["d_w_gate"])
+    assert torch.equal(bwd2["grads"]["w1"], bwd["grads"]["w1"])
+    del inp, fwd, bwd, bwd2, ws
+    torch.cuda.empty_cache()

@@ -131,6 +131,26 @@ __global__ __launch_bounds__(1024) void combine_bwd_kernel(const void* __restric
 constexpr int GB_T = 128, GB_K = 64, GB_S = GB_K + 8, GB_THR = 256;
 enum { BK_DH = 0, BK_DX = 1, BK_DW2 = 2, BK_DW13 = 3 };
 
+// Tuning knobs of the weight-gradient GEMMs (same results for every setting):
+// nontemporal gradient stores, output-column tiles per workgroup, wavefronts per SIMD
+// the register allocation must allow.
+#ifndef MOE_BWD_NT_STORE
+#define MOE_BWD_NT_STORE 1
+#endif
+#ifndef MOE_BWD_RES
+#define MOE_BWD_RES 0
+#endif
+#ifndef MOE_BWD_DEPTH2
+#define MOE_BWD_DEPTH2 0
+#endif
+#ifndef MOE_BWD_NTW
+#define MOE_BWD_NTW 1
+#endif
+#ifndef MOE_BWD_WAVES
+#define MOE_BWD_WAVES 1
+#endif
+constexpr int kBwdNtw = MOE_BWD_NTW;
+
 struct BwdGemm {
   const uint16_t* x;        // activations [T][d]
   const int32_t* perm;
@@ -156,19 +176,29 @@ struct BwdGemm {
   const int* mstart;
   const int* rowstart;
   const int* rowcount;
+  int* tokrow;              // token of each dispatched row [rows]
   int S;
   int MT, NT;               // tiles along M (weight-gradient kinds) and along N
   int* flag;
 };
 
-__device__ __forceinline__ float silu_of(float a) { return a / (1.0f + expf(-a)); }
+// Weight-gradient kinds: a workgroup owns one 128-row block of the output (tile row
+// m0) and kBwdNtw consecutive column tiles.  With MOE_BWD_RES, a segment of at most
+// kResK rows stages its A operand (K x 128) in LDS once and only B streams through,
+// the next tile's first B step loaded before the current tile's stores (measured
+// slower at T = 4096: the larger LDS footprint leaves 2 workgroups per CU instead of
+// 3, and one short tile per workgroup hides latency better).
+constexpr int kResK = MOE_BWD_RES ? 128 : GB_K, kResSteps = kResK / GB_K;
 
 template <int KIND>
-__global__ __launch_bounds__(GB_THR) void bwd_gemm_kernel(BwdGemm g) {
+__global__ __launch_bounds__(GB_THR) __attribute__((amdgpu_waves_per_eu(MOE_BWD_WAVES)))
+void bwd_gemm_kernel(BwdGemm g) {
   constexpr bool WGRAD = KIND >= BK_DW2;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[GB_T * GB_S];
+  constexpr int ASTEPS = WGRAD ? kResSteps : 1;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[ASTEPS * GB_T * GB_S];
   __shared__ __attribute__((aligned(16))) uint16_t sB[GB_T * GB_S];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   // ---- tile decode ----
@@ -194,13 +224,14 @@ __global__ __launch_bounds__(GB_THR) void bwd_gemm_kernel(BwdGemm g) {
     n0 = nt * GB_T;
     K = KIND == BK_DH ? g.d : 2 * g.I;
   } else {
-    const int per = g.MT * g.NT;
+    const int ntw = g.NT / kBwdNtw;   // workgroups along N (each takes kBwdNtw column tiles)
+    const int per = g.MT * ntw;
     int tile;
     if (!xcd_tile<0>(g.S * per, tile)) return;
     s = tile / per;
     const int rem = tile % per;
-    m0 = (rem / g.NT) * GB_T;
-    n0 = (rem % g.NT) * GB_T;
+    m0 = (rem / ntw) * GB_T;
+    n0 = (rem % ntw) * kBwdNtw * GB_T;
     row0 = g.rowstart[s];
     K = g.rowcount[s];
   }
@@ -211,7 +242,10 @@ __global__ __launch_bounds__(GB_THR) void bwd_gemm_kernel(BwdGemm g) {
   // row operand (A of DH / DX): rows lr + 32 i, 16-byte chunk lc of the K-step
   const int lr = tid >> 3, lc = (tid & 7) * 8;
   // K-major operands: K-rows 4 kq .. 4 kq + 3 of the step, columns 8 rb .. 8 rb + 7
-  const int kq = tid & 15, rb = tid >> 4;
+#ifndef MOE_BWD_KMAP
+#define MOE_BWD_KMAP 0
+#endif
+  const int kq = MOE_BWD_KMAP ? tid >> 4 : tid & 15, rb = MOE_BWD_KMAP ? tid & 15 : tid >> 4;
   const uint16_t* arow[4];
   if (!WGRAD) {
     const uint16_t* base = KIND == BK_DH ? g.d_out : g.dadg;
@@ -225,52 +259,67 @@ __global__ __launch_bounds__(GB_THR) void bwd_gemm_kernel(BwdGemm g) {
   const uint16_t* w1b = is_shared ? g.sw1 : g.w1 + e * g.I * (long long)g.d;
   const uint16_t* w3b = is_shared ? g.sw3 : g.w3 + e * g.I * (long long)g.d;
   const uint16_t* w2b = is_shared ? g.sw2 : g.w2 + e * g.d * (long long)g.I;
-  int bad = 0;
-  // source of K-row kg (global K index) of operand `which` (0: A, 1: B), or null for zero
-  auto ksrc = [&](int which, int kg) -> const uint16_t* {
-    if (KIND == BK_DH) return w2b + (long long)kg * g.I + n0 + 8 * rb;
-    if (KIND == BK_DX)
-      return (kg < g.I ? w1b + (long long)kg * g.d : w3b + (long long)(kg - g.I) * g.d) + n0 + 8 * rb;
-    if (kg >= K) return nullptr;
-    const long long j = (long long)row0 + kg;
-    if (KIND == BK_DW2)
-      return which == 0 ? g.d_out + j * g.d + m0 + 8 * rb : g.h + j * g.I + n0 + 8 * rb;
-    if (which == 0) return g.dadg + j * 2LL * g.I + m0 + 8 * rb;
-    long long tok = is_shared ? j - g.Tk : (long long)(g.perm[j] / g.k);
-    if (tok < 0 || tok >= g.T) {
-      bad = 1;
-      tok = 0;
-    }
-    return g.x + tok * g.d + n0 + 8 * rb;
-  };
-
-  f32x16_t acc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
-
-  u32x4_t ra[4], ka[4], kb[4];
+  // K-major sources.  Weight operands (DH, DX): K-row kg of the weight matrix.  Weight-
+  // gradient operands: segment row row0 + kg; rows past the segment's end re-read its
+  // last row and are zeroed after the load (no branches around the loads).
+  const int Klast = K > 0 ? K - 1 : 0;
+  const uint16_t* a_seg = nullptr;   // wgrad A: segment row 0, this thread's columns
+  int lda = 0;
+  if (KIND == BK_DW2) {
+    a_seg = g.d_out + (long long)row0 * g.d + m0 + 8 * rb;
+    lda = g.d;
+  } else if (KIND == BK_DW13) {
+    a_seg = g.dadg + (long long)row0 * 2 * g.I + m0 + 8 * rb;
+    lda = 2 * g.I;
+  }
   const u32x4_t zero4 = {0u, 0u, 0u, 0u};
-  auto gload = [&](int k0) {
+  f32x16_t acc[2][2];
+  u32x4_t ra[4], ka[4], kb[4];
+  auto load_a_to = [&](u32x4_t(&A)[4], int k0) {
     if (!WGRAD) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ra[i] = *(const u32x4_t*)(arow[i] + k0);
+      for (int i = 0; i < 4; ++i) A[i] = *(const u32x4_t*)(arow[i] + k0);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint16_t* p = ksrc(0, k0 + 4 * kq + i);
-        ka[i] = p ? *(const u32x4_t*)p : zero4;
+        const int kg = k0 + 4 * kq + i;
+        const u32x4_t v = *(const u32x4_t*)(a_seg + min(kg, Klast) * lda);
+        A[i] = kg < K ? v : zero4;
       }
     }
+  };
+  auto load_a = [&](int k0) {
+    if (!WGRAD) load_a_to(ra, k0);
+    else load_a_to(ka, k0);
+  };
+  auto load_b_to = [&](u32x4_t(&B)[4], int k0, int c0) {
+    if (KIND == BK_DH || KIND == BK_DX) {
+      // the K-step lies in one weight matrix (I % 64 == 0)
+      const uint16_t* base;
+      int ldb;
+      if (KIND == BK_DH) {
+        base = w2b + (long long)k0 * g.I;
+        ldb = g.I;
+      } else {
+        base = k0 < g.I ? w1b + (long long)k0 * g.d : w3b + (long long)(k0 - g.I) * g.d;
+        ldb = g.d;
+      }
+      base += c0 + 8 * rb;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint16_t* p = ksrc(1, k0 + 4 * kq + i);
-      kb[i] = p ? *(const u32x4_t*)p : zero4;
+      for (int i = 0; i < 4; ++i) B[i] = *(const u32x4_t*)(base + (4 * kq + i) * ldb);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kg = k0 + 4 * kq + i;
+        const int jr = row0 + min(kg, Klast);
+        const uint16_t* p = KIND == BK_DW2 ? g.h + (long long)jr * g.I
+                                           : g.x + (long long)g.tokrow[jr] * g.d;
+        const u32x4_t v = *(const u32x4_t*)(p + c0 + 8 * rb);
+        B[i] = kg < K ? v : zero4;
+      }
     }
   };
+  auto load_b = [&](int k0, int c0) { load_b_to(kb, k0, c0); };
   // 4 K-rows x 8 columns -> LDS rows 8 rb + c, K offset 4 kq (two dwords per row)
   auto tstore = [&](uint16_t* sX, const u32x4_t(&R)[4]) {
 #pragma unroll
@@ -287,19 +336,23 @@ __global__ __launch_bounds__(GB_THR) void bwd_gemm_kernel(BwdGemm g) {
       *(u32x2_t*)&sX[(8 * rb + c) * GB_S + 4 * kq] = v;
     }
   };
-
-  const int nsteps = (K + GB_K - 1) / GB_K;
-  if (nsteps > 0) gload(0);
-  for (int st = 0; st < nsteps; ++st) {
+  auto store_a = [&](uint16_t* sAs) {
     if (!WGRAD) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *(u32x4_t*)&sA[(lr + 32 * i) * GB_S + lc] = ra[i];
+      for (int i = 0; i < 4; ++i) *(u32x4_t*)&sAs[(lr + 32 * i) * GB_S + lc] = ra[i];
     } else {
-      tstore(sA, ka);
+      tstore(sAs, ka);
     }
-    tstore(sB, kb);
-    __syncthreads();
-    if (st + 1 < nsteps) gload((st + 1) * GB_K);
+  };
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+  };
+  auto mma = [&](const uint16_t* sAs) {
 #pragma unroll
     for (int kk = 0; kk < GB_K; kk += 16) {
       const int kc = kk + (lane >> 5) * 8;
@@ -307,7 +360,7 @@ __global__ __launch_bounds__(GB_THR) void bwd_gemm_kernel(BwdGemm g) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
         af[mb] = __builtin_bit_cast(bf16x8_t,
-                                    *(const u32x4_t*)&sA[(wm * 64 + mb * 32 + (lane & 31)) * GB_S + kc]);
+                                    *(const u32x4_t*)&sAs[(wm * 64 + mb * 32 + (lane & 31)) * GB_S + kc]);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
         bf[nb] = __builtin_bit_cast(bf16x8_t,
@@ -318,45 +371,152 @@ __global__ __launch_bounds__(GB_THR) void bwd_gemm_kernel(BwdGemm g) {
         for (int nb = 0; nb < 2; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bf[nb], acc[mb][nb], 0, 0, 0);
     }
-    __syncthreads();
-  }
-  if (bad) raise_flag(g.flag, kFlagCorrupt);
+  };
 
   // ---- epilogue: accumulator element v of a lane is C[i][j], j = lane % 32,
   //      i = 8 (v / 4) + 4 (lane / 32) + v % 4 ----
-  const int j = lane & 31;
+  auto epilogue = [&](int c0) {
+    const int j = lane & 31;
+    // weight gradients: output row m0 + r, column c0 + ..., one matrix per workgroup
+    // (a 128-row block lies in dW1 or in dW3 because I % 128 == 0)
+    float* wbase = nullptr;
+    int wld = 0;
+    if (KIND == BK_DW2) {
+      wbase = (is_shared ? g.sdw2 : g.dw2 + e * g.d * (long long)g.I) + (long long)m0 * g.I + c0;
+      wld = g.I;
+    } else if (KIND == BK_DW13) {
+      float* mat = m0 < g.I ? (is_shared ? g.sdw1 : g.dw1 + e * g.I * (long long)g.d)
+                            : (is_shared ? g.sdw3 : g.dw3 + e * g.I * (long long)g.d);
+      wbase = mat + (long long)(m0 < g.I ? m0 : m0 - g.I) * g.d + c0;
+      wld = g.d;
+    }
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = wm * 64 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (!WGRAD && r >= mrows) continue;
+      for (int v = 0; v < 16; ++v) {
+        const int r = wm * 64 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (!WGRAD && r >= mrows) continue;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int col = n0 + wn * 64 + nb * 32 + j;
-        const float c = acc[mb][nb][v];
-        if (KIND == BK_DH) {
-          const long long orow = (long long)row0 + r;
-          const float a = g.pre[orow * 2 * g.I + col], gg = g.pre[orow * 2 * g.I + g.I + col];
-          const float sg = 1.0f / (1.0f + expf(-a));
-          const float sl = silu_of(a);
-          g.dadg[orow * 2 * g.I + col] = f32_to_bf16(c * gg * (sg * (1.0f + a * (1.0f - sg))));
-          g.dadg[orow * 2 * g.I + g.I + col] = f32_to_bf16(c * sl);
-          g.h[orow * g.I + col] = f32_to_bf16(sl * gg);
-        } else if (KIND == BK_DX) {
-          g.dx_rows[((long long)row0 + r) * g.d + col] = c;
-        } else if (KIND == BK_DW2) {
-          float* dst = is_shared ? g.sdw2 : g.dw2 + e * g.d * (long long)g.I;
-          dst[(long long)(m0 + r) * g.I + col] = c;
-        } else {
-          const int m = m0 + r;
-          float* dst = m < g.I ? (is_shared ? g.sdw1 : g.dw1 + e * g.I * (long long)g.d)
-                               : (is_shared ? g.sdw3 : g.dw3 + e * g.I * (long long)g.d);
-          dst[(long long)(m < g.I ? m : m - g.I) * g.d + col] = c;
+        for (int nb = 0; nb < 2; ++nb) {
+          const int col = c0 + wn * 64 + nb * 32 + j;
+          const float c = acc[mb][nb][v];
+          if (KIND == BK_DH) {
+            const long long orow = (long long)row0 + r;
+            const float a = g.pre[orow * 2 * g.I + col], gg = g.pre[orow * 2 * g.I + g.I + col];
+            const float den = 1.0f + expf(-a);   // silu(a) = a / den as in the forward
+            const float sg = 1.0f / den, sl = a / den;
+            g.dadg[orow * 2 * g.I + col] = f32_to_bf16(c * gg * (sg * (1.0f + a * (1.0f - sg))));
+            g.dadg[orow * 2 * g.I + g.I + col] = f32_to_bf16(c * sl);
+            g.h[orow * g.I + col] = f32_to_bf16(sl * gg);
+          } else if (KIND == BK_DX) {
+            g.dx_rows[((long long)row0 + r) * g.d + col] = c;
+          } else {
+            float* dp = wbase + r * wld + (col - c0);
+            if (MOE_BWD_NT_STORE) __builtin_nontemporal_store(c, dp); else *dp = c;
+          }
         }
       }
     }
+  };
+
+  const int nsteps = (K + GB_K - 1) / GB_K;
+  if (MOE_BWD_RES && WGRAD && nsteps <= kResSteps) {
+    // A resident in LDS for every column tile; B streamed, next tile's step 0 early
+    for (int st = 0; st < nsteps; ++st) {
+      load_a(st * GB_K);
+      store_a(sA + st * GB_T * GB_S);
+    }
+    if (nsteps > 0) load_b(0, n0);
+    for (int q = 0; q < kBwdNtw; ++q) {
+      const int c0 = n0 + q * GB_T;
+      zero_acc();
+      for (int st = 0; st < nsteps; ++st) {
+        tstore(sB, kb);
+        __syncthreads();
+        if (st + 1 < nsteps) load_b((st + 1) * GB_K, c0);
+        else if (q + 1 < kBwdNtw) load_b(0, c0 + GB_T);
+        mma(sA + st * GB_T * GB_S);
+        __syncthreads();
+      }
+      epilogue(c0);
+    }
+  } else if (WGRAD && MOE_BWD_DEPTH2) {
+    // two K-steps of loads in flight: register set 0 holds the even steps, set 1 the odd
+    u32x4_t a1[4], b1[4];
+    for (int q = 0; q < kBwdNtw; ++q) {
+      const int c0 = n0 + q * GB_T;
+      zero_acc();
+      if (nsteps > 0) {
+        load_a_to(ka, 0);
+        load_b_to(kb, 0, c0);
+      }
+      if (nsteps > 1) {
+        load_a_to(a1, GB_K);
+        load_b_to(b1, GB_K, c0);
+      }
+      for (int st = 0; st < nsteps; st += 2) {
+        tstore(sA, ka);
+        tstore(sB, kb);
+        __syncthreads();
+        if (st + 2 < nsteps) {
+          load_a_to(ka, (st + 2) * GB_K);
+          load_b_to(kb, (st + 2) * GB_K, c0);
+        }
+        mma(sA);
+        __syncthreads();
+        if (st + 1 < nsteps) {
+          tstore(sA, a1);
+          tstore(sB, b1);
+          __syncthreads();
+          if (st + 3 < nsteps) {
+            load_a_to(a1, (st + 3) * GB_K);
+            load_b_to(b1, (st + 3) * GB_K, c0);
+          }
+          mma(sA);
+          __syncthreads();
+        }
+      }
+      epilogue(c0);
+    }
+  } else {
+    const int ntiles = WGRAD ? kBwdNtw : 1;
+    for (int q = 0; q < ntiles; ++q) {
+      const int c0 = n0 + q * GB_T;
+      zero_acc();
+      if (nsteps > 0) {
+        load_a(0);
+        load_b(0, c0);
+      }
+      for (int st = 0; st < nsteps; ++st) {
+        store_a(sA);
+        tstore(sB, kb);
+        __syncthreads();
+        if (st + 1 < nsteps) {
+          load_a((st + 1) * GB_K);
+          load_b((st + 1) * GB_K, c0);
+        }
+        mma(sA);
+        __syncthreads();
+      }
+      epilogue(c0);
+    }
   }
+}
+
+// tokrow[j]: the token of dispatched row j (perm[j] / k for routed rows, j - T k for the
+// shared expert's); an out-of-range entry is flagged and read as token 0.
+__global__ __launch_bounds__(256) void tokrow_kernel(const int32_t* __restrict__ perm, int T, int k,
+                                                     long long rows, int* __restrict__ tokrow,
+                                                     int* flag) {
+  const long long j = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (j >= rows) return;
+  const long long Tk = (long long)T * k;
+  long long t = j < Tk ? (long long)(perm[j] / k) : j - Tk;
+  if (t < 0 || t >= T) {
+    raise_flag(flag, kFlagCorrupt);
+    t = 0;
+  }
+  tokrow[j] = (int)t;
 }
 
 // Zero fill by a kernel (callers may capture these calls in a graph).
@@ -574,6 +734,7 @@ static moe_status bwd_setup(const void* x, const uint8_t* x_scale, int dtype, in
     g.sdw3 = shared ? shared_grads->dw3 : nullptr;
     g.sdw2 = shared ? shared_grads->dw2 : nullptr;
   }
+  g.tokrow = (int*)(w + L.tokrow);
   int* seg = (int*)(w + L.seg);
   g.mstart = seg;
   g.rowstart = seg + (E + 2);
@@ -618,14 +779,17 @@ static moe_status bwd_weights(BwdGemm& g, hipStream_t s) {
     }
     return launch_status();
   }
+  const long long rows = g.Tk + (g.S > g.E ? g.T : 0);
+  tokrow_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, s>>>(g.perm, g.T, g.k, rows, g.tokrow, g.flag);
   g.MT = g.d / GB_T;
   g.NT = g.I / GB_T;
-  long long grid = tile_grid((long long)g.S * g.MT * g.NT, 0);
+  if (g.NT % kBwdNtw != 0 || (g.d / GB_T) % kBwdNtw != 0) return MOE_ERR_UNSUPPORTED;
+  long long grid = tile_grid((long long)g.S * g.MT * (g.NT / kBwdNtw), 0);
   if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
   bwd_gemm_kernel<BK_DW2><<<(unsigned)grid, GB_THR, 0, s>>>(g);
   g.MT = 2 * g.I / GB_T;
   g.NT = g.d / GB_T;
-  grid = tile_grid((long long)g.S * g.MT * g.NT, 0);
+  grid = tile_grid((long long)g.S * g.MT * (g.NT / kBwdNtw), 0);
   if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
   bwd_gemm_kernel<BK_DW13><<<(unsigned)grid, GB_THR, 0, s>>>(g);
   return launch_status();

@@ -147,12 +147,13 @@ inline size_t workspace_bytes(int T, int d, int E, int k, int inter, int dtype) 
   return m > c ? m : c;
 }
 
-// Backward pass (bf16 layers): segment table, recomputed pre-activations a | g
+// Backward pass (bf16 layers): segment table, the token of each dispatched row,
+// recomputed pre-activations a | g
 // [rows][2 inter] fp32, their gradients da | dg [rows][2 inter] bf16, h [rows][inter]
 // bf16, the routing-weight gradients through the gate dl [T][k] fp32, the transposed
 // gate [E][d] fp32.
 struct BwdWs {
-  size_t seg, pre, dadg, h, dl, wt, bytes;
+  size_t seg, tokrow, pre, dadg, h, dl, wt, bytes;
   long long rows;
 };
 inline BwdWs bwd_ws(int T, int d, int E, int k, int inter) {
@@ -162,6 +163,7 @@ inline BwdWs bwd_ws(int T, int d, int E, int k, int inter) {
   w.seg = o;  o = align_up(o + (size_t)(3 * (E + 2)) * sizeof(int), 256);
   w.dl = o;   o = align_up(o + (size_t)T * k * sizeof(float), 256);
   w.wt = o;   o = align_up(o + (size_t)E * d * sizeof(float), 256);
+  w.tokrow = o; o = align_up(o + (size_t)w.rows * sizeof(int), 256);
   w.pre = o;  o = align_up(o + (size_t)w.rows * 2 * inter * sizeof(float), 256);
   w.dadg = o; o = align_up(o + (size_t)w.rows * 2 * inter * sizeof(uint16_t), 256);
   w.h = o;    o = align_up(o + (size_t)w.rows * inter * sizeof(uint16_t), 256);

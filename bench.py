@@ -122,6 +122,7 @@ def main():
         sgrads = ({n: torch.empty(shared[n].shape, dtype=torch.float32, device=dev) for n in ("w1", "w3", "w2")}
                   if has_shared else None)
         dx = torch.empty(T, d, dtype=torch.float32, device=dev)
+        pre = torch.empty(rows, 2 * I, dtype=torch.float32, device=dev)
         gate_grad = not (replay and filt is None and inp["weights_in"] is not None)
 
     def step(ev=None):
@@ -140,7 +141,10 @@ def main():
         pg.moe_dispatch(ids, E, ws, offsets=offsets, perm=perm, row_of=row_of)
         if ev is not None:
             ev[2].record()
-        pg.moe_expert_ffn_gate_up(x, routed, shared, offsets, perm, k, ws, x_scale=inp["x_scale"])
+        if bwd:   # training step: keep the pre-activations for the backward
+            pg.moe_expert_ffn_gate_up_save(x, routed, shared, offsets, perm, k, ws, pre=pre)
+        else:
+            pg.moe_expert_ffn_gate_up(x, routed, shared, offsets, perm, k, ws, x_scale=inp["x_scale"])
         if ev is not None:
             ev[3].record()
         pg.moe_expert_ffn_down(dt, T, d, routed, shared, k, ws, out=out)
@@ -154,7 +158,7 @@ def main():
         pg.moe_combine_backward(dy, out, row_of, weights, T, has_shared, dt, d_out=d_out, d_weights=d_weights)
         if ev is not None:
             ev[6].record()
-        pg.moe_expert_ffn_backward_data(x, routed, shared, offsets, perm, k, d_out, ws, dx_rows=dx_rows)
+        pg.moe_expert_ffn_backward_data(x, routed, shared, offsets, perm, k, d_out, ws, dx_rows=dx_rows, pre=pre)
         if ev is not None:
             ev[7].record()
         pg.moe_expert_ffn_backward_weights(x, routed, shared, perm, k, d_out, ws, grads=grads,
@@ -224,11 +228,13 @@ def main():
     if bwd:
         n_all = E + (1 if has_shared else 0)      # the weights half writes every expert's gradients
         bytes_cbwd = T * d * ob + T * k * d * ob * 2 + (T * d * ob if has_shared else 0) + T * k * 12
-        bytes_data = (n_mats * 3 * mat * 2 + T * d * eb + rows * 2 * I * 4 * 2 + rows * d * ob
+        bytes_data = (n_mats * 3 * mat + rows * 2 * I * 4 + rows * d * ob
                       + rows * 2 * I * 2 * 2 + rows * I * 2 + rows * d * 4)
         bytes_wts = n_all * 3 * I * d * 4 + rows * d * ob + rows * I * 2 + rows * 2 * I * 2 + rows * d * eb
         bytes_rbwd = rows * d * 4 + T * d * 4 + 2 * E * d * 4 + d * E * 4 + T * k * d * eb + T * k * 16
-        flops_data = 2.0 * rows * d * I * 5
+        flops_data = 2.0 * rows * d * I * 3
+        stages["ffn_gate_up"]["alg_bytes"] += rows * 2 * I * 4   # the saved pre-activations
+        stages["ffn_gate_up"]["GB_s"] = gbs(stages["ffn_gate_up"]["alg_bytes"], stage_ms["ffn_gate_up"])
         flops_wts = 2.0 * rows * d * I * 3
         for n, b, f in (("combine_backward", bytes_cbwd, None), ("ffn_backward_data", bytes_data, flops_data),
                         ("ffn_backward_weights", bytes_wts, flops_wts), ("route_backward", bytes_rbwd, None)):

@@ -241,6 +241,16 @@ moe_status moe_combine(const void* out, int dtype, const int32_t* row_of, const 
  * Every reduction has one fixed order (no atomics): results are bitwise reproducible.
  * ------------------------------------------------------------------------------ */
 
+/* moe_expert_ffn_gate_up that also keeps the pre-activations for the backward pass:
+ * pre out fp32 [T*k (+T)][2*inter], row j = (x W1, x W3) of dispatched row j, exactly the
+ * values the SwiGLU epilogue uses (bf16 layers only; MOE_ERR_UNSUPPORTED otherwise).
+ * Same results as moe_expert_ffn_gate_up; pass `pre` to moe_expert_ffn_backward. */
+moe_status moe_expert_ffn_gate_up_save(const void* x, const uint8_t* x_scale, int dtype, int T, int d,
+                                       int E, int k, int inter, const moe_expert_bank* routed,
+                                       const moe_expert_bank* shared, const int32_t* offsets,
+                                       const int32_t* perm, float* pre, void* ws, size_t ws_bytes,
+                                       void* stream);
+
 /* Gradients of one expert bank, fp32, in the bank's layout: dw1, dw3 [n][I][d],
  * dw2 [n][d][I]; 16-byte aligned. */
 typedef struct {
@@ -267,6 +277,8 @@ moe_status moe_combine_backward(const void* dy, int dtype, const void* out, cons
 
 /* Backward of moe_expert_ffn (bf16 layers; MOE_ERR_UNSUPPORTED for other dtypes and
  * unless d % 128 == 0 and inter % 128 == 0).  Arguments x .. perm as moe_expert_ffn.
+ *   pre       the pre-activations moe_expert_ffn_gate_up_save kept, or NULL: then they
+ *             are recomputed (same values, bit for bit; one more pass over W1 and W3).
  *   d_out     bf16 [T*k (+T)][d] from moe_combine_backward.
  *   dx_rows   out fp32 [T*k (+T)][d]: each dispatched row's dL/dx, da W1 + dg W3 with
  *             a = x W1, g = x W3 recomputed as the forward computes them, dh = d_out W2,
@@ -279,7 +291,8 @@ moe_status moe_combine_backward(const void* dy, int dtype, const void* out, cons
 moe_status moe_expert_ffn_backward(const void* x, const uint8_t* x_scale, int dtype, int T, int d,
                                    int E, int k, int inter, const moe_expert_bank* routed,
                                    const moe_expert_bank* shared, const int32_t* offsets,
-                                   const int32_t* perm, const void* d_out, float* dx_rows,
+                                   const int32_t* perm, const float* pre, const void* d_out,
+                                   float* dx_rows,
                                    const moe_grad_bank* routed_grads,
                                    const moe_grad_bank* shared_grads, void* ws, size_t ws_bytes,
                                    void* stream);
@@ -291,7 +304,7 @@ moe_status moe_expert_ffn_backward(const void* x, const uint8_t* x_scale, int dt
 moe_status moe_expert_ffn_backward_data(const void* x, const uint8_t* x_scale, int dtype, int T,
                                         int d, int E, int k, int inter,
                                         const moe_expert_bank* routed, const moe_expert_bank* shared,
-                                        const int32_t* offsets, const int32_t* perm,
+                                        const int32_t* offsets, const int32_t* perm, const float* pre,
                                         const void* d_out, float* dx_rows, void* ws, size_t ws_bytes,
                                         void* stream);
 moe_status moe_expert_ffn_backward_weights(const void* x, int dtype, int T, int d, int E, int k,

@@ -19,7 +19,7 @@ __all__ = [
     "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_gate_up", "moe_expert_ffn_down", "moe_combine", "moe_check", "moe_status_string",
     "layer_forward", "moe_backward_workspace_size", "moe_combine_backward", "moe_expert_ffn_backward",
     "moe_route_backward", "layer_backward", "moe_expert_ffn_backward_data",
-    "moe_expert_ffn_backward_weights",
+    "moe_expert_ffn_backward_weights", "moe_expert_ffn_gate_up_save",
 ]
 
 MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
@@ -61,10 +61,12 @@ def lib():
             "moe_backward_workspace_size": [I, I, I, I, I, I, PSZ],
             "moe_combine_backward": [P, I, P, P, P, I, I, I, I, P, P, P],
             "moe_expert_ffn_backward": [P, P, I, I, I, I, I, I, ctypes.POINTER(_Bank),
-                                        ctypes.POINTER(_Bank), P, P, P, P, ctypes.POINTER(_GradBank),
+                                        ctypes.POINTER(_Bank), P, P, P, P, P, ctypes.POINTER(_GradBank),
                                         ctypes.POINTER(_GradBank), P, SZ, P],
+            "moe_expert_ffn_gate_up_save": [P, P, I, I, I, I, I, I, ctypes.POINTER(_Bank),
+                                            ctypes.POINTER(_Bank), P, P, P, P, SZ, P],
             "moe_expert_ffn_backward_data": [P, P, I, I, I, I, I, I, ctypes.POINTER(_Bank),
-                                             ctypes.POINTER(_Bank), P, P, P, P, P, SZ, P],
+                                             ctypes.POINTER(_Bank), P, P, P, P, P, P, SZ, P],
             "moe_expert_ffn_backward_weights": [P, I, I, I, I, I, I, ctypes.POINTER(_Bank),
                                                 ctypes.POINTER(_Bank), P, P, ctypes.POINTER(_GradBank),
                                                 ctypes.POINTER(_GradBank), P, SZ, P],
@@ -343,8 +345,23 @@ def _grad_like(bank):
             for n in ("w1", "w3", "w2")}
 
 
+def moe_expert_ffn_gate_up_save(x, routed: dict, shared, offsets, perm, k, ws: Workspace, pre=None):
+    """GEMM1 half that also returns the fp32 pre-activations [rows][2I] for the backward."""
+    _check_dev(x, offsets, perm)
+    T, d = x.shape
+    E, inter = routed["w1"].shape[0], routed["w1"].shape[1]
+    rows = T * k + (T if shared is not None else 0)
+    pre = torch.empty(rows, 2 * inter, dtype=torch.float32, device=x.device) if pre is None else pre
+    rb, sb = _bank(routed), _bank(shared)
+    _ok(lib().moe_expert_ffn_gate_up_save(_ptr(x), None, _dtype_of(x), T, d, E, k, inter, ctypes.byref(rb),
+                                          ctypes.byref(sb) if sb is not None else None, _ptr(offsets),
+                                          _ptr(perm), _ptr(pre), ws.ptr, ws.nbytes, _stream(x.device)),
+        "moe_expert_ffn_gate_up_save")
+    return pre
+
+
 def moe_expert_ffn_backward(x, routed: dict, shared, offsets, perm, k, d_out, ws: Workspace,
-                            x_scale=None, dx_rows=None, grads=None, shared_grads=None):
+                            x_scale=None, dx_rows=None, grads=None, shared_grads=None, pre=None):
     """Returns (dx_rows [rows][d] fp32, grads {w1, w3, w2} fp32, shared grads or None)."""
     _check_dev(x, x_scale, offsets, perm, d_out)
     T, d = x.shape
@@ -358,14 +375,14 @@ def moe_expert_ffn_backward(x, routed: dict, shared, offsets, perm, k, d_out, ws
     rg, sg = _grads(grads), _grads(shared_grads)
     _ok(lib().moe_expert_ffn_backward(_ptr(x), _ptr(x_scale), _dtype_of(x), T, d, E, k, inter,
                                       ctypes.byref(rb), ctypes.byref(sb) if sb is not None else None,
-                                      _ptr(offsets), _ptr(perm), _ptr(d_out), _ptr(dx_rows),
+                                      _ptr(offsets), _ptr(perm), _ptr(pre), _ptr(d_out), _ptr(dx_rows),
                                       ctypes.byref(rg), ctypes.byref(sg) if sg is not None else None,
                                       ws.ptr, ws.nbytes, _stream(x.device)), "moe_expert_ffn_backward")
     return dx_rows, grads, shared_grads
 
 
 def moe_expert_ffn_backward_data(x, routed: dict, shared, offsets, perm, k, d_out, ws: Workspace,
-                                 x_scale=None, dx_rows=None):
+                                 x_scale=None, dx_rows=None, pre=None):
     _check_dev(x, x_scale, offsets, perm, d_out)
     T, d = x.shape
     E, inter = routed["w1"].shape[0], routed["w1"].shape[1]
@@ -374,7 +391,8 @@ def moe_expert_ffn_backward_data(x, routed: dict, shared, offsets, perm, k, d_ou
     rb, sb = _bank(routed), _bank(shared)
     _ok(lib().moe_expert_ffn_backward_data(_ptr(x), _ptr(x_scale), _dtype_of(x), T, d, E, k, inter,
                                            ctypes.byref(rb), ctypes.byref(sb) if sb is not None else None,
-                                           _ptr(offsets), _ptr(perm), _ptr(d_out), _ptr(dx_rows), ws.ptr,
+                                           _ptr(offsets), _ptr(perm), _ptr(pre), _ptr(d_out), _ptr(dx_rows),
+                                           ws.ptr,
                                            ws.nbytes, _stream(x.device)), "moe_expert_ffn_backward_data")
     return dx_rows
 
@@ -417,7 +435,7 @@ def moe_route_backward(x, w_gate, ids, weights, d_weights, offsets, perm, row_of
 
 
 def layer_backward(inp: dict, k: int, fwd: dict, dy, ws: Workspace, replay: bool = False,
-                   check: bool = True):
+                   check: bool = True, pre=None):
     """Gradients of one layer through the three backward C calls, given the forward's
     routing/dispatch results and expert outputs (``layer_forward``'s dict) and dL/dy.
     The gate gets a gradient unless the routing weights were the caller's."""
@@ -428,7 +446,8 @@ def layer_backward(inp: dict, k: int, fwd: dict, dy, ws: Workspace, replay: bool
     d_out, d_weights = moe_combine_backward(dy, fwd["out"], fwd["row_of"], fwd["weights"], T, has_shared, dt)
     routed = {n: inp.get(n) for n in ("w1", "w3", "w2", "w1_scale", "w3_scale", "w2_scale")}
     dx_rows, grads, sgrads = moe_expert_ffn_backward(x, routed, inp.get("shared"), fwd["offsets"],
-                                                     fwd["perm"], k, d_out, ws, x_scale=inp.get("x_scale"))
+                                                     fwd["perm"], k, d_out, ws, x_scale=inp.get("x_scale"),
+                                                     pre=pre)
     gate_grad = not (replay and inp.get("weights_in") is not None)
     dx, dwg, db = moe_route_backward(x, inp["w_gate"], fwd["ids"], fwd["weights"], d_weights,
                                      fwd["offsets"], fwd["perm"], fwd["row_of"], dx_rows, has_shared, ws,

@@ -675,7 +675,8 @@ static bool grads_ok(const moe_grad_bank* g) {
 // Argument checks and kernel arguments shared by the three expert-backward entry points.
 static moe_status bwd_setup(const void* x, const uint8_t* x_scale, int dtype, int T, int d, int E, int k,
                             int inter, const moe_expert_bank* routed, const moe_expert_bank* shared,
-                            const int32_t* offsets, const int32_t* perm, const void* d_out,
+                            const int32_t* offsets, const int32_t* perm, const float* pre,
+                            const void* d_out,
                             float* dx_rows, const moe_grad_bank* routed_grads,
                             const moe_grad_bank* shared_grads, void* ws, size_t ws_bytes, bool data,
                             bool weights, BwdGemm& g) {
@@ -722,7 +723,8 @@ static moe_status bwd_setup(const void* x, const uint8_t* x_scale, int dtype, in
   g.sw3 = shared ? (const uint16_t*)shared->w3 : nullptr;
   g.sw2 = shared ? (const uint16_t*)shared->w2 : nullptr;
   g.d_out = (const uint16_t*)d_out;
-  g.pre = (const float*)(w + L.pre);
+  if (pre && !aligned(pre, 16)) return MOE_ERR_INVALID_ARG;
+  g.pre = pre ? pre : (const float*)(w + L.pre);
   g.dadg = (uint16_t*)(w + L.dadg);
   g.h = (uint16_t*)(w + L.h);
   g.dx_rows = dx_rows;
@@ -746,12 +748,12 @@ static moe_status bwd_setup(const void* x, const uint8_t* x_scale, int dtype, in
 
 // Data half: recomputed pre-activations, dh with the SwiGLU backward, dx_rows.
 static moe_status bwd_data(BwdGemm& g, const moe_expert_bank* routed, const moe_expert_bank* shared,
-                           const int32_t* offsets, hipStream_t s) {
+                           const int32_t* offsets, bool saved, hipStream_t s) {
   if (g.T == 0) return MOE_OK;
-  moe_status st;
-  if ((st = ffn_recompute_pre(g.x, g.T, g.d, g.E, g.k, g.I, routed, shared, offsets, g.perm,
-                              (int*)g.mstart, (float*)g.pre, g.flag, s)) != MOE_OK)
-    return st;
+  moe_status st = saved ? ffn_seg_table(offsets, g.T, g.E, g.k, g.S > g.E, (int*)g.mstart, g.flag, s)
+                        : ffn_recompute_pre(g.x, g.T, g.d, g.E, g.k, g.I, routed, shared, offsets, g.perm,
+                                            (int*)g.mstart, (float*)g.pre, g.flag, s);
+  if (st != MOE_OK) return st;
   const long long mt_bound =
       (g.Tk + (long long)g.E * (GB_T - 1)) / GB_T + (g.S > g.E ? (g.T + GB_T - 1) / GB_T : 0);
   g.NT = g.I / GB_T;
@@ -799,16 +801,16 @@ extern "C" moe_status moe_expert_ffn_backward(const void* x, const uint8_t* x_sc
                                               int d, int E, int k, int inter,
                                               const moe_expert_bank* routed,
                                               const moe_expert_bank* shared, const int32_t* offsets,
-                                              const int32_t* perm, const void* d_out, float* dx_rows,
-                                              const moe_grad_bank* routed_grads,
+                                              const int32_t* perm, const float* pre, const void* d_out,
+                                              float* dx_rows, const moe_grad_bank* routed_grads,
                                               const moe_grad_bank* shared_grads, void* ws,
                                               size_t ws_bytes, void* stream) {
   BwdGemm g;
-  moe_status st = bwd_setup(x, x_scale, dtype, T, d, E, k, inter, routed, shared, offsets, perm, d_out,
-                            dx_rows, routed_grads, shared_grads, ws, ws_bytes, true, true, g);
+  moe_status st = bwd_setup(x, x_scale, dtype, T, d, E, k, inter, routed, shared, offsets, perm, pre,
+                            d_out, dx_rows, routed_grads, shared_grads, ws, ws_bytes, true, true, g);
   if (st != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  if ((st = bwd_data(g, routed, shared, offsets, s)) != MOE_OK) return st;
+  if ((st = bwd_data(g, routed, shared, offsets, pre != nullptr, s)) != MOE_OK) return st;
   return bwd_weights(g, s);
 }
 
@@ -817,13 +819,14 @@ extern "C" moe_status moe_expert_ffn_backward_data(const void* x, const uint8_t*
                                                    const moe_expert_bank* routed,
                                                    const moe_expert_bank* shared,
                                                    const int32_t* offsets, const int32_t* perm,
-                                                   const void* d_out, float* dx_rows, void* ws,
-                                                   size_t ws_bytes, void* stream) {
+                                                   const float* pre, const void* d_out,
+                                                   float* dx_rows, void* ws, size_t ws_bytes,
+                                                   void* stream) {
   BwdGemm g;
-  moe_status st = bwd_setup(x, x_scale, dtype, T, d, E, k, inter, routed, shared, offsets, perm, d_out,
-                            dx_rows, nullptr, nullptr, ws, ws_bytes, true, false, g);
+  moe_status st = bwd_setup(x, x_scale, dtype, T, d, E, k, inter, routed, shared, offsets, perm, pre,
+                            d_out, dx_rows, nullptr, nullptr, ws, ws_bytes, true, false, g);
   if (st != MOE_OK) return st;
-  return bwd_data(g, routed, shared, offsets, (hipStream_t)stream);
+  return bwd_data(g, routed, shared, offsets, pre != nullptr, (hipStream_t)stream);
 }
 
 extern "C" moe_status moe_expert_ffn_backward_weights(const void* x, int dtype, int T, int d, int E,
@@ -834,8 +837,8 @@ extern "C" moe_status moe_expert_ffn_backward_weights(const void* x, int dtype, 
                                                       const moe_grad_bank* shared_grads, void* ws,
                                                       size_t ws_bytes, void* stream) {
   BwdGemm g;
-  moe_status st = bwd_setup(x, nullptr, dtype, T, d, E, k, inter, routed, shared, nullptr, perm, d_out,
-                            nullptr, routed_grads, shared_grads, ws, ws_bytes, false, true, g);
+  moe_status st = bwd_setup(x, nullptr, dtype, T, d, E, k, inter, routed, shared, nullptr, perm, nullptr,
+                            d_out, nullptr, routed_grads, shared_grads, ws, ws_bytes, false, true, g);
   if (st != MOE_OK) return st;
   if (T > 0 && (!d_out || !aligned(d_out, 16))) return MOE_ERR_INVALID_ARG;
   return bwd_weights(g, (hipStream_t)stream);

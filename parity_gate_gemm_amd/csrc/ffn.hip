@@ -300,6 +300,10 @@ void grouped_gemm_bf16_kernel(GemmArgs g) {
         const float a = acc[mb][0][v], gg = acc[mb][1][v];
         const int col = n0 + wn * 32 + j;
         g.out[orow * g.N + col] = f32_to_bf16(silu_f32(a) * gg);   // 32 features per wave
+        if (g.out_pre) {   // saved for the backward pass
+          g.out_pre[orow * 2 * g.N + col] = a;
+          g.out_pre[orow * 2 * g.N + g.N + col] = gg;
+        }
       } else if (MODE == 2) {
         const int col = n0 + wn * 32 + j;
         g.out_pre[orow * 2 * g.N + col] = acc[mb][0][v];
@@ -1401,7 +1405,8 @@ static void launch_bf16(int wn, unsigned grid, hipStream_t s, const GemmArgs& g)
 static moe_status run_gate_up(const void* x, const uint8_t* xs, int dtype, int T, int d, int E,
                               int k, int inter, const moe_expert_bank* routed,
                               const moe_expert_bank* shared, const int32_t* offsets,
-                              const int32_t* perm, const FfnPlan& p, hipStream_t s) {
+                              const int32_t* perm, const FfnPlan& p, hipStream_t s,
+                              float* pre = nullptr) {
   seg_table_kernel<<<1, 1024, 0, s>>>(offsets, E, p.Tk, T, p.has_shared, p.tm, p.mstart, p.rowstart,
                                       p.rowcount, p.flag);
   if (dtype == MOE_MXFP8) {
@@ -1458,6 +1463,7 @@ static moe_status run_gate_up(const void* x, const uint8_t* xs, int dtype, int T
     g.rowcount = p.rowcount;
     g.S = p.S;
     g.out = (uint16_t*)p.h;
+    g.out_pre = pre;
     g.flag = p.flag;
     const int wn = bf16_wn(inter, 32, MOE_GEMM1_WN);
     g.NT = inter / (32 * wn);
@@ -1576,6 +1582,13 @@ static moe_status run_down(int dtype, int T, int d, int E, int k, int inter,
   return launch_status();
 }
 
+moe_status ffn_seg_table(const int32_t* offsets, int T, int E, int k, int has_shared, int* seg, int* flag,
+                         hipStream_t s) {
+  seg_table_kernel<<<1, 1024, 0, s>>>(offsets, E, (long long)T * k, T, has_shared, BM, seg, seg + (E + 2),
+                                      seg + 2 * (E + 2), flag);
+  return launch_status();
+}
+
 moe_status ffn_recompute_pre(const void* x, int T, int d, int E, int k, int inter,
                              const moe_expert_bank* routed, const moe_expert_bank* shared,
                              const int32_t* offsets, const int32_t* perm, int* seg, float* pre,
@@ -1640,6 +1653,24 @@ extern "C" moe_status moe_expert_ffn_gate_up(const void* x, const uint8_t* x_sca
   const FfnPlan p = plan_of(ws, T, d, E, k, inter, dtype, shared != nullptr);
   return run_gate_up(x, x_scale, dtype, T, d, E, k, inter, routed, shared, offsets, perm, p,
                      (hipStream_t)stream);
+}
+
+extern "C" moe_status moe_expert_ffn_gate_up_save(const void* x, const uint8_t* x_scale, int dtype,
+                                                  int T, int d, int E, int k, int inter,
+                                                  const moe_expert_bank* routed,
+                                                  const moe_expert_bank* shared,
+                                                  const int32_t* offsets, const int32_t* perm,
+                                                  float* pre, void* ws, size_t ws_bytes,
+                                                  void* stream) {
+  moe_status st = check_ffn_shape(dtype, T, d, E, k, inter, routed, shared, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (dtype != MOE_BF16 || MOE_GEMM_DMA) return MOE_ERR_UNSUPPORTED;
+  if (x_scale || !offsets) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !perm || !pre || !aligned(x, 16) || !aligned(pre, 16)) return MOE_ERR_INVALID_ARG;
+  const FfnPlan p = plan_of(ws, T, d, E, k, inter, dtype, shared != nullptr);
+  return run_gate_up(x, x_scale, dtype, T, d, E, k, inter, routed, shared, offsets, perm, p,
+                     (hipStream_t)stream, pre);
 }
 
 extern "C" moe_status moe_expert_ffn_down(int dtype, int T, int d, int E, int k, int inter,

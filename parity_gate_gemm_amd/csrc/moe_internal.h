@@ -256,6 +256,8 @@ inline long long tile_grid(long long bound, int chunk) {
 // tiles into seg (mstart [E + 2], rowstart [E + 2], rowcount [E + 2]) and the GEMM1
 // pre-activations of every dispatched row, pre [rows][2 inter] fp32 (x W1, then x W3),
 // with the forward's MFMA sequence (bf16 only).
+moe_status ffn_seg_table(const int32_t* offsets, int T, int E, int k, int has_shared, int* seg, int* flag,
+                         hipStream_t s);
 moe_status ffn_recompute_pre(const void* x, int T, int d, int E, int k, int inter,
                              const moe_expert_bank* routed, const moe_expert_bank* shared,
                              const int32_t* offsets, const int32_t* perm, int* seg, float* pre,

@@ -105,14 +105,18 @@ def test_dispatch_ffn_combine_host_validation(L):
     assert L.moe_combine_backward(P, 1, P, P, P, 4, 100, 2, 0, P, P, None) == 2           # d % 8
     assert L.moe_combine_backward(None, 1, P, P, P, 4, 128, 2, 0, P, P, None) == 1
     assert L.moe_combine_backward(P, 1, P, P, P, 0, 128, 2, 0, P, P, None) == 0           # T = 0
-    assert L.moe_expert_ffn_backward(P, None, 0, 4, 128, 16, 2, 128, B, None, P, P, P, P, GB, None,
-                                     P, 1 << 30, None) == 2                                # fp32
-    assert L.moe_expert_ffn_backward(P, None, 1, 4, 128, 16, 2, 64, B, None, P, P, P, P, GB, None,
-                                     P, 1 << 30, None) == 2                                # I % 128
-    assert L.moe_expert_ffn_backward(P, None, 1, 4, 128, 16, 2, 128, B, B, P, P, P, P, GB, None,
-                                     P, 1 << 30, None) == 1                                # shared w/o grads
-    assert L.moe_expert_ffn_backward(P, None, 1, 4, 128, 16, 2, 128, B, None, P, P, P, P, GB, None,
-                                     P, 64, None) == 3                                     # workspace
+    assert L.moe_expert_ffn_backward(P, None, 0, 4, 128, 16, 2, 128, B, None, P, P, None, P, P, GB,
+                                     None, P, 1 << 30, None) == 2                          # fp32
+    assert L.moe_expert_ffn_backward(P, None, 1, 4, 128, 16, 2, 64, B, None, P, P, None, P, P, GB,
+                                     None, P, 1 << 30, None) == 2                          # I % 128
+    assert L.moe_expert_ffn_backward(P, None, 1, 4, 128, 16, 2, 128, B, B, P, P, None, P, P, GB,
+                                     None, P, 1 << 30, None) == 1                          # shared w/o grads
+    assert L.moe_expert_ffn_backward(P, None, 1, 4, 128, 16, 2, 128, B, None, P, P, None, P, P, GB,
+                                     None, P, 64, None) == 3                               # workspace
+    assert L.moe_expert_ffn_backward(P, None, 1, 4, 128, 16, 2, 128, B, None, P, P,
+                                     ctypes.c_void_p(0x10008), P, P, GB, None, P, 1 << 30, None) == 1
+    assert L.moe_expert_ffn_gate_up_save(P, None, 2, 4, 128, 16, 2, 128, B, None, P, P, P, P,
+                                         1 << 30, None) in (1, 2)                          # mxfp8
     assert L.moe_route_backward(P, None, 1, 4, 128, P, 16, 2, P, P, P, P, P, P, P, 0, P, None, P,
                                 P, 1 << 30, None) == 1                                     # bias w/o gate
     assert L.moe_route_backward(P, None, 1, 4, 126, P, 16, 2, P, P, P, P, P, P, P, 0, P, P, None,

@@ -163,3 +163,25 @@ def test_backward_fullsize_t4096():
     assert torch.equal(bwd2["grads"]["w1"], bwd["grads"]["w1"])
     del inp, fwd, bwd, bwd2, ws
     torch.cuda.empty_cache()
+
+
+def test_saved_pre_activations_equal_recomputed():
+    """The forward's saved pre-activations give the same forward output and the same
+    gradients, bit for bit, as the backward's recomputation."""
+    wl = synth.Workload("save", T=300, d=256, inter=256, E=6, k=3, shared=True, bias=True, dtype="bf16",
+                        seed=9)
+    inp = to_device(synth.make_layer_inputs(wl, device="cpu"))
+    dy = _dy(wl.T, wl.d, 9)
+    ws = pg.BackwardWorkspace(wl.T, wl.d, wl.E, wl.k, wl.inter, pg.MOE_BF16)
+    say("case saved pre-activations")
+    fwd, ref = _run(inp, wl.k, dy, ws=ws)
+    routed = {n: inp.get(n) for n in ("w1", "w3", "w2", "w1_scale", "w3_scale", "w2_scale")}
+    pre = pg.moe_expert_ffn_gate_up_save(inp["x"], routed, inp["shared"], fwd["offsets"], fwd["perm"],
+                                         wl.k, ws)
+    out = pg.moe_expert_ffn_down(pg.MOE_BF16, wl.T, wl.d, routed, inp["shared"], wl.k, ws)
+    assert torch.equal(out, fwd["out"])
+    got = pg.layer_backward(inp, wl.k, fwd, dy, ws, pre=pre)
+    for n in ("dx", "d_weights", "d_w_gate", "d_bias"):
+        assert torch.equal(got[n], ref[n]), n
+    for n in ("w1", "w3", "w2"):
+        assert torch.equal(got["grads"][n], ref["grads"][n]), n

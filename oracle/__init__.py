@@ -25,4 +25,13 @@ from .moe_oracle import (  # noqa: F401
     softmax_pick_grad,
     silu_grad,
     normwise_rel_err,
+    e2m1_value,
+    E2M1_TABLE,
+    e2m1_rne_codes,
+    e4m3_rne_codes,
+    nvfp4_quantize,
+    nvfp4_dequant,
+    bf16_rne,
+    expert_ffn_nvfp4,
+    layer_nvfp4,
 )

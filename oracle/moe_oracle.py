@@ -439,3 +439,132 @@ def layer_backward(x, w_gate, bias, experts, shared, k: int, dy, ids_in=None, we
                     d_bias[e] += dl[t, r]
     return {"dx": dx, "d_weights": d_weights, "d_w_gate": d_w_gate, "d_bias": d_bias,
             "dw1": dw1, "dw3": dw3, "dw2": dw2, "d_shared": d_shared, "fwd": fwd}
+
+
+# ---------------------------------------------------------------------------
+# NVFP4 (the forward-pass format of Composer 2 Technical Report, §6.1 "Kernels": FP4
+# E2M1 values, one FP8 E4M3 scale per block of 16, one FP32 scale per token; the
+# quantization uses IEEE division)
+# ---------------------------------------------------------------------------
+E2M1_MAGS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def e2m1_value(code: int) -> float:
+    """FP4 E2M1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0; exponent 0 is
+    the subnormal 0.5 m."""
+    v = float(E2M1_MAGS[code & 7])
+    return -v if code & 8 else v
+
+
+E2M1_TABLE = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+
+
+def _rne_codes(x, mags):
+    """Codes (sign << k | magnitude index) of the nearest value on a non-negative grid
+    `mags` (ascending, index = code magnitude bits), ties to the even index, saturating
+    at the largest magnitude.  x: float values (exact)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), mags[-1])
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, len(mags) - 1)
+    lo = np.clip(hi - 1, 0, len(mags) - 1)
+    dlo, dhi = a - mags[lo], mags[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    idx = np.where(pick_hi, hi, lo)
+    return idx, np.signbit(x)
+
+
+def e2m1_rne_codes(x) -> np.ndarray:
+    """Nearest E2M1 code, ties to even, saturating at 6 (the sign kept, -0 -> 8)."""
+    idx, neg = _rne_codes(x, E2M1_MAGS)
+    return (idx + np.where(neg, 8, 0)).astype(np.uint8)
+
+
+def e4m3_rne_codes(x) -> np.ndarray:
+    """Nearest OCP E4M3 code, ties to even, saturating at 448 (non-negative inputs)."""
+    mags = E4M3_TABLE[:127]            # codes 0x00..0x7E ascend in value; 0x7F is NaN
+    idx, neg = _rne_codes(x, mags)
+    assert not np.any(neg & (np.abs(np.asarray(x, dtype=np.float64)) > 0))
+    return idx.astype(np.uint8)
+
+
+def nvfp4_quantize(v):
+    """Rows of v (exact fp32 values, K % 16 == 0) -> (codes [R, K] 0..15, block scale
+    codes [R, K/16] E4M3, row scales [R] fp32).  Per row: s = amax / 2688 (6 * 448, the
+    largest E2M1 times the largest E4M3); per block of 16: S = E4M3_RNE((bamax / s) / 6);
+    per element: E2M1_RNE(v / (S s)).  Every step is one IEEE fp32 operation (division
+    or product) rounded to nearest even, as numpy's float32 arithmetic is; a zero row
+    gets s = 0 and zero codes, a zero block scale gives zero codes."""
+    v = np.asarray(v, dtype=np.float32)
+    R, K = v.shape
+    assert K % 16 == 0
+    blocks = v.reshape(R, K // 16, 16)
+    amax = np.abs(v).max(axis=1) if K else np.zeros(R, np.float32)
+    live = amax > 0
+    s = np.zeros(R, np.float32)
+    s[live] = amax[live] / np.float32(2688.0)
+    bamax = np.abs(blocks).max(axis=2)
+    t = np.zeros_like(bamax)
+    t[live] = bamax[live] / s[live, None]
+    sb = e4m3_rne_codes(t / np.float32(6.0))
+    sbv = E4M3_TABLE[sb].astype(np.float32)
+    den = sbv * s[:, None]                 # fp32 product
+    codes = np.zeros((R, K // 16, 16), dtype=np.uint8)
+    nz = den > 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = blocks / den[..., None]        # fp32 division
+    codes[nz] = e2m1_rne_codes(q[nz])
+    return codes.reshape(R, K), sb, s
+
+
+def nvfp4_dequant(codes, block_scales, row_scales) -> np.ndarray:
+    """Exact values E2M1(code) * E4M3(block scale) * row scale, in float64."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    R, K = codes.shape
+    sb = E4M3_TABLE[np.asarray(block_scales, dtype=np.uint8)]
+    return (E2M1_TABLE[codes] * np.repeat(sb, 16, axis=1)) * f64(row_scales)[:, None]
+
+
+def bf16_rne(v) -> np.ndarray:
+    """float64 -> the nearest bf16 value (ties to even), returned as float64."""
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)   # fp64 -> fp32 RNE
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def expert_ffn_nvfp4(x_rows, w1, w3, w2) -> np.ndarray:
+    """SwiGLU expert in the NVFP4 forward: the rows quantized per row (token), weights
+    given as NVFP4 triples (codes, block scales, row scales) per matrix, h rounded to
+    bf16 and quantized per row before the second GEMM; products exact in float64."""
+    W1, W3, W2 = (nvfp4_dequant(*w) for w in (w1, w3, w2))
+    xq = nvfp4_dequant(*nvfp4_quantize(np.asarray(x_rows, dtype=np.float32)))
+    h = bf16_rne(silu(xq @ W1.T) * (xq @ W3.T))
+    hq = nvfp4_dequant(*nvfp4_quantize(h.astype(np.float32)))
+    return hq @ W2.T
+
+
+def layer_nvfp4(x, w_gate, bias, experts, shared, k: int, ids_in=None, weights_in=None):
+    """The layer forward with NVFP4 experts: routing on the bf16 x as in ``layer``, each
+    expert (and the shared one) through ``expert_ffn_nvfp4``, the same combine."""
+    xf = f64(x)
+    T, d = xf.shape
+    if ids_in is None:
+        ids, w, logits = route(xf, w_gate, bias, k)
+    else:
+        ids, w, logits = route_replay(xf, w_gate, bias, ids_in, weights_in)
+    E = logits.shape[1]
+    offsets, perm, row_of = dispatch(ids, E)
+    rows = np.zeros((T * k, d), dtype=np.float64)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        rows[lo:hi] = expert_ffn_nvfp4(xf[perm[lo:hi] // k], *experts[e])
+    y = np.zeros((T, d), dtype=np.float64)
+    for t in range(T):
+        for r in range(k):
+            y[t] += w[t, r] * rows[row_of[t * k + r]]
+    if shared is not None:
+        y += expert_ffn_nvfp4(xf, *shared)
+    return {"y": y, "ids": ids, "weights": w, "logits": logits,
+            "offsets": offsets, "perm": perm, "row_of": row_of, "rows": rows}

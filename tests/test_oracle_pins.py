@@ -573,3 +573,105 @@ def test_silu_grad_values():
     assert np.allclose(oracle.silu_grad(z), fd, rtol=0, atol=1e-9)
     # large |z|: silu' -> 1 (z >> 0) and -> 0 (z << 0)
     assert abs(oracle.silu_grad(40.0) - 1.0) < 1e-15 and abs(oracle.silu_grad(-40.0)) < 1e-15
+
+
+# ---------------------------------------------------------------------------
+# NVFP4 quantization (E2M1 values, E4M3 scale per 16, fp32 scale per row)
+# ---------------------------------------------------------------------------
+def _brute_nearest(x, mags):
+    """Index of the nearest magnitude, ties to the even index, by exhaustive search."""
+    a = min(abs(x), mags[-1])
+    best = None
+    for i, m in enumerate(mags):
+        dd = abs(a - m)
+        if best is None or dd < best[0] or (dd == best[0] and i % 2 == 0):
+            best = (dd, i)
+    return best[1]
+
+
+def test_e2m1_and_e4m3_rounding_brute_force():
+    rng = np.random.default_rng(40)
+    mags2 = list(oracle.E2M1_TABLE[:8])
+    vals = list(rng.uniform(0, 7, 300)) + [0.5 * (a + b) for a, b in zip(mags2, mags2[1:])]
+    vals += [v * (1 + s * 2.0 ** -20) for v in vals[-7:] for s in (-1, 1)]
+    for v in vals:
+        for sgn in (1.0, -1.0):
+            c = int(oracle.e2m1_rne_codes([sgn * v])[0])
+            assert c & 7 == _brute_nearest(v, mags2), v
+            assert (c >> 3) == (1 if sgn < 0 else 0)
+    mags3 = list(oracle.E4M3_TABLE[:127])
+    vals = list(np.exp(rng.uniform(np.log(2.0 ** -11), np.log(500.0), 400)))
+    vals += [0.5 * (a + b) for a, b in zip(mags3, mags3[1:])][::3]
+    got = oracle.e4m3_rne_codes(vals)
+    for v, c in zip(vals, got):
+        assert int(c) == _brute_nearest(v, mags3), v
+
+
+def test_e4m3_rounding_matches_an_independent_encoder():
+    """The input generator's E4M3 encoder is separate code (integer bit manipulation)."""
+    import torch
+    import synth.inputs as si
+    rng = np.random.default_rng(41)
+    v = np.exp(rng.uniform(np.log(2.0 ** -12), np.log(448.0), 5000)).astype(np.float32)
+    ref = si._e4m3_rne_codes(torch.from_numpy(v)).numpy().astype(np.uint8)
+    assert np.array_equal(oracle.e4m3_rne_codes(v), ref)
+
+
+def test_bf16_rne_matches_torch():
+    import torch
+    rng = np.random.default_rng(42)
+    v = rng.standard_normal(4000) * np.exp(rng.uniform(-30, 30, 4000))
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(oracle.bf16_rne(v.astype(np.float32).astype(np.float64)), ref)
+
+
+def test_nvfp4_quantize_golden():
+    g = json.load(open(os.path.join(GOLDEN, "nvfp4_hand.json")))
+    v = np.asarray(g["rows"], dtype=np.float32)
+    codes, sb, s = oracle.nvfp4_quantize(v)
+    assert codes.tolist() == g["codes"]
+    assert sb.tolist() == g["block_scales"]
+    assert s.tolist() == g["row_scales"]
+    assert np.array_equal(oracle.nvfp4_dequant(codes, sb, s), np.asarray(g["dequant"]))
+
+
+def test_nvfp4_power_of_two_scaling_and_error_bound():
+    rng = np.random.default_rng(43)
+    v = _bf16_values(rng, (24, 64), scale=3.0)
+    v[3] = 0.0                                  # a zero row
+    v[5, :16] = 0.0                             # a zero block
+    codes, sb, s = oracle.nvfp4_quantize(v)
+    assert s[3] == 0 and not codes[3].any() and not sb[3].any()
+    assert not codes[5, :16].any()
+    # scaling a row by 2^j scales its row scale by 2^j and keeps every code
+    for j in (-7, 5):
+        c2, sb2, s2 = oracle.nvfp4_quantize(v * np.float32(2.0 ** j))
+        assert np.array_equal(c2, codes) and np.array_equal(sb2, sb)
+        assert np.array_equal(s2, s * np.float32(2.0 ** j))
+    # each element is within half an E2M1 step (at its magnitude) of its block's grid
+    deq = oracle.nvfp4_dequant(codes, sb, s)
+    den = np.repeat(oracle.E4M3_TABLE[sb], 16, axis=1) * s[:, None]
+    q = np.abs(v.astype(np.float64)) / np.where(den > 0, den, 1)
+    gap = np.where(q < 2, 0.5, np.where(q < 4, 1.0, 2.0))
+    err = np.abs(deq - v) / np.where(den > 0, den, 1)
+    # (the quantizer divides in fp32: a relative 1e-6 covers values within an fp32 ulp of a tie)
+    assert np.all((err <= gap / 2 * (1 + 1e-6)) | (q > 6))
+    # a row's largest element lands on its block's top code (6) or one below
+    assert np.all(np.abs(deq).max(axis=1)[s > 0] > 0)
+
+
+def test_nvfp4_requantize_is_identity_and_layer_plumbing():
+    rng = np.random.default_rng(44)
+    v = _bf16_values(rng, (16, 48), scale=2.0)
+    q = oracle.nvfp4_quantize(v)
+    deq = oracle.nvfp4_dequant(*q).astype(np.float32)
+    q2 = oracle.nvfp4_quantize(deq)          # the grid values quantize to themselves
+    assert all(np.array_equal(a, b) for a, b in zip(q, q2))
+    # identical experts: y_t = sum_r w_tr FFN(x_t) = FFN(x_t) (the weights sum to one)
+    T, d, I, E, k = 6, 32, 32, 5, 2
+    x = _bf16_values(rng, (T, d))
+    wg = _f32(rng.standard_normal((d, E)))
+    mats = [oracle.nvfp4_quantize(_bf16_values(rng, sh, 0.3)) for sh in ((I, d), (I, d), (d, I))]
+    res = oracle.layer_nvfp4(x, wg, None, [tuple(mats)] * E, None, k)
+    ref = oracle.expert_ffn_nvfp4(x, *mats)
+    assert np.allclose(res["y"], ref, rtol=1e-12, atol=1e-12)

@@ -87,7 +87,8 @@ def main():
     t_draw = time.perf_counter() - t_draw
 
     T, d, E, k, I = wl.T, wl.d, wl.E, wl.k, wl.inter
-    dt = {"f32": pg.MOE_F32, "bf16": pg.MOE_BF16, "mxfp8": pg.MOE_MXFP8}[wl.dtype]
+    dt = {"f32": pg.MOE_F32, "bf16": pg.MOE_BF16, "mxfp8": pg.MOE_MXFP8, "nvfp4": pg.MOE_NVFP4}[wl.dtype]
+    xdt = pg.MOE_BF16 if dt == pg.MOE_NVFP4 else dt     # NVFP4 layers: bf16 x, y, routing
     replay = wl.routing == "replay"
     filt = args.replay_filter
     if filt is not None and not replay:
@@ -100,7 +101,7 @@ def main():
         sys.exit(2)
     ws = pg.BackwardWorkspace(T, d, E, k, I, dt) if bwd else pg.Workspace(T, d, E, k, I, dt)
     x, wg, bias = inp["x"], inp["w_gate"], inp["bias"]
-    routed = {n: inp[n] for n in ("w1", "w3", "w2", "w1_scale", "w3_scale", "w2_scale")}
+    routed = {n: inp.get(n) for n in ("w1", "w3", "w2") + pg._BANK_OPT}
     shared = inp["shared"]
     rows = T * k + (T if has_shared else 0)
     odt = torch.float32 if dt == pg.MOE_F32 else torch.bfloat16
@@ -150,7 +151,7 @@ def main():
         pg.moe_expert_ffn_down(dt, T, d, routed, shared, k, ws, out=out)
         if ev is not None:
             ev[4].record()
-        pg.moe_combine(out, row_of, weights, T, has_shared, dt, y=y)
+        pg.moe_combine(out, row_of, weights, T, has_shared, xdt, y=y)
         if ev is not None:
             ev[5].record()
         if not bwd:
@@ -197,14 +198,16 @@ def main():
     # ---- algorithmic work of one step (see the kernel notes in the design doc) ----
     seg = np.diff(offsets.cpu().numpy())
     touched = int((seg > 0).sum())
-    eb = {"f32": 4, "bf16": 2, "mxfp8": 1 + 1 / 32}[wl.dtype]   # MXFP8: codes + E8M0 scales
-    hb = {"f32": 4, "bf16": 2, "mxfp8": 1 + 1 / 32}[wl.dtype]
+    # bytes per element: MXFP8 codes + E8M0 scales; NVFP4 half-byte codes + E4M3 per 16
+    eb = {"f32": 4, "bf16": 2, "mxfp8": 1 + 1 / 32, "nvfp4": 0.5 + 1 / 16}[wl.dtype]
+    hb = eb
     ob = 4 if dt == pg.MOE_F32 else 2
     n_mats = touched + (1 if has_shared else 0)
     mat = I * d * eb
     bytes_gate_up = n_mats * 2 * mat + T * d * eb + rows * I * hb + T * k * 4
     bytes_down = n_mats * mat + rows * I * hb + rows * d * ob
-    bytes_route = T * d * eb + d * E * 4 + T * k * 8 + (E * 4 if bias is not None else 0)
+    xb = 2 if wl.dtype == "nvfp4" else eb       # x as the layer takes it
+    bytes_route = T * d * xb + d * E * 4 + T * k * 8 + (E * 4 if bias is not None else 0)
     if filt is not None:
         bytes_route += T * k * 4        # the replayed ids read besides the filtered ids written
     bytes_dispatch = T * k * 4 * 3 + (E + 1) * 4
@@ -245,13 +248,16 @@ def main():
     # the MXFP8 GEMMs run on the LDS-ring kernel where d and I are multiples of 512
     mx_ring = d % 512 == 0 and I % 512 == 0
     kname = {"f32": "grouped_ffn_f32_kernel", "bf16": "grouped_gemm_bf16_kernel",
-             "mxfp8": "grouped_gemm_mx_ring_kernel" if mx_ring else "grouped_gemm_mx_kernel"}[wl.dtype]
+             "mxfp8": "grouped_gemm_mx_ring_kernel" if mx_ring else "grouped_gemm_mx_kernel",
+             "nvfp4": "grouped_gemm_fp4_kernel"}[wl.dtype]
     dom_kernel = {"ffn_gate_up": f"{kname}<0> (W1/W3 + SwiGLU)", "ffn_down": f"{kname}<1> (W2)"}[dom]
     gemm_tflops = (flops_gate_up + flops_down) / ((stage_ms["ffn_gate_up"] + stage_ms["ffn_down"]) * 1e-3) / 1e12
     mfma_peak = MXFP8_MFMA_PEAK_TFLOPS if wl.dtype == "mxfp8" else BF16_MFMA_PEAK_TFLOPS
     # Weight streaming bounds the grouped GEMMs when tokens per expert are few (the
     # bf16 workloads); the MXFP8 prefill chunk is bound by the block-scaled matrix cores.
-    if wl.dtype == "mxfp8":
+    # NVFP4 operands are decoded to bf16 for the bf16 matrix cores: their peak is bf16's,
+    # and at 0.56 byte per weight the matrix cores, not HBM, bound the GEMMs
+    if wl.dtype in ("mxfp8", "nvfp4"):
         dom_flops = flops_gate_up if dom == "ffn_gate_up" else flops_down
         achieved = dom_flops / (stage_ms[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": mfma_peak, "unit": "TFLOP/s",
@@ -304,6 +310,8 @@ def main():
         result["config"]["pass"] = "forward+backward"
     if wl.dtype != "bf16":
         result["vs_metric_config"] = "this workload is not the metric's configuration (bf16 T=4096)"
+    if wl.dtype == "nvfp4":
+        result["config"]["experts"] = "NVFP4 (E2M1, E4M3 per 16, fp32 per row); x, y bf16"
     if bwd:   # the oracle's backward keeps every touched expert's fp64 gradients: few tokens
         args.cpu_sample = min(args.cpu_sample, 4)
     if args.cpu_sample > 0:
@@ -337,18 +345,24 @@ class _ExpertCache:
 
     def fetch(self, e):
         if e not in self.cache:
-            self.cache[e] = tuple((self.inp[n][e].cpu(),
-                                   None if self.inp.get(n + "_scale") is None else self.inp[n + "_scale"][e].cpu())
+            self.cache[e] = tuple(tuple(None if self.inp.get(n + sfx) is None else self.inp[n + sfx][e].cpu()
+                                        for sfx in ("", "_scale", "_rscale"))
                                   for n in ("w1", "w3", "w2"))
         return self.cache[e]
 
     def __getitem__(self, e):
-        return tuple(_stored_values(t, sc) for t, sc in self.fetch(e))
+        return tuple(_stored_values(*m) for m in self.fetch(e))
 
 
-def _stored_values(t, scale=None):
-    """Host values of a stored tensor (MXFP8 codes decoded by the oracle's decoder)."""
+def _stored_values(t, scale=None, rscale=None):
+    """Host values of a stored tensor (MXFP8 codes decoded by the oracle's decoder); an
+    NVFP4 matrix stays the (codes, block scales, row scales) triple the oracle takes."""
+    import numpy as np
     import oracle
+    if rscale is not None:
+        p = t.numpy()
+        codes = np.stack([p & 15, p >> 4], axis=-1).reshape(p.shape[0], -1)
+        return codes, scale.numpy(), rscale.numpy()
     if scale is None:
         return t.float().numpy()
     return oracle.mx_dequant(t.numpy(), scale.numpy())
@@ -372,7 +386,7 @@ def cpu_baseline(inp, wl, ids, n_tok, log_tau=None, dy=None):
         experts.fetch(int(e))                       # host copies: not part of the timed work
     sh = inp["shared"]
     shared = None if sh is None else tuple(
-        _stored_values(sh[n].cpu(), None if sh.get(n + "_scale") is None else sh[n + "_scale"].cpu())
+        _stored_values(*(None if sh.get(n + sfx) is None else sh[n + sfx].cpu() for sfx in ("", "_scale", "_rscale")))
         for n in ("w1", "w3", "w2"))
     kw = {}
     if wl.routing == "replay":
@@ -381,7 +395,9 @@ def cpu_baseline(inp, wl, ids, n_tok, log_tau=None, dy=None):
     if log_tau is not None:
         fid, fw, _, _ = oracle.route_replay_filtered(x, wg, bias, kw["ids_in"], log_tau)
         kw = {"ids_in": fid, "weights_in": fw}
-    if dy is None:
+    if wl.dtype == "nvfp4":
+        oracle.layer_nvfp4(x, wg, bias, experts, shared, wl.k, **kw)
+    elif dy is None:
         oracle.layer(x, wg, bias, experts, shared, wl.k, **kw)
     else:
         oracle.layer_backward(x, wg, bias, experts, shared, wl.k, dy[rows].float().cpu().numpy(),

@@ -45,6 +45,12 @@
  *       MOE_MXFP8 : OCP MXFP8 x and weights (uint8 E4M3 codes plus one uint8 E8M0
  *                   scale per 32 consecutive elements of the contiguous dimension),
  *                   fp32 accumulation, bf16 expert outputs and y.
+ *       MOE_NVFP4 : the NVFP4 forward (Composer 2 Technical Report, section 6.1
+ *                   "Kernels"): bf16 x and y, NVFP4 expert weights; the expert FFN
+ *                   quantizes x per token and h per row to NVFP4 (E2M1 values, one
+ *                   E4M3 scale per 16 elements, one fp32 scale per row).  Only the
+ *                   expert-FFN calls take MOE_NVFP4; routing, dispatch and combine of
+ *                   such a layer take MOE_BF16 (their tensors are bf16).
  *   - Expert weight layout (per expert, output-major, reduction dimension
  *     contiguous): w1, w3 [I][d] and w2 [d][I]; i.e. the mathematical W1 [d x I]
  *     is stored transposed.  A bank of n experts is n such matrices back to back.
@@ -71,11 +77,14 @@ typedef enum {
   MOE_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2, MOE_NVFP4 = 3 } moe_dtype;
 
 /* One bank of SwiGLU experts (n experts stored back to back; see layout above).
  * The *_scale pointers are the E8M0 scales for MOE_MXFP8 ([n][I][d/32] for w1/w3,
- * [n][d][I/32] for w2) and must be NULL for the other dtypes. */
+ * [n][d][I/32] for w2), the E4M3 block scales for MOE_NVFP4 ([n][I][d/16] for w1/w3,
+ * [n][d][I/16] for w2), and must be NULL for the other dtypes.  MOE_NVFP4 weights are
+ * E2M1 codes packed two per byte (element 2i in the low nibble: w1, w3 [n][I][d/2],
+ * w2 [n][d][I/2]) with one fp32 scale per row in *_rscale ([n][I], [n][I], [n][d]). */
 typedef struct {
   const void* w1;
   const void* w3;
@@ -83,6 +92,9 @@ typedef struct {
   const uint8_t* w1_scale;
   const uint8_t* w3_scale;
   const uint8_t* w2_scale;
+  const float* w1_rscale;   /* MOE_NVFP4 only (else NULL): fp32 scale per weight row */
+  const float* w3_rscale;
+  const float* w2_rscale;
 } moe_expert_bank;
 
 /* Size in bytes of the workspace that every call below accepts for a layer with
@@ -250,6 +262,15 @@ moe_status moe_expert_ffn_gate_up_save(const void* x, const uint8_t* x_scale, in
                                        const moe_expert_bank* shared, const int32_t* offsets,
                                        const int32_t* perm, float* pre, void* ws, size_t ws_bytes,
                                        void* stream);
+
+/* NVFP4 quantization of the rows of a bf16 matrix [rows][K] (K % 16 == 0): per row
+ * s = amax / 2688, per block of 16 S = E4M3_RNE((bamax / s) / 6), per element
+ * E2M1_RNE(v / (S s)), each step one IEEE fp32 operation rounded to nearest even,
+ * saturating (a zero row has s = 0 and zero codes).  codes out [rows][K/2] (two per
+ * byte, element 2i in the low nibble, 8-byte aligned), block_scales out [rows][K/16]
+ * (E4M3 codes), row_scales out fp32 [rows].  src 16-byte aligned. */
+moe_status moe_nvfp4_quantize(const void* src, int rows, int K, uint8_t* codes,
+                              uint8_t* block_scales, float* row_scales, void* stream);
 
 /* Gradients of one expert bank, fp32, in the bank's layout: dw1, dw3 [n][I][d],
  * dw2 [n][d][I]; 16-byte aligned. */

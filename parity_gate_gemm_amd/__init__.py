@@ -13,7 +13,7 @@ import os
 import torch
 
 __all__ = [
-    "MOE_F32", "MOE_BF16", "MOE_MXFP8", "MoeError", "lib", "Workspace",
+    "MOE_F32", "MOE_BF16", "MOE_MXFP8", "MOE_NVFP4", "MoeError", "moe_nvfp4_quantize", "lib", "Workspace",
     "moe_workspace_size", "moe_workspace_init", "moe_route", "moe_route_replay",
     "moe_route_replay_filtered",
     "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_gate_up", "moe_expert_ffn_down", "moe_combine", "moe_check", "moe_status_string",
@@ -22,7 +22,7 @@ __all__ = [
     "moe_expert_ffn_backward_weights", "moe_expert_ffn_gate_up_save",
 ]
 
-MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_MXFP8, MOE_NVFP4 = 0, 1, 2, 3
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 _lib = None
@@ -37,7 +37,8 @@ class MoeError(RuntimeError):
 class _Bank(ctypes.Structure):
     _fields_ = [("w1", ctypes.c_void_p), ("w3", ctypes.c_void_p), ("w2", ctypes.c_void_p),
                 ("w1_scale", ctypes.c_void_p), ("w3_scale", ctypes.c_void_p),
-                ("w2_scale", ctypes.c_void_p)]
+                ("w2_scale", ctypes.c_void_p), ("w1_rscale", ctypes.c_void_p),
+                ("w3_rscale", ctypes.c_void_p), ("w2_rscale", ctypes.c_void_p)]
 
 
 class _GradBank(ctypes.Structure):
@@ -59,6 +60,7 @@ def lib():
             "moe_route": [P, P, I, I, I, P, P, I, I, P, P, P, SZ, P],
             "moe_route_replay": [P, P, I, I, I, P, P, I, I, P, P, P, P, SZ, P],
             "moe_backward_workspace_size": [I, I, I, I, I, I, PSZ],
+            "moe_nvfp4_quantize": [P, I, I, P, P, P, P],
             "moe_combine_backward": [P, I, P, P, P, I, I, I, I, P, P, P],
             "moe_expert_ffn_backward": [P, P, I, I, I, I, I, I, ctypes.POINTER(_Bank),
                                         ctypes.POINTER(_Bank), P, P, P, P, P, ctypes.POINTER(_GradBank),
@@ -202,13 +204,20 @@ def moe_dispatch(ids, E, ws: Workspace, offsets=None, perm=None, row_of=None):
     return offsets, perm, row_of
 
 
+_BANK_OPT = ("w1_scale", "w3_scale", "w2_scale", "w1_rscale", "w3_rscale", "w2_rscale")
+
+
 def _bank(b):
     if b is None:
         return None
-    _check_dev(b["w1"], b["w3"], b["w2"], b.get("w1_scale"), b.get("w3_scale"), b.get("w2_scale"))
+    _check_dev(b["w1"], b["w3"], b["w2"], *(b.get(n) for n in _BANK_OPT))
     return _Bank(b["w1"].data_ptr(), b["w3"].data_ptr(), b["w2"].data_ptr(),
-                 *(b[n].data_ptr() if b.get(n) is not None else None
-                   for n in ("w1_scale", "w3_scale", "w2_scale")))
+                 *(b[n].data_ptr() if b.get(n) is not None else None for n in _BANK_OPT))
+
+
+def _ffn_dtype(x, routed):
+    """The expert FFN's dtype: NVFP4 when the weights carry row scales (x is bf16)."""
+    return MOE_NVFP4 if routed.get("w1_rscale") is not None else _dtype_of(x)
 
 
 def moe_expert_ffn(x, routed: dict, shared, offsets, perm, k, ws: Workspace, x_scale=None, out=None):
@@ -217,7 +226,7 @@ def moe_expert_ffn(x, routed: dict, shared, offsets, perm, k, ws: Workspace, x_s
     T, d = x.shape
     E = routed["w1"].shape[0]
     inter = routed["w1"].shape[1]
-    dt = _dtype_of(x)
+    dt = _ffn_dtype(x, routed)
     rows = T * k + (T if shared is not None else 0)
     if out is None:
         out = torch.empty(rows, d, dtype=torch.float32 if dt == MOE_F32 else torch.bfloat16,
@@ -235,7 +244,7 @@ def moe_expert_ffn_gate_up(x, routed: dict, shared, offsets, perm, k, ws: Worksp
     T, d = x.shape
     E, inter = routed["w1"].shape[0], routed["w1"].shape[1]
     rb, sb = _bank(routed), _bank(shared)
-    _ok(lib().moe_expert_ffn_gate_up(_ptr(x), _ptr(x_scale), _dtype_of(x), T, d, E, k, inter,
+    _ok(lib().moe_expert_ffn_gate_up(_ptr(x), _ptr(x_scale), _ffn_dtype(x, routed), T, d, E, k, inter,
                                      ctypes.byref(rb), ctypes.byref(sb) if sb is not None else None,
                                      _ptr(offsets), _ptr(perm), ws.ptr, ws.nbytes, _stream(x.device)),
         "moe_expert_ffn_gate_up")
@@ -244,6 +253,8 @@ def moe_expert_ffn_gate_up(x, routed: dict, shared, offsets, perm, k, ws: Worksp
 def moe_expert_ffn_down(dtype, T, d, routed: dict, shared, k, ws: Workspace, out=None):
     """GEMM2 half of moe_expert_ffn, after moe_expert_ffn_gate_up on the same workspace."""
     E, inter = routed["w1"].shape[0], routed["w1"].shape[1]
+    if routed.get("w1_rscale") is not None:
+        dtype = MOE_NVFP4
     rows = T * k + (T if shared is not None else 0)
     dev = routed["w1"].device
     if out is None:
@@ -286,7 +297,8 @@ def layer_forward(inp: dict, k: int, ws: Workspace | None = None, replay: bool =
     inter = inp["w1"].shape[1]
     dt = _dtype_of(x)
     if ws is None:
-        ws = Workspace(T, d, E, k, inter, dt, device=x.device)
+        fdt = MOE_NVFP4 if inp.get("w1_rscale") is not None else dt
+        ws = Workspace(T, d, E, k, inter, fdt, device=x.device)
     if replay:
         ids = inp["ids_in"]
         weights = moe_route_replay(x, inp["w_gate"], inp.get("bias"), ids, ws,
@@ -294,7 +306,7 @@ def layer_forward(inp: dict, k: int, ws: Workspace | None = None, replay: bool =
     else:
         ids, weights = moe_route(x, inp["w_gate"], inp.get("bias"), k, ws, x_scale=inp.get("x_scale"))
     offsets, perm, row_of = moe_dispatch(ids, E, ws)
-    routed = {n: inp.get(n) for n in ("w1", "w3", "w2", "w1_scale", "w3_scale", "w2_scale")}
+    routed = {n: inp.get(n) for n in ("w1", "w3", "w2") + _BANK_OPT}
     out = moe_expert_ffn(x, routed, inp.get("shared"), offsets, perm, k, ws, x_scale=inp.get("x_scale"))
     y = moe_combine(out, row_of, weights, T, inp.get("shared") is not None, dt)
     if check:
@@ -459,3 +471,17 @@ def layer_backward(inp: dict, k: int, fwd: dict, dy, ws: Workspace, replay: bool
             raise MoeError(st, "layer_backward")
     return {"dx": dx, "d_weights": d_weights, "d_w_gate": dwg, "d_bias": db, "grads": grads,
             "shared_grads": sgrads, "dx_rows": dx_rows, "d_out": d_out}
+
+
+def moe_nvfp4_quantize(x, codes=None, block_scales=None, row_scales=None):
+    """NVFP4 rows of a bf16 matrix: (codes [R][K/2] uint8, block scales [R][K/16] uint8,
+    row scales [R] fp32)."""
+    _check_dev(x)
+    R, K = x.shape
+    dev = x.device
+    codes = torch.empty(R, K // 2, dtype=torch.uint8, device=dev) if codes is None else codes
+    block_scales = torch.empty(R, K // 16, dtype=torch.uint8, device=dev) if block_scales is None else block_scales
+    row_scales = torch.empty(R, dtype=torch.float32, device=dev) if row_scales is None else row_scales
+    _ok(lib().moe_nvfp4_quantize(_ptr(x), R, K, _ptr(codes), _ptr(block_scales), _ptr(row_scales),
+                                 _stream(dev)), "moe_nvfp4_quantize")
+    return codes, block_scales, row_scales

@@ -15,7 +15,7 @@ using namespace moe;
 extern "C" moe_status moe_workspace_size(int T, int d, int E, int k, int inter, int dtype,
                                          size_t* bytes) {
   if (!bytes || T < 0 || d < 1 || E < 1 || E > kMaxExperts || k < 1 || k > E || k > kMaxTopK ||
-      inter < 1 || !valid_dtype(dtype))
+      inter < 1 || !valid_layer_dtype(dtype))
     return MOE_ERR_INVALID_ARG;
   *bytes = workspace_bytes(T, d, E, k, inter, dtype);
   return MOE_OK;

@@ -638,7 +638,7 @@ using namespace moe;
 extern "C" moe_status moe_backward_workspace_size(int T, int d, int E, int k, int inter, int dtype,
                                                   size_t* bytes) {
   if (!bytes || T < 0 || d < 1 || E < 1 || E > kMaxExperts || k < 1 || k > E || k > kMaxTopK ||
-      inter < 1 || !valid_dtype(dtype))
+      inter < 1 || !valid_layer_dtype(dtype))
     return MOE_ERR_INVALID_ARG;
   const size_t a = workspace_bytes(T, d, E, k, inter, dtype), b = bwd_ws(T, d, E, k, inter).bytes;
   *bytes = a > b ? a : b;

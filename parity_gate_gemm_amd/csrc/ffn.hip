@@ -1306,6 +1306,10 @@ __global__ __launch_bounds__(256) void grouped_ffn_f32_kernel(F32Args g) {
 
 static bool bank_ok(const moe_expert_bank* b, int dtype) {
   if (!b || !b->w1 || !b->w3 || !b->w2) return false;
+  if (dtype == MOE_NVFP4)
+    return b->w1_scale && b->w3_scale && b->w2_scale && b->w1_rscale && b->w3_rscale && b->w2_rscale &&
+           aligned(b->w1, 8) && aligned(b->w3, 8) && aligned(b->w2, 8);
+  if (b->w1_rscale || b->w3_rscale || b->w2_rscale) return false;
   if (dtype == MOE_MXFP8) return b->w1_scale && b->w3_scale && b->w2_scale;
   if (b->w1_scale || b->w3_scale || b->w2_scale) return false;
   if (dtype == MOE_BF16)
@@ -1322,15 +1326,16 @@ static bool mx_bank_aligned(const moe_expert_bank* b) {
 static moe_status check_ffn_shape(int dtype, int T, int d, int E, int k, int inter,
                                   const moe_expert_bank* routed, const moe_expert_bank* shared,
                                   const void* ws, size_t ws_bytes) {
-  if (!valid_dtype(dtype) || T < 0 || d < 1 || E < 1 || E > kMaxExperts || k < 1 || k > E ||
+  if (!valid_layer_dtype(dtype) || T < 0 || d < 1 || E < 1 || E > kMaxExperts || k < 1 || k > E ||
       k > kMaxTopK || inter < 1)
     return MOE_ERR_INVALID_ARG;
   if (!bank_ok(routed, dtype) || (shared && !bank_ok(shared, dtype))) return MOE_ERR_INVALID_ARG;
   if (!ws) return MOE_ERR_INVALID_ARG;
+  if (dtype == MOE_NVFP4 && (d % 256 != 0 || inter % 128 != 0)) return MOE_ERR_UNSUPPORTED;
   if (dtype == MOE_BF16 && (d % 128 != 0 || inter % 64 != 0)) return MOE_ERR_UNSUPPORTED;
   if (dtype == MOE_MXFP8 && (d % 128 != 0 || inter % 128 != 0)) return MOE_ERR_UNSUPPORTED;
   if ((long long)T * k > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
-  if (ws_bytes < ffn_ws(T, E, k, inter, dtype).bytes) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < ffn_ws(T, d, E, k, inter, dtype).bytes) return MOE_ERR_WORKSPACE;
   return MOE_OK;
 }
 
@@ -1341,6 +1346,8 @@ struct FfnPlan {
   int* rowcount;
   void* h;
   uint8_t* hs;
+  uint8_t *xc, *xs, *hc, *hsc;   // NVFP4 quantized x and h
+  float *xr, *hr;
   int S, has_shared;
   long long Tk, rows, mt_bound;
   int tm;   // rows per GEMM tile (the segment table counts tiles of this height)
@@ -1348,7 +1355,7 @@ struct FfnPlan {
 };
 
 static FfnPlan plan_of(void* ws, int T, int d, int E, int k, int inter, int dtype, bool has_shared) {
-  const FfnWs L = ffn_ws(T, E, k, inter, dtype);
+  const FfnWs L = ffn_ws(T, d, E, k, inter, dtype);
   char* w = (char*)ws;
   FfnPlan p;
   p.flag = (int*)w;
@@ -1357,6 +1364,12 @@ static FfnPlan plan_of(void* ws, int T, int d, int E, int k, int inter, int dtyp
   p.rowcount = p.rowstart + (E + 2);
   p.h = w + L.h;
   p.hs = (uint8_t*)(w + L.hs);
+  p.xc = (uint8_t*)(w + L.xc);
+  p.xs = (uint8_t*)(w + L.xs);
+  p.xr = (float*)(w + L.xr);
+  p.hc = (uint8_t*)(w + L.hc);
+  p.hsc = (uint8_t*)(w + L.hsc);
+  p.hr = (float*)(w + L.hr);
   p.has_shared = has_shared ? 1 : 0;
   p.S = E + p.has_shared;
   p.Tk = (long long)T * k;
@@ -1364,7 +1377,7 @@ static FfnPlan plan_of(void* ws, int T, int d, int E, int k, int inter, int dtyp
   // the ring tiles GEMM2's output by XR_N columns and loads scales 16 bytes (512 K) at a time
   p.mx_ring = MOE_MX_RING && dtype == MOE_MXFP8 && d % XR_N == 0 && d % XR_GB == 0 &&
               inter % XR_GB == 0;
-  p.tm = p.mx_ring ? XR_M : dtype == MOE_MXFP8 ? 64 * MOE_MX_WM : BM;
+  p.tm = p.mx_ring ? XR_M : dtype == MOE_MXFP8 ? 64 * MOE_MX_WM : BM;   // NVFP4: BM as bf16
   p.mt_bound = (p.Tk + (long long)E * (p.tm - 1)) / p.tm + (has_shared ? (T + p.tm - 1) / p.tm : 0);
   return p;
 }
@@ -1409,6 +1422,44 @@ static moe_status run_gate_up(const void* x, const uint8_t* xs, int dtype, int T
                               float* pre = nullptr) {
   seg_table_kernel<<<1, 1024, 0, s>>>(offsets, E, p.Tk, T, p.has_shared, p.tm, p.mstart, p.rowstart,
                                       p.rowcount, p.flag);
+  if (dtype == MOE_NVFP4) {
+    moe_status st = nvfp4_quantize_rows((const uint16_t*)x, T, d, nullptr, nullptr, p.xr, (uint16_t*)p.xc, s);
+    if (st != MOE_OK) return st;
+    Nvfp4Gemm q{};
+    q.a = (const uint16_t*)p.xc;
+    q.ar = p.xr;
+    q.perm = perm;
+    q.T = T;
+    q.k = k;
+    q.E = E;
+    q.b0 = (const uint8_t*)routed->w1;
+    q.b1 = (const uint8_t*)routed->w3;
+    q.b0s = routed->w1_scale;
+    q.b1s = routed->w3_scale;
+    q.b0r = routed->w1_rscale;
+    q.b1r = routed->w3_rscale;
+    if (shared) {
+      q.sb0 = (const uint8_t*)shared->w1;
+      q.sb1 = (const uint8_t*)shared->w3;
+      q.sb0s = shared->w1_scale;
+      q.sb1s = shared->w3_scale;
+      q.sb0r = shared->w1_rscale;
+      q.sb1r = shared->w3_rscale;
+    }
+    q.K = d;
+    q.N = inter;
+    q.mstart = p.mstart;
+    q.rowstart = p.rowstart;
+    q.rowcount = p.rowcount;
+    q.S = p.S;
+    q.mt_bound = p.mt_bound;
+    q.out = (uint16_t*)p.h;
+    q.flag = p.flag;
+    if ((st = nvfp4_gemm(0, q, s)) != MOE_OK) return st;
+    // h per row to NVFP4 for the second GEMM
+    return nvfp4_quantize_rows((const uint16_t*)p.h, p.rows, inter, nullptr, nullptr, p.hr, (uint16_t*)p.hc,
+                               s);
+  }
   if (dtype == MOE_MXFP8) {
     MxArgs g{};
     g.a = (const uint8_t*)x;
@@ -1501,6 +1552,33 @@ static moe_status run_gate_up(const void* x, const uint8_t* xs, int dtype, int T
 static moe_status run_down(int dtype, int T, int d, int E, int k, int inter,
                            const moe_expert_bank* routed, const moe_expert_bank* shared, void* out,
                            const FfnPlan& p, hipStream_t s) {
+  if (dtype == MOE_NVFP4) {
+    Nvfp4Gemm q{};
+    q.a = (const uint16_t*)p.hc;
+    q.ar = p.hr;
+    q.perm = nullptr;
+    q.T = T;
+    q.k = k;
+    q.E = E;
+    q.b0 = (const uint8_t*)routed->w2;
+    q.b0s = routed->w2_scale;
+    q.b0r = routed->w2_rscale;
+    if (shared) {
+      q.sb0 = (const uint8_t*)shared->w2;
+      q.sb0s = shared->w2_scale;
+      q.sb0r = shared->w2_rscale;
+    }
+    q.K = inter;
+    q.N = d;
+    q.mstart = p.mstart;
+    q.rowstart = p.rowstart;
+    q.rowcount = p.rowcount;
+    q.S = p.S;
+    q.mt_bound = p.mt_bound;
+    q.out = (uint16_t*)out;
+    q.flag = p.flag;
+    return nvfp4_gemm(1, q, s);
+  }
   if (dtype == MOE_MXFP8) {
     MxArgs g{};
     g.a = (const uint8_t*)p.h;

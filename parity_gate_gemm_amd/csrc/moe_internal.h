@@ -123,26 +123,37 @@ inline DispatchWs dispatch_ws(int T, int E) {
 inline size_t elem_bytes_h(int dtype) { return dtype == MOE_F32 ? 4 : (dtype == MOE_BF16 ? 2 : 1); }
 
 struct FfnWs {
-  size_t h, hs, seg, bytes;
+  size_t h, hs, seg;
+  size_t xc, xs, xr, hc, hsc, hr;   // NVFP4: quantized x (codes, block scales, row scales) and h
+  size_t bytes;
   long long rows;
 };
-// h: intermediate activations [T*k + T][inter] (fp32 / bf16 / E4M3 codes);
+// h: intermediate activations [T*k + T][inter] (fp32 / bf16 / E4M3 codes; bf16 for NVFP4);
 // hs: E8M0 scales of h [T*k + T][inter/32] (MXFP8 only);
-// seg table: mstart[S+1] (int), rowstart[S] (int), rowcount[S] (int), S = E + 1.
-inline FfnWs ffn_ws(int T, int E, int k, int inter, int dtype) {
+// seg table: mstart[S+1] (int), rowstart[S] (int), rowcount[S] (int), S = E + 1;
+// NVFP4 only: x and h quantized per row to NVFP4, kept as their decoded values
+// E2M1 * E4M3 (exact in bf16; [T][d] and [rows][inter]) and fp32 row scales.
+inline FfnWs ffn_ws(int T, int d, int E, int k, int inter, int dtype) {
   FfnWs w;
   w.rows = (long long)T * k + T;
+  const bool nv = dtype == MOE_NVFP4;
   size_t o = kHeaderBytes;
-  w.h = o;   o = align_up(o + (size_t)w.rows * inter * elem_bytes_h(dtype), 256);
+  w.h = o;   o = align_up(o + (size_t)w.rows * inter * (nv ? 2 : elem_bytes_h(dtype)), 256);
   w.hs = o;  o = align_up(o + (dtype == MOE_MXFP8 ? (size_t)w.rows * (inter / 32) : 0), 256);
   w.seg = o; o = align_up(o + (size_t)(3 * (E + 2)) * sizeof(int), 256);
+  const size_t tn = nv ? (size_t)T : 0, rn = nv ? (size_t)w.rows : 0;
+  w.xc = o;  o = align_up(o + tn * d * 2, 256);           // decoded x (bf16)
+  w.xs = o;  o = align_up(o, 256);
+  w.xr = o;  o = align_up(o + tn * sizeof(float), 256);
+  w.hc = o;  o = align_up(o + rn * inter * 2, 256);       // decoded h (bf16)
+  w.hsc = o; o = align_up(o, 256);
+  w.hr = o;  o = align_up(o + rn * sizeof(float), 256);
   w.bytes = o;
   return w;
 }
 
 inline size_t workspace_bytes(int T, int d, int E, int k, int inter, int dtype) {
-  (void)d;
-  size_t a = route_ws(T, d, E).bytes, b = dispatch_ws(T, E).bytes, c = ffn_ws(T, E, k, inter, dtype).bytes;
+  size_t a = route_ws(T, d, E).bytes, b = dispatch_ws(T, E).bytes, c = ffn_ws(T, d, E, k, inter, dtype).bytes;
   size_t m = a > b ? a : b;
   return m > c ? m : c;
 }
@@ -172,6 +183,8 @@ inline BwdWs bwd_ws(int T, int d, int E, int k, int inter) {
 }
 
 inline bool valid_dtype(int dt) { return dt == MOE_F32 || dt == MOE_BF16 || dt == MOE_MXFP8; }
+// The expert FFN (and the workspace) also takes NVFP4 experts (with bf16 x).
+inline bool valid_layer_dtype(int dt) { return valid_dtype(dt) || dt == MOE_NVFP4; }
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 inline moe_status launch_status() {
@@ -238,7 +251,7 @@ constexpr int kXcds = 8;      // MI355X: 8 XCDs, workgroups dealt round-robin
 template <int CHUNK>
 __device__ __forceinline__ bool xcd_tile(int total, int& tile) {
   const int xcd = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
-  if (CHUNK == 0) {
+  if constexpr (CHUNK == 0) {
     const int per = (total + kXcds - 1) / kXcds;
     if (q >= per) return false;
     tile = xcd * per + q;
@@ -252,6 +265,37 @@ inline long long tile_grid(long long bound, int chunk) {
   const long long g = chunk == 0 ? kXcds : (long long)kXcds * chunk;
   return (bound + g - 1) / g * g;
 }
+// NVFP4 expert FFN (nvfp4.hip).
+struct Nvfp4Gemm {
+  const uint16_t* a;       // A decoded (E2M1 * E4M3, bf16) [rows][K], fp32 row scales
+  const float* ar;
+  const int32_t* perm;     // GEMM1: the A row of output row j is token perm[j] / k
+  int T, k, E;
+  const uint8_t* b0;       // GEMM1: W1 and W3 banks; GEMM2: W2
+  const uint8_t* b1;
+  const uint8_t* b0s;
+  const uint8_t* b1s;
+  const float* b0r;
+  const float* b1r;
+  const uint8_t* sb0;      // shared expert
+  const uint8_t* sb1;
+  const uint8_t* sb0s;
+  const uint8_t* sb1s;
+  const float* sb0r;
+  const float* sb1r;
+  int K, N;
+  const int* mstart;
+  const int* rowstart;
+  const int* rowcount;
+  int S;
+  long long mt_bound;
+  uint16_t* out;
+  int* flag;
+};
+moe_status nvfp4_quantize_rows(const uint16_t* src, long long rows, int K, uint8_t* codes, uint8_t* bscale,
+                               float* rscale, uint16_t* dec, hipStream_t s);
+moe_status nvfp4_gemm(int mode, const Nvfp4Gemm& q, hipStream_t s);
+
 // Backward-pass support from the forward FFN (ffn.hip): the segment table for 128-row
 // tiles into seg (mstart [E + 2], rowstart [E + 2], rowcount [E + 2]) and the GEMM1
 // pre-activations of every dispatched row, pre [rows][2 inter] fp32 (x W1, then x W3),

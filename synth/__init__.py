@@ -14,5 +14,6 @@ from .inputs import (  # noqa: F401
     zipf_replay_ids,
     dirichlet_weights,
     mxfp8_quantize,
+    nvfp4_quantize,
     bf16_round,
 )

@@ -42,7 +42,7 @@ class Workload:
     E: int = 384
     k: int = 8
     shared: bool = False
-    dtype: str = "bf16"          # "f32" | "bf16" | "mxfp8"
+    dtype: str = "bf16"          # "f32" | "bf16" | "mxfp8" | "nvfp4" (bf16 x, NVFP4 experts)
     routing: str = "learned"     # "learned" | "replay"
     bias: bool = False
     seed: int = 0
@@ -62,6 +62,9 @@ WORKLOADS = {
                                  dtype="bf16", seed=3),
     "mxfp8_t32768": Workload("mxfp8_t32768", T=32768, d=7168, inter=2048, shared=True,
                              dtype="mxfp8", bias=True, seed=4),
+    # the bf16 T = 4096 layer with NVFP4 experts (the pages' forward format)
+    "nvfp4_t4096": Workload("nvfp4_t4096", T=4096, d=7168, inter=2048, shared=True,
+                            dtype="nvfp4", seed=5),
 }
 
 
@@ -142,6 +145,55 @@ def mxfp8_quantize(v: torch.Tensor):
     return codes, scales
 
 
+E2M1_MIDS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)   # midpoints of 0, .5, 1, 1.5, 2, 3, 4, 6
+NV_BLOCK = 16
+
+
+def _e2m1_rne_codes(q: torch.Tensor) -> torch.Tensor:
+    """fp32 values -> FP4 E2M1 codes (sign bit 3), nearest, ties to the even code,
+    saturating at 6."""
+    a = q.abs().clamp(max=6.0)
+    mids = torch.tensor(E2M1_MIDS, dtype=torch.float32, device=q.device)
+    idx = torch.bucketize(a, mids)                       # first midpoint >= a
+    tie = (idx < len(E2M1_MIDS)) & (a == mids[idx.clamp(max=len(E2M1_MIDS) - 1)])
+    idx = torch.where(tie & (idx % 2 == 1), idx + 1, idx)
+    sign = torch.signbit(q).to(torch.int64)
+    return (idx | (sign << 3)).to(torch.uint8)
+
+
+def nvfp4_quantize(v: torch.Tensor):
+    """Quantise fp32 ``v[..., K]`` (K % 16 == 0) to NVFP4 along the last dim: row scale
+    s = amax / 2688 (fp32), block scale E4M3_RNE((bamax / s) / 6) per 16, elements
+    E2M1_RNE(v / (S s)).  Returns (codes packed two per byte, element 2i in the low
+    nibble [..., K/2] uint8, block scales [..., K/16] uint8 E4M3, row scales [...] fp32)."""
+    assert v.shape[-1] % NV_BLOCK == 0
+    shp = v.shape
+    v = v.to(torch.float32)
+    blocks = v.reshape(*shp[:-1], shp[-1] // NV_BLOCK, NV_BLOCK)
+    amax = v.abs().amax(dim=-1)
+    s = torch.where(amax > 0, amax / 2688.0, torch.zeros_like(amax))
+    bamax = blocks.abs().amax(dim=-1)
+    safe = torch.where(s > 0, s, torch.ones_like(s)).unsqueeze(-1)
+    t = torch.where(s.unsqueeze(-1) > 0, bamax / safe, torch.zeros_like(bamax))
+    sb = _e4m3_rne_codes((t / 6.0).clamp(max=E4M3_MAX))
+    sbv = _e4m3_values(sb)
+    den = sbv * s.unsqueeze(-1)
+    q = blocks / torch.where(den > 0, den, torch.ones_like(den)).unsqueeze(-1)
+    codes = torch.where(den.unsqueeze(-1) > 0, _e2m1_rne_codes(q), torch.zeros_like(q, dtype=torch.uint8))
+    codes = codes.reshape(*shp[:-1], shp[-1])
+    packed = codes[..., 0::2] | (codes[..., 1::2] << 4)
+    return packed.contiguous(), sb.contiguous(), s.contiguous()
+
+
+def _e4m3_values(c: torch.Tensor) -> torch.Tensor:
+    """E4M3 codes (non-negative, finite) -> fp32 values."""
+    c = c.to(torch.int64)
+    e, m = (c >> 3) & 15, c & 7
+    sub = m.to(torch.float32) * 2.0 ** -9
+    nor = (1.0 + m.to(torch.float32) / 8.0) * torch.pow(2.0, (e - 7).to(torch.float32))
+    return torch.where(e == 0, sub, nor)
+
+
 # ---------------------------------------------------------------------------
 # Replayed routing for the router-replay workload
 # ---------------------------------------------------------------------------
@@ -173,6 +225,8 @@ def _store(v: torch.Tensor, dtype: str):
         return bf16_round(v).contiguous(), None
     if dtype == "mxfp8":
         return mxfp8_quantize(v)
+    if dtype == "nvfp4":
+        return nvfp4_quantize(v)
     raise ValueError(dtype)
 
 
@@ -190,7 +244,7 @@ def _draw_gate(wl: Workload, device: str, draw_device: str | None):
         return t
 
     out = {}
-    x, xs = _store(randn(wl.T, wl.d), wl.dtype)
+    x, xs = _store(randn(wl.T, wl.d), "bf16" if wl.dtype == "nvfp4" else wl.dtype)   # NVFP4 layers take bf16 x
     out["x"], out["x_scale"] = x.to(device), (xs.to(device) if xs is not None else None)
     out["w_gate"] = randn(wl.d, wl.E, std=1.0 / math.sqrt(wl.d)).to(device)
     out["bias"] = randn(wl.E, std=math.sqrt(0.5)).to(device) if wl.bias else None
@@ -216,13 +270,21 @@ def make_layer_inputs(wl: Workload, device: str = "cpu", draw_device: str | None
     out, randn = _draw_gate(wl, device, draw_device)
     T, d, I, E = wl.T, wl.d, wl.inter, wl.E
 
-    elt = {"f32": torch.float32, "bf16": torch.bfloat16, "mxfp8": torch.uint8}[wl.dtype]
+    elt = {"f32": torch.float32, "bf16": torch.bfloat16, "mxfp8": torch.uint8, "nvfp4": torch.uint8}[wl.dtype]
+    pk = 2 if wl.dtype == "nvfp4" else 1      # NVFP4: two codes per byte
 
     def bank(n):
-        t = {"w1": torch.empty(n, I, d, dtype=elt, device=device),
-             "w3": torch.empty(n, I, d, dtype=elt, device=device),
-             "w2": torch.empty(n, d, I, dtype=elt, device=device)}
-        if wl.dtype == "mxfp8":
+        t = {"w1": torch.empty(n, I, d // pk, dtype=elt, device=device),
+             "w3": torch.empty(n, I, d // pk, dtype=elt, device=device),
+             "w2": torch.empty(n, d, I // pk, dtype=elt, device=device)}
+        if wl.dtype == "nvfp4":
+            t["w1_scale"] = torch.empty(n, I, d // NV_BLOCK, dtype=torch.uint8, device=device)
+            t["w3_scale"] = torch.empty(n, I, d // NV_BLOCK, dtype=torch.uint8, device=device)
+            t["w2_scale"] = torch.empty(n, d, I // NV_BLOCK, dtype=torch.uint8, device=device)
+            t["w1_rscale"] = torch.empty(n, I, dtype=torch.float32, device=device)
+            t["w3_rscale"] = torch.empty(n, I, dtype=torch.float32, device=device)
+            t["w2_rscale"] = torch.empty(n, d, dtype=torch.float32, device=device)
+        elif wl.dtype == "mxfp8":
             t["w1_scale"] = torch.empty(n, I, d // MX_BLOCK, dtype=torch.uint8, device=device)
             t["w3_scale"] = torch.empty(n, I, d // MX_BLOCK, dtype=torch.uint8, device=device)
             t["w2_scale"] = torch.empty(n, d, I // MX_BLOCK, dtype=torch.uint8, device=device)
@@ -232,10 +294,12 @@ def make_layer_inputs(wl: Workload, device: str = "cpu", draw_device: str | None
 
     def fill(b, e):
         for name, shape, fan in (("w1", (I, d), d), ("w3", (I, d), d), ("w2", (d, I), I)):
-            v, s = _store(randn(*shape, std=1.0 / math.sqrt(fan)), wl.dtype)
-            b[name][e].copy_(v)
-            if s is not None:
-                b[name + "_scale"][e].copy_(s)
+            st = _store(randn(*shape, std=1.0 / math.sqrt(fan)), wl.dtype)
+            b[name][e].copy_(st[0])
+            if st[1] is not None:
+                b[name + "_scale"][e].copy_(st[1])
+            if len(st) > 2:
+                b[name + "_rscale"][e].copy_(st[2])
 
     routed = bank(E)
     for e in range(E):

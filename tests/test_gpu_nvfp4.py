@@ -1,0 +1,108 @@
+"""GPU parity of the NVFP4 forward (E2M1 values, an E4M3 scale per 16, an fp32 scale per
+row; the expert FFN quantizes x per token and h per row) against the oracle.
+
+The quantizer is compared bit for bit (codes, block scales, row scales) on rows built to
+hit every rounding case: zeros, zero blocks, exact ties of the E2M1 grid, saturation,
+values near the E4M3 subnormal range.  The layer output is compared normwise: the GPU's
+h (fp32 accumulation) can round to bf16, and then to E2M1, differently from the oracle's
+exact h at a few rounding boundaries, which the bar covers.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity_gate_gemm_amd as pg
+import synth
+from _gpu_common import host, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+BAR = 2e-2
+
+
+def _unpack(packed):
+    p = packed.cpu().numpy()
+    return np.stack([p & 15, p >> 4], axis=-1).reshape(p.shape[0], -1)
+
+
+def _check_quant(x):
+    c, sb, s = pg.moe_nvfp4_quantize(x)
+    rc, rsb, rs = oracle.nvfp4_quantize(x.float().cpu().numpy())
+    assert np.array_equal(s.cpu().numpy(), rs), "row scales"
+    assert np.array_equal(sb.cpu().numpy(), rsb), "block scales"
+    got = _unpack(c)
+    bad = np.argwhere(got != rc)
+    assert bad.size == 0, (bad[:5], got[tuple(bad[0])], rc[tuple(bad[0])])
+
+
+def test_nvfp4_quantizer_bit_exact():
+    g = torch.Generator().manual_seed(1)
+    for R, K, scale in [(64, 256, 1.0), (33, 7168, 3.0), (17, 2048, 1e-3), (8, 16, 1e4)]:
+        say(f"case nvfp4 quantize {R}x{K} scale {scale}")
+        x = (torch.randn(R, K, generator=g) * scale).to(torch.bfloat16)
+        x[0] = 0                                    # zero row
+        x[1, :16] = 0                               # zero block
+        if K >= 64:
+            # a row whose block maxima sit on the E2M1 grid times 448 s, and exact ties
+            row = torch.tensor([6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0] * (K // 8))
+            x[2] = row.to(torch.bfloat16)
+            x[3] = (row * -1.0).to(torch.bfloat16)
+        _check_quant(x.cuda())
+
+
+def _oracle_experts(inp):
+    def mats(b, e):
+        out = []
+        for n in ("w1", "w3", "w2"):
+            c = b[n][e] if e is not None else b[n]
+            sc = b[n + "_scale"][e] if e is not None else b[n + "_scale"]
+            rs = b[n + "_rscale"][e] if e is not None else b[n + "_rscale"]
+            out.append((_unpack(c), sc.cpu().numpy(), rs.cpu().numpy()))
+        return tuple(out)
+
+    class Lazy:
+        def __getitem__(self, e):
+            return mats(inp, e)
+
+    sh = inp.get("shared")
+    return Lazy(), (mats(sh, None) if sh is not None else None)
+
+
+def _compare(res, inp, rows, k):
+    experts, shared = _oracle_experts(inp)
+    x = host(inp["x"])[rows]
+    ref = oracle.layer_nvfp4(x, host(inp["w_gate"]), host(inp.get("bias")), experts, shared, k)
+    assert np.array_equal(res["ids"].cpu().numpy()[rows], ref["ids"])
+    err = oracle.normwise_rel_err(host(res["y"])[rows], ref["y"])
+    say(f"  normwise err {err:.3e}")
+    assert err <= BAR
+    return err
+
+
+SMALL = [(100, 256, 128, 8, 2, True), (300, 512, 256, 16, 4, False), (1, 256, 128, 4, 1, True)]
+
+
+@pytest.mark.parametrize("T,d,I,E,k,shared", SMALL)
+def test_nvfp4_layer_small(T, d, I, E, k, shared):
+    wl = synth.Workload("nv", T=T, d=d, inter=I, E=E, k=k, shared=shared, dtype="nvfp4", seed=3)
+    inp = to_device(synth.make_layer_inputs(wl, device="cpu"))
+    say(f"case nvfp4 layer T={T} d={d} I={I} E={E} k={k}")
+    res = pg.layer_forward(inp, k)
+    _compare(res, inp, np.arange(T), k)
+
+
+def test_nvfp4_layer_fullsize_sampled():
+    wl = synth.WORKLOADS["nvfp4_t4096"]
+    say("drawing nvfp4_t4096 inputs on the GPU")
+    inp = synth.make_layer_inputs(wl, device="cuda")
+    res = pg.layer_forward(inp, wl.k)
+    rng = np.random.default_rng(4)
+    rows = np.array(sorted(set(rng.integers(0, wl.T, 3).tolist()) | {wl.T - 1}))
+    say(f"case nvfp4_t4096 rows {rows.tolist()}")
+    _compare(res, inp, rows, wl.k)
+    # bitwise repeatable
+    res2 = pg.layer_forward(inp, wl.k)
+    assert torch.equal(res2["y"], res["y"])
+    del inp, res, res2
+    torch.cuda.empty_cache()

@@ -101,8 +101,11 @@ def main():
         sys.exit(2)
     ws = pg.BackwardWorkspace(T, d, E, k, I, dt) if bwd else pg.Workspace(T, d, E, k, I, dt)
     x, wg, bias = inp["x"], inp["w_gate"], inp["bias"]
-    routed = {n: inp.get(n) for n in ("w1", "w3", "w2") + pg._BANK_OPT}
-    shared = inp["shared"]
+    # NVFP4 banks run K-blocked (packed once here, outside the timed region); the oracle
+    # baseline reads the row-major form in `inp`
+    run_inp = pg.nvfp4_pack_inputs(inp) if wl.dtype == "nvfp4" else inp
+    routed = {n: run_inp.get(n) for n in ("w1", "w3", "w2") + pg._BANK_OPT}
+    shared = run_inp["shared"]
     rows = T * k + (T if has_shared else 0)
     odt = torch.float32 if dt == pg.MOE_F32 else torch.bfloat16
     ids = inp["ids_in"] if replay and filt is None else torch.empty(T, k, dtype=torch.int32, device=dev)

@@ -81,10 +81,12 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2, MOE_NVFP4 = 3 } moe_dty
 
 /* One bank of SwiGLU experts (n experts stored back to back; see layout above).
  * The *_scale pointers are the E8M0 scales for MOE_MXFP8 ([n][I][d/32] for w1/w3,
- * [n][d][I/32] for w2), the E4M3 block scales for MOE_NVFP4 ([n][I][d/16] for w1/w3,
- * [n][d][I/16] for w2), and must be NULL for the other dtypes.  MOE_NVFP4 weights are
- * E2M1 codes packed two per byte (element 2i in the low nibble: w1, w3 [n][I][d/2],
- * w2 [n][d][I/2]) with one fp32 scale per row in *_rscale ([n][I], [n][I], [n][d]). */
+ * [n][d][I/32] for w2), the E4M3 block scales for MOE_NVFP4, and must be NULL for the
+ * other dtypes.  MOE_NVFP4 weights are E2M1 codes two per byte (element 2i in the low
+ * nibble) with one E4M3 scale per 16 elements of a row and one fp32 scale per row in
+ * *_rscale ([n][I], [n][I], [n][d]); codes and block scales are K-blocked, as
+ * moe_nvfp4_pack_weights writes them from the row-major form (codes [R][K/2], scales
+ * [R][K/16] per matrix of R rows: I rows of d for w1/w3, d rows of I for w2). */
 typedef struct {
   const void* w1;
   const void* w3;
@@ -207,10 +209,15 @@ moe_status moe_dispatch(const int32_t* ids, int T, int E, int k,
  * For MOE_MXFP8 the intermediate h is requantised to MXFP8 per row (one E8M0
  * scale per 32 columns, E4M3 elements rounded to nearest even and saturated at
  * +-448) before the W2 GEMM, so it is consumed by the same block-scaled MFMA.
+ * For MOE_NVFP4, x is quantized per token and h per row to NVFP4 (the quantizer of
+ * moe_nvfp4_quantize) before their GEMMs; both GEMMs run on the decoded values (E2M1
+ * times E4M3, exact in fp16) with fp32 accumulation, and the two operands' fp32 row
+ * scales multiply the accumulator.
  * MOE_ERR_UNSUPPORTED: MOE_BF16 needs d % 128 == 0 and inter % 64 == 0;
- * MOE_MXFP8 needs d % 128 == 0 and inter % 128 == 0.
- * MOE_ERR_INVALID_ARG: x or a weight pointer not 16-byte aligned (bf16, MXFP8),
- * or an MXFP8 scale pointer not 4-byte aligned. */
+ * MOE_MXFP8 needs d % 128 == 0 and inter % 128 == 0; MOE_NVFP4 needs d % 256 == 0 and
+ * inter % 128 == 0.
+ * MOE_ERR_INVALID_ARG: x or a weight pointer not 16-byte aligned (bf16, MXFP8,
+ * NVFP4), or an MXFP8 or NVFP4 scale pointer not 4-byte aligned. */
 moe_status moe_expert_ffn(const void* x, const uint8_t* x_scale, int dtype, int T, int d,
                           int E, int k, int inter,
                           const moe_expert_bank* routed, const moe_expert_bank* shared,
@@ -271,6 +278,17 @@ moe_status moe_expert_ffn_gate_up_save(const void* x, const uint8_t* x_scale, in
  * (E4M3 codes), row_scales out fp32 [rows].  src 16-byte aligned. */
 moe_status moe_nvfp4_quantize(const void* src, int rows, int K, uint8_t* codes,
                               uint8_t* block_scales, float* row_scales, void* stream);
+
+/* K-blocking of n NVFP4 weight matrices of R rows x K columns (R % 32 == 0,
+ * K % 64 == 0), the layout moe_expert_bank takes for MOE_NVFP4: from row-major codes
+ * [n][R][K/2] and block scales [n][R][K/16] to packed_codes [n][R/32][K/64][32][32]
+ * (tile of rows 32 g .. 32 g + 31 and columns 64 s .. 64 s + 63: row r's 32 code bytes,
+ * unchanged, at 32 r) and packed_scales [n][R/32][K/64][32][4] (row r's 4 block scales
+ * at 4 r).  A pure permutation of bytes; same sizes as the inputs.  codes and
+ * packed_codes 16-byte aligned, the scales 4-byte aligned, outputs must not overlap the
+ * inputs or each other (MOE_ERR_INVALID_ARG). */
+moe_status moe_nvfp4_pack_weights(const uint8_t* codes, const uint8_t* block_scales, int n, int R, int K,
+                                  uint8_t* packed_codes, uint8_t* packed_scales, void* stream);
 
 /* Gradients of one expert bank, fp32, in the bank's layout: dw1, dw3 [n][I][d],
  * dw2 [n][d][I]; 16-byte aligned. */

@@ -13,7 +13,8 @@ import os
 import torch
 
 __all__ = [
-    "MOE_F32", "MOE_BF16", "MOE_MXFP8", "MOE_NVFP4", "MoeError", "moe_nvfp4_quantize", "lib", "Workspace",
+    "MOE_F32", "MOE_BF16", "MOE_MXFP8", "MOE_NVFP4", "MoeError", "moe_nvfp4_quantize",
+    "moe_nvfp4_pack_weights", "nvfp4_pack_inputs", "lib", "Workspace",
     "moe_workspace_size", "moe_workspace_init", "moe_route", "moe_route_replay",
     "moe_route_replay_filtered",
     "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_gate_up", "moe_expert_ffn_down", "moe_combine", "moe_check", "moe_status_string",
@@ -61,6 +62,7 @@ def lib():
             "moe_route_replay": [P, P, I, I, I, P, P, I, I, P, P, P, P, SZ, P],
             "moe_backward_workspace_size": [I, I, I, I, I, I, PSZ],
             "moe_nvfp4_quantize": [P, I, I, P, P, P, P],
+            "moe_nvfp4_pack_weights": [P, P, I, I, I, P, P, P],
             "moe_combine_backward": [P, I, P, P, P, I, I, I, I, P, P, P],
             "moe_expert_ffn_backward": [P, P, I, I, I, I, I, I, ctypes.POINTER(_Bank),
                                         ctypes.POINTER(_Bank), P, P, P, P, P, ctypes.POINTER(_GradBank),
@@ -471,6 +473,41 @@ def layer_backward(inp: dict, k: int, fwd: dict, dy, ws: Workspace, replay: bool
             raise MoeError(st, "layer_backward")
     return {"dx": dx, "d_weights": d_weights, "d_w_gate": dwg, "d_bias": db, "grads": grads,
             "shared_grads": sgrads, "dx_rows": dx_rows, "d_out": d_out}
+
+
+def moe_nvfp4_pack_weights(codes, block_scales):
+    """K-blocked copy of NVFP4 weight matrices: codes [n][R][K/2] and block scales
+    [n][R][K/16] (or one matrix without the leading n) -> (packed codes, packed scales),
+    the layout an NVFP4 expert bank takes."""
+    _check_dev(codes, block_scales)
+    shape = codes.shape
+    c = codes.reshape(-1, shape[-2], shape[-1]).contiguous()
+    sc = block_scales.reshape(-1, shape[-2], block_scales.shape[-1]).contiguous()
+    n, R, K = c.shape[0], c.shape[1], c.shape[2] * 2
+    if sc.shape != (n, R, K // 16):
+        raise ValueError(f"block scales {tuple(block_scales.shape)} do not match codes {tuple(shape)}")
+    pc, ps = torch.empty_like(c), torch.empty_like(sc)
+    _ok(lib().moe_nvfp4_pack_weights(_ptr(c), _ptr(sc), n, R, K, _ptr(pc), _ptr(ps), _stream(c.device)),
+        "moe_nvfp4_pack_weights")
+    return pc.reshape(shape), ps.reshape(block_scales.shape)
+
+
+def nvfp4_pack_inputs(inp):
+    """A copy of a layer's input dict whose NVFP4 expert weights (row-major codes and
+    block scales, routed and shared) are K-blocked for the expert FFN."""
+    out = dict(inp)
+
+    def pack(b):
+        b = dict(b)
+        for n in ("w1", "w3", "w2"):
+            b[n], b[n + "_scale"] = moe_nvfp4_pack_weights(b[n], b[n + "_scale"])
+        return b
+
+    out.update({kk: vv for kk, vv in pack({n: inp[n] for n in ("w1", "w3", "w2", "w1_scale", "w3_scale",
+                                                               "w2_scale")}).items()})
+    if inp.get("shared") is not None:
+        out["shared"] = pack(inp["shared"])
+    return out
 
 
 def moe_nvfp4_quantize(x, codes=None, block_scales=None, row_scales=None):

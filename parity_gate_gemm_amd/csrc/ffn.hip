@@ -1308,7 +1308,9 @@ static bool bank_ok(const moe_expert_bank* b, int dtype) {
   if (!b || !b->w1 || !b->w3 || !b->w2) return false;
   if (dtype == MOE_NVFP4)
     return b->w1_scale && b->w3_scale && b->w2_scale && b->w1_rscale && b->w3_rscale && b->w2_rscale &&
-           aligned(b->w1, 8) && aligned(b->w3, 8) && aligned(b->w2, 8);
+           aligned(b->w1, 16) && aligned(b->w3, 16) && aligned(b->w2, 16) && aligned(b->w1_scale, 4) &&
+           aligned(b->w3_scale, 4) && aligned(b->w2_scale, 4) && aligned(b->w1_rscale, 4) &&
+           aligned(b->w3_rscale, 4) && aligned(b->w2_rscale, 4);
   if (b->w1_rscale || b->w3_rscale || b->w2_rscale) return false;
   if (dtype == MOE_MXFP8) return b->w1_scale && b->w3_scale && b->w2_scale;
   if (b->w1_scale || b->w3_scale || b->w2_scale) return false;

@@ -128,3 +128,24 @@ def test_dispatch_ffn_combine_host_validation(L):
     assert n.value >= pg.moe_workspace_size(4096, 7168, 384, 8, 2048, 1)
     assert L.moe_check(None, 0, None) == 1
     assert L.moe_workspace_init(None, 0, None) == 1
+
+
+def test_nvfp4_host_validation(L):
+    P = FAKE
+    A = ctypes.c_void_p(0x20000)          # a second, disjoint fake range
+    # quantizer: bad K, nulls, misalignment; rows == 0 is a no-op
+    assert L.moe_nvfp4_quantize(P, 4, 24, P, P, P, None) == 1
+    assert L.moe_nvfp4_quantize(P, 4, 32, None, P, P, None) == 1
+    assert L.moe_nvfp4_quantize(ctypes.c_void_p(0x10008), 4, 32, A, P, P, None) == 1
+    assert L.moe_nvfp4_quantize(None, 0, 32, None, None, None, None) == 0
+    # K-blocking: R % 32, K % 64, nulls, alignment, overlap; empty is a no-op
+    big = ctypes.c_void_p(0x100000)
+    assert L.moe_nvfp4_pack_weights(P, A, 1, 48, 64, big, ctypes.c_void_p(0x200000), None) == 1
+    assert L.moe_nvfp4_pack_weights(P, A, 1, 32, 96, big, ctypes.c_void_p(0x200000), None) == 1
+    assert L.moe_nvfp4_pack_weights(P, None, 1, 32, 64, big, ctypes.c_void_p(0x200000), None) == 1
+    assert L.moe_nvfp4_pack_weights(ctypes.c_void_p(0x10004), A, 1, 32, 64, big,
+                                    ctypes.c_void_p(0x200000), None) == 1
+    assert L.moe_nvfp4_pack_weights(P, A, 1, 32, 64, P, ctypes.c_void_p(0x200000), None) == 1   # in place
+    assert L.moe_nvfp4_pack_weights(P, A, 1, 32, 64, big, big, None) == 1                     # outputs overlap
+    assert L.moe_nvfp4_pack_weights(None, None, 0, 32, 64, None, None, None) == 0
+    assert L.moe_nvfp4_pack_weights(P, A, -1, 32, 64, big, big, None) == 1

@@ -51,6 +51,26 @@ def test_nvfp4_quantizer_bit_exact():
         _check_quant(x.cuda())
 
 
+def _pack_ref(codes, scales):
+    """The K-blocked layout by reshaping: tiles of 32 rows x 64 columns, row-major inside."""
+    n, R, K2 = codes.shape
+    c = codes.reshape(n, R // 32, 32, K2 // 32, 32).transpose(0, 1, 3, 2, 4)
+    s = scales.reshape(n, R // 32, 32, K2 // 32, 4).transpose(0, 1, 3, 2, 4)
+    return np.ascontiguousarray(c).reshape(n, R, K2), np.ascontiguousarray(s).reshape(n, R, K2 // 8)
+
+
+@pytest.mark.parametrize("n,R,K", [(1, 32, 64), (3, 96, 192), (2, 2048, 7168 // 4)])
+def test_nvfp4_pack_weights_bit_exact(n, R, K):
+    say(f"case nvfp4 pack n={n} R={R} K={K}")
+    g = torch.Generator().manual_seed(n * 7 + R)
+    codes = torch.randint(0, 256, (n, R, K // 2), generator=g, dtype=torch.uint8)
+    scales = torch.randint(0, 256, (n, R, K // 16), generator=g, dtype=torch.uint8)
+    pc, ps = pg.moe_nvfp4_pack_weights(codes.cuda(), scales.cuda())
+    rc, rs = _pack_ref(codes.numpy(), scales.numpy())
+    assert np.array_equal(pc.cpu().numpy(), rc)
+    assert np.array_equal(ps.cpu().numpy(), rs)
+
+
 def _oracle_experts(inp):
     def mats(b, e):
         out = []
@@ -88,7 +108,7 @@ def test_nvfp4_layer_small(T, d, I, E, k, shared):
     wl = synth.Workload("nv", T=T, d=d, inter=I, E=E, k=k, shared=shared, dtype="nvfp4", seed=3)
     inp = to_device(synth.make_layer_inputs(wl, device="cpu"))
     say(f"case nvfp4 layer T={T} d={d} I={I} E={E} k={k}")
-    res = pg.layer_forward(inp, k)
+    res = pg.layer_forward(pg.nvfp4_pack_inputs(inp), k)
     _compare(res, inp, np.arange(T), k)
 
 
@@ -96,13 +116,14 @@ def test_nvfp4_layer_fullsize_sampled():
     wl = synth.WORKLOADS["nvfp4_t4096"]
     say("drawing nvfp4_t4096 inputs on the GPU")
     inp = synth.make_layer_inputs(wl, device="cuda")
-    res = pg.layer_forward(inp, wl.k)
+    packed = pg.nvfp4_pack_inputs(inp)
+    res = pg.layer_forward(packed, wl.k)
     rng = np.random.default_rng(4)
     rows = np.array(sorted(set(rng.integers(0, wl.T, 3).tolist()) | {wl.T - 1}))
     say(f"case nvfp4_t4096 rows {rows.tolist()}")
     _compare(res, inp, rows, wl.k)
     # bitwise repeatable
-    res2 = pg.layer_forward(inp, wl.k)
+    res2 = pg.layer_forward(packed, wl.k)
     assert torch.equal(res2["y"], res["y"])
-    del inp, res, res2
+    del inp, packed, res, res2
     torch.cuda.empty_cache()

@@ -332,7 +332,7 @@ def measured_traffic(workload):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = open(os.path.join(ROOT, "parity_gate_gemm_amd", "csrc", "ffn.hip"), "rb").read()
+    src = open(os.path.join(ROOT, "parity_gate_gemm_amd", "csrc", rec.get("kernel_source", "ffn.hip")), "rb").read()
     if hashlib.sha256(src).hexdigest() != rec["ffn_source_sha256"]:
         return None
     return rec["fetch_bytes"] + rec["write_bytes"]

@@ -525,7 +525,8 @@ def nvfp4_dequant(codes, block_scales, row_scales) -> np.ndarray:
 
 
 def bf16_rne(v) -> np.ndarray:
-    """float64 -> the nearest bf16 value (ties to even), returned as float64."""
+    """float64 -> float32 (nearest, ties to even) -> bf16 (nearest, ties to even), returned
+    as float64: the bf16 rounding of the value's fp32 rounding, as for an h computed in fp32."""
     f = np.asarray(v, dtype=np.float64).astype(np.float32)   # fp64 -> fp32 RNE
     u = f.view(np.uint32).astype(np.uint64)
     u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000

@@ -1457,10 +1457,7 @@ static moe_status run_gate_up(const void* x, const uint8_t* xs, int dtype, int T
     q.mt_bound = p.mt_bound;
     q.out = (uint16_t*)p.h;
     q.flag = p.flag;
-    if ((st = nvfp4_gemm(0, q, s)) != MOE_OK) return st;
-    // h per row to NVFP4 for the second GEMM
-    return nvfp4_quantize_rows((const uint16_t*)p.h, p.rows, inter, nullptr, nullptr, p.hr, (uint16_t*)p.hc,
-                               s);
+    return nvfp4_gemm(0, q, s);   // h (bf16) is quantized by the GEMM2 half
   }
   if (dtype == MOE_MXFP8) {
     MxArgs g{};
@@ -1555,6 +1552,10 @@ static moe_status run_down(int dtype, int T, int d, int E, int k, int inter,
                            const moe_expert_bank* routed, const moe_expert_bank* shared, void* out,
                            const FfnPlan& p, hipStream_t s) {
   if (dtype == MOE_NVFP4) {
+    // h per row to NVFP4 (decoded values and row scales) for the second GEMM
+    const moe_status st =
+        nvfp4_quantize_rows((const uint16_t*)p.h, p.rows, inter, nullptr, nullptr, p.hr, (uint16_t*)p.hc, s);
+    if (st != MOE_OK) return st;
     Nvfp4Gemm q{};
     q.a = (const uint16_t*)p.hc;
     q.ar = p.hr;

@@ -675,3 +675,40 @@ def test_nvfp4_requantize_is_identity_and_layer_plumbing():
     res = oracle.layer_nvfp4(x, wg, None, [tuple(mats)] * E, None, k)
     ref = oracle.expert_ffn_nvfp4(x, *mats)
     assert np.allclose(res["y"], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_nvfp4_expert_ffn_closed_form():
+    """A case whose every step has a closed form.  Token t is c_t e_{j_t}; W1 holds one 2 per
+    column (hidden unit pi(j) of input j), W3 is all ones, so a = 2 xq_t at unit pi(j_t) and
+    0 elsewhere and g = xq_t at every unit: h has one nonzero per row, silu(2 xq) xq.  A row
+    with a single nonzero v quantizes to code 6 under block scale 448, i.e. to
+    sign(v) 2688 fl32(|v| / 2688).  So y[t, o] = Q(bf16(silu(2 xq) xq)) W2[o, pi(j_t)] with
+    xq = Q(c_t).  (d = I, so a transposed W2 would go unnoticed by shapes alone.)"""
+    import torch
+    d = I = 32
+    rng = np.random.default_rng(45)
+    pi = rng.permutation(I)
+    one = 0x38                                        # E4M3 code of 1.0
+    code_of = {0.0: 0, 1.0: 2, 2.0: 4, 6.0: 7}        # E2M1 magnitudes -> codes
+    w1c = np.zeros((I, d), np.uint8)
+    w1c[pi, np.arange(d)] = code_of[2.0]              # W1[pi(j), j] = 2
+    w1 = (w1c, np.full((I, d // 16), one, np.uint8), np.ones(I, np.float32))
+    w3 = (np.full((I, d), code_of[1.0], np.uint8), np.full((I, d // 16), one, np.uint8), np.ones(I, np.float32))
+    w2 = (rng.integers(0, 16, (d, I)).astype(np.uint8), rng.integers(0x20, 0x48, (d, I // 16)).astype(np.uint8),
+          rng.uniform(0.5, 2.0, d).astype(np.float32))
+    W2 = oracle.nvfp4_dequant(*w2)
+
+    def q1(v):                                        # NVFP4 value of a row's only nonzero
+        return np.sign(v) * 2688.0 * float(np.float32(abs(v)) / np.float32(2688.0))
+
+    cs = [1.0, -0.75, 2.5, 0.3125, -3.0, 0.0390625]
+    js = rng.integers(0, d, len(cs))
+    x = np.zeros((len(cs), d), np.float32)
+    x[np.arange(len(cs)), js] = cs
+    y = oracle.expert_ffn_nvfp4(x, w1, w3, w2)
+    for t, (c, j) in enumerate(zip(cs, js)):
+        xq = q1(c)
+        h = (2 * xq) / (1 + np.exp(-2 * xq)) * xq
+        hb = float(torch.tensor(h, dtype=torch.float64).float().bfloat16().double())
+        ref = q1(hb) * W2[:, pi[j]]
+        assert np.allclose(y[t], ref, rtol=1e-13, atol=0), t

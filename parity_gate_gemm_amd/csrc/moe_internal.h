@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <math.h>
 
 #include "../../include/moe.h"
 
@@ -241,6 +242,14 @@ __device__ __forceinline__ double load_act_f64(const void* x, const uint8_t* xs,
 // ---------------------------------------------------------------------------
 constexpr int kXcds = 8;      // MI355X: 8 XCDs, workgroups dealt round-robin
 
+// Row tiles per raster group of the grouped GEMMs: within a group, consecutive tiles
+// share a weight slab (column tile) and the group's activation rows are reused by every
+// column tile.
+#ifndef MOE_GEMM_GROUP_M
+#define MOE_GEMM_GROUP_M 8
+#endif
+constexpr int kGroupM = MOE_GEMM_GROUP_M;
+
 // Tile of this workgroup.  Workgroup b runs on XCD b % 8.  With CHUNK == 0, XCD x takes
 // the x-th eighth of the tile list; otherwise the list is cut into chunks of CHUNK tiles
 // dealt round-robin to the XCDs.  Either way an XCD runs its tiles in list order, so
@@ -265,6 +274,39 @@ inline long long tile_grid(long long bound, int chunk) {
   const long long g = chunk == 0 ? kXcds : (long long)kXcds * chunk;
   return (bound + g - 1) / g * g;
 }
+__device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + expf(-a)); }
+
+// MXFP8 expert FFN GEMMs (mxfp8.hip) over the segment table of the FFN: GEMM1 (mode 0:
+// x W1, x W3, SwiGLU, h requantised to MXFP8 per row) and GEMM2 (mode 1: h W2 -> bf16).
+struct MxArgs {
+  const uint8_t* a;          // GEMM1: x codes [T][d]; GEMM2: h codes [rows][I]
+  const uint8_t* as;         // matching E8M0 scales [.][K/32]
+  const int32_t* perm;
+  int T, k, E;
+  long long Tk;
+  const uint8_t* b0;         // GEMM1: W1 codes; GEMM2: W2 codes
+  const uint8_t* b1;         // GEMM1: W3 codes
+  const uint8_t* b0s;
+  const uint8_t* b1s;
+  const uint8_t* sb0;        // shared expert
+  const uint8_t* sb1;
+  const uint8_t* sb0s;
+  const uint8_t* sb1s;
+  int K, N, NT;
+  const int* mstart;
+  const int* rowstart;
+  const int* rowcount;
+  int S;
+  void* out;                 // GEMM1: h codes [rows][I]; GEMM2: bf16 [rows][d]
+  uint8_t* out_scale;        // GEMM1: h scales [rows][I/32]
+  int* flag;
+};
+// Rows per tile of the MXFP8 GEMMs for hidden size d and intermediate size inter (the
+// segment table counts tiles of this height).
+int mx_tile_rows(int d, int inter);
+// Launch GEMM1 (mode 0) or GEMM2 (mode 1); mt_bound bounds the segment table's row tiles.
+moe_status mx_gemm(int mode, MxArgs g, long long mt_bound, hipStream_t s);
+
 // NVFP4 expert FFN (nvfp4.hip).
 struct Nvfp4Gemm {
   const uint16_t* a;       // A decoded (E2M1 * E4M3, bf16) [rows][K], fp32 row scales

@@ -1,0 +1,764 @@
+// MXFP8 grouped GEMMs of the expert FFN (Composer 2 Technical Report, section 6.1
+// "Kernels": MoE weights and activations in MXFP8, E4M3 elements with one E8M0 scale per
+// 32; OCP Microscaling Formats v1.0 for the encoding).  Same segment table, tile order
+// and per-output reduction order rules as the bf16 grouped GEMM in ffn.hip: a tile never
+// mixes experts and every output is one fixed chain of scaled MFMAs over ascending K.
+#include <math.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// MXFP8 tile shape: wavefronts along M and N, 32-row B blocks per wavefront.
+#ifndef MOE_MX_WM
+#define MOE_MX_WM 2
+#endif
+#ifndef MOE_MX_WN
+#define MOE_MX_WN 2
+#endif
+#ifndef MOE_MX_FN
+#define MOE_MX_FN 2
+#endif
+#ifndef MOE_MX_WAVES
+#define MOE_MX_WAVES 1   // minimum wavefronts per SIMD the register allocation must allow
+#endif
+#ifndef MOE_MX_RING
+#define MOE_MX_RING 1   // MXFP8 GEMMs on the LDS ring where the shape tiles
+#endif
+#ifndef MOE_MX_XCD_CHUNK
+#define MOE_MX_XCD_CHUNK 16
+#endif
+constexpr int kMxXcdChunk = MOE_MX_XCD_CHUNK;
+
+// ---------------------------------------------------------------------------
+// MXFP8 path (OCP MX: E4M3 elements, one E8M0 scale per 32 elements along K) on the
+// block-scaled matrix cores: v_mfma_scale_f32_32x32x64_f8f6f4.  Lane l of an operand
+// holds row (or column) l % 32; with h = l / 32, its bytes 0..15 are k = 16h..16h+15 of
+// the instruction's 64-wide k range and bytes 16..31 are k = 32+16h..32+16h+15, so
+// k-block 0 (k < 32) is split over both lane halves, and lane half h supplies the E8M0
+// scale of k-block h.
+// GEMM1 requantises h = silu(x W1) * (x W3) to MXFP8 row by row (one 32-column block per
+// half wavefront) for GEMM2; GEMM2 writes bf16.
+// ---------------------------------------------------------------------------
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+constexpr int MBK = 128;               // reduction step in elements (= bytes)
+constexpr int MLDS = MBK + 16;         // LDS row stride in bytes
+
+
+// fp32 (already divided by its block scale) -> E4M3 code, round to nearest even,
+// saturating to +-448 (NaN -> 0x7F).
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fabsf(v);
+  if (a != a) return 0x7Fu;
+  if (!(a < 448.0f)) return sign | 0x7Eu;
+  const uint32_t ua = __float_as_uint(a);
+  if (ua < 0x00800000u) return sign;                 // below 2^-126: rounds to zero
+  const int e = (int)(ua >> 23) - 127;
+  const uint32_t full = (ua & 0x7FFFFFu) | 0x800000u;
+  const int shift = e >= -6 ? 20 : 20 + (-6 - e);
+  if (shift > 24) return sign;                       // below 2^-10: rounds to zero
+  uint32_t keep = full >> shift;
+  const uint32_t rem = full & ((1u << shift) - 1u), half = 1u << (shift - 1);
+  keep += (rem > half || (rem == half && (keep & 1u))) ? 1u : 0u;
+  if (e >= -6) {
+    int ef = e + 7;
+    if (keep == 16u) {
+      ++ef;
+      keep = 8u;
+    }
+    return sign | ((uint32_t)ef << 3) | (keep - 8u);
+  }
+  return sign | keep;                                // subnormal grid (keep == 8: 2^-6)
+}
+
+// Requantise one row's 32-feature MX block (this value and the 31 other lanes of the
+// half wavefront) and store code and scale: OCP MX scale 2^(floor(log2 amax) - 8).
+__device__ __forceinline__ void mx_store_h(float h, bool live, uint8_t* code, uint8_t* scale,
+                                           bool first) {
+  float amax = fabsf(h);
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  int se;
+  uint32_t scode;
+  if (amax == 0.0f) {
+    se = -127;
+    scode = 0;
+  } else if (!(amax <= 3.0e38f)) {
+    se = 0;
+    scode = 255;
+  } else {
+    se = min(max(ilogbf(amax) - 8, -127), 127);
+    scode = (uint32_t)(se + 127);
+  }
+  if (live) {
+    *code = (uint8_t)e4m3_rne_sat(ldexpf(h, -se));
+    if (first) *scale = (uint8_t)scode;
+  }
+}
+
+// Requantise one MX block (32 consecutive fp32 features of a row, at `src` in LDS, read
+// by one lane) and store its 32 codes (two 16-byte stores) and its scale.  Same scale
+// rule and encoding as mx_store_h.  Two passes over LDS (the block's amax, then the
+// codes) keep few values live.
+__device__ __forceinline__ void mx_store_block(const uint8_t* src, uint8_t* code, uint8_t* scale) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float4 t = *(const float4*)(src + 16 * c);
+    amax = fmaxf(fmaxf(amax, fmaxf(fabsf(t.x), fabsf(t.y))), fmaxf(fabsf(t.z), fabsf(t.w)));
+  }
+  int se;
+  uint32_t scode;
+  if (amax == 0.0f) {
+    se = -127;
+    scode = 0;
+  } else if (!(amax <= 3.0e38f)) {
+    se = 0;
+    scode = 255;
+  } else {
+    se = min(max(ilogbf(amax) - 8, -127), 127);
+    scode = (uint32_t)(se + 127);
+  }
+  // v_cvt_pk_fp8_f32 rounds to nearest even onto the OCP E4M3 grid; with its input
+  // clamped to +-448 it equals e4m3_rne_sat (checked on every rounding boundary of
+  // every binade from 2^-20 to 2^10, the subnormal grid, +-0 and the infinities), and
+  // NaN is kept as 0x7F explicitly
+  u32x4_t w[2];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float4 t = *(const float4*)(src + 16 * c);
+    const float v[4] = {ldexpf(t.x, -se), ldexpf(t.y, -se), ldexpf(t.z, -se), ldexpf(t.w, -se)};
+    int d = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(v[0], -448.0f), 448.0f),
+                                            fminf(fmaxf(v[1], -448.0f), 448.0f), 0, false);
+    d = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(v[2], -448.0f), 448.0f),
+                                        fminf(fmaxf(v[3], -448.0f), 448.0f), d, true);
+    uint32_t du = (uint32_t)d;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      if (v[b] != v[b]) du = (du & ~(0xFFu << (8 * b))) | (0x7Fu << (8 * b));
+    w[c >> 2][c & 3] = du;
+  }
+  *(u32x4_t*)code = w[0];
+  *(u32x4_t*)(code + 16) = w[1];
+  *scale = (uint8_t)scode;
+}
+
+// Tile: (64 WM) rows x (32 FN WN) staged B rows, WM x WN wavefronts; each wavefront
+// owns 64 rows x 32 FN B rows as 2 x FN MFMA blocks.  K advances 128 bytes a step:
+// registers -> LDS (144-byte rows) -> two 64-wide MFMA steps, with the next step's
+// loads in flight.  GEMM1 (MODE 0): B rows alternate 32-row blocks of W1 and W3, so a
+// wavefront's blocks 2p and 2p + 1 are the W1 and W3 halves of 32 features.
+template <int MODE, int WM, int WN, int FN>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(MOE_MX_WAVES)))
+void grouped_gemm_mx_kernel(MxArgs g) {
+  constexpr int NTHR = 64 * WM * WN;
+  constexpr int TM = 64 * WM;                 // tile rows
+  constexpr int TB = 32 * FN * WN;            // staged B rows
+  constexpr int RSTEP = NTHR / 8;             // loader row stride (8 threads per 128-byte row)
+  constexpr int LA = TM / RSTEP, LB = TB / RSTEP;
+  static_assert(LA * RSTEP == TM && LB * RSTEP == TB && FN % 2 == 0, "tile shape");
+  __shared__ __attribute__((aligned(16))) uint8_t sA[TM * MLDS];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[TB * MLDS];
+  __shared__ uint32_t sAs[TM];
+  __shared__ uint32_t sBs[TB];
+
+  const int total = g.mstart[g.S] * g.NT;
+  int tile;
+  if (!xcd_tile<0>(total, tile)) return;
+  int lo = 0, hi = g.S;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (g.mstart[mid] * g.NT <= tile) lo = mid; else hi = mid;
+  }
+  const int s = lo;
+  const int mtiles = g.mstart[s + 1] - g.mstart[s];
+  const int local = tile - g.mstart[s] * g.NT;
+  const int grp = local / (kGroupM * g.NT), rem = local % (kGroupM * g.NT);
+  const int gm = min(kGroupM, mtiles - grp * kGroupM);
+  const int nt = rem / gm, mt = grp * kGroupM + rem % gm;
+  const int row0 = g.rowstart[s] + mt * TM;
+  const int mrows = min(TM, g.rowcount[s] - mt * TM);
+  const int n0 = nt * (MODE == 0 ? TB / 2 : TB);
+  const bool is_shared = (s == g.E);
+  const long long e = is_shared ? 0 : s;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int lr = tid >> 3, lc = (tid & 7) * 16;     // loader: rows lr + RSTEP i, 16-byte chunk lc
+  const int KB = g.K / 32;                           // scale bytes per row
+
+  // source row of A tile row r (rows past the segment re-read the tile's first row)
+  auto a_src = [&](int r, int& bad) -> long long {
+    const long long jr = (long long)row0 + (r < mrows ? r : 0);
+    long long src;
+    if (MODE == 0) {
+      src = is_shared ? jr - g.Tk : (long long)(g.perm[jr] / g.k);
+      if (src < 0 || src >= g.T) {
+        bad = 1;
+        src = 0;
+      }
+    } else {
+      src = jr;
+    }
+    return src;
+  };
+  // row (within expert e's matrix) of staged B row r, with its code and scale banks
+  auto b_row = [&](int r, const uint8_t*& bank, const uint8_t*& sbank) -> long long {
+    if (MODE == 0) {
+      const int blk = r >> 5, within = r & 31;
+      const bool w3 = blk & 1;
+      bank = w3 ? (is_shared ? g.sb1 : g.b1) : (is_shared ? g.sb0 : g.b0);
+      sbank = w3 ? (is_shared ? g.sb1s : g.b1s) : (is_shared ? g.sb0s : g.b0s);
+      return (long long)n0 + (blk >> 1) * 32 + within;
+    }
+    bank = is_shared ? g.sb0 : g.b0;
+    sbank = is_shared ? g.sb0s : g.b0s;
+    return (long long)n0 + r;
+  };
+
+  int bad = 0;
+  const uint8_t* aptr[LA];
+  const uint8_t* bptr[LB];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) aptr[i] = g.a + a_src(lr + RSTEP * i, bad) * (long long)g.K + lc;
+#pragma unroll
+  for (int i = 0; i < LB; ++i) {
+    const uint8_t *bank, *sbank;
+    const long long br = b_row(lr + RSTEP * i, bank, sbank);
+    bptr[i] = bank + (e * g.N + br) * (long long)g.K + lc;
+  }
+  // Scale rows: thread t < TM stages A row t's four scale bytes of the step, threads
+  // TM .. TM + TB - 1 those of B row t - TM (strided when there are fewer threads).
+  constexpr int NS = (TM + TB + NTHR - 1) / NTHR;
+  const uint8_t* sptr[NS];
+  bool sact[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int sr = tid + NTHR * i;
+    sact[i] = sr < TM + TB;
+    if (sr < TM) {
+      sptr[i] = g.as + a_src(sr, bad) * (long long)KB;
+    } else {
+      const uint8_t *bank, *sbank;
+      const long long br = b_row(sact[i] ? sr - TM : 0, bank, sbank);
+      sptr[i] = sbank + (e * g.N + br) * (long long)KB;
+    }
+  }
+  if (bad) raise_flag(g.flag, kFlagCorrupt);
+
+  f32x16_t acc[2][FN];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < FN; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+
+  u32x4_t ra[LA], rb[LB];
+  uint32_t rs[NS];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) ra[i] = *(const u32x4_t*)(aptr[i]);
+#pragma unroll
+  for (int i = 0; i < LB; ++i) rb[i] = *(const u32x4_t*)(bptr[i]);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) rs[i] = sact[i] ? *(const uint32_t*)(sptr[i]) : 0u;
+
+  for (int k0 = 0; k0 < g.K; k0 += MBK) {
+#pragma unroll
+    for (int i = 0; i < LA; ++i) *(u32x4_t*)&sA[(lr + RSTEP * i) * MLDS + lc] = ra[i];
+#pragma unroll
+    for (int i = 0; i < LB; ++i) *(u32x4_t*)&sB[(lr + RSTEP * i) * MLDS + lc] = rb[i];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int sr = tid + NTHR * i;
+      if (sr < TM) sAs[sr] = rs[i];
+      else if (sact[i]) sBs[sr - TM] = rs[i];
+    }
+    __syncthreads();
+    const int kn = k0 + MBK;
+    if (kn < g.K) {
+#pragma unroll
+      for (int i = 0; i < LA; ++i) ra[i] = *(const u32x4_t*)(aptr[i] + kn);
+#pragma unroll
+      for (int i = 0; i < LB; ++i) rb[i] = *(const u32x4_t*)(bptr[i] + kn);
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+        if (sact[i]) rs[i] = *(const uint32_t*)(sptr[i] + kn / 32);
+    }
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int kc = sub * 64 + (lane >> 5) * 16;       // bytes 0..15; bytes 16..31 at kc + 32
+      const int sh = 8 * (sub * 2 + (lane >> 5));       // scale byte of k-block (2 sub + half)
+      i32x8_t af[2], bf[FN];
+      int sa[2], sb[FN];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int row = wm * 64 + mb * 32 + (lane & 31);
+        const u32x4_t u0 = *(const u32x4_t*)&sA[row * MLDS + kc];
+        const u32x4_t u1 = *(const u32x4_t*)&sA[row * MLDS + kc + 32];
+        af[mb] = (i32x8_t){(int)u0[0], (int)u0[1], (int)u0[2], (int)u0[3],
+                           (int)u1[0], (int)u1[1], (int)u1[2], (int)u1[3]};
+        sa[mb] = (int)((sAs[row] >> sh) & 0xFFu);
+      }
+#pragma unroll
+      for (int nb = 0; nb < FN; ++nb) {
+        const int row = (wn * FN + nb) * 32 + (lane & 31);
+        const u32x4_t u0 = *(const u32x4_t*)&sB[row * MLDS + kc];
+        const u32x4_t u1 = *(const u32x4_t*)&sB[row * MLDS + kc + 32];
+        bf[nb] = (i32x8_t){(int)u0[0], (int)u0[1], (int)u0[2], (int)u0[3],
+                           (int)u1[0], (int)u1[1], (int)u1[2], (int)u1[3]};
+        sb[nb] = (int)((sBs[row] >> sh) & 0xFFu);
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < FN; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              af[mb], bf[nb], acc[mb][nb], 0, 0, 0, sa[mb], 0, sb[nb]);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue.  Accumulator element v of a lane is C[i][j], j = lane % 32,
+  //      i = 8 (v / 4) + 4 (lane / 32) + v % 4. ----
+  const int j = lane & 31;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int i = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      const int r = wm * 64 + mb * 32 + i;
+      const long long orow = (long long)row0 + r;
+      if (MODE == 0) {
+        // One MX block = this row's 32 features, spread over the 32 lanes of a half.
+#pragma unroll
+        for (int p = 0; p < FN / 2; ++p) {
+          const float hv = silu_f32(acc[mb][2 * p][v]) * acc[mb][2 * p + 1][v];
+          const int col = n0 + (wn * FN / 2 + p) * 32 + j;
+          mx_store_h(hv, r < mrows, (uint8_t*)g.out + orow * g.N + col,
+                     g.out_scale + orow * (g.N / 32) + col / 32, j == 0);
+        }
+      } else {
+        if (r < mrows) {
+#pragma unroll
+          for (int nb = 0; nb < FN; ++nb) {
+            const int col = n0 + (wn * FN + nb) * 32 + j;
+            ((uint16_t*)g.out)[orow * g.N + col] = f32_to_bf16(acc[mb][nb][v]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8 grouped GEMM on a four-stage LDS ring (the path for shapes it tiles: N of
+// GEMM2 a multiple of 256).  Tiles are 256 rows x 256 staged B rows; K advances 64
+// bytes (one MFMA k range) a step.  Eight wavefronts, 2 along M x 4 along N, each own
+// 128 rows x 64 B rows as 4 x 2 MFMA blocks, two wavefronts per SIMD.
+// Loads go straight from global memory into LDS (global_load_lds_dwordx4: lane l of a
+// wavefront writes its 16 bytes at base + 16 l), three steps ahead of the step being
+// multiplied.  A stage holds the A tile (256 rows x 64 B) and the B tile (256 x 64 B).
+// E8M0 scales travel in groups of 16 bytes per row (512 K, eight steps), into one of two
+// scale buffers, issued eight steps before their first use: a per-step scale load
+// would cost one memory request per row for 2 bytes.
+// The 16-byte chunk c of a row r is stored in slot c ^ ((r >> 2) & 3), so the sixteen
+// rows that one ds_read_b128 phase touches fall in distinct banks.
+// Row blocks past the tile's valid rows are not multiplied (a wavefront skips its
+// 32-row blocks that hold no valid row), so a short tile costs MFMA time in
+// proportion to its 32-row blocks.  Every output is the same MFMA chain as in
+// grouped_gemm_mx_kernel (K ascending in 64-wide scaled MFMAs from zero), hence the
+// same bits.
+// The loads are issued from inline assembly: the compiler then treats the fragment
+// reads as ordinary LDS loads (it does not wait for the ring's outstanding loads before
+// each of them), and the K loop orders them itself with an explicit vmcnt wait and
+// s_barrier per step.  No other global load is in flight inside the K loop.
+// ---------------------------------------------------------------------------
+constexpr int XR_M = 256;                        // tile rows
+constexpr int XR_N = 256;                        // staged B rows
+constexpr int XR_K = 128;                        // K bytes per ring step (two MFMA k ranges)
+constexpr int XR_ST = 2;                         // ring stages
+constexpr int XR_A = 0, XR_B = XR_M * XR_K;      // tile offsets within a stage
+constexpr int XR_STAGE = (XR_M + XR_N) * XR_K;   // 64 KB
+constexpr int XR_GS = 4;                         // steps per scale group (16 E8M0 bytes per row)
+constexpr int XR_GB = XR_GS * XR_K;              // K per scale group
+constexpr int XR_SC = XR_ST * XR_STAGE;          // two scale-group buffers after the stages
+constexpr int XR_SCB = (XR_M + XR_N) * 16;       // bytes per scale-group buffer (A rows, then B)
+constexpr int XR_LDS = XR_SC + 2 * XR_SCB;       // 144 KB
+constexpr int XR_EPI_ROW = 144;                  // epilogue staging: bytes per local row
+constexpr int XR_EPI = 128 * XR_EPI_ROW;         // epilogue staging per wavefront (18 KB)
+static_assert(XR_LDS <= 160 * 1024 && 8 * XR_EPI <= XR_LDS, "LDS budget");
+
+// slot of the 16-byte chunk c of row r: c ^ ((r >> 1) & 7); the sixteen rows that one
+// ds_read_b128 phase touches (one chunk each) then fall in distinct banks
+__device__ __forceinline__ int xr_swz(int r) { return (r >> 1) & 7; }
+
+// global_load_lds_dwordx4 (lane l writes its 16 bytes at lds + 16 l) from a
+// wavefront-uniform base plus a 32-bit per-lane offset, or from a per-lane address
+__device__ __forceinline__ void xr_load16(uint32_t lds, uint32_t off, const void* base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base)
+               : "memory");
+}
+__device__ __forceinline__ void xr_load16(uint32_t lds, const void* src) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory");
+}
+// Wait until at most N ring loads of this wavefront are outstanding and every LDS
+// access of this wavefront has completed, then meet the other wavefronts.
+template <int N>
+__device__ __forceinline__ void xr_sync() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// One 64-wide k range of fragments: NB of the wavefront's 4 row blocks, 2 B blocks.
+template <int NB>
+struct XrFrag {
+  i32x8_t a[NB > 0 ? NB : 1], b[2];
+};
+// The E8M0 scales of one step for a lane: word w of a block holds, from its low byte, the
+// scales of k-blocks 4 (j % 4) + lane / 32 + 0, 1, 2, ... of the row, so the first k range
+// takes byte 0 (MFMA op_sel 0) and the second byte 2 (op_sel 2).
+template <int NB>
+struct XrScale {
+  int a[NB > 0 ? NB : 1], b[2];
+};
+
+// Read k range `half` (0 or 1) of the stage at st.  aof/bof: this lane's chunk of k
+// range 0 (k range 1 is XOR 64, the second 16 bytes XOR 32).
+template <int NB>
+__device__ __forceinline__ void xr_read(XrFrag<NB>& f, const uint8_t* st, uint32_t aof, uint32_t bof,
+                                        int half) {
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const uint32_t o = (bof ^ (64 * half)) + nb * 32 * XR_K;
+    const u32x4_t lo = *(const u32x4_t*)(st + o);
+    const u32x4_t hi = *(const u32x4_t*)(st + (o ^ 32));
+    f.b[nb] = (i32x8_t){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb) {
+    const uint32_t o = (aof ^ (64 * half)) + mb * 32 * XR_K;
+    const u32x4_t lo = *(const u32x4_t*)(st + o);
+    const u32x4_t hi = *(const u32x4_t*)(st + (o ^ 32));
+    f.a[mb] = (i32x8_t){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+}
+// asf/bsf: this lane's row's 16-byte scale group in the scale buffer scb; sc: the step's
+// first k-block within the group (a multiple of 4); sh = 8 (lane / 32).
+template <int NB>
+__device__ __forceinline__ void xr_read_scales(XrScale<NB>& sc4, const uint8_t* scb, uint32_t asf,
+                                               uint32_t bsf, int sc, int sh) {
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) sc4.b[nb] = (int)(*(const uint32_t*)(scb + bsf + nb * 32 * 16 + sc) >> sh);
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb)
+    sc4.a[mb] = (int)(*(const uint32_t*)(scb + asf + mb * 32 * 16 + sc) >> sh);
+}
+
+// An empty asm that reads every accumulator: the MFMAs before it are issued before the
+// ring loads and barriers that follow it in program order (the compiler would otherwise
+// sink them next to their next use).
+__device__ __forceinline__ void xr_pin(const f32x16_t (&acc)[4][2]) {
+  asm volatile("" ::"a"(acc[0][0]), "a"(acc[0][1]), "a"(acc[1][0]), "a"(acc[1][1]), "a"(acc[2][0]),
+               "a"(acc[2][1]), "a"(acc[3][0]), "a"(acc[3][1]));
+}
+
+template <int NB, int SEL>
+__device__ __forceinline__ void xr_mfma(const XrFrag<NB>& f, const XrScale<NB>& sc4, f32x16_t (&acc)[4][2]) {
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[mb], f.b[nb], acc[mb][nb], 0, 0, SEL,
+                                                                   sc4.a[mb], SEL, sc4.b[nb]);
+}
+
+// Load sources: A rows at abase + aoff[i] (wavefront-uniform base, per-lane offset), B
+// rows at bbase + boff[i], scale groups at sbase + soff (A rows, waves 0..3) or at the
+// per-lane bsp (B rows, waves 4..7).
+struct XrSrc {
+  const uint8_t* abase;
+  const uint8_t* bbase;
+  const uint8_t* sbase;
+  const uint8_t* bsp;
+  uint32_t aoff[4], boff[4], soff;
+};
+
+// The K loop of a wavefront that multiplies NB of its 4 row blocks (NB = 0: it only
+// loads and synchronises).  Step j (K bytes 128 j .. 128 j + 127) lives in stage j % 2.
+// At step j: wait for its data, meet (every wavefront is then done with step j - 1, whose
+// stage takes step j + 1's loads), multiply.  Scale group g (steps 4 g .. 4 g + 3) goes
+// out at step 4 (g - 1), after that step's data, into buffer g % 2.
+template <int NB>
+__device__ __forceinline__ void xr_kloop(const uint8_t* ring, uint32_t ring_lds, int nsteps, const XrSrc& src,
+                                         int wave, uint32_t aof, uint32_t bof, uint32_t asf, uint32_t bsf,
+                                         int sh, f32x16_t (&acc)[4][2]) {
+  const uint32_t la = XR_A + wave * 4096, lb = XR_B + wave * 4096;
+  const uint32_t ls = wave < 4 ? wave * 1024 : XR_M * 16 + (wave - 4) * 1024;
+  const int ngroups = nsteps / XR_GS;
+  auto issue = [&](int j) {
+    const uint32_t st = ring_lds + (uint32_t)(j & 1) * XR_STAGE;
+    const int k0 = j * XR_K;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xr_load16(st + la + 1024 * i, src.aoff[i], src.abase + k0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xr_load16(st + lb + 1024 * i, src.boff[i], src.bbase + k0);
+  };
+  auto issue_scales = [&](int grp) {
+    const uint32_t dst = ring_lds + XR_SC + (uint32_t)(grp & 1) * XR_SCB + ls;
+    if (wave < 4)
+      xr_load16(dst, src.soff, src.sbase + 16 * grp);
+    else
+      xr_load16(dst, src.bsp + 16 * grp);
+  };
+  auto scales_at = [&](int j) { return j >= 0 && j % XR_GS == 0 && j / XR_GS + 1 < ngroups; };
+
+  issue_scales(0);
+  issue(0);
+  for (int j = 0; j < nsteps; ++j) {
+    // step j's data went out at step j - 1 (or before the loop), followed only by that
+    // step's scale group (loads complete in issue order)
+    if (scales_at(j - 1))
+      xr_sync<1>();
+    else
+      xr_sync<0>();
+    if (j + 1 < nsteps) issue(j + 1);
+    if (scales_at(j)) issue_scales(j / XR_GS + 1);
+    if constexpr (NB > 0) {
+      const uint8_t* st = ring + (j & 1) * XR_STAGE;
+      const uint8_t* scb = ring + XR_SC + ((j / XR_GS) & 1) * XR_SCB;
+      XrScale<NB> sc4;
+      xr_read_scales<NB>(sc4, scb, asf, bsf, (j % XR_GS) * (XR_K / 32), sh);
+      XrFrag<NB> f;
+      xr_read<NB>(f, st, aof, bof, 0);
+      xr_mfma<NB, 0>(f, sc4, acc);
+      xr_read<NB>(f, st, aof, bof, 1);
+      xr_mfma<NB, 2>(f, sc4, acc);
+      xr_pin(acc);
+    }
+  }
+}
+
+// MXFP8 grouped GEMM, 256 x 256 tiles, eight wavefronts (2 along M x 4 along N, two per
+// SIMD), each 4 row blocks x 2 B blocks of 32 x 32.  A wavefront whose 32-row blocks
+// hold no valid row skips their MFMAs, so a short tile costs MFMA time in proportion to
+// its valid 32-row blocks on the busier half.
+template <int MODE>
+__global__ __launch_bounds__(512) void grouped_gemm_mx_ring_kernel(MxArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[XR_LDS];
+
+  // ---- tile decode (as grouped_gemm_mx_kernel, tiles of XR_M rows) ----
+  const int total = g.mstart[g.S] * g.NT;
+  int tile;
+  if (!xcd_tile<kMxXcdChunk>(total, tile)) return;
+  int lo = 0, hi = g.S;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (g.mstart[mid] * g.NT <= tile) lo = mid; else hi = mid;
+  }
+  const int s = lo;
+  const int mtiles = g.mstart[s + 1] - g.mstart[s];
+  const int local = tile - g.mstart[s] * g.NT;
+  const int grp = local / (kGroupM * g.NT), rem = local % (kGroupM * g.NT);
+  const int gm = min(kGroupM, mtiles - grp * kGroupM);
+  const int nt = rem / gm, mt = grp * kGroupM + rem % gm;
+  const int row0 = g.rowstart[s] + mt * XR_M;
+  const int mrows = min(XR_M, g.rowcount[s] - mt * XR_M);
+  const int n0 = nt * (MODE == 0 ? XR_N / 2 : XR_N);
+  const bool is_shared = (s == g.E);
+  const long long e = is_shared ? 0 : s;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int KB = g.K / 32;   // scale bytes per row
+
+  int bad = 0;
+  // source row of A tile row r (rows past the segment re-read the tile's first row)
+  auto a_src = [&](int r) -> long long {
+    const long long jr = (long long)row0 + (r < mrows ? r : 0);
+    if (MODE != 0) return jr;
+    long long src = is_shared ? jr - g.Tk : (long long)(g.perm[jr] / g.k);
+    if (src < 0 || src >= g.T) {
+      bad = 1;
+      src = 0;
+    }
+    return src;
+  };
+  // row (within expert e's matrix) of staged B row r; GEMM1 alternates 32-row blocks of
+  // W1 and W3 for the same 32 features
+  auto b_row = [&](int r, const uint8_t*& bank, const uint8_t*& sbank) -> long long {
+    if (MODE == 0) {
+      const int blk = r >> 5;
+      const bool w3 = blk & 1;
+      bank = w3 ? (is_shared ? g.sb1 : g.b1) : (is_shared ? g.sb0 : g.b0);
+      sbank = w3 ? (is_shared ? g.sb1s : g.b1s) : (is_shared ? g.sb0s : g.b0s);
+      return (long long)n0 + (blk >> 1) * 32 + (r & 31);
+    }
+    bank = is_shared ? g.sb0 : g.b0;
+    sbank = is_shared ? g.sb0s : g.b0s;
+    return (long long)n0 + r;
+  };
+
+  // ---- loader: wavefront w fills A rows and B rows 32 w .. 32 w + 31 (four loads of 8
+  //      rows each; lane l -> row + l / 8, slot l % 8 <- chunk slot ^ swz(row); the B rows
+  //      are one 32-row block, so one bank) and the 16-byte scale groups of A rows
+  //      64 w + l (w < 4) or B rows 64 (w - 4) + l.  Every byte offset from a load's base
+  //      fits 32 bits (one activation matrix, or one expert's matrix). ----
+  XrSrc src;
+  src.abase = g.a;
+  src.sbase = g.as;
+  {
+    const uint8_t *bank, *sbank;
+    b_row(32 * wave, bank, sbank);
+    src.bbase = bank + e * g.N * (long long)g.K;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 32 * wave + 8 * i + (lane >> 3);
+    const int chunk = (lane & 7) ^ xr_swz(r);
+    src.aoff[i] = (uint32_t)(a_src(r) * g.K + 16 * chunk);
+    const uint8_t *bank, *sbank;
+    const long long br = b_row(r, bank, sbank);
+    src.boff[i] = (uint32_t)(br * g.K + 16 * chunk);
+  }
+  src.soff = (uint32_t)(a_src(64 * (wave & 3) + lane) * KB);
+  {
+    const uint8_t *bank, *sbank;   // GEMM1: W1 scales for lanes 0..31, W3 for 32..63
+    const long long br = b_row(64 * (wave & 3) + lane, bank, sbank);
+    src.bsp = sbank + (e * g.N + br) * (long long)KB;
+  }
+  if (bad) raise_flag(g.flag, kFlagCorrupt);
+
+  // ---- fragment offsets within a stage: lane reads row (block base + lane % 32),
+  //      chunks lane / 32 and 2 + lane / 32 of the k range ----
+  const int j32 = lane & 31, hh = lane >> 5;
+  const int ra = 128 * wm + j32, rb = 64 * wn + j32;
+  const uint32_t aof = XR_A + ra * XR_K + 16 * (hh ^ xr_swz(ra));
+  const uint32_t bof = XR_B + rb * XR_K + 16 * (hh ^ xr_swz(rb));
+  const uint32_t asf = ra * 16, bsf = XR_M * 16 + rb * 16;   // within a scale buffer
+  const int sh = 8 * hh;
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_u8*)ring;
+  const int nsteps = g.K / XR_K;
+  // 32-row blocks of this wavefront that hold a valid row (uniform per wavefront)
+  const int nb_act = min(4, max(0, (mrows - wm * 128 + 31) >> 5));
+  switch (nb_act) {
+    case 4: xr_kloop<4>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, sh, acc); break;
+    case 3: xr_kloop<3>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, sh, acc); break;
+    case 2: xr_kloop<2>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, sh, acc); break;
+    case 1: xr_kloop<1>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, sh, acc); break;
+    default: xr_kloop<0>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, sh, acc); break;
+  }
+
+  // ---- epilogue through LDS: each wavefront stages its 128 x (32 or 64) outputs
+  //      row-major in its own 18 KB of the (now idle) ring, then writes whole MX blocks
+  //      (GEMM1) or 16-byte row chunks (GEMM2).  Accumulator element v of a lane is
+  //      C[i][j], j = lane % 32, i = 8 (v / 4) + 4 (lane / 32) + v % 4; the wavefront's
+  //      local row 32 mb + i is tile row 128 wm + 32 mb + i. ----
+  __syncthreads();   // every wavefront is done reading the ring
+  uint8_t* stg = ring + wave * XR_EPI;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    if (mb >= nb_act) break;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int rl = 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
+      if (MODE == 0) {
+        // B blocks 0 and 1 are the W1 and W3 halves of the same 32 features
+        *(float*)(stg + rl * XR_EPI_ROW + j32 * 4) = silu_f32(acc[mb][0][v]) * acc[mb][1][v];
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          *(uint16_t*)(stg + rl * XR_EPI_ROW + (32 * nb + j32) * 2) = f32_to_bf16(acc[mb][nb][v]);
+      }
+    }
+  }
+  // (a wavefront reads back only what it wrote: its LDS accesses complete in order)
+  if (MODE == 0) {
+    // lane l: local rows l and 64 + l, one MX block (the wavefront's 32 features) each
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      const int rl = 64 * q2 + lane;
+      const int r = 128 * wm + rl;
+      if ((rl >> 5) < nb_act && r < mrows) {
+        const long long orow = (long long)row0 + r;
+        const int col = n0 + 32 * wn;
+        mx_store_block(stg + rl * XR_EPI_ROW, (uint8_t*)g.out + orow * g.N + col,
+                       g.out_scale + orow * (g.N / 32) + col / 32);
+      }
+    }
+  } else {
+    // lane l: local row 8 q + l / 8, 16-byte chunk l % 8 of the row's 64 outputs
+    const int c = lane & 7;
+#pragma unroll 4
+    for (int q2 = 0; q2 < 16; ++q2) {
+      const int rl = 8 * q2 + (lane >> 3);
+      const int r = 128 * wm + rl;
+      if ((rl >> 5) < nb_act && r < mrows) {
+        const u32x4_t t = *(const u32x4_t*)(stg + rl * XR_EPI_ROW + 16 * c);
+        *(u32x4_t*)((uint16_t*)g.out + ((long long)row0 + r) * g.N + n0 + wn * 64 + 8 * c) = t;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+// Both GEMMs run on the ring kernel when it tiles the shape: GEMM2's output in XR_N
+// columns, and 16-byte (XR_GB-element) scale groups along both reductions.
+static bool mx_ring_ok(int d, int inter) {
+  return MOE_MX_RING && d % XR_N == 0 && d % XR_GB == 0 && inter % XR_GB == 0;
+}
+
+int mx_tile_rows(int d, int inter) { return mx_ring_ok(d, inter) ? XR_M : 64 * MOE_MX_WM; }
+
+moe_status mx_gemm(int mode, MxArgs g, long long mt_bound, hipStream_t s) {
+  const int d = mode == 0 ? g.K : g.N, inter = mode == 0 ? g.N : g.K;
+  const bool ring = mx_ring_ok(d, inter);
+  if (mode == 0) {
+    g.NT = ring ? inter / (XR_N / 2) : inter / (16 * MOE_MX_FN * MOE_MX_WN);
+  } else {
+    // the configured tile where its width divides d, else 64-column tiles of the same
+    // height (same bits: every output is the same MFMA chain)
+    const bool wide = d % (32 * MOE_MX_FN * MOE_MX_WN) == 0;
+    g.NT = ring ? d / XR_N : wide ? d / (32 * MOE_MX_FN * MOE_MX_WN) : d / 64;
+  }
+  const long long grid = tile_grid(mt_bound * g.NT, ring ? kMxXcdChunk : 0);
+  if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+  if (grid == 0) return MOE_OK;
+  if (ring) {
+    if (mode == 0)
+      grouped_gemm_mx_ring_kernel<0><<<(unsigned)grid, 512, 0, s>>>(g);
+    else
+      grouped_gemm_mx_ring_kernel<1><<<(unsigned)grid, 512, 0, s>>>(g);
+  } else if (mode == 0) {
+    grouped_gemm_mx_kernel<0, MOE_MX_WM, MOE_MX_WN, MOE_MX_FN>
+        <<<(unsigned)grid, 64 * MOE_MX_WM * MOE_MX_WN, 0, s>>>(g);
+  } else if (d % (32 * MOE_MX_FN * MOE_MX_WN) == 0) {
+    grouped_gemm_mx_kernel<1, MOE_MX_WM, MOE_MX_WN, MOE_MX_FN>
+        <<<(unsigned)grid, 64 * MOE_MX_WM * MOE_MX_WN, 0, s>>>(g);
+  } else {
+    grouped_gemm_mx_kernel<1, MOE_MX_WM, 1, 2><<<(unsigned)grid, 64 * MOE_MX_WM, 0, s>>>(g);
+  }
+  return MOE_OK;
+}
+
+}  // namespace moe

@@ -207,8 +207,9 @@ moe_status moe_dispatch(const int32_t* ids, int T, int E, int k,
  * every row of every segment), so a token's output row does not depend on which
  * other tokens share its expert.
  * For MOE_MXFP8 the intermediate h is requantised to MXFP8 per row (one E8M0
- * scale per 32 columns, E4M3 elements rounded to nearest even and saturated at
- * +-448) before the W2 GEMM, so it is consumed by the same block-scaled MFMA.
+ * scale per 32 columns: the smallest power of two that maps the block's largest
+ * magnitude to at most 448, so no element saturates; E4M3 elements rounded to
+ * nearest even) before the W2 GEMM, so it is consumed by the same block-scaled MFMA.
  * For MOE_NVFP4, x is quantized per token and h per row to NVFP4 (the quantizer of
  * moe_nvfp4_quantize) before their GEMMs; both GEMMs run on the decoded values (E2M1
  * times E4M3, exact in fp16) with fp32 accumulation, and the two operands' fp32 row

@@ -76,15 +76,13 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
   return sign | keep;                                // subnormal grid (keep == 8: 2^-6)
 }
 
-// Requantise one row's 32-feature MX block (this value and the 31 other lanes of the
-// half wavefront) and store code and scale: OCP MX scale 2^(floor(log2 amax) - 8).
-__device__ __forceinline__ void mx_store_h(float h, bool live, uint8_t* code, uint8_t* scale,
-                                           bool first) {
-  float amax = fabsf(h);
-#pragma unroll
-  for (int off = 1; off < 32; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  int se;
-  uint32_t scode;
+// E8M0 scale 2^se of one MX block whose largest magnitude is amax: the smallest power of
+// two X with amax / X <= 448, the largest E4M3 value, so that no element of the block
+// saturates.  (The conversion OCP MX v1.0 suggests, X = 2^(floor(log2 amax) - 8), leaves
+// amax / X in [256, 512) and clamps a block's largest elements to 448 whenever amax / X
+// exceeds 448; both give the same X otherwise.)  All-zero blocks get code 0 (2^-127),
+// non-finite ones code 255 (NaN).
+__device__ __forceinline__ void mx_block_scale(float amax, int& se, uint32_t& scode) {
   if (amax == 0.0f) {
     se = -127;
     scode = 0;
@@ -92,9 +90,23 @@ __device__ __forceinline__ void mx_store_h(float h, bool live, uint8_t* code, ui
     se = 0;
     scode = 255;
   } else {
-    se = min(max(ilogbf(amax) - 8, -127), 127);
+    int e = ilogbf(amax) - 8;
+    if (ldexpf(amax, -e) > 448.0f) ++e;   // exact: a power-of-two scaling
+    se = min(max(e, -127), 127);
     scode = (uint32_t)(se + 127);
   }
+}
+
+// Requantise one row's 32-feature MX block (this value and the 31 other lanes of the
+// half wavefront) and store its code and the block's scale (mx_block_scale).
+__device__ __forceinline__ void mx_store_h(float h, bool live, uint8_t* code, uint8_t* scale,
+                                           bool first) {
+  float amax = fabsf(h);
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  int se;
+  uint32_t scode;
+  mx_block_scale(amax, se, scode);
   if (live) {
     *code = (uint8_t)e4m3_rne_sat(ldexpf(h, -se));
     if (first) *scale = (uint8_t)scode;
@@ -103,8 +115,8 @@ __device__ __forceinline__ void mx_store_h(float h, bool live, uint8_t* code, ui
 
 // Requantise one MX block (32 consecutive fp32 features of a row, at `src` in LDS, read
 // by one lane) and store its 32 codes (two 16-byte stores) and its scale.  Same scale
-// rule and encoding as mx_store_h.  Two passes over LDS (the block's amax, then the
-// codes) keep few values live.
+// rule (mx_block_scale) and encoding as mx_store_h.  Two passes over LDS (the block's
+// amax, then the codes) keep few values live.
 __device__ __forceinline__ void mx_store_block(const uint8_t* src, uint8_t* code, uint8_t* scale) {
   float amax = 0.0f;
 #pragma unroll
@@ -114,16 +126,7 @@ __device__ __forceinline__ void mx_store_block(const uint8_t* src, uint8_t* code
   }
   int se;
   uint32_t scode;
-  if (amax == 0.0f) {
-    se = -127;
-    scode = 0;
-  } else if (!(amax <= 3.0e38f)) {
-    se = 0;
-    scode = 255;
-  } else {
-    se = min(max(ilogbf(amax) - 8, -127), 127);
-    scode = (uint32_t)(se + 127);
-  }
+  mx_block_scale(amax, se, scode);
   // v_cvt_pk_fp8_f32 rounds to nearest even onto the OCP E4M3 grid; with its input
   // clamped to +-448 it equals e4m3_rne_sat (checked on every rounding boundary of
   // every binade from 2^-20 to 2^10, the subnormal grid, +-0 and the infinities), and

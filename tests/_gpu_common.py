@@ -87,6 +87,7 @@ def compare_rows(res_gpu, ref, rows, dtype, replay=False):
     assert np.max(np.abs(w - ref["weights"])) <= WEIGHT_TOL, np.max(np.abs(w - ref["weights"]))
     y = host(res_gpu["y"])[rows]
     err = oracle.normwise_rel_err(y, ref["y"])
+    say(f"  normwise err {err:.3e} (bar {TOL[dtype]})")
     assert err <= TOL[dtype], err
     return err
 

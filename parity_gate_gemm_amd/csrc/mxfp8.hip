@@ -716,7 +716,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_mx_ring_kernel(MxArgs g) {
       const int r = 128 * wm + rl;
       if ((rl >> 5) < nb_act && r < mrows) {
         const u32x4_t t = *(const u32x4_t*)(stg + rl * XR_EPI_ROW + 16 * c);
-        *(u32x4_t*)((uint16_t*)g.out + ((long long)row0 + r) * g.N + n0 + wn * 64 + 8 * c) = t;
+        // nontemporal: the expert outputs are read once, by the combine
+        __builtin_nontemporal_store(t, (u32x4_t*)((uint16_t*)g.out + ((long long)row0 + r) * g.N + n0 + wn * 64 + 8 * c));
       }
     }
   }

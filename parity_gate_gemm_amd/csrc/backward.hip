@@ -28,6 +28,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------
 // combine backward: one workgroup per token; d_w by a per-thread fp32 FMA chain over
@@ -129,6 +131,8 @@ __global__ __launch_bounds__(1024) void combine_bwd_kernel(const void* __restric
 // before the 8-byte LDS writes; K-rows past a segment's end read as zero.
 // ---------------------------------------------------------------------------
 constexpr int GB_T = 128, GB_K = 64, GB_S = GB_K + 8, GB_THR = 256;
+constexpr int GB_KS = GB_T + 8;   // K-major weight tile of the data kinds: row pitch (elements)
+static_assert(GB_K * GB_KS <= GB_T * GB_S, "the K-major tile fits in sB");
 enum { BK_DH = 0, BK_DX = 1, BK_DW2 = 2, BK_DW13 = 3 };
 
 // Tuning knobs of the weight-gradient GEMMs (same results for every setting):
@@ -246,6 +250,11 @@ void bwd_gemm_kernel(BwdGemm g) {
 #define MOE_BWD_KMAP 0
 #endif
   const int kq = MOE_BWD_KMAP ? tid >> 4 : tid & 15, rb = MOE_BWD_KMAP ? tid & 15 : tid >> 4;
+  // Weight operand of the data kinds (DH, DX): K-rows 4 bkq .. 4 bkq + 3 of the step,
+  // columns 8 brb .. 8 brb + 7, so one load instruction of a wavefront reads four whole
+  // 256-byte row pieces; the tile goes to LDS as it is (K-major) and the MFMA fragments
+  // are read with the transposing ds_read_b64_tr_b16.
+  const int bkq = tid >> 4, brb = tid & 15;
   const uint16_t* arow[4];
   if (!WGRAD) {
     const uint16_t* base = KIND == BK_DH ? g.d_out : g.dadg;
@@ -304,9 +313,9 @@ void bwd_gemm_kernel(BwdGemm g) {
         base = k0 < g.I ? w1b + (long long)k0 * g.d : w3b + (long long)(k0 - g.I) * g.d;
         ldb = g.d;
       }
-      base += c0 + 8 * rb;
+      base += c0 + 8 * brb;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) B[i] = *(const u32x4_t*)(base + (4 * kq + i) * ldb);
+      for (int i = 0; i < 4; ++i) B[i] = *(const u32x4_t*)(base + (4 * bkq + i) * ldb);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -336,6 +345,16 @@ void bwd_gemm_kernel(BwdGemm g) {
       *(u32x2_t*)&sX[(8 * rb + c) * GB_S + 4 * kq] = v;
     }
   };
+  // data kinds: the weight tile K-major in sB, row pitch GB_KS (conflict-free 16-byte
+  // stores: a quarter-wavefront writes one 256-byte row piece)
+  auto store_bk = [&](const u32x4_t(&R)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(u32x4_t*)&sB[(4 * bkq + i) * GB_KS + 8 * brb] = R[i];
+  };
+  auto store_b = [&](const u32x4_t(&R)[4]) {
+    if (!WGRAD) store_bk(R);
+    else tstore(sB, R);
+  };
   auto store_a = [&](uint16_t* sAs) {
     if (!WGRAD) {
 #pragma unroll
@@ -362,9 +381,27 @@ void bwd_gemm_kernel(BwdGemm g) {
         af[mb] = __builtin_bit_cast(bf16x8_t,
                                     *(const u32x4_t*)&sAs[(wm * 64 + mb * 32 + (lane & 31)) * GB_S + kc]);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-        bf[nb] = __builtin_bit_cast(bf16x8_t,
-                                    *(const u32x4_t*)&sB[(wn * 64 + nb * 32 + (lane & 31)) * GB_S + kc]);
+      for (int nb = 0; nb < 2; ++nb) {
+        if (!WGRAD) {
+          // ds_read_b64_tr_b16: in each 16-lane group, lane i receives halfword i % 4 of
+          // the 8-byte chunks that lanes 4 q + i / 4 (q = 0..3) address.  Lane 4 q + p
+          // addresses K-row kc0 + q, columns cg + 4 p .. cg + 4 p + 3, so lane i receives
+          // column cg + i at K-rows kc0 .. kc0 + 3: the MFMA operand of column lane % 32,
+          // k = kc .. kc + 7, in two reads.
+          const int i16 = lane & 15;
+          const int cg = wn * 64 + nb * 32 + 16 * ((lane >> 4) & 1);
+          const int kc0 = kc + (i16 >> 2);
+          const uint16_t* p0 = &sB[kc0 * GB_KS + cg + 4 * (i16 & 3)];
+          typedef __attribute__((address_space(3))) v4i16_t lds_v4;
+          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(p0));
+          const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(p0 + 4 * GB_KS));
+          const v8i16_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          bf[nb] = __builtin_bit_cast(bf16x8_t, v);
+        } else {
+          bf[nb] = __builtin_bit_cast(bf16x8_t,
+                                      *(const u32x4_t*)&sB[(wn * 64 + nb * 32 + (lane & 31)) * GB_S + kc]);
+        }
+      }
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -489,7 +526,7 @@ void bwd_gemm_kernel(BwdGemm g) {
       }
       for (int st = 0; st < nsteps; ++st) {
         store_a(sA);
-        tstore(sB, kb);
+        store_b(kb);
         __syncthreads();
         if (st + 1 < nsteps) {
           load_a((st + 1) * GB_K);

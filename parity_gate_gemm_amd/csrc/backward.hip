@@ -141,12 +141,6 @@ enum { BK_DH = 0, BK_DX = 1, BK_DW2 = 2, BK_DW13 = 3 };
 #ifndef MOE_BWD_NT_STORE
 #define MOE_BWD_NT_STORE 1
 #endif
-#ifndef MOE_BWD_RES
-#define MOE_BWD_RES 0
-#endif
-#ifndef MOE_BWD_DEPTH2
-#define MOE_BWD_DEPTH2 0
-#endif
 #ifndef MOE_BWD_NTW
 #define MOE_BWD_NTW 1
 #endif
@@ -187,19 +181,13 @@ struct BwdGemm {
 };
 
 // Weight-gradient kinds: a workgroup owns one 128-row block of the output (tile row
-// m0) and kBwdNtw consecutive column tiles.  With MOE_BWD_RES, a segment of at most
-// kResK rows stages its A operand (K x 128) in LDS once and only B streams through,
-// the next tile's first B step loaded before the current tile's stores (measured
-// slower at T = 4096: the larger LDS footprint leaves 2 workgroups per CU instead of
-// 3, and one short tile per workgroup hides latency better).
-constexpr int kResK = MOE_BWD_RES ? 128 : GB_K, kResSteps = kResK / GB_K;
+// m0) and kBwdNtw consecutive column tiles.
 
 template <int KIND>
 __global__ __launch_bounds__(GB_THR) __attribute__((amdgpu_waves_per_eu(MOE_BWD_WAVES)))
 void bwd_gemm_kernel(BwdGemm g) {
   constexpr bool WGRAD = KIND >= BK_DW2;
-  constexpr int ASTEPS = WGRAD ? kResSteps : 1;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[ASTEPS * GB_T * GB_S];
+  __shared__ __attribute__((aligned(16))) uint16_t sA[GB_T * GB_S];
   __shared__ __attribute__((aligned(16))) uint16_t sB[GB_T * GB_S];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -245,15 +233,11 @@ void bwd_gemm_kernel(BwdGemm g) {
   // ---- loaders ----
   // row operand (A of DH / DX): rows lr + 32 i, 16-byte chunk lc of the K-step
   const int lr = tid >> 3, lc = (tid & 7) * 8;
-  // K-major operands: K-rows 4 kq .. 4 kq + 3 of the step, columns 8 rb .. 8 rb + 7
-#ifndef MOE_BWD_KMAP
-#define MOE_BWD_KMAP 0
-#endif
-  const int kq = MOE_BWD_KMAP ? tid >> 4 : tid & 15, rb = MOE_BWD_KMAP ? tid & 15 : tid >> 4;
-  // Weight operand of the data kinds (DH, DX): K-rows 4 bkq .. 4 bkq + 3 of the step,
-  // columns 8 brb .. 8 brb + 7, so one load instruction of a wavefront reads four whole
-  // 256-byte row pieces; the tile goes to LDS as it is (K-major) and the MFMA fragments
-  // are read with the transposing ds_read_b64_tr_b16.
+  // K-major operands (the weights of the data kinds; both operands of the weight-gradient
+  // kinds): K-rows 4 bkq .. 4 bkq + 3 of the step, columns 8 brb .. 8 brb + 7, so one load
+  // instruction of a wavefront reads four whole 256-byte row pieces.  The tile goes to
+  // LDS as it is (K-major, row pitch GB_KS) and the MFMA fragments are read from it with
+  // the transposing ds_read_b64_tr_b16 (k_frag).
   const int bkq = tid >> 4, brb = tid & 15;
   const uint16_t* arow[4];
   if (!WGRAD) {
@@ -275,10 +259,10 @@ void bwd_gemm_kernel(BwdGemm g) {
   const uint16_t* a_seg = nullptr;   // wgrad A: segment row 0, this thread's columns
   int lda = 0;
   if (KIND == BK_DW2) {
-    a_seg = g.d_out + (long long)row0 * g.d + m0 + 8 * rb;
+    a_seg = g.d_out + (long long)row0 * g.d + m0 + 8 * brb;
     lda = g.d;
   } else if (KIND == BK_DW13) {
-    a_seg = g.dadg + (long long)row0 * 2 * g.I + m0 + 8 * rb;
+    a_seg = g.dadg + (long long)row0 * 2 * g.I + m0 + 8 * brb;
     lda = 2 * g.I;
   }
   const u32x4_t zero4 = {0u, 0u, 0u, 0u};
@@ -291,7 +275,7 @@ void bwd_gemm_kernel(BwdGemm g) {
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int kg = k0 + 4 * kq + i;
+        const int kg = k0 + 4 * bkq + i;
         const u32x4_t v = *(const u32x4_t*)(a_seg + min(kg, Klast) * lda);
         A[i] = kg < K ? v : zero4;
       }
@@ -319,48 +303,28 @@ void bwd_gemm_kernel(BwdGemm g) {
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int kg = k0 + 4 * kq + i;
+        const int kg = k0 + 4 * bkq + i;
         const int jr = row0 + min(kg, Klast);
         const uint16_t* p = KIND == BK_DW2 ? g.h + (long long)jr * g.I
                                            : g.x + (long long)g.tokrow[jr] * g.d;
-        const u32x4_t v = *(const u32x4_t*)(p + c0 + 8 * rb);
+        const u32x4_t v = *(const u32x4_t*)(p + c0 + 8 * brb);
         B[i] = kg < K ? v : zero4;
       }
     }
   };
   auto load_b = [&](int k0, int c0) { load_b_to(kb, k0, c0); };
-  // 4 K-rows x 8 columns -> LDS rows 8 rb + c, K offset 4 kq (two dwords per row)
-  auto tstore = [&](uint16_t* sX, const u32x4_t(&R)[4]) {
+  // a K-major tile as it is, row pitch GB_KS (conflict-free 16-byte stores: a quarter-
+  // wavefront writes one 256-byte row piece)
+  auto store_k = [&](uint16_t* sX, const u32x4_t(&R)[4]) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint32_t s0 = R[0][c >> 1], s1 = R[1][c >> 1], s2 = R[2][c >> 1], s3 = R[3][c >> 1];
-      u32x2_t v;
-      if ((c & 1) == 0) {
-        v[0] = (s0 & 0xffffu) | (s1 << 16);
-        v[1] = (s2 & 0xffffu) | (s3 << 16);
-      } else {
-        v[0] = (s0 >> 16) | (s1 & 0xffff0000u);
-        v[1] = (s2 >> 16) | (s3 & 0xffff0000u);
-      }
-      *(u32x2_t*)&sX[(8 * rb + c) * GB_S + 4 * kq] = v;
-    }
+    for (int i = 0; i < 4; ++i) *(u32x4_t*)&sX[(4 * bkq + i) * GB_KS + 8 * brb] = R[i];
   };
-  // data kinds: the weight tile K-major in sB, row pitch GB_KS (conflict-free 16-byte
-  // stores: a quarter-wavefront writes one 256-byte row piece)
-  auto store_bk = [&](const u32x4_t(&R)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4_t*)&sB[(4 * bkq + i) * GB_KS + 8 * brb] = R[i];
-  };
-  auto store_b = [&](const u32x4_t(&R)[4]) {
-    if (!WGRAD) store_bk(R);
-    else tstore(sB, R);
-  };
-  auto store_a = [&](uint16_t* sAs) {
+  auto store_a = [&]() {
     if (!WGRAD) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *(u32x4_t*)&sAs[(lr + 32 * i) * GB_S + lc] = ra[i];
+      for (int i = 0; i < 4; ++i) *(u32x4_t*)&sA[(lr + 32 * i) * GB_S + lc] = ra[i];
     } else {
-      tstore(sAs, ka);
+      store_k(sA, ka);
     }
   };
   auto zero_acc = [&]() {
@@ -371,37 +335,36 @@ void bwd_gemm_kernel(BwdGemm g) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
   };
-  auto mma = [&](const uint16_t* sAs) {
+  // MFMA operand of 32-row (or 32-column) block cb of a K-major tile, k = kc .. kc + 7.
+  // ds_read_b64_tr_b16: in each 16-lane group, lane i receives halfword i % 4 of the
+  // 8-byte chunks that lanes 4 q + i / 4 (q = 0..3) address, as element q.  Lane 4 q + p
+  // addresses K-row kc + q, columns c + 4 p .. c + 4 p + 3, so lane i receives column c + i
+  // at K-rows kc .. kc + 3; a second read gives kc + 4 .. kc + 7.
+  auto k_frag = [&](const uint16_t* sX, int cb, int kc) {
+    typedef __attribute__((address_space(3))) v4i16_t lds_v4;
+    const int i16 = lane & 15;
+    const int c = cb + 16 * ((lane >> 4) & 1);
+    const uint16_t* p0 = &sX[(kc + (i16 >> 2)) * GB_KS + c + 4 * (i16 & 3)];
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(p0));
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(p0 + 4 * GB_KS));
+    const v8i16_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+  };
+  auto mma = [&]() {
 #pragma unroll
     for (int kk = 0; kk < GB_K; kk += 16) {
       const int kc = kk + (lane >> 5) * 8;
       bf16x8_t af[2], bf[2];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        af[mb] = __builtin_bit_cast(bf16x8_t,
-                                    *(const u32x4_t*)&sAs[(wm * 64 + mb * 32 + (lane & 31)) * GB_S + kc]);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        if (!WGRAD) {
-          // ds_read_b64_tr_b16: in each 16-lane group, lane i receives halfword i % 4 of
-          // the 8-byte chunks that lanes 4 q + i / 4 (q = 0..3) address.  Lane 4 q + p
-          // addresses K-row kc0 + q, columns cg + 4 p .. cg + 4 p + 3, so lane i receives
-          // column cg + i at K-rows kc0 .. kc0 + 3: the MFMA operand of column lane % 32,
-          // k = kc .. kc + 7, in two reads.
-          const int i16 = lane & 15;
-          const int cg = wn * 64 + nb * 32 + 16 * ((lane >> 4) & 1);
-          const int kc0 = kc + (i16 >> 2);
-          const uint16_t* p0 = &sB[kc0 * GB_KS + cg + 4 * (i16 & 3)];
-          typedef __attribute__((address_space(3))) v4i16_t lds_v4;
-          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(p0));
-          const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(p0 + 4 * GB_KS));
-          const v8i16_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          bf[nb] = __builtin_bit_cast(bf16x8_t, v);
-        } else {
-          bf[nb] = __builtin_bit_cast(bf16x8_t,
-                                      *(const u32x4_t*)&sB[(wn * 64 + nb * 32 + (lane & 31)) * GB_S + kc]);
-        }
+      for (int mb = 0; mb < 2; ++mb) {
+        if (WGRAD)
+          af[mb] = k_frag(sA, wm * 64 + mb * 32, kc);
+        else   // row operand: row lane % 32 of the block, k = kc .. kc + 7
+          af[mb] = __builtin_bit_cast(bf16x8_t,
+                                      *(const u32x4_t*)&sA[(wm * 64 + mb * 32 + (lane & 31)) * GB_S + kc]);
       }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) bf[nb] = k_frag(sB, wn * 64 + nb * 32, kc);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -457,86 +420,26 @@ void bwd_gemm_kernel(BwdGemm g) {
   };
 
   const int nsteps = (K + GB_K - 1) / GB_K;
-  if (MOE_BWD_RES && WGRAD && nsteps <= kResSteps) {
-    // A resident in LDS for every column tile; B streamed, next tile's step 0 early
+  const int ntiles = WGRAD ? kBwdNtw : 1;
+  for (int q = 0; q < ntiles; ++q) {
+    const int c0 = n0 + q * GB_T;
+    zero_acc();
+    if (nsteps > 0) {
+      load_a(0);
+      load_b(0, c0);
+    }
     for (int st = 0; st < nsteps; ++st) {
-      load_a(st * GB_K);
-      store_a(sA + st * GB_T * GB_S);
+      store_a();
+      store_k(sB, kb);
+      __syncthreads();
+      if (st + 1 < nsteps) {
+        load_a((st + 1) * GB_K);
+        load_b((st + 1) * GB_K, c0);
+      }
+      mma();
+      __syncthreads();
     }
-    if (nsteps > 0) load_b(0, n0);
-    for (int q = 0; q < kBwdNtw; ++q) {
-      const int c0 = n0 + q * GB_T;
-      zero_acc();
-      for (int st = 0; st < nsteps; ++st) {
-        tstore(sB, kb);
-        __syncthreads();
-        if (st + 1 < nsteps) load_b((st + 1) * GB_K, c0);
-        else if (q + 1 < kBwdNtw) load_b(0, c0 + GB_T);
-        mma(sA + st * GB_T * GB_S);
-        __syncthreads();
-      }
-      epilogue(c0);
-    }
-  } else if (WGRAD && MOE_BWD_DEPTH2) {
-    // two K-steps of loads in flight: register set 0 holds the even steps, set 1 the odd
-    u32x4_t a1[4], b1[4];
-    for (int q = 0; q < kBwdNtw; ++q) {
-      const int c0 = n0 + q * GB_T;
-      zero_acc();
-      if (nsteps > 0) {
-        load_a_to(ka, 0);
-        load_b_to(kb, 0, c0);
-      }
-      if (nsteps > 1) {
-        load_a_to(a1, GB_K);
-        load_b_to(b1, GB_K, c0);
-      }
-      for (int st = 0; st < nsteps; st += 2) {
-        tstore(sA, ka);
-        tstore(sB, kb);
-        __syncthreads();
-        if (st + 2 < nsteps) {
-          load_a_to(ka, (st + 2) * GB_K);
-          load_b_to(kb, (st + 2) * GB_K, c0);
-        }
-        mma(sA);
-        __syncthreads();
-        if (st + 1 < nsteps) {
-          tstore(sA, a1);
-          tstore(sB, b1);
-          __syncthreads();
-          if (st + 3 < nsteps) {
-            load_a_to(a1, (st + 3) * GB_K);
-            load_b_to(b1, (st + 3) * GB_K, c0);
-          }
-          mma(sA);
-          __syncthreads();
-        }
-      }
-      epilogue(c0);
-    }
-  } else {
-    const int ntiles = WGRAD ? kBwdNtw : 1;
-    for (int q = 0; q < ntiles; ++q) {
-      const int c0 = n0 + q * GB_T;
-      zero_acc();
-      if (nsteps > 0) {
-        load_a(0);
-        load_b(0, c0);
-      }
-      for (int st = 0; st < nsteps; ++st) {
-        store_a(sA);
-        store_b(kb);
-        __syncthreads();
-        if (st + 1 < nsteps) {
-          load_a((st + 1) * GB_K);
-          load_b((st + 1) * GB_K, c0);
-        }
-        mma(sA);
-        __syncthreads();
-      }
-      epilogue(c0);
-    }
+    epilogue(c0);
   }
 }
 

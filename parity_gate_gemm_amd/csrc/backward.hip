@@ -184,7 +184,9 @@ struct BwdGemm {
 // m0) and kBwdNtw consecutive column tiles.
 
 template <int KIND>
-__global__ __launch_bounds__(GB_THR) __attribute__((amdgpu_waves_per_eu(MOE_BWD_WAVES)))
+// The weight-gradient kinds fit in 128 registers without spilling, so they run four
+// wavefronts per SIMD (four workgroups per CU); the data kinds would spill and keep three.
+__global__ __launch_bounds__(GB_THR) __attribute__((amdgpu_waves_per_eu(KIND >= BK_DW2 ? 4 : MOE_BWD_WAVES)))
 void bwd_gemm_kernel(BwdGemm g) {
   constexpr bool WGRAD = KIND >= BK_DW2;
   __shared__ __attribute__((aligned(16))) uint16_t sA[GB_T * GB_S];

@@ -181,6 +181,27 @@ def test_full_softmax_equals_restricted_form_and_sums_to_one():
 
 
 # ---------------------------------------------------------------------------
+# the parity metric
+# ---------------------------------------------------------------------------
+def test_normwise_rel_err_hand_values():
+    # max |y - y_ref| / max |y_ref| over the whole array, the reference in the
+    # denominator: 8 / 2 = 4.  Swapped arguments would give 8 / 8 = 1.
+    assert oracle.normwise_rel_err([[2.0, 8.0]], [[2.0, 0.0]]) == 4.0
+    assert oracle.normwise_rel_err([[2.0, 0.0]], [[2.0, 8.0]]) == 1.0
+    # one max over all rows, not per row: row 0's error 1 over the global max 10
+    # is 0.1; a per-row maximum would give 1 / 1 = 1 for row 0.
+    y_ref = [[1.0, 0.0], [10.0, 0.0]]
+    y = [[2.0, 0.0], [10.0, 0.5]]
+    assert oracle.normwise_rel_err(y, y_ref) == 0.1
+    # sign of the difference does not matter; equal arrays give 0
+    assert oracle.normwise_rel_err([[-3.0]], [[1.0]]) == 4.0
+    assert oracle.normwise_rel_err(y_ref, y_ref) == 0.0
+    # an all-zero reference: the absolute maximum of y (0 when y is zero too)
+    assert oracle.normwise_rel_err([[0.0, -0.25]], [[0.0, 0.0]]) == 0.25
+    assert oracle.normwise_rel_err([[0.0]], [[0.0]]) == 0.0
+
+
+# ---------------------------------------------------------------------------
 # dispatch
 # ---------------------------------------------------------------------------
 def test_dispatch_golden():

@@ -138,7 +138,10 @@ def mxfp8_quantize(v: torch.Tensor):
     _, ex = torch.frexp(amax)               # amax = m * 2^ex, m in [0.5, 1)
     se = (ex.to(torch.int64) - 1) - E4M3_EMAX
     se = torch.where(amax == 0, torch.full_like(se, -127), se).clamp(-127, 127)
-    q = torch.ldexp(blocks.to(torch.float64), (-se).unsqueeze(-1).to(torch.float64))
+    # v / X = v * 2^-se, exact in float64: 2^-se (|se| <= 127) is built from its
+    # exponent bits and the fp32 values times it neither overflow nor underflow.
+    pow2 = ((1023 - se) << 52).view(torch.float64)
+    q = blocks.to(torch.float64) * pow2.unsqueeze(-1)
     q = q.clamp(-E4M3_MAX, E4M3_MAX).to(torch.float32)
     codes = _e4m3_rne_codes(q).reshape(shp)
     scales = (se + 127).to(torch.uint8)

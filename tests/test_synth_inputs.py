@@ -102,3 +102,34 @@ def test_small_bf16_mxfp8_replay_variants():
     assert m["w2_scale"].shape == (12, 64, 1) and m["bias"].shape == (12,)
     r = synth.make_layer_inputs(base.with_(routing="replay"))
     assert r["ids_in"].shape == (16, 3) and r["weights_in"].dtype == torch.float32
+
+
+def _mx_quantize_with_ldexp(v):
+    """The encoder as first written (scaling by torch.ldexp), kept to show the
+    power-of-two multiply that replaced it gives the same codes and scales."""
+    shp = v.shape
+    blocks = v.to(torch.float32).reshape(*shp[:-1], shp[-1] // 32, 32)
+    amax = blocks.abs().amax(dim=-1)
+    _, ex = torch.frexp(amax)
+    se = (ex.to(torch.int64) - 1) - 8
+    se = torch.where(amax == 0, torch.full_like(se, -127), se).clamp(-127, 127)
+    q = torch.ldexp(blocks.to(torch.float64), (-se).unsqueeze(-1).to(torch.float64))
+    q = q.clamp(-448.0, 448.0).to(torch.float32)
+    return _e4m3_rne_codes(q).reshape(shp), (se + 127).to(torch.uint8)
+
+
+def test_mx_quantize_equals_ldexp_form():
+    rng = np.random.default_rng(3)
+    rows = []
+    for lg in range(-149, 128, 3):                      # every fp32 binade, subnormals included
+        rows.append(rng.standard_normal(64) * 2.0 ** lg)
+    v = np.concatenate([np.clip(np.stack(rows), -3.4e38, 3.4e38),
+                        rng.standard_normal((64, 64))]).astype(np.float32)
+    v[3, :32] = 0.0
+    v[4, 5] = np.float32(3.4028235e38)
+    v[5, 7] = -np.float32(1.4e-45)
+    t = torch.from_numpy(v)
+    c1, s1 = synth.mxfp8_quantize(t)
+    c0, s0 = _mx_quantize_with_ldexp(t)
+    assert torch.equal(c1, c0) and torch.equal(s1, s0)
+    assert int(s1.min()) == 0 and int(s1.max()) == 127 + 119   # both ends of the E8M0 range met

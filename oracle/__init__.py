@@ -7,11 +7,13 @@ from .moe_oracle import (  # noqa: F401
     e4m3_value,
     e8m0_value,
     E4M3_TABLE,
+    E8M0_TABLE,
     mx_dequant,
     exact_logits,
     topk_ids,
     softmax_pick_renormalise,
     route,
+    route_certified,
     route_replay,
     route_replay_filtered,
     validate_replay_ids,

@@ -145,6 +145,70 @@ def test_duplicate_gate_columns_tie_to_lower_index():
 
 
 # ---------------------------------------------------------------------------
+# certified routing (the fast form of route for large batches)
+# ---------------------------------------------------------------------------
+def _mx_values(rng, shape):
+    """Random exact MXFP8 values: E4M3 codes times one power of two per 32-block."""
+    codes = rng.integers(0, 256, size=shape).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0             # no NaN codes
+    scales = rng.integers(120, 125, size=shape[:-1] + (shape[-1] // 32,)).astype(np.uint8)
+    return oracle.mx_dequant(codes, scales)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "f32", "mxfp8"])
+def test_route_certified_equals_route_on_random_inputs(kind):
+    rng = np.random.default_rng({"bf16": 40, "f32": 41, "mxfp8": 42}[kind])
+    T, d, E, k = 48, 256, 40, 8
+    x = {"bf16": lambda: _bf16_values(rng, (T, d)),
+         "f32": lambda: _f32(rng.standard_normal((T, d))),
+         "mxfp8": lambda: _mx_values(rng, (T, d))}[kind]()
+    w = _f32(rng.standard_normal((d, E)) / 16)
+    b = _f32(rng.standard_normal(E) * 0.7) if kind != "f32" else None
+    ids, wts, n_exact = oracle.route_certified(x, w, b, k)
+    ids0, wts0, _ = oracle.route(x, w, b, k)
+    assert np.array_equal(ids, ids0)
+    assert np.max(np.abs(wts - wts0)) <= 1e-12
+    assert n_exact < T
+
+
+def test_route_certified_ties_and_near_ties():
+    """Exact ties (a duplicated gate column), all-equal logits (x = 0) and near ties
+    built so that a left-to-right fp64 sum orders two experts the wrong way: column a
+    sums 1 + 64 * 2^-53 = 1 + 2^-47 exactly, which such a sum rounds to 1; column b is
+    1 + 31 * 2^-52, just below a.  Every token must get route()'s ids."""
+    rng = np.random.default_rng(43)
+    d, E, k = 72, 12, 4
+    w = _f32(rng.standard_normal((d, E)) / 8)
+    w[:, 7] = w[:, 3]                                  # experts 3 and 7 tie exactly
+    x = _bf16_values(rng, (30, d))
+    x[5] = 0.0                                         # every logit 0: ids 0..k-1
+    near = np.zeros((4, d), np.float32)
+    near[:, 0] = 1.0
+    near[:, 1:65] = 2.0 ** -53
+    x = np.concatenate([x, near])
+    w[:, 10] = 0.0
+    w[:65, 10] = 1.0                                   # column a: 1 + 2^-47 on the near rows
+    w = w.astype(np.float64)                           # the near-tie weights need fp64
+    w[:, 11] = 0.0
+    w[0, 11] = 1.0 + 31 * 2.0 ** -52                   # column b
+    w[:, 9] = 0.0
+    w[0, 9] = 1.0 + 2.0 ** -52                         # a third, lower near-tie column
+    ids, wts, n_exact = oracle.route_certified(x, w, None, k)
+    ids0, wts0, logits0 = oracle.route(x, w, None, k)
+    assert np.array_equal(ids, ids0)
+    assert np.max(np.abs(wts - wts0)) <= 1e-12
+    assert list(ids[5]) == [0, 1, 2, 3]
+    for t in range(30, 34):
+        assert list(ids[t][:3]) == [10, 11, 9]         # exact order a > b > third
+        assert logits0[t, 10] > logits0[t, 11] > logits0[t, 9]
+    for t in range(30):
+        row = list(ids[t])
+        if 7 in row:
+            assert 3 in row and row.index(3) < row.index(7)
+    assert n_exact >= 5
+
+
+# ---------------------------------------------------------------------------
 # gate weights
 # ---------------------------------------------------------------------------
 def test_weights_closed_forms():

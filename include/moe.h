@@ -111,6 +111,12 @@ moe_status moe_workspace_size(int T, int d, int E, int k, int inter, int dtype, 
 moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Learned routing: gate GEMM, softmax over the E experts, top-k, renormalise.
+ * Defined by: a gating layer picks 8 of 384 experts for each token in each MoE layer,
+ * and a hidden-state difference in the fifth decimal can change the pick (Training
+ * Data podcast page "How Cursor Trained Composer on Fireworks", section on floating
+ * point and MoE; page "Cursor 訓練 Composer 2 的五大工程挑戰", section "浮點數的陷阱").
+ * The pages name neither the gating function nor a tie rule: softmax, top-k with ties
+ * to the lower index, and renormalisation are this library's reading.
  *   x       [T][d] activations in `dtype` (x_scale [T][d/32] E8M0 for MOE_MXFP8,
  *           else NULL; the gate reads the exact dequantised values).
  *   w_gate  fp32 [d][E], 16-byte aligned when E % 4 == 0 (else 4-byte aligned);
@@ -118,10 +124,13 @@ moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
  *           and the weights).
  *   ids     out int32 [T][k]: the k experts with the largest logits, ordered by
  *           (logit descending, expert index ascending).  The selection equals the
- *           one made on the exactly rounded logits: an fp64 GEMM with a rigorous
- *           per-token error bound decides every token it can, and tokens whose
- *           top-(k+1) ordering the bound cannot certify are recomputed with exact
- *           (error-free) summation on the device.
+ *           one made on the exactly rounded logits.  A first pass with a rigorous
+ *           per-logit error bound (the fp64 gate GEMM for fp32 activations and small
+ *           batches; for large bf16 / MXFP8 batches a bf16 matrix-core screen over an
+ *           exact three-way bf16 split of w_gate, followed by fp64 logits of the
+ *           experts the screen cannot exclude) decides every token it can certify;
+ *           the other tokens are recomputed with exact (error-free) summation on the
+ *           device.
  *   weights out fp32 [T][k]: softmax probabilities of the chosen experts
  *           renormalised to sum to one (computed in fp64 from the fp64 logits,
  *           rounded once), in the same column order as ids.
@@ -184,6 +193,10 @@ moe_status moe_route_replay_filtered(const void* x, const uint8_t* x_scale, int 
 /* Counting sort of the T*k (token, slot) pairs by (expert ascending, token
  * ascending), the grouped GEMM's input order.  Positions come from deterministic
  * histograms and prefix sums, never from atomic position counters.
+ * Defined by: tokens are dispatched to their experts and the expert outputs combined
+ * back (Composer 2 Technical Report, section 6.1 "Parallelism", DeepEP dispatch and
+ * combine), and each expert's tokens form one group of the grouped GEMM (section 6.1
+ * "Kernels", Figure 10).  Here the dispatch is local to one GPU.
  *   ids     int32 [T][k] (from moe_route or replayed).  An id outside [0, E) sets
  *           MOE_ERR_BAD_IDS and is treated as expert 0 so every output stays a
  *           valid permutation.
@@ -196,6 +209,10 @@ moe_status moe_dispatch(const int32_t* ids, int T, int E, int k,
 
 /* Grouped SwiGLU expert FFN over the dispatched segments (one grouped GEMM for
  * W1 and W3 with the SwiGLU epilogue, one for W2).
+ * Defined by: the MoE layer runs its experts as grouped GEMMs, with MXFP8 (E4M3
+ * values, one E8M0 scale per 32) or NVFP4 operands (Composer 2 Technical Report,
+ * section 6.1 "Kernels", Figure 10).  The expert's form (SwiGLU) and the shared expert
+ * are not on the pages; they are this library's workload.
  *   x        [T][d] activations in `dtype` (x_scale as in moe_route); rows are
  *            gathered through perm inside the GEMM (no separate permuted copy).
  *   routed   bank of E experts; shared: bank of 1 always-on expert, or NULL.
@@ -240,7 +257,11 @@ moe_status moe_expert_ffn_down(int dtype, int T, int d, int E, int k, int inter,
                                const moe_expert_bank* routed, const moe_expert_bank* shared,
                                void* out, void* ws, size_t ws_bytes, void* stream);
 
-/* Fixed-order combine: y[t] = round( (...((w[t,0]*O0 + w[t,1]*O1) + ...) + w[t,k-1]*O_{k-1})
+/* Defined by: the combine of the expert outputs is kept in BF16 (Composer 2 Technical
+ * Report, section 6.1 "Parallelism"), and batch-invariant kernels sum in one fixed
+ * order so inference and training agree bit for bit (both podcast pages, sections on
+ * floating point and MoE).
+ * Fixed-order combine: y[t] = round( (...((w[t,0]*O0 + w[t,1]*O1) + ...) + w[t,k-1]*O_{k-1})
  * + S[t] ) with O_r = out[row_of[t*k + r]] and S[t] = out[T*k + t] when has_shared;
  * fp32 fused multiply-adds in rank order r = 0..k-1, shared output last, one final
  * rounding to the output dtype.  No atomics.

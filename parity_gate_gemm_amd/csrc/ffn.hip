@@ -23,29 +23,10 @@ constexpr int BNR = 128;      // B rows (output features) staged per tile
 constexpr int BK = 64;        // reduction step
 constexpr int LDSS = BK + 8;  // LDS row stride in bf16 elements (144 B: conflict-free 16-B reads)
 
-// Tuning knobs of the bf16 grouped GEMM (same results for every setting).
-#ifndef MOE_GEMM_DEPTH
-#define MOE_GEMM_DEPTH 1
-#endif
-#ifndef MOE_GEMM_NT_B
-#define MOE_GEMM_NT_B 0
-#endif
-constexpr int kGemmDepth = MOE_GEMM_DEPTH;   // K-steps of loads in flight per thread
-constexpr bool kGemmNtB = MOE_GEMM_NT_B != 0; // nontemporal weight loads
 // Widest tile (wavefronts along N) each bf16 GEMM uses where the shape divides; the
 // narrower tiles give the same bits (each output is the same MFMA sequence over K).
-#ifndef MOE_GEMM1_WN
-#define MOE_GEMM1_WN 4
-#endif
-#ifndef MOE_GEMM2_WN
-#define MOE_GEMM2_WN 4
-#endif
-#ifndef MOE_GEMM_DMA
-#define MOE_GEMM_DMA 0
-#endif
-#ifndef MOE_GEMM_NARROW_WAVES
-#define MOE_GEMM_NARROW_WAVES 1
-#endif
+constexpr int kGemm1Wn = 4;
+constexpr int kGemm2Wn = 4;
 
 
 // Segment table: segment s < E is routed expert s (rows offsets[s]..offsets[s+1]-1),
@@ -117,10 +98,14 @@ struct GemmArgs {
 // of the 128 x (64 * WN) tile as 2 x 2 MFMA 32x32x16 blocks.  In GEMM1 the staged B
 // rows alternate 32-row blocks of W1 and W3 for the same features, so a wavefront's
 // two column blocks are the W1 and W3 halves of 32 features.
+// Rows past the segment's end are neither loaded nor multiplied: their LDS rows hold
+// zeros, and a wavefront skips the MFMAs of a 32-row block that holds no valid row (a
+// row of an MFMA result depends only on the same row of A, so the valid rows get the
+// same bits whatever is skipped).
 // Wide tiles (WN >= 4) are held to 128 registers so that 4 wavefronts fit per SIMD.
-template <int MODE, int DEPTH, bool NT_B, int WN>
+template <int MODE, int WN>
 __global__ __launch_bounds__(128 * WN)
-__attribute__((amdgpu_waves_per_eu(WN >= 4 ? 4 : MOE_GEMM_NARROW_WAVES)))
+__attribute__((amdgpu_waves_per_eu(WN >= 4 ? 4 : 1)))
 void grouped_gemm_bf16_kernel(GemmArgs g) {
   constexpr bool G1 = MODE != 1;                // GEMM1 operands (gathered x; W1 / W3)
   constexpr int NTHR = 128 * WN;
@@ -156,14 +141,16 @@ void grouped_gemm_bf16_kernel(GemmArgs g) {
   const int wm = wave / WN, wn = wave % WN;
   const int lr = tid >> 3, lc = (tid & 7) * 8;   // loader: rows lr + RSTEP i, column chunk lc
 
-  // ---- per-thread source rows.  A tile row r >= mrows only feeds output row r,
-  //      which is never stored, so it re-reads the tile's first row instead. ----
+  // ---- per-thread source rows.  A tile row r >= mrows is not loaded (zeros in LDS);
+  //      it only feeds output row r, which is never stored. ----
   const uint16_t* aptr[LA];
   const uint16_t* bptr[LB];
+  bool alive[LA];
   int bad = 0;
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
     const int r = lr + RSTEP * i;
+    alive[i] = r < mrows;
     const long long j = (long long)row0 + (r < mrows ? r : 0);
     long long src;
     if (G1) {
@@ -206,58 +193,55 @@ void grouped_gemm_bf16_kernel(GemmArgs g) {
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+  // 32-row blocks of this wavefront that hold at least one valid row (wave-uniform)
+  const bool live0 = wm * 64 < mrows, live1 = wm * 64 + 32 < mrows;
 
-  // K loop: DEPTH register sets keep DEPTH K-steps of global loads in flight; each
-  // step goes registers -> LDS -> MFMA.  Weight (B) loads may bypass L2 retention
-  // (nontemporal): every weight byte is used by one tile only.
-  u32x4_t ra[DEPTH][LA], rb[DEPTH][LB];
-  auto gload = [&](u32x4_t(&A)[LA], u32x4_t(&B)[LB], int kofs) {
+  // K loop: one K-step of global loads in flight per thread; each step goes
+  // registers -> LDS -> MFMA.
+  u32x4_t ra[LA], rb[LB];
 #pragma unroll
-    for (int i = 0; i < LA; ++i) A[i] = *(const u32x4_t*)(aptr[i] + kofs);
+  for (int i = 0; i < LA; ++i) ra[i] = u32x4_t{0u, 0u, 0u, 0u};
+  auto gload = [&](int kofs) {
 #pragma unroll
-    for (int i = 0; i < LB; ++i) {
-      if (NT_B)
-        B[i] = __builtin_nontemporal_load((const u32x4_t*)(bptr[i] + kofs));
-      else
-        B[i] = *(const u32x4_t*)(bptr[i] + kofs);
-    }
+    for (int i = 0; i < LA; ++i)
+      if (alive[i]) ra[i] = *(const u32x4_t*)(aptr[i] + kofs);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) rb[i] = *(const u32x4_t*)(bptr[i] + kofs);
   };
-  auto step = [&](u32x4_t(&A)[LA], u32x4_t(&B)[LB], int knext) {
+  gload(0);
+  for (int k0 = 0; k0 < g.K; k0 += BK) {
 #pragma unroll
-    for (int i = 0; i < LA; ++i) *(u32x4_t*)&sA[(lr + RSTEP * i) * LDSS + lc] = A[i];
+    for (int i = 0; i < LA; ++i) *(u32x4_t*)&sA[(lr + RSTEP * i) * LDSS + lc] = ra[i];
 #pragma unroll
-    for (int i = 0; i < LB; ++i) *(u32x4_t*)&sB[(lr + RSTEP * i) * LDSS + lc] = B[i];
+    for (int i = 0; i < LB; ++i) *(u32x4_t*)&sB[(lr + RSTEP * i) * LDSS + lc] = rb[i];
     __syncthreads();
-    if (knext < g.K) gload(A, B, knext);
+    if (k0 + BK < g.K) gload(k0 + BK);
+    if (live0) {
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      const int kc = kk + (lane >> 5) * 8;
-      bf16x8_t af[2], bf[2];
+      for (int kk = 0; kk < BK; kk += 16) {
+        const int kc = kk + (lane >> 5) * 8;
+        bf16x8_t af[2], bf[2];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const u32x4_t u = *(const u32x4_t*)&sA[(wm * 64 + mb * 32 + (lane & 31)) * LDSS + kc];
-        af[mb] = __builtin_bit_cast(bf16x8_t, u);
-      }
+        for (int mb = 0; mb < 2; ++mb) {
+          const u32x4_t u = *(const u32x4_t*)&sA[(wm * 64 + mb * 32 + (lane & 31)) * LDSS + kc];
+          af[mb] = __builtin_bit_cast(bf16x8_t, u);
+        }
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const u32x4_t u = *(const u32x4_t*)&sB[(wn * 64 + nb * 32 + (lane & 31)) * LDSS + kc];
-        bf[nb] = __builtin_bit_cast(bf16x8_t, u);
-      }
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+        for (int nb = 0; nb < 2; ++nb) {
+          const u32x4_t u = *(const u32x4_t*)&sB[(wn * 64 + nb * 32 + (lane & 31)) * LDSS + kc];
+          bf[nb] = __builtin_bit_cast(bf16x8_t, u);
+        }
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bf[nb], acc[mb][nb], 0, 0, 0);
+          acc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0], bf[nb], acc[0][nb], 0, 0, 0);
+        if (live1) {
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            acc[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1], bf[nb], acc[1][nb], 0, 0, 0);
+        }
+      }
     }
     __syncthreads();
-  };
-#pragma unroll
-  for (int s2 = 0; s2 < DEPTH; ++s2)
-    if (s2 * BK < g.K) gload(ra[s2], rb[s2], s2 * BK);
-  for (int k0 = 0; k0 < g.K; k0 += DEPTH * BK) {
-#pragma unroll
-    for (int s2 = 0; s2 < DEPTH; ++s2)
-      if (k0 + s2 * BK < g.K) step(ra[s2], rb[s2], k0 + (s2 + DEPTH) * BK);
   }
 
   // ---- epilogue.  Accumulator element v of a lane is C[i][j] with
@@ -289,222 +273,6 @@ void grouped_gemm_bf16_kernel(GemmArgs g) {
         for (int nb = 0; nb < 2; ++nb) {
           const int col = n0 + wn * 64 + nb * 32 + j;
           __builtin_nontemporal_store(f32_to_bf16(acc[mb][nb][v]), &g.out[orow * g.N + col]);
-        }
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// bf16 grouped GEMM with a three-stage LDS ring filled by direct global->LDS loads
-// (global_load_lds_dwordx4: lane l of a wavefront writes its 16 bytes at base + 16 l).
-// No registers hold data in flight, so two K-steps of loads stay outstanding while a
-// third is multiplied.  Same tile order, tile shape (128 x 64 WN), MFMA sequence and
-// epilogue as grouped_gemm_bf16_kernel, hence the same bits.
-// A stage holds the A tile (128 rows) then the B tile (64 WN rows), 128 bytes per row.
-// The sixteen-byte chunk c of row r is stored in slot c ^ swz(r), swz(r) = (r ^ (r >> 3)) & 7:
-// the 8 (or 16) consecutive rows one ds_read_b128 phase touches then fall in distinct banks.
-// Synchronisation per K-step: wait for this wavefront's loads of the step (s_waitcnt
-// vmcnt), then s_barrier, so every wavefront's loads of the step have landed and every
-// wavefront has finished reading the stage that the next loads overwrite.
-// ---------------------------------------------------------------------------
-constexpr int kDmaStages = 3;
-
-__device__ __forceinline__ int lds_swz(int r) { return (r ^ (r >> 3)) & 7; }
-
-// s_waitcnt with only vmcnt limited (expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-template <int MODE, int WN>
-__global__ __launch_bounds__(128 * WN) void grouped_gemm_bf16_dma_kernel(GemmArgs g) {
-  constexpr int NTHR = 128 * WN, NW = 2 * WN;
-  constexpr int BNW = 64 * WN;
-  constexpr int LA = BM / (8 * NW), LB = BNW / (8 * NW);   // 1 KB load instructions per wavefront
-  constexpr int STAGE = (BM + BNW) * 128;                  // bytes per stage
-  static_assert(LA * 8 * NW == BM && LB * 8 * NW == BNW, "loader shape");
-  static_assert(kDmaStages * STAGE <= 160 * 1024, "LDS budget");
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[STAGE];
-
-  // ---- tile decode (identical to grouped_gemm_bf16_kernel) ----
-  const int total = g.mstart[g.S] * g.NT;
-  int tile;
-  if (!xcd_tile<0>(total, tile)) return;
-  int lo = 0, hi = g.S;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (g.mstart[mid] * g.NT <= tile) lo = mid; else hi = mid;
-  }
-  const int s = lo;
-  const int mtiles = g.mstart[s + 1] - g.mstart[s];
-  const int local = tile - g.mstart[s] * g.NT;
-  const int grp = local / (kGroupM * g.NT), rem = local % (kGroupM * g.NT);
-  const int gm = min(kGroupM, mtiles - grp * kGroupM);
-  const int nt = rem / gm, mt = grp * kGroupM + rem % gm;
-  const int row0 = g.rowstart[s] + mt * BM;
-  const int mrows = min(BM, g.rowcount[s] - mt * BM);
-  const int n0 = nt * (MODE == 0 ? BNW / 2 : BNW);
-  const bool is_shared = (s == g.E);
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-
-  // ---- loader: instruction i of this wavefront fills stage rows 8 (wave LA + i) + lane / 8
-  //      (A) or 8 (wave LB + i) + lane / 8 (B), slot lane % 8 <- chunk slot ^ swz(row). ----
-  const uint16_t* aptr[LA];
-  const uint16_t* bptr[LB];
-  int bad = 0;
-#pragma unroll
-  for (int i = 0; i < LA; ++i) {
-    const int r = 8 * (wave * LA + i) + (lane >> 3);
-    const int chunk = (lane & 7) ^ lds_swz(r);
-    const long long j = (long long)row0 + (r < mrows ? r : 0);
-    long long src;
-    if (MODE == 0) {
-      src = is_shared ? j - g.Tk : (long long)(g.perm[j] / g.k);
-      if (src < 0 || src >= g.T) {
-        bad = 1;
-        src = 0;
-      }
-    } else {
-      src = j;
-    }
-    aptr[i] = g.a + src * (long long)g.K + chunk * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < LB; ++i) {
-    const int r = 8 * (wave * LB + i) + (lane >> 3);
-    const int chunk = (lane & 7) ^ lds_swz(r);
-    long long brow;
-    const uint16_t* bank;
-    if (MODE == 0) {
-      const int blk = r >> 5, within = r & 31;
-      bank = (blk & 1) ? (is_shared ? g.sb1 : g.b1) : (is_shared ? g.sb0 : g.b0);
-      brow = (long long)n0 + (blk >> 1) * 32 + within;
-    } else {
-      bank = is_shared ? g.sb0 : g.b0;
-      brow = (long long)n0 + r;
-    }
-    const long long e = is_shared ? 0 : s;
-    bptr[i] = bank + (e * g.N + brow) * (long long)g.K + chunk * 8;
-  }
-  if (bad) raise_flag(g.flag, kFlagCorrupt);
-
-  typedef __attribute__((address_space(3))) void* lds_ptr;
-  auto issue = [&](uint8_t* st, int k0) {
-#if defined(__HIP_DEVICE_COMPILE__)   // a gfx950 builtin: device pass only
-#pragma unroll
-    for (int i = 0; i < LA; ++i)
-      __builtin_amdgcn_global_load_lds(aptr[i] + k0, (lds_ptr)(st + (wave * LA + i) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < LB; ++i)
-      __builtin_amdgcn_global_load_lds(bptr[i] + k0, (lds_ptr)(st + BM * 128 + (wave * LB + i) * 1024), 16,
-                                       0, 0);
-#endif
-  };
-
-  // ---- fragment addresses: lane reads row (block base + lane % 32), chunk 2 kk + lane / 32.
-  //      Offsets within a stage, for A blocks [b][kk] and B blocks [b][kk]. ----
-  uint32_t aof[2][4], bof[2][4];
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int ra = wm * 64 + b * 32 + (lane & 31);
-    const int rb = wn * 64 + b * 32 + (lane & 31);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int chunk = 2 * kk + (lane >> 5);
-      aof[b][kk] = ra * 128 + ((chunk ^ lds_swz(ra)) << 4);
-      bof[b][kk] = BM * 128 + rb * 128 + ((chunk ^ lds_swz(rb)) << 4);
-    }
-  }
-  f32x16_t acc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
-
-  // The fragment reads are issued from inline assembly, each batch ending in its own
-  // lgkmcnt(0) wait, so that the compiler does not tie them to the outstanding
-  // global->LDS loads of the other stages (it would wait for all of them); the
-  // ordering against those loads is the explicit vmcnt wait and barrier of the K loop.
-  auto compute = [&](uint32_t st) {
-#pragma unroll
-    for (int kp = 0; kp < 4; kp += 2) {
-      u32x4_t f[8];
-      asm volatile(
-          "ds_read_b128 %0, %8\n\t"
-          "ds_read_b128 %1, %9\n\t"
-          "ds_read_b128 %2, %10\n\t"
-          "ds_read_b128 %3, %11\n\t"
-          "ds_read_b128 %4, %12\n\t"
-          "ds_read_b128 %5, %13\n\t"
-          "ds_read_b128 %6, %14\n\t"
-          "ds_read_b128 %7, %15\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5]),
-            "=&v"(f[6]), "=&v"(f[7])
-          : "v"(st + aof[0][kp]), "v"(st + aof[1][kp]), "v"(st + bof[0][kp]), "v"(st + bof[1][kp]),
-            "v"(st + aof[0][kp + 1]), "v"(st + aof[1][kp + 1]), "v"(st + bof[0][kp + 1]),
-            "v"(st + bof[1][kp + 1]));
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8_t, f[4 * h + mb]), __builtin_bit_cast(bf16x8_t, f[4 * h + 2 + nb]),
-                acc[mb][nb], 0, 0, 0);
-    }
-  };
-
-  // ---- K loop over the ring; stage i lives in st[i % 3] ----
-  typedef __attribute__((address_space(3))) uint8_t lds_u8;
-  const uint32_t l0 = (uint32_t)(uintptr_t)(lds_u8*)st0, l1 = (uint32_t)(uintptr_t)(lds_u8*)st1,
-                 l2 = (uint32_t)(uintptr_t)(lds_u8*)st2;
-  const int nsteps = g.K / BK;
-  issue(st0, 0);
-  if (nsteps > 1) issue(st1, BK);
-  auto kstep = [&](int i, uint32_t cur, uint8_t* nxt) {
-    if (i + 1 < nsteps)
-      wait_vmcnt<LA + LB>();
-    else
-      wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    if (i + 2 < nsteps) issue(nxt, (i + 2) * BK);
-    compute(cur);
-  };
-  for (int i = 0; i < nsteps; i += kDmaStages) {
-    kstep(i, l0, st2);
-    if (i + 1 < nsteps) kstep(i + 1, l1, st0);
-    if (i + 2 < nsteps) kstep(i + 2, l2, st1);
-  }
-
-  // ---- epilogue (as grouped_gemm_bf16_kernel) ----
-  const int j = lane & 31;
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int i = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      const int r = wm * 64 + mb * 32 + i;
-      if (r >= mrows) continue;
-      const long long orow = (long long)row0 + r;
-      if (MODE == 0) {
-        const int col = n0 + wn * 32 + j;
-        g.out[orow * g.N + col] = f32_to_bf16(silu_f32(acc[mb][0][v]) * acc[mb][1][v]);
-      } else {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const int col = n0 + wn * 64 + nb * 32 + j;
-          g.out[orow * g.N + col] = f32_to_bf16(acc[mb][nb][v]);
         }
       }
     }
@@ -656,26 +424,10 @@ static int bf16_wn(int n, int per_wave, int max_wn) {
 
 template <int MODE>
 static void launch_bf16(int wn, unsigned grid, hipStream_t s, const GemmArgs& g) {
-#if MOE_GEMM_DMA
-  if (wn == 4) {
-    grouped_gemm_bf16_dma_kernel<MODE, 4><<<grid, 512, 0, s>>>(g);
-    return;
-  }
-#endif
-  switch (wn) {
-#if MOE_GEMM1_WN >= 8 || MOE_GEMM2_WN >= 8
-    case 8:
-      grouped_gemm_bf16_kernel<MODE, kGemmDepth, kGemmNtB, 8><<<grid, 1024, 0, s>>>(g);
-      break;
-#endif
-#if MOE_GEMM1_WN >= 4 || MOE_GEMM2_WN >= 4
-    case 4:
-      grouped_gemm_bf16_kernel<MODE, kGemmDepth, kGemmNtB, 4><<<grid, 512, 0, s>>>(g);
-      break;
-#endif
-    default:
-      grouped_gemm_bf16_kernel<MODE, kGemmDepth, kGemmNtB, 2><<<grid, 256, 0, s>>>(g);
-  }
+  if (wn == 4)
+    grouped_gemm_bf16_kernel<MODE, 4><<<grid, 512, 0, s>>>(g);
+  else
+    grouped_gemm_bf16_kernel<MODE, 2><<<grid, 256, 0, s>>>(g);
 }
 
 // GEMM1 half: segment table, then h = silu(x W1) * (x W3) for every dispatched row.
@@ -771,7 +523,7 @@ static moe_status run_gate_up(const void* x, const uint8_t* xs, int dtype, int T
     g.out = (uint16_t*)p.h;
     g.out_pre = pre;
     g.flag = p.flag;
-    const int wn = bf16_wn(inter, 32, MOE_GEMM1_WN);
+    const int wn = bf16_wn(inter, 32, kGemm1Wn);
     g.NT = inter / (32 * wn);
     const long long grid = tile_grid(p.mt_bound * g.NT, 0);
     if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
@@ -880,7 +632,7 @@ static moe_status run_down(int dtype, int T, int d, int E, int k, int inter,
     g.S = p.S;
     g.out = (uint16_t*)out;
     g.flag = p.flag;
-    const int wn = bf16_wn(d, 64, MOE_GEMM2_WN);
+    const int wn = bf16_wn(d, 64, kGemm2Wn);
     g.NT = d / (64 * wn);
     const long long grid = tile_grid(p.mt_bound * g.NT, 0);
     if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
@@ -946,7 +698,7 @@ moe_status ffn_recompute_pre(const void* x, int T, int d, int E, int k, int inte
   g.out = nullptr;
   g.out_pre = pre;
   g.flag = flag;
-  const int wn = bf16_wn(inter, 32, MOE_GEMM1_WN);
+  const int wn = bf16_wn(inter, 32, kGemm1Wn);
   g.NT = inter / (32 * wn);
   const long long mt_bound = (Tk + (long long)E * (BM - 1)) / BM + (has_shared ? (T + BM - 1) / BM : 0);
   const long long grid = tile_grid(mt_bound * g.NT, 0);
@@ -990,7 +742,7 @@ extern "C" moe_status moe_expert_ffn_gate_up_save(const void* x, const uint8_t* 
                                                   void* stream) {
   moe_status st = check_ffn_shape(dtype, T, d, E, k, inter, routed, shared, ws, ws_bytes);
   if (st != MOE_OK) return st;
-  if (dtype != MOE_BF16 || MOE_GEMM_DMA) return MOE_ERR_UNSUPPORTED;
+  if (dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (x_scale || !offsets) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !perm || !pre || !aligned(x, 16) || !aligned(pre, 16)) return MOE_ERR_INVALID_ARG;

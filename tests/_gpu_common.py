@@ -92,6 +92,61 @@ def compare_rows(res_gpu, ref, rows, dtype, replay=False):
     return err
 
 
+def check_routing_every_token(inp, res, k, E):
+    """Every token's ids bit-exact against the oracle's certified routing (the ids of
+    ``oracle.route``), every weight within WEIGHT_TOL, and offsets / perm / row_of equal
+    to ``oracle.dispatch`` of the oracle's ids."""
+    x = values(inp["x"], inp.get("x_scale"))
+    ids, w, n_exact = oracle.route_certified(x, host(inp["w_gate"]), host(inp.get("bias")), k)
+    del x
+    gids = res["ids"].cpu().numpy()
+    T = ids.shape[0]
+    bad = np.nonzero((gids != ids).any(axis=1))[0]
+    say(f"  ids exact on {T - len(bad)}/{T} tokens ({n_exact} decided by exact sums in the oracle)")
+    assert len(bad) == 0, bad[:10]
+    gw = res["weights"].cpu().numpy().astype(np.float64)
+    werr = float(np.max(np.abs(gw - w))) if T else 0.0
+    say(f"  weights max abs err {werr:.2e} over {T} tokens")
+    assert werr <= WEIGHT_TOL
+    off, perm, row_of = oracle.dispatch(ids, E)
+    assert np.array_equal(res["offsets"].cpu().numpy(), off)
+    assert np.array_equal(res["perm"].cpu().numpy(), perm)
+    assert np.array_equal(res["row_of"].cpu().numpy(), row_of)
+    say(f"  offsets, perm and row_of exact on {T * k} pairs")
+    return ids
+
+
+def sample_rows(ids, offsets, perm, k, tile, shared, n, seed):
+    """About n token rows that cover the grouped GEMM's edge cases: the first and last
+    token of the largest segment and the tokens on its first row-tile boundaries, the
+    last token of the largest segment with a ragged (partial) last tile, tokens on the
+    shared expert's tile boundaries, the first and last token, then random tokens."""
+    ids = np.asarray(ids)
+    off = np.asarray(offsets).astype(np.int64)
+    perm = np.asarray(perm).astype(np.int64)
+    T = ids.shape[0]
+    seg = np.diff(off)
+    rows = {0, T - 1}
+    e_big = int(np.argmax(seg))
+    toks = perm[off[e_big]:off[e_big + 1]] // k
+    rows |= {int(toks[0]), int(toks[-1])}
+    for b in range(tile, min(len(toks), 3 * tile + 1), tile):
+        rows |= {int(toks[b - 1]), int(toks[b])}
+    ragged = [e for e in range(len(seg)) if seg[e] % tile]
+    if ragged:
+        e_r = max(ragged, key=lambda e: seg[e])
+        rows.add(int(perm[off[e_r + 1] - 1] // k))
+    if shared:
+        for b in range(tile, min(T, 3 * tile + 1), tile):
+            rows |= {b - 1, b}
+        rows |= {T // 2, (T // tile) * tile - 1}
+    rng = np.random.default_rng(seed)
+    while len(rows) < min(n, T):
+        rows.add(int(rng.integers(0, T)))
+    rows = {r for r in rows if 0 <= r < T}
+    return np.array(sorted(rows))
+
+
 def check_dispatch_properties(ids_gpu, offsets, perm, row_of, E):
     """Properties that pin the counting sort at any size (computed on the host)."""
     ids = ids_gpu.cpu().numpy().astype(np.int64)

@@ -1,11 +1,15 @@
 """GPU parity at the full workload sizes, in the launch configuration the benchmark
 times (one workspace, the five C calls on the current stream).
 
-The oracle recomputes sampled tokens one by one (routing and every expert FFN are
-row-local, so a token's oracle result does not depend on the rest of the batch).
-Dispatch is checked bit-exactly against the oracle where its input ids come from the
-generator (router replay) and by its defining properties elsewhere.  Determinism:
-10 runs bitwise, and a token permutation permutes the output bitwise.
+Routing is checked on every token: the oracle's certified routing (an fp64 product
+with a rigorous per-logit bound, exact sums for every token the bound cannot order)
+gives exactly the ids of the oracle's exact-logit routing, and the GPU ids, weights and
+dispatch arrays are compared with it and with the oracle's dispatch of those ids.
+The layer output is compared on sampled tokens that cover the grouped GEMM's edges
+(routing and every expert FFN are row-local, so a token's oracle result does not depend
+on the rest of the batch); on the small-batch workload on every token.
+Determinism: 10 runs bitwise, a token permutation permutes the output bitwise, and a
+token alone gives its row of the batch bitwise.
 """
 import numpy as np
 import pytest
@@ -14,68 +18,95 @@ import torch
 import oracle
 import parity_gate_gemm_amd as pg
 import synth
-from _gpu_common import (check_dispatch_properties, compare_rows, oracle_for_rows, run_layer,
-                         say)
+from _gpu_common import (check_routing_every_token, compare_rows, oracle_for_rows, run_layer,
+                         sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 
-
-def _sample_rows(res, T, n, seed):
-    """n token rows: the first token of the largest segment (multi-tile), the last
-    token of the batch, and random others."""
-    rng = np.random.default_rng(seed)
-    ids = res["ids"].cpu().numpy()
-    off = res["offsets"].cpu().numpy()
-    e_big = int(np.argmax(np.diff(off)))
-    t_big = int(np.nonzero((ids == e_big).any(axis=1))[0][-1])
-    rows = {t_big, T - 1}
-    while len(rows) < n:
-        rows.add(int(rng.integers(0, T)))
-    return np.array(sorted(rows))
+BF16_TILE = 128      # rows per tile of the bf16 grouped GEMMs
+MX_TILE = 256        # rows per tile of the MXFP8 grouped GEMMs at d, I multiples of 512
 
 
-@pytest.fixture(scope="module")
-def c2():
-    wl = synth.WORKLOADS["bf16_t4096"]
-    say("drawing bf16_t4096 inputs on the GPU")
+def _fixture(name):
+    wl = synth.WORKLOADS[name]
+    say(f"drawing {name} inputs on the GPU")
     inp = synth.make_layer_inputs(wl, device="cuda")
     torch.cuda.synchronize()
-    yield wl, inp
-    del inp
+    return wl, inp
+
+
+def _permuted(inp, p):
+    out = dict(inp, x=inp["x"][p].contiguous())
+    if inp.get("x_scale") is not None:
+        out["x_scale"] = inp["x_scale"][p].contiguous()
+    if inp.get("ids_in") is not None:
+        out["ids_in"] = inp["ids_in"][p].contiguous()
+    if inp.get("weights_in") is not None:
+        out["weights_in"] = inp["weights_in"][p].contiguous()
+    return out
+
+
+def _invariance(wl, inp, base, ws, seed, singles, replay=False):
+    """10 runs bitwise, a token permutation, and single tokens against the batch."""
+    for _ in range(9):
+        r = run_layer(inp, wl.k, replay=replay, ws=ws)
+        assert torch.equal(r["y"], base["y"]) and torch.equal(r["ids"], base["ids"])
+    say("  10 runs bitwise equal")
+    p = torch.randperm(wl.T, generator=torch.Generator().manual_seed(seed)).cuda()
+    rp = run_layer(_permuted(inp, p), wl.k, replay=replay, ws=ws)
+    assert torch.equal(rp["ids"], base["ids"][p])
+    assert torch.equal(rp["weights"], base["weights"][p])
+    assert torch.equal(rp["y"], base["y"][p])
+    say("  token permutation permutes ids, weights and y bitwise")
+    for t in singles:
+        one = _permuted(inp, torch.tensor([t], device="cuda"))
+        r1 = run_layer(one, wl.k, replay=replay)
+        assert torch.equal(r1["ids"][0], base["ids"][t])
+        assert torch.equal(r1["weights"][0], base["weights"][t])
+        assert torch.equal(r1["y"][0], base["y"][t])
+    say(f"  tokens {list(singles)} alone equal their batch rows bitwise")
+
+
+# ---------------------------------------------------------------------------
+# bf16, T = 4096, learned routing, shared expert
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def c2():
+    wl, inp = _fixture("bf16_t4096")
+    ws = pg.Workspace(wl.T, wl.d, wl.E, wl.k, wl.inter, pg.MOE_BF16)
+    res = run_layer(inp, wl.k, ws=ws)
+    yield wl, inp, ws, res
+    del inp, res
     torch.cuda.empty_cache()
 
 
+def test_bf16_t4096_routing_and_dispatch_every_token(c2):
+    wl, inp, _, res = c2
+    say("case bf16_t4096 routing and dispatch on every token")
+    check_routing_every_token(inp, res, wl.k, wl.E)
+
+
 def test_bf16_t4096_sampled_parity(c2):
-    wl, inp = c2
-    say("case bf16_t4096 sampled parity")
-    res = run_layer(inp, wl.k)
-    check_dispatch_properties(res["ids"], res["offsets"], res["perm"], res["row_of"], wl.E)
-    rows = _sample_rows(res, wl.T, 4, 1)
-    ref = oracle_for_rows(inp, rows, wl.k)
-    err = compare_rows(res, ref, rows, "bf16")
-    say(f"  rows {rows.tolist()} normwise err {err:.3e}")
+    wl, inp, _, res = c2
+    rows = sample_rows(res["ids"].cpu().numpy(), res["offsets"].cpu().numpy(),
+                       res["perm"].cpu().numpy(), wl.k, BF16_TILE, True, 32, 1)
+    say(f"case bf16_t4096 layer output on {len(rows)} tokens {rows.tolist()}")
+    err = compare_rows(res, oracle_for_rows(inp, rows, wl.k), rows, "bf16")
+    say(f"  normwise err {err:.3e}")
 
 
 def test_bf16_t4096_determinism_and_permutation(c2):
-    wl, inp = c2
-    say("case bf16_t4096 determinism")
-    ws = pg.Workspace(wl.T, wl.d, wl.E, wl.k, wl.inter, pg.MOE_BF16)
-    base = run_layer(inp, wl.k, ws=ws)
-    for _ in range(9):
-        r = run_layer(inp, wl.k, ws=ws)
-        assert torch.equal(r["y"], base["y"]) and torch.equal(r["ids"], base["ids"])
-    p = torch.randperm(wl.T, generator=torch.Generator().manual_seed(1)).cuda()
-    rp = run_layer(dict(inp, x=inp["x"][p].contiguous()), wl.k, ws=ws)
-    assert torch.equal(rp["ids"], base["ids"][p])
-    assert torch.equal(rp["y"], base["y"][p])
+    wl, inp, ws, res = c2
+    say("case bf16_t4096 determinism, permutation, single tokens")
+    _invariance(wl, inp, res, ws, 1, (0, 2049, wl.T - 1))
 
 
+# ---------------------------------------------------------------------------
+# router replay: Zipf(1.2) ids, Dirichlet(1) weights, same shapes as bf16 T = 4096
+# ---------------------------------------------------------------------------
 @pytest.fixture(scope="module")
 def c3():
-    wl = synth.WORKLOADS["replay_zipf_t4096"]
-    say("drawing replay_zipf_t4096 inputs on the GPU")
-    inp = synth.make_layer_inputs(wl, device="cuda")
-    torch.cuda.synchronize()
+    wl, inp = _fixture("replay_zipf_t4096")
     yield wl, inp
     del inp
     torch.cuda.empty_cache()
@@ -87,23 +118,20 @@ def test_replay_zipf_t4096(c3):
     ws = pg.Workspace(wl.T, wl.d, wl.E, wl.k, wl.inter, pg.MOE_BF16)
     res = run_layer(inp, wl.k, replay=True, ws=ws)
     assert torch.equal(res["weights"], inp["weights_in"])
-    off, perm, row_of = oracle.dispatch(inp["ids_in"].cpu().numpy(), wl.E)
+    ids_in = inp["ids_in"].cpu().numpy()
+    off, perm, row_of = oracle.dispatch(ids_in, wl.E)
     assert np.array_equal(res["offsets"].cpu().numpy(), off)
     assert np.array_equal(res["perm"].cpu().numpy(), perm)
     assert np.array_equal(res["row_of"].cpu().numpy(), row_of)
     seg = np.diff(off)
-    say(f"  segment rows: max {seg.max()} median {int(np.median(seg))} min {seg.min()}")
-    rows = _sample_rows(dict(res, ids=inp["ids_in"]), wl.T, 4, 2)
+    say(f"  dispatch exact on {wl.T * wl.k} pairs; segment rows: max {seg.max()} "
+        f"median {int(np.median(seg))} min {seg.min()}")
+    rows = sample_rows(ids_in, off, perm, wl.k, BF16_TILE, True, 32, 2)
+    say(f"  layer output on {len(rows)} tokens {rows.tolist()}")
     ref = oracle_for_rows(inp, rows, wl.k, replay=True)
     err = compare_rows(dict(res, ids=inp["ids_in"]), ref, rows, "bf16", replay=True)
-    say(f"  rows {rows.tolist()} normwise err {err:.3e}")
-    # bitwise over 10 runs and under token reordering
-    for _ in range(9):
-        assert torch.equal(run_layer(inp, wl.k, replay=True, ws=ws)["y"], res["y"])
-    p = torch.randperm(wl.T, generator=torch.Generator().manual_seed(2)).cuda()
-    pin = dict(inp, x=inp["x"][p].contiguous(), ids_in=inp["ids_in"][p].contiguous(),
-               weights_in=inp["weights_in"][p].contiguous())
-    assert torch.equal(run_layer(pin, wl.k, replay=True, ws=ws)["y"], res["y"][p])
+    say(f"  normwise err {err:.3e}")
+    _invariance(wl, inp, res, ws, 2, (0, 1234, wl.T - 1), replay=True)
 
 
 def test_replay_of_learned_ids_equals_learned_t4096(c3):
@@ -119,61 +147,74 @@ def test_replay_of_learned_ids_equals_learned_t4096(c3):
     assert torch.equal(rep2["y"], learned["y"])
 
 
+# ---------------------------------------------------------------------------
+# small batch, weight streaming: T = 128, no shared expert
+# ---------------------------------------------------------------------------
 @pytest.fixture(scope="module")
 def c4():
-    wl = synth.WORKLOADS["bf16_t128_stream"]
-    say("drawing bf16_t128_stream inputs on the GPU")
-    inp = synth.make_layer_inputs(wl, device="cuda")
-    torch.cuda.synchronize()
-    yield wl, inp
-    del inp
+    wl, inp = _fixture("bf16_t128_stream")
+    ws = pg.Workspace(wl.T, wl.d, wl.E, wl.k, wl.inter, pg.MOE_BF16)
+    res = run_layer(inp, wl.k, ws=ws)
+    yield wl, inp, ws, res
+    del inp, res
     torch.cuda.empty_cache()
 
 
-def test_bf16_t128_stream(c4):
-    wl, inp = c4
-    say("case bf16_t128_stream")
-    res = run_layer(inp, wl.k)
-    check_dispatch_properties(res["ids"], res["offsets"], res["perm"], res["row_of"], wl.E)
+def test_bf16_t128_stream_routing_and_dispatch_every_token(c4):
+    wl, inp, _, res = c4
+    say("case bf16_t128_stream routing and dispatch on every token")
+    check_routing_every_token(inp, res, wl.k, wl.E)
     touched = int((np.diff(res["offsets"].cpu().numpy()) > 0).sum())
     say(f"  experts touched: {touched} of {wl.E}")
     assert touched >= 0.85 * wl.E
-    rows = _sample_rows(res, wl.T, 4, 3)
-    ref = oracle_for_rows(inp, rows, wl.k)
-    err = compare_rows(res, ref, rows, "bf16")
-    say(f"  rows {rows.tolist()} normwise err {err:.3e}")
-    for _ in range(9):
-        assert torch.equal(run_layer(inp, wl.k)["y"], res["y"])
 
 
+def test_bf16_t128_stream_every_token_output(c4):
+    wl, inp, _, res = c4
+    rows = np.arange(wl.T)
+    say(f"case bf16_t128_stream layer output on all {wl.T} tokens")
+    err = compare_rows(res, oracle_for_rows(inp, rows, wl.k), rows, "bf16")
+    say(f"  normwise err {err:.3e}")
+
+
+def test_bf16_t128_stream_determinism_and_permutation(c4):
+    wl, inp, ws, res = c4
+    say("case bf16_t128_stream determinism, permutation, single tokens")
+    _invariance(wl, inp, res, ws, 3, (0, 77, wl.T - 1))
+
+
+# ---------------------------------------------------------------------------
+# MXFP8, T = 32768, learned routing with a logit bias, shared expert
+# ---------------------------------------------------------------------------
 @pytest.fixture(scope="module")
 def c5():
-    wl = synth.WORKLOADS["mxfp8_t32768"]
-    say("drawing mxfp8_t32768 inputs on the GPU")
-    inp = synth.make_layer_inputs(wl, device="cuda")
-    torch.cuda.synchronize()
-    yield wl, inp
-    del inp
+    wl, inp = _fixture("mxfp8_t32768")
+    ws = pg.Workspace(wl.T, wl.d, wl.E, wl.k, wl.inter, pg.MOE_MXFP8)
+    res = run_layer(inp, wl.k, ws=ws)
+    yield wl, inp, ws, res
+    del inp, res
     torch.cuda.empty_cache()
 
 
-def test_mxfp8_t32768(c5):
-    wl, inp = c5
-    say("case mxfp8_t32768")
-    ws = pg.Workspace(wl.T, wl.d, wl.E, wl.k, wl.inter, pg.MOE_MXFP8)
-    res = run_layer(inp, wl.k, ws=ws)
-    check_dispatch_properties(res["ids"], res["offsets"], res["perm"], res["row_of"], wl.E)
+def test_mxfp8_t32768_routing_and_dispatch_every_token(c5):
+    wl, inp, _, res = c5
+    say("case mxfp8_t32768 routing and dispatch on every token")
+    check_routing_every_token(inp, res, wl.k, wl.E)
     seg = np.diff(res["offsets"].cpu().numpy())
     say(f"  segment rows: max {seg.max()} median {int(np.median(seg))} min {seg.min()} "
         f"touched {(seg > 0).sum()}")
-    rows = _sample_rows(res, wl.T, 4, 5)
-    ref = oracle_for_rows(inp, rows, wl.k)
-    err = compare_rows(res, ref, rows, "mxfp8")
-    say(f"  rows {rows.tolist()} normwise err {err:.3e}")
-    for _ in range(9):
-        assert torch.equal(run_layer(inp, wl.k, ws=ws)["y"], res["y"])
-    p = torch.randperm(wl.T, generator=torch.Generator().manual_seed(4)).cuda()
-    pin = dict(inp, x=inp["x"][p].contiguous(), x_scale=inp["x_scale"][p].contiguous())
-    rp = run_layer(pin, wl.k, ws=ws)
-    assert torch.equal(rp["ids"], res["ids"][p])
-    assert torch.equal(rp["y"], res["y"][p])
+
+
+def test_mxfp8_t32768_sampled_parity(c5):
+    wl, inp, _, res = c5
+    rows = sample_rows(res["ids"].cpu().numpy(), res["offsets"].cpu().numpy(),
+                       res["perm"].cpu().numpy(), wl.k, MX_TILE, True, 32, 5)
+    say(f"case mxfp8_t32768 layer output on {len(rows)} tokens {rows.tolist()}")
+    err = compare_rows(res, oracle_for_rows(inp, rows, wl.k), rows, "mxfp8")
+    say(f"  normwise err {err:.3e}")
+
+
+def test_mxfp8_t32768_determinism_and_permutation(c5):
+    wl, inp, ws, res = c5
+    say("case mxfp8_t32768 determinism, permutation, single tokens")
+    _invariance(wl, inp, res, ws, 4, (0, 16385, wl.T - 1))

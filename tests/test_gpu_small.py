@@ -38,6 +38,26 @@ def test_tiny_fp32_workload():
     assert err < 1e-5          # fp32 end to end: far inside the 2e-2 bar
 
 
+def test_tiny_fp32_workload_determinism_permutation_single_tokens():
+    wl = synth.WORKLOADS["tiny_fp32_t32"]
+    say("case tiny_fp32_t32 determinism, permutation, single tokens")
+    inp = _inputs(wl)
+    base = run_layer(inp, wl.k)
+    for _ in range(9):
+        r = run_layer(inp, wl.k)
+        assert torch.equal(r["y"], base["y"]) and torch.equal(r["ids"], base["ids"])
+    p = torch.randperm(wl.T, generator=torch.Generator().manual_seed(0)).cuda()
+    rp = run_layer(dict(inp, x=inp["x"][p].contiguous()), wl.k)
+    assert torch.equal(rp["ids"], base["ids"][p])
+    assert torch.equal(rp["weights"], base["weights"][p])
+    assert torch.equal(rp["y"], base["y"][p])
+    for t in range(wl.T):
+        r1 = run_layer(dict(inp, x=inp["x"][t:t + 1].contiguous()), wl.k)
+        assert torch.equal(r1["ids"][0], base["ids"][t])
+        assert torch.equal(r1["weights"][0], base["weights"][t])
+        assert torch.equal(r1["y"][0], base["y"][t])
+
+
 SMALL = [
     # T, d, I, E, k, shared, bias, dtype
     (1, 128, 64, 16, 2, False, False, "bf16"),
@@ -207,7 +227,8 @@ def test_nonfinite_input_is_flagged():
     assert ei.value.status == 5                # MOE_ERR_NONFINITE
 
 
-@pytest.mark.parametrize("dtype,d,I", [("bf16", 256, 128), ("mxfp8", 256, 128), ("mxfp8", 1024, 512)])
+@pytest.mark.parametrize("dtype,d,I", [("bf16", 256, 128), ("mxfp8", 256, 128), ("mxfp8", 1024, 512),
+                                       ("f32", 128, 64)])
 def test_determinism_permutation_and_batch_invariance_small(dtype, d, I):
     wl = synth.Workload("inv", T=333, d=d, inter=I, E=64, k=8, shared=True, bias=True,
                         dtype=dtype, seed=21)

@@ -500,6 +500,150 @@ def layer_backward(x, w_gate, bias, experts, shared, k: int, dy, ids_in=None, we
 
 
 # ---------------------------------------------------------------------------
+# MXFP8 backward (Composer 2 Technical Report, §6.1 "Kernels": the MoE backward runs in
+# MXFP8, E4M3 values with one E8M0 scale per block of 32; Figure 10: the layer is trained
+# as one grouped-GEMM flow).  The page fixes the format, not the quantisation axes or
+# the scale rule; the readings here:
+#   * every backward GEMM takes both operands in MXFP8 blocked along that GEMM's own
+#     reduction dimension, quantised from the exact value of the operand;
+#   * the scale of a block is the smallest power of two X with amax / X <= 448 (no
+#     element saturates), elements round to the nearest E4M3 value, ties to the even
+#     code; an all-zero block has X = 2^-127 and zeros;
+#   * the forward's h is quantised per row along I before the second GEMM (the MXFP8
+#     forward), so hq is what the forward multiplied and what dW2 multiplies;
+#   * data gradients (dh = d_out W2, dx = da W1 + dg W3) reduce over d or I: their
+#     activation operands are quantised per row (token-local) and their weight operands
+#     are the weights requantised along the other axis;
+#   * weight gradients reduce over the expert's rows: both operands are quantised along
+#     the rows in blocks of 32 starting at the expert's first row, the last block padded
+#     with zeros.
+# Everything else (products, sums, SwiGLU and its derivative) is exact float64.
+# ---------------------------------------------------------------------------
+def mx_quantize(v, axis: int = -1, block: int = 32) -> np.ndarray:
+    """MXFP8 values of exact ``v`` blocked along ``axis`` (its length a multiple of
+    ``block``): per block X = the smallest power of two with amax / X <= 448, clamped to
+    2^-127 .. 2^127, elements X * E4M3_RNE(v / X).  Returns float64 values."""
+    v = np.moveaxis(f64(v), axis, -1)
+    K = v.shape[-1]
+    assert K % block == 0
+    b = v.reshape(v.shape[:-1] + (K // block, block))
+    amax = np.abs(b).max(axis=-1)
+    _, ex = np.frexp(amax)                       # amax = m 2^ex, m in [0.5, 1)
+    e = ex.astype(np.int64) - 1 - 8              # floor(log2 amax) - 8
+    e = np.where(np.ldexp(amax, -e) > 448.0, e + 1, e)
+    e = np.where(amax == 0, -127, np.clip(e, -127, 127))
+    q = np.ldexp(b, -e[..., None])               # exact: a power-of-two scaling
+    idx, neg = _rne_codes(q, E4M3_TABLE[:127])   # magnitudes 0 .. 448 ascend with the code
+    vals = np.where(neg, -1.0, 1.0) * E4M3_TABLE[idx]
+    out = np.ldexp(vals, e[..., None]).reshape(v.shape)
+    return np.moveaxis(out, -1, axis)
+
+
+def _no_quant(v, axis: int = -1) -> np.ndarray:
+    return f64(v)
+
+
+def layer_backward_mxfp8(x, w_gate, bias, experts, shared, k: int, dy, ids_in=None,
+                         weights_in=None, quant=mx_quantize):
+    """Gradients of L = <dy, y> through the MXFP8 layer, under the readings above.
+
+    Same arguments and result keys as ``layer_backward`` (the inputs are the exact
+    dequantised values), plus "y" (the forward with hq), "dh_rows" (dL/dh of every
+    dispatched row, then the shared rows) and "hq_rows".  ``quant(v, axis)`` is the
+    quantiser; passing an identity turns this into the exact chain rule of the
+    unquantised layer (``layer_backward``).
+    """
+    xf = f64(x)
+    dyf = f64(dy)
+    T, d = xf.shape
+    if ids_in is None:
+        ids, w, logits = route(xf, w_gate, bias, k)
+    else:
+        ids, w, logits = route_replay(xf, w_gate, bias, ids_in, weights_in)
+    E = logits.shape[1]
+    offsets, perm, row_of = dispatch(ids, E)
+
+    def fwd(xr, w1, w3, w2):
+        a = xr @ f64(w1).T
+        g = xr @ f64(w3).T
+        hq = quant(silu(a) * g, 1)
+        return a, g, hq, hq @ f64(w2).T
+
+    def bwd(xr, a, g, hq, do, w1, w3, w2):
+        n = xr.shape[0]
+        pad = (-n) % 32
+
+        def rows(m):          # quantised along the rows, zero-padded to whole blocks
+            mp = np.concatenate([m, np.zeros((pad, m.shape[1]))]) if pad else m
+            return quant(mp, 0)[:n]
+
+        dh = quant(do, 1) @ quant(w2, 0)
+        da = dh * g * silu_grad(a)
+        dg = dh * silu(a)
+        dx = quant(da, 1) @ quant(w1, 0) + quant(dg, 1) @ quant(w3, 0)
+        xq = rows(xr)
+        return dx, rows(da).T @ xq, rows(dg).T @ xq, rows(do).T @ rows(hq), dh
+
+    I = f64(experts[0][0]).shape[0] if E else 0
+    rows_out = np.zeros((T * k, d))
+    saved = {}
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        ws = experts[e]
+        a, g, hq, o = fwd(xf[perm[lo:hi] // k], *ws)
+        rows_out[lo:hi] = o
+        saved[e] = (a, g, hq)
+    y = np.zeros((T, d))
+    for t in range(T):
+        for r in range(k):
+            y[t] += w[t, r] * rows_out[row_of[t * k + r]]
+    if shared is not None:
+        sa, sg, shq, so = fwd(xf, *shared)
+        y += so
+    d_weights = np.empty((T, k))
+    d_rows = np.empty_like(rows_out)
+    for t in range(T):
+        for r in range(k):
+            j = row_of[t * k + r]
+            d_weights[t, r] = float(dyf[t] @ rows_out[j])
+            d_rows[j] = w[t, r] * dyf[t]
+    dx = np.zeros((T, d))
+    dw1, dw3, dw2 = {}, {}, {}
+    dh_rows = np.zeros((T * k + (T if shared is not None else 0), I))
+    hq_rows = np.zeros_like(dh_rows)
+    for e, (a, g, hq) in saved.items():
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        toks = perm[lo:hi] // k
+        gx, dw1[e], dw3[e], dw2[e], dh_rows[lo:hi] = bwd(xf[toks], a, g, hq, d_rows[lo:hi], *experts[e])
+        hq_rows[lo:hi] = hq
+        np.add.at(dx, toks, gx)
+    d_shared = None
+    if shared is not None:
+        gx, s1, s3, s2, dh_rows[T * k:] = bwd(xf, sa, sg, shq, dyf, *shared)
+        hq_rows[T * k:] = shq
+        dx += gx
+        d_shared = (s1, s3, s2)
+    d_w_gate = np.zeros((d, E))
+    d_bias = None if bias is None else np.zeros(E)
+    if weights_in is None:
+        dl = softmax_pick_grad(w, d_weights)
+        wg = f64(w_gate)
+        for t in range(T):
+            for r in range(k):
+                e = int(ids[t, r])
+                dx[t] += dl[t, r] * wg[:, e]
+                d_w_gate[:, e] += dl[t, r] * xf[t]
+                if d_bias is not None:
+                    d_bias[e] += dl[t, r]
+    return {"dx": dx, "d_weights": d_weights, "d_w_gate": d_w_gate, "d_bias": d_bias,
+            "dw1": dw1, "dw3": dw3, "dw2": dw2, "d_shared": d_shared, "y": y,
+            "dh_rows": dh_rows, "hq_rows": hq_rows, "ids": ids, "weights": w,
+            "offsets": offsets, "perm": perm, "row_of": row_of}
+
+
+# ---------------------------------------------------------------------------
 # NVFP4 (the forward-pass format of Composer 2 Technical Report, §6.1 "Kernels": FP4
 # E2M1 values, one FP8 E4M3 scale per block of 16, one FP32 scale per token; the
 # quantization uses IEEE division)

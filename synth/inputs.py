@@ -260,6 +260,9 @@ def make_gate_inputs(wl: Workload, device: str = "cpu", draw_device: str | None 
     return _draw_gate(wl, device, draw_device)[0]
 
 
+EXPERT_CHUNK = 16    # experts whose weights are stored (rounded / quantised) together
+
+
 def make_layer_inputs(wl: Workload, device: str = "cpu", draw_device: str | None = None):
     """Draw one layer's inputs for workload ``wl`` (see module docstring for the recipe).
 
@@ -295,22 +298,35 @@ def make_layer_inputs(wl: Workload, device: str = "cpu", draw_device: str | None
             t["w1_scale"] = t["w3_scale"] = t["w2_scale"] = None
         return t
 
-    def fill(b, e):
-        for name, shape, fan in (("w1", (I, d), d), ("w3", (I, d), d), ("w2", (d, I), I)):
-            st = _store(randn(*shape, std=1.0 / math.sqrt(fan)), wl.dtype)
-            b[name][e].copy_(st[0])
-            if st[1] is not None:
-                b[name + "_scale"][e].copy_(st[1])
-            if len(st) > 2:
-                b[name + "_rscale"][e].copy_(st[2])
+    shapes = (("w1", (I, d), d), ("w3", (I, d), d), ("w2", (d, I), I))
 
+    def fill(b, e0, n):
+        """Experts e0 .. e0 + n - 1: drawn one matrix at a time in the recipe's order,
+        then stored (rounded or quantised) together; every storage rule acts on rows of
+        one matrix, so the result equals storing each matrix on its own."""
+        stage = {name: torch.empty((n,) + shape, dtype=torch.float32, device=draw_dev)
+                 for name, shape, _ in shapes}
+        for i in range(n):
+            for name, shape, fan in shapes:
+                stage[name][i].copy_(randn(*shape, std=1.0 / math.sqrt(fan)))
+        for name, _, _ in shapes:
+            st = _store(stage[name], wl.dtype)
+            b[name][e0:e0 + n].copy_(st[0])
+            if st[1] is not None:
+                b[name + "_scale"][e0:e0 + n].copy_(st[1])
+            if len(st) > 2:
+                b[name + "_rscale"][e0:e0 + n].copy_(st[2])
+            del st
+        del stage
+
+    draw_dev = draw_device or device
     routed = bank(E)
-    for e in range(E):
-        fill(routed, e)
+    for e0 in range(0, E, EXPERT_CHUNK):
+        fill(routed, e0, min(EXPERT_CHUNK, E - e0))
     out.update(routed)
     if wl.shared:
         sh = bank(1)
-        fill(sh, 0)
+        fill(sh, 0, 1)
         out["shared"] = {kk: (vv[0] if vv is not None else None) for kk, vv in sh.items()}
     else:
         out["shared"] = None

@@ -797,3 +797,157 @@ def test_nvfp4_expert_ffn_closed_form():
         hb = float(torch.tensor(h, dtype=torch.float64).float().bfloat16().double())
         ref = q1(hb) * W2[:, pi[j]]
         assert np.allclose(y[t], ref, rtol=1e-13, atol=0), t
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 quantiser and the MXFP8 backward
+# ---------------------------------------------------------------------------
+FINITE_E4M3 = sorted(set(abs(v) for v in oracle.E4M3_TABLE.tolist() if not math.isnan(v)))
+
+
+def _mx_brute(block):
+    """Smallest power of two X with amax / X <= 448 by search, then every element the
+    nearest grid value (ties: the even code, i.e. the grid index that is even)."""
+    amax = max(abs(v) for v in block)
+    if amax == 0:
+        return [0.0] * len(block)
+    e = -200
+    while amax / 2.0 ** e > 448.0:
+        e += 1
+    X = 2.0 ** e
+    out = []
+    for v in block:
+        q = abs(v) / X
+        best = min(range(len(FINITE_E4M3)), key=lambda i: (abs(FINITE_E4M3[i] - q), i % 2))
+        out.append(math.copysign(FINITE_E4M3[best] * X, v) if FINITE_E4M3[best] else 0.0)
+    return out
+
+
+def test_mx_quantize_brute_force_and_scale_rule():
+    rng = np.random.default_rng(60)
+    rows = [rng.standard_normal(32) * s for s in (1e-3, 0.3, 1.0, 7.0, 900.0, 2.0 ** -60)]
+    mids = [(a + b) / 2 for a, b in zip(FINITE_E4M3[1:-1], FINITE_E4M3[2:])]
+    tie = np.array(mids[:31] + [448.0])             # exact midpoints: ties to even
+    rows += [tie, -tie, tie * 2.0 ** -5]
+    sat = np.full(32, 0.5)
+    sat[0] = 449.0 / 448.0 * 2.0 ** 8               # amax / 2^(floor log2 - 8) > 448: next power
+    rows += [sat, np.zeros(32)]
+    v = np.stack(rows)
+    q = oracle.mx_quantize(v)
+    for r in range(len(rows)):
+        want = _mx_brute(list(v[r]))
+        assert np.array_equal(q[r], np.array(want)), r
+    # the block maximum keeps its magnitude up to half a step: no element saturates
+    # (449/448 * 2^8 takes X = 2: 128.3 -> 128, not X = 1, which would clamp to 448)
+    assert q[len(rows) - 2][0] == 256.0
+    assert oracle.mx_quantize(np.zeros((2, 64))).tolist() == np.zeros((2, 64)).tolist()
+
+
+def test_mx_quantize_round_trip_scaling_and_axis():
+    rng = np.random.default_rng(61)
+    v = rng.standard_normal((8, 96)) * 3
+    q = oracle.mx_quantize(v)
+    assert np.array_equal(oracle.mx_quantize(q), q)                    # representable: unchanged
+    for s in (-7, 3, 20):
+        assert np.array_equal(oracle.mx_quantize(v * 2.0 ** s), q * 2.0 ** s)
+    assert np.array_equal(oracle.mx_quantize(v.T, axis=0), q.T)
+    err = np.abs(q - v)
+    X = np.repeat(2.0 ** np.ceil(np.log2(np.abs(v).reshape(8, 3, 32).max(-1) / 448)), 32, axis=1)
+    assert np.all(err <= X * 2.0 ** -4 * np.maximum(np.abs(q) / X, 2.0 ** -6) * 2)   # half an E4M3 step
+
+
+def _mx_layer(seed, T=40, d=64, I=32, E=6, k=2, shared=True, bias=True):
+    rng = np.random.default_rng(seed)
+    x = oracle.mx_quantize(rng.standard_normal((T, d)))
+    wg = rng.standard_normal((d, E)) / 8
+    b = rng.standard_normal(E) * 0.3 if bias else None
+    mk = lambda *s: oracle.mx_quantize(rng.standard_normal(s) / np.sqrt(s[-1]))  # noqa: E731
+    experts = [(mk(I, d), mk(I, d), mk(d, I)) for _ in range(E)]
+    sh = (mk(I, d), mk(I, d), mk(d, I)) if shared else None
+    dy = rng.standard_normal((T, d))
+    return x, wg, b, experts, sh, k, dy, rng
+
+
+@pytest.mark.parametrize("mode", ["learned", "replay_gate_weights", "replay_caller_weights"])
+def test_mxfp8_backward_without_quantisation_is_the_exact_chain_rule(mode):
+    x, wg, b, experts, sh, k, dy, rng = _mx_layer(62)
+    T, E = x.shape[0], wg.shape[1]
+    kw = {}
+    if mode != "learned":
+        kw["ids_in"] = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    if mode == "replay_caller_weights":
+        kw["weights_in"] = rng.dirichlet(np.ones(k), size=T)
+    g = oracle.layer_backward_mxfp8(x, wg, b, experts, sh, k, dy, quant=lambda v, axis=-1: np.asarray(v, float), **kw)
+    ref = oracle.layer_backward(x, wg, b, experts, sh, k, dy, dense=False, **kw)
+    rel = lambda a, r: float(np.max(np.abs(a - r)) / max(np.max(np.abs(r)), 1e-300))  # noqa: E731
+    assert rel(g["y"], ref["fwd"]["y"]) < 1e-12
+    for n in ("dx", "d_weights", "d_w_gate"):
+        assert rel(g[n], ref[n]) < 1e-12, n
+    for n in ("dw1", "dw3", "dw2"):
+        assert set(g[n]) == set(ref[n])
+        for e in g[n]:
+            assert rel(g[n][e], ref[n][e]) < 1e-12, (n, e)
+    for i in range(3):
+        assert rel(g["d_shared"][i], ref["d_shared"][i]) < 1e-12
+
+
+def test_mxfp8_backward_quantisation_axes():
+    """A power-of-two scaling S commutes with MX quantisation of the scaled values, and
+    S = 2^16 pushes the other elements of a block it shares with them below the E4M3
+    range, so each check holds only with the right axis: (1) one token's dy times S scales
+    that token's dx by S and leaves every other token's dx as it was (data gradients
+    quantised per row); (2) one column of every W2 times S scales that column of dL/dh by
+    S and no other (W2 requantised along d); (3) one column of dy times S scales that row
+    of every dW2 by S and no other (weight-gradient operands quantised along the rows);
+    (4) with that input feature zero in x and caller weights, one column of W1 and W3
+    times S scales that column of dx by S and no other (W1, W3 requantised along I)."""
+    x, wg, b, experts, sh, k, dy, rng = _mx_layer(63)
+    T, E = x.shape[0], wg.shape[1]
+    S = 2.0 ** 16
+    g0 = oracle.layer_backward_mxfp8(x, wg, b, experts, sh, k, dy)
+    # the forward's h is quantised per row along I: its rows are MX values already
+    assert np.array_equal(oracle.mx_quantize(g0["hq_rows"]), g0["hq_rows"])
+    # (1)
+    dy1 = dy.copy()
+    dy1[7] *= S
+    g1 = oracle.layer_backward_mxfp8(x, wg, b, experts, sh, k, dy1)
+    others = np.arange(T) != 7
+    assert np.array_equal(g1["dx"][others], g0["dx"][others])
+    assert np.array_equal(g1["dx"][7], S * g0["dx"][7])
+    # (2)
+    n0 = 5
+    ex2 = [(a, c, w2.copy()) for a, c, w2 in experts]
+    for _, _, w2 in ex2:
+        w2[:, n0] *= S
+    sh2 = (sh[0], sh[1], sh[2].copy())
+    sh2[2][:, n0] *= S
+    g2 = oracle.layer_backward_mxfp8(x, wg, b, ex2, sh2, k, dy)
+    keep = np.arange(g0["dh_rows"].shape[1]) != n0
+    assert np.array_equal(g2["dh_rows"][:, keep], g0["dh_rows"][:, keep])
+    assert np.array_equal(g2["dh_rows"][:, n0], S * g0["dh_rows"][:, n0])
+    # (3)
+    c0 = 11
+    dy3 = dy.copy()
+    dy3[:, c0] *= S
+    g3 = oracle.layer_backward_mxfp8(x, wg, b, experts, sh, k, dy3)
+    rows = np.arange(dy.shape[1]) != c0
+    for e in g0["dw2"]:
+        assert np.array_equal(g3["dw2"][e][rows], g0["dw2"][e][rows])
+        assert np.array_equal(g3["dw2"][e][c0], S * g0["dw2"][e][c0])
+    # (4)
+    i0 = 9
+    x4 = x.copy()
+    x4[:, i0] = 0.0
+    kw = {"ids_in": g0["ids"], "weights_in": g0["weights"]}
+    g4a = oracle.layer_backward_mxfp8(x4, wg, b, experts, sh, k, dy, **kw)
+    ex4 = [(w1.copy(), w3.copy(), w2) for w1, w3, w2 in experts]
+    for w1, w3, _ in ex4:
+        w1[:, i0] *= S
+        w3[:, i0] *= S
+    sh4 = (sh[0].copy(), sh[1].copy(), sh[2])
+    sh4[0][:, i0] *= S
+    sh4[1][:, i0] *= S
+    g4b = oracle.layer_backward_mxfp8(x4, wg, b, ex4, sh4, k, dy, **kw)
+    cols = np.arange(x.shape[1]) != i0
+    assert np.array_equal(g4b["dx"][:, cols], g4a["dx"][:, cols])
+    assert np.array_equal(g4b["dx"][:, i0], S * g4a["dx"][:, i0])

@@ -133,3 +133,24 @@ def test_mx_quantize_equals_ldexp_form():
     c0, s0 = _mx_quantize_with_ldexp(t)
     assert torch.equal(c1, c0) and torch.equal(s1, s0)
     assert int(s1.min()) == 0 and int(s1.max()) == 127 + 119   # both ends of the E8M0 range met
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "mxfp8", "nvfp4", "f32"])
+def test_chunked_storage_equals_per_matrix_storage(dtype):
+    """Expert weights are stored (rounded or quantised) 16 experts at a time; the
+    result must equal storing each drawn matrix on its own, in the recipe's order."""
+    from synth.inputs import _draw_gate, _store
+    wl = synth.Workload("chunk", T=8, d=64, inter=32, E=37, k=2, shared=True, bias=True,
+                        dtype=dtype, seed=11)
+    got = synth.make_layer_inputs(wl)
+    _, randn = _draw_gate(wl, "cpu", None)
+    for e in list(range(wl.E)) + ["shared"]:
+        for name, shape, fan in (("w1", (32, 64), 64), ("w3", (32, 64), 64), ("w2", (64, 32), 32)):
+            st = _store(randn(*shape, std=1.0 / math.sqrt(fan)), dtype)
+            src = got["shared"] if e == "shared" else {kk: v[e] for kk, v in got.items()
+                                                        if kk[:2] in ("w1", "w3", "w2") and v is not None}
+            assert torch.equal(src[name], st[0]), (e, name)
+            if st[1] is not None:
+                assert torch.equal(src[name + "_scale"], st[1])
+            if len(st) > 2:
+                assert torch.equal(src[name + "_rscale"], st[2])

@@ -71,7 +71,7 @@ inline int screen_parts(int T, int d, int E) {
 
 struct RouteWs {
   size_t logits, tok_flag, xnorm, wnorm, part, xsq, wsq;   // fp64 gate GEMM path
-  size_t wt, planes, cand, cval, ccount, screen, sxsq, pcnt, pairs;   // screened path
+  size_t wt, planes, cand, cval, ccount, screen, sxsq, pblk, pcnt, pairs;   // screened path
   size_t bytes;
 };
 inline RouteWs route_ws(int T, int d, int E) {
@@ -93,7 +93,8 @@ inline RouteWs route_ws(int T, int d, int E) {
   const size_t nz = d % 64 == 0 ? (size_t)screen_parts(T, d, E) : 1;
   w.screen = o;   o = align_up(o + nz * T * E * sizeof(double), 256);
   w.sxsq = o;     o = align_up(o + nz * T * sizeof(double), 256);
-  w.pcnt = o;     o = align_up(o + (size_t)(2 * E + 1) * sizeof(int), 256);
+  w.pblk = o;     o = align_up(o + (size_t)((T + 255) / 256) * E * sizeof(int), 256);
+  w.pcnt = o;     o = align_up(o + (size_t)(3 * E + 2) * sizeof(int), 256);
   w.pairs = o;    o = align_up(o + (size_t)T * kCandMax * sizeof(int32_t), 256);
   w.bytes = o;
   return w;

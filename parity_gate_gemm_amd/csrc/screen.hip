@@ -476,75 +476,106 @@ __global__ __launch_bounds__(256) void screen_cand_kernel(
 // whose candidate list holds e and gives each (token, slot) pair to one wavefront.
 // cval[t][j] = wave_dot(x_t, w_e) + b_e.
 // ---------------------------------------------------------------------------
-// Candidate pairs grouped by expert: per-expert counts, their exclusive scan, then
-// each (token, slot) pair placed in its expert's range (the order inside a range is
-// whatever the atomics give; every pair's value is computed on its own, so the results
-// do not depend on it).
-__global__ __launch_bounds__(1024) void pair_clear_kernel(int* __restrict__ cnt, int E) {
-  for (int e = threadIdx.x; e < 2 * E + 1; e += blockDim.x) cnt[e] = 0;
-}
+// Candidate pairs grouped by expert, in (expert, token) order, with positions from
+// counts and prefix sums only.  A workgroup owns 256 tokens, one per thread; LDS holds,
+// per expert and wavefront, the 64-bit mask of the wavefront's tokens that list the
+// expert (built with atomic OR, whose result does not depend on the order of the
+// updates).  A pair's rank inside its workgroup is the number of set bits of earlier
+// tokens; a replayed row that names an expert twice (flagged as bad ids) keeps only its
+// first occurrence, whose value every later lookup finds first.
+constexpr int PAIR_TOK = 256;
 
-// Counts in LDS per workgroup of 256 tokens, one global atomic per touched expert.
-__global__ __launch_bounds__(256) void pair_count_kernel(const int32_t* __restrict__ cand,
-                                                         const int* __restrict__ ccount, int T, int E,
-                                                         int* __restrict__ cnt) {
-  __shared__ int h[kMaxExperts];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) h[e] = 0;
-  __syncthreads();
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t < T) {
-    const int m = ccount[t];
-    for (int j = 0; j < m; ++j) atomicAdd(&h[cand[(size_t)t * kCandMax + j]], 1);
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x)
-    if (h[e]) atomicAdd(&cnt[e], h[e]);
-}
-
-// cnt[0..E): counts -> start[0..E] (exclusive scan, written to cnt + E), cursors zeroed.
-__global__ __launch_bounds__(1024) void pair_scan_kernel(int* __restrict__ cnt, int E) {
-  __shared__ int c[kMaxExperts];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) c[e] = cnt[e];
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int e = 0; e < E; ++e) {
-      cnt[E + e] = run;
-      run += c[e];
-    }
-    cnt[2 * E] = run;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;   // now the placement cursors
-}
-
-// Each workgroup reserves one range per touched expert, then fills it from LDS cursors.
-__global__ __launch_bounds__(256) void pair_place_kernel(const int32_t* __restrict__ cand,
-                                                         const int* __restrict__ ccount, int T, int E,
-                                                         int* __restrict__ cnt,
-                                                         int32_t* __restrict__ pairs) {
-  __shared__ int h[kMaxExperts];
-  __shared__ int base[kMaxExperts];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) h[e] = 0;
-  __syncthreads();
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  const int m = t < T ? ccount[t] : 0;
-  for (int j = 0; j < m; ++j) atomicAdd(&h[cand[(size_t)t * kCandMax + j]], 1);
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    base[e] = h[e] ? cnt[E + e] + atomicAdd(&cnt[e], h[e]) : 0;
-    h[e] = 0;
-  }
-  __syncthreads();
+__device__ __forceinline__ uint32_t pair_mark(const int32_t* __restrict__ cand, int t, int m,
+                                              uint64_t (*bits)[4]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint64_t me = 1ull << lane;
+  uint32_t dup = 0;
   for (int j = 0; j < m; ++j) {
     const int e = cand[(size_t)t * kCandMax + j];
-    pairs[base[e] + atomicAdd(&h[e], 1)] = t * kCandMax + j;
+    if (atomicOr(&bits[e][wave], me) & me) dup |= 1u << j;
+  }
+  return dup;
+}
+
+// Per-workgroup pair counts: pblk[b][e] = number of tokens of workgroup b listing e.
+__global__ __launch_bounds__(PAIR_TOK) void pair_count_kernel(const int32_t* __restrict__ cand,
+                                                              const int* __restrict__ ccount, int T,
+                                                              int E, int* __restrict__ pblk) {
+  __shared__ uint64_t bits[kMaxExperts][4];
+  for (int i = threadIdx.x; i < 4 * E; i += PAIR_TOK) bits[i >> 2][i & 3] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * PAIR_TOK + threadIdx.x;
+  pair_mark(cand, t, t < T ? ccount[t] : 0, bits);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += PAIR_TOK)
+    pblk[(size_t)blockIdx.x * E + e] = __popcll(bits[e][0]) + __popcll(bits[e][1]) +
+                                       __popcll(bits[e][2]) + __popcll(bits[e][3]);
+}
+
+// pblk[b][e] -> exclusive prefix over workgroups (the workgroup's base inside expert e's
+// range); cnt[E .. 2E] = exclusive prefix of the experts' totals (range starts, cnt[2E] =
+// all pairs); cnt[2E+1 .. 3E+1] = exclusive prefix of the experts' chunk counts
+// (ceil(total / rf_p); cnt[3E+1] = all chunks).  cnt[0 .. E) keeps the totals.
+__global__ __launch_bounds__(1024) void pair_scan_kernel(int* __restrict__ pblk, int nblk,
+                                                         int* __restrict__ cnt, int E, int rf_p) {
+  __shared__ int tot[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int b0 = 0; b0 < nblk; b0 += 8) {   // eight loads in flight per thread
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = b0 + u < nblk ? pblk[(size_t)(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (b0 + u < nblk) pblk[(size_t)(b0 + u) * E + e] = run;
+        run += v[u];
+      }
+    }
+    tot[e] = run;
+    cnt[e] = run;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0, ch = 0;
+    for (int e = 0; e < E; ++e) {
+      cnt[E + e] = run;
+      cnt[2 * E + 1 + e] = ch;
+      run += tot[e];
+      ch += (tot[e] + rf_p - 1) / rf_p;
+    }
+    cnt[2 * E] = run;
+    cnt[3 * E + 1] = ch;
   }
 }
 
-// Chunks of RF_P consecutive pairs (expert order; 8 to 64 by batch size) per
-// workgroup, one wavefront per pair; the gate column of the chunk's first expert is staged in LDS (when it fits) and
-// read from there by every pair of that expert.
+// Each pair at: its expert's range start + the workgroup's base + its rank.
+__global__ __launch_bounds__(PAIR_TOK) void pair_place_kernel(const int32_t* __restrict__ cand,
+                                                              const int* __restrict__ ccount, int T,
+                                                              int E, const int* __restrict__ pblk,
+                                                              const int* __restrict__ cnt,
+                                                              int32_t* __restrict__ pairs) {
+  __shared__ uint64_t bits[kMaxExperts][4];
+  for (int i = threadIdx.x; i < 4 * E; i += PAIR_TOK) bits[i >> 2][i & 3] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * PAIR_TOK + threadIdx.x;
+  const int m = t < T ? ccount[t] : 0;
+  const uint32_t dup = pair_mark(cand, t, m, bits);
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int j = 0; j < m; ++j) {
+    if ((dup >> j) & 1u) continue;
+    const int e = cand[(size_t)t * kCandMax + j];
+    int rank = __popcll(bits[e][wave] & below);
+    for (int w = 0; w < wave; ++w) rank += __popcll(bits[e][w]);
+    pairs[cnt[E + e] + pblk[(size_t)blockIdx.x * E + e] + rank] = t * kCandMax + j;
+  }
+}
+
+// Chunks of at most RF_P pairs of one expert (8 to 64 by batch size) per workgroup,
+// one wavefront per pair.  The chunk's gate column is staged in LDS when d fits and
+// every pair reads it from there (wave_dot_lds), else every pair reads it from memory
+// (wave_dot): which of the two computes a pair depends on d alone, never on the batch.
 constexpr int RF_W = 8, RF_LDS_MAX = 16384;
 
 // wave_dot with w in LDS: the same fma sequence (lane-strided blocks of 8, ascending,
@@ -582,29 +613,36 @@ __device__ double wave_dot_lds(const void* __restrict__ x, const uint8_t* __rest
 
 __global__ __launch_bounds__(64 * RF_W) void screen_refine_kernel(
     const void* __restrict__ x, const uint8_t* __restrict__ xs, int dtype, int T, int d,
-    const float* __restrict__ wt, const float* __restrict__ bias, const int32_t* __restrict__ cand,
-    const int32_t* __restrict__ pairs, const int* __restrict__ cnt, int E, int RF_P,
-    double* __restrict__ cval) {
+    const float* __restrict__ wt, const float* __restrict__ bias, const int32_t* __restrict__ pairs,
+    const int* __restrict__ cnt, int E, int RF_P, double* __restrict__ cval) {
   extern __shared__ __attribute__((aligned(16))) float wl[];   // d floats when d <= RF_LDS_MAX
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int np = cnt[2 * E];
+  const int* start = cnt + E;            // [E + 1] pair range starts
+  const int* cst = cnt + 2 * E + 1;      // [E + 1] chunk starts
+  const int nch = cst[E];
   const bool stage = d <= RF_LDS_MAX;
-  for (int c0 = blockIdx.x * RF_P; c0 < np; c0 += gridDim.x * RF_P) {
-    const int es = cand[pairs[c0]];
+  for (int c = blockIdx.x; c < nch; c += gridDim.x) {
+    int lo = 0, hi = E;                  // the expert e with cst[e] <= c < cst[e + 1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (cst[mid] <= c) lo = mid; else hi = mid;
+    }
+    const int e = lo;
+    const int p0 = start[e] + (c - cst[e]) * RF_P;
+    const int p1 = min(p0 + RF_P, start[e + 1]);
     if (stage) {
       __syncthreads();   // the previous chunk's readers are done
-      const float* src = wt + (size_t)es * d;
+      const float* src = wt + (size_t)e * d;
       for (int i = 4 * threadIdx.x; i < d; i += 4 * 64 * RF_W) *(float4*)(wl + i) = *(const float4*)(src + i);
       __syncthreads();
     }
-    const int cend = min(c0 + RF_P, np);
-    for (int p = c0 + wave; p < cend; p += RF_W) {
+    const double b = bias ? (double)bias[e] : 0.0;
+    for (int p = p0 + wave; p < p1; p += RF_W) {
       const int tj = pairs[p];
       const int t = tj / kCandMax;
-      const int e = cand[tj];
-      const double v = (stage && e == es) ? wave_dot_lds(x, xs, dtype, t, d, wl)
-                                          : wave_dot(x, xs, dtype, t, d, wt + (size_t)e * d);
-      if (lane == 0) cval[tj] = bias ? v + (double)bias[e] : v;
+      const double v = stage ? wave_dot_lds(x, xs, dtype, t, d, wl)
+                             : wave_dot(x, xs, dtype, t, d, wt + (size_t)e * d);
+      if (lane == 0) cval[tj] = bias ? v + b : v;
     }
   }
 }
@@ -908,8 +946,9 @@ struct ScreenWs {
   int32_t* cand;
   double* cval;
   int* ccount;
-  int* pcnt;        // per-expert pair counts / cursors [E], starts [E + 1]
-  int32_t* pairs;   // candidate pairs t * kCandMax + j in expert order
+  int* pblk;        // per-workgroup pair counts, then bases [ceil(T / 256)][E]
+  int* pcnt;        // totals [E], range starts [E + 1], chunk starts [E + 1]
+  int32_t* pairs;   // candidate pairs t * kCandMax + j in (expert, token) order
 };
 
 static ScreenWs screen_ws_of(char* w, int T, int d, int E) {
@@ -925,6 +964,7 @@ static ScreenWs screen_ws_of(char* w, int T, int d, int E) {
   s.cand = (int32_t*)(w + L.cand);
   s.cval = (double*)(w + L.cval);
   s.ccount = (int*)(w + L.ccount);
+  s.pblk = (int*)(w + L.pblk);
   s.pcnt = (int*)(w + L.pcnt);
   s.pairs = (int32_t*)(w + L.pairs);
   return s;
@@ -934,17 +974,18 @@ static ScreenWs screen_ws_of(char* w, int T, int d, int E) {
 static moe_status refine_pairs(const void* x, const uint8_t* xs, int dtype, int T, int d, int E, int k,
                                const float* bias, const ScreenWs& S, hipStream_t s) {
   (void)k;
-  pair_clear_kernel<<<1, 1024, 0, s>>>(S.pcnt, E);
-  pair_count_kernel<<<(T + 255) / 256, 256, 0, s>>>(S.cand, S.ccount, T, E, S.pcnt);
-  pair_scan_kernel<<<1, 1024, 0, s>>>(S.pcnt, E);
-  pair_place_kernel<<<(T + 255) / 256, 256, 0, s>>>(S.cand, S.ccount, T, E, S.pcnt, S.pairs);
+  if (T == 0) return MOE_OK;
   // about 8 pairs per token: aim at >= 1024 chunks
   int rf_p = 8;
   while (rf_p < 64 && (long long)rf_p * 2 * 1024 <= (long long)T * 8) rf_p *= 2;
-  const long long nblk = ((long long)T * kCandMax + rf_p - 1) / rf_p;
+  const int nblk = (T + PAIR_TOK - 1) / PAIR_TOK;
+  pair_count_kernel<<<nblk, PAIR_TOK, 0, s>>>(S.cand, S.ccount, T, E, S.pblk);
+  pair_scan_kernel<<<1, 1024, 0, s>>>(S.pblk, nblk, S.pcnt, E, rf_p);
+  pair_place_kernel<<<nblk, PAIR_TOK, 0, s>>>(S.cand, S.ccount, T, E, S.pblk, S.pcnt, S.pairs);
+  const long long nch_bound = ((long long)T * kCandMax + rf_p - 1) / rf_p + E;
   const size_t lds = d <= RF_LDS_MAX ? (size_t)d * sizeof(float) : 0;
-  screen_refine_kernel<<<(unsigned)(nblk < 2048 ? nblk : 2048), 64 * RF_W, lds, s>>>(
-      x, xs, dtype, T, d, S.wt, bias, S.cand, S.pairs, S.pcnt, E, rf_p, S.cval);
+  screen_refine_kernel<<<(unsigned)(nch_bound < 2048 ? nch_bound : 2048), 64 * RF_W, lds, s>>>(
+      x, xs, dtype, T, d, S.wt, bias, S.pairs, S.pcnt, E, rf_p, S.cval);
   return launch_status();
 }
 

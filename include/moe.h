@@ -207,6 +207,25 @@ moe_status moe_dispatch(const int32_t* ids, int T, int E, int k,
                         int32_t* offsets, int32_t* perm, int32_t* row_of,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* moe_dispatch for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels and
+ * the same results, with the scratch (per-block histograms, expert totals and the error
+ * flag) in a library-owned static device array of 4 MiB instead of a caller workspace.
+ * The array exists once per GPU and is held until the process ends; the call itself
+ * allocates nothing.  Arguments as moe_dispatch, plus
+ *   status_out  device int32 or NULL: receives MOE_OK, or MOE_ERR_BAD_IDS when an id
+ *               was outside [0, E) (treated as expert 0, as moe_dispatch does), once the
+ *               call's kernels have run (no host synchronisation).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (two
+ * streams, two threads) race, and must be ordered by the caller.  The caller's device
+ * must be current (hipSetDevice) and own `stream`.
+ * MOE_ERR_UNSUPPORTED when the scratch would exceed 4 MiB: it takes 256 bytes plus
+ * (ceil(T / 64) + 1) * E * 4 bytes, each part rounded up to 256 bytes (up to 174,656
+ * tokens at E = 384, 65,408 at E = 1024); MOE_ERR_HIP when the array's device address
+ * cannot be obtained.  Other argument checks as moe_dispatch. */
+moe_status moe_dispatch_noalloc(const int32_t* ids, int T, int E, int k, int32_t* offsets,
+                                int32_t* perm, int32_t* row_of, int32_t* status_out, void* stream);
+
 /* Grouped SwiGLU expert FFN over the dispatched segments (one grouped GEMM for
  * W1 and W3 with the SwiGLU epilogue, one for W2).
  * Defined by: the MoE layer runs its experts as grouped GEMMs, with MXFP8 (E4M3

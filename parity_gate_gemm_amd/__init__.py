@@ -17,7 +17,7 @@ __all__ = [
     "moe_nvfp4_pack_weights", "nvfp4_pack_inputs", "lib", "Workspace",
     "moe_workspace_size", "moe_workspace_init", "moe_route", "moe_route_replay",
     "moe_route_replay_filtered",
-    "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_gate_up", "moe_expert_ffn_down", "moe_combine", "moe_check", "moe_status_string",
+    "moe_dispatch", "moe_dispatch_noalloc", "moe_expert_ffn", "moe_expert_ffn_gate_up", "moe_expert_ffn_down", "moe_combine", "moe_check", "moe_status_string",
     "layer_forward", "moe_backward_workspace_size", "moe_combine_backward", "moe_expert_ffn_backward",
     "moe_route_backward", "layer_backward", "moe_expert_ffn_backward_data",
     "moe_expert_ffn_backward_weights", "moe_expert_ffn_gate_up_save",
@@ -78,6 +78,7 @@ def lib():
             "moe_route_replay_filtered": [P, P, I, I, I, P, P, I, I, P, ctypes.c_double, P, P, P, SZ,
                                           P],
             "moe_dispatch": [P, I, I, I, P, P, P, P, SZ, P],
+            "moe_dispatch_noalloc": [P, I, I, I, P, P, P, P, P],
             "moe_expert_ffn": [P, P, I, I, I, I, I, I, ctypes.POINTER(_Bank), ctypes.POINTER(_Bank),
                                P, P, P, P, SZ, P],
             "moe_expert_ffn_gate_up": [P, P, I, I, I, I, I, I, ctypes.POINTER(_Bank),
@@ -203,6 +204,20 @@ def moe_dispatch(ids, E, ws: Workspace, offsets=None, perm=None, row_of=None):
     row_of = torch.empty(T * k, dtype=torch.int32, device=dev) if row_of is None else row_of
     _ok(lib().moe_dispatch(_ptr(ids), T, E, k, _ptr(offsets), _ptr(perm), _ptr(row_of), ws.ptr,
                            ws.nbytes, _stream(dev)), "moe_dispatch")
+    return offsets, perm, row_of
+
+
+def moe_dispatch_noalloc(ids, E, offsets=None, perm=None, row_of=None, status=None):
+    """moe_dispatch on the library's static scratch (no workspace); ``status`` is an
+    optional int32 device tensor of one element that receives the device status."""
+    _check_dev(ids)
+    T, k = ids.shape
+    dev = ids.device
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev) if perm is None else perm
+    row_of = torch.empty(T * k, dtype=torch.int32, device=dev) if row_of is None else row_of
+    _ok(lib().moe_dispatch_noalloc(_ptr(ids), T, E, k, _ptr(offsets), _ptr(perm), _ptr(row_of),
+                                   _ptr(status), _stream(dev)), "moe_dispatch_noalloc")
     return offsets, perm, row_of
 
 

@@ -4,6 +4,8 @@
 // dispatch/combine paragraph).  Sort key (expert ascending, token ascending, slot
 // ascending).  Positions come from per-block histograms and prefix sums; integer LDS
 // atomics only count, so the result is the same bits whatever the schedule.
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -109,6 +111,61 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __
   }
 }
 
+// Writes the device error flag of one no-allocation dispatch to the caller's status.
+__global__ void dispatch_status_kernel(const int* flag, int32_t* status) {
+  if (threadIdx.x == 0) *status = (*flag & (kFlagBadId | kFlagDupId)) ? MOE_ERR_BAD_IDS : MOE_OK;
+}
+
+__global__ void clear_flag_kernel(int* flag) {
+  if (threadIdx.x == 0) *flag = 0;
+}
+
+// The four dispatch kernels on a scratch area laid out as dispatch_ws (header flag,
+// per-block histograms, expert totals).
+static void dispatch_launch(const int32_t* ids, int T, int E, int k, int32_t* offsets, int32_t* perm,
+                            int32_t* row_of, char* w, hipStream_t s) {
+  const DispatchWs L = dispatch_ws(T, E);
+  int* hist = (int*)(w + L.hist);
+  int* total = (int*)(w + L.total);
+  if (T > 0) {
+    dispatch_hist_kernel<<<L.nblocks, 256, 0, s>>>(ids, T, E, k, hist, (int*)w);
+    dispatch_colscan_kernel<<<E, 256, 0, s>>>(hist, L.nblocks, E, total);
+    dispatch_offsets_kernel<<<1, 1024, 0, s>>>(total, E, offsets);
+    dispatch_scatter_kernel<<<L.nblocks, 256, 0, s>>>(ids, T, E, k, hist, offsets, perm, row_of);
+  } else {
+    // Empty batch: every segment is empty.
+    zero_offsets_kernel<<<1, 1024, 0, s>>>(E, offsets);
+  }
+}
+
+// Scratch of moe_dispatch_noalloc: one copy per GPU, held until the process ends.
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+// Device address of `scratch` on the current device (hipGetSymbolAddress once per
+// device; host code never passes the symbol itself).
+static char* scratch_ptr(int* err) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = 1;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      *err = 1;
+      return nullptr;
+    }
+    ptrs[dev] = p;
+  }
+  *err = 0;
+  return (char*)ptrs[dev];
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -122,18 +179,24 @@ extern "C" moe_status moe_dispatch(const int32_t* ids, int T, int E, int k, int3
   const DispatchWs L = dispatch_ws(T, E);
   if (ws_bytes < L.bytes) return MOE_ERR_WORKSPACE;
   if (T > 0 && (!ids || !perm || !row_of)) return MOE_ERR_INVALID_ARG;
+  dispatch_launch(ids, T, E, k, offsets, perm, row_of, (char*)ws, (hipStream_t)stream);
+  return launch_status();
+}
+
+extern "C" moe_status moe_dispatch_noalloc(const int32_t* ids, int T, int E, int k, int32_t* offsets,
+                                           int32_t* perm, int32_t* row_of, int32_t* status_out,
+                                           void* stream) {
+  if (T < 0 || E < 1 || E > kMaxExperts || k < 1 || k > kMaxTopK) return MOE_ERR_INVALID_ARG;
+  if (!offsets) return MOE_ERR_INVALID_ARG;
+  if ((long long)T * k > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+  if (dispatch_ws(T, E).bytes > kNoAllocScratchBytes) return MOE_ERR_UNSUPPORTED;
+  if (T > 0 && (!ids || !perm || !row_of)) return MOE_ERR_INVALID_ARG;
+  int err = 0;
+  char* w = scratch_ptr(&err);
+  if (err) return MOE_ERR_HIP;
   hipStream_t s = (hipStream_t)stream;
-  char* w = (char*)ws;
-  int* hist = (int*)(w + L.hist);
-  int* total = (int*)(w + L.total);
-  if (T > 0) {
-    dispatch_hist_kernel<<<L.nblocks, 256, 0, s>>>(ids, T, E, k, hist, (int*)w);
-    dispatch_colscan_kernel<<<E, 256, 0, s>>>(hist, L.nblocks, E, total);
-    dispatch_offsets_kernel<<<1, 1024, 0, s>>>(total, E, offsets);
-    dispatch_scatter_kernel<<<L.nblocks, 256, 0, s>>>(ids, T, E, k, hist, offsets, perm, row_of);
-  } else {
-    // Empty batch: every segment is empty.
-    zero_offsets_kernel<<<1, 1024, 0, s>>>(E, offsets);
-  }
+  clear_flag_kernel<<<1, 64, 0, s>>>((int*)w);   // the last call's flag stays in the array
+  dispatch_launch(ids, T, E, k, offsets, perm, row_of, w, s);
+  if (status_out) dispatch_status_kernel<<<1, 64, 0, s>>>((const int*)w, status_out);
   return launch_status();
 }

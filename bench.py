@@ -309,6 +309,9 @@ def main():
     }
 
     result["roofline"]["traffic"] = measured_traffic(wl.name) if dom == "ffn_gate_up" else None
+    counters = measured_mfma(wl.name)
+    if counters is not None:
+        result["mfma"]["counters"] = counters
     if bwd:
         result["config"]["pass"] = "forward+backward"
     if wl.dtype != "bf16":
@@ -336,6 +339,22 @@ def measured_traffic(workload):
     if hashlib.sha256(src).hexdigest() != rec["ffn_source_sha256"]:
         return None
     return rec["fetch_bytes"] + rec["write_bytes"]
+
+
+def measured_mfma(workload):
+    """Matrix-core counters of the grouped GEMMs from the committed rocprofv3 summary
+    (SQ_VALU_MFMA_BUSY_CYCLES over the SIMD cycles, the implied clock, the counted
+    matrix operations), or None when there is none or the kernel source changed."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"mfma_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, "parity_gate_gemm_amd", "csrc", rec["kernel_source"]), "rb").read()
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        return None
+    return {k: {"mfma_busy": round(v["mfma_busy"], 4), "clock_ghz": round(v["clock_ghz"], 3),
+                "mfma_ops": v["ops"]} for k, v in rec["kernels"].items() if "grouped_gemm" in k}
 
 
 class _ExpertCache:

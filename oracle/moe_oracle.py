@@ -543,6 +543,36 @@ def _no_quant(v, axis: int = -1) -> np.ndarray:
     return f64(v)
 
 
+def expert_forward_mxfp8(x_rows, w1, w3, w2, quant=mx_quantize):
+    """One expert of the MXFP8 layer: a = x W1, g = x W3, hq = MX_I(silu(a) g) (per row),
+    out = hq W2.  Returns (a, g, hq, out)."""
+    xr = f64(x_rows)
+    a = xr @ f64(w1).T
+    g = xr @ f64(w3).T
+    hq = quant(silu(a) * g, 1)
+    return a, g, hq, hq @ f64(w2).T
+
+
+def expert_backward_mxfp8(x_rows, a, g, hq, d_out_rows, w1, w3, w2, quant=mx_quantize):
+    """The MXFP8 backward of one expert over its rows (readings above): returns (dx rows,
+    dW1, dW3, dW2, dL/dh rows)."""
+    xr = f64(x_rows)
+    do = f64(d_out_rows)
+    n = xr.shape[0]
+    pad = (-n) % 32
+
+    def rows(m):          # quantised along the rows, zero-padded to whole blocks
+        mp = np.concatenate([m, np.zeros((pad, m.shape[1]))]) if pad else m
+        return quant(mp, 0)[:n]
+
+    dh = quant(do, 1) @ quant(w2, 0)
+    da = dh * g * silu_grad(a)
+    dg = dh * silu(a)
+    dx = quant(da, 1) @ quant(w1, 0) + quant(dg, 1) @ quant(w3, 0)
+    xq = rows(xr)
+    return dx, rows(da).T @ xq, rows(dg).T @ xq, rows(do).T @ rows(hq), dh
+
+
 def layer_backward_mxfp8(x, w_gate, bias, experts, shared, k: int, dy, ids_in=None,
                          weights_in=None, quant=mx_quantize):
     """Gradients of L = <dy, y> through the MXFP8 layer, under the readings above.
@@ -562,28 +592,6 @@ def layer_backward_mxfp8(x, w_gate, bias, experts, shared, k: int, dy, ids_in=No
         ids, w, logits = route_replay(xf, w_gate, bias, ids_in, weights_in)
     E = logits.shape[1]
     offsets, perm, row_of = dispatch(ids, E)
-
-    def fwd(xr, w1, w3, w2):
-        a = xr @ f64(w1).T
-        g = xr @ f64(w3).T
-        hq = quant(silu(a) * g, 1)
-        return a, g, hq, hq @ f64(w2).T
-
-    def bwd(xr, a, g, hq, do, w1, w3, w2):
-        n = xr.shape[0]
-        pad = (-n) % 32
-
-        def rows(m):          # quantised along the rows, zero-padded to whole blocks
-            mp = np.concatenate([m, np.zeros((pad, m.shape[1]))]) if pad else m
-            return quant(mp, 0)[:n]
-
-        dh = quant(do, 1) @ quant(w2, 0)
-        da = dh * g * silu_grad(a)
-        dg = dh * silu(a)
-        dx = quant(da, 1) @ quant(w1, 0) + quant(dg, 1) @ quant(w3, 0)
-        xq = rows(xr)
-        return dx, rows(da).T @ xq, rows(dg).T @ xq, rows(do).T @ rows(hq), dh
-
     I = f64(experts[0][0]).shape[0] if E else 0
     rows_out = np.zeros((T * k, d))
     saved = {}
@@ -591,8 +599,7 @@ def layer_backward_mxfp8(x, w_gate, bias, experts, shared, k: int, dy, ids_in=No
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi == lo:
             continue
-        ws = experts[e]
-        a, g, hq, o = fwd(xf[perm[lo:hi] // k], *ws)
+        a, g, hq, o = expert_forward_mxfp8(xf[perm[lo:hi] // k], *experts[e], quant=quant)
         rows_out[lo:hi] = o
         saved[e] = (a, g, hq)
     y = np.zeros((T, d))
@@ -600,7 +607,7 @@ def layer_backward_mxfp8(x, w_gate, bias, experts, shared, k: int, dy, ids_in=No
         for r in range(k):
             y[t] += w[t, r] * rows_out[row_of[t * k + r]]
     if shared is not None:
-        sa, sg, shq, so = fwd(xf, *shared)
+        sa, sg, shq, so = expert_forward_mxfp8(xf, *shared, quant=quant)
         y += so
     d_weights = np.empty((T, k))
     d_rows = np.empty_like(rows_out)
@@ -616,12 +623,13 @@ def layer_backward_mxfp8(x, w_gate, bias, experts, shared, k: int, dy, ids_in=No
     for e, (a, g, hq) in saved.items():
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         toks = perm[lo:hi] // k
-        gx, dw1[e], dw3[e], dw2[e], dh_rows[lo:hi] = bwd(xf[toks], a, g, hq, d_rows[lo:hi], *experts[e])
+        gx, dw1[e], dw3[e], dw2[e], dh_rows[lo:hi] = expert_backward_mxfp8(
+            xf[toks], a, g, hq, d_rows[lo:hi], *experts[e], quant=quant)
         hq_rows[lo:hi] = hq
         np.add.at(dx, toks, gx)
     d_shared = None
     if shared is not None:
-        gx, s1, s3, s2, dh_rows[T * k:] = bwd(xf, sa, sg, shq, dyf, *shared)
+        gx, s1, s3, s2, dh_rows[T * k:] = expert_backward_mxfp8(xf, sa, sg, shq, dyf, *shared, quant=quant)
         hq_rows[T * k:] = shq
         dx += gx
         d_shared = (s1, s3, s2)

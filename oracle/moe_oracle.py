@@ -574,15 +574,19 @@ def expert_backward_mxfp8(x_rows, a, g, hq, d_out_rows, w1, w3, w2, quant=mx_qua
 
 
 def layer_backward_mxfp8(x, w_gate, bias, experts, shared, k: int, dy, ids_in=None,
-                         weights_in=None, quant=mx_quantize):
+                         weights_in=None, quant=mx_quantize, grad_round=None):
     """Gradients of L = <dy, y> through the MXFP8 layer, under the readings above.
 
     Same arguments and result keys as ``layer_backward`` (the inputs are the exact
     dequantised values), plus "y" (the forward with hq), "dh_rows" (dL/dh of every
-    dispatched row, then the shared rows) and "hq_rows".  ``quant(v, axis)`` is the
-    quantiser; passing an identity turns this into the exact chain rule of the
-    unquantised layer (``layer_backward``).
+    dispatched row, then the shared rows) and "hq_rows".  The gradient of each
+    dispatched row's expert output, w_tr dy_t, is rounded to the layer's gradient type,
+    bf16 (``grad_round``, default ``bf16_rne``), before it enters the expert backward.
+    ``quant(v, axis)`` is the quantiser; an identity quantiser and rounding turn this
+    into the exact chain rule of the unquantised layer (``layer_backward``).
     """
+    if grad_round is None:
+        grad_round = bf16_rne
     xf = f64(x)
     dyf = f64(dy)
     T, d = xf.shape
@@ -615,7 +619,7 @@ def layer_backward_mxfp8(x, w_gate, bias, experts, shared, k: int, dy, ids_in=No
         for r in range(k):
             j = row_of[t * k + r]
             d_weights[t, r] = float(dyf[t] @ rows_out[j])
-            d_rows[j] = w[t, r] * dyf[t]
+            d_rows[j] = grad_round(w[t, r] * dyf[t])
     dx = np.zeros((T, d))
     dw1, dw3, dw2 = {}, {}, {}
     dh_rows = np.zeros((T * k + (T if shared is not None else 0), I))

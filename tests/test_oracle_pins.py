@@ -877,7 +877,8 @@ def test_mxfp8_backward_without_quantisation_is_the_exact_chain_rule(mode):
         kw["ids_in"] = np.stack([rng.permutation(E)[:k] for _ in range(T)])
     if mode == "replay_caller_weights":
         kw["weights_in"] = rng.dirichlet(np.ones(k), size=T)
-    g = oracle.layer_backward_mxfp8(x, wg, b, experts, sh, k, dy, quant=lambda v, axis=-1: np.asarray(v, float), **kw)
+    ident = lambda v, axis=-1: np.asarray(v, float)  # noqa: E731
+    g = oracle.layer_backward_mxfp8(x, wg, b, experts, sh, k, dy, quant=ident, grad_round=ident, **kw)
     ref = oracle.layer_backward(x, wg, b, experts, sh, k, dy, dense=False, **kw)
     rel = lambda a, r: float(np.max(np.abs(a - r)) / max(np.max(np.abs(r)), 1e-300))  # noqa: E731
     assert rel(g["y"], ref["fwd"]["y"]) < 1e-12
@@ -951,3 +952,26 @@ def test_mxfp8_backward_quantisation_axes():
     cols = np.arange(x.shape[1]) != i0
     assert np.array_equal(g4b["dx"][:, cols], g4a["dx"][:, cols])
     assert np.array_equal(g4b["dx"][:, i0], S * g4a["dx"][:, i0])
+
+
+def test_mxfp8_backward_rounds_the_expert_output_gradient_to_bf16():
+    """With W2 = the identity (d = I) and no MX quantisation, dL/dh of a dispatched row is
+    its expert-output gradient itself: it must be w_tr dy_t rounded to bf16 (and differ
+    from the unrounded product somewhere), the shared rows dy exactly."""
+    rng = np.random.default_rng(64)
+    T, d, E, k = 12, 32, 4, 2
+    x = rng.standard_normal((T, d))
+    wg = rng.standard_normal((d, E)) / 4
+    eye = np.eye(d)
+    experts = [(rng.standard_normal((d, d)) / 6, rng.standard_normal((d, d)) / 6, eye) for _ in range(E)]
+    sh = (rng.standard_normal((d, d)) / 6, rng.standard_normal((d, d)) / 6, eye)
+    dy = oracle.bf16_rne(rng.standard_normal((T, d)))
+    ident = lambda v, axis=-1: np.asarray(v, float)  # noqa: E731
+    g = oracle.layer_backward_mxfp8(x, wg, None, experts, sh, k, dy, quant=ident)
+    dh = g["dh_rows"]
+    assert np.array_equal(oracle.bf16_rne(dh), dh)
+    raw = np.stack([g["weights"][t, r] * dy[t] for t in range(T) for r in range(k)])
+    rows = np.array([g["row_of"][t * k + r] for t in range(T) for r in range(k)])
+    assert np.array_equal(dh[rows], oracle.bf16_rne(raw))
+    assert np.any(dh[rows] != raw)
+    assert np.array_equal(dh[T * k:], dy)

@@ -38,8 +38,8 @@ def parse():
                     help="replay workloads: route with the plausibility filter at ln tau = LOG_TAU "
                          "(the replayed ids are filtered and the weights come from the gate)")
     ap.add_argument("--backward", action="store_true",
-                    help="bf16 workloads: a step is the forward and the backward pass of the layer "
-                         "(dL/dy drawn once, fp32 weight and gate gradients)")
+                    help="bf16 and MXFP8 workloads: a step is the forward and the backward pass of the "
+                         "layer (dL/dy drawn once, fp32 weight and gate gradients)")
     ap.add_argument("--cpu-sample", type=int, default=32,
                     help="tokens of the same batch the CPU oracle is timed on (0: skip)")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
@@ -96,9 +96,10 @@ def main():
         sys.exit(2)
     has_shared = inp["shared"] is not None
     bwd = args.backward
-    if bwd and wl.dtype != "bf16":
-        print("--backward runs the bf16 workloads only", file=sys.stderr)
+    if bwd and wl.dtype not in ("bf16", "mxfp8"):
+        print("--backward runs the bf16 and MXFP8 workloads only", file=sys.stderr)
         sys.exit(2)
+    mxb = bwd and wl.dtype == "mxfp8"
     ws = pg.BackwardWorkspace(T, d, E, k, I, dt) if bwd else pg.Workspace(T, d, E, k, I, dt)
     x, wg, bias = inp["x"], inp["w_gate"], inp["bias"]
     # NVFP4 banks run K-blocked (packed once here, outside the timed region); the oracle
@@ -128,6 +129,10 @@ def main():
         dx = torch.empty(T, d, dtype=torch.float32, device=dev)
         pre = torch.empty(rows, 2 * I, dtype=torch.float32, device=dev)
         gate_grad = not (replay and filt is None and inp["weights_in"] is not None)
+        if mxb:   # the weights requantised for the backward: once per weight version, untimed
+            tb_r = pg.moe_mxfp8_transpose_weights({n: routed[n] for n in ("w1", "w3", "w2", "w1_scale",
+                                                                            "w3_scale", "w2_scale")})
+            tb_s = pg.moe_mxfp8_transpose_weights(shared) if has_shared else None
 
     def step(ev=None):
         if ev is not None:
@@ -146,7 +151,8 @@ def main():
         if ev is not None:
             ev[2].record()
         if bwd:   # training step: keep the pre-activations for the backward
-            pg.moe_expert_ffn_gate_up_save(x, routed, shared, offsets, perm, k, ws, pre=pre)
+            pg.moe_expert_ffn_gate_up_save(x, routed, shared, offsets, perm, k, ws, pre=pre,
+                                           x_scale=inp["x_scale"])
         else:
             pg.moe_expert_ffn_gate_up(x, routed, shared, offsets, perm, k, ws, x_scale=inp["x_scale"])
         if ev is not None:
@@ -162,17 +168,22 @@ def main():
         pg.moe_combine_backward(dy, out, row_of, weights, T, has_shared, dt, d_out=d_out, d_weights=d_weights)
         if ev is not None:
             ev[6].record()
-        pg.moe_expert_ffn_backward_data(x, routed, shared, offsets, perm, k, d_out, ws, dx_rows=dx_rows, pre=pre)
+        if mxb:
+            pg.moe_expert_ffn_backward_mxfp8(x, inp["x_scale"], routed, shared, tb_r, tb_s, offsets, perm, k, d_out,
+                                             ws, pre=pre, dx_rows=dx_rows, grads=grads, shared_grads=sgrads)
+        else:
+            pg.moe_expert_ffn_backward_data(x, routed, shared, offsets, perm, k, d_out, ws, dx_rows=dx_rows,
+                                            pre=pre)
+            if ev is not None:
+                ev[7].record()
+            pg.moe_expert_ffn_backward_weights(x, routed, shared, perm, k, d_out, ws, grads=grads,
+                                               shared_grads=sgrads)
         if ev is not None:
-            ev[7].record()
-        pg.moe_expert_ffn_backward_weights(x, routed, shared, perm, k, d_out, ws, grads=grads,
-                                           shared_grads=sgrads)
-        if ev is not None:
-            ev[8].record()
+            ev[8 - mxb].record()
         pg.moe_route_backward(x, wg, ids, weights, d_weights, offsets, perm, row_of, dx_rows, has_shared, ws,
-                              gate_grad=gate_grad, bias_grad=bias is not None, dx=dx)
+                              gate_grad=gate_grad, bias_grad=bias is not None, dx=dx, x_scale=inp["x_scale"])
         if ev is not None:
-            ev[9].record()
+            ev[9 - mxb].record()
 
     for _ in range(args.warmup):
         step()
@@ -180,7 +191,8 @@ def main():
     if st != 0:
         raise pg.MoeError(st, "warmup")
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(10 if bwd else 6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range((9 if mxb else 10) if bwd else 6)]
+              for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -192,7 +204,9 @@ def main():
         raise pg.MoeError(st, "timed steps")
 
     names = ["route", "dispatch", "ffn_gate_up", "ffn_down", "combine"]
-    if bwd:
+    if mxb:
+        names += ["combine_backward", "ffn_backward", "route_backward"]
+    elif bwd:
         names += ["combine_backward", "ffn_backward_data", "ffn_backward_weights", "route_backward"]
     stage_ms = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1])
                                   for i in range(args.steps)])) for j, n in enumerate(names)}
@@ -242,8 +256,16 @@ def main():
         stages["ffn_gate_up"]["alg_bytes"] += rows * 2 * I * 4   # the saved pre-activations
         stages["ffn_gate_up"]["GB_s"] = gbs(stages["ffn_gate_up"]["alg_bytes"], stage_ms["ffn_gate_up"])
         flops_wts = 2.0 * rows * d * I * 3
-        for n, b, f in (("combine_backward", bytes_cbwd, None), ("ffn_backward_data", bytes_data, flops_data),
-                        ("ffn_backward_weights", bytes_wts, flops_wts), ("route_backward", bytes_rbwd, None)):
+        parts = [("combine_backward", bytes_cbwd, None), ("route_backward", bytes_rbwd, None)]
+        if mxb:
+            # MXFP8 expert backward, one call: the requantised weights (fp8 + scales), the saved
+            # pre-activations, d_out, x, the dx rows written and every expert's fp32 gradients
+            bytes_mxb = (n_mats * 3 * mat + rows * 2 * I * 4 + rows * d * ob + T * d * eb + rows * d * 4
+                         + n_all * 3 * I * d * 4)
+            parts.append(("ffn_backward", bytes_mxb, flops_data + flops_wts))
+        else:
+            parts += [("ffn_backward_data", bytes_data, flops_data), ("ffn_backward_weights", bytes_wts, flops_wts)]
+        for n, b, f in parts:
             stages[n] = {"ms": stage_ms[n], "alg_bytes": b, "GB_s": gbs(b, stage_ms[n])}
             if f is not None:
                 stages[n]["TFLOP_s"] = f / (stage_ms[n] * 1e-3) / 1e12
@@ -270,19 +292,26 @@ def main():
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
 
-    if bwd:
+    if mxb:
+        # the expert backward: MXFP8 GEMMs, bound by its HBM traffic (every expert's fp32
+        # gradients dominate it)
+        bdom = "ffn_backward"
+        dom_kernel = ("moe_expert_ffn_backward_mxfp8: mx_bwd_gemm_kernel<0..2> + MX quantisers (dh, dx; "
+                      "dW2, dW1 | dW3 of every expert)")
+    if bwd and not mxb:
         # the step's largest stage is one of the two backward halves; both stream HBM
         bdom = max(("ffn_backward_data", "ffn_backward_weights"), key=lambda n: stage_ms[n])
         dom_kernel = {"ffn_backward_data": "bwd_gemm_kernel<0>/<1> + recompute (dx half: "
                                            "a, g; dh with SwiGLU backward; dx rows)",
                       "ffn_backward_weights": "bwd_gemm_kernel<2>, <3> (dW2; dW1 and dW3, fp32 "
                                               "gradients of every expert)"}[bdom]
+    if bwd:
         achieved = stages[bdom]["GB_s"]
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
         dom = bdom
     result = {
-        "metric": METRIC if not bwd else "MoE-layer forward+backward tokens/s, 384-expert top-8 d=7168 bf16",
+        "metric": METRIC if not bwd else f"MoE-layer forward+backward tokens/s, 384-expert top-8 d=7168 {wl.dtype}",
         "value": T / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -421,6 +450,8 @@ def cpu_baseline(inp, wl, ids, n_tok, log_tau=None, dy=None):
         oracle.layer_nvfp4(x, wg, bias, experts, shared, wl.k, **kw)
     elif dy is None:
         oracle.layer(x, wg, bias, experts, shared, wl.k, **kw)
+    elif wl.dtype == "mxfp8":
+        oracle.layer_backward_mxfp8(x, wg, bias, experts, shared, wl.k, dy[rows].float().cpu().numpy(), **kw)
     else:
         oracle.layer_backward(x, wg, bias, experts, shared, wl.k, dy[rows].float().cpu().numpy(),
                               dense=False, **kw)

@@ -303,8 +303,9 @@ moe_status moe_combine(const void* out, int dtype, const int32_t* row_of, const 
 
 /* moe_expert_ffn_gate_up that also keeps the pre-activations for the backward pass:
  * pre out fp32 [T*k (+T)][2*inter], row j = (x W1, x W3) of dispatched row j, exactly the
- * values the SwiGLU epilogue uses (bf16 layers only; MOE_ERR_UNSUPPORTED otherwise).
- * Same results as moe_expert_ffn_gate_up; pass `pre` to moe_expert_ffn_backward. */
+ * values the SwiGLU epilogue uses (bf16 and MXFP8 layers; MOE_ERR_UNSUPPORTED otherwise).
+ * Same results as moe_expert_ffn_gate_up; pass `pre` to moe_expert_ffn_backward (bf16) or
+ * moe_expert_ffn_backward_mxfp8. */
 moe_status moe_expert_ffn_gate_up_save(const void* x, const uint8_t* x_scale, int dtype, int T, int d,
                                        int E, int k, int inter, const moe_expert_bank* routed,
                                        const moe_expert_bank* shared, const int32_t* offsets,
@@ -393,6 +394,62 @@ moe_status moe_expert_ffn_backward_weights(const void* x, int dtype, int T, int 
                                            const void* d_out, const moe_grad_bank* routed_grads,
                                            const moe_grad_bank* shared_grads, void* ws,
                                            size_t ws_bytes, void* stream);
+
+/* The expert weights of an MXFP8 layer requantised for the backward's data-gradient
+ * GEMMs, whose reductions run along the other axis of each weight (Composer 2
+ * Technical Report, section 6.1 "Kernels": the MoE backward in MXFP8, one E8M0 scale
+ * per 32 elements of the reduction):
+ *   w2t  [n][I][d] E4M3 codes, w2t_scale [n][I][d/32]: row c of expert e is column c of
+ *        W2[e] (over d), quantised along d;
+ *   w13t [n][d][2I] codes, w13t_scale [n][d][2I/32]: row i of expert e is column i of
+ *        W1[e] (over I), then column i of W3[e], quantised along I.
+ * Scales are the smallest power of two that maps a block's largest magnitude to at most
+ * 448; elements round to the nearest E4M3 value, ties to even.  Codes 16-byte aligned,
+ * scales 4-byte aligned. */
+typedef struct {
+  uint8_t* w2t;
+  uint8_t* w2t_scale;
+  uint8_t* w13t;
+  uint8_t* w13t_scale;
+} moe_mxfp8_tbank;
+
+/* Writes the requantised weights of an MXFP8 bank of n experts (w1, w3 [n][I][d] and w2
+ * [n][d][I] with their E8M0 scales, as moe_expert_bank holds them) into `out`; call once
+ * per weight version.  Requires d % 128 == 0 and inter % 128 == 0 (else
+ * MOE_ERR_UNSUPPORTED); MOE_ERR_INVALID_ARG for missing or misaligned pointers. */
+moe_status moe_mxfp8_transpose_weights(const moe_expert_bank* bank, int n, int d, int inter,
+                                       const moe_mxfp8_tbank* out, void* stream);
+
+/* Backward of moe_expert_ffn for MXFP8 layers, with every backward GEMM on the
+ * block-scaled matrix cores and both of its operands in MXFP8 blocked along its own
+ * reduction dimension (Composer 2 Technical Report, section 6.1 "Kernels", Figure 10):
+ *   dh = MX_row(d_out) . MX_d(W2)^T, da = dh g silu'(a), dg = dh silu(a),
+ *   dx_rows = MX_row(da | dg) . MX_I(W1 | W3)^T        (row-local: a token's dx rows do
+ *                                                     not depend on the other tokens),
+ *   dW2 = MX_rows(d_out)^T MX_rows(hq), dW1 | dW3 = MX_rows(da | dg)^T MX_rows(x)
+ * where MX_row quantises each row, MX_rows quantises along the expert's rows in blocks
+ * of 32 from its first row (zero-padded), and hq is the forward's MXFP8 h (recomputed
+ * from the pre-activations with the forward's arithmetic).
+ *   x, x_scale   the layer's MXFP8 activations [T][d] and scales [T][d/32].
+ *   routed, shared, offsets, perm  as moe_expert_ffn; routed_t, shared_t: the banks'
+ *                requantised weights (moe_mxfp8_transpose_weights); shared_t NULL iff
+ *                shared is NULL.
+ *   pre          fp32 [T*k (+T)][2*inter] from moe_expert_ffn_gate_up_save, or NULL:
+ *                then recomputed with the forward's GEMM (one more pass over W1, W3).
+ *   d_out        bf16 [T*k (+T)][d] from moe_combine_backward.
+ *   dx_rows      out fp32 [T*k (+T)][d]; routed_grads, shared_grads out fp32, as
+ *                moe_expert_ffn_backward (every expert written, zero without rows).
+ *   ws           sized by moe_backward_workspace_size(..., MOE_MXFP8).
+ * MOE_ERR_UNSUPPORTED unless d % 128 == 0 and inter % 128 == 0. */
+moe_status moe_expert_ffn_backward_mxfp8(const void* x, const uint8_t* x_scale, int T, int d, int E,
+                                         int k, int inter, const moe_expert_bank* routed,
+                                         const moe_expert_bank* shared,
+                                         const moe_mxfp8_tbank* routed_t,
+                                         const moe_mxfp8_tbank* shared_t, const int32_t* offsets,
+                                         const int32_t* perm, const float* pre, const void* d_out,
+                                         float* dx_rows, const moe_grad_bank* routed_grads,
+                                         const moe_grad_bank* shared_grads, void* ws,
+                                         size_t ws_bytes, void* stream);
 
 /* Backward of the routing and of the token gather.
  *   dx        out fp32 [T][d]: sum_r dx_rows[row_of[t,r]] (r ascending), plus

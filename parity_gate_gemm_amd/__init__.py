@@ -20,7 +20,8 @@ __all__ = [
     "moe_dispatch", "moe_dispatch_noalloc", "moe_expert_ffn", "moe_expert_ffn_gate_up", "moe_expert_ffn_down", "moe_combine", "moe_check", "moe_status_string",
     "layer_forward", "moe_backward_workspace_size", "moe_combine_backward", "moe_expert_ffn_backward",
     "moe_route_backward", "layer_backward", "moe_expert_ffn_backward_data",
-    "moe_expert_ffn_backward_weights", "moe_expert_ffn_gate_up_save",
+    "moe_expert_ffn_backward_weights", "moe_expert_ffn_gate_up_save", "moe_mxfp8_transpose_weights",
+    "moe_expert_ffn_backward_mxfp8",
 ]
 
 MOE_F32, MOE_BF16, MOE_MXFP8, MOE_NVFP4 = 0, 1, 2, 3
@@ -44,6 +45,11 @@ class _Bank(ctypes.Structure):
 
 class _GradBank(ctypes.Structure):
     _fields_ = [("dw1", ctypes.c_void_p), ("dw3", ctypes.c_void_p), ("dw2", ctypes.c_void_p)]
+
+
+class _TBank(ctypes.Structure):
+    _fields_ = [("w2t", ctypes.c_void_p), ("w2t_scale", ctypes.c_void_p), ("w13t", ctypes.c_void_p),
+                ("w13t_scale", ctypes.c_void_p)]
 
 
 def lib():
@@ -79,6 +85,10 @@ def lib():
                                           P],
             "moe_dispatch": [P, I, I, I, P, P, P, P, SZ, P],
             "moe_dispatch_noalloc": [P, I, I, I, P, P, P, P, P],
+            "moe_mxfp8_transpose_weights": [ctypes.POINTER(_Bank), I, I, I, ctypes.POINTER(_TBank), P],
+            "moe_expert_ffn_backward_mxfp8": [P, P, I, I, I, I, I, ctypes.POINTER(_Bank), ctypes.POINTER(_Bank),
+                                              ctypes.POINTER(_TBank), ctypes.POINTER(_TBank), P, P, P, P, P,
+                                              ctypes.POINTER(_GradBank), ctypes.POINTER(_GradBank), P, SZ, P],
             "moe_expert_ffn": [P, P, I, I, I, I, I, I, ctypes.POINTER(_Bank), ctypes.POINTER(_Bank),
                                P, P, P, P, SZ, P],
             "moe_expert_ffn_gate_up": [P, P, I, I, I, I, I, I, ctypes.POINTER(_Bank),
@@ -302,11 +312,13 @@ def moe_check(ws: Workspace) -> int:
 
 
 def layer_forward(inp: dict, k: int, ws: Workspace | None = None, replay: bool = False,
-                  check: bool = True):
+                  check: bool = True, save_pre: bool = False):
     """One MoE layer forward through the five C calls.
 
     ``inp`` holds device tensors: x, x_scale, w_gate, bias, w1, w3, w2 (+ *_scale),
-    shared (dict or None) and, for replay, ids_in / weights_in.
+    shared (dict or None) and, for replay, ids_in / weights_in.  With ``save_pre`` the
+    expert FFN runs as its two halves, the first keeping the fp32 pre-activations for
+    the backward (returned as "pre").
     """
     x = inp["x"]
     T, d = x.shape
@@ -324,14 +336,20 @@ def layer_forward(inp: dict, k: int, ws: Workspace | None = None, replay: bool =
         ids, weights = moe_route(x, inp["w_gate"], inp.get("bias"), k, ws, x_scale=inp.get("x_scale"))
     offsets, perm, row_of = moe_dispatch(ids, E, ws)
     routed = {n: inp.get(n) for n in ("w1", "w3", "w2") + _BANK_OPT}
-    out = moe_expert_ffn(x, routed, inp.get("shared"), offsets, perm, k, ws, x_scale=inp.get("x_scale"))
+    pre = None
+    if save_pre:
+        pre = moe_expert_ffn_gate_up_save(x, routed, inp.get("shared"), offsets, perm, k, ws,
+                                          x_scale=inp.get("x_scale"))
+        out = moe_expert_ffn_down(dt, T, d, routed, inp.get("shared"), k, ws)
+    else:
+        out = moe_expert_ffn(x, routed, inp.get("shared"), offsets, perm, k, ws, x_scale=inp.get("x_scale"))
     y = moe_combine(out, row_of, weights, T, inp.get("shared") is not None, dt)
     if check:
         st = moe_check(ws)
         if st != 0:
             raise MoeError(st, "layer_forward")
     return {"y": y, "ids": ids, "weights": weights, "offsets": offsets, "perm": perm,
-            "row_of": row_of, "out": out}
+            "row_of": row_of, "out": out, "pre": pre}
 
 
 # ---------------------------------------------------------------------------
@@ -374,15 +392,16 @@ def _grad_like(bank):
             for n in ("w1", "w3", "w2")}
 
 
-def moe_expert_ffn_gate_up_save(x, routed: dict, shared, offsets, perm, k, ws: Workspace, pre=None):
+def moe_expert_ffn_gate_up_save(x, routed: dict, shared, offsets, perm, k, ws: Workspace, pre=None,
+                                x_scale=None):
     """GEMM1 half that also returns the fp32 pre-activations [rows][2I] for the backward."""
-    _check_dev(x, offsets, perm)
+    _check_dev(x, offsets, perm, x_scale)
     T, d = x.shape
     E, inter = routed["w1"].shape[0], routed["w1"].shape[1]
     rows = T * k + (T if shared is not None else 0)
     pre = torch.empty(rows, 2 * inter, dtype=torch.float32, device=x.device) if pre is None else pre
     rb, sb = _bank(routed), _bank(shared)
-    _ok(lib().moe_expert_ffn_gate_up_save(_ptr(x), None, _dtype_of(x), T, d, E, k, inter, ctypes.byref(rb),
+    _ok(lib().moe_expert_ffn_gate_up_save(_ptr(x), _ptr(x_scale), _dtype_of(x), T, d, E, k, inter, ctypes.byref(rb),
                                           ctypes.byref(sb) if sb is not None else None, _ptr(offsets),
                                           _ptr(perm), _ptr(pre), ws.ptr, ws.nbytes, _stream(x.device)),
         "moe_expert_ffn_gate_up_save")
@@ -474,9 +493,17 @@ def layer_backward(inp: dict, k: int, fwd: dict, dy, ws: Workspace, replay: bool
     has_shared = inp.get("shared") is not None
     d_out, d_weights = moe_combine_backward(dy, fwd["out"], fwd["row_of"], fwd["weights"], T, has_shared, dt)
     routed = {n: inp.get(n) for n in ("w1", "w3", "w2", "w1_scale", "w3_scale", "w2_scale")}
-    dx_rows, grads, sgrads = moe_expert_ffn_backward(x, routed, inp.get("shared"), fwd["offsets"],
-                                                     fwd["perm"], k, d_out, ws, x_scale=inp.get("x_scale"),
-                                                     pre=pre)
+    if dt == MOE_MXFP8:   # the requantised weights: from the caller, else made here
+        rt = inp.get("routed_t") or moe_mxfp8_transpose_weights(routed)
+        st = inp.get("shared_t") if inp.get("shared") is None or inp.get("shared_t") is not None else \
+            moe_mxfp8_transpose_weights(inp["shared"])
+        dx_rows, grads, sgrads = moe_expert_ffn_backward_mxfp8(x, inp["x_scale"], routed, inp.get("shared"), rt,
+                                                               st, fwd["offsets"], fwd["perm"], k, d_out, ws,
+                                                               pre=pre)
+    else:
+        dx_rows, grads, sgrads = moe_expert_ffn_backward(x, routed, inp.get("shared"), fwd["offsets"],
+                                                         fwd["perm"], k, d_out, ws, x_scale=inp.get("x_scale"),
+                                                         pre=pre)
     gate_grad = not (replay and inp.get("weights_in") is not None)
     dx, dwg, db = moe_route_backward(x, inp["w_gate"], fwd["ids"], fwd["weights"], d_weights,
                                      fwd["offsets"], fwd["perm"], fwd["row_of"], dx_rows, has_shared, ws,
@@ -488,6 +515,55 @@ def layer_backward(inp: dict, k: int, fwd: dict, dy, ws: Workspace, replay: bool
             raise MoeError(st, "layer_backward")
     return {"dx": dx, "d_weights": d_weights, "d_w_gate": dwg, "d_bias": db, "grads": grads,
             "shared_grads": sgrads, "dx_rows": dx_rows, "d_out": d_out}
+
+
+def moe_mxfp8_transpose_weights(bank: dict) -> dict:
+    """The requantised weights of an MXFP8 bank (w1, w3 [n][I][d], w2 [n][d][I] with their
+    scales; a shared bank may drop the leading n) for the MXFP8 backward: w2t [n][I][d],
+    w13t [n][d][2I] and their scales."""
+    _check_dev(*(bank[n] for n in ("w1", "w3", "w2", "w1_scale", "w3_scale", "w2_scale")))
+    one = bank["w1"].dim() == 2
+    w1 = bank["w1"].unsqueeze(0) if one else bank["w1"]
+    n, inter, d = w1.shape
+    dev = w1.device
+    out = {"w2t": torch.empty(n, inter, d, dtype=torch.uint8, device=dev),
+           "w2t_scale": torch.empty(n, inter, d // 32, dtype=torch.uint8, device=dev),
+           "w13t": torch.empty(n, d, 2 * inter, dtype=torch.uint8, device=dev),
+           "w13t_scale": torch.empty(n, d, 2 * inter // 32, dtype=torch.uint8, device=dev)}
+    tb = _TBank(*(out[k].data_ptr() for k in ("w2t", "w2t_scale", "w13t", "w13t_scale")))
+    _ok(lib().moe_mxfp8_transpose_weights(ctypes.byref(_bank(bank)), n, d, inter, ctypes.byref(tb),
+                                          _stream(dev)), "moe_mxfp8_transpose_weights")
+    return {k: (v[0] if one else v) for k, v in out.items()}
+
+
+def _tbank(t):
+    if t is None:
+        return None
+    _check_dev(*t.values())
+    return _TBank(*(t[k].data_ptr() for k in ("w2t", "w2t_scale", "w13t", "w13t_scale")))
+
+
+def moe_expert_ffn_backward_mxfp8(x, x_scale, routed: dict, shared, routed_t: dict, shared_t, offsets, perm,
+                                  k, d_out, ws: Workspace, pre=None, dx_rows=None, grads=None,
+                                  shared_grads=None):
+    """Returns (dx_rows [rows][d] fp32, grads {w1, w3, w2} fp32, shared grads or None)."""
+    _check_dev(x, x_scale, offsets, perm, d_out, pre)
+    T, d = x.shape
+    E, inter = routed["w1"].shape[0], routed["w1"].shape[1]
+    rows = T * k + (T if shared is not None else 0)
+    dx_rows = torch.empty(rows, d, dtype=torch.float32, device=x.device) if dx_rows is None else dx_rows
+    grads = _grad_like(routed) if grads is None else grads
+    if shared is not None and shared_grads is None:
+        shared_grads = _grad_like(shared)
+    rb, sb = _bank(routed), _bank(shared)
+    rt, st = _tbank(routed_t), _tbank(shared_t)
+    rg, sg = _grads(grads), _grads(shared_grads)
+    ref = lambda v: ctypes.byref(v) if v is not None else None  # noqa: E731
+    _ok(lib().moe_expert_ffn_backward_mxfp8(_ptr(x), _ptr(x_scale), T, d, E, k, inter, ref(rb), ref(sb), ref(rt),
+                                            ref(st), _ptr(offsets), _ptr(perm), _ptr(pre), _ptr(d_out),
+                                            _ptr(dx_rows), ref(rg), ref(sg), ws.ptr, ws.nbytes, _stream(x.device)),
+        "moe_expert_ffn_backward_mxfp8")
+    return dx_rows, grads, shared_grads
 
 
 def moe_nvfp4_pack_weights(codes, block_scales):

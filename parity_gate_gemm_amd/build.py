@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["api.hip", "route.hip", "screen.hip", "dispatch.hip", "ffn.hip", "mxfp8.hip", "combine.hip", "backward.hip", "nvfp4.hip"]
+SOURCES = ["api.hip", "route.hip", "screen.hip", "dispatch.hip", "ffn.hip", "mxfp8.hip", "combine.hip", "backward.hip", "nvfp4.hip", "mxfp8_bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -466,7 +466,7 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(float* __restrict__ p, l
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
     p[i] = 0.0f;
 }
-static void zero_fill(float* p, long long n, hipStream_t s) {
+void zero_fill(float* p, long long n, hipStream_t s) {
   if (n <= 0) return;
   const long long blocks = (n + 255) / 256;
   zero_fill_kernel<<<(unsigned)(blocks < 65536 ? blocks : 65536), 256, 0, s>>>(p, n);
@@ -582,7 +582,8 @@ extern "C" moe_status moe_backward_workspace_size(int T, int d, int E, int k, in
   if (!bytes || T < 0 || d < 1 || E < 1 || E > kMaxExperts || k < 1 || k > E || k > kMaxTopK ||
       inter < 1 || !valid_layer_dtype(dtype))
     return MOE_ERR_INVALID_ARG;
-  const size_t a = workspace_bytes(T, d, E, k, inter, dtype), b = bwd_ws(T, d, E, k, inter).bytes;
+  const size_t a = workspace_bytes(T, d, E, k, inter, dtype);
+  const size_t b = dtype == MOE_MXFP8 ? mxfp8_backward_ws_bytes(T, d, E, k, inter) : bwd_ws(T, d, E, k, inter).bytes;
   *bytes = a > b ? a : b;
   return MOE_OK;
 }

@@ -19,7 +19,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int BM = kGemmBM;   // 128 rows per tile
-constexpr int BNR = 128;      // B rows (output features) staged per tile
 constexpr int BK = 64;        // reduction step
 constexpr int LDSS = BK + 8;  // LDS row stride in bf16 elements (144 B: conflict-free 16-B reads)
 
@@ -498,6 +497,7 @@ static moe_status run_gate_up(const void* x, const uint8_t* xs, int dtype, int T
     g.S = p.S;
     g.out = p.h;
     g.out_scale = p.hs;
+    g.out_pre = pre;
     g.flag = p.flag;
     const moe_status st = mx_gemm(0, g, p.mt_bound, s);
     if (st != MOE_OK) return st;
@@ -660,6 +660,13 @@ static moe_status run_down(int dtype, int T, int d, int E, int k, int inter,
   return launch_status();
 }
 
+moe_status ffn_seg_table_rows(const int32_t* offsets, int T, int E, int k, int has_shared, int tm, int* seg,
+                              int* flag, hipStream_t s) {
+  seg_table_kernel<<<1, 1024, 0, s>>>(offsets, E, (long long)T * k, T, has_shared, tm, seg, seg + (E + 2),
+                                      seg + 2 * (E + 2), flag);
+  return launch_status();
+}
+
 moe_status ffn_seg_table(const int32_t* offsets, int T, int E, int k, int has_shared, int* seg, int* flag,
                          hipStream_t s) {
   seg_table_kernel<<<1, 1024, 0, s>>>(offsets, E, (long long)T * k, T, has_shared, BM, seg, seg + (E + 2),
@@ -742,10 +749,13 @@ extern "C" moe_status moe_expert_ffn_gate_up_save(const void* x, const uint8_t* 
                                                   void* stream) {
   moe_status st = check_ffn_shape(dtype, T, d, E, k, inter, routed, shared, ws, ws_bytes);
   if (st != MOE_OK) return st;
-  if (dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-  if (x_scale || !offsets) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_BF16 && dtype != MOE_MXFP8) return MOE_ERR_UNSUPPORTED;
+  if ((dtype == MOE_MXFP8) != (x_scale != nullptr) || !offsets) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !perm || !pre || !aligned(x, 16) || !aligned(pre, 16)) return MOE_ERR_INVALID_ARG;
+  if (dtype == MOE_MXFP8 && (!aligned(x_scale, 4) || !mx_bank_aligned(routed) ||
+                             (shared && !mx_bank_aligned(shared))))
+    return MOE_ERR_INVALID_ARG;
   const FfnPlan p = plan_of(ws, T, d, E, k, inter, dtype, shared != nullptr);
   return run_gate_up(x, x_scale, dtype, T, d, E, k, inter, routed, shared, offsets, perm, p,
                      (hipStream_t)stream, pre);

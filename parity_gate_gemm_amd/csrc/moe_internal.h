@@ -300,12 +300,14 @@ struct MxArgs {
   int S;
   void* out;                 // GEMM1: h codes [rows][I]; GEMM2: bf16 [rows][d]
   uint8_t* out_scale;        // GEMM1: h scales [rows][I/32]
+  float* out_pre;            // GEMM1 (mode 0, optional; mode 2): fp32 x W1 | x W3 [rows][2I]
   int* flag;
 };
 // Rows per tile of the MXFP8 GEMMs for hidden size d and intermediate size inter (the
 // segment table counts tiles of this height).
 int mx_tile_rows(int d, int inter);
-// Launch GEMM1 (mode 0) or GEMM2 (mode 1); mt_bound bounds the segment table's row tiles.
+// Launch GEMM1 (mode 0; mode 2: only the pre-activations into out_pre) or GEMM2 (mode 1);
+// mt_bound bounds the segment table's row tiles.
 moe_status mx_gemm(int mode, MxArgs g, long long mt_bound, hipStream_t s);
 
 // NVFP4 expert FFN (nvfp4.hip).
@@ -343,6 +345,13 @@ moe_status nvfp4_gemm(int mode, const Nvfp4Gemm& q, hipStream_t s);
 // tiles into seg (mstart [E + 2], rowstart [E + 2], rowcount [E + 2]) and the GEMM1
 // pre-activations of every dispatched row, pre [rows][2 inter] fp32 (x W1, then x W3),
 // with the forward's MFMA sequence (bf16 only).
+// Zero fill of n floats by a kernel (backward.hip).
+void zero_fill(float* p, long long n, hipStream_t s);
+// Workspace bytes of the MXFP8 backward (mxfp8_bwd.hip).
+size_t mxfp8_backward_ws_bytes(int T, int d, int E, int k, int inter);
+// Segment table with tiles of tm rows (ffn_seg_table: tm = kGemmBM).
+moe_status ffn_seg_table_rows(const int32_t* offsets, int T, int E, int k, int has_shared, int tm, int* seg,
+                              int* flag, hipStream_t s);
 moe_status ffn_seg_table(const int32_t* offsets, int T, int E, int k, int has_shared, int* seg, int* flag,
                          hipStream_t s);
 moe_status ffn_recompute_pre(const void* x, int T, int d, int E, int k, int inter,

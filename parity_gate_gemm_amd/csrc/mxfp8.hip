@@ -6,6 +6,7 @@
 #include <math.h>
 
 #include "moe_internal.h"
+#include "mx_common.h"
 
 namespace moe {
 
@@ -48,109 +49,6 @@ constexpr int MBK = 128;               // reduction step in elements (= bytes)
 constexpr int MLDS = MBK + 16;         // LDS row stride in bytes
 
 
-// fp32 (already divided by its block scale) -> E4M3 code, round to nearest even,
-// saturating to +-448 (NaN -> 0x7F).
-__device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const float a = fabsf(v);
-  if (a != a) return 0x7Fu;
-  if (!(a < 448.0f)) return sign | 0x7Eu;
-  const uint32_t ua = __float_as_uint(a);
-  if (ua < 0x00800000u) return sign;                 // below 2^-126: rounds to zero
-  const int e = (int)(ua >> 23) - 127;
-  const uint32_t full = (ua & 0x7FFFFFu) | 0x800000u;
-  const int shift = e >= -6 ? 20 : 20 + (-6 - e);
-  if (shift > 24) return sign;                       // below 2^-10: rounds to zero
-  uint32_t keep = full >> shift;
-  const uint32_t rem = full & ((1u << shift) - 1u), half = 1u << (shift - 1);
-  keep += (rem > half || (rem == half && (keep & 1u))) ? 1u : 0u;
-  if (e >= -6) {
-    int ef = e + 7;
-    if (keep == 16u) {
-      ++ef;
-      keep = 8u;
-    }
-    return sign | ((uint32_t)ef << 3) | (keep - 8u);
-  }
-  return sign | keep;                                // subnormal grid (keep == 8: 2^-6)
-}
-
-// E8M0 scale 2^se of one MX block whose largest magnitude is amax: the smallest power of
-// two X with amax / X <= 448, the largest E4M3 value, so that no element of the block
-// saturates.  (The conversion OCP MX v1.0 suggests, X = 2^(floor(log2 amax) - 8), leaves
-// amax / X in [256, 512) and clamps a block's largest elements to 448 whenever amax / X
-// exceeds 448; both give the same X otherwise.)  All-zero blocks get code 0 (2^-127),
-// non-finite ones code 255 (NaN).
-__device__ __forceinline__ void mx_block_scale(float amax, int& se, uint32_t& scode) {
-  if (amax == 0.0f) {
-    se = -127;
-    scode = 0;
-  } else if (!(amax <= 3.0e38f)) {
-    se = 0;
-    scode = 255;
-  } else {
-    int e = ilogbf(amax) - 8;
-    if (ldexpf(amax, -e) > 448.0f) ++e;   // exact: a power-of-two scaling
-    se = min(max(e, -127), 127);
-    scode = (uint32_t)(se + 127);
-  }
-}
-
-// Requantise one row's 32-feature MX block (this value and the 31 other lanes of the
-// half wavefront) and store its code and the block's scale (mx_block_scale).
-__device__ __forceinline__ void mx_store_h(float h, bool live, uint8_t* code, uint8_t* scale,
-                                           bool first) {
-  float amax = fabsf(h);
-#pragma unroll
-  for (int off = 1; off < 32; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  int se;
-  uint32_t scode;
-  mx_block_scale(amax, se, scode);
-  if (live) {
-    *code = (uint8_t)e4m3_rne_sat(ldexpf(h, -se));
-    if (first) *scale = (uint8_t)scode;
-  }
-}
-
-// Requantise one MX block (32 consecutive fp32 features of a row, at `src` in LDS, read
-// by one lane) and store its 32 codes (two 16-byte stores) and its scale.  Same scale
-// rule (mx_block_scale) and encoding as mx_store_h.  Two passes over LDS (the block's
-// amax, then the codes) keep few values live.
-__device__ __forceinline__ void mx_store_block(const uint8_t* src, uint8_t* code, uint8_t* scale) {
-  float amax = 0.0f;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const float4 t = *(const float4*)(src + 16 * c);
-    amax = fmaxf(fmaxf(amax, fmaxf(fabsf(t.x), fabsf(t.y))), fmaxf(fabsf(t.z), fabsf(t.w)));
-  }
-  int se;
-  uint32_t scode;
-  mx_block_scale(amax, se, scode);
-  // v_cvt_pk_fp8_f32 rounds to nearest even onto the OCP E4M3 grid; with its input
-  // clamped to +-448 it equals e4m3_rne_sat (checked on every rounding boundary of
-  // every binade from 2^-20 to 2^10, the subnormal grid, +-0 and the infinities), and
-  // NaN is kept as 0x7F explicitly
-  u32x4_t w[2];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const float4 t = *(const float4*)(src + 16 * c);
-    const float v[4] = {ldexpf(t.x, -se), ldexpf(t.y, -se), ldexpf(t.z, -se), ldexpf(t.w, -se)};
-    int d = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(v[0], -448.0f), 448.0f),
-                                            fminf(fmaxf(v[1], -448.0f), 448.0f), 0, false);
-    d = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(v[2], -448.0f), 448.0f),
-                                        fminf(fmaxf(v[3], -448.0f), 448.0f), d, true);
-    uint32_t du = (uint32_t)d;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      if (v[b] != v[b]) du = (du & ~(0xFFu << (8 * b))) | (0x7Fu << (8 * b));
-    w[c >> 2][c & 3] = du;
-  }
-  *(u32x4_t*)code = w[0];
-  *(u32x4_t*)(code + 16) = w[1];
-  *scale = (uint8_t)scode;
-}
-
 // Tile: (64 WM) rows x (32 FN WN) staged B rows, WM x WN wavefronts; each wavefront
 // owns 64 rows x 32 FN B rows as 2 x FN MFMA blocks.  K advances 128 bytes a step:
 // registers -> LDS (144-byte rows) -> two 64-wide MFMA steps, with the next step's
@@ -186,7 +84,8 @@ void grouped_gemm_mx_kernel(MxArgs g) {
   const int nt = rem / gm, mt = grp * kGroupM + rem % gm;
   const int row0 = g.rowstart[s] + mt * TM;
   const int mrows = min(TM, g.rowcount[s] - mt * TM);
-  const int n0 = nt * (MODE == 0 ? TB / 2 : TB);
+  constexpr bool G1 = MODE != 1;             // GEMM1 operands (modes 0 and 2)
+  const int n0 = nt * (G1 ? TB / 2 : TB);
   const bool is_shared = (s == g.E);
   const long long e = is_shared ? 0 : s;
 
@@ -199,7 +98,7 @@ void grouped_gemm_mx_kernel(MxArgs g) {
   auto a_src = [&](int r, int& bad) -> long long {
     const long long jr = (long long)row0 + (r < mrows ? r : 0);
     long long src;
-    if (MODE == 0) {
+    if (G1) {
       src = is_shared ? jr - g.Tk : (long long)(g.perm[jr] / g.k);
       if (src < 0 || src >= g.T) {
         bad = 1;
@@ -212,7 +111,7 @@ void grouped_gemm_mx_kernel(MxArgs g) {
   };
   // row (within expert e's matrix) of staged B row r, with its code and scale banks
   auto b_row = [&](int r, const uint8_t*& bank, const uint8_t*& sbank) -> long long {
-    if (MODE == 0) {
+    if (G1) {
       const int blk = r >> 5, within = r & 31;
       const bool w3 = blk & 1;
       bank = w3 ? (is_shared ? g.sb1 : g.b1) : (is_shared ? g.sb0 : g.b0);
@@ -337,14 +236,20 @@ void grouped_gemm_mx_kernel(MxArgs g) {
       const int i = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
       const int r = wm * 64 + mb * 32 + i;
       const long long orow = (long long)row0 + r;
-      if (MODE == 0) {
+      if (G1) {
         // One MX block = this row's 32 features, spread over the 32 lanes of a half.
 #pragma unroll
         for (int p = 0; p < FN / 2; ++p) {
-          const float hv = silu_f32(acc[mb][2 * p][v]) * acc[mb][2 * p + 1][v];
           const int col = n0 + (wn * FN / 2 + p) * 32 + j;
-          mx_store_h(hv, r < mrows, (uint8_t*)g.out + orow * g.N + col,
-                     g.out_scale + orow * (g.N / 32) + col / 32, j == 0);
+          if (g.out_pre && r < mrows) {   // pre-activations for the backward pass
+            g.out_pre[orow * 2 * g.N + col] = acc[mb][2 * p][v];
+            g.out_pre[orow * 2 * g.N + g.N + col] = acc[mb][2 * p + 1][v];
+          }
+          if (MODE == 0) {
+            const float hv = silu_f32(acc[mb][2 * p][v]) * acc[mb][2 * p + 1][v];
+            mx_store_h(hv, r < mrows, (uint8_t*)g.out + orow * g.N + col,
+                       g.out_scale + orow * (g.N / 32) + col / 32, j == 0);
+          }
         }
       } else {
         if (r < mrows) {
@@ -574,7 +479,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_mx_ring_kernel(MxArgs g) {
   const int nt = rem / gm, mt = grp * kGroupM + rem % gm;
   const int row0 = g.rowstart[s] + mt * XR_M;
   const int mrows = min(XR_M, g.rowcount[s] - mt * XR_M);
-  const int n0 = nt * (MODE == 0 ? XR_N / 2 : XR_N);
+  constexpr bool G1 = MODE != 1;   // GEMM1 operands (modes 0 and 2)
+  const int n0 = nt * (G1 ? XR_N / 2 : XR_N);
   const bool is_shared = (s == g.E);
   const long long e = is_shared ? 0 : s;
 
@@ -587,7 +493,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_mx_ring_kernel(MxArgs g) {
   // source row of A tile row r (rows past the segment re-read the tile's first row)
   auto a_src = [&](int r) -> long long {
     const long long jr = (long long)row0 + (r < mrows ? r : 0);
-    if (MODE != 0) return jr;
+    if (!G1) return jr;
     long long src = is_shared ? jr - g.Tk : (long long)(g.perm[jr] / g.k);
     if (src < 0 || src >= g.T) {
       bad = 1;
@@ -598,7 +504,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_mx_ring_kernel(MxArgs g) {
   // row (within expert e's matrix) of staged B row r; GEMM1 alternates 32-row blocks of
   // W1 and W3 for the same 32 features
   auto b_row = [&](int r, const uint8_t*& bank, const uint8_t*& sbank) -> long long {
-    if (MODE == 0) {
+    if (G1) {
       const int blk = r >> 5;
       const bool w3 = blk & 1;
       bank = w3 ? (is_shared ? g.sb1 : g.b1) : (is_shared ? g.sb0 : g.b0);
@@ -675,6 +581,23 @@ __global__ __launch_bounds__(512) void grouped_gemm_mx_ring_kernel(MxArgs g) {
   //      (GEMM1) or 16-byte row chunks (GEMM2).  Accumulator element v of a lane is
   //      C[i][j], j = lane % 32, i = 8 (v / 4) + 4 (lane / 32) + v % 4; the wavefront's
   //      local row 32 mb + i is tile row 128 wm + 32 mb + i. ----
+  if (G1 && g.out_pre) {   // pre-activations for the backward pass, from the accumulators
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      if (mb >= nb_act) break;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 128 * wm + 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
+        if (r < mrows) {
+          const long long orow = (long long)row0 + r;
+          const int col = n0 + 32 * wn + j32;
+          g.out_pre[orow * 2 * g.N + col] = acc[mb][0][v];
+          g.out_pre[orow * 2 * g.N + g.N + col] = acc[mb][1][v];
+        }
+      }
+    }
+  }
+  if (MODE == 2) return;
   __syncthreads();   // every wavefront is done reading the ring
   uint8_t* stg = ring + wave * XR_EPI;
 #pragma unroll
@@ -735,9 +658,10 @@ static bool mx_ring_ok(int d, int inter) {
 int mx_tile_rows(int d, int inter) { return mx_ring_ok(d, inter) ? XR_M : 64 * MOE_MX_WM; }
 
 moe_status mx_gemm(int mode, MxArgs g, long long mt_bound, hipStream_t s) {
-  const int d = mode == 0 ? g.K : g.N, inter = mode == 0 ? g.N : g.K;
+  const bool g1 = mode != 1;
+  const int d = g1 ? g.K : g.N, inter = g1 ? g.N : g.K;
   const bool ring = mx_ring_ok(d, inter);
-  if (mode == 0) {
+  if (g1) {
     g.NT = ring ? inter / (XR_N / 2) : inter / (16 * MOE_MX_FN * MOE_MX_WN);
   } else {
     // the configured tile where its width divides d, else 64-column tiles of the same
@@ -751,10 +675,15 @@ moe_status mx_gemm(int mode, MxArgs g, long long mt_bound, hipStream_t s) {
   if (ring) {
     if (mode == 0)
       grouped_gemm_mx_ring_kernel<0><<<(unsigned)grid, 512, 0, s>>>(g);
+    else if (mode == 2)
+      grouped_gemm_mx_ring_kernel<2><<<(unsigned)grid, 512, 0, s>>>(g);
     else
       grouped_gemm_mx_ring_kernel<1><<<(unsigned)grid, 512, 0, s>>>(g);
   } else if (mode == 0) {
     grouped_gemm_mx_kernel<0, MOE_MX_WM, MOE_MX_WN, MOE_MX_FN>
+        <<<(unsigned)grid, 64 * MOE_MX_WM * MOE_MX_WN, 0, s>>>(g);
+  } else if (mode == 2) {
+    grouped_gemm_mx_kernel<2, MOE_MX_WM, MOE_MX_WN, MOE_MX_FN>
         <<<(unsigned)grid, 64 * MOE_MX_WM * MOE_MX_WN, 0, s>>>(g);
   } else if (d % (32 * MOE_MX_FN * MOE_MX_WN) == 0) {
     grouped_gemm_mx_kernel<1, MOE_MX_WM, MOE_MX_WN, MOE_MX_FN>

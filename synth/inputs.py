@@ -62,6 +62,9 @@ WORKLOADS = {
                                  dtype="bf16", seed=3),
     "mxfp8_t32768": Workload("mxfp8_t32768", T=32768, d=7168, inter=2048, shared=True,
                              dtype="mxfp8", bias=True, seed=4),
+    # the MXFP8 layer at the training batch of the bf16 layer (the backward's workload)
+    "mxfp8_t4096": Workload("mxfp8_t4096", T=4096, d=7168, inter=2048, shared=True,
+                            dtype="mxfp8", bias=True, seed=6),
     # the bf16 T = 4096 layer with NVFP4 experts (the pages' forward format)
     "nvfp4_t4096": Workload("nvfp4_t4096", T=4096, d=7168, inter=2048, shared=True,
                             dtype="nvfp4", seed=5),

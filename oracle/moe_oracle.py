@@ -553,6 +553,19 @@ def expert_forward_mxfp8(x_rows, w1, w3, w2, quant=mx_quantize):
     return a, g, hq, hq @ f64(w2).T
 
 
+def expert_forward_nvfp4(x_rows, w1, w3, w2):
+    """One expert of the NVFP4 forward (``expert_ffn_nvfp4``), keeping what its MXFP8
+    backward takes: (xq, a, g, hq, out, (W1, W3, W2)) with xq the rows quantized to NVFP4
+    per row, a = xq W1, g = xq W3, hq = NVFP4(bf16(silu(a) g)) per row, out = hq W2, and
+    the weights' exact values."""
+    W1, W3, W2 = (nvfp4_dequant(*w) for w in (w1, w3, w2))
+    xq = nvfp4_dequant(*nvfp4_quantize(np.asarray(x_rows, dtype=np.float32)))
+    a = xq @ W1.T
+    g = xq @ W3.T
+    hq = nvfp4_dequant(*nvfp4_quantize(bf16_rne(silu(a) * g).astype(np.float32)))
+    return xq, a, g, hq, hq @ W2.T, (W1, W3, W2)
+
+
 def expert_backward_mxfp8(x_rows, a, g, hq, d_out_rows, w1, w3, w2, quant=mx_quantize):
     """The MXFP8 backward of one expert over its rows (readings above): returns (dx rows,
     dW1, dW3, dW2, dL/dh rows)."""
@@ -574,7 +587,7 @@ def expert_backward_mxfp8(x_rows, a, g, hq, d_out_rows, w1, w3, w2, quant=mx_qua
 
 
 def layer_backward_mxfp8(x, w_gate, bias, experts, shared, k: int, dy, ids_in=None,
-                         weights_in=None, quant=mx_quantize, grad_round=None):
+                         weights_in=None, quant=mx_quantize, grad_round=None, forward="mxfp8"):
     """Gradients of L = <dy, y> through the MXFP8 layer, under the readings above.
 
     Same arguments and result keys as ``layer_backward`` (the inputs are the exact
@@ -584,7 +597,13 @@ def layer_backward_mxfp8(x, w_gate, bias, experts, shared, k: int, dy, ids_in=No
     bf16 (``grad_round``, default ``bf16_rne``), before it enters the expert backward.
     ``quant(v, axis)`` is the quantiser; an identity quantiser and rounding turn this
     into the exact chain rule of the unquantised layer (``layer_backward``).
+    With forward="nvfp4" the layer's forward is the NVFP4 one (``layer_nvfp4``: experts
+    and shared given as NVFP4 triples, x bf16): its backward is the same MXFP8 backward
+    on the forward's operands as that forward quantized them (xq, the weights' NVFP4
+    values, hq; Composer 2 Technical Report, §6.1 "Kernels": NVFP4 forward, MXFP8
+    backward).
     """
+    nv = forward == "nvfp4"
     if grad_round is None:
         grad_round = bf16_rne
     xf = f64(x)
@@ -596,22 +615,31 @@ def layer_backward_mxfp8(x, w_gate, bias, experts, shared, k: int, dy, ids_in=No
         ids, w, logits = route_replay(xf, w_gate, bias, ids_in, weights_in)
     E = logits.shape[1]
     offsets, perm, row_of = dispatch(ids, E)
-    I = f64(experts[0][0]).shape[0] if E else 0
+    I = f64(experts[0][0]).shape[0] if E and not nv else 0
     rows_out = np.zeros((T * k, d))
     saved = {}
+
+    def fwd(xr, ws):
+        if nv:
+            return expert_forward_nvfp4(xr, *ws)
+        a, g, hq, o = expert_forward_mxfp8(xr, *ws, quant=quant)
+        return xr, a, g, hq, o, ws
+
+    if nv and E:
+        I = nvfp4_dequant(*experts[0][0]).shape[0]
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi == lo:
             continue
-        a, g, hq, o = expert_forward_mxfp8(xf[perm[lo:hi] // k], *experts[e], quant=quant)
+        xq, a, g, hq, o, wv = fwd(xf[perm[lo:hi] // k], experts[e])
         rows_out[lo:hi] = o
-        saved[e] = (a, g, hq)
+        saved[e] = (xq, a, g, hq, wv)
     y = np.zeros((T, d))
     for t in range(T):
         for r in range(k):
             y[t] += w[t, r] * rows_out[row_of[t * k + r]]
     if shared is not None:
-        sa, sg, shq, so = expert_forward_mxfp8(xf, *shared, quant=quant)
+        sxq, sa, sg, shq, so, swv = fwd(xf, shared)
         y += so
     d_weights = np.empty((T, k))
     d_rows = np.empty_like(rows_out)
@@ -624,16 +652,16 @@ def layer_backward_mxfp8(x, w_gate, bias, experts, shared, k: int, dy, ids_in=No
     dw1, dw3, dw2 = {}, {}, {}
     dh_rows = np.zeros((T * k + (T if shared is not None else 0), I))
     hq_rows = np.zeros_like(dh_rows)
-    for e, (a, g, hq) in saved.items():
+    for e, (xq, a, g, hq, wv) in saved.items():
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         toks = perm[lo:hi] // k
         gx, dw1[e], dw3[e], dw2[e], dh_rows[lo:hi] = expert_backward_mxfp8(
-            xf[toks], a, g, hq, d_rows[lo:hi], *experts[e], quant=quant)
+            xq, a, g, hq, d_rows[lo:hi], *wv, quant=quant)
         hq_rows[lo:hi] = hq
         np.add.at(dx, toks, gx)
     d_shared = None
     if shared is not None:
-        gx, s1, s3, s2, dh_rows[T * k:] = expert_backward_mxfp8(xf, sa, sg, shq, dyf, *shared, quant=quant)
+        gx, s1, s3, s2, dh_rows[T * k:] = expert_backward_mxfp8(sxq, sa, sg, shq, dyf, *swv, quant=quant)
         hq_rows[T * k:] = shq
         dx += gx
         d_shared = (s1, s3, s2)

@@ -975,3 +975,27 @@ def test_mxfp8_backward_rounds_the_expert_output_gradient_to_bf16():
     assert np.array_equal(dh[rows], oracle.bf16_rne(raw))
     assert np.any(dh[rows] != raw)
     assert np.array_equal(dh[T * k:], dy)
+
+
+def test_mxfp8_backward_of_the_nvfp4_forward():
+    """With forward="nvfp4" the backward's forward is the pinned NVFP4 layer (same ids and
+    y, the same expert outputs), and the expert forward hands the MXFP8 backward (pinned
+    above) the x the NVFP4 forward multiplied: its per-row NVFP4 values."""
+    rng = np.random.default_rng(65)
+    T, d, I, E, k = 24, 64, 32, 4, 2
+    x = _bf16_values(rng, (T, d))
+    wg = rng.standard_normal((d, E)) / 6
+    b = rng.standard_normal(E) * 0.2
+    mk = lambda *sh: oracle.nvfp4_quantize(_bf16_values(rng, sh, 1 / np.sqrt(sh[-1])))  # noqa: E731
+    experts = [(mk(I, d), mk(I, d), mk(d, I)) for _ in range(E)]
+    sh = (mk(I, d), mk(I, d), mk(d, I))
+    dy = oracle.bf16_rne(rng.standard_normal((T, d)))
+    g = oracle.layer_backward_mxfp8(x, wg, b, experts, sh, k, dy, forward="nvfp4")
+    ref = oracle.layer_nvfp4(x, wg, b, experts, sh, k)
+    assert np.array_equal(g["ids"], ref["ids"])
+    assert np.max(np.abs(g["y"] - ref["y"])) <= 1e-12 * np.max(np.abs(ref["y"]))
+    xq, _, _, _, out, _ = oracle.expert_forward_nvfp4(x[:5], *experts[1])
+    assert np.array_equal(out, oracle.expert_ffn_nvfp4(x[:5], *experts[1]))
+    assert np.array_equal(xq, oracle.nvfp4_dequant(*oracle.nvfp4_quantize(np.asarray(x[:5], np.float32))))
+    for e in g["dw1"]:
+        assert g["dw1"][e].shape == (I, d) and g["dw2"][e].shape == (d, I)

@@ -96,10 +96,10 @@ def main():
         sys.exit(2)
     has_shared = inp["shared"] is not None
     bwd = args.backward
-    if bwd and wl.dtype not in ("bf16", "mxfp8"):
-        print("--backward runs the bf16 and MXFP8 workloads only", file=sys.stderr)
+    if bwd and wl.dtype not in ("bf16", "mxfp8", "nvfp4"):
+        print("--backward runs the bf16, MXFP8 and NVFP4 workloads only", file=sys.stderr)
         sys.exit(2)
-    mxb = bwd and wl.dtype == "mxfp8"
+    mxb = bwd and wl.dtype in ("mxfp8", "nvfp4")     # the backward in MXFP8
     ws = pg.BackwardWorkspace(T, d, E, k, I, dt) if bwd else pg.Workspace(T, d, E, k, I, dt)
     x, wg, bias = inp["x"], inp["w_gate"], inp["bias"]
     # NVFP4 banks run K-blocked (packed once here, outside the timed region); the oracle
@@ -123,15 +123,15 @@ def main():
         d_out = torch.empty(rows, d, dtype=odt, device=dev)
         d_weights = torch.empty(T, k, dtype=torch.float32, device=dev)
         dx_rows = torch.empty(rows, d, dtype=torch.float32, device=dev)
-        grads = {n: torch.empty(routed[n].shape, dtype=torch.float32, device=dev) for n in ("w1", "w3", "w2")}
-        sgrads = ({n: torch.empty(shared[n].shape, dtype=torch.float32, device=dev) for n in ("w1", "w3", "w2")}
+        gshape = lambda b, n: b[n].shape[:-1] + ((d if n != "w2" else I),)  # noqa: E731  (NVFP4: packed codes)
+        grads = {n: torch.empty(gshape(routed, n), dtype=torch.float32, device=dev) for n in ("w1", "w3", "w2")}
+        sgrads = ({n: torch.empty(gshape(shared, n), dtype=torch.float32, device=dev) for n in ("w1", "w3", "w2")}
                   if has_shared else None)
         dx = torch.empty(T, d, dtype=torch.float32, device=dev)
         pre = torch.empty(rows, 2 * I, dtype=torch.float32, device=dev)
         gate_grad = not (replay and filt is None and inp["weights_in"] is not None)
         if mxb:   # the weights requantised for the backward: once per weight version, untimed
-            tb_r = pg.moe_mxfp8_transpose_weights({n: routed[n] for n in ("w1", "w3", "w2", "w1_scale",
-                                                                            "w3_scale", "w2_scale")})
+            tb_r = pg.moe_mxfp8_transpose_weights(routed)
             tb_s = pg.moe_mxfp8_transpose_weights(shared) if has_shared else None
 
     def step(ev=None):
@@ -165,10 +165,13 @@ def main():
             ev[5].record()
         if not bwd:
             return
-        pg.moe_combine_backward(dy, out, row_of, weights, T, has_shared, dt, d_out=d_out, d_weights=d_weights)
+        pg.moe_combine_backward(dy, out, row_of, weights, T, has_shared, xdt, d_out=d_out, d_weights=d_weights)
         if ev is not None:
             ev[6].record()
-        if mxb:
+        if mxb and wl.dtype == "nvfp4":
+            pg.moe_expert_ffn_backward_nvfp4(x, routed, shared, tb_r, tb_s, offsets, perm, k, d_out, ws, pre,
+                                             dx_rows=dx_rows, grads=grads, shared_grads=sgrads)
+        elif mxb:
             pg.moe_expert_ffn_backward_mxfp8(x, inp["x_scale"], routed, shared, tb_r, tb_s, offsets, perm, k, d_out,
                                              ws, pre=pre, dx_rows=dx_rows, grads=grads, shared_grads=sgrads)
         else:
@@ -446,12 +449,13 @@ def cpu_baseline(inp, wl, ids, n_tok, log_tau=None, dy=None):
     if log_tau is not None:
         fid, fw, _, _ = oracle.route_replay_filtered(x, wg, bias, kw["ids_in"], log_tau)
         kw = {"ids_in": fid, "weights_in": fw}
-    if wl.dtype == "nvfp4":
+    if wl.dtype == "nvfp4" and dy is None:
         oracle.layer_nvfp4(x, wg, bias, experts, shared, wl.k, **kw)
     elif dy is None:
         oracle.layer(x, wg, bias, experts, shared, wl.k, **kw)
-    elif wl.dtype == "mxfp8":
-        oracle.layer_backward_mxfp8(x, wg, bias, experts, shared, wl.k, dy[rows].float().cpu().numpy(), **kw)
+    elif wl.dtype in ("mxfp8", "nvfp4"):
+        oracle.layer_backward_mxfp8(x, wg, bias, experts, shared, wl.k, dy[rows].float().cpu().numpy(),
+                                    forward=wl.dtype, **kw)
     else:
         oracle.layer_backward(x, wg, bias, experts, shared, wl.k, dy[rows].float().cpu().numpy(),
                               dense=False, **kw)

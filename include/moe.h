@@ -303,7 +303,8 @@ moe_status moe_combine(const void* out, int dtype, const int32_t* row_of, const 
 
 /* moe_expert_ffn_gate_up that also keeps the pre-activations for the backward pass:
  * pre out fp32 [T*k (+T)][2*inter], row j = (x W1, x W3) of dispatched row j, exactly the
- * values the SwiGLU epilogue uses (bf16 and MXFP8 layers; MOE_ERR_UNSUPPORTED otherwise).
+ * values the SwiGLU epilogue uses (bf16, MXFP8 and NVFP4 layers, for NVFP4 with both row
+ * scales applied; MOE_ERR_UNSUPPORTED for fp32).
  * Same results as moe_expert_ffn_gate_up; pass `pre` to moe_expert_ffn_backward (bf16) or
  * moe_expert_ffn_backward_mxfp8. */
 moe_status moe_expert_ffn_gate_up_save(const void* x, const uint8_t* x_scale, int dtype, int T, int d,
@@ -450,6 +451,34 @@ moe_status moe_expert_ffn_backward_mxfp8(const void* x, const uint8_t* x_scale, 
                                          float* dx_rows, const moe_grad_bank* routed_grads,
                                          const moe_grad_bank* shared_grads, void* ws,
                                          size_t ws_bytes, void* stream);
+
+/* The MXFP8 backward (moe_expert_ffn_backward_mxfp8) of a layer whose forward ran in
+ * NVFP4 (Composer 2 Technical Report, section 6.1 "Kernels": an NVFP4 forward paired with
+ * an MXFP8 backward).  The backward GEMMs take the forward's operands as the forward
+ * quantized them: the weights' NVFP4 values, x quantized per token and h per row to
+ * NVFP4 (recomputed from `pre` with the forward's arithmetic), each requantised to MXFP8
+ * along the backward GEMM's reduction.
+ *   x          the layer's bf16 activations [T][d]; routed, shared: the K-blocked NVFP4
+ *              banks the forward took; routed_t, shared_t: moe_nvfp4_transpose_weights.
+ *   pre        required: fp32 [T*k (+T)][2*inter] from moe_expert_ffn_gate_up_save with
+ *              MOE_NVFP4 (x W1, x W3 with both row scales applied).
+ * Other arguments and results as moe_expert_ffn_backward_mxfp8; ws sized by
+ * moe_backward_workspace_size(..., MOE_NVFP4).  MOE_ERR_UNSUPPORTED unless
+ * d % 256 == 0 and inter % 128 == 0. */
+moe_status moe_expert_ffn_backward_nvfp4(const void* x, int T, int d, int E, int k, int inter,
+                                         const moe_expert_bank* routed, const moe_expert_bank* shared,
+                                         const moe_mxfp8_tbank* routed_t,
+                                         const moe_mxfp8_tbank* shared_t, const int32_t* offsets,
+                                         const int32_t* perm, const float* pre, const void* d_out,
+                                         float* dx_rows, const moe_grad_bank* routed_grads,
+                                         const moe_grad_bank* shared_grads, void* ws,
+                                         size_t ws_bytes, void* stream);
+
+/* moe_mxfp8_transpose_weights for a K-blocked NVFP4 bank (moe_nvfp4_pack_weights):
+ * w2t and w13t as there, requantised to MXFP8 from the exact NVFP4 values (E2M1 x E4M3 x
+ * row scale).  Requires d % 256 == 0 and inter % 128 == 0. */
+moe_status moe_nvfp4_transpose_weights(const moe_expert_bank* bank, int n, int d, int inter,
+                                       const moe_mxfp8_tbank* out, void* stream);
 
 /* Backward of the routing and of the token gather.
  *   dx        out fp32 [T][d]: sum_r dx_rows[row_of[t,r]] (r ascending), plus

@@ -21,7 +21,7 @@ __all__ = [
     "layer_forward", "moe_backward_workspace_size", "moe_combine_backward", "moe_expert_ffn_backward",
     "moe_route_backward", "layer_backward", "moe_expert_ffn_backward_data",
     "moe_expert_ffn_backward_weights", "moe_expert_ffn_gate_up_save", "moe_mxfp8_transpose_weights",
-    "moe_expert_ffn_backward_mxfp8",
+    "moe_expert_ffn_backward_mxfp8", "moe_nvfp4_transpose_weights", "moe_expert_ffn_backward_nvfp4",
 ]
 
 MOE_F32, MOE_BF16, MOE_MXFP8, MOE_NVFP4 = 0, 1, 2, 3
@@ -86,6 +86,10 @@ def lib():
             "moe_dispatch": [P, I, I, I, P, P, P, P, SZ, P],
             "moe_dispatch_noalloc": [P, I, I, I, P, P, P, P, P],
             "moe_mxfp8_transpose_weights": [ctypes.POINTER(_Bank), I, I, I, ctypes.POINTER(_TBank), P],
+            "moe_nvfp4_transpose_weights": [ctypes.POINTER(_Bank), I, I, I, ctypes.POINTER(_TBank), P],
+            "moe_expert_ffn_backward_nvfp4": [P, I, I, I, I, I, ctypes.POINTER(_Bank), ctypes.POINTER(_Bank),
+                                              ctypes.POINTER(_TBank), ctypes.POINTER(_TBank), P, P, P, P, P,
+                                              ctypes.POINTER(_GradBank), ctypes.POINTER(_GradBank), P, SZ, P],
             "moe_expert_ffn_backward_mxfp8": [P, P, I, I, I, I, I, ctypes.POINTER(_Bank), ctypes.POINTER(_Bank),
                                               ctypes.POINTER(_TBank), ctypes.POINTER(_TBank), P, P, P, P, P,
                                               ctypes.POINTER(_GradBank), ctypes.POINTER(_GradBank), P, SZ, P],
@@ -401,7 +405,8 @@ def moe_expert_ffn_gate_up_save(x, routed: dict, shared, offsets, perm, k, ws: W
     rows = T * k + (T if shared is not None else 0)
     pre = torch.empty(rows, 2 * inter, dtype=torch.float32, device=x.device) if pre is None else pre
     rb, sb = _bank(routed), _bank(shared)
-    _ok(lib().moe_expert_ffn_gate_up_save(_ptr(x), _ptr(x_scale), _dtype_of(x), T, d, E, k, inter, ctypes.byref(rb),
+    _ok(lib().moe_expert_ffn_gate_up_save(_ptr(x), _ptr(x_scale), _ffn_dtype(x, routed), T, d, E, k, inter,
+                                          ctypes.byref(rb),
                                           ctypes.byref(sb) if sb is not None else None, _ptr(offsets),
                                           _ptr(perm), _ptr(pre), ws.ptr, ws.nbytes, _stream(x.device)),
         "moe_expert_ffn_gate_up_save")
@@ -492,8 +497,14 @@ def layer_backward(inp: dict, k: int, fwd: dict, dy, ws: Workspace, replay: bool
     dt = _dtype_of(x)
     has_shared = inp.get("shared") is not None
     d_out, d_weights = moe_combine_backward(dy, fwd["out"], fwd["row_of"], fwd["weights"], T, has_shared, dt)
-    routed = {n: inp.get(n) for n in ("w1", "w3", "w2", "w1_scale", "w3_scale", "w2_scale")}
-    if dt == MOE_MXFP8:   # the requantised weights: from the caller, else made here
+    routed = {n: inp.get(n) for n in ("w1", "w3", "w2") + _BANK_OPT}
+    if inp.get("w1_rscale") is not None:   # NVFP4 forward, MXFP8 backward
+        rt = inp.get("routed_t") or moe_mxfp8_transpose_weights(routed)
+        st = inp.get("shared_t") if inp.get("shared") is None or inp.get("shared_t") is not None else \
+            moe_mxfp8_transpose_weights(inp["shared"])
+        dx_rows, grads, sgrads = moe_expert_ffn_backward_nvfp4(x, routed, inp.get("shared"), rt, st, fwd["offsets"],
+                                                               fwd["perm"], k, d_out, ws, pre)
+    elif dt == MOE_MXFP8:   # the requantised weights: from the caller, else made here
         rt = inp.get("routed_t") or moe_mxfp8_transpose_weights(routed)
         st = inp.get("shared_t") if inp.get("shared") is None or inp.get("shared_t") is not None else \
             moe_mxfp8_transpose_weights(inp["shared"])
@@ -519,20 +530,22 @@ def layer_backward(inp: dict, k: int, fwd: dict, dy, ws: Workspace, replay: bool
 
 def moe_mxfp8_transpose_weights(bank: dict) -> dict:
     """The requantised weights of an MXFP8 bank (w1, w3 [n][I][d], w2 [n][d][I] with their
-    scales; a shared bank may drop the leading n) for the MXFP8 backward: w2t [n][I][d],
-    w13t [n][d][2I] and their scales."""
-    _check_dev(*(bank[n] for n in ("w1", "w3", "w2", "w1_scale", "w3_scale", "w2_scale")))
+    scales; a shared bank may drop the leading n), or of a K-blocked NVFP4 bank (with row
+    scales), for the MXFP8 backward: w2t [n][I][d], w13t [n][d][2I] and their scales."""
+    _check_dev(*(bank.get(n) for n in ("w1", "w3", "w2") + _BANK_OPT))
+    nv = bank.get("w1_rscale") is not None
     one = bank["w1"].dim() == 2
     w1 = bank["w1"].unsqueeze(0) if one else bank["w1"]
     n, inter, d = w1.shape
+    d = d * 2 if nv else d          # NVFP4: two codes per byte
     dev = w1.device
     out = {"w2t": torch.empty(n, inter, d, dtype=torch.uint8, device=dev),
            "w2t_scale": torch.empty(n, inter, d // 32, dtype=torch.uint8, device=dev),
            "w13t": torch.empty(n, d, 2 * inter, dtype=torch.uint8, device=dev),
            "w13t_scale": torch.empty(n, d, 2 * inter // 32, dtype=torch.uint8, device=dev)}
     tb = _TBank(*(out[k].data_ptr() for k in ("w2t", "w2t_scale", "w13t", "w13t_scale")))
-    _ok(lib().moe_mxfp8_transpose_weights(ctypes.byref(_bank(bank)), n, d, inter, ctypes.byref(tb),
-                                          _stream(dev)), "moe_mxfp8_transpose_weights")
+    fn = lib().moe_nvfp4_transpose_weights if nv else lib().moe_mxfp8_transpose_weights
+    _ok(fn(ctypes.byref(_bank(bank)), n, d, inter, ctypes.byref(tb), _stream(dev)), "moe_*_transpose_weights")
     return {k: (v[0] if one else v) for k, v in out.items()}
 
 
@@ -563,6 +576,31 @@ def moe_expert_ffn_backward_mxfp8(x, x_scale, routed: dict, shared, routed_t: di
                                             ref(st), _ptr(offsets), _ptr(perm), _ptr(pre), _ptr(d_out),
                                             _ptr(dx_rows), ref(rg), ref(sg), ws.ptr, ws.nbytes, _stream(x.device)),
         "moe_expert_ffn_backward_mxfp8")
+    return dx_rows, grads, shared_grads
+
+
+def moe_expert_ffn_backward_nvfp4(x, routed: dict, shared, routed_t: dict, shared_t, offsets, perm, k, d_out,
+                                  ws: Workspace, pre, dx_rows=None, grads=None, shared_grads=None):
+    """The MXFP8 backward of an NVFP4 layer (bf16 x, K-blocked NVFP4 banks, saved pre).
+    Returns (dx_rows, grads, shared grads or None)."""
+    _check_dev(x, offsets, perm, d_out, pre)
+    T, d = x.shape
+    E, inter = routed["w1"].shape[0], routed["w1"].shape[1]
+    rows = T * k + (T if shared is not None else 0)
+    dx_rows = torch.empty(rows, d, dtype=torch.float32, device=x.device) if dx_rows is None else dx_rows
+    gl = lambda b: {n: torch.empty(b[n].shape[:-1] + (d if n != "w2" else inter,), dtype=torch.float32,  # noqa: E731
+                                   device=x.device) for n in ("w1", "w3", "w2")}
+    grads = gl(routed) if grads is None else grads
+    if shared is not None and shared_grads is None:
+        shared_grads = gl(shared)
+    rb, sb = _bank(routed), _bank(shared)
+    rt, st = _tbank(routed_t), _tbank(shared_t)
+    rg, sg = _grads(grads), _grads(shared_grads)
+    ref = lambda v: ctypes.byref(v) if v is not None else None  # noqa: E731
+    _ok(lib().moe_expert_ffn_backward_nvfp4(_ptr(x), T, d, E, k, inter, ref(rb), ref(sb), ref(rt), ref(st),
+                                            _ptr(offsets), _ptr(perm), _ptr(pre), _ptr(d_out), _ptr(dx_rows),
+                                            ref(rg), ref(sg), ws.ptr, ws.nbytes, _stream(x.device)),
+        "moe_expert_ffn_backward_nvfp4")
     return dx_rows, grads, shared_grads
 
 

@@ -583,7 +583,9 @@ extern "C" moe_status moe_backward_workspace_size(int T, int d, int E, int k, in
       inter < 1 || !valid_layer_dtype(dtype))
     return MOE_ERR_INVALID_ARG;
   const size_t a = workspace_bytes(T, d, E, k, inter, dtype);
-  const size_t b = dtype == MOE_MXFP8 ? mxfp8_backward_ws_bytes(T, d, E, k, inter) : bwd_ws(T, d, E, k, inter).bytes;
+  const size_t b = dtype == MOE_MXFP8 || dtype == MOE_NVFP4
+                       ? mxfp8_backward_ws_bytes(T, d, E, k, inter, dtype == MOE_NVFP4)
+                       : bwd_ws(T, d, E, k, inter).bytes;
   *bytes = a > b ? a : b;
   return MOE_OK;
 }

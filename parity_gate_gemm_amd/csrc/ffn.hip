@@ -469,6 +469,7 @@ static moe_status run_gate_up(const void* x, const uint8_t* xs, int dtype, int T
     q.S = p.S;
     q.mt_bound = p.mt_bound;
     q.out = (uint16_t*)p.h;
+    q.out_pre = pre;
     q.flag = p.flag;
     return nvfp4_gemm(0, q, s);   // h (bf16) is quantized by the GEMM2 half
   }
@@ -749,7 +750,7 @@ extern "C" moe_status moe_expert_ffn_gate_up_save(const void* x, const uint8_t* 
                                                   void* stream) {
   moe_status st = check_ffn_shape(dtype, T, d, E, k, inter, routed, shared, ws, ws_bytes);
   if (st != MOE_OK) return st;
-  if (dtype != MOE_BF16 && dtype != MOE_MXFP8) return MOE_ERR_UNSUPPORTED;
+  if (dtype != MOE_BF16 && dtype != MOE_MXFP8 && dtype != MOE_NVFP4) return MOE_ERR_UNSUPPORTED;
   if ((dtype == MOE_MXFP8) != (x_scale != nullptr) || !offsets) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !perm || !pre || !aligned(x, 16) || !aligned(pre, 16)) return MOE_ERR_INVALID_ARG;

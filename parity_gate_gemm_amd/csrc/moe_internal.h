@@ -335,8 +335,12 @@ struct Nvfp4Gemm {
   int S;
   long long mt_bound;
   uint16_t* out;
+  float* out_pre;          // GEMM1 (optional): fp32 a | g [rows][2N] with the row scales applied
   int* flag;
 };
+// h = bf16(silu(a) g) of rows of fp32 pre-activations a | g [rows][2I], with the NVFP4
+// GEMM1's epilogue arithmetic (nvfp4.hip).
+moe_status nvfp4_h_from_pre(const float* pre, long long rows, int I, uint16_t* h, hipStream_t s);
 moe_status nvfp4_quantize_rows(const uint16_t* src, long long rows, int K, uint8_t* codes, uint8_t* bscale,
                                float* rscale, uint16_t* dec, hipStream_t s);
 moe_status nvfp4_gemm(int mode, const Nvfp4Gemm& q, hipStream_t s);
@@ -347,8 +351,8 @@ moe_status nvfp4_gemm(int mode, const Nvfp4Gemm& q, hipStream_t s);
 // with the forward's MFMA sequence (bf16 only).
 // Zero fill of n floats by a kernel (backward.hip).
 void zero_fill(float* p, long long n, hipStream_t s);
-// Workspace bytes of the MXFP8 backward (mxfp8_bwd.hip).
-size_t mxfp8_backward_ws_bytes(int T, int d, int E, int k, int inter);
+// Workspace bytes of the MXFP8 backward (mxfp8_bwd.hip) of an MXFP8 or an NVFP4 layer.
+size_t mxfp8_backward_ws_bytes(int T, int d, int E, int k, int inter, bool nvfp4_layer);
 // Segment table with tiles of tm rows (ffn_seg_table: tm = kGemmBM).
 moe_status ffn_seg_table_rows(const int32_t* offsets, int T, int E, int k, int has_shared, int tm, int* seg,
                               int* flag, hipStream_t s);

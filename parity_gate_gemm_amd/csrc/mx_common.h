@@ -136,6 +136,39 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   return (c & 0x80u) ? -v : v;
 }
 
+// Exact-input versions for values held in float64: the block scale of mx_block_scale and
+// the nearest-even E4M3 code of v / X (|v / X| <= 448 by that scale).
+__device__ __forceinline__ void mx_block_scale_f64(double amax, int& se, uint32_t& scode) {
+  if (amax == 0.0) {
+    se = -127;
+    scode = 0;
+  } else if (!(amax <= 3.0e38)) {
+    se = 0;
+    scode = 255;
+  } else {
+    int e = ilogb(amax) - 8;
+    if (ldexp(amax, -e) > 448.0) ++e;
+    se = min(max(e, -127), 127);
+    scode = (uint32_t)(se + 127);
+  }
+}
+__device__ __forceinline__ uint32_t e4m3_rne_f64(double v) {
+  const uint32_t sign = signbit(v) ? 0x80u : 0u;
+  const double a = fabs(v);
+  if (a != a) return 0x7Fu;
+  if (!(a < 448.0)) return sign | 0x7Eu;
+  if (a == 0.0) return sign;
+  int ee = ilogb(a);
+  if (ee < -6) ee = -6;                                  // subnormal grid below 2^-6
+  uint32_t m = (uint32_t)rint(ldexp(a, 3 - ee));         // steps of 2^(ee - 3), ties to even
+  if (ee == -6 && m < 8) return sign | m;                // subnormal (or zero)
+  if (m == 16) {
+    ++ee;
+    m = 8;
+  }
+  return sign | ((uint32_t)(ee + 7) << 3) | (m - 8);
+}
+
 }  // namespace moe
 
 #endif  // LIBMOE_MX_COMMON_H

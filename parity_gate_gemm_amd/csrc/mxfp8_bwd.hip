@@ -119,7 +119,8 @@ __global__ __launch_bounds__(256) void mx_rowq_kernel(const void* __restrict__ s
 enum { kColBf16 = 0, kColF32 = 1, kColMx = 2, kColPre = 3 };
 struct ColqArgs {
   const void* src;
-  const uint8_t* src_s;     // MXFP8 source scales, src_ld / 32 per row
+  const uint8_t* src_s;     // MXFP8 source scales, src_ld / 32 per row; NVFP4 block scales
+  const float* src_r;       // NVFP4 sources: fp32 scale per source row
   long long src_ld;         // elements per source row
   long long src_mat;        // matrix mode: elements between matrices
   int gather;               // segment mode: source row of dispatched row j = its token
@@ -246,6 +247,122 @@ __global__ __launch_bounds__(256) void mx_colq_kernel(ColqArgs a) {
   for (int i = 0; i < 8; ++i)
     w[i >> 2][i & 3] = mx_pack4(ldexpf(t[4 * i][threadIdx.x], -se), ldexpf(t[4 * i + 1][threadIdx.x], -se),
                                 ldexpf(t[4 * i + 2][threadIdx.x], -se), ldexpf(t[4 * i + 3][threadIdx.x], -se));
+  uint8_t* o = obase + (long long)c * a.out_ld + kout;
+  *(u32x4_t*)o = w[0];
+  *(u32x4_t*)(o + 16) = w[1];
+  osbase[(long long)c * (a.out_ld / 32) + kout / 32] = (uint8_t)scode;
+}
+
+// ---------------------------------------------------------------------------
+// Column quantiser for the operands of an NVFP4 layer (same blocks and outputs as
+// mx_colq_kernel), on values held exactly in float64: an NVFP4 value E2M1 x E4M3 x row
+// scale has up to 30 significant bits.
+//   kColNvDec (segment mode): decoded rows E2M1 x E4M3 in fp16 [rows][C] (the forward
+//             quantizer's output) times the fp32 scale of the source row, src_r[row];
+//   kColNvW (matrix mode): K-blocked NVFP4 weight matrices of R rows x C columns (codes
+//             [R/32][C/64][32][32 bytes], block scales [R/32][C/64][32][4 bytes]) with
+//             one fp32 scale per row.
+// ---------------------------------------------------------------------------
+enum { kColNvDec = 4, kColNvW = 5 };
+
+__device__ __forceinline__ double e2m1_f64(uint32_t c) {
+  const double m[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  const double v = m[c & 7u];
+  return (c & 8u) ? -v : v;
+}
+
+template <int KIND>
+__global__ __launch_bounds__(256) void mx_colq_nv_kernel(ColqArgs a) {
+  __shared__ double t[32][CQ_COLS + 1];
+  __shared__ long long srow[32];   // source row (over all matrices in matrix mode), -1: padding
+  const int q = blockIdx.x;
+  const int c0 = blockIdx.y * CQ_COLS;
+  int s, r0;
+  long long kout;
+  uint8_t* obase;
+  uint8_t* osbase;
+  if (a.kst) {
+    const int kq = 32 * q;
+    if (kq >= a.kst[a.S]) return;
+    int lo = 0, hi = a.S;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.kst[mid] <= kq) lo = mid; else hi = mid;
+    }
+    s = lo;
+    r0 = kq - a.kst[s];
+    kout = kq;
+    obase = a.out;
+    osbase = a.out_s;
+  } else {
+    const int per = a.R / 32;
+    s = q / per;
+    r0 = (q % per) * 32;
+    if (s >= a.S) return;
+    kout = a.col0 + r0;
+    obase = a.out + s * a.out_mat;
+    osbase = a.out_s + s * (a.out_mat / 32);
+  }
+  if (threadIdx.x < 32) {
+    const int r = r0 + threadIdx.x;
+    long long row = -1;
+    if (a.kst) {
+      if (r < a.rowcount[s]) {
+        const long long j = (long long)a.rowstart[s] + r;
+        row = j;
+        if (a.gather) {
+          row = j >= a.Tk ? j - a.Tk : (long long)(a.perm[j] / a.k);
+          if (row < 0 || row >= a.T) {
+            raise_flag(a.flag, kFlagCorrupt);
+            row = 0;
+          }
+        }
+      }
+    } else {
+      row = (long long)s * a.R + r;
+    }
+    srow[threadIdx.x] = row;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 32 * CQ_COLS; i += 256) {
+    const int rr = i / CQ_COLS, cc = i % CQ_COLS, c = c0 + cc;
+    const long long row = srow[rr];
+    double v = 0.0;
+    if (row >= 0 && c < a.C) {
+      if (KIND == kColNvDec) {
+        const uint16_t bits = ((const uint16_t*)a.src)[row * a.C + c];
+        v = (double)(float)__builtin_bit_cast(_Float16, bits) * (double)a.src_r[row];
+      } else {
+        const long long m = row / a.R;
+        const int r = (int)(row % a.R);
+        const long long tile = (long long)(r / 32) * (a.C / 64) + c / 64;
+        const uint8_t* codes = (const uint8_t*)a.src + m * ((long long)a.R * a.C / 2);
+        const uint8_t* sc = a.src_s + m * ((long long)a.R * a.C / 16);
+        const uint32_t byte = codes[tile * 1024 + (r % 32) * 32 + (c % 64) / 2];
+        const uint32_t code = (c & 1) ? (byte >> 4) : (byte & 15u);
+        const uint32_t scode = sc[tile * 128 + (r % 32) * 4 + (c % 64) / 16];
+        v = e2m1_f64(code) * (double)e4m3_to_f32(scode) * (double)a.src_r[row];
+      }
+    }
+    t[rr][cc] = v;
+  }
+  __syncthreads();
+  const int c = c0 + threadIdx.x;
+  if (c >= a.C) return;
+  double amax = 0.0;
+#pragma unroll 8
+  for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(t[i][threadIdx.x]));
+  int se;
+  uint32_t scode;
+  mx_block_scale_f64(amax, se, scode);
+  u32x4_t w[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t u = 0;
+#pragma unroll
+    for (int z = 0; z < 4; ++z) u |= e4m3_rne_f64(ldexp(t[4 * i + z][threadIdx.x], -se)) << (8 * z);
+    w[i >> 2][i & 3] = u;
+  }
   uint8_t* o = obase + (long long)c * a.out_ld + kout;
   *(u32x4_t*)o = w[0];
   *(u32x4_t*)(o + 16) = w[1];
@@ -491,7 +608,10 @@ static unsigned colq_blocks_y(int C) { return (unsigned)((C + CQ_COLS - 1) / CQ_
 template <int KIND>
 static void colq_launch(const ColqArgs& a, long long nq, hipStream_t s) {
   if (nq <= 0) return;
-  mx_colq_kernel<KIND><<<dim3((unsigned)nq, colq_blocks_y(a.C)), 256, 0, s>>>(a);
+  if constexpr (KIND == kColNvDec || KIND == kColNvW)
+    mx_colq_nv_kernel<KIND><<<dim3((unsigned)nq, colq_blocks_y(a.C)), 256, 0, s>>>(a);
+  else
+    mx_colq_kernel<KIND><<<dim3((unsigned)nq, colq_blocks_y(a.C)), 256, 0, s>>>(a);
 }
 
 static void rowq_launch(const void* src, bool bf16, long long R, int C, uint8_t* codes, uint8_t* scales,
@@ -507,10 +627,12 @@ static void rowq_launch(const void* src, bool bf16, long long R, int C, uint8_t*
 
 // Workspace of the MXFP8 backward (after the prefix the route backward shares).
 struct MxBwdWs {
-  size_t seg, fseg, kst, pre, dq, dqs, dadg, dgq, dgqs, dT, dTs, hT, hTs, gT, gTs, xT, xTs, bytes;
+  size_t seg, fseg, kst, pre, dq, dqs, dadg, dgq, dgqs, dT, dTs, hT, hTs, gT, gTs, xT, xTs;
+  size_t xc, xr, hb, hc, hr;   // NVFP4 layers: x and h as the forward quantized them
+  size_t bytes;
   long long rows, kp;
 };
-static MxBwdWs mxbwd_ws(int T, int d, int E, int k, int inter) {
+static MxBwdWs mxbwd_ws(int T, int d, int E, int k, int inter, bool nv) {
   const BwdWs B = bwd_ws(T, d, E, k, inter);
   MxBwdWs w;
   w.rows = (long long)T * k + T;
@@ -535,12 +657,20 @@ static MxBwdWs mxbwd_ws(int T, int d, int E, int k, int inter) {
   w.gTs = take((size_t)2 * inter * (KP / 32));
   w.xT = take((size_t)d * KP);
   w.xTs = take((size_t)d * (KP / 32));
+  w.xc = w.xr = w.hb = w.hc = w.hr = 0;
+  if (nv) {
+    w.xc = take((size_t)T * d * 2);
+    w.xr = take((size_t)T * sizeof(float));
+    w.hb = take(R * inter * 2);
+    w.hc = take(R * inter * 2);
+    w.hr = take(R * sizeof(float));
+  }
   w.bytes = o;
   return w;
 }
 
-size_t mxfp8_backward_ws_bytes(int T, int d, int E, int k, int inter) {
-  return mxbwd_ws(T, d, E, k, inter).bytes;
+size_t mxfp8_backward_ws_bytes(int T, int d, int E, int k, int inter, bool nvfp4_layer) {
+  return mxbwd_ws(T, d, E, k, inter, nvfp4_layer).bytes;
 }
 
 static bool tbank_ok(const moe_mxfp8_tbank* t) {
@@ -597,7 +727,10 @@ extern "C" moe_status moe_mxfp8_transpose_weights(const moe_expert_bank* bank, i
   return launch_status();
 }
 
-extern "C" moe_status moe_expert_ffn_backward_mxfp8(
+// The MXFP8 backward of the expert FFN of an MXFP8 layer (nv == false: MXFP8 x, pre
+// optional) or of an NVFP4 layer (nv == true: bf16 x, pre required; x and h enter the
+// weight gradients as the forward quantized them to NVFP4).
+static moe_status mx_backward(bool nv,
     const void* x, const uint8_t* x_scale, int T, int d, int E, int k, int inter,
     const moe_expert_bank* routed, const moe_expert_bank* shared, const moe_mxfp8_tbank* routed_t,
     const moe_mxfp8_tbank* shared_t, const int32_t* offsets, const int32_t* perm, const float* pre,
@@ -616,7 +749,7 @@ extern "C" moe_status moe_expert_ffn_backward_mxfp8(
     if (gb && (!gb->dw1 || !gb->dw3 || !gb->dw2 || !aligned(gb->dw1, 16) || !aligned(gb->dw3, 16) ||
                !aligned(gb->dw2, 16)))
       return MOE_ERR_INVALID_ARG;
-  const MxBwdWs L = mxbwd_ws(T, d, E, k, inter);
+  const MxBwdWs L = mxbwd_ws(T, d, E, k, inter, nv);
   if (ws_bytes < L.bytes) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
@@ -634,8 +767,8 @@ extern "C" moe_status moe_expert_ffn_backward_mxfp8(
     }
     return launch_status();
   }
-  if (!x || !x_scale || !offsets || !perm || !d_out || !dx_rows || !aligned(x, 16) || !aligned(d_out, 16) ||
-      !aligned(dx_rows, 16) || (pre && !aligned(pre, 16)))
+  if (!x || (nv ? x_scale != nullptr : !x_scale) || (nv && !pre) || !offsets || !perm || !d_out || !dx_rows ||
+      !aligned(x, 16) || !aligned(d_out, 16) || !aligned(dx_rows, 16) || (pre && !aligned(pre, 16)))
     return MOE_ERR_INVALID_ARG;
   if (!routed->w1 || !routed->w3 || !routed->w2 || !routed->w1_scale || !routed->w3_scale || !routed->w2_scale)
     return MOE_ERR_INVALID_ARG;
@@ -643,7 +776,7 @@ extern "C" moe_status moe_expert_ffn_backward_mxfp8(
   const long long rows = Tk + (shared ? T : 0);
   const int S = E + has_shared;
   float* prew = (float*)(w + L.pre);
-  if (!pre) {
+  if (!pre && !nv) {
     // the pre-activations, recomputed with the forward's GEMM1 (same MFMA sequence)
     int* fseg = (int*)(w + L.fseg);
     const int tm = mx_tile_rows(d, inter);
@@ -755,26 +888,49 @@ extern "C" moe_status moe_expert_ffn_backward_mxfp8(
   c.out = (uint8_t*)(w + L.dT);
   c.out_s = (uint8_t*)(w + L.dTs);
   colq_launch<kColBf16>(c, nq, s);
-  c.src = pre;                // hq rows (from a | g) -> hT [I][Kp]
-  c.src_ld = 2 * inter;
-  c.C = inter;
-  c.out = (uint8_t*)(w + L.hT);
-  c.out_s = (uint8_t*)(w + L.hTs);
-  colq_launch<kColPre>(c, nq, s);
+  if (nv) {                   // the forward's NVFP4 h: bf16(silu(a) g) quantized per row
+    uint16_t* hb = (uint16_t*)(w + L.hb);
+    if ((st = nvfp4_h_from_pre(pre, rows, inter, hb, s)) != MOE_OK) return st;
+    if ((st = nvfp4_quantize_rows(hb, rows, inter, nullptr, nullptr, (float*)(w + L.hr),
+                                  (uint16_t*)(w + L.hc), s)) != MOE_OK)
+      return st;
+    c.src = w + L.hc;         // hq rows -> hT [I][Kp]
+    c.src_r = (const float*)(w + L.hr);
+    c.C = inter;
+    c.out = (uint8_t*)(w + L.hT);
+    c.out_s = (uint8_t*)(w + L.hTs);
+    colq_launch<kColNvDec>(c, nq, s);
+  } else {
+    c.src = pre;              // hq rows (from a | g) -> hT [I][Kp]
+    c.src_ld = 2 * inter;
+    c.C = inter;
+    c.out = (uint8_t*)(w + L.hT);
+    c.out_s = (uint8_t*)(w + L.hTs);
+    colq_launch<kColPre>(c, nq, s);
+  }
   c.src = dadg;               // da | dg rows -> gT [2I][Kp]
   c.src_ld = 2 * inter;
   c.C = 2 * inter;
   c.out = (uint8_t*)(w + L.gT);
   c.out_s = (uint8_t*)(w + L.gTs);
   colq_launch<kColF32>(c, nq, s);
-  c.src = x;                  // the gathered tokens' x -> xT [d][Kp]
-  c.src_s = x_scale;
-  c.src_ld = d;
-  c.C = d;
+  c.C = d;                    // the gathered tokens' x -> xT [d][Kp]
   c.gather = 1;
   c.out = (uint8_t*)(w + L.xT);
   c.out_s = (uint8_t*)(w + L.xTs);
-  colq_launch<kColMx>(c, nq, s);
+  if (nv) {                   // x as the forward quantized it to NVFP4 (per token)
+    if ((st = nvfp4_quantize_rows((const uint16_t*)x, T, d, nullptr, nullptr, (float*)(w + L.xr),
+                                  (uint16_t*)(w + L.xc), s)) != MOE_OK)
+      return st;
+    c.src = w + L.xc;
+    c.src_r = (const float*)(w + L.xr);
+    colq_launch<kColNvDec>(c, nq, s);
+  } else {
+    c.src = x;
+    c.src_s = x_scale;
+    c.src_ld = d;
+    colq_launch<kColMx>(c, nq, s);
+  }
 
   MxBwdGemm q{};
   q.kst = kst;
@@ -815,5 +971,72 @@ extern "C" moe_status moe_expert_ffn_backward_mxfp8(
   grid = tile_grid((long long)S * q.MT * q.NT, 0);
   if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
   mx_bwd_gemm_kernel<MB_DW><<<(unsigned)grid, BB_THR, 0, s>>>(q);
+  return launch_status();
+}
+
+extern "C" moe_status moe_expert_ffn_backward_mxfp8(
+    const void* x, const uint8_t* x_scale, int T, int d, int E, int k, int inter,
+    const moe_expert_bank* routed, const moe_expert_bank* shared, const moe_mxfp8_tbank* routed_t,
+    const moe_mxfp8_tbank* shared_t, const int32_t* offsets, const int32_t* perm, const float* pre,
+    const void* d_out, float* dx_rows, const moe_grad_bank* routed_grads,
+    const moe_grad_bank* shared_grads, void* ws, size_t ws_bytes, void* stream) {
+  if (routed && (routed->w1_rscale || routed->w3_rscale || routed->w2_rscale)) return MOE_ERR_INVALID_ARG;
+  return mx_backward(false, x, x_scale, T, d, E, k, inter, routed, shared, routed_t, shared_t, offsets, perm,
+                     pre, d_out, dx_rows, routed_grads, shared_grads, ws, ws_bytes, stream);
+}
+
+extern "C" moe_status moe_expert_ffn_backward_nvfp4(
+    const void* x, int T, int d, int E, int k, int inter, const moe_expert_bank* routed,
+    const moe_expert_bank* shared, const moe_mxfp8_tbank* routed_t, const moe_mxfp8_tbank* shared_t,
+    const int32_t* offsets, const int32_t* perm, const float* pre, const void* d_out, float* dx_rows,
+    const moe_grad_bank* routed_grads, const moe_grad_bank* shared_grads, void* ws, size_t ws_bytes,
+    void* stream) {
+  if (d % 256 != 0) return MOE_ERR_UNSUPPORTED;
+  if (routed && (!routed->w1_rscale || !routed->w3_rscale || !routed->w2_rscale)) return MOE_ERR_INVALID_ARG;
+  return mx_backward(true, x, nullptr, T, d, E, k, inter, routed, shared, routed_t, shared_t, offsets, perm, pre,
+                     d_out, dx_rows, routed_grads, shared_grads, ws, ws_bytes, stream);
+}
+
+extern "C" moe_status moe_nvfp4_transpose_weights(const moe_expert_bank* bank, int n, int d, int inter,
+                                                  const moe_mxfp8_tbank* out, void* stream) {
+  if (!bank || !out || n < 0 || d < 1 || inter < 1) return MOE_ERR_INVALID_ARG;
+  if (d % 256 != 0 || inter % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!bank->w1 || !bank->w3 || !bank->w2 || !bank->w1_scale || !bank->w3_scale || !bank->w2_scale ||
+      !bank->w1_rscale || !bank->w3_rscale || !bank->w2_rscale || !tbank_ok(out))
+    return MOE_ERR_INVALID_ARG;
+  if (n == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  ColqArgs a{};
+  a.kst = nullptr;
+  a.S = n;
+  // W2 [n][d][I] (K-blocked along I) -> W2t [n][I][d], blocks along d
+  a.src = bank->w2;
+  a.src_s = bank->w2_scale;
+  a.src_r = bank->w2_rscale;
+  a.R = d;
+  a.C = inter;
+  a.out = out->w2t;
+  a.out_s = out->w2t_scale;
+  a.out_ld = d;
+  a.out_mat = (long long)inter * d;
+  a.col0 = 0;
+  colq_launch<kColNvW>(a, (long long)n * (d / 32), s);
+  // W1, W3 [n][I][d] (K-blocked along d) -> W13t [n][d][2I], blocks along I
+  a.R = inter;
+  a.C = d;
+  a.out = out->w13t;
+  a.out_s = out->w13t_scale;
+  a.out_ld = 2 * inter;
+  a.out_mat = (long long)d * 2 * inter;
+  a.src = bank->w1;
+  a.src_s = bank->w1_scale;
+  a.src_r = bank->w1_rscale;
+  a.col0 = 0;
+  colq_launch<kColNvW>(a, (long long)n * (inter / 32), s);
+  a.src = bank->w3;
+  a.src_s = bank->w3_scale;
+  a.src_r = bank->w3_rscale;
+  a.col0 = inter;
+  colq_launch<kColNvW>(a, (long long)n * (inter / 32), s);
   return launch_status();
 }

@@ -190,6 +190,7 @@ struct Fp4Args {
   const int* rowcount;
   int S;
   uint16_t* out;           // MODE 0: h [rows][N] bf16; MODE 1: out [rows][N] bf16
+  float* out_pre;          // MODE 0 (optional): a | g [rows][2N] for the backward pass
   int* flag;
 };
 
@@ -456,12 +457,28 @@ void grouped_gemm_fp4_kernel(Fp4Args g) {
       if (MODE == 0) {
         const float a = acc[mb][0][v] * as * cs[0], gg = acc[mb][1][v] * as * cs[1];
         o[0] = f32_to_bf16(fp4_silu(a) * gg);
+        if (g.out_pre) {   // pre-activations for the backward pass
+          float* pr = g.out_pre + ((long long)row0 + rl + i) * 2 * g.N + c0 + l32;
+          pr[0] = a;
+          pr[g.N] = gg;
+        }
       } else {
         o[0] = f32_to_bf16(acc[mb][0][v] * as * cs[0]);
         o[32] = f32_to_bf16(acc[mb][1][v] * as * cs[1]);
       }
     }
   }
+}
+
+// h = bf16(silu(a) g) from the saved pre-activations, the GEMM1 epilogue's arithmetic.
+__global__ __launch_bounds__(256) void nvfp4_h_from_pre_kernel(const float* __restrict__ pre, long long n,
+                                                               int I, uint16_t* __restrict__ h) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n) return;
+  const long long r = idx / I;
+  const int c = (int)(idx % I);
+  const float a = pre[r * 2 * I + c], gg = pre[r * 2 * I + I + c];
+  h[idx] = f32_to_bf16(fp4_silu(a) * gg);
 }
 
 // ---------------------------------------------------------------------------
@@ -497,6 +514,15 @@ moe_status nvfp4_quantize_rows(const uint16_t* src, long long rows, int K, uint8
   return launch_status();
 }
 
+moe_status nvfp4_h_from_pre(const float* pre, long long rows, int I, uint16_t* h, hipStream_t s) {
+  const long long n = rows * I;
+  if (n <= 0) return MOE_OK;
+  const long long blocks = (n + 255) / 256;
+  if (blocks > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+  nvfp4_h_from_pre_kernel<<<(unsigned)blocks, 256, 0, s>>>(pre, n, I, h);
+  return launch_status();
+}
+
 moe_status nvfp4_gemm(int mode, const Nvfp4Gemm& q, hipStream_t s) {
   Fp4Args g{};
   g.a = q.a;
@@ -525,6 +551,7 @@ moe_status nvfp4_gemm(int mode, const Nvfp4Gemm& q, hipStream_t s) {
   g.rowcount = q.rowcount;
   g.S = q.S;
   g.out = q.out;
+  g.out_pre = q.out_pre;
   g.flag = q.flag;
   // columns per tile: 8 wavefronts x 32 features (GEMM1) or x 64 columns (GEMM2)
   const int per = FP_NW * (mode == 0 ? 32 : 64);

@@ -38,7 +38,7 @@ def parse():
                     help="replay workloads: route with the plausibility filter at ln tau = LOG_TAU "
                          "(the replayed ids are filtered and the weights come from the gate)")
     ap.add_argument("--backward", action="store_true",
-                    help="bf16 and MXFP8 workloads: a step is the forward and the backward pass of the "
+                    help="bf16, MXFP8 and NVFP4 workloads: a step is the forward and the backward pass of the "
                          "layer (dL/dy drawn once, fp32 weight and gate gradients)")
     ap.add_argument("--cpu-sample", type=int, default=32,
                     help="tokens of the same batch the CPU oracle is timed on (0: skip)")

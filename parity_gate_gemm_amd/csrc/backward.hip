@@ -405,8 +405,7 @@ void bwd_gemm_kernel(BwdGemm g) {
           if (KIND == BK_DH) {
             const long long orow = (long long)row0 + r;
             const float a = g.pre[orow * 2 * g.I + col], gg = g.pre[orow * 2 * g.I + g.I + col];
-            const float den = 1.0f + expf(-a);   // silu(a) = a / den as in the forward
-            const float sg = 1.0f / den, sl = a / den;
+            const float sg = sigmoid_f32(a), sl = silu_f32(a);   // as in the forward
             g.dadg[orow * 2 * g.I + col] = f32_to_bf16(c * gg * (sg * (1.0f + a * (1.0f - sg))));
             g.dadg[orow * 2 * g.I + g.I + col] = f32_to_bf16(c * sl);
             g.h[orow * g.I + col] = f32_to_bf16(sl * gg);

@@ -275,7 +275,14 @@ inline long long tile_grid(long long bound, int chunk) {
   const long long g = chunk == 0 ? kXcds : (long long)kXcds * chunk;
   return (bound + g - 1) / g * g;
 }
-__device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + expf(-a)); }
+// sigmoid(a) = 1 / (1 + e^-a) from the hardware 2^x and reciprocal (each within about one
+// ulp), two instructions instead of the library's exp and IEEE division; silu(a) = a sigmoid(a).
+// Every kernel that forms silu (forward epilogues, the backward's recomputation of h and
+// its derivative) uses these two, so a backward sees the same h as its forward.
+__device__ __forceinline__ float sigmoid_f32(float a) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * -1.4426950408889634f));
+}
+__device__ __forceinline__ float silu_f32(float a) { return a * sigmoid_f32(a); }
 
 // MXFP8 expert FFN GEMMs (mxfp8.hip) over the segment table of the FFN: GEMM1 (mode 0:
 // x W1, x W3, SwiGLU, h requantised to MXFP8 per row) and GEMM2 (mode 1: h W2 -> bf16).

@@ -582,9 +582,9 @@ __global__ __launch_bounds__(BB_THR) void mx_bwd_gemm_kernel(MxBwdGemm g) {
           if (r < mrows) {
             const long long jr = (long long)row0 + r;
             const float av = g.pre[jr * 2 * g.I + col], gv = g.pre[jr * 2 * g.I + g.I + col];
-            const float sg = 1.0f / (1.0f + expf(-av));
+            const float sg = sigmoid_f32(av);
             const float da = c * gv * (sg * (1.0f + av * (1.0f - sg)));
-            const float dg = c * (av * sg);
+            const float dg = c * silu_f32(av);
             g.out[jr * g.ldo + col] = da;
             g.out[jr * g.ldo + g.I + col] = dg;
           }

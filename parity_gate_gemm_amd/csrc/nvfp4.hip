@@ -194,7 +194,6 @@ struct Fp4Args {
   int* flag;
 };
 
-__device__ __forceinline__ float fp4_silu(float a) { return a / (1.0f + expf(-a)); }
 
 __device__ __forceinline__ int fp4_swz(int r) { return (r ^ (r >> 3)) & 7; }
 
@@ -456,7 +455,7 @@ void grouped_gemm_fp4_kernel(Fp4Args g) {
       uint16_t* o = obase + (long long)i * g.N;
       if (MODE == 0) {
         const float a = acc[mb][0][v] * as * cs[0], gg = acc[mb][1][v] * as * cs[1];
-        o[0] = f32_to_bf16(fp4_silu(a) * gg);
+        o[0] = f32_to_bf16(silu_f32(a) * gg);
         if (g.out_pre) {   // pre-activations for the backward pass
           float* pr = g.out_pre + ((long long)row0 + rl + i) * 2 * g.N + c0 + l32;
           pr[0] = a;
@@ -478,7 +477,7 @@ __global__ __launch_bounds__(256) void nvfp4_h_from_pre_kernel(const float* __re
   const long long r = idx / I;
   const int c = (int)(idx % I);
   const float a = pre[r * 2 * I + c], gg = pre[r * 2 * I + I + c];
-  h[idx] = f32_to_bf16(fp4_silu(a) * gg);
+  h[idx] = f32_to_bf16(silu_f32(a) * gg);
 }
 
 // ---------------------------------------------------------------------------

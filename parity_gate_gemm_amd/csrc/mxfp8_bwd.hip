@@ -254,6 +254,126 @@ __global__ __launch_bounds__(256) void mx_colq_kernel(ColqArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Column quantiser for the dispatched-row operands (segment mode), 128 padded rows x 64
+// columns per workgroup: whole 16-byte source chunks per load, and the four 32-row
+// blocks of a column written by four neighbouring lanes as one 128-byte run of its
+// output row (plus one 4-byte store of their scales).  Every 32-row block is quantised
+// exactly as in mx_colq_kernel (same decode, scale rule and encoding), so both give the
+// same bytes; segments start at multiples of 128 padded rows, so a workgroup never
+// straddles two.
+// ---------------------------------------------------------------------------
+constexpr int C4_R = 128, C4_C = 64;
+
+template <int KIND>
+__global__ __launch_bounds__(256) void mx_colq4_kernel(ColqArgs a) {
+  __shared__ float t[C4_R][C4_C + 1];
+  __shared__ long long srow[C4_R];
+  const int kq = C4_R * blockIdx.x;
+  if (kq >= a.kst[a.S]) return;
+  const int c0 = blockIdx.y * C4_C;
+  int lo = 0, hi = a.S;   // kst[lo] <= kq < kst[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.kst[mid] <= kq) lo = mid; else hi = mid;
+  }
+  const int s = lo, r0 = kq - a.kst[s];
+  const int tid = threadIdx.x;
+  if (tid < C4_R) {
+    const int r = r0 + tid;
+    long long off = -1;
+    if (r < a.rowcount[s]) {
+      const long long j = (long long)a.rowstart[s] + r;
+      long long src = j;
+      if (a.gather) {
+        src = j >= a.Tk ? j - a.Tk : (long long)(a.perm[j] / a.k);
+        if (src < 0 || src >= a.T) {
+          raise_flag(a.flag, kFlagCorrupt);
+          src = 0;
+        }
+      }
+      off = src * a.src_ld;
+    }
+    srow[tid] = off;
+  }
+  __syncthreads();
+  // ---- loads: chunks of EPC elements (16 bytes of the source) ----
+  constexpr int EPC = KIND == kColBf16 ? 8 : KIND == kColMx ? 16 : 4;
+  constexpr int CPR = C4_C / EPC;   // chunks per row
+#pragma unroll 4
+  for (int i = tid; i < C4_R * CPR; i += 256) {
+    const int rr = i / CPR, cc = (i % CPR) * EPC, c = c0 + cc;
+    const long long off = srow[rr];
+    float v[EPC];
+#pragma unroll
+    for (int u = 0; u < EPC; ++u) v[u] = 0.0f;
+    if (off >= 0 && c < a.C) {
+      if (KIND == kColBf16) {
+        const u32x4_t q = *(const u32x4_t*)((const uint16_t*)a.src + off + c);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = bf16_to_f32((uint16_t)(q[u >> 1] >> (16 * (u & 1))));
+      } else if (KIND == kColF32) {
+        const float4 q = *(const float4*)((const float*)a.src + off + c);
+        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+      } else if (KIND == kColMx) {
+        const u32x4_t q = *(const u32x4_t*)((const uint8_t*)a.src + off + c);
+        const int sc = (int)a.src_s[off / 32 + c / 32];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = ldexpf(e4m3_to_f32((q[u >> 2] >> (8 * (u & 3))) & 0xffu), sc - 127);
+      } else {
+        const float4 qa = *(const float4*)((const float*)a.src + off + c);
+        const float4 qg = *(const float4*)((const float*)a.src + off + a.C + c);
+        v[0] = silu_f32(qa.x) * qg.x; v[1] = silu_f32(qa.y) * qg.y;
+        v[2] = silu_f32(qa.z) * qg.z; v[3] = silu_f32(qa.w) * qg.w;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < EPC; ++u) t[rr][cc + u] = v[u];
+  }
+  __syncthreads();
+  if (KIND == kColPre) {
+    // the forward's h: each row's 32-feature blocks quantised along the row
+    const int rr = tid >> 1, b = tid & 1;
+    float amax = 0.0f;
+#pragma unroll 8
+    for (int u = 0; u < 32; ++u) amax = fmaxf(amax, fabsf(t[rr][32 * b + u]));
+    int se;
+    uint32_t scode;
+    mx_block_scale(amax, se, scode);
+#pragma unroll 8
+    for (int u = 0; u < 32; u += 4) {
+      float* p = &t[rr][32 * b + u];
+      const uint32_t w = mx_pack4(ldexpf(p[0], -se), ldexpf(p[1], -se), ldexpf(p[2], -se), ldexpf(p[3], -se));
+#pragma unroll
+      for (int z = 0; z < 4; ++z) p[z] = ldexpf(e4m3_to_f32((w >> (8 * z)) & 0xffu), se);
+    }
+    __syncthreads();
+  }
+  // ---- lane (column cl, block g): rows 32 g .. 32 g + 31 of column c0 + cl ----
+  const int cl = tid >> 2, g = tid & 3, c = c0 + cl;
+  float amax = 0.0f;
+#pragma unroll 8
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(t[32 * g + i][cl]));
+  int se;
+  uint32_t scode;
+  mx_block_scale(amax, se, scode);
+  u32x4_t w[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 32 * g + 4 * i;
+    w[i >> 2][i & 3] = mx_pack4(ldexpf(t[r][cl], -se), ldexpf(t[r + 1][cl], -se), ldexpf(t[r + 2][cl], -se),
+                                ldexpf(t[r + 3][cl], -se));
+  }
+  // the four scale codes of the column, gathered on its first lane
+  const uint32_t s1 = __shfl_down(scode, 1), s2 = __shfl_down(scode, 2), s3 = __shfl_down(scode, 3);
+  if (c >= a.C) return;
+  uint8_t* o = a.out + (long long)c * a.out_ld + kq + 32 * g;
+  *(u32x4_t*)o = w[0];
+  *(u32x4_t*)(o + 16) = w[1];
+  if (g == 0)
+    *(uint32_t*)(a.out_s + (long long)c * (a.out_ld / 32) + kq / 32) = scode | (s1 << 8) | (s2 << 16) | (s3 << 24);
+}
+
+// ---------------------------------------------------------------------------
 // Column quantiser for the operands of an NVFP4 layer (same blocks and outputs as
 // mx_colq_kernel), on values held exactly in float64: an NVFP4 value E2M1 x E4M3 x row
 // scale has up to 30 significant bits.
@@ -608,10 +728,15 @@ static unsigned colq_blocks_y(int C) { return (unsigned)((C + CQ_COLS - 1) / CQ_
 template <int KIND>
 static void colq_launch(const ColqArgs& a, long long nq, hipStream_t s) {
   if (nq <= 0) return;
-  if constexpr (KIND == kColNvDec || KIND == kColNvW)
+  if constexpr (KIND == kColNvDec || KIND == kColNvW) {
     mx_colq_nv_kernel<KIND><<<dim3((unsigned)nq, colq_blocks_y(a.C)), 256, 0, s>>>(a);
-  else
+  } else if (a.kst && a.C % 16 == 0 && a.src_ld % 16 == 0 && nq % 4 == 0) {
+    // segment mode: 128-row workgroups (16-byte source chunks stay aligned and inside
+    // a row; the padded K is a multiple of 128)
+    mx_colq4_kernel<KIND><<<dim3((unsigned)(nq / 4), (unsigned)((a.C + C4_C - 1) / C4_C)), 256, 0, s>>>(a);
+  } else {
     mx_colq_kernel<KIND><<<dim3((unsigned)nq, colq_blocks_y(a.C)), 256, 0, s>>>(a);
+  }
 }
 
 static void rowq_launch(const void* src, bool bf16, long long R, int C, uint8_t* codes, uint8_t* scales,

@@ -65,6 +65,15 @@ inline int screen_parts(int T, int d, int E) {
   if (nz > 16) nz = 16;
   if (nz > steps / 4) nz = steps / 4;
   if (nz < 1) nz = 1;
+  // a split K: as many (expert tile, K part) slices as a multiple of the 8 XCDs where the
+  // limits allow (each XCD then runs whole slices, see gate_screen_kernel)
+  const int et = (E + 127) / 128;
+  if (nz > 1)
+    for (int z = nz; z <= 16 && z <= steps / 4; ++z)
+      if ((et * z) % 8 == 0 && (steps + (steps + z - 1) / z - 1) / ((steps + z - 1) / z) == z) {
+        nz = z;
+        break;
+      }
   const int spart = (steps + nz - 1) / nz;
   return (steps + spart - 1) / spart;
 }

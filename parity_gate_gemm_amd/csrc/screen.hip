@@ -120,7 +120,27 @@ __global__ __launch_bounds__(SC_THR) void gate_screen_kernel(const void* __restr
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int we = wave >> 2, wt = wave & 3;
-  const int e0 = blockIdx.x * SC_E, t0 = blockIdx.y * SC_T;
+  // workgroup -> (expert tile bx, token tile by, K part bz).  When the (expert tile, K
+  // part) slices are a multiple of the 8 XCDs, XCD b % 8 runs slices xcd, xcd + 8, ...
+  // one after another with all token tiles of a slice side by side: a slice's plane rows
+  // are then read from HBM once per XCD and shared through its L2.
+  const int ex = (E + SC_E - 1) / SC_E, ty = (T + SC_T - 1) / SC_T;
+  const int nslice = (int)(gridDim.x / ty);   // ex * parts
+  int bx, by, bz;
+  {
+    const int b = blockIdx.x;
+    if (nslice % kXcds == 0) {
+      const int q = b / kXcds, p = b % kXcds + kXcds * (q / ty);
+      by = q % ty;
+      bx = p % ex;
+      bz = p / ex;
+    } else {
+      bx = b % ex;
+      by = (b / ex) % ty;
+      bz = b / (ex * ty);
+    }
+  }
+  const int e0 = bx * SC_E, t0 = by * SC_T;
   const size_t plane = (size_t)E * d;
   const int nb32 = d / 32;
 
@@ -168,7 +188,7 @@ __global__ __launch_bounds__(SC_THR) void gate_screen_kernel(const void* __restr
       acc32[mb][v] = 0.0f;
       acc64[mb][v] = 0.0;
     }
-  const bool do_xn = blockIdx.x == 0 && we == 0;
+  const bool do_xn = bx == 0 && we == 0;
   double xsq = 0.0, csq = 0.0;    // csq: this chunk's sum of squared (unscaled) activations
   const int trow = wt * 32 + (lane & 31);
 
@@ -187,7 +207,7 @@ __global__ __launch_bounds__(SC_THR) void gate_screen_kernel(const void* __restr
     }
   };
 
-  const int st0 = blockIdx.z * spart;
+  const int st0 = bz * spart;
   const int nsteps = min(d / SC_K - st0, spart);
   gload(st0 * SC_K);
   for (int st = 0; st < nsteps; ++st) {
@@ -257,7 +277,7 @@ __global__ __launch_bounds__(SC_THR) void gate_screen_kernel(const void* __restr
   // outputs: accumulator element v is expert row 8 (v / 4) + 4 (lane / 32) + v % 4 of
   // the block, token column lane % 32
   const int t = t0 + trow;
-  double* sz = s + (size_t)blockIdx.z * T * E;
+  double* sz = s + (size_t)bz * T * E;
   if (t < T) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -269,7 +289,7 @@ __global__ __launch_bounds__(SC_THR) void gate_screen_kernel(const void* __restr
   }
   if (do_xn) {
     const double v = xsq + __shfl_xor(xsq, 32);
-    if (lane < 32 && t < T) xsqp[(size_t)blockIdx.z * T + t] = v;
+    if (lane < 32 && t < T) xsqp[(size_t)bz * T + t] = v;
   }
 }
 
@@ -1014,11 +1034,11 @@ moe_status screen_route_select(const void* x, const uint8_t* xs, int dtype, int 
   const int nz = screen_parts(T, d, E);
   const int spart = (nsteps + nz - 1) / nz;
   const dim3 grid((E + SC_E - 1) / SC_E, (T + SC_T - 1) / SC_T, (nsteps + spart - 1) / spart);
-  (void)tiles;
+  const unsigned nwg = (unsigned)tiles * grid.z;   // one-dimensional: see gate_screen_kernel
   if (dtype == MOE_BF16)
-    gate_screen_kernel<MOE_BF16><<<grid, SC_THR, 0, s>>>(x, xs, T, d, E, spart, S.planes, S.logits, S.xsq);
+    gate_screen_kernel<MOE_BF16><<<nwg, SC_THR, 0, s>>>(x, xs, T, d, E, spart, S.planes, S.logits, S.xsq);
   else
-    gate_screen_kernel<MOE_MXFP8><<<grid, SC_THR, 0, s>>>(x, xs, T, d, E, spart, S.planes, S.logits, S.xsq);
+    gate_screen_kernel<MOE_MXFP8><<<nwg, SC_THR, 0, s>>>(x, xs, T, d, E, spart, S.planes, S.logits, S.xsq);
   const int chunk = dtype == MOE_BF16 ? 64 : 32;
   const double tg = 2.0 * gamma_n(d + 1, 0x1p-53);
   const double cs = 2.0 * (gamma_n(3.0 * chunk, 0x1p-23) * (1.0 + 0x1p-6) + gamma_n(d + 1, 0x1p-53));

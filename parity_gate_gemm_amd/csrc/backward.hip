@@ -545,29 +545,58 @@ __global__ __launch_bounds__(1024) void route_bwd_dx_kernel(
 }
 
 // dWg[:, e] = sum over expert e's dispatched rows (token ascending) of dl x_t, db[e] the
-// sum of those dl; workgroup (column chunk of 256, expert e).
+// sum of those dl; workgroup (column chunk of 256, expert e).  The rows' tokens and dl
+// go through LDS in chunks of 256, so a thread's activation loads do not wait on each
+// other; each sum is one chain in ascending row order.
 __global__ __launch_bounds__(256) void route_bwd_wgate_kernel(
     const void* __restrict__ x, const uint8_t* __restrict__ xs, int dtype, int T, int d, int k, int E,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
     const float* __restrict__ dl, float* __restrict__ dwg, float* __restrict__ db, int* flag) {
+  __shared__ int stok[256];
+  __shared__ float sq[256];
   const int e = blockIdx.y, c = blockIdx.x * 256 + threadIdx.x;
   const long long Tk = (long long)T * k;
   long long lo = offsets[e], hi = offsets[e + 1];
   lo = lo < 0 ? 0 : (lo > Tk ? Tk : lo);
   hi = hi < lo ? lo : (hi > Tk ? Tk : hi);
+  const int cc = c < d ? c : 0;
   float acc = 0.0f, bacc = 0.0f;
-  int bad = 0;
-  for (long long n = lo; n < hi; ++n) {
-    long long p = perm[n];
-    if (p < 0 || p >= Tk) {
-      bad = 1;
-      p = 0;
+  for (long long base = lo; base < hi; base += 256) {
+    const int n = (int)(hi - base < 256 ? hi - base : 256);
+    if ((int)threadIdx.x < n) {
+      long long p = perm[base + threadIdx.x];
+      if (p < 0 || p >= Tk) {
+        raise_flag(flag, kFlagCorrupt);
+        p = 0;
+      }
+      stok[threadIdx.x] = (int)(p / k);
+      sq[threadIdx.x] = dl[p];
     }
-    const float q = dl[p];
-    if (c < d) acc = fmaf(q, (float)load_act_f64(x, xs, dtype, (size_t)(p / k), d, c), acc);
-    bacc += q;
+    __syncthreads();
+    if (dtype == MOE_MXFP8) {
+      // the E4M3 code decoded exactly by the hardware, times the block scale 2^(s - 127)
+      // (an fp32 value for every s < 255): one rounding of the exact product, the value
+      // load_act_f64 gives after its conversion to fp32
+#pragma unroll 8
+      for (int i = 0; i < n; ++i) {
+        const float q = sq[i];
+        const size_t row = (size_t)stok[i];
+        const int code = ((const uint8_t*)x)[row * d + cc];
+        const uint32_t se = xs[row * (size_t)(d / 32) + cc / 32];
+        const float sc = se == 0 ? 0x1p-127f : se == 255 ? __uint_as_float(0x7fc00000u) : __uint_as_float(se << 23);
+        acc = fmaf(q, __builtin_amdgcn_cvt_pk_f32_fp8(code, false)[0] * sc, acc);
+        bacc += q;
+      }
+    } else {
+#pragma unroll 8
+      for (int i = 0; i < n; ++i) {
+        const float q = sq[i];
+        acc = fmaf(q, (float)load_act_f64(x, xs, dtype, (size_t)stok[i], d, cc), acc);
+        bacc += q;
+      }
+    }
+    __syncthreads();
   }
-  if (bad && threadIdx.x == 0) raise_flag(flag, kFlagCorrupt);
   if (c < d) dwg[(size_t)c * E + e] = acc;
   if (db && blockIdx.x == 0 && threadIdx.x == 0) db[e] = bacc;
 }

@@ -299,7 +299,8 @@ def main():
         # the expert backward: MXFP8 GEMMs, bound by its HBM traffic (every expert's fp32
         # gradients dominate it)
         bdom = "ffn_backward"
-        dom_kernel = ("moe_expert_ffn_backward_mxfp8: mx_bwd_gemm_kernel<0..2> + MX quantisers (dh, dx; "
+        call = "moe_expert_ffn_backward_nvfp4" if wl.dtype == "nvfp4" else "moe_expert_ffn_backward_mxfp8"
+        dom_kernel = (f"{call}: mx_bwd_gemm_kernel<0..2> + MX quantisers (dh, dx; "
                       "dW2, dW1 | dW3 of every expert)")
     if bwd and not mxb:
         # the step's largest stage is one of the two backward halves; both stream HBM
@@ -358,17 +359,25 @@ def main():
     print(json.dumps(result))
 
 
+def _sources_sha(files):
+    """SHA-256 of the kernel's source files (the .hip file and the headers it includes),
+    concatenated in the listed order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, "parity_gate_gemm_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic(workload):
     """HBM bytes per GEMM1 launch from the committed rocprofv3 FETCH_SIZE + WRITE_SIZE
     summary (each scaled by the plain-copy calibration), or None when no summary exists
-    for this workload or the kernel source changed since the counters were taken."""
-    import hashlib
+    for this workload or the kernel's sources changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"gemm1_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = open(os.path.join(ROOT, "parity_gate_gemm_amd", "csrc", rec.get("kernel_source", "ffn.hip")), "rb").read()
-    if hashlib.sha256(src).hexdigest() != rec["ffn_source_sha256"]:
+    if "kernel_sources" not in rec or _sources_sha(rec["kernel_sources"]) != rec["sources_sha256"]:
         return None
     return rec["fetch_bytes"] + rec["write_bytes"]
 
@@ -377,13 +386,11 @@ def measured_mfma(workload):
     """Matrix-core counters of the grouped GEMMs from the committed rocprofv3 summary
     (SQ_VALU_MFMA_BUSY_CYCLES over the SIMD cycles, the implied clock, the counted
     matrix operations), or None when there is none or the kernel source changed."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"mfma_{workload}_counters.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = open(os.path.join(ROOT, "parity_gate_gemm_amd", "csrc", rec["kernel_source"]), "rb").read()
-    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+    if "kernel_sources" not in rec or _sources_sha(rec["kernel_sources"]) != rec["sources_sha256"]:
         return None
     return {k: {"mfma_busy": round(v["mfma_busy"], 4), "clock_ghz": round(v["clock_ghz"], 3),
                 "mfma_ops": v["ops"]} for k, v in rec["kernels"].items() if "grouped_gemm" in k}

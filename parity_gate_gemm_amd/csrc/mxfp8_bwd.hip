@@ -725,11 +725,90 @@ __global__ __launch_bounds__(BB_THR) void mx_bwd_gemm_kernel(MxBwdGemm g) {
 // ---------------------------------------------------------------------------
 static unsigned colq_blocks_y(int C) { return (unsigned)((C + CQ_COLS - 1) / CQ_COLS); }
 
+// mx_colq_nv_kernel<kColNvDec> in the layout of mx_colq4_kernel: 128 padded rows x 64
+// columns per workgroup, 16-byte loads of the decoded fp16 rows, the four 32-row blocks of
+// a column quantised (in float64, as mx_colq_nv_kernel) by four neighbouring lanes that
+// store one 128-byte run of the output row.  Same bytes as mx_colq_nv_kernel.
+__global__ __launch_bounds__(256) void mx_colq4_nv_kernel(ColqArgs a) {
+  __shared__ double t[C4_R][C4_C + 1];
+  __shared__ long long srow[C4_R];
+  const int kq = C4_R * blockIdx.x;
+  if (kq >= a.kst[a.S]) return;
+  const int c0 = blockIdx.y * C4_C;
+  int lo = 0, hi = a.S;   // kst[lo] <= kq < kst[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.kst[mid] <= kq) lo = mid; else hi = mid;
+  }
+  const int s = lo, r0 = kq - a.kst[s];
+  const int tid = threadIdx.x;
+  if (tid < C4_R) {
+    const int r = r0 + tid;
+    long long row = -1;
+    if (r < a.rowcount[s]) {
+      const long long j = (long long)a.rowstart[s] + r;
+      row = j;
+      if (a.gather) {
+        row = j >= a.Tk ? j - a.Tk : (long long)(a.perm[j] / a.k);
+        if (row < 0 || row >= a.T) {
+          raise_flag(a.flag, kFlagCorrupt);
+          row = 0;
+        }
+      }
+    }
+    srow[tid] = row;
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int i = tid; i < C4_R * (C4_C / 8); i += 256) {
+    const int rr = i / (C4_C / 8), cc = (i % (C4_C / 8)) * 8, c = c0 + cc;
+    const long long row = srow[rr];
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = 0.0;
+    if (row >= 0 && c < a.C) {
+      const u32x4_t q = *(const u32x4_t*)((const uint16_t*)a.src + row * a.C + c);
+      const double rs = (double)a.src_r[row];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = (double)(float)__builtin_bit_cast(_Float16, (uint16_t)(q[u >> 1] >> (16 * (u & 1)))) * rs;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[rr][cc + u] = v[u];
+  }
+  __syncthreads();
+  const int cl = tid >> 2, g = tid & 3, c = c0 + cl;
+  double amax = 0.0;
+#pragma unroll 8
+  for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(t[32 * g + i][cl]));
+  int se;
+  uint32_t scode;
+  mx_block_scale_f64(amax, se, scode);
+  u32x4_t w[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t u = 0;
+#pragma unroll
+    for (int z = 0; z < 4; ++z) u |= e4m3_rne_f64(ldexp(t[32 * g + 4 * i + z][cl], -se)) << (8 * z);
+    w[i >> 2][i & 3] = u;
+  }
+  const uint32_t s1 = __shfl_down(scode, 1), s2 = __shfl_down(scode, 2), s3 = __shfl_down(scode, 3);
+  if (c >= a.C) return;
+  uint8_t* o = a.out + (long long)c * a.out_ld + kq + 32 * g;
+  *(u32x4_t*)o = w[0];
+  *(u32x4_t*)(o + 16) = w[1];
+  if (g == 0)
+    *(uint32_t*)(a.out_s + (long long)c * (a.out_ld / 32) + kq / 32) = scode | (s1 << 8) | (s2 << 16) | (s3 << 24);
+}
+
 template <int KIND>
 static void colq_launch(const ColqArgs& a, long long nq, hipStream_t s) {
   if (nq <= 0) return;
   if constexpr (KIND == kColNvDec || KIND == kColNvW) {
-    mx_colq_nv_kernel<KIND><<<dim3((unsigned)nq, colq_blocks_y(a.C)), 256, 0, s>>>(a);
+    if (KIND == kColNvDec && a.kst && a.C % 16 == 0 && nq % 4 == 0)
+      mx_colq4_nv_kernel<<<dim3((unsigned)(nq / 4), (unsigned)((a.C + C4_C - 1) / C4_C)), 256, 0, s>>>(a);
+    else
+      mx_colq_nv_kernel<KIND><<<dim3((unsigned)nq, colq_blocks_y(a.C)), 256, 0, s>>>(a);
   } else if (a.kst && a.C % 16 == 0 && a.src_ld % 16 == 0 && nq % 4 == 0) {
     // segment mode: 128-row workgroups (16-byte source chunks stay aligned and inside
     // a row; the padded K is a multiple of 128)

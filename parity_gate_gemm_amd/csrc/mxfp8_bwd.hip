@@ -254,13 +254,13 @@ __global__ __launch_bounds__(256) void mx_colq_kernel(ColqArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Column quantiser for the dispatched-row operands (segment mode), 128 padded rows x 64
-// columns per workgroup: whole 16-byte source chunks per load, and the four 32-row
-// blocks of a column written by four neighbouring lanes as one 128-byte run of its
-// output row (plus one 4-byte store of their scales).  Every 32-row block is quantised
-// exactly as in mx_colq_kernel (same decode, scale rule and encoding), so both give the
-// same bytes; segments start at multiples of 128 padded rows, so a workgroup never
-// straddles two.
+// Column quantiser in 128-row blocks (segment mode: the dispatched-row operands; matrix
+// mode: the weights), 64 columns per workgroup: whole 16-byte source chunks per load,
+// and the four 32-row blocks of a column written by four neighbouring lanes as one
+// 128-byte run of its output row (plus one 4-byte store of their scales).  Every 32-row
+// block is quantised exactly as in mx_colq_kernel (same decode, scale rule and
+// encoding), so both give the same bytes; segments start at multiples of 128 padded
+// rows, so a workgroup never straddles two.
 // ---------------------------------------------------------------------------
 constexpr int C4_R = 128, C4_C = 64;
 
@@ -268,20 +268,40 @@ template <int KIND>
 __global__ __launch_bounds__(256) void mx_colq4_kernel(ColqArgs a) {
   __shared__ float t[C4_R][C4_C + 1];
   __shared__ long long srow[C4_R];
-  const int kq = C4_R * blockIdx.x;
-  if (kq >= a.kst[a.S]) return;
   const int c0 = blockIdx.y * C4_C;
-  int lo = 0, hi = a.S;   // kst[lo] <= kq < kst[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.kst[mid] <= kq) lo = mid; else hi = mid;
+  int s, r0;
+  long long kout;
+  uint8_t* obase;
+  uint8_t* osbase;
+  if (a.kst) {   // segment mode: padded K positions kout .. kout + 127 of one segment
+    const int kq = C4_R * blockIdx.x;
+    if (kq >= a.kst[a.S]) return;
+    int lo = 0, hi = a.S;   // kst[lo] <= kq < kst[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.kst[mid] <= kq) lo = mid; else hi = mid;
+    }
+    s = lo;
+    r0 = kq - a.kst[s];
+    kout = kq;
+    obase = a.out;
+    osbase = a.out_s;
+  } else {       // matrix mode: rows r0 .. r0 + 127 of matrix s
+    const int per = a.R / C4_R;
+    s = blockIdx.x / per;
+    r0 = (blockIdx.x % per) * C4_R;
+    if (s >= a.S) return;
+    kout = a.col0 + r0;
+    obase = a.out + s * a.out_mat;
+    osbase = a.out_s + s * (a.out_mat / 32);
   }
-  const int s = lo, r0 = kq - a.kst[s];
   const int tid = threadIdx.x;
   if (tid < C4_R) {
     const int r = r0 + tid;
     long long off = -1;
-    if (r < a.rowcount[s]) {
+    if (!a.kst) {
+      off = s * a.src_mat + (long long)r * a.src_ld;
+    } else if (r < a.rowcount[s]) {
       const long long j = (long long)a.rowstart[s] + r;
       long long src = j;
       if (a.gather) {
@@ -366,11 +386,11 @@ __global__ __launch_bounds__(256) void mx_colq4_kernel(ColqArgs a) {
   // the four scale codes of the column, gathered on its first lane
   const uint32_t s1 = __shfl_down(scode, 1), s2 = __shfl_down(scode, 2), s3 = __shfl_down(scode, 3);
   if (c >= a.C) return;
-  uint8_t* o = a.out + (long long)c * a.out_ld + kq + 32 * g;
+  uint8_t* o = obase + (long long)c * a.out_ld + kout + 32 * g;
   *(u32x4_t*)o = w[0];
   *(u32x4_t*)(o + 16) = w[1];
   if (g == 0)
-    *(uint32_t*)(a.out_s + (long long)c * (a.out_ld / 32) + kq / 32) = scode | (s1 << 8) | (s2 << 16) | (s3 << 24);
+    *(uint32_t*)(osbase + (long long)c * (a.out_ld / 32) + kout / 32) = scode | (s1 << 8) | (s2 << 16) | (s3 << 24);
 }
 
 // ---------------------------------------------------------------------------
@@ -809,9 +829,11 @@ static void colq_launch(const ColqArgs& a, long long nq, hipStream_t s) {
       mx_colq4_nv_kernel<<<dim3((unsigned)(nq / 4), (unsigned)((a.C + C4_C - 1) / C4_C)), 256, 0, s>>>(a);
     else
       mx_colq_nv_kernel<KIND><<<dim3((unsigned)nq, colq_blocks_y(a.C)), 256, 0, s>>>(a);
-  } else if (a.kst && a.C % 16 == 0 && a.src_ld % 16 == 0 && nq % 4 == 0) {
-    // segment mode: 128-row workgroups (16-byte source chunks stay aligned and inside
-    // a row; the padded K is a multiple of 128)
+  } else if (a.C % 16 == 0 && a.src_ld % 16 == 0 && nq % 4 == 0 &&
+             (a.kst || (a.R % C4_R == 0 && a.col0 % C4_R == 0 && a.out_ld % C4_R == 0 && a.src_mat % 16 == 0))) {
+    // 128-row workgroups: 16-byte source chunks stay aligned and inside a row, and the
+    // 128-row blocks (segments padded to 128 rows; whole matrices of R rows) stay inside
+    // one segment or matrix and start output runs and scale words on aligned offsets
     mx_colq4_kernel<KIND><<<dim3((unsigned)(nq / 4), (unsigned)((a.C + C4_C - 1) / C4_C)), 256, 0, s>>>(a);
   } else {
     mx_colq_kernel<KIND><<<dim3((unsigned)nq, colq_blocks_y(a.C)), 256, 0, s>>>(a);

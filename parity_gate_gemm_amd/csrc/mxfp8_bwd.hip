@@ -745,27 +745,50 @@ __global__ __launch_bounds__(BB_THR) void mx_bwd_gemm_kernel(MxBwdGemm g) {
 // ---------------------------------------------------------------------------
 static unsigned colq_blocks_y(int C) { return (unsigned)((C + CQ_COLS - 1) / CQ_COLS); }
 
-// mx_colq_nv_kernel<kColNvDec> in the layout of mx_colq4_kernel: 128 padded rows x 64
-// columns per workgroup, 16-byte loads of the decoded fp16 rows, the four 32-row blocks of
-// a column quantised (in float64, as mx_colq_nv_kernel) by four neighbouring lanes that
-// store one 128-byte run of the output row.  Same bytes as mx_colq_nv_kernel.
+// mx_colq_nv_kernel in the layout of mx_colq4_kernel: 128 rows x 64 columns per
+// workgroup, 16-byte loads (kColNvDec: 8 decoded fp16 values of a row; kColNvW: 32 codes
+// of a row of one K-blocked 32 x 64 block, with its two E4M3 block scales), the four
+// 32-row blocks of a column quantised in float64 (as mx_colq_nv_kernel) by four
+// neighbouring lanes that store one 128-byte run of the output row.  Same bytes as
+// mx_colq_nv_kernel.
+template <int KIND>
 __global__ __launch_bounds__(256) void mx_colq4_nv_kernel(ColqArgs a) {
   __shared__ double t[C4_R][C4_C + 1];
   __shared__ long long srow[C4_R];
-  const int kq = C4_R * blockIdx.x;
-  if (kq >= a.kst[a.S]) return;
   const int c0 = blockIdx.y * C4_C;
-  int lo = 0, hi = a.S;   // kst[lo] <= kq < kst[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.kst[mid] <= kq) lo = mid; else hi = mid;
+  int s, r0;
+  long long kout;
+  uint8_t* obase;
+  uint8_t* osbase;
+  if (a.kst) {   // segment mode
+    const int kq = C4_R * blockIdx.x;
+    if (kq >= a.kst[a.S]) return;
+    int lo = 0, hi = a.S;   // kst[lo] <= kq < kst[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.kst[mid] <= kq) lo = mid; else hi = mid;
+    }
+    s = lo;
+    r0 = kq - a.kst[s];
+    kout = kq;
+    obase = a.out;
+    osbase = a.out_s;
+  } else {       // matrix mode
+    const int per = a.R / C4_R;
+    s = blockIdx.x / per;
+    r0 = (blockIdx.x % per) * C4_R;
+    if (s >= a.S) return;
+    kout = a.col0 + r0;
+    obase = a.out + s * a.out_mat;
+    osbase = a.out_s + s * (a.out_mat / 32);
   }
-  const int s = lo, r0 = kq - a.kst[s];
   const int tid = threadIdx.x;
   if (tid < C4_R) {
     const int r = r0 + tid;
     long long row = -1;
-    if (r < a.rowcount[s]) {
+    if (!a.kst) {
+      row = (long long)s * a.R + r;
+    } else if (r < a.rowcount[s]) {
       const long long j = (long long)a.rowstart[s] + r;
       row = j;
       if (a.gather) {
@@ -779,22 +802,42 @@ __global__ __launch_bounds__(256) void mx_colq4_nv_kernel(ColqArgs a) {
     srow[tid] = row;
   }
   __syncthreads();
+  if (KIND == kColNvDec) {
 #pragma unroll 4
-  for (int i = tid; i < C4_R * (C4_C / 8); i += 256) {
-    const int rr = i / (C4_C / 8), cc = (i % (C4_C / 8)) * 8, c = c0 + cc;
-    const long long row = srow[rr];
-    double v[8];
+    for (int i = tid; i < C4_R * (C4_C / 8); i += 256) {
+      const int rr = i / (C4_C / 8), cc = (i % (C4_C / 8)) * 8, c = c0 + cc;
+      const long long row = srow[rr];
+      double v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = 0.0;
-    if (row >= 0 && c < a.C) {
-      const u32x4_t q = *(const u32x4_t*)((const uint16_t*)a.src + row * a.C + c);
-      const double rs = (double)a.src_r[row];
+      for (int u = 0; u < 8; ++u) v[u] = 0.0;
+      if (row >= 0 && c < a.C) {
+        const u32x4_t q = *(const u32x4_t*)((const uint16_t*)a.src + row * a.C + c);
+        const double rs = (double)a.src_r[row];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        v[u] = (double)(float)__builtin_bit_cast(_Float16, (uint16_t)(q[u >> 1] >> (16 * (u & 1)))) * rs;
+        for (int u = 0; u < 8; ++u)
+          v[u] = (double)(float)__builtin_bit_cast(_Float16, (uint16_t)(q[u >> 1] >> (16 * (u & 1)))) * rs;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[rr][cc + u] = v[u];
     }
+  } else {
+    // thread: row rr of the tile, codes of columns c0 + 32 h .. c0 + 32 h + 31
+    const int rr = tid >> 1, h = tid & 1;
+    const long long row = srow[rr];
+    const long long m = row / a.R;
+    const int r = (int)(row % a.R);
+    const long long tile = (long long)(r / 32) * (a.C / 64) + c0 / 64;
+    const uint8_t* codes = (const uint8_t*)a.src + m * ((long long)a.R * a.C / 2) + tile * 1024 + (r % 32) * 32 + 16 * h;
+    const uint8_t* sc = a.src_s + m * ((long long)a.R * a.C / 16) + tile * 128 + (r % 32) * 4 + 2 * h;
+    const u32x4_t q = *(const u32x4_t*)codes;
+    const double rs = (double)a.src_r[row];
+    const double s0 = (double)e4m3_to_f32(sc[0]) * rs, s1 = (double)e4m3_to_f32(sc[1]) * rs;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) t[rr][cc + u] = v[u];
+    for (int u = 0; u < 32; ++u) {
+      const uint32_t byte = (q[u >> 3] >> (8 * ((u >> 1) & 3))) & 0xffu;
+      const uint32_t code = (u & 1) ? (byte >> 4) : (byte & 15u);
+      t[rr][32 * h + u] = e2m1_f64(code) * (u < 16 ? s0 : s1);
+    }
   }
   __syncthreads();
   const int cl = tid >> 2, g = tid & 3, c = c0 + cl;
@@ -814,19 +857,21 @@ __global__ __launch_bounds__(256) void mx_colq4_nv_kernel(ColqArgs a) {
   }
   const uint32_t s1 = __shfl_down(scode, 1), s2 = __shfl_down(scode, 2), s3 = __shfl_down(scode, 3);
   if (c >= a.C) return;
-  uint8_t* o = a.out + (long long)c * a.out_ld + kq + 32 * g;
+  uint8_t* o = obase + (long long)c * a.out_ld + kout + 32 * g;
   *(u32x4_t*)o = w[0];
   *(u32x4_t*)(o + 16) = w[1];
   if (g == 0)
-    *(uint32_t*)(a.out_s + (long long)c * (a.out_ld / 32) + kq / 32) = scode | (s1 << 8) | (s2 << 16) | (s3 << 24);
+    *(uint32_t*)(osbase + (long long)c * (a.out_ld / 32) + kout / 32) = scode | (s1 << 8) | (s2 << 16) | (s3 << 24);
 }
 
 template <int KIND>
 static void colq_launch(const ColqArgs& a, long long nq, hipStream_t s) {
   if (nq <= 0) return;
   if constexpr (KIND == kColNvDec || KIND == kColNvW) {
-    if (KIND == kColNvDec && a.kst && a.C % 16 == 0 && nq % 4 == 0)
-      mx_colq4_nv_kernel<<<dim3((unsigned)(nq / 4), (unsigned)((a.C + C4_C - 1) / C4_C)), 256, 0, s>>>(a);
+    if (nq % 4 == 0 && a.C % 64 == 0 &&
+        (KIND == kColNvDec ? a.kst != nullptr
+                           : !a.kst && a.R % C4_R == 0 && a.col0 % C4_R == 0 && a.out_ld % C4_R == 0))
+      mx_colq4_nv_kernel<KIND><<<dim3((unsigned)(nq / 4), (unsigned)(a.C / C4_C)), 256, 0, s>>>(a);
     else
       mx_colq_nv_kernel<KIND><<<dim3((unsigned)nq, colq_blocks_y(a.C)), 256, 0, s>>>(a);
   } else if (a.C % 16 == 0 && a.src_ld % 16 == 0 && nq % 4 == 0 &&

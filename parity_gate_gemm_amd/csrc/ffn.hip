@@ -408,7 +408,7 @@ static FfnPlan plan_of(void* ws, int T, int d, int E, int k, int inter, int dtyp
   p.S = E + p.has_shared;
   p.Tk = (long long)T * k;
   p.rows = p.Tk + (has_shared ? T : 0);
-  p.tm = dtype == MOE_MXFP8 ? mx_tile_rows(d, inter) : BM;   // NVFP4: BM as bf16
+  p.tm = dtype == MOE_MXFP8 ? mx_tile_rows(d, inter, p.Tk, E) : BM;   // NVFP4: BM as bf16
   p.mt_bound = (p.Tk + (long long)E * (p.tm - 1)) / p.tm + (has_shared ? (T + p.tm - 1) / p.tm : 0);
   return p;
 }
@@ -500,6 +500,7 @@ static moe_status run_gate_up(const void* x, const uint8_t* xs, int dtype, int T
     g.out_scale = p.hs;
     g.out_pre = pre;
     g.flag = p.flag;
+    g.tm = p.tm;
     const moe_status st = mx_gemm(0, g, p.mt_bound, s);
     if (st != MOE_OK) return st;
   } else if (dtype == MOE_BF16) {
@@ -612,6 +613,7 @@ static moe_status run_down(int dtype, int T, int d, int E, int k, int inter,
     g.S = p.S;
     g.out = out;
     g.flag = p.flag;
+    g.tm = p.tm;
     const moe_status st = mx_gemm(1, g, p.mt_bound, s);
     if (st != MOE_OK) return st;
   } else if (dtype == MOE_BF16) {

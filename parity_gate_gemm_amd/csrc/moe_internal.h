@@ -318,10 +318,12 @@ struct MxArgs {
   uint8_t* out_scale;        // GEMM1: h scales [rows][I/32]
   float* out_pre;            // GEMM1 (mode 0, optional; mode 2): fp32 x W1 | x W3 [rows][2I]
   int* flag;
+  int tm;                    // rows per tile (mx_tile_rows), as counted by the segment table
 };
-// Rows per tile of the MXFP8 GEMMs for hidden size d and intermediate size inter (the
-// segment table counts tiles of this height).
-int mx_tile_rows(int d, int inter);
+// Rows per tile of the MXFP8 GEMMs for hidden size d, intermediate size inter and Tk
+// routed rows over E experts (the segment table counts tiles of this height).  Every
+// row's result is the same whatever the tile height.
+int mx_tile_rows(int d, int inter, long long Tk, int E);
 // Launch GEMM1 (mode 0; mode 2: only the pre-activations into out_pre) or GEMM2 (mode 1);
 // mt_bound bounds the segment table's row tiles.
 moe_status mx_gemm(int mode, MxArgs g, long long mt_bound, hipStream_t s);

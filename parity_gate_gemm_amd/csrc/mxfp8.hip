@@ -377,9 +377,12 @@ __device__ __forceinline__ void xr_pin(const f32x16_t (&acc)[4][2]) {
   asm volatile("" ::"a"(acc[0][0]), "a"(acc[0][1]), "a"(acc[1][0]), "a"(acc[1][1]), "a"(acc[2][0]),
                "a"(acc[2][1]), "a"(acc[3][0]), "a"(acc[3][1]));
 }
+__device__ __forceinline__ void xr_pin(const f32x16_t (&acc)[2][2]) {
+  asm volatile("" ::"a"(acc[0][0]), "a"(acc[0][1]), "a"(acc[1][0]), "a"(acc[1][1]));
+}
 
-template <int NB, int SEL>
-__device__ __forceinline__ void xr_mfma(const XrFrag<NB>& f, const XrScale<NB>& sc4, f32x16_t (&acc)[4][2]) {
+template <int NB, int SEL, int MB>
+__device__ __forceinline__ void xr_mfma(const XrFrag<NB>& f, const XrScale<NB>& sc4, f32x16_t (&acc)[MB][2]) {
 #pragma unroll
   for (int mb = 0; mb < NB; ++mb)
 #pragma unroll
@@ -647,6 +650,268 @@ __global__ __launch_bounds__(512) void grouped_gemm_mx_ring_kernel(MxArgs g) {
 }
 
 // ---------------------------------------------------------------------------
+// Ring kernel for short segments (few rows per expert, where the GEMMs stream the
+// weights from HBM): 128 x 256 tiles over a three-stage ring, so two K steps of weight
+// rows are in flight per workgroup, and half the activation rows of the 256-row tile.
+// Eight wavefronts (2 along M x 4 along N), each 2 row blocks x 2 B blocks of 32 x 32;
+// same fragment layout, swizzle, scale staging and per-output MFMA chain as
+// grouped_gemm_mx_ring_kernel (K ascending in 64-wide scaled MFMAs from zero), hence the
+// same bits for every row whatever the tile height.
+// ---------------------------------------------------------------------------
+constexpr int XS_M = 128;                        // tile rows
+constexpr int XS_ST = 3;                         // ring stages
+constexpr int XS_A = 0, XS_B = XS_M * XR_K;      // tile offsets within a stage
+constexpr int XS_STAGE = (XS_M + XR_N) * XR_K;   // 48 KB
+constexpr int XS_SC = XS_ST * XS_STAGE;          // two scale-group buffers after the stages
+constexpr int XS_SCB = (XS_M + XR_N) * 16;       // bytes per scale-group buffer (A rows, then B)
+constexpr int XS_LDS = XS_SC + 2 * XS_SCB;       // 156 KB
+constexpr int XS_EPI = 64 * XR_EPI_ROW;          // epilogue staging per wavefront (9 KB)
+static_assert(XS_LDS <= 160 * 1024 && 8 * XS_EPI <= XS_LDS, "LDS budget");
+
+// The K loop of a wavefront that multiplies NB of its 2 row blocks (NB = 0: it only loads
+// and synchronises).  Step j lives in stage j % 3.  At step j: wait for its data (loads
+// complete in issue order), meet (every wavefront is then done with step j - 1, whose
+// stage takes step j + 2's loads), multiply.  Scale group g (steps 4 g .. 4 g + 3) goes
+// out at step 4 (g - 1) into buffer g % 2.  Per step a wavefront issues 2 A loads and 4 B
+// loads; waves 0..3 each load the scale groups of 32 A rows, waves 4..7 of 64 B rows.
+template <int NB>
+__device__ __forceinline__ void xs_kloop(const uint8_t* ring, uint32_t ring_lds, int nsteps, const XrSrc& src,
+                                         int wave, int lane, uint32_t aof, uint32_t bof, uint32_t asf,
+                                         uint32_t bsf, int sh, f32x16_t (&acc)[2][2]) {
+  const uint32_t la = XS_A + wave * 2048, lb = XS_B + wave * 4096;
+  const uint32_t ls = wave < 4 ? wave * 512 : XS_M * 16 + (wave - 4) * 1024;
+  const int ngroups = nsteps / XR_GS;
+  auto issue = [&](int j) {
+    const uint32_t st = ring_lds + (uint32_t)(j % XS_ST) * XS_STAGE;
+    const int k0 = j * XR_K;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) xr_load16(st + la + 1024 * i, src.aoff[i], src.abase + k0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xr_load16(st + lb + 1024 * i, src.boff[i], src.bbase + k0);
+  };
+  auto issue_scales = [&](int grp) {
+    const uint32_t dst = ring_lds + XS_SC + (uint32_t)(grp & 1) * XS_SCB + ls;
+    if (wave < 4) {
+      if (lane < 32) xr_load16(dst, src.soff, src.sbase + 16 * grp);
+    } else {
+      xr_load16(dst, src.bsp + 16 * grp);
+    }
+  };
+  auto scales_at = [&](int j) { return j >= 0 && j % XR_GS == 0 && j / XR_GS + 1 < ngroups; };
+
+  issue_scales(0);
+  issue(0);
+  if (nsteps > 1) issue(1);
+  for (int j = 0; j < nsteps; ++j) {
+    // issued after step j's loads: step j + 1's (6), and the scale group issued at step
+    // j - 2 or j - 1 (at most one of them)
+    const bool nxt = j + 1 < nsteps;
+    const bool sc = scales_at(j - 1) || (j >= 2 && scales_at(j - 2));
+    if (nxt && sc)
+      xr_sync<7>();
+    else if (nxt)
+      xr_sync<6>();
+    else if (sc)
+      xr_sync<1>();
+    else
+      xr_sync<0>();
+    if (j + 2 < nsteps) issue(j + 2);
+    if (scales_at(j)) issue_scales(j / XR_GS + 1);
+    if constexpr (NB > 0) {
+      const uint8_t* st = ring + (j % XS_ST) * XS_STAGE;
+      const uint8_t* scb = ring + XS_SC + ((j / XR_GS) & 1) * XS_SCB;
+      XrScale<NB> sc4;
+      xr_read_scales<NB>(sc4, scb, asf, bsf, (j % XR_GS) * (XR_K / 32), sh);
+      XrFrag<NB> f;
+      xr_read<NB>(f, st, aof, bof, 0);
+      xr_mfma<NB, 0>(f, sc4, acc);
+      xr_read<NB>(f, st, aof, bof, 1);
+      xr_mfma<NB, 2>(f, sc4, acc);
+      xr_pin(acc);
+    }
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(512) void grouped_gemm_mx_ring128_kernel(MxArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[XS_LDS];
+
+  // ---- tile decode (as grouped_gemm_mx_ring_kernel, tiles of XS_M rows) ----
+  const int total = g.mstart[g.S] * g.NT;
+  int tile;
+  if (!xcd_tile<kMxXcdChunk>(total, tile)) return;
+  int lo = 0, hi = g.S;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (g.mstart[mid] * g.NT <= tile) lo = mid; else hi = mid;
+  }
+  const int s = lo;
+  const int mtiles = g.mstart[s + 1] - g.mstart[s];
+  const int local = tile - g.mstart[s] * g.NT;
+  const int grp = local / (kGroupM * g.NT), rem = local % (kGroupM * g.NT);
+  const int gm = min(kGroupM, mtiles - grp * kGroupM);
+  const int nt = rem / gm, mt = grp * kGroupM + rem % gm;
+  const int row0 = g.rowstart[s] + mt * XS_M;
+  const int mrows = min(XS_M, g.rowcount[s] - mt * XS_M);
+  constexpr bool G1 = MODE != 1;   // GEMM1 operands (modes 0 and 2)
+  const int n0 = nt * (G1 ? XR_N / 2 : XR_N);
+  const bool is_shared = (s == g.E);
+  const long long e = is_shared ? 0 : s;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int KB = g.K / 32;   // scale bytes per row
+
+  int bad = 0;
+  // source row of A tile row r (rows past the segment re-read the tile's first row)
+  auto a_src = [&](int r) -> long long {
+    const long long jr = (long long)row0 + (r < mrows ? r : 0);
+    if (!G1) return jr;
+    long long src = is_shared ? jr - g.Tk : (long long)(g.perm[jr] / g.k);
+    if (src < 0 || src >= g.T) {
+      bad = 1;
+      src = 0;
+    }
+    return src;
+  };
+  // row (within expert e's matrix) of staged B row r; GEMM1 alternates 32-row blocks of
+  // W1 and W3 for the same 32 features
+  auto b_row = [&](int r, const uint8_t*& bank, const uint8_t*& sbank) -> long long {
+    if (G1) {
+      const int blk = r >> 5;
+      const bool w3 = blk & 1;
+      bank = w3 ? (is_shared ? g.sb1 : g.b1) : (is_shared ? g.sb0 : g.b0);
+      sbank = w3 ? (is_shared ? g.sb1s : g.b1s) : (is_shared ? g.sb0s : g.b0s);
+      return (long long)n0 + (blk >> 1) * 32 + (r & 31);
+    }
+    bank = is_shared ? g.sb0 : g.b0;
+    sbank = is_shared ? g.sb0s : g.b0s;
+    return (long long)n0 + r;
+  };
+
+  // ---- loader: wavefront w fills A rows 16 w .. 16 w + 15 (two loads of 8 rows) and B
+  //      rows 32 w .. 32 w + 31 (four loads; one 32-row block, so one bank); lane l ->
+  //      row + l / 8, slot l % 8 <- chunk slot ^ swz(row).  Scale groups: A rows
+  //      32 w + l (w < 4, lanes < 32) or B rows 64 (w - 4) + l. ----
+  XrSrc src;
+  src.abase = g.a;
+  src.sbase = g.as;
+  {
+    const uint8_t *bank, *sbank;
+    b_row(32 * wave, bank, sbank);
+    src.bbase = bank + e * g.N * (long long)g.K;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 16 * wave + 8 * i + (lane >> 3);
+    const int chunk = (lane & 7) ^ xr_swz(r);
+    src.aoff[i] = (uint32_t)(a_src(r) * g.K + 16 * chunk);
+  }
+  src.aoff[2] = src.aoff[3] = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 32 * wave + 8 * i + (lane >> 3);
+    const int chunk = (lane & 7) ^ xr_swz(r);
+    const uint8_t *bank, *sbank;
+    const long long br = b_row(r, bank, sbank);
+    src.boff[i] = (uint32_t)(br * g.K + 16 * chunk);
+  }
+  src.soff = (uint32_t)(a_src(32 * (wave & 3) + (lane & 31)) * KB);
+  {
+    const uint8_t *bank, *sbank;   // GEMM1: W1 scales for lanes 0..31, W3 for 32..63
+    const long long br = b_row(64 * (wave & 3) + lane, bank, sbank);
+    src.bsp = sbank + (e * g.N + br) * (long long)KB;
+  }
+  if (bad) raise_flag(g.flag, kFlagCorrupt);
+
+  // ---- fragment offsets within a stage ----
+  const int j32 = lane & 31, hh = lane >> 5;
+  const int ra = 64 * wm + j32, rb = 64 * wn + j32;
+  const uint32_t aof = XS_A + ra * XR_K + 16 * (hh ^ xr_swz(ra));
+  const uint32_t bof = XS_B + rb * XR_K + 16 * (hh ^ xr_swz(rb));
+  const uint32_t asf = ra * 16, bsf = XS_M * 16 + rb * 16;   // within a scale buffer
+  const int sh = 8 * hh;
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_u8*)ring;
+  const int nsteps = g.K / XR_K;
+  const int nb_act = min(2, max(0, (mrows - wm * 64 + 31) >> 5));
+  switch (nb_act) {
+    case 2: xs_kloop<2>(ring, ring_lds, nsteps, src, wave, lane, aof, bof, asf, bsf, sh, acc); break;
+    case 1: xs_kloop<1>(ring, ring_lds, nsteps, src, wave, lane, aof, bof, asf, bsf, sh, acc); break;
+    default: xs_kloop<0>(ring, ring_lds, nsteps, src, wave, lane, aof, bof, asf, bsf, sh, acc); break;
+  }
+
+  // ---- epilogue (as grouped_gemm_mx_ring_kernel; the wavefront's local row 32 mb + i
+  //      is tile row 64 wm + 32 mb + i) ----
+  if (G1 && g.out_pre) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      if (mb >= nb_act) break;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 64 * wm + 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
+        if (r < mrows) {
+          const long long orow = (long long)row0 + r;
+          const int col = n0 + 32 * wn + j32;
+          g.out_pre[orow * 2 * g.N + col] = acc[mb][0][v];
+          g.out_pre[orow * 2 * g.N + g.N + col] = acc[mb][1][v];
+        }
+      }
+    }
+  }
+  if (MODE == 2) return;
+  __syncthreads();   // every wavefront is done reading the ring
+  uint8_t* stg = ring + wave * XS_EPI;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    if (mb >= nb_act) break;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int rl = 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
+      if (MODE == 0) {
+        *(float*)(stg + rl * XR_EPI_ROW + j32 * 4) = silu_f32(acc[mb][0][v]) * acc[mb][1][v];
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          *(uint16_t*)(stg + rl * XR_EPI_ROW + (32 * nb + j32) * 2) = f32_to_bf16(acc[mb][nb][v]);
+      }
+    }
+  }
+  if (MODE == 0) {
+    // lane l: local row l, one MX block (the wavefront's 32 features)
+    const int r = 64 * wm + lane;
+    if ((lane >> 5) < nb_act && r < mrows) {
+      const long long orow = (long long)row0 + r;
+      const int col = n0 + 32 * wn;
+      mx_store_block(stg + lane * XR_EPI_ROW, (uint8_t*)g.out + orow * g.N + col,
+                     g.out_scale + orow * (g.N / 32) + col / 32);
+    }
+  } else {
+    // lane l: local row 8 q + l / 8, 16-byte chunk l % 8 of the row's 64 outputs
+    const int c = lane & 7;
+#pragma unroll 4
+    for (int q2 = 0; q2 < 8; ++q2) {
+      const int rl = 8 * q2 + (lane >> 3);
+      const int r = 64 * wm + rl;
+      if ((rl >> 5) < nb_act && r < mrows) {
+        const u32x4_t t = *(const u32x4_t*)(stg + rl * XR_EPI_ROW + 16 * c);
+        __builtin_nontemporal_store(t, (u32x4_t*)((uint16_t*)g.out + ((long long)row0 + r) * g.N + n0 + wn * 64 + 8 * c));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 // Both GEMMs run on the ring kernel when it tiles the shape: GEMM2's output in XR_N
@@ -655,12 +920,19 @@ static bool mx_ring_ok(int d, int inter) {
   return MOE_MX_RING && d % XR_N == 0 && d % XR_GB == 0 && inter % XR_GB == 0;
 }
 
-int mx_tile_rows(int d, int inter) { return mx_ring_ok(d, inter) ? XR_M : 64 * MOE_MX_WM; }
+// The 128-row ring where the experts average at most 128 routed rows (the GEMMs stream
+// the weights; two K steps in flight), the 256-row ring above that (MFMA-bound).
+int mx_tile_rows(int d, int inter, long long Tk, int E) {
+  if (!mx_ring_ok(d, inter)) return 64 * MOE_MX_WM;
+  return Tk <= (long long)XS_M * E ? XS_M : XR_M;
+}
 
 moe_status mx_gemm(int mode, MxArgs g, long long mt_bound, hipStream_t s) {
   const bool g1 = mode != 1;
   const int d = g1 ? g.K : g.N, inter = g1 ? g.N : g.K;
   const bool ring = mx_ring_ok(d, inter);
+  // the kernel's tile height must be the one the segment table counted
+  if (ring ? (g.tm != XS_M && g.tm != XR_M) : g.tm != 64 * MOE_MX_WM) return MOE_ERR_INVALID_ARG;
   if (g1) {
     g.NT = ring ? inter / (XR_N / 2) : inter / (16 * MOE_MX_FN * MOE_MX_WN);
   } else {
@@ -672,7 +944,14 @@ moe_status mx_gemm(int mode, MxArgs g, long long mt_bound, hipStream_t s) {
   const long long grid = tile_grid(mt_bound * g.NT, ring ? kMxXcdChunk : 0);
   if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
   if (grid == 0) return MOE_OK;
-  if (ring) {
+  if (ring && g.tm == XS_M) {
+    if (mode == 0)
+      grouped_gemm_mx_ring128_kernel<0><<<(unsigned)grid, 512, 0, s>>>(g);
+    else if (mode == 2)
+      grouped_gemm_mx_ring128_kernel<2><<<(unsigned)grid, 512, 0, s>>>(g);
+    else
+      grouped_gemm_mx_ring128_kernel<1><<<(unsigned)grid, 512, 0, s>>>(g);
+  } else if (ring) {
     if (mode == 0)
       grouped_gemm_mx_ring_kernel<0><<<(unsigned)grid, 512, 0, s>>>(g);
     else if (mode == 2)

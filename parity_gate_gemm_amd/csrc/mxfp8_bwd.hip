@@ -1050,7 +1050,7 @@ static moe_status mx_backward(bool nv,
   if (!pre && !nv) {
     // the pre-activations, recomputed with the forward's GEMM1 (same MFMA sequence)
     int* fseg = (int*)(w + L.fseg);
-    const int tm = mx_tile_rows(d, inter);
+    const int tm = mx_tile_rows(d, inter, Tk, E);
     moe_status st = ffn_seg_table_rows(offsets, T, E, k, has_shared, tm, fseg, flag, s);
     if (st != MOE_OK) return st;
     MxArgs m{};
@@ -1077,6 +1077,7 @@ static moe_status mx_backward(bool nv,
     m.S = S;
     m.out_pre = prew;
     m.flag = flag;
+    m.tm = tm;
     const long long mtb = (Tk + (long long)E * (tm - 1)) / tm + (shared ? (T + tm - 1) / tm : 0);
     if ((st = mx_gemm(2, m, mtb, s)) != MOE_OK) return st;
     pre = prew;

@@ -319,6 +319,8 @@ struct MxArgs {
   float* out_pre;            // GEMM1 (mode 0, optional; mode 2): fp32 x W1 | x W3 [rows][2I]
   int* flag;
   int tm;                    // rows per tile (mx_tile_rows), as counted by the segment table
+  const float* pre_in;       // backward dh (mode 3): the forward's x W1 | x W3 [rows][2N]
+  float* out_f;              // backward: da | dg [rows][2N] (mode 3); dx rows [rows][N] (mode 4)
 };
 // Rows per tile of the MXFP8 GEMMs for hidden size d, intermediate size inter and Tk
 // routed rows over E experts (the segment table counts tiles of this height).  Every
@@ -327,6 +329,12 @@ int mx_tile_rows(int d, int inter, long long Tk, int E);
 // Launch GEMM1 (mode 0; mode 2: only the pre-activations into out_pre) or GEMM2 (mode 1);
 // mt_bound bounds the segment table's row tiles.
 moe_status mx_gemm(int mode, MxArgs g, long long mt_bound, hipStream_t s);
+// The MXFP8 backward's data GEMMs on the 128-row ring (A: row-quantised gradient rows;
+// B: the requantised weights, rows N x K per expert): mode 3 dh = dq W2t^T with the SwiGLU
+// backward at pre_in into out_f (da | dg), mode 4 dx rows = dgq W13t^T into out_f.
+// MOE_ERR_UNSUPPORTED where the ring does not tile d and inter (the caller then uses its
+// own kernel); the segment table must count 128-row tiles.
+moe_status mx_gemm_bwd_data(int mode, int d, int inter, MxArgs g, long long mt_bound, hipStream_t s);
 
 // NVFP4 expert FFN (nvfp4.hip).
 struct Nvfp4Gemm {

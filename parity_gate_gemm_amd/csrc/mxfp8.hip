@@ -753,7 +753,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_mx_ring128_kernel(MxArgs g) 
   const int nt = rem / gm, mt = grp * kGroupM + rem % gm;
   const int row0 = g.rowstart[s] + mt * XS_M;
   const int mrows = min(XS_M, g.rowcount[s] - mt * XS_M);
-  constexpr bool G1 = MODE != 1;   // GEMM1 operands (modes 0 and 2)
+  constexpr bool G1 = MODE == 0 || MODE == 2;   // GEMM1 operands (gathered x; W1 | W3)
   const int n0 = nt * (G1 ? XR_N / 2 : XR_N);
   const bool is_shared = (s == g.E);
   const long long e = is_shared ? 0 : s;
@@ -870,6 +870,34 @@ __global__ __launch_bounds__(512) void grouped_gemm_mx_ring128_kernel(MxArgs g) 
     }
   }
   if (MODE == 2) return;
+  if (MODE >= 3) {
+    // backward data GEMMs: fp32 rows straight from the accumulators (mode 3 with the
+    // SwiGLU backward at the saved pre-activations: da = dh g silu'(a), dg = dh silu(a))
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      if (mb >= nb_act) break;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 64 * wm + 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
+        if (r >= mrows) continue;
+        const long long jr = (long long)row0 + r;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const int col = n0 + 64 * wn + 32 * nb + j32;
+          const float c = acc[mb][nb][v];
+          if (MODE == 4) {
+            g.out_f[jr * g.N + col] = c;
+          } else {
+            const float av = g.pre_in[jr * 2 * g.N + col], gv = g.pre_in[jr * 2 * g.N + g.N + col];
+            const float sg = sigmoid_f32(av);
+            g.out_f[jr * 2 * g.N + col] = c * gv * (sg * (1.0f + av * (1.0f - sg)));
+            g.out_f[jr * 2 * g.N + g.N + col] = c * silu_f32(av);
+          }
+        }
+      }
+    }
+    return;
+  }
   __syncthreads();   // every wavefront is done reading the ring
   uint8_t* stg = ring + wave * XS_EPI;
 #pragma unroll
@@ -970,6 +998,19 @@ moe_status mx_gemm(int mode, MxArgs g, long long mt_bound, hipStream_t s) {
   } else {
     grouped_gemm_mx_kernel<1, MOE_MX_WM, 1, 2><<<(unsigned)grid, 64 * MOE_MX_WM, 0, s>>>(g);
   }
+  return MOE_OK;
+}
+
+moe_status mx_gemm_bwd_data(int mode, int d, int inter, MxArgs g, long long mt_bound, hipStream_t s) {
+  if ((mode != 3 && mode != 4) || !mx_ring_ok(d, inter)) return MOE_ERR_UNSUPPORTED;
+  g.NT = g.N / XR_N;
+  const long long grid = tile_grid(mt_bound * g.NT, kMxXcdChunk);
+  if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+  if (grid == 0) return MOE_OK;
+  if (mode == 3)
+    grouped_gemm_mx_ring128_kernel<3><<<(unsigned)grid, 512, 0, s>>>(g);
+  else
+    grouped_gemm_mx_ring128_kernel<4><<<(unsigned)grid, 512, 0, s>>>(g);
   return MOE_OK;
 }
 

@@ -1119,9 +1119,35 @@ static moe_status mx_backward(bool nv,
   g.pre = pre;
   g.out = dadg;
   g.ldo = 2 * inter;
-  long long grid = tile_grid(mt_bound * g.NT, 0);
-  if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
-  mx_bwd_gemm_kernel<MB_DH><<<(unsigned)grid, BB_THR, 0, s>>>(g);
+  // where the ring tiles the shape, both data GEMMs run on the forward's 128-row ring
+  // kernel (same MFMA chains, so the same bits as mx_bwd_gemm_kernel)
+  MxArgs r{};
+  r.E = E;
+  r.mstart = seg;
+  r.rowstart = seg + (E + 2);
+  r.rowcount = seg + 2 * (E + 2);
+  r.S = S;
+  r.flag = flag;
+  r.tm = BB_T;
+  r.a = dq;
+  r.as = dqs;
+  r.b0 = routed_t->w2t;
+  r.b0s = routed_t->w2t_scale;
+  r.sb0 = shared ? shared_t->w2t : nullptr;
+  r.sb0s = shared ? shared_t->w2t_scale : nullptr;
+  r.K = d;
+  r.N = inter;
+  r.pre_in = pre;
+  r.out_f = dadg;
+  long long grid = 0;
+  moe_status rst = mx_gemm_bwd_data(3, d, inter, r, mt_bound, s);
+  if (rst == MOE_ERR_UNSUPPORTED) {
+    grid = tile_grid(mt_bound * g.NT, 0);
+    if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+    mx_bwd_gemm_kernel<MB_DH><<<(unsigned)grid, BB_THR, 0, s>>>(g);
+  } else if (rst != MOE_OK) {
+    return rst;
+  }
   rowq_launch(dadg, false, rows, 2 * inter, dgq, dgqs, s);
   g.a = dgq;
   g.as = dgqs;
@@ -1136,9 +1162,24 @@ static moe_status mx_backward(bool nv,
   g.NT = d / BB_T;
   g.out = dx_rows;
   g.ldo = d;
-  grid = tile_grid(mt_bound * g.NT, 0);
-  if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
-  mx_bwd_gemm_kernel<MB_DX><<<(unsigned)grid, BB_THR, 0, s>>>(g);
+  r.a = dgq;
+  r.as = dgqs;
+  r.b0 = routed_t->w13t;
+  r.b0s = routed_t->w13t_scale;
+  r.sb0 = shared ? shared_t->w13t : nullptr;
+  r.sb0s = shared ? shared_t->w13t_scale : nullptr;
+  r.K = 2 * inter;
+  r.N = d;
+  r.pre_in = nullptr;
+  r.out_f = dx_rows;
+  rst = mx_gemm_bwd_data(4, d, inter, r, mt_bound, s);
+  if (rst == MOE_ERR_UNSUPPORTED) {
+    grid = tile_grid(mt_bound * g.NT, 0);
+    if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
+    mx_bwd_gemm_kernel<MB_DX><<<(unsigned)grid, BB_THR, 0, s>>>(g);
+  } else if (rst != MOE_OK) {
+    return rst;
+  }
 
   // ---- weights half: transposed operands quantised along the rows, then the GEMMs ----
   const long long nq = L.kp / 32;

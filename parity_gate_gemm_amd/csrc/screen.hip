@@ -361,24 +361,6 @@ __device__ double wave_dot(const void* __restrict__ x, const uint8_t* __restrict
   return acc;
 }
 
-// Adds the K parts of the screen (into part 0) and of the squared norms.
-__global__ __launch_bounds__(256) void screen_reduce_kernel(double* __restrict__ s,
-                                                            double* __restrict__ xsqp, int T, int E,
-                                                            int nz) {
-  const size_t n = (size_t)T * E;
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) {
-    double v = s[i];
-    for (int z = 1; z < nz; ++z) v += s[(size_t)z * n + i];
-    s[i] = v;
-  }
-  if (i < (size_t)T) {
-    double v = xsqp[i];
-    for (int z = 1; z < nz; ++z) v += xsqp[(size_t)z * T + i];
-    xsqp[i] = v;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Candidates, one wavefront per token: lower/upper screen bounds (bias added in
 // fp64), L = k-th largest lower bound, candidates = experts whose upper bound reaches
@@ -538,9 +520,11 @@ __global__ __launch_bounds__(PAIR_TOK) void pair_count_kernel(const int32_t* __r
 // (ceil(total / rf_p); cnt[3E+1] = all chunks).  cnt[0 .. E) keeps the totals.
 __global__ __launch_bounds__(1024) void pair_scan_kernel(int* __restrict__ pblk, int nblk,
                                                          int* __restrict__ cnt, int E, int rf_p) {
-  __shared__ int tot[kMaxExperts];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int run = 0;
+  static_assert(kMaxExperts <= 1024, "one expert per thread");
+  __shared__ int wsum[2][16];
+  const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
+  int run = 0;
+  if (e < E) {
     for (int b0 = 0; b0 < nblk; b0 += 8) {   // eight loads in flight per thread
       int v[8];
 #pragma unroll
@@ -551,20 +535,37 @@ __global__ __launch_bounds__(1024) void pair_scan_kernel(int* __restrict__ pblk,
         run += v[u];
       }
     }
-    tot[e] = run;
     cnt[e] = run;
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0, ch = 0;
-    for (int e = 0; e < E; ++e) {
-      cnt[E + e] = run;
-      cnt[2 * E + 1 + e] = ch;
-      run += tot[e];
-      ch += (tot[e] + rf_p - 1) / rf_p;
+  // exclusive prefixes over the experts of the totals and of the chunk counts: inclusive
+  // scans within each wavefront, then of the wavefront sums
+  const int tot = run, chn = e < E ? (run + rf_p - 1) / rf_p : 0;
+  int a = tot, c = chn;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int ua = __shfl_up(a, off), uc = __shfl_up(c, off);
+    if (lane >= off) {
+      a += ua;
+      c += uc;
     }
-    cnt[2 * E] = run;
-    cnt[3 * E + 1] = ch;
+  }
+  if (lane == 63) {
+    wsum[0][wave] = a;
+    wsum[1][wave] = c;
+  }
+  __syncthreads();
+  int ba = 0, bc = 0;
+  for (int w = 0; w < wave; ++w) {
+    ba += wsum[0][w];
+    bc += wsum[1][w];
+  }
+  if (e < E) {
+    cnt[E + e] = ba + a - tot;
+    cnt[2 * E + 1 + e] = bc + c - chn;
+  }
+  if (e == E - 1) {
+    cnt[2 * E] = ba + a;
+    cnt[3 * E + 1] = bc + c;
   }
 }
 
@@ -1043,13 +1044,10 @@ moe_status screen_route_select(const void* x, const uint8_t* xs, int dtype, int 
   const double tg = 2.0 * gamma_n(d + 1, 0x1p-53);
   const double cs = 2.0 * (gamma_n(3.0 * chunk, 0x1p-23) * (1.0 + 0x1p-6) + gamma_n(d + 1, 0x1p-53));
   const double ca = 2.0 * (4.0 * d + 64.0) * 0x1p-126;
+  // the candidates add the K parts themselves (ascending part order)
   const int nzl = (int)grid.z;
-  if (nzl > 1) {
-    const size_t n = (size_t)T * E;
-    screen_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(S.logits, S.xsq, T, E, nzl);
-  }
 #define MOE_CAND(NV)                                                                             \
-  screen_cand_kernel<NV><<<(T + 3) / 4, 256, 0, s>>>(S.logits, 1, S.xsq, S.xnorm, S.wnorm, bias,   \
+  screen_cand_kernel<NV><<<(T + 3) / 4, 256, 0, s>>>(S.logits, nzl, S.xsq, S.xnorm, S.wnorm, bias, \
                                                      xs, dtype, T, d, E, k, cs, tg, ca, S.cand,     \
                                                      S.ccount, S.tok_flag, ids, flag)
   if (E <= 128) MOE_CAND(2);

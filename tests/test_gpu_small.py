@@ -69,9 +69,12 @@ SMALL = [
     (200, 128, 128, 16, 4, True, True, "mxfp8"),
     (300, 256, 256, 4, 2, True, False, "mxfp8"),   # 150 rows/expert: 2 row tiles, ragged
     (1, 128, 128, 384, 8, False, True, "mxfp8"),
-    # d and I multiples of 512: the MXFP8 GEMMs run on the 256-row LDS-ring tiles
+    # d and I multiples of 512: the MXFP8 GEMMs run on the LDS-ring tiles, 256 rows where the
+    # experts average more than 128 routed rows, else 128 rows over three stages
     (700, 1024, 512, 16, 4, True, True, "mxfp8"),   # 175 rows/expert (1 ragged tile); shared 3 tiles
     (1500, 512, 512, 4, 2, False, False, "mxfp8"),  # 750 rows/expert: 3 row tiles, ragged
+    (300, 512, 512, 8, 2, True, True, "mxfp8"),     # 128-row tiles: 75 rows/expert, skewed by the bias
+    (100, 1024, 512, 32, 4, False, False, "mxfp8"), # 128-row tiles: ~12 rows/expert, one partial tile
     (50, 64, 32, 16, 3, True, True, "f32"),
     (5, 96, 40, 1024, 32, True, False, "f32"),     # largest E and k
 ]

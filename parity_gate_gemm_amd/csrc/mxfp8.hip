@@ -619,21 +619,23 @@ __global__ __launch_bounds__(512) void grouped_gemm_mx_ring_kernel(MxArgs g) {
       }
     }
   }
-  // (a wavefront reads back only what it wrote: its LDS accesses complete in order)
   if (MODE == 0) {
-    // lane l: local rows l and 64 + l, one MX block (the wavefront's 32 features) each
+    // thread i: tile row (i + 512 q) / 4, MX block (i % 4: wavefront column wn's 32
+    // features), staged by wavefront (row / 128, i % 4); four neighbouring lanes write a
+    // row's 128 code bytes and its 4 scale bytes contiguously
+    __syncthreads();
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
-      const int rl = 64 * q2 + lane;
-      const int r = 128 * wm + rl;
-      if ((rl >> 5) < nb_act && r < mrows) {
+      const int idx = tid + 512 * q2, r = idx >> 2, b = idx & 3;
+      if (r < mrows) {
         const long long orow = (long long)row0 + r;
-        const int col = n0 + 32 * wn;
-        mx_store_block(stg + rl * XR_EPI_ROW, (uint8_t*)g.out + orow * g.N + col,
-                       g.out_scale + orow * (g.N / 32) + col / 32);
+        const int col = n0 + 32 * b;
+        mx_store_block(ring + ((r >> 7) * 4 + b) * XR_EPI + (r & 127) * XR_EPI_ROW,
+                       (uint8_t*)g.out + orow * g.N + col, g.out_scale + orow * (g.N / 32) + col / 32);
       }
     }
   } else {
+    // (a wavefront reads back only what it wrote: its LDS accesses complete in order)
     // lane l: local row 8 q + l / 8, 16-byte chunk l % 8 of the row's 64 outputs
     const int c = lane & 7;
 #pragma unroll 4
@@ -916,13 +918,14 @@ __global__ __launch_bounds__(512) void grouped_gemm_mx_ring128_kernel(MxArgs g) 
     }
   }
   if (MODE == 0) {
-    // lane l: local row l, one MX block (the wavefront's 32 features)
-    const int r = 64 * wm + lane;
-    if ((lane >> 5) < nb_act && r < mrows) {
+    // thread i: tile row i / 4, MX block i % 4, staged by wavefront (row / 64, i % 4)
+    __syncthreads();
+    const int r = tid >> 2, b = tid & 3;
+    if (r < mrows) {
       const long long orow = (long long)row0 + r;
-      const int col = n0 + 32 * wn;
-      mx_store_block(stg + lane * XR_EPI_ROW, (uint8_t*)g.out + orow * g.N + col,
-                     g.out_scale + orow * (g.N / 32) + col / 32);
+      const int col = n0 + 32 * b;
+      mx_store_block(ring + ((r >> 6) * 4 + b) * XS_EPI + (r & 63) * XR_EPI_ROW,
+                     (uint8_t*)g.out + orow * g.N + col, g.out_scale + orow * (g.N / 32) + col / 32);
     }
   } else {
     // lane l: local row 8 q + l / 8, 16-byte chunk l % 8 of the row's 64 outputs

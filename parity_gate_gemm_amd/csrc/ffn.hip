@@ -24,10 +24,8 @@ constexpr int LDSS = BK + 8;  // LDS row stride in bf16 elements (144 B: conflic
 
 // Widest tile (wavefronts along N) each bf16 GEMM uses where the shape divides; the
 // narrower tiles give the same bits (each output is the same MFMA sequence over K).
-// GEMM2 takes 512 output columns per tile (16 wavefronts, one workgroup per CU): the row
-// tile's activations are then read once per 512 columns.
 constexpr int kGemm1Wn = 4;
-constexpr int kGemm2Wn = 8;
+constexpr int kGemm2Wn = 4;
 
 
 // Segment table: segment s < E is routed expert s (rows offsets[s]..offsets[s+1]-1),
@@ -425,9 +423,7 @@ static int bf16_wn(int n, int per_wave, int max_wn) {
 
 template <int MODE>
 static void launch_bf16(int wn, unsigned grid, hipStream_t s, const GemmArgs& g) {
-  if (wn == 8)
-    grouped_gemm_bf16_kernel<MODE, 8><<<grid, 1024, 0, s>>>(g);
-  else if (wn == 4)
+  if (wn == 4)
     grouped_gemm_bf16_kernel<MODE, 4><<<grid, 512, 0, s>>>(g);
   else
     grouped_gemm_bf16_kernel<MODE, 2><<<grid, 256, 0, s>>>(g);

@@ -124,15 +124,21 @@ __global__ __launch_bounds__(1024) void combine_bwd_kernel(const void* __restric
 //   DX   : C[n][j] = sum_i dadg[n][i] W13[e][i][j]     rows x d,  K = 2I  (W13 = W1 then W3)
 //   DW2  : C[j][i] = sum_n d_out[n][j] h[n][i]         d x I,     K = the segment's rows
 //   DW13 : C[i][j] = sum_n dadg[n][i] x[tok(n)][j]     2I x d,    K = the segment's rows
-// Tile 128 x 128, 4 wavefronts of 64 x 64 (2 x 2 MFMA 32x32x16 blocks), K steps of 64
-// through LDS rows of 64 K-values (144-byte stride).  An operand stored with K as its
-// row index ("K-major": the weight operands of DH and DX, both operands of the weight
-// gradients) is read as 4 K-rows x 8 columns per thread and transposed in registers
-// before the 8-byte LDS writes; K-rows past a segment's end read as zero.
+// Tiles of 128 rows x 64 NWN columns, 2 x NWN wavefronts of 64 x 64 (2 x 2 MFMA 32x32x16
+// blocks), K steps of 64 through LDS.  The weight-gradient kinds use NWN = 2 (128 x 128);
+// the data kinds NWN = 4 (128 x 256, two workgroups per CU) where the output width is a
+// multiple of 256, else NWN = 2.  A row operand (A of DH and DX) sits in LDS rows of 64
+// K-values (144-byte stride).  An operand stored with K as its row index ("K-major": the
+// weight operands of DH and DX, both operands of the weight gradients) is loaded as whole
+// row pieces, 4 K-rows per thread, stored to LDS as it is and read transposed (k_frag);
+// K-rows past a segment's end read as zero.  The tile width changes which workgroup
+// computes an output, not its MFMA sequence, so both widths give the same bits.
 // ---------------------------------------------------------------------------
-constexpr int GB_T = 128, GB_K = 64, GB_S = GB_K + 8, GB_THR = 256;
-constexpr int GB_KS = GB_T + 8;   // K-major weight tile of the data kinds: row pitch (elements)
-static_assert(GB_K * GB_KS <= GB_T * GB_S, "the K-major tile fits in sB");
+constexpr int GB_T = 128, GB_K = 64, GB_S = GB_K + 8;
+// K-major tile of 64 NWN columns: row pitch (elements); threads per workgroup
+__host__ __device__ constexpr int gb_ks(int nwn) { return 64 * nwn + 8; }
+__host__ __device__ constexpr int gb_thr(int nwn) { return 128 * nwn; }
+static_assert(GB_K * gb_ks(2) <= GB_T * GB_S, "the weight-gradient kinds' K-major A tile fits in sA");
 enum { BK_DH = 0, BK_DX = 1, BK_DW2 = 2, BK_DW13 = 3 };
 
 // Tuning knobs of the weight-gradient GEMMs (same results for every setting):
@@ -183,17 +189,23 @@ struct BwdGemm {
 // Weight-gradient kinds: a workgroup owns one 128-row block of the output (tile row
 // m0) and kBwdNtw consecutive column tiles.
 
-template <int KIND>
+template <int KIND, int NWN>
 // The weight-gradient kinds fit in 128 registers without spilling, so they run four
-// wavefronts per SIMD (four workgroups per CU); the data kinds would spill and keep three.
-__global__ __launch_bounds__(GB_THR) __attribute__((amdgpu_waves_per_eu(KIND >= BK_DW2 ? 4 : MOE_BWD_WAVES)))
+// wavefronts per SIMD (four workgroups per CU); the 128 x 256 data kinds are held to 128
+// registers too (two workgroups of eight wavefronts per CU); the 128 x 128 data kinds
+// would spill there and keep three.
+__global__ __launch_bounds__(gb_thr(NWN))
+__attribute__((amdgpu_waves_per_eu(KIND >= BK_DW2 || NWN == 4 ? 4 : MOE_BWD_WAVES)))
 void bwd_gemm_kernel(BwdGemm g) {
   constexpr bool WGRAD = KIND >= BK_DW2;
+  static_assert(NWN == 2 || (NWN == 4 && !WGRAD), "tile widths");
+  constexpr int TN = 64 * NWN, KS = gb_ks(NWN), THR = gb_thr(NWN);
+  constexpr int SB = GB_K * KS > GB_T * GB_S ? GB_K * KS : GB_T * GB_S;
   __shared__ __attribute__((aligned(16))) uint16_t sA[GB_T * GB_S];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[GB_T * GB_S];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[SB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / NWN, wn = wave % NWN;
 
   // ---- tile decode ----
   int s, row0, mrows = GB_T, K, m0 = 0, n0;
@@ -215,7 +227,7 @@ void bwd_gemm_kernel(BwdGemm g) {
     const int nt = rem / gm, mt = grp * GM + rem % gm;
     row0 = g.rowstart[s] + mt * GB_T;
     mrows = min(GB_T, g.rowcount[s] - mt * GB_T);
-    n0 = nt * GB_T;
+    n0 = nt * TN;
     K = KIND == BK_DH ? g.d : 2 * g.I;
   } else {
     const int ntw = g.NT / kBwdNtw;   // workgroups along N (each takes kBwdNtw column tiles)
@@ -233,21 +245,24 @@ void bwd_gemm_kernel(BwdGemm g) {
   const long long e = is_shared ? 0 : s;
 
   // ---- loaders ----
-  // row operand (A of DH / DX): rows lr + 32 i, 16-byte chunk lc of the K-step
+  // row operand (A of DH / DX): rows lr + RP i, 16-byte chunk lc of the K-step
+  constexpr int RP = THR / 8, NA = GB_T / RP;
   const int lr = tid >> 3, lc = (tid & 7) * 8;
   // K-major operands (the weights of the data kinds; both operands of the weight-gradient
   // kinds): K-rows 4 bkq .. 4 bkq + 3 of the step, columns 8 brb .. 8 brb + 7, so one load
-  // instruction of a wavefront reads four whole 256-byte row pieces.  The tile goes to
-  // LDS as it is (K-major, row pitch GB_KS) and the MFMA fragments are read from it with
-  // the transposing ds_read_b64_tr_b16 (k_frag).
-  const int bkq = tid >> 4, brb = tid & 15;
-  const uint16_t* arow[4];
+  // instruction of a wavefront reads whole row pieces (four of 256 bytes, or two of 512).
+  // The tile goes to LDS as it is (K-major, row pitch KS) and the MFMA fragments are read
+  // from it with the transposing ds_read_b64_tr_b16 (k_frag).
+  constexpr int CPR = TN / 8;   // 16-byte chunks per K-row of the tile
+  static_assert(THR / CPR * 4 == GB_K, "four K-rows per thread");
+  const int bkq = tid / CPR, brb = tid % CPR;
+  const uint16_t* arow[NA];
   if (!WGRAD) {
     const uint16_t* base = KIND == BK_DH ? g.d_out : g.dadg;
     const long long ld = KIND == BK_DH ? g.d : 2LL * g.I;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = lr + 32 * i;
+    for (int i = 0; i < NA; ++i) {
+      const int r = lr + RP * i;
       arow[i] = base + ((long long)row0 + (r < mrows ? r : 0)) * ld + lc;
     }
   }
@@ -269,12 +284,13 @@ void bwd_gemm_kernel(BwdGemm g) {
   }
   const u32x4_t zero4 = {0u, 0u, 0u, 0u};
   f32x16_t acc[2][2];
-  u32x4_t ra[4], ka[4], kb[4];
-  auto load_a_to = [&](u32x4_t(&A)[4], int k0) {
-    if (!WGRAD) {
+  u32x4_t ra[NA], ka[4], kb[4];
+  auto load_ra = [&](int k0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) A[i] = *(const u32x4_t*)(arow[i] + k0);
-    } else {
+    for (int i = 0; i < NA; ++i) ra[i] = *(const u32x4_t*)(arow[i] + k0);
+  };
+  auto load_a_to = [&](u32x4_t(&A)[4], int k0) {
+    {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int kg = k0 + 4 * bkq + i;
@@ -284,7 +300,7 @@ void bwd_gemm_kernel(BwdGemm g) {
     }
   };
   auto load_a = [&](int k0) {
-    if (!WGRAD) load_a_to(ra, k0);
+    if (!WGRAD) load_ra(k0);
     else load_a_to(ka, k0);
   };
   auto load_b_to = [&](u32x4_t(&B)[4], int k0, int c0) {
@@ -315,16 +331,16 @@ void bwd_gemm_kernel(BwdGemm g) {
     }
   };
   auto load_b = [&](int k0, int c0) { load_b_to(kb, k0, c0); };
-  // a K-major tile as it is, row pitch GB_KS (conflict-free 16-byte stores: a quarter-
-  // wavefront writes one 256-byte row piece)
+  // a K-major tile as it is, row pitch KS (conflict-free 16-byte stores: 16 lanes write
+  // 256 contiguous bytes of one row)
   auto store_k = [&](uint16_t* sX, const u32x4_t(&R)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4_t*)&sX[(4 * bkq + i) * GB_KS + 8 * brb] = R[i];
+    for (int i = 0; i < 4; ++i) *(u32x4_t*)&sX[(4 * bkq + i) * KS + 8 * brb] = R[i];
   };
   auto store_a = [&]() {
     if (!WGRAD) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *(u32x4_t*)&sA[(lr + 32 * i) * GB_S + lc] = ra[i];
+      for (int i = 0; i < NA; ++i) *(u32x4_t*)&sA[(lr + RP * i) * GB_S + lc] = ra[i];
     } else {
       store_k(sA, ka);
     }
@@ -346,15 +362,19 @@ void bwd_gemm_kernel(BwdGemm g) {
     typedef __attribute__((address_space(3))) v4i16_t lds_v4;
     const int i16 = lane & 15;
     const int c = cb + 16 * ((lane >> 4) & 1);
-    const uint16_t* p0 = &sX[(kc + (i16 >> 2)) * GB_KS + c + 4 * (i16 & 3)];
+    const uint16_t* p0 = &sX[(kc + (i16 >> 2)) * KS + c + 4 * (i16 & 3)];
     const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(p0));
-    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(p0 + 4 * GB_KS));
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(p0 + 4 * KS));
     const v8i16_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8_t, v);
   };
-  auto mma = [&]() {
+  // kvalid: K-values of this step that lie inside the reduction.  The weight-gradient
+  // kinds stop after the last 16-row chunk holding one: the rest of the step is zero
+  // padding, whose products (+0) would change no sum except a -0 into +0.
+  auto mma = [&](int kvalid) {
 #pragma unroll
     for (int kk = 0; kk < GB_K; kk += 16) {
+      if (WGRAD && kk >= kvalid) break;
       const int kc = kk + (lane >> 5) * 8;
       bf16x8_t af[2], bf[2];
 #pragma unroll
@@ -423,7 +443,7 @@ void bwd_gemm_kernel(BwdGemm g) {
   const int nsteps = (K + GB_K - 1) / GB_K;
   const int ntiles = WGRAD ? kBwdNtw : 1;
   for (int q = 0; q < ntiles; ++q) {
-    const int c0 = n0 + q * GB_T;
+    const int c0 = n0 + q * TN;
     zero_acc();
     if (nsteps > 0) {
       load_a(0);
@@ -437,7 +457,7 @@ void bwd_gemm_kernel(BwdGemm g) {
         load_a((st + 1) * GB_K);
         load_b((st + 1) * GB_K, c0);
       }
-      mma();
+      mma(K - st * GB_K);
       __syncthreads();
     }
     epilogue(c0);
@@ -729,14 +749,18 @@ static moe_status bwd_data(BwdGemm& g, const moe_expert_bank* routed, const moe_
   if (st != MOE_OK) return st;
   const long long mt_bound =
       (g.Tk + (long long)g.E * (GB_T - 1)) / GB_T + (g.S > g.E ? (g.T + GB_T - 1) / GB_T : 0);
-  g.NT = g.I / GB_T;
+  // 256-column tiles where the output width allows them, else 128
+  const bool wide_dh = g.I % 256 == 0, wide_dx = g.d % 256 == 0;
+  g.NT = g.I / (wide_dh ? 256 : 128);
   long long grid = tile_grid(mt_bound * g.NT, 0);
   if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
-  bwd_gemm_kernel<BK_DH><<<(unsigned)grid, GB_THR, 0, s>>>(g);
-  g.NT = g.d / GB_T;
+  if (wide_dh) bwd_gemm_kernel<BK_DH, 4><<<(unsigned)grid, gb_thr(4), 0, s>>>(g);
+  else bwd_gemm_kernel<BK_DH, 2><<<(unsigned)grid, gb_thr(2), 0, s>>>(g);
+  g.NT = g.d / (wide_dx ? 256 : 128);
   grid = tile_grid(mt_bound * g.NT, 0);
   if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
-  bwd_gemm_kernel<BK_DX><<<(unsigned)grid, GB_THR, 0, s>>>(g);
+  if (wide_dx) bwd_gemm_kernel<BK_DX, 4><<<(unsigned)grid, gb_thr(4), 0, s>>>(g);
+  else bwd_gemm_kernel<BK_DX, 2><<<(unsigned)grid, gb_thr(2), 0, s>>>(g);
   return launch_status();
 }
 
@@ -761,12 +785,12 @@ static moe_status bwd_weights(BwdGemm& g, hipStream_t s) {
   if (g.NT % kBwdNtw != 0 || (g.d / GB_T) % kBwdNtw != 0) return MOE_ERR_UNSUPPORTED;
   long long grid = tile_grid((long long)g.S * g.MT * (g.NT / kBwdNtw), 0);
   if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
-  bwd_gemm_kernel<BK_DW2><<<(unsigned)grid, GB_THR, 0, s>>>(g);
+  bwd_gemm_kernel<BK_DW2, 2><<<(unsigned)grid, gb_thr(2), 0, s>>>(g);
   g.MT = 2 * g.I / GB_T;
   g.NT = g.d / GB_T;
   grid = tile_grid((long long)g.S * g.MT * (g.NT / kBwdNtw), 0);
   if (grid > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
-  bwd_gemm_kernel<BK_DW13><<<(unsigned)grid, GB_THR, 0, s>>>(g);
+  bwd_gemm_kernel<BK_DW13, 2><<<(unsigned)grid, gb_thr(2), 0, s>>>(g);
   return launch_status();
 }
 

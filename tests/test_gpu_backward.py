@@ -6,8 +6,9 @@ Every gradient (dx, the routing-weight gradients, the gate's, every expert's dW1
 max |ref|), to 2e-2: the bf16 roundings of h, of the expert outputs and of the
 gradients fed to the bf16 GEMMs are inside that bar, as for the forward.  Shapes
 span several 128-row tiles, ragged segments, experts with no rows (their gradients
-must be exactly zero), k = 1 and the three routing modes (learned, replay with the
-gate's weights, replay with caller weights: no gate gradient).  The backward is
+must be exactly zero), k = 1, the three routing modes (learned, replay with the
+gate's weights, replay with caller weights: no gate gradient) and both column-tile
+widths of the dh and dx GEMMs (256 where I or d is a multiple of 256, else 128).  The backward is
 bitwise reproducible run to run, and a token's dx does not depend on the batch.
 """
 import numpy as np
@@ -87,6 +88,9 @@ CASES = [
     ("k1_no_shared", 150, 256, 128, 12, 1, False, True, "learned", 4),
     ("replay_gate_weights", 100, 128, 256, 8, 3, True, True, "replay_gate", 5),
     ("replay_caller_weights", 100, 128, 128, 8, 3, True, True, "replay", 6),
+    # dh and dx on two 256-column tiles each; then widths that take the 128-column tiles (3 each)
+    ("wide_tiles_two_columns", 200, 512, 512, 6, 2, True, True, "learned", 7),
+    ("narrow_tiles_width_384", 120, 384, 384, 5, 2, False, True, "learned", 8),
 ]
 
 

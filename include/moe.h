@@ -491,7 +491,8 @@ moe_status moe_nvfp4_transpose_weights(const moe_expert_bank* bank, int n, int d
  *             dx_t += sum_r dl_tr w_gate[:, ids_tr].
  *   d_bias    out fp32 [E] (sum of dl per expert) or NULL; requires d_w_gate.
  *   ids, weights, d_weights [T][k]; offsets, perm, row_of from moe_dispatch;
- *   x as moe_route.  ws: moe_backward_workspace_size.  MOE_ERR_UNSUPPORTED: d % 4. */
+ *   x as moe_route (read only for d_w_gate; MOE_ERR_INVALID_ARG if it is not 16-byte
+ *   aligned then).  ws: moe_backward_workspace_size.  MOE_ERR_UNSUPPORTED: d % 4. */
 moe_status moe_route_backward(const void* x, const uint8_t* x_scale, int dtype, int T, int d,
                               const float* w_gate, int E, int k, const int32_t* ids,
                               const float* weights, const float* d_weights, const int32_t* offsets,

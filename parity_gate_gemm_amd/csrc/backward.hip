@@ -565,22 +565,26 @@ __global__ __launch_bounds__(1024) void route_bwd_dx_kernel(
 }
 
 // dWg[:, e] = sum over expert e's dispatched rows (token ascending) of dl x_t, db[e] the
-// sum of those dl; workgroup (column chunk of 256, expert e).  The rows' tokens and dl
-// go through LDS in chunks of 256, so a thread's activation loads do not wait on each
-// other; each sum is one chain in ascending row order.
+// sum of those dl; workgroup (column chunk of 1024, expert e), four adjacent columns per
+// thread, so a wavefront reads 256 contiguous bytes of an MXFP8 row per load (512 bf16,
+// 1024 fp32) and one scale byte serves the thread's four columns.  The rows' tokens and
+// dl go through LDS in chunks of 256, and a thread issues the activation loads of 16 rows
+// before their multiply-adds; each sum is one chain in ascending row order.
+constexpr int kWgB = 16;   // rows per batch of loads in flight
 __global__ __launch_bounds__(256) void route_bwd_wgate_kernel(
     const void* __restrict__ x, const uint8_t* __restrict__ xs, int dtype, int T, int d, int k, int E,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
     const float* __restrict__ dl, float* __restrict__ dwg, float* __restrict__ db, int* flag) {
   __shared__ int stok[256];
   __shared__ float sq[256];
-  const int e = blockIdx.y, c = blockIdx.x * 256 + threadIdx.x;
+  const int e = blockIdx.y, c = (blockIdx.x * 256 + threadIdx.x) * 4;   // d % 4 == 0
   const long long Tk = (long long)T * k;
   long long lo = offsets[e], hi = offsets[e + 1];
   lo = lo < 0 ? 0 : (lo > Tk ? Tk : lo);
   hi = hi < lo ? lo : (hi > Tk ? Tk : hi);
   const int cc = c < d ? c : 0;
-  float acc = 0.0f, bacc = 0.0f;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float bacc = 0.0f;
   for (long long base = lo; base < hi; base += 256) {
     const int n = (int)(hi - base < 256 ? hi - base : 256);
     if ((int)threadIdx.x < n) {
@@ -593,31 +597,77 @@ __global__ __launch_bounds__(256) void route_bwd_wgate_kernel(
       sq[threadIdx.x] = dl[p];
     }
     __syncthreads();
-    if (dtype == MOE_MXFP8) {
-      // the E4M3 code decoded exactly by the hardware, times the block scale 2^(s - 127)
-      // (an fp32 value for every s < 255): one rounding of the exact product, the value
-      // load_act_f64 gives after its conversion to fp32
-#pragma unroll 8
-      for (int i = 0; i < n; ++i) {
-        const float q = sq[i];
-        const size_t row = (size_t)stok[i];
-        const int code = ((const uint8_t*)x)[row * d + cc];
-        const uint32_t se = xs[row * (size_t)(d / 32) + cc / 32];
-        const float sc = se == 0 ? 0x1p-127f : se == 255 ? __uint_as_float(0x7fc00000u) : __uint_as_float(se << 23);
-        acc = fmaf(q, __builtin_amdgcn_cvt_pk_f32_fp8(code, false)[0] * sc, acc);
-        bacc += q;
+    // rows in batches of kWgB: every load of a batch is issued before its first
+    // multiply-add.  A batch's rows past n re-read row n - 1 and their results are
+    // discarded (selects, no branch, so the loads stay ahead of the arithmetic).
+    for (int i0 = 0; i0 < n; i0 += kWgB) {
+      float q[kWgB], v[kWgB][4];
+      if (dtype == MOE_MXFP8) {
+        // each E4M3 code decoded exactly by the hardware, times the block scale
+        // 2^(s - 127) (an fp32 value for every s < 255; s = 0 gives the subnormal 2^-127,
+        // s = 255 NaN, both by setting bit 22): one rounding of the exact product, the
+        // value load_act_f64 gives after its conversion to fp32
+        int codes[kWgB];
+        uint32_t se[kWgB];
+#pragma unroll
+        for (int j = 0; j < kWgB; ++j) {
+          const int r = min(i0 + j, n - 1);
+          const size_t row = (size_t)stok[r];
+          q[j] = sq[r];
+          codes[j] = *(const int*)((const uint8_t*)x + row * d + cc);
+          se[j] = xs[row * (size_t)(d / 32) + cc / 32];
+        }
+#pragma unroll
+        for (int j = 0; j < kWgB; ++j) {
+          const float sc = __uint_as_float((se[j] << 23) | ((uint32_t)(se[j] == 0 || se[j] == 255) << 22));
+          const auto v01 = __builtin_amdgcn_cvt_pk_f32_fp8(codes[j], false);
+          const auto v23 = __builtin_amdgcn_cvt_pk_f32_fp8(codes[j], true);
+          v[j][0] = v01[0] * sc;
+          v[j][1] = v01[1] * sc;
+          v[j][2] = v23[0] * sc;
+          v[j][3] = v23[1] * sc;
+        }
+      } else if (dtype == MOE_BF16) {
+#pragma unroll
+        for (int j = 0; j < kWgB; ++j) {
+          const int r = min(i0 + j, n - 1);
+          q[j] = sq[r];
+          const u32x2_t u = *(const u32x2_t*)((const uint16_t*)x + (size_t)stok[r] * d + cc);
+          v[j][0] = __uint_as_float(u[0] << 16);
+          v[j][1] = __uint_as_float(u[0] & 0xffff0000u);
+          v[j][2] = __uint_as_float(u[1] << 16);
+          v[j][3] = __uint_as_float(u[1] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kWgB; ++j) {
+          const int r = min(i0 + j, n - 1);
+          q[j] = sq[r];
+          const float4 f = *(const float4*)((const float*)x + (size_t)stok[r] * d + cc);
+          v[j][0] = f.x;
+          v[j][1] = f.y;
+          v[j][2] = f.z;
+          v[j][3] = f.w;
+        }
       }
-    } else {
-#pragma unroll 8
-      for (int i = 0; i < n; ++i) {
-        const float q = sq[i];
-        acc = fmaf(q, (float)load_act_f64(x, xs, dtype, (size_t)stok[i], d, cc), acc);
-        bacc += q;
+#pragma unroll
+      for (int j = 0; j < kWgB; ++j) {
+        const bool live = i0 + j < n;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float a = fmaf(q[j], v[j][t], acc[t]);
+          acc[t] = live ? a : acc[t];
+        }
+        const float b = bacc + q[j];
+        bacc = live ? b : bacc;
       }
     }
     __syncthreads();
   }
-  if (c < d) dwg[(size_t)c * E + e] = acc;
+  if (c < d) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dwg[(size_t)(c + j) * E + e] = acc[j];
+  }
   if (db && blockIdx.x == 0 && threadIdx.x == 0) db[e] = bacc;
 }
 
@@ -868,7 +918,8 @@ extern "C" moe_status moe_route_backward(const void* x, const uint8_t* x_scale, 
   }
   if (!x || !row_of || !dx_rows || !dx || !aligned(dx_rows, 16) || !aligned(dx, 16))
     return MOE_ERR_INVALID_ARG;
-  if (d_w_gate && (!w_gate || !ids || !weights || !d_weights || !offsets || !perm))
+  if (d_w_gate && (!w_gate || !ids || !weights || !d_weights || !offsets || !perm ||
+                   !aligned(x, 16)))
     return MOE_ERR_INVALID_ARG;
   float* dl = nullptr;
   float* wt = nullptr;
@@ -882,7 +933,7 @@ extern "C" moe_status moe_route_backward(const void* x, const uint8_t* x_scale, 
   const int thr = ((q4 + passes - 1) / passes + 63) / 64 * 64;
   route_bwd_dx_kernel<<<T, thr, 0, s>>>(dx_rows, row_of, T, d, k, has_shared ? 1 : 0, ids, dl, wt, E, dx);
   if (d_w_gate)
-    route_bwd_wgate_kernel<<<dim3((d + 255) / 256, E), 256, 0, s>>>(x, x_scale, dtype, T, d, k, E, offsets,
-                                                                    perm, dl, d_w_gate, d_bias, (int*)w);
+    route_bwd_wgate_kernel<<<dim3((d + 1023) / 1024, E), 256, 0, s>>>(x, x_scale, dtype, T, d, k, E, offsets,
+                                                                      perm, dl, d_w_gate, d_bias, (int*)w);
   return launch_status();
 }

@@ -300,9 +300,13 @@ __global__ __launch_bounds__(SC_THR) void gate_screen_kernel(const void* __restr
 // serves the learned path, router replay and the weights, so their values agree bit
 // for bit.  Requires d % 8 == 0.
 // ---------------------------------------------------------------------------
+// The helpers are instantiated per activation type (DT: MOE_BF16 or MOE_MXFP8) so their
+// unrolled loops hold no branch on it: a branch there made every load wait for the one
+// before it.
+template <int DT>
 __device__ __forceinline__ void wave_dot_xload(const void* __restrict__ x, const uint8_t* __restrict__ xs,
-                                               int dtype, int t, int d, int i0, double (&xv)[8]) {
-  if (dtype == MOE_BF16) {
+                                               int t, int d, int i0, double (&xv)[8]) {
+  if constexpr (DT == MOE_BF16) {
     const u32x4_t u = *(const u32x4_t*)((const uint16_t*)x + (size_t)t * d + i0);
 #pragma unroll
     for (int q = 0; q < 8; ++q)
@@ -325,25 +329,27 @@ __device__ __forceinline__ void wave_dot_xload(const void* __restrict__ x, const
   }
 }
 
+template <int DT>
 __device__ __forceinline__ void wave_dot_load(const void* __restrict__ x, const uint8_t* __restrict__ xs,
-                                              int dtype, int t, int d, const float* __restrict__ w,
+                                              int t, int d, const float* __restrict__ w,
                                               int i0, double (&xv)[8], float (&wv)[8]) {
-  wave_dot_xload(x, xs, dtype, t, d, i0, xv);
+  wave_dot_xload<DT>(x, xs, t, d, i0, xv);
   const float4 w0 = *(const float4*)(w + i0), w1 = *(const float4*)(w + i0 + 4);
   wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w;
   wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
 }
 
-__device__ double wave_dot(const void* __restrict__ x, const uint8_t* __restrict__ xs, int dtype,
-                           int t, int d, const float* __restrict__ w) {
+template <int DT>
+__device__ double wave_dot_t(const void* __restrict__ x, const uint8_t* __restrict__ xs,
+                             int t, int d, const float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
   double acc = 0.0;
   int i0 = 8 * lane;
   for (; i0 + 512 < d; i0 += 1024) {     // two iterations' loads issued before their fmas
     double xa[8], xb[8];
     float wa[8], wb[8];
-    wave_dot_load(x, xs, dtype, t, d, w, i0, xa, wa);
-    wave_dot_load(x, xs, dtype, t, d, w, i0 + 512, xb, wb);
+    wave_dot_load<DT>(x, xs, t, d, w, i0, xa, wa);
+    wave_dot_load<DT>(x, xs, t, d, w, i0 + 512, xb, wb);
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc = fma(xa[q], (double)wa[q], acc);
 #pragma unroll
@@ -352,13 +358,17 @@ __device__ double wave_dot(const void* __restrict__ x, const uint8_t* __restrict
   if (i0 < d) {
     double xa[8];
     float wa[8];
-    wave_dot_load(x, xs, dtype, t, d, w, i0, xa, wa);
+    wave_dot_load<DT>(x, xs, t, d, w, i0, xa, wa);
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc = fma(xa[q], (double)wa[q], acc);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
   return acc;
+}
+__device__ __forceinline__ double wave_dot(const void* __restrict__ x, const uint8_t* __restrict__ xs,
+                                           int dtype, int t, int d, const float* __restrict__ w) {
+  return dtype == MOE_BF16 ? wave_dot_t<MOE_BF16>(x, xs, t, d, w) : wave_dot_t<MOE_MXFP8>(x, xs, t, d, w);
 }
 
 // ---------------------------------------------------------------------------
@@ -602,15 +612,16 @@ constexpr int RF_W = 8, RF_LDS_MAX = 16384;
 // wave_dot with w in LDS: the same fma sequence (lane-strided blocks of 8, ascending,
 // then the same butterfly) as wave_dot, hence the same bits; activation loads run up
 // to 4 blocks ahead.
-__device__ double wave_dot_lds(const void* __restrict__ x, const uint8_t* __restrict__ xs, int dtype,
-                               int t, int d, const float* w) {
+template <int DT>
+__device__ double wave_dot_lds_t(const void* __restrict__ x, const uint8_t* __restrict__ xs,
+                                 int t, int d, const float* w) {
   const int lane = threadIdx.x & 63;
   double acc = 0.0;
   int i0 = 8 * lane;
   for (; i0 + 3 * 512 < d; i0 += 4 * 512) {
     double xa[4][8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) wave_dot_xload(x, xs, dtype, t, d, i0 + 512 * u, xa[u]);
+    for (int u = 0; u < 4; ++u) wave_dot_xload<DT>(x, xs, t, d, i0 + 512 * u, xa[u]);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const float4 w0 = *(const float4*)(w + i0 + 512 * u), w1 = *(const float4*)(w + i0 + 512 * u + 4);
@@ -621,7 +632,7 @@ __device__ double wave_dot_lds(const void* __restrict__ x, const uint8_t* __rest
   }
   for (; i0 < d; i0 += 512) {
     double xa[8];
-    wave_dot_xload(x, xs, dtype, t, d, i0, xa);
+    wave_dot_xload<DT>(x, xs, t, d, i0, xa);
     const float4 w0 = *(const float4*)(w + i0), w1 = *(const float4*)(w + i0 + 4);
     const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
@@ -630,6 +641,11 @@ __device__ double wave_dot_lds(const void* __restrict__ x, const uint8_t* __rest
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
   return acc;
+}
+__device__ __forceinline__ double wave_dot_lds(const void* __restrict__ x, const uint8_t* __restrict__ xs,
+                                               int dtype, int t, int d, const float* w) {
+  return dtype == MOE_BF16 ? wave_dot_lds_t<MOE_BF16>(x, xs, t, d, w)
+                           : wave_dot_lds_t<MOE_MXFP8>(x, xs, t, d, w);
 }
 
 __global__ __launch_bounds__(64 * RF_W) void screen_refine_kernel(

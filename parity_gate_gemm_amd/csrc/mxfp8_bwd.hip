@@ -316,38 +316,53 @@ __global__ __launch_bounds__(256) void mx_colq4_kernel(ColqArgs a) {
     srow[tid] = off;
   }
   __syncthreads();
-  // ---- loads: chunks of EPC elements (16 bytes of the source) ----
+  // ---- loads: chunks of EPC elements (16 bytes of the source), NI per thread, all
+  //      issued before the first is decoded; a chunk outside the source (padding row,
+  //      column past C) loads the source's first chunk instead and is stored as zeros ----
   constexpr int EPC = KIND == kColBf16 ? 8 : KIND == kColMx ? 16 : 4;
   constexpr int CPR = C4_C / EPC;   // chunks per row
-#pragma unroll 4
-  for (int i = tid; i < C4_R * CPR; i += 256) {
-    const int rr = i / CPR, cc = (i % CPR) * EPC, c = c0 + cc;
+  constexpr int NI = C4_R * CPR / 256;
+  static_assert(C4_R * CPR % 256 == 0, "whole chunks per thread");
+  u32x4_t qa[NI], qg[NI];   // qg: the g half of a pre-activation row (kColPre)
+  int sc[NI];
+  bool ok[NI];
+#pragma unroll
+  for (int n = 0; n < NI; ++n) {
+    const int i = tid + 256 * n;
+    const int rr = i / CPR, c = c0 + (i % CPR) * EPC;
     const long long off = srow[rr];
+    ok[n] = off >= 0 && c < a.C;
+    const long long o = ok[n] ? off + c : 0;
+    if (KIND == kColBf16) {
+      qa[n] = *(const u32x4_t*)((const uint16_t*)a.src + o);
+    } else if (KIND == kColMx) {
+      qa[n] = *(const u32x4_t*)((const uint8_t*)a.src + o);
+      sc[n] = (int)a.src_s[o / 32];
+    } else {
+      qa[n] = *(const u32x4_t*)((const float*)a.src + o);
+      if (KIND == kColPre) qg[n] = *(const u32x4_t*)((const float*)a.src + o + a.C);
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NI; ++n) {
+    const int i = tid + 256 * n;
+    const int rr = i / CPR, cc = (i % CPR) * EPC;
     float v[EPC];
+    if (KIND == kColBf16) {
 #pragma unroll
-    for (int u = 0; u < EPC; ++u) v[u] = 0.0f;
-    if (off >= 0 && c < a.C) {
-      if (KIND == kColBf16) {
-        const u32x4_t q = *(const u32x4_t*)((const uint16_t*)a.src + off + c);
+      for (int u = 0; u < 8; ++u) v[u] = bf16_to_f32((uint16_t)(qa[n][u >> 1] >> (16 * (u & 1))));
+    } else if (KIND == kColF32) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = bf16_to_f32((uint16_t)(q[u >> 1] >> (16 * (u & 1))));
-      } else if (KIND == kColF32) {
-        const float4 q = *(const float4*)((const float*)a.src + off + c);
-        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-      } else if (KIND == kColMx) {
-        const u32x4_t q = *(const u32x4_t*)((const uint8_t*)a.src + off + c);
-        const int sc = (int)a.src_s[off / 32 + c / 32];
+      for (int u = 0; u < 4; ++u) v[u] = __uint_as_float(qa[n][u]);
+    } else if (KIND == kColMx) {
 #pragma unroll
-        for (int u = 0; u < 16; ++u) v[u] = ldexpf(e4m3_to_f32((q[u >> 2] >> (8 * (u & 3))) & 0xffu), sc - 127);
-      } else {
-        const float4 qa = *(const float4*)((const float*)a.src + off + c);
-        const float4 qg = *(const float4*)((const float*)a.src + off + a.C + c);
-        v[0] = silu_f32(qa.x) * qg.x; v[1] = silu_f32(qa.y) * qg.y;
-        v[2] = silu_f32(qa.z) * qg.z; v[3] = silu_f32(qa.w) * qg.w;
-      }
+      for (int u = 0; u < 16; ++u) v[u] = ldexpf(e4m3_to_f32((qa[n][u >> 2] >> (8 * (u & 3))) & 0xffu), sc[n] - 127);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = silu_f32(__uint_as_float(qa[n][u])) * __uint_as_float(qg[n][u]);
     }
 #pragma unroll
-    for (int u = 0; u < EPC; ++u) t[rr][cc + u] = v[u];
+    for (int u = 0; u < EPC; ++u) t[rr][cc + u] = ok[n] ? v[u] : 0.0f;
   }
   __syncthreads();
   if (KIND == kColPre) {
@@ -803,22 +818,32 @@ __global__ __launch_bounds__(256) void mx_colq4_nv_kernel(ColqArgs a) {
   }
   __syncthreads();
   if (KIND == kColNvDec) {
-#pragma unroll 4
-    for (int i = tid; i < C4_R * (C4_C / 8); i += 256) {
-      const int rr = i / (C4_C / 8), cc = (i % (C4_C / 8)) * 8, c = c0 + cc;
-      const long long row = srow[rr];
-      double v[8];
+    // the thread's NI chunks loaded before the first is decoded; a chunk outside the
+    // source (padding row, column past C) loads row 0's first chunk and stores zeros
+    constexpr int CPR = C4_C / 8, NI = C4_R * CPR / 256;
+    u32x4_t q[NI];
+    float rsf[NI];
+    bool ok[NI];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = 0.0;
-      if (row >= 0 && c < a.C) {
-        const u32x4_t q = *(const u32x4_t*)((const uint16_t*)a.src + row * a.C + c);
-        const double rs = (double)a.src_r[row];
+    for (int n = 0; n < NI; ++n) {
+      const int i = tid + 256 * n;
+      const int c = c0 + (i % CPR) * 8;
+      const long long row = srow[i / CPR];
+      ok[n] = row >= 0 && c < a.C;
+      const long long rw = ok[n] ? row : 0;
+      q[n] = *(const u32x4_t*)((const uint16_t*)a.src + rw * a.C + (ok[n] ? c : 0));
+      rsf[n] = a.src_r[rw];
+    }
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          v[u] = (double)(float)__builtin_bit_cast(_Float16, (uint16_t)(q[u >> 1] >> (16 * (u & 1)))) * rs;
+    for (int n = 0; n < NI; ++n) {
+      const int i = tid + 256 * n;
+      const int rr = i / CPR, cc = (i % CPR) * 8;
+      const double rs = (double)rsf[n];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const double v = (double)(float)__builtin_bit_cast(_Float16, (uint16_t)(q[n][u >> 1] >> (16 * (u & 1)))) * rs;
+        t[rr][cc + u] = ok[n] ? v : 0.0;
       }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) t[rr][cc + u] = v[u];
     }
   } else {
     // thread: row rr of the tile, codes of columns c0 + 32 h .. c0 + 32 h + 31

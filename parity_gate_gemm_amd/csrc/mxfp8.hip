@@ -370,17 +370,6 @@ __device__ __forceinline__ void xr_read_scales(XrScale<NB>& sc4, const uint8_t* 
     sc4.a[mb] = (int)(*(const uint32_t*)(scb + asf + mb * 32 * 16 + sc) >> sh);
 }
 
-// An empty asm that reads every accumulator: the MFMAs before it are issued before the
-// ring loads and barriers that follow it in program order (the compiler would otherwise
-// sink them next to their next use).
-__device__ __forceinline__ void xr_pin(const f32x16_t (&acc)[4][2]) {
-  asm volatile("" ::"a"(acc[0][0]), "a"(acc[0][1]), "a"(acc[1][0]), "a"(acc[1][1]), "a"(acc[2][0]),
-               "a"(acc[2][1]), "a"(acc[3][0]), "a"(acc[3][1]));
-}
-__device__ __forceinline__ void xr_pin(const f32x16_t (&acc)[2][2]) {
-  asm volatile("" ::"a"(acc[0][0]), "a"(acc[0][1]), "a"(acc[1][0]), "a"(acc[1][1]));
-}
-
 template <int NB, int SEL, int MB>
 __device__ __forceinline__ void xr_mfma(const XrFrag<NB>& f, const XrScale<NB>& sc4, f32x16_t (&acc)[MB][2]) {
 #pragma unroll
@@ -452,7 +441,8 @@ __device__ __forceinline__ void xr_kloop(const uint8_t* ring, uint32_t ring_lds,
       xr_mfma<NB, 0>(f, sc4, acc);
       xr_read<NB>(f, st, aof, bof, 1);
       xr_mfma<NB, 2>(f, sc4, acc);
-      xr_pin(acc);
+      // the step's MFMAs stay ahead of the next step's wait, barrier and loads
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -729,7 +719,8 @@ __device__ __forceinline__ void xs_kloop(const uint8_t* ring, uint32_t ring_lds,
       xr_mfma<NB, 0>(f, sc4, acc);
       xr_read<NB>(f, st, aof, bof, 1);
       xr_mfma<NB, 2>(f, sc4, acc);
-      xr_pin(acc);
+      // the step's MFMAs stay ahead of the next step's wait, barrier and loads
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }

@@ -5,6 +5,8 @@
 // mixes experts and every output is one fixed chain of scaled MFMAs over ascending K.
 #include <math.h>
 
+#include <algorithm>
+
 #include "moe_internal.h"
 #include "mx_common.h"
 
@@ -300,7 +302,15 @@ constexpr int XR_SCB = (XR_M + XR_N) * 16;       // bytes per scale-group buffer
 constexpr int XR_LDS = XR_SC + 2 * XR_SCB;       // 144 KB
 constexpr int XR_EPI_ROW = 144;                  // epilogue staging: bytes per local row
 constexpr int XR_EPI = 128 * XR_EPI_ROW;         // epilogue staging per wavefront (18 KB)
+// The 256-row kernel stages its epilogue in halves of 64 local rows per wavefront
+// (9 KB): wavefronts 0..6 in stage 1, wavefront 7 in a spare area after the scale
+// buffers, so stage 0 and scale buffer 0 can take the next tile's first loads meanwhile.
+constexpr int XR_EPH = 64 * XR_EPI_ROW;          // 9 KB
+constexpr int XR_SPARE = XR_LDS;
+constexpr int XR_LDS_P = XR_SPARE + 16 * 1024;   // 160 KB (its last 4 bytes: the next tile's position)
+constexpr int kTileCtr = 16;                     // header ints 16 .. 23: per-XCD tile counters
 static_assert(XR_LDS <= 160 * 1024 && 8 * XR_EPI <= XR_LDS, "LDS budget");
+static_assert(7 * XR_EPH <= XR_STAGE && XR_EPH <= 16 * 1024 && XR_LDS_P <= 160 * 1024, "LDS budget");
 
 // slot of the 16-byte chunk c of row r: c ^ ((r >> 1) & 7); the sixteen rows that one
 // ds_read_b128 phase touches (one chunk each) then fall in distinct banks
@@ -391,6 +401,21 @@ struct XrSrc {
   uint32_t aoff[4], boff[4], soff;
 };
 
+// Scale group 0 and step 0 of a tile into scale buffer 0 and stage 0 (this wavefront's
+// share), in the order the K loop's first wait expects.
+__device__ __forceinline__ void xr_issue_first(uint32_t ring_lds, const XrSrc& src, int wave) {
+  const uint32_t ls = wave < 4 ? wave * 1024 : XR_M * 16 + (wave - 4) * 1024;
+  if (wave < 4)
+    xr_load16(ring_lds + XR_SC + ls, src.soff, src.sbase);
+  else
+    xr_load16(ring_lds + XR_SC + ls, src.bsp);
+  const uint32_t la = XR_A + wave * 4096, lb = XR_B + wave * 4096;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xr_load16(ring_lds + la + 1024 * i, src.aoff[i], src.abase);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xr_load16(ring_lds + lb + 1024 * i, src.boff[i], src.bbase);
+}
+
 // The K loop of a wavefront that multiplies NB of its 4 row blocks (NB = 0: it only
 // loads and synchronises).  Step j (K bytes 128 j .. 128 j + 127) lives in stage j % 2.
 // At step j: wait for its data, meet (every wavefront is then done with step j - 1, whose
@@ -399,7 +424,7 @@ struct XrSrc {
 template <int NB>
 __device__ __forceinline__ void xr_kloop(const uint8_t* ring, uint32_t ring_lds, int nsteps, const XrSrc& src,
                                          int wave, uint32_t aof, uint32_t bof, uint32_t asf, uint32_t bsf,
-                                         int sh, f32x16_t (&acc)[4][2]) {
+                                         int sh, f32x16_t (&acc)[4][2], int* ctr, int& qn) {
   const uint32_t la = XR_A + wave * 4096, lb = XR_B + wave * 4096;
   const uint32_t ls = wave < 4 ? wave * 1024 : XR_M * 16 + (wave - 4) * 1024;
   const int ngroups = nsteps / XR_GS;
@@ -420,8 +445,7 @@ __device__ __forceinline__ void xr_kloop(const uint8_t* ring, uint32_t ring_lds,
   };
   auto scales_at = [&](int j) { return j >= 0 && j % XR_GS == 0 && j / XR_GS + 1 < ngroups; };
 
-  issue_scales(0);
-  issue(0);
+  // scale group 0 and step 0 went out before the call (xr_issue_first)
   for (int j = 0; j < nsteps; ++j) {
     // step j's data went out at step j - 1 (or before the loop), followed only by that
     // step's scale group (loads complete in issue order)
@@ -431,6 +455,9 @@ __device__ __forceinline__ void xr_kloop(const uint8_t* ring, uint32_t ring_lds,
       xr_sync<0>();
     if (j + 1 < nsteps) issue(j + 1);
     if (scales_at(j)) issue_scales(j / XR_GS + 1);
+    // the next tile's index, fetched along with step 2's loads (its reply comes before
+    // theirs, so the next step's wait does not stall on it)
+    if (ctr && j == 1 && threadIdx.x == 0) qn = atomicAdd(ctr, 1);
     if constexpr (NB > 0) {
       const uint8_t* st = ring + (j & 1) * XR_STAGE;
       const uint8_t* scb = ring + XR_SC + ((j / XR_GS) & 1) * XR_SCB;
@@ -447,18 +474,29 @@ __device__ __forceinline__ void xr_kloop(const uint8_t* ring, uint32_t ring_lds,
   }
 }
 
-// MXFP8 grouped GEMM, 256 x 256 tiles, eight wavefronts (2 along M x 4 along N, two per
-// SIMD), each 4 row blocks x 2 B blocks of 32 x 32.  A wavefront whose 32-row blocks
-// hold no valid row skips their MFMAs, so a short tile costs MFMA time in proportion to
-// its valid 32-row blocks on the busier half.
-template <int MODE>
-__global__ __launch_bounds__(512) void grouped_gemm_mx_ring_kernel(MxArgs g) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[XR_LDS];
+// A pointer the whole wavefront holds, kept in scalar registers.
+__device__ __forceinline__ const uint8_t* xr_uniform(const uint8_t* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 
-  // ---- tile decode (as grouped_gemm_mx_kernel, tiles of XR_M rows) ----
-  const int total = g.mstart[g.S] * g.NT;
-  int tile;
-  if (!xcd_tile<kMxXcdChunk>(total, tile)) return;
+// Rows, columns and loader sources of one 256-row tile.
+struct XrTile {
+  int row0, mrows, n0;
+  XrSrc src;
+};
+
+// Decode tile `tile` of the segment-major tile list (as grouped_gemm_mx_kernel, tiles of
+// XR_M rows) and set up this thread's loader sources: wavefront w fills A rows and B rows
+// 32 w .. 32 w + 31 (four loads of 8 rows each; lane l -> row + l / 8, slot l % 8 <- chunk
+// slot ^ swz(row); the B rows are one 32-row block, so one bank) and the 16-byte scale
+// groups of A rows 64 w + l (w < 4) or B rows 64 (w - 4) + l.  Every byte offset from a
+// load's base fits 32 bits (one activation matrix, or one expert's matrix).  A tile row
+// past the segment re-reads the tile's first row; a routed row whose token is out of
+// range sets `bad` and reads token 0.
+template <int MODE>
+__device__ __forceinline__ void xr_decode(const MxArgs& g, int tile, int wave, int lane, XrTile& t, int& bad) {
   int lo = 0, hi = g.S;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -476,14 +514,11 @@ __global__ __launch_bounds__(512) void grouped_gemm_mx_ring_kernel(MxArgs g) {
   const int n0 = nt * (G1 ? XR_N / 2 : XR_N);
   const bool is_shared = (s == g.E);
   const long long e = is_shared ? 0 : s;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
   const int KB = g.K / 32;   // scale bytes per row
+  t.row0 = row0;
+  t.mrows = mrows;
+  t.n0 = n0;
 
-  int bad = 0;
-  // source row of A tile row r (rows past the segment re-read the tile's first row)
   auto a_src = [&](int r) -> long long {
     const long long jr = (long long)row0 + (r < mrows ? r : 0);
     if (!G1) return jr;
@@ -508,36 +543,67 @@ __global__ __launch_bounds__(512) void grouped_gemm_mx_ring_kernel(MxArgs g) {
     sbank = is_shared ? g.sb0s : g.b0s;
     return (long long)n0 + r;
   };
-
-  // ---- loader: wavefront w fills A rows and B rows 32 w .. 32 w + 31 (four loads of 8
-  //      rows each; lane l -> row + l / 8, slot l % 8 <- chunk slot ^ swz(row); the B rows
-  //      are one 32-row block, so one bank) and the 16-byte scale groups of A rows
-  //      64 w + l (w < 4) or B rows 64 (w - 4) + l.  Every byte offset from a load's base
-  //      fits 32 bits (one activation matrix, or one expert's matrix). ----
-  XrSrc src;
-  src.abase = g.a;
-  src.sbase = g.as;
+  t.src.abase = g.a;
+  t.src.sbase = g.as;
   {
     const uint8_t *bank, *sbank;
     b_row(32 * wave, bank, sbank);
-    src.bbase = bank + e * g.N * (long long)g.K;
+    t.src.bbase = xr_uniform(bank + e * g.N * (long long)g.K);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 32 * wave + 8 * i + (lane >> 3);
     const int chunk = (lane & 7) ^ xr_swz(r);
-    src.aoff[i] = (uint32_t)(a_src(r) * g.K + 16 * chunk);
+    t.src.aoff[i] = (uint32_t)(a_src(r) * g.K + 16 * chunk);
     const uint8_t *bank, *sbank;
     const long long br = b_row(r, bank, sbank);
-    src.boff[i] = (uint32_t)(br * g.K + 16 * chunk);
+    t.src.boff[i] = (uint32_t)(br * g.K + 16 * chunk);
   }
-  src.soff = (uint32_t)(a_src(64 * (wave & 3) + lane) * KB);
+  t.src.soff = (uint32_t)(a_src(64 * (wave & 3) + lane) * KB);
   {
     const uint8_t *bank, *sbank;   // GEMM1: W1 scales for lanes 0..31, W3 for 32..63
     const long long br = b_row(64 * (wave & 3) + lane, bank, sbank);
-    src.bsp = sbank + (e * g.N + br) * (long long)KB;
+    t.src.bsp = sbank + (e * g.N + br) * (long long)KB;
   }
-  if (bad) raise_flag(g.flag, kFlagCorrupt);
+}
+
+// MXFP8 grouped GEMM, 256 x 256 tiles, eight wavefronts (2 along M x 4 along N, two per
+// SIMD), each 4 row blocks x 2 B blocks of 32 x 32.  A wavefront whose 32-row blocks
+// hold no valid row skips their MFMAs, so a short tile costs MFMA time in proportion to
+// its valid 32-row blocks on the busier half.
+// PERSIST (GEMM2, whose tiles have only I / 128 K steps, so a tile's start and epilogue
+// weigh more): one workgroup per CU walks its XCD's share of the tile list (the tiles
+// xcd_tile<kMxXcdChunk> deals to that XCD, in order), taking the next position from a
+// per-XCD counter; a tile's scale group 0 and first K step go out before the previous
+// tile's epilogue, which stages its outputs in halves through stage 1 and a spare area.
+// Otherwise (GEMM1, measured 3% slower persistent) one tile per workgroup.  A tile's
+// result does not depend on which workgroup computes it or when.
+template <int MODE>
+__global__ __launch_bounds__(512) void grouped_gemm_mx_ring_kernel(MxArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[XR_LDS_P];
+  constexpr bool G1 = MODE != 1;   // GEMM1 operands (modes 0 and 2)
+  constexpr bool PERSIST = MODE == 1;
+
+  const int total = g.mstart[g.S] * g.NT;
+  const int xcd = blockIdx.x % kXcds;
+  auto tile_of = [&](int q) { return ((q / kMxXcdChunk) * kXcds + xcd) * kMxXcdChunk + q % kMxXcdChunk; };
+  // PERSIST: the XCD's next tile position, from a per-XCD counter in the workspace header
+  // (cleared before the launch), read by thread 0 and handed to the workgroup through LDS
+  int* const ctr = PERSIST ? g.flag + kTileCtr + xcd : nullptr;
+  int* const s_q = (int*)(ring + XR_LDS_P - 4);
+  const int tid = threadIdx.x, lane = tid & 63;
+  int tile;
+  if constexpr (PERSIST) {
+    if (tid == 0) *s_q = atomicAdd(ctr, 1);
+    __syncthreads();
+    tile = tile_of(*s_q);
+    if (tile >= total) return;
+  } else {
+    if (!xcd_tile<kMxXcdChunk>(total, tile)) return;
+  }
+
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
 
   // ---- fragment offsets within a stage: lane reads row (block base + lane % 32),
   //      chunks lane / 32 and 2 + lane / 32 of the k range ----
@@ -548,97 +614,149 @@ __global__ __launch_bounds__(512) void grouped_gemm_mx_ring_kernel(MxArgs g) {
   const uint32_t asf = ra * 16, bsf = XR_M * 16 + rb * 16;   // within a scale buffer
   const int sh = 8 * hh;
 
-  f32x16_t acc[4][2];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
-
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_u8*)ring;
   const int nsteps = g.K / XR_K;
-  // 32-row blocks of this wavefront that hold a valid row (uniform per wavefront)
-  const int nb_act = min(4, max(0, (mrows - wm * 128 + 31) >> 5));
-  switch (nb_act) {
-    case 4: xr_kloop<4>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, sh, acc); break;
-    case 3: xr_kloop<3>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, sh, acc); break;
-    case 2: xr_kloop<2>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, sh, acc); break;
-    case 1: xr_kloop<1>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, sh, acc); break;
-    default: xr_kloop<0>(ring, ring_lds, nsteps, src, wave, aof, bof, asf, bsf, sh, acc); break;
-  }
+  // this wavefront's epilogue staging (64 local rows per half)
+  uint8_t* stg = ring + (wave < 7 ? XR_STAGE + wave * XR_EPH : XR_SPARE);
 
-  // ---- epilogue through LDS: each wavefront stages its 128 x (32 or 64) outputs
-  //      row-major in its own 18 KB of the (now idle) ring, then writes whole MX blocks
-  //      (GEMM1) or 16-byte row chunks (GEMM2).  Accumulator element v of a lane is
-  //      C[i][j], j = lane % 32, i = 8 (v / 4) + 4 (lane / 32) + v % 4; the wavefront's
-  //      local row 32 mb + i is tile row 128 wm + 32 mb + i. ----
-  if (G1 && g.out_pre) {   // pre-activations for the backward pass, from the accumulators
+  int bad = 0;
+  XrTile cur;
+  xr_decode<MODE>(g, tile, wave, lane, cur, bad);
+  xr_issue_first(ring_lds, cur.src, wave);
+  for (;;) {
+    int qn = 0;
+    const int row0 = cur.row0, mrows = cur.mrows, n0 = cur.n0;
+
+    f32x16_t acc[4][2];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      if (mb >= nb_act) break;
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = 128 * wm + 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
-        if (r < mrows) {
-          const long long orow = (long long)row0 + r;
-          const int col = n0 + 32 * wn + j32;
-          g.out_pre[orow * 2 * g.N + col] = acc[mb][0][v];
-          g.out_pre[orow * 2 * g.N + g.N + col] = acc[mb][1][v];
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+    // 32-row blocks of this wavefront that hold a valid row (uniform per wavefront)
+    const int nb_act = min(4, max(0, (mrows - wm * 128 + 31) >> 5));
+    switch (nb_act) {
+      case 4: xr_kloop<4>(ring, ring_lds, nsteps, cur.src, wave, aof, bof, asf, bsf, sh, acc, ctr, qn); break;
+      case 3: xr_kloop<3>(ring, ring_lds, nsteps, cur.src, wave, aof, bof, asf, bsf, sh, acc, ctr, qn); break;
+      case 2: xr_kloop<2>(ring, ring_lds, nsteps, cur.src, wave, aof, bof, asf, bsf, sh, acc, ctr, qn); break;
+      case 1: xr_kloop<1>(ring, ring_lds, nsteps, cur.src, wave, aof, bof, asf, bsf, sh, acc, ctr, qn); break;
+      default: xr_kloop<0>(ring, ring_lds, nsteps, cur.src, wave, aof, bof, asf, bsf, sh, acc, ctr, qn); break;
+    }
+
+    // ---- epilogue.  Accumulator element v of a lane is C[i][j], j = lane % 32,
+    //      i = 8 (v / 4) + 4 (lane / 32) + v % 4; the wavefront's local row 32 mb + i is
+    //      tile row 128 wm + 32 mb + i. ----
+    // (the lane's row and column indices are re-derived per tile through an opaque copy,
+    // so the compiler does not hoist the per-element addresses out of the tile loop and
+    // keep them live across the K loop)
+    int lane_t = lane;
+    asm volatile("" : "+v"(lane_t));
+    const int j32 = lane_t & 31, hh = lane_t >> 5;
+    if (G1 && g.out_pre) {   // pre-activations for the backward pass, from the accumulators
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        if (mb >= nb_act) break;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = 128 * wm + 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
+          if (r < mrows) {
+            const long long orow = (long long)row0 + r;
+            const int col = n0 + 32 * wn + j32;
+            g.out_pre[orow * 2 * g.N + col] = acc[mb][0][v];
+            g.out_pre[orow * 2 * g.N + g.N + col] = acc[mb][1][v];
+          }
         }
       }
     }
-  }
-  if (MODE == 2) return;
-  __syncthreads();   // every wavefront is done reading the ring
-  uint8_t* stg = ring + wave * XR_EPI;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    if (mb >= nb_act) break;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int rl = 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
-      if (MODE == 0) {
-        // B blocks 0 and 1 are the W1 and W3 halves of the same 32 features
-        *(float*)(stg + rl * XR_EPI_ROW + j32 * 4) = silu_f32(acc[mb][0][v]) * acc[mb][1][v];
-      } else {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          *(uint16_t*)(stg + rl * XR_EPI_ROW + (32 * nb + j32) * 2) = f32_to_bf16(acc[mb][nb][v]);
+    if (PERSIST && tid == 0) *s_q = qn;
+    __syncthreads();   // every wavefront is done reading the ring; the next position is out
+    qn = PERSIST ? *s_q : 0;
+    const int tn = PERSIST ? tile_of(qn) : total;
+    const bool more = tn < total;
+    XrTile nxt;
+    // the next tile's first loads, into stage 0 and scale buffer 0
+    auto prefetch = [&]() {
+      if (more) {
+        xr_decode<MODE>(g, tn, wave, lane, nxt, bad);
+        xr_issue_first(ring_lds, nxt.src, wave);
       }
-    }
-  }
-  if (MODE == 0) {
-    // thread i: tile row (i + 512 q) / 4, MX block (i % 4: wavefront column wn's 32
-    // features), staged by wavefront (row / 128, i % 4); four neighbouring lanes write a
-    // row's 128 code bytes and its 4 scale bytes contiguously
-    __syncthreads();
+    };
+    if (MODE != 0) prefetch();   // GEMM2: before its epilogue; pre-activations only: no epilogue
+    if (MODE == 1) {
+      // two halves: local rows 64 h .. 64 h + 63 of every wavefront (blocks 2 h, 2 h + 1),
+      // staged in stage 1 and the spare area; a wavefront reads back only what it wrote
+      // (its LDS accesses complete in order)
 #pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2) {
-      const int idx = tid + 512 * q2, r = idx >> 2, b = idx & 3;
-      if (r < mrows) {
-        const long long orow = (long long)row0 + r;
-        const int col = n0 + 32 * b;
-        mx_store_block(ring + ((r >> 7) * 4 + b) * XR_EPI + (r & 127) * XR_EPI_ROW,
-                       (uint8_t*)g.out + orow * g.N + col, g.out_scale + orow * (g.N / 32) + col / 32);
-      }
-    }
-  } else {
-    // (a wavefront reads back only what it wrote: its LDS accesses complete in order)
-    // lane l: local row 8 q + l / 8, 16-byte chunk l % 8 of the row's 64 outputs
-    const int c = lane & 7;
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2) {
+          const int mb = 2 * h + m2;
+          if (mb >= nb_act) break;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int rl = 32 * m2 + 8 * (v >> 2) + 4 * hh + (v & 3);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+              *(uint16_t*)(stg + rl * XR_EPI_ROW + (32 * nb + j32) * 2) = f32_to_bf16(acc[mb][nb][v]);
+          }
+        }
+        // lane l: local row 8 q + l / 8 of the half, 16-byte chunk l % 8 of its 64 outputs
+        const int c = lane & 7;
 #pragma unroll 4
-    for (int q2 = 0; q2 < 16; ++q2) {
-      const int rl = 8 * q2 + (lane >> 3);
-      const int r = 128 * wm + rl;
-      if ((rl >> 5) < nb_act && r < mrows) {
-        const u32x4_t t = *(const u32x4_t*)(stg + rl * XR_EPI_ROW + 16 * c);
-        // nontemporal: the expert outputs are read once, by the combine
-        __builtin_nontemporal_store(t, (u32x4_t*)((uint16_t*)g.out + ((long long)row0 + r) * g.N + n0 + wn * 64 + 8 * c));
+        for (int q2 = 0; q2 < 8; ++q2) {
+          const int rl = 8 * q2 + (lane >> 3);
+          const int r = 128 * wm + 64 * h + rl;
+          if (((64 * h + rl) >> 5) < nb_act && r < mrows) {
+            const u32x4_t t = *(const u32x4_t*)(stg + rl * XR_EPI_ROW + 16 * c);
+            // nontemporal: the expert outputs are read once, by the combine
+            __builtin_nontemporal_store(
+                t, (u32x4_t*)((uint16_t*)g.out + ((long long)row0 + r) * g.N + n0 + wn * 64 + 8 * c));
+          }
+        }
       }
+    } else if (MODE == 0) {
+      // each wavefront stages its 128 x 32 values of h in its own 18 KB of the ring, then
+      // thread i requantises tile row (i + 512 q) / 4, MX block i % 4 (wavefront column
+      // wn's 32 features), staged by wavefront (row / 128, i % 4); four neighbouring lanes
+      // write a row's 128 code bytes and its 4 scale bytes contiguously
+      uint8_t* st1 = ring + wave * XR_EPI;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        if (mb >= nb_act) break;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int rl = 32 * mb + 8 * (v >> 2) + 4 * hh + (v & 3);
+          // B blocks 0 and 1 are the W1 and W3 halves of the same 32 features
+          *(float*)(st1 + rl * XR_EPI_ROW + j32 * 4) = silu_f32(acc[mb][0][v]) * acc[mb][1][v];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const int idx = tid + 512 * q2, r = idx >> 2, b = idx & 3;
+        if (r < mrows) {
+          const long long orow = (long long)row0 + r;
+          const int col = n0 + 32 * b;
+          mx_store_block(ring + ((r >> 7) * 4 + b) * XR_EPI + (r & 127) * XR_EPI_ROW,
+                         (uint8_t*)g.out + orow * g.N + col, g.out_scale + orow * (g.N / 32) + col / 32);
+        }
+      }
+      __syncthreads();   // every staging read is done (the stores may still be in flight)
+      prefetch();
     }
+    if (!more) break;
+    tile = tn;
+    cur = nxt;
+    cur.row0 = __builtin_amdgcn_readfirstlane(cur.row0);
+    cur.mrows = __builtin_amdgcn_readfirstlane(cur.mrows);
+    cur.n0 = __builtin_amdgcn_readfirstlane(cur.n0);
+    cur.src.abase = xr_uniform(cur.src.abase);
+    cur.src.bbase = xr_uniform(cur.src.bbase);
+    cur.src.sbase = xr_uniform(cur.src.sbase);
   }
+  if (bad) raise_flag(g.flag, kFlagCorrupt);
 }
 
 // ---------------------------------------------------------------------------
@@ -949,6 +1067,25 @@ int mx_tile_rows(int d, int inter, long long Tk, int E) {
   return Tk <= (long long)XS_M * E ? XS_M : XR_M;
 }
 
+__global__ void mx_ctr_clear_kernel(int* p) {
+  if (threadIdx.x < kXcds) p[threadIdx.x] = 0;
+}
+
+// Workgroups of a persistent launch: the current device's CUs, rounded down to a multiple
+// of the XCD count (cached per device).
+static long long mx_persistent_grid() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kXcds * 32;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < kXcds)
+      n = kXcds * 32;
+    cus[dev] = n;
+  }
+  return (long long)(cus[dev] / kXcds) * kXcds;
+}
+
 moe_status mx_gemm(int mode, MxArgs g, long long mt_bound, hipStream_t s) {
   const bool g1 = mode != 1;
   const int d = g1 ? g.K : g.N, inter = g1 ? g.N : g.K;
@@ -974,12 +1111,16 @@ moe_status mx_gemm(int mode, MxArgs g, long long mt_bound, hipStream_t s) {
     else
       grouped_gemm_mx_ring128_kernel<1><<<(unsigned)grid, 512, 0, s>>>(g);
   } else if (ring) {
-    if (mode == 0)
+    if (mode == 0) {
       grouped_gemm_mx_ring_kernel<0><<<(unsigned)grid, 512, 0, s>>>(g);
-    else if (mode == 2)
+    } else if (mode == 2) {
       grouped_gemm_mx_ring_kernel<2><<<(unsigned)grid, 512, 0, s>>>(g);
-    else
-      grouped_gemm_mx_ring_kernel<1><<<(unsigned)grid, 512, 0, s>>>(g);
+    } else {
+      // persistent: at most one workgroup per CU (each holds 160 KB of LDS)
+      const unsigned pgrid = (unsigned)std::min<long long>(grid, mx_persistent_grid());
+      mx_ctr_clear_kernel<<<1, 64, 0, s>>>(g.flag + kTileCtr);
+      grouped_gemm_mx_ring_kernel<1><<<pgrid, 512, 0, s>>>(g);
+    }
   } else if (mode == 0) {
     grouped_gemm_mx_kernel<0, MOE_MX_WM, MOE_MX_WN, MOE_MX_FN>
         <<<(unsigned)grid, 64 * MOE_MX_WM * MOE_MX_WN, 0, s>>>(g);

@@ -288,3 +288,27 @@ def test_mxfp8_h_requantisation_without_saturation():
     rows = np.arange(wl.T)
     err = compare_rows(res, oracle_for_rows(inp, rows, wl.k), rows, "mxfp8")
     assert err <= 4.5e-2, err
+
+
+def test_mxfp8_persistent_gemm2_several_tiles_per_workgroup():
+    """An MXFP8 layer on the 256-row ring tiles whose down projection has 48 row tiles x
+    16 column tiles = 768 tiles, three per workgroup of the persistent GEMM2 (one per CU):
+    every workgroup finishes a tile's epilogue while the next tile's first loads are in
+    flight.  Sampled rows against the oracle, the routing and dispatch of every token,
+    bitwise repeats and one token alone (128-row tiles, one tile per workgroup) against
+    its row in the batch."""
+    from _gpu_common import check_routing_every_token, sample_rows
+    wl = synth.Workload("pers", T=4096, d=4096, inter=512, E=8, k=2, shared=True, bias=True,
+                        dtype="mxfp8", seed=77)
+    say("case mxfp8 persistent GEMM2 T=4096 d=4096 I=512 E=8 k=2 shared bias")
+    inp = synth.make_layer_inputs(wl, device="cuda")
+    base = run_layer(inp, wl.k)
+    check_routing_every_token(inp, base, wl.k, wl.E)
+    rows = sample_rows(base["ids"].cpu().numpy(), base["offsets"].cpu().numpy(),
+                       base["perm"].cpu().numpy(), wl.k, 256, True, 48, seed=5)
+    compare_rows(base, oracle_for_rows(inp, rows, wl.k), rows, "mxfp8")
+    for _ in range(3):
+        assert torch.equal(run_layer(inp, wl.k)["y"], base["y"])
+    for t in (0, 2049, 4095):
+        one = dict(inp, x=inp["x"][t:t + 1].contiguous(), x_scale=inp["x_scale"][t:t + 1].contiguous())
+        assert torch.equal(run_layer(one, wl.k)["y"][0], base["y"][t])

@@ -457,6 +457,7 @@ __device__ __forceinline__ void xr_kloop(const uint8_t* ring, uint32_t ring_lds,
     if (scales_at(j)) issue_scales(j / XR_GS + 1);
     // the next tile's index, fetched along with step 2's loads (its reply comes before
     // theirs, so the next step's wait does not stall on it)
+    // (the ring runs at least 4 steps; were there fewer, qn would stay negative: no next tile)
     if (ctr && j == 1 && threadIdx.x == 0) qn = atomicAdd(ctr, 1);
     if constexpr (NB > 0) {
       const uint8_t* st = ring + (j & 1) * XR_STAGE;
@@ -625,7 +626,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_mx_ring_kernel(MxArgs g) {
   xr_decode<MODE>(g, tile, wave, lane, cur, bad);
   xr_issue_first(ring_lds, cur.src, wave);
   for (;;) {
-    int qn = 0;
+    int qn = -1;   // stays negative (no next tile) unless the K loop fetched a position
     const int row0 = cur.row0, mrows = cur.mrows, n0 = cur.n0;
 
     f32x16_t acc[4][2];
@@ -672,8 +673,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_mx_ring_kernel(MxArgs g) {
     }
     if (PERSIST && tid == 0) *s_q = qn;
     __syncthreads();   // every wavefront is done reading the ring; the next position is out
-    qn = PERSIST ? *s_q : 0;
-    const int tn = PERSIST ? tile_of(qn) : total;
+    qn = PERSIST ? *s_q : -1;
+    const int tn = qn >= 0 ? tile_of(qn) : total;
     const bool more = tn < total;
     XrTile nxt;
     // the next tile's first loads, into stage 0 and scale buffer 0

@@ -1,0 +1,61 @@
+"""The layer forward (route, dispatch, both expert GEMMs, combine) captured once into a
+HIP graph and replayed: every call is a plain kernel launch on the caller's stream (no
+allocation, no memset, no host synchronisation), so a replay must give the eager call's
+bits.  Replays alternate two input batches copied into the captured input buffer, with
+eager work and synchronisations between them."""
+import pytest
+import torch
+
+import parity_gate_gemm_amd as pg
+import synth
+from _gpu_common import say, to_device
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # dtype, T, d, I, E, k: bf16 grouped GEMMs; MXFP8 on 128-row ring tiles; MXFP8 on the
+    # 256-row tiles (persistent GEMM2, whose tile counters are cleared by a kernel each call)
+    ("bf16", 300, 256, 128, 16, 4),
+    ("mxfp8", 300, 512, 512, 16, 4),
+    ("mxfp8", 1000, 512, 512, 8, 2),
+]
+
+
+@pytest.mark.parametrize("dtype,T,d,I,E,k", CASES)
+def test_layer_forward_replays_from_a_hip_graph(dtype, T, d, I, E, k):
+    say(f"case graph {dtype} T={T} d={d} I={I} E={E} k={k}")
+    wl = synth.Workload("graph", T=T, d=d, inter=I, E=E, k=k, shared=True, bias=True, dtype=dtype, seed=31)
+    inp = to_device(synth.make_layer_inputs(wl, device="cpu"))
+    other = to_device(synth.make_layer_inputs(wl.with_(seed=32), device="cpu"))
+    batches = [inp, dict(inp, x=other["x"], x_scale=other["x_scale"])]
+    ws = pg.Workspace(T, d, E, k, I, pg.MOE_MXFP8 if dtype == "mxfp8" else pg.MOE_BF16, device="cuda")
+    eager = [pg.layer_forward(b, k, ws=ws) for b in batches]
+    assert not torch.equal(eager[0]["y"], eager[1]["y"])
+
+    static = dict(inp, x=inp["x"].clone(),
+                  x_scale=None if inp["x_scale"] is None else inp["x_scale"].clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pg.layer_forward(static, k, ws=ws, check=False)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        res = pg.layer_forward(static, k, ws=ws, check=False)
+    torch.cuda.synchronize()
+
+    for rep in range(4):
+        b = rep % 2
+        static["x"].copy_(batches[b]["x"])
+        if static["x_scale"] is not None:
+            static["x_scale"].copy_(batches[b]["x_scale"])
+        graph.replay()
+        torch.cuda.synchronize()
+        for name in ("ids", "weights", "offsets", "perm", "row_of", "y"):
+            assert torch.equal(res[name], eager[b][name]), (rep, name)
+        # eager work between the replays
+        again = pg.layer_forward(batches[1 - b], k, ws=ws)
+        assert torch.equal(again["y"], eager[1 - b]["y"])
+    assert pg.moe_check(ws) == 0
+    say("  4 replays bitwise equal to the eager calls")

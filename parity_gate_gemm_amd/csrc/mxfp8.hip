@@ -455,9 +455,9 @@ __device__ __forceinline__ void xr_kloop(const uint8_t* ring, uint32_t ring_lds,
       xr_sync<0>();
     if (j + 1 < nsteps) issue(j + 1);
     if (scales_at(j)) issue_scales(j / XR_GS + 1);
-    // the next tile's index, fetched along with step 2's loads (its reply comes before
-    // theirs, so the next step's wait does not stall on it)
-    // (the ring runs at least 4 steps; were there fewer, qn would stay negative: no next tile)
+    // the next tile's position, fetched right after step 2's loads go out, so its latency
+    // overlaps theirs (the ring runs at least 4 steps; were there fewer, qn would stay
+    // negative: no next tile)
     if (ctr && j == 1 && threadIdx.x == 0) qn = atomicAdd(ctr, 1);
     if constexpr (NB > 0) {
       const uint8_t* st = ring + (j & 1) * XR_STAGE;

@@ -553,6 +553,37 @@ def expert_forward_mxfp8(x_rows, w1, w3, w2, quant=mx_quantize):
     return a, g, hq, hq @ f64(w2).T
 
 
+def layer_mxfp8(x, w_gate, bias, experts, shared, k: int, ids_in=None, weights_in=None,
+                quant=mx_quantize):
+    """The MXFP8 layer's forward with h requantised to MXFP8 per row before the down
+    projection (the MoE activations travel as E4M3 values with one E8M0 scale per 32:
+    Composer 2 Technical Report, §6.1 "Kernels"; the scale rule is ``mx_quantize``'s):
+    routing and dispatch as in ``layer``, each expert (and the shared one) through
+    ``expert_forward_mxfp8``, the same combine.  Exact float64 otherwise."""
+    xf = f64(x)
+    T, d = xf.shape
+    if ids_in is None:
+        ids, w, logits = route(xf, w_gate, bias, k)
+    else:
+        ids, w, logits = route_replay(xf, w_gate, bias, ids_in, weights_in)
+    E = logits.shape[1]
+    offsets, perm, row_of = dispatch(ids, E)
+    rows = np.zeros((T * k, d), dtype=np.float64)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        rows[lo:hi] = expert_forward_mxfp8(xf[perm[lo:hi] // k], *experts[e], quant=quant)[3]
+    y = np.zeros((T, d), dtype=np.float64)
+    for t in range(T):
+        for r in range(k):
+            y[t] += w[t, r] * rows[row_of[t * k + r]]
+    if shared is not None:
+        y += expert_forward_mxfp8(xf, *shared, quant=quant)[3]
+    return {"y": y, "ids": ids, "weights": w, "logits": logits,
+            "offsets": offsets, "perm": perm, "row_of": row_of, "rows": rows}
+
+
 def expert_forward_nvfp4(x_rows, w1, w3, w2):
     """One expert of the NVFP4 forward (``expert_ffn_nvfp4``), keeping what its MXFP8
     backward takes: (xq, a, g, hq, out, (W1, W3, W2)) with xq the rows quantized to NVFP4

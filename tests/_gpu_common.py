@@ -11,6 +11,14 @@ import parity_gate_gemm_amd as pg
 
 TOL = {"f32": 2e-2, "bf16": 2e-2, "mxfp8": 6e-2}   # normwise max-abs-rel bar
 WEIGHT_TOL = 2e-6                                   # fp32 weights vs fp64 oracle
+# MXFP8 layers against the oracle that requantises h per row as the library does
+# (oracle.layer_mxfp8): what is left is the bf16 rounding of the expert outputs and of y
+# (relative Frobenius error about 2.5e-3) and the rare E4M3 code, or block scale, that a
+# last-bit difference of h moves across a rounding boundary.  Such a flip can show in
+# the largest elements of a row (normwise up to 4.6e-2 measured), so the normwise bar
+# stays the MXFP8 one and the relative Frobenius error, which isolated flips barely move,
+# must stay below 6e-3 (against the exact h it is about 2.7e-2).
+FROB_MX_HQ = 6e-3
 
 
 def say(*a):
@@ -66,8 +74,9 @@ def to_device(inp, device="cuda"):
     return out
 
 
-def oracle_for_rows(inp, rows, k, replay=False):
-    """Oracle layer on a subset of token rows (routing and FFN are row-local)."""
+def oracle_for_rows(inp, rows, k, replay=False, layer=oracle.layer):
+    """Oracle layer on a subset of token rows (routing and FFN are row-local);
+    ``layer=oracle.layer_mxfp8`` for the MXFP8 layer with h requantised."""
     xs = inp.get("x_scale")
     x = values(inp["x"][rows], None if xs is None else xs[rows])
     kw = {}
@@ -75,8 +84,8 @@ def oracle_for_rows(inp, rows, k, replay=False):
         kw["ids_in"] = inp["ids_in"].cpu().numpy()[rows]
         if inp.get("weights_in") is not None:
             kw["weights_in"] = host(inp["weights_in"])[rows]
-    return oracle.layer(x, host(inp["w_gate"]), host(inp.get("bias")), LazyExperts(inp),
-                        shared_of(inp), k, **kw)
+    return layer(x, host(inp["w_gate"]), host(inp.get("bias")), LazyExperts(inp),
+                 shared_of(inp), k, **kw)
 
 
 def compare_rows(res_gpu, ref, rows, dtype, replay=False):
@@ -90,6 +99,19 @@ def compare_rows(res_gpu, ref, rows, dtype, replay=False):
     say(f"  normwise err {err:.3e} (bar {TOL[dtype]})")
     assert err <= TOL[dtype], err
     return err
+
+
+def compare_rows_hq(res_gpu, ref_mx, rows):
+    """An MXFP8 layer's y against ``oracle.layer_mxfp8`` on the same rows: normwise
+    within the MXFP8 bar and relative Frobenius error within FROB_MX_HQ."""
+    y = host(res_gpu["y"])[rows]
+    nw = oracle.normwise_rel_err(y, ref_mx["y"])
+    fr = float(np.linalg.norm(y - ref_mx["y"]) / np.linalg.norm(ref_mx["y"]))
+    say(f"  against the requantised h: normwise {nw:.3e} (bar {TOL['mxfp8']}), "
+        f"Frobenius {fr:.3e} (bar {FROB_MX_HQ})")
+    assert nw <= TOL["mxfp8"], nw
+    assert fr <= FROB_MX_HQ, fr
+    return fr
 
 
 def check_routing_every_token(inp, res, k, E):

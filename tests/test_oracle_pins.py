@@ -868,6 +868,48 @@ def _mx_layer(seed, T=40, d=64, I=32, E=6, k=2, shared=True, bias=True):
     return x, wg, b, experts, sh, k, dy, rng
 
 
+def test_layer_mxfp8_identity_projections_give_the_quantised_h():
+    """With W1 = W3 = W2 = the identity (d = I = 32), k = 1 (weight exactly 1) and both
+    experts equal, y = MX(silu(x) x) row by row: the forward multiplies the per-row MXFP8
+    requantisation of h.  It differs from the exact h, and one token alone gives its row
+    of the batch (the quantisation never mixes tokens)."""
+    rng = np.random.default_rng(71)
+    T, d, E = 9, 32, 2
+    x = oracle.mx_quantize(rng.standard_normal((T, d)) * 2.0)
+    wg = rng.standard_normal((d, E))
+    eye = np.eye(d)
+    experts = [(eye, eye, eye)] * E
+    y = oracle.layer_mxfp8(x, wg, None, experts, None, 1)["y"]
+    h = x * x / (1.0 + np.exp(-x))
+    assert np.array_equal(y, oracle.mx_quantize(h, axis=1))
+    assert not np.array_equal(y, h)
+    for t in (0, 4, 8):
+        one = oracle.layer_mxfp8(x[t:t + 1], wg, None, experts, None, 1)["y"]
+        assert np.array_equal(one[0], y[t])
+
+
+@pytest.mark.parametrize("mode", ["learned", "replay"])
+def test_layer_mxfp8_is_the_mxfp8_backward_forward_and_layer_without_quantisation(mode):
+    """The forward of ``layer_backward_mxfp8`` (an independent loop over the same
+    readings) gives the same y bit for bit; with an identity quantiser the layer is the
+    unquantised ``layer``, bit for bit, with the same routing and dispatch."""
+    x, wg, b, experts, sh, k, dy, rng = _mx_layer(64)
+    T, E = x.shape[0], wg.shape[1]
+    kw = {} if mode == "learned" else {"ids_in": np.stack([rng.permutation(E)[:k] for _ in range(T)])}
+    f = oracle.layer_mxfp8(x, wg, b, experts, sh, k, **kw)
+    g = oracle.layer_backward_mxfp8(x, wg, b, experts, sh, k, dy, **kw)
+    assert np.array_equal(f["y"], g["y"])
+    ident = lambda v, axis=-1: np.asarray(v, float)  # noqa: E731
+    u = oracle.layer_mxfp8(x, wg, b, experts, sh, k, quant=ident, **kw)
+    ref = oracle.layer(x, wg, b, experts, sh, k, **kw)
+    assert np.array_equal(u["y"], ref["y"])
+    for n in ("ids", "weights", "offsets", "perm", "row_of"):
+        assert np.array_equal(u[n], ref[n]) and np.array_equal(f[n], ref[n]), n
+    # the quantised h moves y by a few percent of its size, not more
+    rel = float(np.linalg.norm(f["y"] - ref["y"]) / np.linalg.norm(ref["y"]))
+    assert 1e-3 < rel < 0.1, rel
+
+
 @pytest.mark.parametrize("mode", ["learned", "replay_gate_weights", "replay_caller_weights"])
 def test_mxfp8_backward_without_quantisation_is_the_exact_chain_rule(mode):
     x, wg, b, experts, sh, k, dy, rng = _mx_layer(62)

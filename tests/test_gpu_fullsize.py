@@ -18,8 +18,8 @@ import torch
 import oracle
 import parity_gate_gemm_amd as pg
 import synth
-from _gpu_common import (check_routing_every_token, compare_rows, oracle_for_rows, run_layer,
-                         sample_rows, say)
+from _gpu_common import (check_routing_every_token, compare_rows, compare_rows_hq, oracle_for_rows,
+                         run_layer, sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -212,6 +212,8 @@ def test_mxfp8_t32768_sampled_parity(c5):
     say(f"case mxfp8_t32768 layer output on {len(rows)} tokens {rows.tolist()}")
     err = compare_rows(res, oracle_for_rows(inp, rows, wl.k), rows, "mxfp8")
     say(f"  normwise err {err:.3e}")
+    # the same tokens against the oracle that requantises h as the library does
+    compare_rows_hq(res, oracle_for_rows(inp, rows, wl.k, layer=oracle.layer_mxfp8), rows)
 
 
 def test_mxfp8_t32768_determinism_and_permutation(c5):

@@ -3,9 +3,10 @@ row; the expert FFN quantizes x per token and h per row) against the oracle.
 
 The quantizer is compared bit for bit (codes, block scales, row scales) on rows built to
 hit every rounding case: zeros, zero blocks, exact ties of the E2M1 grid, saturation,
-values near the E4M3 subnormal range.  The layer output is compared normwise: the GPU's
-h (fp32 accumulation) can round to bf16, and then to E2M1, differently from the oracle's
-exact h at a few rounding boundaries, which the bar covers.
+values near the E4M3 subnormal range.  The layer output is compared normwise and by its
+relative Frobenius error: the GPU's h (fp32 accumulation) can round to bf16, and then to
+E2M1, differently from the oracle's exact h at a few rounding boundaries, which the
+normwise bar covers; the Frobenius bar is that of the bf16 roundings of the outputs.
 """
 import numpy as np
 import pytest
@@ -19,6 +20,10 @@ from _gpu_common import host, say, to_device
 pytestmark = pytest.mark.gpu
 
 BAR = 2e-2
+# relative Frobenius bar: what is left once the oracle quantizes x and h as the layer does
+# is the bf16 rounding of the expert outputs and of y (measured 2.2-2.6e-3 on 25 seeded
+# layers, normwise 2.9-4.3e-3)
+FROB = 6e-3
 
 
 def _unpack(packed):
@@ -94,9 +99,12 @@ def _compare(res, inp, rows, k):
     x = host(inp["x"])[rows]
     ref = oracle.layer_nvfp4(x, host(inp["w_gate"]), host(inp.get("bias")), experts, shared, k)
     assert np.array_equal(res["ids"].cpu().numpy()[rows], ref["ids"])
-    err = oracle.normwise_rel_err(host(res["y"])[rows], ref["y"])
-    say(f"  normwise err {err:.3e}")
+    y = host(res["y"])[rows]
+    err = oracle.normwise_rel_err(y, ref["y"])
+    fr = float(np.linalg.norm(y - ref["y"]) / np.linalg.norm(ref["y"]))
+    say(f"  normwise err {err:.3e} (bar {BAR}), relative Frobenius {fr:.3e} (bar {FROB})")
     assert err <= BAR
+    assert fr <= FROB
     return err
 
 

@@ -18,6 +18,8 @@ CASES = [
     ("bf16", 300, 256, 128, 16, 4),
     ("mxfp8", 300, 512, 512, 16, 4),
     ("mxfp8", 1000, 512, 512, 8, 2),
+    # NVFP4 forward: x quantized per token inside the call, fp16-MFMA GEMMs on decoded codes
+    ("nvfp4", 300, 256, 128, 16, 4),
 ]
 
 
@@ -27,8 +29,11 @@ def test_layer_forward_replays_from_a_hip_graph(dtype, T, d, I, E, k):
     wl = synth.Workload("graph", T=T, d=d, inter=I, E=E, k=k, shared=True, bias=True, dtype=dtype, seed=31)
     inp = to_device(synth.make_layer_inputs(wl, device="cpu"))
     other = to_device(synth.make_layer_inputs(wl.with_(seed=32), device="cpu"))
+    if dtype == "nvfp4":   # the weight banks K-blocked once, outside the graph
+        inp = pg.nvfp4_pack_inputs(inp)
     batches = [inp, dict(inp, x=other["x"], x_scale=other["x_scale"])]
-    ws = pg.Workspace(T, d, E, k, I, pg.MOE_MXFP8 if dtype == "mxfp8" else pg.MOE_BF16, device="cuda")
+    fdt = {"bf16": pg.MOE_BF16, "mxfp8": pg.MOE_MXFP8, "nvfp4": pg.MOE_NVFP4}[dtype]
+    ws = pg.Workspace(T, d, E, k, I, fdt, device="cuda")
     eager = [pg.layer_forward(b, k, ws=ws) for b in batches]
     assert not torch.equal(eager[0]["y"], eager[1]["y"])
 

@@ -4,7 +4,8 @@ rule in fp64.
 Every gradient (dx, the routing-weight gradients, the gate's, every expert's dW1 / dW3
 / dW2 and the shared expert's) is compared as a whole tensor, normwise (max |err| /
 max |ref|), to 2e-2: the bf16 roundings of h, of the expert outputs and of the
-gradients fed to the bf16 GEMMs are inside that bar, as for the forward.  Shapes
+gradients fed to the bf16 GEMMs are inside that bar, as for the forward; on the small
+layers also by its relative Frobenius error, to 6e-3, which those roundings fix.  Shapes
 span several 128-row tiles, ragged segments, experts with no rows (their gradients
 must be exactly zero), k = 1, the three routing modes (learned, replay with the
 gate's weights, replay with caller weights: no gate gradient) and both column-tile
@@ -23,6 +24,9 @@ from _gpu_common import LazyExperts, host, say, shared_of, to_device, values
 pytestmark = pytest.mark.gpu
 
 BAR = 2e-2
+# relative Frobenius bar of the small layers' whole gradient tensors, from the same bf16
+# roundings (each element off by at most 2^-9, about 1.1e-3 rms; measured 1.4-3.3e-3)
+BAR_FRO = 6e-3
 
 
 def _nerr(got, ref):
@@ -30,6 +34,14 @@ def _nerr(got, ref):
     ref = np.asarray(ref, dtype=np.float64)
     den = np.max(np.abs(ref))
     return float(np.max(np.abs(got - ref)) / (den if den > 0 else 1.0))
+
+
+def _ferr(got, ref):
+    """Relative Frobenius error (0 against an all-zero reference only if got is zero)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    fro = np.linalg.norm(ref)
+    return float(np.linalg.norm(got - ref) / (fro if fro > 0 else 1.0))
 
 
 def _dy(T, d, seed):
@@ -58,25 +70,27 @@ def _oracle(inp, k, dy, replay=False):
 
 
 def _compare(bwd, ref, E, has_shared, gate):
-    errs = {"dx": _nerr(host(bwd["dx"]), ref["dx"]),
-            "d_weights": _nerr(host(bwd["d_weights"]), ref["d_weights"])}
+    pairs = {"dx": (host(bwd["dx"]), ref["dx"]),
+             "d_weights": (host(bwd["d_weights"]), ref["d_weights"])}
     for n in ("w1", "w3", "w2"):
         got = host(bwd["grads"][n])
-        errs["d" + n] = _nerr(got, ref["d" + n])
+        pairs["d" + n] = (got, ref["d" + n])
         for e in range(E):          # experts without rows: exactly zero
             if not ref["d" + n][e].any():
                 assert not got[e].any(), (n, e)
     if has_shared:
         for i, n in enumerate(("w1", "w3", "w2")):
-            errs["shared_d" + n] = _nerr(host(bwd["shared_grads"][n]), ref["d_shared"][i])
+            pairs["shared_d" + n] = (host(bwd["shared_grads"][n]), ref["d_shared"][i])
     if gate:
-        errs["d_w_gate"] = _nerr(host(bwd["d_w_gate"]), ref["d_w_gate"])
+        pairs["d_w_gate"] = (host(bwd["d_w_gate"]), ref["d_w_gate"])
         if ref["d_bias"] is not None:
-            errs["d_bias"] = _nerr(host(bwd["d_bias"]), ref["d_bias"])
+            pairs["d_bias"] = (host(bwd["d_bias"]), ref["d_bias"])
     else:
         assert bwd["d_w_gate"] is None
-    say("  " + ", ".join(f"{a} {b:.2e}" for a, b in errs.items()))
-    bad = {a: b for a, b in errs.items() if not b <= BAR}
+    errs = {a: _nerr(*gr) for a, gr in pairs.items()}
+    fros = {a: _ferr(*gr) for a, gr in pairs.items()}
+    say("  " + ", ".join(f"{a} {errs[a]:.2e}/{fros[a]:.2e}" for a in errs))
+    bad = {a: (errs[a], fros[a]) for a in errs if not (errs[a] <= BAR and fros[a] <= BAR_FRO)}
     assert not bad, bad
 
 
